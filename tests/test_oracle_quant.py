@@ -1,0 +1,171 @@
+"""Pins of the oracle's encoders and quantisers.
+
+- E4M3 element encoding: torch's fp32 -> float8_e4m3fn cast (round to nearest even) on every
+  midpoint, midpoint +- 1 ulp and random values up to 464 (torch returns NaN above 464, where the
+  oracle saturates to 448 by the reading taken for overflow).
+- E2M1 element encoding: numpy's half-to-even np.round on the spacing of each binade.
+- floor(log2): the defining inequality 2^j <= a < 2^(j+1), checked exactly.
+- Block scale rule: closed cases (powers of two and their predecessors, zero, clamps).
+- Block quantiser: torch's cast of x * 2^(127-E) (E4M3), the binade rounding (E2M1).
+- int8/int4 quantiser: torch's fp32 division, fp16 conversion and half-to-even rounding.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_quantized_amd import synth
+from conftest import read_golden
+
+
+def torch_enc_e4m3(v32):
+    return torch.from_numpy(np.ascontiguousarray(v32, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def e2m1_table():
+    return np.array([float(v) for _, v in read_golden("e2m1_values.txt")])
+
+
+def grid_enc_e2m1(v):
+    """Nearest E2M1 value by rounding |v| on its binade's spacing with np.round (half to even)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    sp = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
+    r = np.minimum(np.round(a / sp) * sp, 6.0)
+    tab = e2m1_table()[:8]
+    mag = np.array([int(np.where(tab == x)[0][0]) for x in r.ravel()]).reshape(r.shape)
+    return (mag | (np.signbit(v) * 8)).astype(np.uint8)
+
+
+def test_enc_e4m3_matches_torch_in_range(orc):
+    pos = np.arange(0x7F, dtype=np.uint8)
+    vals = torch.from_numpy(pos).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mids = (vals[:-1] + vals[1:]) / 2
+    mids32 = mids.astype(np.float32)
+    assert np.array_equal(mids32.astype(np.float64), mids)          # midpoints are fp32 values
+    up = np.nextafter(mids32, np.float32(np.inf))
+    dn = np.nextafter(mids32, np.float32(-np.inf))
+    g = np.random.Generator(np.random.PCG64(7))
+    rnd = (g.random(20000) * 464.0).astype(np.float32)
+    tiny = (g.random(5000) * 2.0 ** -8).astype(np.float32)
+    allv = np.concatenate([mids32, up, dn, rnd, tiny, vals.astype(np.float32)])
+    allv = np.concatenate([allv, -allv])
+    got = orc.enc_elem(0, allv.astype(np.float64))
+    assert np.array_equal(got, torch_enc_e4m3(allv))
+
+
+def test_enc_e4m3_saturates_and_keeps_sign(orc):
+    big = np.array([464.0001, 480.0, 511.9, 512.0, 1e6, 3e38])
+    assert np.all(orc.enc_elem(0, big) == 0x7E)
+    assert np.all(orc.enc_elem(0, -big) == 0xFE)
+    assert orc.enc_elem(0, [-0.0])[0] == 0x80
+    assert orc.enc_elem(0, [-2.0 ** -11])[0] == 0x80      # rounds to zero, sign kept
+    assert orc.enc_elem(0, [2.0 ** -10])[0] == 0x00       # tie between 0 and 2^-9: even code 0
+
+
+def test_enc_e2m1_matches_binade_rounding(orc):
+    tab = e2m1_table()[:8]
+    mids = (tab[:-1] + tab[1:]) / 2
+    eps = 1e-9
+    g = np.random.Generator(np.random.PCG64(8))
+    vals = np.concatenate([tab, mids, mids + eps, mids - eps, g.random(5000) * 6.0, [6.5, 7.99, 8.0, 100.0]])
+    vals = np.concatenate([vals, -vals])
+    assert np.array_equal(orc.enc_elem(4, vals), grid_enc_e2m1(vals))
+    # ties listed by hand: 0.25->0, 0.75->1, 1.25->1, 1.75->2, 2.5->2, 3.5->4, 5->4
+    got = orc.enc_elem(4, [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    assert list(e2m1_table()[got]) == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
+
+
+def test_floor_log2_defining_inequality(orc):
+    g = np.random.Generator(np.random.PCG64(9))
+    vals = list(g.random(2000) * 10.0 ** g.integers(-40, 38, 2000))
+    for j in range(-149, 128):
+        p = math.ldexp(1.0, j)
+        vals += [p, np.nextafter(p, 0.0), np.nextafter(p, np.inf)]
+    for a in vals:
+        if a <= 0:
+            continue
+        j = orc.floor_log2(a)
+        assert math.ldexp(1.0, j) <= a < math.ldexp(1.0, j + 1)
+
+
+@pytest.mark.parametrize("fmt,emax", [(0, 8), (4, 2)])
+def test_scale_rule_closed_cases(orc, fmt, emax):
+    for j in range(-60, 60):
+        p = math.ldexp(1.0, j)
+        assert orc.mx_scale_code(fmt, p) == j - emax + 127
+        assert orc.mx_scale_code(fmt, float(np.nextafter(np.float32(p), np.float32(0)))) == j - 1 - emax + 127
+    assert orc.mx_scale_code(fmt, 0.0) == 0
+    assert orc.mx_scale_code(fmt, 1e-44) == 0                 # clamps at 0
+    assert orc.mx_scale_code(fmt, 3e38) == min(254, 127 - emax + 127)
+
+
+def test_mx_quantize_e4m3_vs_torch(orc):
+    rows, cols = 64, 512
+    x = synth.normal((rows, cols), 1.0, 1000)
+    x[3, :32] = 0.0                                           # all-zero block
+    x[4, 32:64] *= 1e-30                                      # tiny block
+    codes, scales = orc.mx_quantize(0, x)
+    for r in range(rows):
+        for b in range(cols // 32):
+            blk = x[r, 32 * b:32 * b + 32].astype(np.float64)
+            amax = np.max(np.abs(blk))
+            E = int(scales[r, b])
+            if amax == 0:
+                assert E == 0
+            else:
+                j = E - 127 + 8
+                assert math.ldexp(1.0, j) <= amax < math.ldexp(1.0, j + 1)
+            v = (blk * math.ldexp(1.0, 127 - E)).astype(np.float32)
+            ref = torch_enc_e4m3(v)
+            sat = np.abs(v) > 464
+            ref[sat] = np.where(v[sat] < 0, 0xFE, 0x7E)
+            assert np.array_equal(codes[r, 32 * b:32 * b + 32], ref)
+
+
+def test_mx_quantize_e2m1_vs_binade_rounding(orc):
+    rows, cols = 32, 256
+    x = synth.normal((rows, cols), 1.0, 1040)
+    codes, scales = orc.mx_quantize(4, x)
+    assert codes.shape == (rows, cols // 2)
+    nib = np.empty((rows, cols), np.uint8)
+    nib[:, 0::2] = codes & 0xF
+    nib[:, 1::2] = codes >> 4
+    for r in range(rows):
+        for b in range(cols // 32):
+            blk = x[r, 32 * b:32 * b + 32].astype(np.float64)
+            E = int(scales[r, b])
+            j = E - 127 + 2
+            assert math.ldexp(1.0, j) <= np.max(np.abs(blk)) < math.ldexp(1.0, j + 1)
+            assert np.array_equal(nib[r, 32 * b:32 * b + 32], grid_enc_e2m1(blk * math.ldexp(1.0, 127 - E)))
+
+
+def test_mx_quantize_nonfinite_block(orc):
+    x = synth.normal((2, 64), 1.0, 5)
+    x[0, 3] = np.inf
+    x[1, 40] = np.nan
+    for fmt in (0, 4):
+        codes, scales = orc.mx_quantize(fmt, x)
+        assert scales[0, 0] == 0xFF and scales[1, 1] == 0xFF
+        assert scales[0, 1] != 0xFF and scales[1, 0] != 0xFF
+        per = 32 if fmt == 0 else 16
+        assert not codes[0, :per].any() and not codes[1, per:].any()
+
+
+@pytest.mark.parametrize("fw,qmax", [(32, 127), (33, 7)])
+def test_int_quantize_vs_torch(orc, fw, qmax):
+    K, N = 256, 96
+    w = synth.normal((K, N), 0.02, 1031)
+    w[32:64, 5] = 0.0                                         # zero block -> s = 0, q = 0
+    q, s = orc.int_quantize(fw, w)
+    wt = torch.from_numpy(w).view(K // 32, 32, N)
+    amax = wt.abs().amax(dim=1)
+    s_ref = (amax / qmax).to(torch.float16)
+    assert np.array_equal(s.view(np.uint16), s_ref.numpy().view(np.uint16))
+    sf = s_ref.float().unsqueeze(1)
+    q_ref = torch.where(sf == 0, torch.zeros_like(wt), torch.round(wt / sf)).clamp(-qmax, qmax)
+    assert np.array_equal(q, q_ref.reshape(K, N).to(torch.int8).numpy())
+    # every non-zero block reaches the end of the range
+    qa = np.abs(q.astype(np.int32)).reshape(K // 32, 32, N).max(axis=1)
+    assert np.all((qa == qmax) | (amax.numpy() == 0))
