@@ -225,10 +225,14 @@ void orc_dequant(int fmt, int64_t rows, int64_t cols, const uint8_t* codes, cons
 /* The element search is brute force over the format's own decode values (not bit arithmetic). */
 /* ------------------------------------------------------------------------------------------ */
 
-/* Nearest finite code magnitude for |v| (search over codes 0..ncodes-1 of the positive half). */
+/* Nearest finite code magnitude for |v| (search over codes 0..ncodes-1 of the positive half).
+ * Values at or beyond the largest finite element saturate to it; below it every candidate
+ * distance that can decide the choice is exact in fp64. */
 static unsigned nearest_code(double av, int fmt) {
   unsigned best = 0, ncodes = (fmt == ORC_E4M3) ? 0x7Fu : 8u; /* E4M3: 0x00..0x7E are finite */
   double bestd = INFINITY;
+  double vmax = (fmt == ORC_E4M3) ? orc_dec_e4m3(0x7Eu) : orc_dec_e2m1(7u);
+  if (av >= vmax) return ncodes - 1u;
   for (unsigned c = 0; c < ncodes; c++) {
     double d = fabs(av - (fmt == ORC_E4M3 ? orc_dec_e4m3(c) : orc_dec_e2m1(c)));
     if (d < bestd || (d == bestd && (c & 1u) == 0u)) { bestd = d; best = c; }

@@ -64,6 +64,14 @@ def test_enc_e4m3_saturates_and_keeps_sign(orc):
     assert orc.enc_elem(0, [2.0 ** -10])[0] == 0x00       # tie between 0 and 2^-9: even code 0
 
 
+def test_enc_saturates_far_beyond_range(orc):
+    # Far above the largest element the fp64 distances to every code coincide; the encoder must
+    # still return the largest finite code (E4M3 0x7E = 448, E2M1 7 = 6), with the sign kept.
+    huge = np.array([1e6, 1e30, 3.4e38, 1e300])
+    assert np.all(orc.enc_elem(0, huge) == 0x7E) and np.all(orc.enc_elem(0, -huge) == 0xFE)
+    assert np.all(orc.enc_elem(4, huge) == 7) and np.all(orc.enc_elem(4, -huge) == 15)
+
+
 def test_enc_e2m1_matches_binade_rounding(orc):
     tab = e2m1_table()[:8]
     mids = (tab[:-1] + tab[1:]) / 2
