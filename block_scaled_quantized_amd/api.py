@@ -1,0 +1,161 @@
+"""ctypes binding of libmxgemm.so (declared in include/mxgemm.h).
+
+Argument marshalling only: every entry point has the C name, takes torch tensors (or raw integer
+pointers) and an optional stream, checks nothing beyond what it needs to marshal, and raises
+MXError when the library returns a non-zero status. All arithmetic runs in the HIP library; if
+the shared library is missing this module raises at import time.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmxgemm.so")
+
+MX_E4M3, MX_E2M1, MX_E8M0, MX_F16, MX_INT8, MX_INT4 = 0, 4, 8, 16, 32, 33
+MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_FORMAT, MX_ERR_ARCH, MX_ERR_LAUNCH, MX_ERR_NOMEM = \
+    0, -1, -2, -3, -4, -5, -6, -7
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_scaled_quantized_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i, _u, _i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_int64
+
+EXPORTS = {
+    "mx_strerror": (ctypes.c_char_p, [_i]),
+    "mx_version": (_i, []),
+    "mxgemm_create": (_i, [ctypes.POINTER(_vp), _i, _i, _i, _i, _i, _u]),
+    "mxgemm_run": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "mxgemm_destroy": (_i, [_vp]),
+    "mxgemm_plan_info": (_i, [_vp, ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i)]),
+    "mxmatvec_run": (_i, [_i, _i, _i, _vp, _vp, _i, _vp, _vp, _vp]),
+    "mx_pack_run": (_i, [_i, _vp, _i, _i, _vp, _vp, _vp]),
+    "mx_unpack_run": (_i, [_i, _vp, _vp, _i, _i, _vp, _vp]),
+    "mx_pack_host": (_i, [_i, _vp, _i64, _i64, _vp, _vp]),
+    "mx_unpack_host": (_i, [_i, _vp, _vp, _i64, _i64, _vp]),
+    "mx_encode_host": (ctypes.c_uint8, [_i, ctypes.c_float]),
+    "mx_decode_host": (ctypes.c_float, [_i, ctypes.c_uint8]),
+}
+for _name, (_res, _args) in EXPORTS.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+class MXError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {mx_strerror(status)} (status {status})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != MX_OK:
+        raise MXError(status, where)
+
+
+def _ptr(t) -> int | None:
+    """Device/host address of a tensor or ndarray, or an int passed through (None stays None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if hasattr(t, "data_ptr"):
+        return t.data_ptr()
+    return t.ctypes.data  # numpy
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def mx_strerror(status: int) -> str:
+    return _lib.mx_strerror(status).decode()
+
+
+def mx_version() -> int:
+    return _lib.mx_version()
+
+
+class Plan:
+    """Owns an mxgemm_t; released by mxgemm_destroy when garbage-collected or on close()."""
+
+    def __init__(self, handle: int, M: int, N: int, K: int, fa: int, fb: int):
+        self.handle, self.M, self.N, self.K, self.fa, self.fb = handle, M, N, K, fa, fb
+
+    def close(self):
+        if self.handle:
+            _lib.mxgemm_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def mxgemm_create(M: int, N: int, K: int, fa: int, fb: int, flags: int = 0) -> Plan:
+    h = _vp()
+    _check(_lib.mxgemm_create(ctypes.byref(h), M, N, K, fa, fb, flags), "mxgemm_create")
+    return Plan(h.value, M, N, K, fa, fb)
+
+
+def mxgemm_plan_info(plan: Plan):
+    a, b, c = _i(), _i(), _i()
+    _check(_lib.mxgemm_plan_info(plan.handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "mxgemm_plan_info")
+    return a.value, b.value, c.value
+
+
+def mxgemm_run(plan: Plan, A, SA, B, SB, C, stream=None) -> None:
+    _check(_lib.mxgemm_run(plan.handle, _ptr(A), _ptr(SA), _ptr(B), _ptr(SB), _ptr(C), _stream(stream)), "mxgemm_run")
+
+
+def mxgemm_destroy(plan: Plan) -> None:
+    plan.close()
+
+
+def mxmatvec_run(M: int, N: int, K: int, x, W, fw: int, Ws, y, stream=None) -> None:
+    _check(_lib.mxmatvec_run(M, N, K, _ptr(x), _ptr(W), fw, _ptr(Ws), _ptr(y), _stream(stream)), "mxmatvec_run")
+
+
+def mx_pack_run(f: int, src, rows: int, cols: int, codes, scales, stream=None) -> None:
+    _check(_lib.mx_pack_run(f, _ptr(src), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)), "mx_pack_run")
+
+
+def mx_unpack_run(f: int, codes, scales, rows: int, cols: int, out, stream=None) -> None:
+    _check(_lib.mx_unpack_run(f, _ptr(codes), _ptr(scales), rows, cols, _ptr(out), _stream(stream)), "mx_unpack_run")
+
+
+def mx_pack_host(f: int, src, rows: int, cols: int, codes, scales) -> None:
+    _check(_lib.mx_pack_host(f, _ptr(src), rows, cols, _ptr(codes), _ptr(scales)), "mx_pack_host")
+
+
+def mx_unpack_host(f: int, codes, scales, rows: int, cols: int, out) -> None:
+    _check(_lib.mx_unpack_host(f, _ptr(codes), _ptr(scales), rows, cols, _ptr(out)), "mx_unpack_host")
+
+
+def mx_encode_host(f: int, v: float) -> int:
+    return int(_lib.mx_encode_host(f, v))
+
+
+def mx_decode_host(f: int, code: int) -> float:
+    return float(_lib.mx_decode_host(f, code))
+
+
+# ---- allocation helpers (torch for device memory; sizes follow the layouts in mxgemm.h) --------
+
+def mx_shapes(fmt: int, rows: int, K: int):
+    """(codes shape, scales shape) of an MX operand with `rows` rows of K elements."""
+    return ((rows, K // 2) if fmt == MX_E2M1 else (rows, K)), (rows, K // 32)
+
+
+def int_shapes(fw: int, K: int, N: int):
+    """(codes shape, scales shape) of an int8/int4 weight W[K][N]."""
+    return ((K, N // 2) if fw == MX_INT4 else (K, N)), (K // 32, N)

@@ -1,0 +1,148 @@
+// api.cpp -- the C ABI of libmxgemm (declared in include/mxgemm.h): argument validation, GEMM
+// plans (tile choice), device architecture check and dispatch to the kernels.
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "common.h"
+
+namespace mx {
+int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
+                int N, int K, hipStream_t stream);
+int matvec_launch(int M, int N, int K, const void* x, const void* W, bool int8, const void* Ws, void* y,
+                  hipStream_t stream);
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+}  // namespace
+
+int check_arch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return MX_ERR_ARCH;
+  }
+  if (dev < kMaxDevices) {
+    int v = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (v) return v == 1 ? MX_OK : MX_ERR_ARCH;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return MX_ERR_ARCH;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? MX_OK : MX_ERR_ARCH;
+}
+
+}  // namespace mx
+
+using namespace mx;
+
+struct mxgemm_plan {
+  int M, N, K, fa, fb, kind, tile_id;
+};
+
+namespace {
+
+struct TileInfo {
+  int bm, bn, eff_pct;
+};
+// Tile ids understood by gemm_launch, with a rough per-CU efficiency used to rank them.
+constexpr TileInfo kTiles[] = {{256, 256, 100}, {256, 224, 97}, {128, 128, 60}, {64, 64, 30}};
+constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+constexpr int kCUs = 256;
+
+int choose_tile(int M, int N) {
+  if (const char* env = std::getenv("MXGEMM_TILE")) {
+    int t = std::atoi(env);
+    if (t >= 0 && t < kNumTiles) return t;
+  }
+  int best = 0;
+  double best_cost = 1e300;
+  for (int t = 0; t < kNumTiles; t++) {
+    const int64_t tiles = (int64_t)((M + kTiles[t].bm - 1) / kTiles[t].bm) * ((N + kTiles[t].bn - 1) / kTiles[t].bn);
+    const int64_t waves = (tiles + kCUs - 1) / kCUs;
+    const double cost = (double)waves * kTiles[t].bm * kTiles[t].bn * 100.0 / kTiles[t].eff_pct;
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = t;
+    }
+  }
+  return best;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_strerror(int s) {
+  switch (s) {
+    case MX_OK: return "ok";
+    case MX_ERR_NULL: return "a required pointer is NULL";
+    case MX_ERR_SHAPE: return "unsupported or invalid dimensions";
+    case MX_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case MX_ERR_FORMAT: return "unsupported format or format pair";
+    case MX_ERR_ARCH: return "current device is not gfx950 (or no device)";
+    case MX_ERR_LAUNCH: return "kernel launch failed";
+    case MX_ERR_NOMEM: return "host allocation failed";
+    default: return "unknown status";
+  }
+}
+
+int mx_version(void) { return 100; }
+
+int mxgemm_create(mxgemm_t* out, int M, int N, int K, int fa, int fb, unsigned flags) {
+  if (!out) return MX_ERR_NULL;
+  *out = nullptr;
+  if (flags != 0u) return MX_ERR_FORMAT;
+  int kind;
+  if (fa == MX_E4M3 && fb == MX_E4M3) kind = 0;
+  else if (fa == MX_E2M1 && fb == MX_E2M1) kind = 1;
+  else if (fa == MX_F16 && fb == MX_F16) kind = 2;
+  else return MX_ERR_FORMAT;
+  if (M < 1 || N < 1 || K < 32 || M > MX_MAX_DIM || N > MX_MAX_DIM || K > MX_MAX_DIM) return MX_ERR_SHAPE;
+  if (kind != 2 && K % 32) return MX_ERR_SHAPE;
+  if (kind == 2 && (K % 8 || N % 8)) return MX_ERR_SHAPE;
+  mxgemm_plan* p = new (std::nothrow) mxgemm_plan{M, N, K, fa, fb, kind, choose_tile(M, N)};
+  if (!p) return MX_ERR_NOMEM;
+  *out = p;
+  return MX_OK;
+}
+
+int mxgemm_destroy(mxgemm_t p) {
+  delete p;
+  return MX_OK;
+}
+
+int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k) {
+  if (!p || !tile_m || !tile_n || !tile_k) return MX_ERR_NULL;
+  *tile_m = kTiles[p->tile_id].bm;
+  *tile_n = kTiles[p->tile_id].bn;
+  *tile_k = p->kind == 0 ? 128 : (p->kind == 1 ? 256 : 64);
+  return MX_OK;
+}
+
+int mxgemm_run(mxgemm_t p, const void* A, const void* SA, const void* B, const void* SB, void* C, void* stream) {
+  if (!p || !A || !B || !C) return MX_ERR_NULL;
+  if (p->kind != 2 && (!SA || !SB)) return MX_ERR_NULL;
+  if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return MX_ERR_ALIGN;
+  if (p->kind != 2 && (!aligned16(SA) || !aligned16(SB))) return MX_ERR_ALIGN;
+  if (int a = check_arch()) return a;
+  return gemm_launch(p->kind, p->tile_id, A, SA, B, SB, C, p->M, p->N, p->K, as_stream(stream));
+}
+
+int mxmatvec_run(int M, int N, int K, const void* x, const void* W, int fw, const void* Ws, void* y, void* stream) {
+  if (!x || !W || !Ws || !y) return MX_ERR_NULL;
+  if (fw != MX_INT8 && fw != MX_INT4) return MX_ERR_FORMAT;
+  if (M < 1 || M > 8 || N < 1 || N > MX_MAX_DIM || K < 32 || K > MX_MAX_DIM || K % 32) return MX_ERR_SHAPE;
+  if (fw == MX_INT8 ? (N % 16) : (N % 32)) return MX_ERR_SHAPE;
+  if (!aligned16(x) || !aligned16(W) || !aligned16(Ws) || !aligned16(y)) return MX_ERR_ALIGN;
+  if (int a = check_arch()) return a;
+  return matvec_launch(M, N, K, x, W, fw == MX_INT8, Ws, y, as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,183 @@
+// codec.hip -- GPU pack (quantise) and unpack (dequantise) kernels for the MX and integer
+// weight formats. Same rules as the host codec (quant_rules.h), hence bit-identical results.
+//
+// MX pack: 8 lanes own one 32-element block (4 elements each, one 16-byte load per lane); the
+// block amax and the non-finite flag are reduced over those 8 lanes with xor shuffles; every lane
+// then encodes its 4 elements into one 32-bit (E4M3) or 16-bit (E2M1) store. A wave covers eight
+// consecutive blocks, i.e. 1 KiB of contiguous fp32 input.
+#include "quant_rules.h"
+
+using namespace mx;
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void pack_mx_kernel(bool fp8, const float* __restrict__ src,
+                                                           int64_t nblocks, int64_t blocks_per_row,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales) {
+  const int sub = threadIdx.x & 7;
+  const int64_t stride = (int64_t)gridDim.x * (kThreads / 8);
+  for (int64_t blk = (int64_t)blockIdx.x * (kThreads / 8) + (threadIdx.x >> 3); blk < nblocks; blk += stride) {
+    const float4 v = reinterpret_cast<const float4*>(src)[blk * 8 + sub];
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    uint32_t amax = 0u, nonfinite = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      uint32_t a = fbits(x[i]) & 0x7FFFFFFFu;
+      nonfinite |= (uint32_t)(a >= 0x7F800000u);
+      amax = a > amax ? a : amax;
+    }
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      uint32_t o = (uint32_t)__shfl_xor((int)amax, off, 8);
+      amax = o > amax ? o : amax;
+      nonfinite |= (uint32_t)__shfl_xor((int)nonfinite, off, 8);
+    }
+    int t;
+    const uint32_t E = mx_block_scale(amax, nonfinite != 0u, fp8, &t);
+    if (sub == 0) {
+      const int64_t r = blk / blocks_per_row, b = blk % blocks_per_row;
+      scales[r * blocks_per_row + b] = (uint8_t)E;
+    }
+    if (fp8) {
+      uint32_t w = 0u;
+      if (!nonfinite) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) w |= enc_elem_scaled(true, x[i], t) << (8 * i);
+      }
+      reinterpret_cast<uint32_t*>(codes)[blk * 8 + sub] = w;
+    } else {
+      uint32_t w = 0u;
+      if (!nonfinite) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) w |= enc_elem_scaled(false, x[i], t) << (4 * i);
+      }
+      reinterpret_cast<uint16_t*>(codes)[blk * 8 + sub] = (uint16_t)w;
+    }
+  }
+}
+
+// Integer weights: one thread per (32-row block, column pair); columns are contiguous across
+// threads, so every row access of a wave is coalesced.
+__global__ __launch_bounds__(kThreads) void pack_int_kernel(bool i8, const float* __restrict__ w, int K, int N,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint16_t* __restrict__ scales) {
+  const int pairs = (N + 1) / 2;
+  const int64_t total = (int64_t)(K / 32) * pairs;
+  const int qmax = i8 ? 127 : 7;
+  for (int64_t id = (int64_t)blockIdx.x * kThreads + threadIdx.x; id < total; id += (int64_t)gridDim.x * kThreads) {
+    const int b = (int)(id / pairs), n0 = 2 * (int)(id % pairs);
+    const bool two = n0 + 1 < N;
+    float amax0 = 0.0f, amax1 = 0.0f;
+    for (int k = 32 * b; k < 32 * b + 32; k++) {
+      amax0 = fmaxf(amax0, fabsf(w[(int64_t)k * N + n0]));
+      if (two) amax1 = fmaxf(amax1, fabsf(w[(int64_t)k * N + n0 + 1]));
+    }
+    const uint16_t sb0 = int_block_scale(amax0, qmax), sb1 = int_block_scale(amax1, qmax);
+    scales[(int64_t)b * N + n0] = sb0;
+    if (two) scales[(int64_t)b * N + n0 + 1] = sb1;
+    const float s0 = dec_f16(sb0), s1 = dec_f16(sb1);
+    for (int k = 32 * b; k < 32 * b + 32; k++) {
+      const int64_t i = (int64_t)k * N + n0;
+      const int q0 = int_quant(w[i], s0, qmax);
+      const int q1 = two ? int_quant(w[i + 1], s1, qmax) : 0;
+      if (i8) {
+        codes[i] = (uint8_t)(int8_t)q0;
+        if (two) codes[i + 1] = (uint8_t)(int8_t)q1;
+      } else {
+        codes[i / 2] = (uint8_t)(((unsigned)q0 & 0xFu) | (((unsigned)q1 & 0xFu) << 4));  // N even
+      }
+    }
+  }
+}
+
+// MX unpack: one thread per 4 consecutive elements of a row (cols % 32 == 0).
+__global__ __launch_bounds__(kThreads) void unpack_mx_kernel(bool fp8, const uint8_t* __restrict__ codes,
+                                                             const uint8_t* __restrict__ scales, int64_t nquads,
+                                                             int64_t cols, float* __restrict__ out) {
+  for (int64_t qd = (int64_t)blockIdx.x * kThreads + threadIdx.x; qd < nquads; qd += (int64_t)gridDim.x * kThreads) {
+    const int64_t e0 = qd * 4, r = e0 / cols, c = e0 % cols;
+    const float s = dec_e8m0(scales[r * (cols / 32) + c / 32]);
+    uint32_t w = fp8 ? reinterpret_cast<const uint32_t*>(codes)[qd] : reinterpret_cast<const uint16_t*>(codes)[qd];
+    float4 o;
+    if (fp8) {
+      o = make_float4(dec_e4m3(w & 255u) * s, dec_e4m3((w >> 8) & 255u) * s, dec_e4m3((w >> 16) & 255u) * s,
+                      dec_e4m3(w >> 24) * s);
+    } else {
+      o = make_float4(dec_e2m1(w & 15u) * s, dec_e2m1((w >> 4) & 15u) * s, dec_e2m1((w >> 8) & 15u) * s,
+                      dec_e2m1((w >> 12) & 15u) * s);
+    }
+    reinterpret_cast<float4*>(out)[qd] = o;
+  }
+}
+
+// Integer unpack: one thread per element; the fp16 scale is shared by 32 rows of a column.
+__global__ __launch_bounds__(kThreads) void unpack_int_kernel(bool i8, const uint8_t* __restrict__ codes,
+                                                              const uint16_t* __restrict__ scales, int64_t total,
+                                                              int64_t cols, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total; i += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = i / cols, c = i % cols;
+    int q;
+    if (i8) q = (int)(int8_t)codes[i];
+    else q = (int)(((codes[i / 2] >> (4 * (i & 1))) & 0xFu) ^ 8u) - 8;
+    out[i] = (float)q * dec_f16(scales[(r / 32) * cols + c]);
+  }
+}
+
+int grid_for(int64_t work_items, int per_block) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  return (int)(g < 1 ? 1 : (g > 65536 ? 65536 : g));
+}
+
+}  // namespace
+
+extern "C" int mx_pack_run(int f, const float* src, int rows, int cols, void* codes, void* scales, void* stream) {
+  if (!src || !codes || !scales) return MX_ERR_NULL;
+  if (rows < 1 || cols < 1 || rows > MX_MAX_DIM || cols > MX_MAX_DIM) return MX_ERR_SHAPE;
+  if (!aligned16(src) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGN;
+  hipStream_t st = as_stream(stream);
+  if (f == MX_E4M3 || f == MX_E2M1) {
+    if (cols % 32) return MX_ERR_SHAPE;
+    if (int a = check_arch()) return a;
+    const int64_t nblocks = (int64_t)rows * (cols / 32);
+    hipLaunchKernelGGL(pack_mx_kernel, dim3(grid_for(nblocks, kThreads / 8)), dim3(kThreads), 0, st,
+                       f == MX_E4M3, src, nblocks, (int64_t)(cols / 32), (uint8_t*)codes, (uint8_t*)scales);
+    return launch_status();
+  }
+  if (f == MX_INT8 || f == MX_INT4) {
+    if (rows % 32 || (f == MX_INT4 && cols % 2)) return MX_ERR_SHAPE;
+    if (int a = check_arch()) return a;
+    const int64_t items = (int64_t)(rows / 32) * ((cols + 1) / 2);
+    hipLaunchKernelGGL(pack_int_kernel, dim3(grid_for(items, kThreads)), dim3(kThreads), 0, st, f == MX_INT8, src,
+                       rows, cols, (uint8_t*)codes, (uint16_t*)scales);
+    return launch_status();
+  }
+  return MX_ERR_FORMAT;
+}
+
+extern "C" int mx_unpack_run(int f, const void* codes, const void* scales, int rows, int cols, float* out,
+                             void* stream) {
+  if (!codes || !scales || !out) return MX_ERR_NULL;
+  if (rows < 1 || cols < 1 || rows > MX_MAX_DIM || cols > MX_MAX_DIM) return MX_ERR_SHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(out)) return MX_ERR_ALIGN;
+  hipStream_t st = as_stream(stream);
+  if (f == MX_E4M3 || f == MX_E2M1) {
+    if (cols % 32) return MX_ERR_SHAPE;
+    if (int a = check_arch()) return a;
+    const int64_t nquads = (int64_t)rows * cols / 4;
+    hipLaunchKernelGGL(unpack_mx_kernel, dim3(grid_for(nquads, kThreads)), dim3(kThreads), 0, st, f == MX_E4M3,
+                       (const uint8_t*)codes, (const uint8_t*)scales, nquads, (int64_t)cols, out);
+    return launch_status();
+  }
+  if (f == MX_INT8 || f == MX_INT4) {
+    if (rows % 32 || (f == MX_INT4 && cols % 2)) return MX_ERR_SHAPE;
+    if (int a = check_arch()) return a;
+    const int64_t total = (int64_t)rows * cols;
+    hipLaunchKernelGGL(unpack_int_kernel, dim3(grid_for(total, kThreads)), dim3(kThreads), 0, st, f == MX_INT8,
+                       (const uint8_t*)codes, (const uint16_t*)scales, total, (int64_t)cols, out);
+    return launch_status();
+  }
+  return MX_ERR_FORMAT;
+}

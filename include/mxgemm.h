@@ -1,0 +1,171 @@
+/*
+ * mxgemm.h -- C ABI of libmxgemm.so: block-scaled (MX) quantized GEMM, fp16 GEMM, int8/int4
+ * dequant matvec and the MX/int codecs, for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ *  - Every function returns an mx_status; 0 is success. Arguments are validated before any work
+ *    is queued, and nothing is written when validation fails.
+ *  - Device pointers are owned by the caller (allocated with hipMalloc or by a framework); the
+ *    library never allocates, frees or retains them. Host pointers likewise.
+ *  - `stream` is a hipStream_t passed as an opaque pointer (NULL = the default stream). GPU entry
+ *    points only enqueue work on that stream and return; they never synchronise. Calls on
+ *    different streams may run concurrently.
+ *  - Device pointers must be 16-byte aligned. Matrices are dense and row-major with the leading
+ *    dimension equal to the row length given below.
+ *  - A GPU entry point called on a device that is not gfx950 returns MX_ERR_ARCH.
+ *
+ * Formats (the pages name the types, the OCP Microscaling v1.0 formats give their bits):
+ *  - MX_E4M3: FP8 E4M3 "FN" (bias 7, S.1111.111 = NaN, no Inf, max 448), one byte per element.
+ *  - MX_E2M1: FP4 E2M1 (bias 1, +-{0,.5,1,1.5,2,3,4,6}), two elements per byte, the element with
+ *    the even index in the low nibble.
+ *  - Scales of MX operands: E8M0 bytes, value 2^(e-127), 0xFF = NaN; one scale per 32
+ *    consecutive elements along K ("Scale planes: one MTLTensor = data + scales" and the
+ *    auxiliary-plane blockFactors {32,1} of the WWDC26 session 330 summary).
+ *  - MX_F16: IEEE binary16. MX_INT8: two's-complement bytes. MX_INT4: two's-complement nibbles,
+ *    packed two per byte along the C-order linear index, the even index in the low nibble
+ *    ("TensorOps ... notes", section "VALIDATED ON M4 MAX", fact 5).
+ */
+#ifndef MXGEMM_H
+#define MXGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MX_OK = 0,
+  MX_ERR_NULL = -1,    /* a required pointer is NULL */
+  MX_ERR_SHAPE = -2,   /* a dimension is out of range or violates a divisibility rule */
+  MX_ERR_ALIGN = -3,   /* a device pointer is not 16-byte aligned */
+  MX_ERR_FORMAT = -4,  /* unsupported format or format pair */
+  MX_ERR_ARCH = -5,    /* the current device is not gfx950, or no device is present */
+  MX_ERR_LAUNCH = -6,  /* the HIP runtime reported an error when queueing a kernel */
+  MX_ERR_NOMEM = -7    /* host allocation of a plan failed */
+} mx_status;
+
+/* MX_E8M0 names the scale format; it is accepted only by mx_decode_host. */
+typedef enum { MX_E4M3 = 0, MX_E2M1 = 4, MX_E8M0 = 8, MX_F16 = 16, MX_INT8 = 32, MX_INT4 = 33 } mx_format;
+
+/* Largest accepted dimension of any matrix (rows or columns). */
+#define MX_MAX_DIM (1 << 20)
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* mx_strerror(int status);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int mx_version(void);
+
+/* ------------------------------------------------------------------------------------------ */
+/* GEMM plans.                                                                                  */
+/* ------------------------------------------------------------------------------------------ */
+
+typedef struct mxgemm_plan* mxgemm_t;
+
+/*
+ * mxgemm_create -- validate a GEMM problem C[M,N] = A[M,K] * B[K,N] and choose its kernel.
+ *
+ * Operation ("TensorOps ... notes", sections "Scale planes" and "Kernel-phase findings"; WWDC26
+ * session 330 summary, sections on the MXFP8 tensor type and the quantized matmul2d):
+ *   C[m,n] = sum_k (dec(A[m,k]) * 2^(SA[m,k/32]-127)) * (dec(B[k,n]) * 2^(SB[n,k/32]-127)),
+ * accumulated in fp32 and written once as fp16 (rounded to nearest even). C is overwritten
+ * (C = A*B, not C += A*B). For fa == fb == MX_F16 there are no scales: C = A*B in fp32, fp16 out.
+ *
+ * Supported pairs: (MX_E4M3, MX_E4M3), (MX_E2M1, MX_E2M1), (MX_F16, MX_F16).
+ * Shape rules: 1 <= M, N <= MX_MAX_DIM; 32 <= K <= MX_MAX_DIM; MX formats need K % 32 == 0;
+ * MX_F16 needs K % 8 == 0 and N % 8 == 0.
+ * `flags` must be 0 (reserved). Host only: queues no GPU work. *out receives a plan that holds
+ * host metadata only; release it with mxgemm_destroy. A plan may be used from several threads
+ * and streams at once.
+ */
+int mxgemm_create(mxgemm_t* out, int M, int N, int K, int fa, int fb, unsigned flags);
+
+/*
+ * mxgemm_run -- queue the GEMM of plan p on `stream`.
+ *
+ * Layouts (all device pointers, 16-byte aligned):
+ *   MX:  A  codes [M][K] (E4M3) or [M][K/2] (E2M1), K contiguous;
+ *        SA E8M0 [M][K/32];
+ *        B  codes stored K-contiguous, i.e. [N][K] (E4M3) or [N][K/2] (E2M1): the scaled right
+ *           operand is the transposed one ("Kernel-phase findings", fact 2);
+ *        SB E8M0 [N][K/32];
+ *   F16: A binary16 [M][K]; B binary16 [K][N] (row-major K x N); SA = SB = NULL.
+ *   C:   binary16 [M][N].
+ * Errors: MX_ERR_NULL (p, A, B, C, or a scale pointer of an MX plan), MX_ERR_ALIGN, MX_ERR_ARCH,
+ * MX_ERR_LAUNCH. Non-finite inputs propagate: a NaN code or a 0xFF scale makes every output it
+ * contributes to NaN.
+ */
+int mxgemm_run(mxgemm_t p, const void* A, const void* SA, const void* B, const void* SB, void* C,
+               void* stream);
+
+/* mxgemm_destroy -- release a plan (NULL is accepted and ignored). */
+int mxgemm_destroy(mxgemm_t p);
+
+/* Kernel tile chosen by a plan (for reports): block rows, block cols, K per pipeline stage. */
+int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Dequant matvec for decode.                                                                   */
+/* ------------------------------------------------------------------------------------------ */
+
+/*
+ * mxmatvec_run -- y[m,n] = sum_b Ws[b,n] * sum_{k=32b}^{32b+31} x[m,k] * q[k,n], accumulated in
+ * fp32, y written as fp16. This is the per-32-row block form with arbitrary fp16 scales
+ * ("TensorOps ... notes", section "Kernel-phase findings", revised kernel strategy; int4 packing
+ * from section "VALIDATED ON M4 MAX", fact 5).
+ *
+ *   x  binary16 [M][K]      W int8 [K][N]  (fw = MX_INT8)  or packed int4 [K][N/2] (fw = MX_INT4)
+ *   Ws binary16 [K/32][N]   y binary16 [M][N]
+ * Shape rules: 1 <= M <= 8; K % 32 == 0, 32 <= K <= MX_MAX_DIM; 1 <= N <= MX_MAX_DIM;
+ * N % 16 == 0 (int8) or N % 32 == 0 (int4). Device pointers, 16-byte aligned.
+ * Uses no scratch memory: every output is finished by one workgroup.
+ */
+int mxmatvec_run(int M, int N, int K, const void* x, const void* W, int fw, const void* Ws, void* y,
+                 void* stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Codecs on the GPU (bit-exact with the host codecs below).                                    */
+/* ------------------------------------------------------------------------------------------ */
+
+/*
+ * mx_pack_run -- quantise fp32 src [rows][cols] on the GPU.
+ *  f = MX_E4M3 / MX_E2M1: blocks of 32 along cols. Per block: amax = max|x|; E = clamp(
+ *      floor(log2 amax) - emax + 127, 0, 254) with emax = 8 (E4M3) or 2 (E2M1) (amax = 0 gives
+ *      E = 0); codes = x * 2^(127-E) rounded to the nearest element value, ties to the even
+ *      code, saturated to +-448 / +-6, sign kept (negative values that round to zero give -0).
+ *      A block holding Inf or NaN gets E = 0xFF and zero codes. codes: [rows][cols] or
+ *      [rows][cols/2]; scales: E8M0 [rows][cols/32]. cols % 32 == 0.
+ *  f = MX_INT8 / MX_INT4: src is a weight W [K=rows][N=cols], blocks of 32 along rows. Per
+ *      column and block: s = fp16(amax / qmax) (fp32 division, nearest-even to fp16) with
+ *      qmax = 127 or 7; q = clamp(round_half_even(fp32(w / s)), -qmax, qmax), q = 0 where
+ *      s = 0. codes: int8 [rows][cols] or packed int4 [rows][cols/2]; scales: binary16
+ *      [rows/32][cols]. rows % 32 == 0; cols % 2 == 0 for MX_INT4.
+ */
+int mx_pack_run(int f, const float* src, int rows, int cols, void* codes, void* scales, void* stream);
+
+/*
+ * mx_unpack_run -- dequantise to fp32 on the GPU: out = fp32(value * scale), the exact product
+ * rounded once to fp32 (nearest even; subnormals kept; overflow gives +-Inf; NaN propagates).
+ * Layouts as in mx_pack_run (MX: scales along cols; INT8/INT4: scales along rows).
+ */
+int mx_unpack_run(int f, const void* codes, const void* scales, int rows, int cols, float* out,
+                  void* stream);
+
+/* ------------------------------------------------------------------------------------------ */
+/* Host codecs (CPU, synchronous, same definitions and layouts as the GPU codecs).              */
+/* ------------------------------------------------------------------------------------------ */
+
+int mx_pack_host(int f, const float* src, int64_t rows, int64_t cols, void* codes, void* scales);
+int mx_unpack_host(int f, const void* codes, const void* scales, int64_t rows, int64_t cols, float* out);
+
+/* Single-element encoder/decoder of the host codec. mx_encode_host: f = MX_E4M3 or MX_E2M1,
+ * nearest code, ties to even, saturating, sign kept (0 for other f). mx_decode_host: f = MX_E4M3,
+ * MX_E2M1 (low nibble), MX_E8M0, MX_INT8 or MX_INT4 (low nibble); NaN for other f. */
+uint8_t mx_encode_host(int f, float v);
+float mx_decode_host(int f, uint8_t code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXGEMM_H */

@@ -1,0 +1,143 @@
+"""CPU-side checks of libmxgemm.so: it loads, exports every function include/mxgemm.h declares,
+its host codec is bit-identical to the oracle, and argument validation returns the documented
+status codes without queueing any GPU work."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_scaled_quantized_amd import synth
+from conftest import ROOT
+
+api = pytest.importorskip("block_scaled_quantized_amd.api")
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "mxgemm.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*\b(mx[a-z0-9_]+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 12, names
+    lib = ctypes.CDLL(api.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in mxgemm.h but not exported"
+    assert set(names) == set(api.EXPORTS), "binding and header disagree"
+
+
+def test_strerror_and_version():
+    assert api.mx_strerror(0) == "ok"
+    for s in range(-7, 0):
+        assert api.mx_strerror(s) and api.mx_strerror(s) != "unknown status"
+    assert api.mx_version() >= 100
+
+
+def test_host_element_codec_all_codes(orc):
+    for code in range(256):
+        a, b = api.mx_decode_host(api.MX_E4M3, code), orc.dec_e4m3([code])[0]
+        assert (np.isnan(a) and np.isnan(b)) or (a == b and np.signbit(a) == np.signbit(b))
+        e = api.mx_decode_host(api.MX_E8M0, code)
+        r = orc.dec_e8m0([code])[0]
+        assert (np.isnan(e) and np.isnan(r)) or e == r
+    for code in range(16):
+        assert api.mx_decode_host(api.MX_E2M1, code) == orc.dec_e2m1([code])[0]
+        assert api.mx_decode_host(api.MX_INT4, code) == orc.dec_int4([code])[0]
+    g = np.random.Generator(np.random.PCG64(3))
+    vals = np.concatenate([g.standard_normal(3000) * 100, g.standard_normal(3000) * 1e-3,
+                           [0.0, -0.0, 448.0, 464.0, 465.0, 1e30, -1e30, 6.0, 7.0, 5.0, 0.25]]).astype(np.float32)
+    for v in vals:
+        assert api.mx_encode_host(api.MX_E4M3, float(v)) == orc.enc_elem(0, [float(v)])[0], v
+        assert api.mx_encode_host(api.MX_E2M1, float(v)) == orc.enc_elem(4, [float(v)])[0], v
+
+
+def _edge_rows(cols, seed):
+    x = synth.normal((16, cols), 1.0, seed)
+    x[0] = 0.0
+    x[1, :32] = -0.0
+    x[2] *= np.float32(1e-40)             # subnormal fp32 sources
+    x[3] *= np.float32(3e37)              # huge blocks
+    x[4, 5] = np.inf
+    x[5, 40] = np.nan
+    x[6, :32] = np.float32(2.0) ** np.arange(-16, 16, dtype=np.float32)
+    x[7] = np.float32(448.0 * 3) * np.sign(x[7])  # saturation after scaling
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", [0, 4])
+def test_host_mx_pack_matches_oracle(orc, fmt):
+    cols = 256
+    for seed, x in [(1, synth.normal((96, cols), 1.0, 1)), (2, synth.normal((64, cols), 0.02, 2)), (3, _edge_rows(cols, 3))]:
+        rows = x.shape[0]
+        cs, ss = api.mx_shapes(fmt, rows, cols)
+        codes = np.zeros(cs, np.uint8)
+        scales = np.zeros(ss, np.uint8)
+        api.mx_pack_host(fmt, x, rows, cols, codes, scales)
+        oc, os_ = orc.mx_quantize(fmt, x)
+        assert np.array_equal(scales, os_), seed
+        assert np.array_equal(codes, oc), seed
+        out = np.zeros((rows, cols), np.float32)
+        api.mx_unpack_host(fmt, codes, scales, rows, cols, out)
+        ref = orc.dequant(fmt, oc, os_, rows, cols)
+        assert np.array_equal(np.isnan(out), np.isnan(ref))
+        fin = ~np.isnan(ref)
+        assert np.array_equal(out.view(np.uint32)[fin], ref.view(np.uint32)[fin])
+
+
+@pytest.mark.parametrize("fw", [32, 33])
+def test_host_int_pack_matches_oracle(orc, fw):
+    K, N = 128, 64
+    w = synth.normal((K, N), 0.02, 1031)
+    w[32:64, 3] = 0.0
+    w[64:96, 4] *= np.float32(1e-6)
+    cs, ss = api.int_shapes(fw, K, N)
+    codes = np.zeros(cs, np.uint8)
+    scales = np.zeros(ss, np.float16)
+    api.mx_pack_host(fw, w, K, N, codes, scales)
+    q, s = orc.int_quantize(fw, w)
+    assert np.array_equal(scales.view(np.uint16), s.view(np.uint16))
+    ref_codes = q.view(np.uint8) if fw == 32 else orc.pack_int4(q)
+    assert np.array_equal(codes, ref_codes)
+    out = np.zeros((K, N), np.float32)
+    api.mx_unpack_host(fw, codes, scales, K, N, out)
+    assert np.array_equal(out.view(np.uint32), orc.dequant(fw, ref_codes, s, K, N).view(np.uint32))
+
+
+def test_validation_errors_without_gpu():
+    lib = ctypes.CDLL(api.LIB_PATH)
+    for f in api.EXPORTS:
+        getattr(lib, f).restype = api.EXPORTS[f][0]
+        getattr(lib, f).argtypes = api.EXPORTS[f][1]
+    h = ctypes.c_void_p()
+    assert lib.mxgemm_create(None, 16, 16, 32, 0, 0, 0) == api.MX_ERR_NULL
+    assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 48, 0, 0, 0) == api.MX_ERR_SHAPE     # K % 32
+    assert lib.mxgemm_create(ctypes.byref(h), 0, 16, 32, 0, 0, 0) == api.MX_ERR_SHAPE
+    assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 4, 0) == api.MX_ERR_FORMAT     # mixed pair
+    assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 0, 1) == api.MX_ERR_FORMAT     # flags
+    assert lib.mxgemm_create(ctypes.byref(h), 16, 12, 32, 16, 16, 0) == api.MX_ERR_SHAPE    # fp16 N % 8
+    assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 0, 0) == api.MX_OK
+    tm, tn, tk = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert lib.mxgemm_plan_info(h, ctypes.byref(tm), ctypes.byref(tn), ctypes.byref(tk)) == 0
+    assert (tm.value, tn.value, tk.value) == (64, 64, 128)
+    assert lib.mxgemm_run(h, None, 16, 16, 16, 16, None) == api.MX_ERR_NULL
+    assert lib.mxgemm_run(h, 16, None, 16, 16, 16, None) == api.MX_ERR_NULL               # scales needed
+    assert lib.mxgemm_run(h, 17, 16, 16, 16, 16, None) == api.MX_ERR_ALIGN
+    assert lib.mxgemm_destroy(h) == 0
+    assert lib.mxgemm_destroy(None) == 0
+    assert lib.mxmatvec_run(9, 16, 32, 16, 16, 32, 16, 16, None) == api.MX_ERR_SHAPE       # M > 8
+    assert lib.mxmatvec_run(1, 16, 40, 16, 16, 32, 16, 16, None) == api.MX_ERR_SHAPE       # K % 32
+    assert lib.mxmatvec_run(1, 16, 32, 16, 16, 33, 16, 16, None) == api.MX_ERR_SHAPE       # int4 N % 32
+    assert lib.mxmatvec_run(1, 16, 32, 16, 16, 0, 16, 16, None) == api.MX_ERR_FORMAT
+    assert lib.mxmatvec_run(1, 16, 32, None, 16, 32, 16, 16, None) == api.MX_ERR_NULL
+    assert lib.mxmatvec_run(1, 16, 32, 16, 24, 32, 16, 16, None) == api.MX_ERR_ALIGN
+    assert lib.mx_pack_run(0, 16, 4, 48, 16, 16, None) == api.MX_ERR_SHAPE
+    assert lib.mx_pack_run(32, 16, 40, 16, 16, 16, None) == api.MX_ERR_SHAPE
+    assert lib.mx_pack_run(16, 16, 32, 32, 16, 16, None) == api.MX_ERR_FORMAT
+    assert lib.mx_unpack_run(0, 16, None, 4, 32, 16, None) == api.MX_ERR_NULL
+    assert lib.mx_unpack_run(0, 16, 16, 4, 32, 8, None) == api.MX_ERR_ALIGN
+    buf = np.zeros(64, np.float32)
+    assert lib.mx_pack_host(0, buf.ctypes.data, 1, 40, buf.ctypes.data, buf.ctypes.data) == api.MX_ERR_SHAPE
+    assert lib.mx_pack_host(16, buf.ctypes.data, 1, 32, buf.ctypes.data, buf.ctypes.data) == api.MX_ERR_FORMAT
