@@ -1,0 +1,250 @@
+"""Benchmark of the block-scaled quantized GEMM / dequant matvec path on one MI355X.
+
+Prints ONE JSON line. The headline step is one MXFP8 GEMM of the prefill shape M=2048 (tokens),
+K=4096, N=14336 (E4M3 data, E8M0 scales per 32 along K, fp32 accumulation, fp16 C): `value` is
+its throughput in TFLOP/s (2*M*N*K per step over the HIP-event time of the timed steps, inputs
+already resident in HBM). The other workloads of the path are measured in the same run and
+reported under "detail": the MXFP4 GEMM (M=4096, N=8192, K=8192), the fp16 GEMM (4096^3), the
+small MXFP8 GEMM (128x256x128, a latency figure), the int8/int4 dequant matvec (M=1 and M=8,
+K=4096, N=14336; GB/s of algorithmic bytes) and the GPU pack/unpack codecs.
+
+Timing: W warm-up steps, then K steps between two HIP events recorded on the stream the kernels
+are launched on, bracketed by device synchronisation. Inputs rotate over several copies so that
+repeats are not served by the 256 MB Infinity Cache (3 sets for GEMMs, >= 384 MB of weights for
+the matvec). The CPU baseline is the oracle timed on the host on a bounded row sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {  # MI355X dense peaks (256 CUs x 2.4 GHz x flop/clk/CU) and HBM bandwidth
+    "mxfp8": 5033.2, "mxfp4": 10066.3, "fp16": 2516.6, "hbm_gbs": 8000.0,
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", default="", help="comma list of detail workloads to run (default all)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from block_scaled_quantized_amd import api, synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+
+    def d(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def timed(fn, steps, warmup):
+        """Mean ms per call of fn(i) over `steps` calls, HIP events on the launch stream."""
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def mx_operands(fmt, M, N, K, wl, sigma_b, copies):
+        a_src = synth.normal((M, K), 1.0, synth.seed_for(wl, 0))
+        b_src = synth.normal((N, K), sigma_b, synth.seed_for(wl, 1))
+        cs, ss = api.mx_shapes(fmt, M, K)
+        A = torch.empty(cs, dtype=torch.uint8, device=dev)
+        SA = torch.empty(ss, dtype=torch.uint8, device=dev)
+        api.mx_pack_run(fmt, d(a_src), M, K, A, SA)
+        cs, ss = api.mx_shapes(fmt, N, K)
+        B = torch.empty(cs, dtype=torch.uint8, device=dev)
+        SB = torch.empty(ss, dtype=torch.uint8, device=dev)
+        api.mx_pack_run(fmt, d(b_src), N, K, B, SB)
+        sets = [(A, SA, B, SB)] + [(A.clone(), SA.clone(), B.clone(), SB.clone()) for _ in range(copies - 1)]
+        torch.cuda.synchronize()
+        return sets, a_src, b_src
+
+    # ---------------- headline: MXFP8 prefill GEMM ----------------------------------------
+    M, N, K = 2048, 14336, 4096
+    sets, a_src, b_src = mx_operands(api.MX_E4M3, M, N, K, synth.MXFP8_PREFILL, 0.02, 3)
+    plan = api.mxgemm_create(M, N, K, api.MX_E4M3, api.MX_E4M3)
+    tile = api.mxgemm_plan_info(plan)
+    Cs = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(3)]
+
+    def step(i):
+        A, SA, B, SB = sets[i % 3]
+        api.mxgemm_run(plan, A, SA, B, SB, Cs[i % 3], stream)
+
+    log("timing mxfp8 prefill GEMM")
+    ms = timed(step, args.steps, args.warmup)
+    flops = 2.0 * M * N * K
+    tflops = flops / (ms * 1e-3) / 1e12
+    C0 = Cs[0]
+
+    detail = {}
+    only = set(filter(None, args.only.split(",")))
+
+    def want(name):
+        return not only or name in only
+
+    # ---------------- MXFP4 GEMM -------------------------------------------------------------
+    if want("mxfp4_large"):
+        log("timing mxfp4 GEMM")
+        M4, N4, K4 = 4096, 8192, 8192
+        s4, _, _ = mx_operands(api.MX_E2M1, M4, N4, K4, synth.MXFP4_LARGE, 1.0, 3)
+        p4 = api.mxgemm_create(M4, N4, K4, api.MX_E2M1, api.MX_E2M1)
+        C4 = [torch.empty((M4, N4), dtype=torch.float16, device=dev) for _ in range(3)]
+        t = timed(lambda i: api.mxgemm_run(p4, *s4[i % 3], C4[i % 3], stream), args.steps, args.warmup)
+        tf = 2.0 * M4 * N4 * K4 / (t * 1e-3) / 1e12
+        detail["mxfp4_gemm_4096x8192x8192"] = {"ms": t, "tflops": tf, "frac_peak": tf / PEAK["mxfp4"],
+                                               "tile": api.mxgemm_plan_info(p4)}
+        del s4, C4
+
+    # ---------------- fp16 GEMM ----------------------------------------------------------------
+    if want("f16_square"):
+        log("timing fp16 GEMM")
+        Mf = Nf = Kf = 4096
+        Af = d(synth.uniform_pm1((Mf, Kf), synth.seed_for(synth.F16_SQUARE, 0)).astype(np.float16))
+        Bf = d(synth.uniform_pm1((Kf, Nf), synth.seed_for(synth.F16_SQUARE, 1)).astype(np.float16))
+        fsets = [(Af, Bf)] + [(Af.clone(), Bf.clone()) for _ in range(2)]
+        pf = api.mxgemm_create(Mf, Nf, Kf, api.MX_F16, api.MX_F16)
+        Cf = [torch.empty((Mf, Nf), dtype=torch.float16, device=dev) for _ in range(3)]
+        t = timed(lambda i: api.mxgemm_run(pf, fsets[i % 3][0], None, fsets[i % 3][1], None, Cf[i % 3], stream),
+                  args.steps, args.warmup)
+        tf = 2.0 * Mf * Nf * Kf / (t * 1e-3) / 1e12
+        detail["fp16_gemm_4096x4096x4096"] = {"ms": t, "tflops": tf, "frac_peak": tf / PEAK["fp16"],
+                                              "tile": api.mxgemm_plan_info(pf)}
+        del fsets, Cf
+
+    # ---------------- small MXFP8 GEMM (latency) -----------------------------------------------
+    if want("mxfp8_small"):
+        log("timing small mxfp8 GEMM")
+        Ms, Ns, Ks = 128, 256, 128
+        ss_, _, _ = mx_operands(api.MX_E4M3, Ms, Ns, Ks, synth.MXFP8_SMALL, 1.0, 1)
+        ps = api.mxgemm_create(Ms, Ns, Ks, api.MX_E4M3, api.MX_E4M3)
+        Csm = torch.empty((Ms, Ns), dtype=torch.float16, device=dev)
+        t = timed(lambda i: api.mxgemm_run(ps, *ss_[0], Csm, stream), args.steps, args.warmup)
+        detail["mxfp8_gemm_128x256x128"] = {"us": t * 1e3, "tflops": 2.0 * Ms * Ns * Ks / (t * 1e-3) / 1e12,
+                                            "tile": api.mxgemm_plan_info(ps)}
+
+    # ---------------- dequant matvec ---------------------------------------------------------------
+    if want("matvec"):
+        log("timing matvec")
+        Km, Nm = 4096, 14336
+        w = synth.normal((Km, Nm), 0.02, synth.seed_for(synth.MATVEC, 1))
+        x8 = synth.normal((8, Km), 1.0, synth.seed_for(synth.MATVEC, 0)).astype(np.float16)
+        wd = d(w)
+        xd = d(x8)
+        for fw, name, copies in ((api.MX_INT8, "int8", 7), (api.MX_INT4, "int4", 12)):
+            cs, ss = api.int_shapes(fw, Km, Nm)
+            W = torch.empty(cs, dtype=torch.uint8, device=dev)
+            Ws = torch.empty(ss, dtype=torch.float16, device=dev)
+            api.mx_pack_run(fw, wd, Km, Nm, W, Ws)
+            wsets = [(W, Ws)] + [(W.clone(), Ws.clone()) for _ in range(copies - 1)]
+            for Mv in (1, 8):
+                y = torch.empty((Mv, Nm), dtype=torch.float16, device=dev)
+                xv = xd[:Mv].contiguous()
+                t = timed(lambda i: api.mxmatvec_run(Mv, Nm, Km, xv, wsets[i % copies][0], fw, wsets[i % copies][1],
+                                                     y, stream), args.steps, args.warmup)
+                nbytes = W.numel() + Ws.numel() * 2 + Mv * Km * 2 + Mv * Nm * 2
+                gbs = nbytes / (t * 1e-3) / 1e9
+                detail[f"matvec_{name}_M{Mv}"] = {"us": t * 1e3, "gbs": gbs, "frac_hbm": gbs / PEAK["hbm_gbs"],
+                                                  "bytes": nbytes, "weight_copies": copies}
+            del wsets
+        del wd
+
+    # ---------------- codecs -------------------------------------------------------------------------
+    if want("codec"):
+        log("timing codecs")
+        rows, cols = 2048, 4096
+        src = d(a_src)
+        A8 = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        S8 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+        t = timed(lambda i: api.mx_pack_run(api.MX_E4M3, src, rows, cols, A8, S8, stream), args.steps, args.warmup)
+        nbytes = rows * cols * 4 + rows * cols + rows * cols // 32
+        detail["pack_e4m3_2048x4096"] = {"us": t * 1e3, "gbs": nbytes / (t * 1e-3) / 1e9}
+        out = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+        t = timed(lambda i: api.mx_unpack_run(api.MX_E4M3, A8, S8, rows, cols, out, stream), args.steps, args.warmup)
+        detail["unpack_e4m3_2048x4096"] = {"us": t * 1e3, "gbs": nbytes / (t * 1e-3) / 1e9}
+
+    # ---------------- CPU baseline: the oracle on a bounded sample ------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        import oracle as orc
+        torch.cuda.synchronize()
+        oB, oSB = orc.mx_quantize(orc.E4M3, b_src)
+        oA, oSA = orc.mx_quantize(orc.E4M3, a_src[:64])
+        threads = orc.num_threads()
+        rows_done, t_cpu, R = 0, 0.0, None
+        chunk = max(1, threads)
+        gpu_rows = C0[:64].cpu().numpy().astype(np.float64)
+        worst = 0.0
+        while rows_done < 64 and t_cpu < 12.0:
+            n = min(chunk, 64 - rows_done)
+            t0 = time.perf_counter()
+            ref = orc.mxgemm(orc.E4M3, orc.E4M3, oA, oSA, oB, oSB, 64, N, K, row0=rows_done, nrows=n)
+            t_cpu += time.perf_counter() - t0
+            if R is None:
+                R = orc.rms_ab(orc.dequant(orc.E4M3, oA, oSA, 64, K), orc.dequant(orc.E4M3, oB, oSB, N, K).T)
+            ok, ratio, _ = orc.check(gpu_rows[rows_done:rows_done + n], ref, K, R)
+            worst = max(worst, ratio)
+            rows_done += n
+        cpu_tflops = 2.0 * rows_done * N * K / t_cpu / 1e12
+        cpu = {"value": cpu_tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+               "sample": f"rows 0..{rows_done - 1} of C for the MXFP8 GEMM M=2048,N=14336,K=4096 "
+                         f"({rows_done}x{N}x{K} MACs in {t_cpu:.1f} s, fp64, closed-form decode per element)",
+               "seconds": t_cpu, "gpu_rows_worst_err_over_bound": worst}
+
+    out = {
+        "metric": "block-scaled GEMM TFLOPS & % MFMA peak (MXFP8/MXFP4); int8 matvec GB/s",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8 (e4m3 x e8m0/32, fp32 accumulate, fp16 out)",
+        "data": "synthetic: seeded PCG64, activations N(0,1), weights 0.02*N(0,1), quantised on the GPU",
+        "config": {"workload": "mxfp8_gemm_prefill M=2048 N=14336 K=4096", "M": M, "N": N, "K": K,
+                   "tile_m_n_k": list(tile), "input_sets_rotated": 3},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK["mxfp8"], "unit": "TFLOP/s",
+                     "frac": tflops / PEAK["mxfp8"], "traffic": None,
+                     "kernel": f"gemm_kernel<E4M3, {tile[0]}x{tile[1]}>", "flops_per_launch": flops},
+        "cpu_baseline": cpu,
+        "detail": detail,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -11,6 +11,6 @@ __all__ = ["synth", "api"]
 
 def __getattr__(name):
     if name == "api":
-        from . import api
-        return api
+        import importlib
+        return importlib.import_module(__name__ + ".api")
     raise AttributeError(name)

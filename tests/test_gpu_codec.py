@@ -1,0 +1,93 @@
+"""GPU pack (quantise) and unpack (dequantise) against the oracle: bit-exact on every output."""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_quantized_amd import synth
+from gpu_common import bitequal_f32, dev, empty, gpu_int_pack, gpu_mx_pack, host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def edge_rows(cols, seed):
+    x = synth.normal((24, cols), 1.0, seed)
+    x[0] = 0.0
+    x[1, :32] = -0.0
+    x[2] *= np.float32(1e-40)                      # subnormal fp32 sources
+    x[3] *= np.float32(3e37)                       # blocks near the fp32 top
+    x[4, 5] = np.inf
+    x[5, 40] = np.nan
+    x[6, :32] = np.float32(2.0) ** np.arange(-16, 16, dtype=np.float32)
+    x[7] = np.float32(1344.0) * np.sign(x[7])      # saturating elements
+    x[8, :32] = np.float32(2.0) ** np.float32(-130)  # amax below 2^-127: scale clamps to 0
+    x[9, 32:64] = -np.inf
+    # exact ties of the element grids after scaling (block amax 448 -> scale 2^0 for E4M3)
+    grid = torch.arange(0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    mids = (grid[:-1] + grid[1:]) / 2
+    x[10, :32] = np.float32(448.0)
+    x[10, 1:32] = mids[np.linspace(0, len(mids) - 1, 31).astype(int)]
+    x[12, :32] = -x[10, :32]
+    x[11, :32] = np.float32(4.0)                   # E2M1 block amax 4 -> scale 2^0
+    x[11, 1:16] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25, -1.75, -2.5,
+                            -3.5, -5.0, 0.1], np.float32)
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt", [0, 4])
+@pytest.mark.parametrize("case", ["normal1", "normal002", "edges", "prefill_rows"])
+def test_mx_pack_unpack_bitexact(orc, fmt, case):
+    api = require_gpu()
+    say(f"mx pack fmt={fmt} case={case}")
+    if case == "normal1":
+        x = synth.normal((384, 512), 1.0, 1000)
+    elif case == "normal002":
+        x = synth.normal((256, 1024), 0.02, 1021)
+    elif case == "edges":
+        x = edge_rows(256, 7)
+    else:
+        x = synth.normal((64, 4096), 1.0, 1020)
+    rows, cols = x.shape
+    codes, scales = gpu_mx_pack(api, fmt, x)
+    oc, os_ = orc.mx_quantize(fmt, x)
+    assert np.array_equal(host(scales), os_)
+    assert np.array_equal(host(codes), oc)
+    out = empty((rows, cols), torch.float32)
+    api.mx_unpack_run(fmt, codes, scales, rows, cols, out)
+    assert bitequal_f32(host(out), orc.dequant(fmt, oc, os_, rows, cols))
+
+
+@pytest.mark.parametrize("fmt", [0, 4])
+def test_mx_unpack_every_code_and_scale(orc, fmt):
+    api = require_gpu()
+    say(f"mx unpack exhaustive fmt={fmt}")
+    # every code byte against every scale byte: 256 rows (one per scale) x 256 or 512 columns
+    cols = 256 if fmt == 0 else 512
+    per_row = np.arange(256, dtype=np.uint8)
+    codes = np.tile(per_row, (256, 1)) if fmt == 0 else np.tile(np.repeat(per_row, 1), (256, 1))
+    codes = np.ascontiguousarray(codes[:, : (cols if fmt == 0 else cols // 2)])
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], cols // 32, axis=1)
+    out = empty((256, cols), torch.float32)
+    api.mx_unpack_run(fmt, dev(codes), dev(scales), 256, cols, out)
+    assert bitequal_f32(host(out), orc.dequant(fmt, codes, scales, 256, cols))
+
+
+@pytest.mark.parametrize("fw", [32, 33])
+@pytest.mark.parametrize("shape", [(4096, 14336), (96, 48), (64, 34)])
+def test_int_pack_unpack_bitexact(orc, fw, shape):
+    api = require_gpu()
+    K, N = shape
+    if fw == 33 and N % 2:
+        pytest.skip("int4 needs an even column count")
+    say(f"int pack fw={fw} K={K} N={N}")
+    w = synth.normal((K, N), 0.02, 1031)
+    if K <= 96:
+        w[32:64, 3] = 0.0
+        w[0:32, 5] *= np.float32(1e-30)
+    codes, scales = gpu_int_pack(api, fw, w)
+    q, s = orc.int_quantize(fw, w)
+    ref_codes = q.view(np.uint8) if fw == 32 else orc.pack_int4(q)
+    assert np.array_equal(host(scales).view(np.uint16), s.view(np.uint16))
+    assert np.array_equal(host(codes), ref_codes)
+    out = empty((K, N), torch.float32)
+    api.mx_unpack_run(fw, codes, scales, K, N, out)
+    assert bitequal_f32(host(out), orc.dequant(fw, ref_codes, s, K, N))

@@ -1,0 +1,220 @@
+"""GPU GEMMs (MXFP8, MXFP4, fp16) against the oracle.
+
+Inputs are seeded fp32 sources; the GPU quantises them with mx_pack_run, the oracle with its own
+quantiser, and the two code/scale planes must agree bit for bit before the products are compared.
+Products must meet |C_gpu - C_ref| <= 2^-10 |C_ref| + 1e-3 sqrt(K) R (R = rms of |a_mk b_kn|), with
+NaN positions equal. Small and ragged shapes are compared on every output; the full-size
+workloads on sampled outputs (all four corners included) plus a finiteness check of all of C.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_quantized_amd import synth
+from gpu_common import dev, empty, gpu_gemm, gpu_mx_pack, host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def R_of(orc, fmt, A, SA, B, SB, M, N, K):
+    return orc.rms_ab(orc.dequant(fmt, A, SA, M, K), orc.dequant(fmt, B, SB, N, K).T)
+
+
+def mx_case(orc, api, fmt, M, N, K, seed, sigma_b=1.0, tile=None):
+    a_src = synth.normal((M, K), 1.0, seed)
+    b_src = synth.normal((N, K), sigma_b, seed + 1)   # B drawn in its K-contiguous storage order
+    A, SA = gpu_mx_pack(api, fmt, a_src)
+    B, SB = gpu_mx_pack(api, fmt, b_src)
+    oA, oSA = orc.mx_quantize(fmt, a_src)
+    oB, oSB = orc.mx_quantize(fmt, b_src)
+    assert np.array_equal(host(A), oA) and np.array_equal(host(SA), oSA)
+    assert np.array_equal(host(B), oB) and np.array_equal(host(SB), oSB)
+    old = os.environ.get("MXGEMM_TILE")
+    if tile is not None:
+        os.environ["MXGEMM_TILE"] = str(tile)
+    try:
+        C = gpu_gemm(api, fmt, A, SA, B, SB, M, N, K)
+    finally:
+        if tile is not None:
+            if old is None:
+                del os.environ["MXGEMM_TILE"]
+            else:
+                os.environ["MXGEMM_TILE"] = old
+    return C, (oA, oSA, oB, oSB)
+
+
+@pytest.mark.parametrize("fmt", [0, 4])
+def test_mx_small_config_full(orc, fmt):
+    """MXFP8 M=128, N=256, K=128 (and the same shape in MXFP4): every output."""
+    api = require_gpu()
+    M, N, K = 128, 256, 128
+    say(f"mx small fmt={fmt}")
+    C, (oA, oSA, oB, oSB) = mx_case(orc, api, fmt, M, N, K, synth.seed_for(synth.MXFP8_SMALL, 0))
+    ref = orc.mxgemm(fmt, fmt, oA, oSA, oB, oSB, M, N, K)
+    ok, ratio, bad = orc.check(C, ref, K, R_of(orc, fmt, oA, oSA, oB, oSB, M, N, K))
+    assert ok, (ratio, bad)
+
+
+@pytest.mark.parametrize("fmt", [0, 4])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+def test_mx_every_tile_ragged(orc, fmt, tile):
+    """Each tile configuration on a shape spanning several tiles with ragged M, N and K tails."""
+    api = require_gpu()
+    M, N, K = 300, 520, 416          # K = 13 blocks: partial last stage for both formats
+    say(f"mx ragged fmt={fmt} tile={tile}")
+    C, (oA, oSA, oB, oSB) = mx_case(orc, api, fmt, M, N, K, 4242 + tile, tile=tile)
+    ref = orc.mxgemm(fmt, fmt, oA, oSA, oB, oSB, M, N, K)
+    ok, ratio, bad = orc.check(C, ref, K, R_of(orc, fmt, oA, oSA, oB, oSB, M, N, K))
+    assert ok, (ratio, bad)
+
+
+@pytest.mark.parametrize("fmt", [0, 4])
+@pytest.mark.parametrize("shape", [(1, 1, 32), (1, 8, 64), (17, 3, 96), (5, 129, 4096), (64, 64, 288)])
+def test_mx_degenerate_shapes(orc, fmt, shape):
+    api = require_gpu()
+    M, N, K = shape
+    say(f"mx degenerate fmt={fmt} shape={shape}")
+    C, (oA, oSA, oB, oSB) = mx_case(orc, api, fmt, M, N, K, 77 + M + N + K)
+    ref = orc.mxgemm(fmt, fmt, oA, oSA, oB, oSB, M, N, K)
+    ok, ratio, bad = orc.check(C, ref, K, R_of(orc, fmt, oA, oSA, oB, oSB, M, N, K))
+    assert ok, (ratio, bad)
+
+
+def small_codes(fmt, shape, seed):
+    """Random codes of magnitude <= 4 (E4M3: exponent field <= 8, every subnormal) or any E2M1
+    byte, so that sums of a few hundred products stay inside the fp16 range."""
+    if fmt == 4:
+        return synth.random_bytes(shape, seed)
+    b = synth.random_bytes(shape, seed)                  # sign and mantissa bits
+    e = synth.random_ints(shape, 0, 8, seed + 1000)      # exponent field 0..8: |value| < 2
+    return ((b & 0x87) | (e << 3)).astype(np.uint8)
+
+
+def test_mx_fp16_overflow_is_inf(orc):
+    """Sums beyond 65504 are written as +-Inf (fp16 nearest-even overflow) with the right sign."""
+    api = require_gpu()
+    M, N, K = 32, 32, 256
+    say("mx fp16 overflow")
+    A = synth.random_bytes((M, K), 25, exclude=(0x7F, 0xFF))
+    B = np.full((N, K), 0x7E, np.uint8)                   # 448 everywhere
+    A[:, :] = 0x7E
+    A[1::2, :] = 0xFE                                      # odd rows -448
+    SA = np.full((M, K // 32), 127, np.uint8)
+    SB = np.full((N, K // 32), 127, np.uint8)
+    C = gpu_gemm(api, 0, dev(A), dev(SA), dev(B), dev(SB), M, N, K)
+    assert np.all(C[0::2] == np.inf) and np.all(C[1::2] == -np.inf)
+    ref = orc.mxgemm(0, 0, A, SA, B, SB, M, N, K)
+    ok, ratio, bad = orc.check(C, ref, K, R_of(orc, 0, A, SA, B, SB, M, N, K))
+    assert ok, (ratio, bad)
+
+
+@pytest.mark.parametrize("fmt", [0, 4])
+def test_mx_nonfinite_and_extreme_scales(orc, fmt):
+    """NaN scale (0xFF), NaN E4M3 codes, the smallest and largest scales."""
+    api = require_gpu()
+    M, N, K = 64, 96, 256
+    say(f"mx nonfinite fmt={fmt}")
+    rb = K if fmt == 0 else K // 2
+    A = small_codes(fmt, (M, rb), 5)
+    B = small_codes(fmt, (N, rb), 6)
+    SA = synth.random_ints((M, K // 32), 118, 128, 7)
+    SB = synth.random_ints((N, K // 32), 118, 128, 8)
+    SA[3, 2] = 0xFF                      # NaN scale: row 3
+    SB[10, 5] = 0xFF                     # NaN scale: column 10
+    SA[5, 1:] = 0                        # 2^-127 in row 5 (tiny but finite products)
+    SA[:, 0] = 1                         # block 0: 2^-126 on every row of A ...
+    SB[20, 0] = 254                      # ... so the largest scale 2^127 on column 20 stays in range
+    if fmt == 0:
+        A[7, 33] = 0x7F                  # NaN code: row 7
+        B[30, 200] = 0xFF                # NaN code: column 30
+    C = gpu_gemm(api, fmt, dev(A), dev(SA), dev(B), dev(SB), M, N, K)
+    ref = orc.mxgemm(fmt, fmt, A, SA, B, SB, M, N, K)
+    fin = ~np.isnan(ref)
+    R = orc.rms_ab(np.nan_to_num(orc.dequant(fmt, A, SA, M, K)), np.nan_to_num(orc.dequant(fmt, B, SB, N, K)).T)
+    assert np.array_equal(np.isnan(C), ~fin)
+    ok, ratio, bad = orc.check(C[fin], ref[fin], K, R)
+    assert ok, (ratio, bad)
+
+
+def test_mx_unit_scales_fp8_exact_products(orc):
+    """Scale 127 everywhere: the oracle equals a plain fp8 matmul; the GPU must match within the bound."""
+    api = require_gpu()
+    M, N, K = 256, 256, 512
+    say("mx unit scales")
+    A = small_codes(0, (M, K), 15)
+    B = small_codes(0, (N, K), 16)
+    SA = np.full((M, K // 32), 127, np.uint8)
+    SB = np.full((N, K // 32), 127, np.uint8)
+    C = gpu_gemm(api, 0, dev(A), dev(SA), dev(B), dev(SB), M, N, K)
+    ref = orc.mxgemm(0, 0, A, SA, B, SB, M, N, K)
+    ok, ratio, bad = orc.check(C, ref, K, R_of(orc, 0, A, SA, B, SB, M, N, K))
+    assert ok, (ratio, bad)
+
+
+@pytest.mark.parametrize("name,fmt,M,N,K,sigma_b,wl", [
+    ("mxfp8_prefill", 0, 2048, 14336, 4096, 0.02, synth.MXFP8_PREFILL),
+    ("mxfp4_large", 4, 4096, 8192, 8192, 1.0, synth.MXFP4_LARGE),
+])
+def test_mx_full_size_sampled(orc, name, fmt, M, N, K, sigma_b, wl):
+    api = require_gpu()
+    say(f"full size {name}")
+    a_src = synth.normal((M, K), 1.0, synth.seed_for(wl, 0))
+    b_src = synth.normal((N, K), sigma_b, synth.seed_for(wl, 1))
+    A, SA = gpu_mx_pack(api, fmt, a_src)
+    B, SB = gpu_mx_pack(api, fmt, b_src)
+    C = gpu_gemm(api, fmt, A, SA, B, SB, M, N, K)
+    assert np.isfinite(C).all()
+    oA, oSA = orc.mx_quantize(fmt, a_src)
+    oB, oSB = orc.mx_quantize(fmt, b_src)
+    del a_src, b_src
+    assert np.array_equal(host(SA), oSA) and np.array_equal(host(SB), oSB)
+    assert np.array_equal(host(A), oA) and np.array_equal(host(B), oB)
+    ms, ns = synth.sample_points(M, N, 2048, 99)
+    ref = orc.mxgemm_points(fmt, fmt, oA, oSA, oB, oSB, K, ms, ns)
+    ok, ratio, bad = orc.check(C[ms, ns], ref, K, R_of(orc, fmt, oA, oSA, oB, oSB, M, N, K))
+    say(f"{name}: worst err/bound {ratio:.3f}")
+    assert ok, (ratio, bad)
+
+
+def fp16_case(orc, api, M, N, K, seed, tile=None):
+    A = synth.uniform_pm1((M, K), seed).astype(np.float16)
+    B = synth.uniform_pm1((K, N), seed + 1).astype(np.float16)
+    old = os.environ.get("MXGEMM_TILE")
+    if tile is not None:
+        os.environ["MXGEMM_TILE"] = str(tile)
+    try:
+        C = gpu_gemm(api, api.MX_F16, dev(A), None, dev(B), None, M, N, K)
+    finally:
+        if tile is not None:
+            if old is None:
+                del os.environ["MXGEMM_TILE"]
+            else:
+                os.environ["MXGEMM_TILE"] = old
+    return A, B, C
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+def test_f16_every_tile_ragged(orc, tile):
+    api = require_gpu()
+    M, N, K = 300, 520, 200
+    say(f"f16 ragged tile={tile}")
+    A, B, C = fp16_case(orc, api, M, N, K, 500 + tile, tile=tile)
+    ref = orc.gemm_f16(A, B)
+    ok, ratio, bad = orc.check(C, ref, K, orc.rms_ab(A.astype(np.float64), B.astype(np.float64)))
+    assert ok, (ratio, bad)
+
+
+def test_f16_square_full_size_sampled(orc):
+    """fp16 GEMM M=N=K=4096, U(-1,1) inputs."""
+    api = require_gpu()
+    M = N = K = 4096
+    say("f16 square 4096")
+    A, B, C = fp16_case(orc, api, M, N, K, synth.seed_for(synth.F16_SQUARE, 0))
+    assert np.isfinite(C).all()
+    ms, ns = synth.sample_points(M, N, 2048, 98)
+    ref = orc.gemm_f16_points(A, B, ms, ns)
+    ok, ratio, bad = orc.check(C[ms, ns], ref, K, orc.rms_ab(A.astype(np.float64), B.astype(np.float64)))
+    say(f"f16 square: worst err/bound {ratio:.3f}")
+    assert ok, (ratio, bad)

@@ -1,0 +1,75 @@
+"""GPU int8/int4 dequant matvec against the oracle.
+
+Weights W [K][N] are drawn 0.02*N(0,1) and quantised by the GPU codec (checked bit-exact against
+the oracle's quantiser first); x is fp16 from N(0,1). Every output is compared with the oracle's
+fp64 block formula under |y - y_ref| <= 2^-10 |y_ref| + 1e-3 sqrt(K) R, R the rms of |x_mk w_kn|
+over the dequantised weights.
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_scaled_quantized_amd import synth
+from gpu_common import dev, empty, gpu_int_pack, host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(orc, api, fw, M, K, N, seed_w, seed_x):
+    w = synth.normal((K, N), 0.02, seed_w)
+    x = synth.normal((8, K), 1.0, seed_x).astype(np.float16)[:M]
+    W, Ws = gpu_int_pack(api, fw, w)
+    q, s = orc.int_quantize(fw, w)
+    oW = q.view(np.uint8) if fw == api.MX_INT8 else orc.pack_int4(q)
+    assert np.array_equal(host(W), oW) and np.array_equal(host(Ws).view(np.uint16), s.view(np.uint16))
+    y = empty((M, N), torch.float16)
+    api.mxmatvec_run(M, N, K, dev(x), W, fw, Ws, y)
+    got = host(y).astype(np.float64)
+    ref = orc.matvec(fw, x, oW, s, K, N)
+    wdeq = orc.dequant(fw, oW, s, K, N)
+    R = orc.rms_ab(x.astype(np.float64), wdeq)
+    ok, ratio, bad = orc.check(got, ref, K, R)
+    return ok, ratio, bad
+
+
+@pytest.mark.parametrize("fw", [32, 33])
+@pytest.mark.parametrize("M", [1, 8])
+def test_matvec_decode_shape_full(orc, fw, M):
+    """K=4096, N=14336 at M=1 and M=8: every output."""
+    api = require_gpu()
+    say(f"matvec fw={fw} M={M} full size")
+    ok, ratio, bad = run_case(orc, api, fw, M, 4096, 14336, synth.seed_for(synth.MATVEC, 1),
+                              synth.seed_for(synth.MATVEC, 0))
+    say(f"worst err/bound {ratio:.3f}")
+    assert ok, (ratio, bad)
+
+
+@pytest.mark.parametrize("fw", [32, 33])
+@pytest.mark.parametrize("M,K,N", [(1, 32, 32), (2, 64, 96), (3, 96, 160), (5, 4096, 64), (7, 1024, 1056),
+                                   (8, 160, 4128), (4, 8192, 512), (6, 544, 14336)])
+def test_matvec_ragged(orc, fw, M, K, N):
+    api = require_gpu()
+    say(f"matvec fw={fw} M={M} K={K} N={N}")
+    ok, ratio, bad = run_case(orc, api, fw, M, K, N, 7 * K + N, 3 * M + K)
+    assert ok, (ratio, bad)
+
+
+def test_matvec_zero_block_and_repeat(orc):
+    """An all-zero weight block (scale 0) and two calls in a row on the same output buffer."""
+    api = require_gpu()
+    say("matvec zero block + repeat")
+    M, K, N = 4, 128, 64
+    w = synth.normal((K, N), 0.02, 3)
+    w[32:64, :] = 0.0
+    x = synth.normal((M, K), 1.0, 4).astype(np.float16)
+    W, Ws = gpu_int_pack(api, api.MX_INT8, w)
+    y = empty((M, N), torch.float16)
+    api.mxmatvec_run(M, N, K, dev(x), W, api.MX_INT8, Ws, y)
+    first = host(y).copy()
+    api.mxmatvec_run(M, N, K, dev(x), W, api.MX_INT8, Ws, y)
+    assert np.array_equal(first.view(np.uint16), host(y).view(np.uint16))     # deterministic
+    q, s = orc.int_quantize(api.MX_INT8, w)
+    ref = orc.matvec(api.MX_INT8, x, q.view(np.uint8), s, K, N)
+    ok, ratio, bad = orc.check(first.astype(np.float64), ref, K,
+                               orc.rms_ab(x.astype(np.float64), orc.dequant(32, q.view(np.uint8), s, K, N)))
+    assert ok, (ratio, bad)
