@@ -108,7 +108,7 @@ def main():
     C0 = Cs[0]
 
     detail = {}
-    only = set(filter(None, args.only.split(",")))
+    only = set(filter(None, args.only.split(",")))  # "none" skips every detail workload
 
     def want(name):
         return not only or name in only
@@ -239,7 +239,8 @@ def main():
                    "tile_m_n_k": list(tile), "input_sets_rotated": 3},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK["mxfp8"], "unit": "TFLOP/s",
                      "frac": tflops / PEAK["mxfp8"], "traffic": None,
-                     "kernel": f"gemm_kernel<E4M3, {tile[0]}x{tile[1]}>", "flops_per_launch": flops},
+                     "kernel": f"{'gemm_pp_kernel' if tile[3] == 2 else 'gemm_kernel'}<E4M3, {tile[0]}x{tile[1]}>",
+                     "flops_per_launch": flops},
         "cpu_baseline": cpu,
         "detail": detail,
     }

@@ -29,7 +29,7 @@ EXPORTS = {
     "mxgemm_create": (_i, [ctypes.POINTER(_vp), _i, _i, _i, _i, _i, _u]),
     "mxgemm_run": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mxgemm_destroy": (_i, [_vp]),
-    "mxgemm_plan_info": (_i, [_vp, ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i)]),
+    "mxgemm_plan_info": (_i, [_vp, ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "mxmatvec_run": (_i, [_i, _i, _i, _vp, _vp, _i, _vp, _vp, _vp]),
     "mx_pack_run": (_i, [_i, _vp, _i, _i, _vp, _vp, _vp]),
     "mx_unpack_run": (_i, [_i, _vp, _vp, _i, _i, _vp, _vp]),
@@ -108,9 +108,11 @@ def mxgemm_create(M: int, N: int, K: int, fa: int, fb: int, flags: int = 0) -> P
 
 
 def mxgemm_plan_info(plan: Plan):
-    a, b, c = _i(), _i(), _i()
-    _check(_lib.mxgemm_plan_info(plan.handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)), "mxgemm_plan_info")
-    return a.value, b.value, c.value
+    """(tile_m, tile_n, tile_k, variant) of the kernel chosen by the plan."""
+    a, b, c, v = _i(), _i(), _i(), _i()
+    _check(_lib.mxgemm_plan_info(plan.handle, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c), ctypes.byref(v)),
+           "mxgemm_plan_info")
+    return a.value, b.value, c.value, v.value
 
 
 def mxgemm_run(plan: Plan, A, SA, B, SB, C, stream=None) -> None:

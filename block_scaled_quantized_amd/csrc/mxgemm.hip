@@ -7,9 +7,9 @@
 // by the CDNA4 scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4): no dequantised copy of any
 // operand exists anywhere.
 //
-// Structure of one workgroup (256 threads = 4 waves in a 2x2 arrangement):
-//  - Output tile BM x BN; each wave owns (BM/2) x (BN/2) as 16x16 MFMA fragments whose fp32
-//    accumulators stay in registers for the whole K loop.
+// Structure of one workgroup (WAVES_M x WAVES_N waves of 64 lanes; 4 or 8 waves):
+//  - Output tile BM x BN; each wave owns (BM/WAVES_M) x (BN/WAVES_N) as 16x16 MFMA fragments
+//    whose fp32 accumulators stay in registers for the whole K loop.
 //  - K advances in stages of 128 bytes per operand row (128 E4M3 / 256 E2M1 / 64 fp16 elements).
 //    Two LDS buffers alternate. The copy of stage s+1 is issued with direct global->LDS loads
 //    (global_load_lds_dwordx4 / _dword: no staging registers, no LDS write instructions) before
@@ -17,9 +17,11 @@
 //    Only a K-tail stage (K not a multiple of the stage), an unaligned scale plane, or the fp16
 //    right operand (which needs a transpose) take a register path instead.
 //  - LDS rows are 128 bytes = 8 chunks of 16 bytes; chunk c of row r is stored at chunk
-//    c ^ ((r ^ (r >> 3)) & 7), so the 16 rows read by one fragment load hit distinct banks. A
-//    direct load writes 64 lanes x 16 bytes = 8 whole rows, so each lane fetches the logical
-//    chunk that lands at its physical slot.
+//    c ^ (r & 7). For the fragment reads (16 rows x one chunk per quarter-wave) this XOR layout
+//    measured conflict-free on gfx950 (4 clocks per ds_read_b128, the 256 B/clk LDS peak), while
+//    an unswizzled layout costs 4x and the variant c ^ ((r ^ (r >> 3)) & 7) 2x. A direct load
+//    writes 64 lanes x 16 bytes = 8 whole rows, so each lane fetches the logical chunk that lands
+//    at its physical slot.
 //  - The MFMA's first operand is the B fragment and its second the A fragment, so each lane ends
 //    with 4 consecutive n of one output row m and writes them with one 8-byte store.
 //  - Workgroup ids are remapped so that each of the 8 XCDs (private L2 each) works on a
@@ -45,17 +47,17 @@ typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
 
 enum Kind { KIND_E4M3 = 0, KIND_E2M1 = 1, KIND_F16 = 2 };
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr int kRowBytes = 128;  // bytes of one operand row per pipeline stage
 
-MX_DEV int swz(int row) { return (row ^ (row >> 3)) & 7; }
+MX_DEV int swz(int row) { return row & 7; }
 MX_DEV int lds_off(int row, int chunk) { return row * kRowBytes + ((chunk ^ swz(row)) << 4); }
 
-template <int KIND, int BM_, int BN_>
+template <int KIND, int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_;
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int NWAVES = WAVES_M * WAVES_N, THREADS = 64 * NWAVES;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr int KSTEP = KIND == KIND_E4M3 ? 128 : (KIND == KIND_E2M1 ? 256 : 64);
   static constexpr int NSB = KSTEP / 32;  // E8M0 bytes per row per stage
@@ -63,16 +65,15 @@ struct Cfg {
   static constexpr int SCALE_DW = KIND == KIND_F16 ? 0 : (BM + BN) * NSB / 4;  // scale dwords per stage
   static constexpr int STAGE_BYTES = TILE_BYTES + 4 * SCALE_DW;
   static constexpr int LDS_BYTES = 2 * STAGE_BYTES;
-  // direct loads: one wave instruction moves 8 rows (16 B per lane) or 64 scale dwords
-  static constexpr int A_INSTR = BM / 8 / kWaves;
-  static constexpr int B_INSTR = KIND == KIND_F16 ? 0 : BN / 8 / kWaves;
-  static constexpr int S_INSTR = (SCALE_DW + 63) / 64;  // spread over the waves
+  // direct loads: one wave instruction moves 8 rows (16 B per lane) or 64 scale dwords; the
+  // instructions of a stage are dealt round-robin to the waves
+  static constexpr int ROW_INSTR = (BM + (KIND == KIND_F16 ? 0 : BN)) / 8;
+  static constexpr int S_INSTR = (SCALE_DW + 63) / 64;
   // register path (tail stage / fp16 right operand)
-  static constexpr int A_CHUNKS = BM * 8 / kThreads;
-  static constexpr int B_CHUNKS = KIND == KIND_F16 ? 0 : BN * 8 / kThreads;
-  static constexpr int B_MICRO = KIND == KIND_F16 ? (BN + kThreads - 1) / kThreads : 0;  // 8x8 fp16 blocks
-  static_assert(BM % 32 == 0 && BN % 32 == 0, "tile");
-  static_assert((BM / 8) % kWaves == 0 && (KIND == KIND_F16 || (BN / 8) % kWaves == 0), "direct loads");
+  static constexpr int A_CHUNKS = (BM * 8 + THREADS - 1) / THREADS;
+  static constexpr int B_CHUNKS = KIND == KIND_F16 ? 0 : (BN * 8 + THREADS - 1) / THREADS;
+  static constexpr int B_MICRO = KIND == KIND_F16 ? (BN + THREADS - 1) / THREADS : 0;  // 8x8 fp16 blocks
+  static_assert(BM % 32 == 0 && BN % 32 == 0 && WM % 16 == 0 && WN % 16 == 0, "tile");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -96,52 +97,107 @@ MX_DEV void g2l(const void* g, char* lds_wave_base, int size) {
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)g, (lds_ptr_t)lds_wave_base, 4, 0, 0);
 }
 
+// Buffer resources (scalar registers) over the tile's rows of A, B and their scale planes. Direct
+// copies address them with a loop-invariant 32-bit per-lane offset (VGPR) plus a wave-uniform
+// offset (SGPR), which keeps per-instruction addresses out of the vector register file.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;  // raw (untyped) buffer, 32-bit data format, no swizzle
+
+MX_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcFlags);
+}
+
+MX_DEV void b2l(rsrc_t r, char* lds_wave_base, uint32_t voff, uint32_t soff, int size) {
+  if (size == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 16, voff, soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 4, voff, soff, 0, 0);
+}
+
+struct TileSrc {
+  rsrc_t a, b, sa, sb;   // rows [m0, m0+rows_a) of A/SA and [n0, n0+rows_b) of B/SB
+  int rows_a, rows_b;
+};
+
+template <class CF>
+MX_DEV TileSrc tile_src(const Args& p, int m0, int n0) {
+  TileSrc t;
+  t.rows_a = min(CF::BM, p.M - m0);
+  t.rows_b = min(CF::BN, p.N - n0);
+  t.a = make_rsrc(p.A + (int64_t)m0 * p.a_row_bytes, (uint32_t)(t.rows_a * p.a_row_bytes));
+  t.b = make_rsrc(p.B + (int64_t)n0 * p.a_row_bytes, (uint32_t)(t.rows_b * p.a_row_bytes));
+  t.sa = make_rsrc(p.SA + (int64_t)m0 * p.nblk, (uint32_t)(t.rows_a * p.nblk));
+  t.sb = make_rsrc(p.SB + (int64_t)n0 * p.nblk, (uint32_t)(t.rows_b * p.nblk));
+  return t;
+}
+
 // Direct copy of the code rows of stage s (A, and B for MX kinds) into one LDS stage buffer.
-template <class CF, int KIND>
-MX_DEV void issue_direct_rows(const Args& p, char* buf, int m0, int n0, int s, int wave, int lane) {
-  const int64_t kbyte0 = (int64_t)s * kRowBytes;
+// Lane l of an instruction fills tile row r0 + l/8, physical chunk l%8; with the (row & 7)
+// swizzle its byte offset inside the 8-row group, (l/8)*row_bytes + ((l%8) ^ (l/8))*16, is the
+// same for every instruction. Groups that reach past the last row clamp each lane's row instead.
+template <class CF, int KIND, int NW = CF::NWAVES>
+MX_DEV void issue_direct_rows(const Args& p, const TileSrc& t, char* buf, int s, int wave, int lane) {
+  const uint32_t kbyte0 = (uint32_t)(s * kRowBytes), rb = (uint32_t)p.a_row_bytes;
   const int rsub = lane >> 3, pch = lane & 7;
+  const uint32_t chunk_off = (uint32_t)((pch ^ rsub) << 4), lane_off = (uint32_t)rsub * rb + chunk_off;
 #pragma unroll
-  for (int i = 0; i < CF::A_INSTR; i++) {
-    const int r0 = (wave * CF::A_INSTR + i) * 8, row = r0 + rsub;
-    const int gr = min(m0 + row, p.M - 1);
-    const uint8_t* g = p.A + (int64_t)gr * p.a_row_bytes + kbyte0 + ((pch ^ swz(row)) << 4);
-    g2l(g, buf + r0 * kRowBytes, 16);
-  }
-#pragma unroll
-  for (int i = 0; i < CF::B_INSTR; i++) {
-    const int r0 = (wave * CF::B_INSTR + i) * 8, row = r0 + rsub;
-    const int gr = min(n0 + row, p.N - 1);
-    const uint8_t* g = p.B + (int64_t)gr * p.a_row_bytes + kbyte0 + ((pch ^ swz(CF::BM + row)) << 4);
-    g2l(g, buf + (CF::BM + r0) * kRowBytes, 16);
+  for (int i0 = 0; i0 < CF::ROW_INSTR; i0 += NW) {
+    const int i = i0 + wave;
+    if (CF::ROW_INSTR % NW == 0 || i < CF::ROW_INSTR) {
+      const int r0 = i * 8;  // tile row: A rows first, then B rows
+      const bool isA = r0 < CF::BM;
+      const int rloc = isA ? r0 : r0 - CF::BM;
+      const int rows = isA ? t.rows_a : t.rows_b;
+      const rsrc_t r = isA ? t.a : t.b;
+      if (rloc + 8 <= rows) {
+        b2l(r, buf + r0 * kRowBytes, lane_off, (uint32_t)rloc * rb + kbyte0, 16);
+      } else {
+        const int cr = min(rloc + rsub, rows - 1);
+        b2l(r, buf + r0 * kRowBytes, (uint32_t)cr * rb + kbyte0 + chunk_off, 0u, 16);
+      }
+    }
   }
 }
 
 // Direct copy of the stage's scale dwords (A rows then B rows, NSB bytes each); needs K/32 % 4 == 0.
-template <class CF>
-MX_DEV void issue_direct_scales(const Args& p, char* buf, int m0, int n0, int s, int wave, int lane) {
-  constexpr int per_row = CF::NSB / 4;
+// Instruction i covers scale dwords 64i..64i+63, i.e. 64 / (NSB/4) rows.
+template <class CF, int NW = CF::NWAVES>
+MX_DEV void issue_direct_scales(const Args& p, const TileSrc& t, char* buf, int s, int wave, int lane) {
+  constexpr int per_row = CF::NSB / 4, rows_per_instr = 64 / per_row;
+  static_assert(CF::BM % rows_per_instr == 0, "scale instructions must not straddle A and B rows");
+  const int lrow = lane / per_row, ldw = lane % per_row;
+  const uint32_t nb = (uint32_t)p.nblk, sbyte0 = (uint32_t)(s * CF::NSB);
+  const uint32_t lane_off = (uint32_t)lrow * nb + 4 * ldw;
 #pragma unroll
-  for (int i = wave; i < CF::S_INSTR; i += kWaves) {
+  for (int i = wave; i < CF::S_INSTR; i += NW) {
     const int did = i * 64 + lane;
     if (did < CF::SCALE_DW) {
-      const int row = did / per_row, dw = did % per_row;
-      const bool isA = row < CF::BM;
-      const int gr = isA ? min(m0 + row, p.M - 1) : min(n0 + row - CF::BM, p.N - 1);
-      const uint8_t* g = (isA ? p.SA : p.SB) + (int64_t)gr * p.nblk + s * CF::NSB + 4 * dw;
-      g2l(g, buf + CF::TILE_BYTES + i * 256, 4);
+      const int r0 = i * rows_per_instr;
+      const bool isA = r0 < CF::BM;
+      const int rloc = isA ? r0 : r0 - CF::BM;
+      const int rows = isA ? t.rows_a : t.rows_b;
+      const rsrc_t r = isA ? t.sa : t.sb;
+      if (rloc + rows_per_instr <= rows) {
+        b2l(r, buf + CF::TILE_BYTES + i * 256, lane_off, (uint32_t)rloc * nb + sbyte0, 4);
+      } else {
+        const int cr = min(rloc + lrow, rows - 1);
+        b2l(r, buf + CF::TILE_BYTES + i * 256, (uint32_t)cr * nb + sbyte0 + 4 * ldw, 0u, 4);
+      }
     }
   }
 }
 
 // Register path for one stage: zero-filled codes past K, scale 127 (= 1.0) for blocks past K.
-template <class CF, int KIND>
+template <class CF, int KIND, int NTHR = CF::THREADS>
 MX_DEV void copy_stage_regs(const Args& p, char* buf, int m0, int n0, int s, int tid, bool rows, bool scales) {
   const int64_t kbyte0 = (int64_t)s * kRowBytes;
+  constexpr int A_CH = (CF::BM * 8 + NTHR - 1) / NTHR;
+  constexpr int B_CH = KIND == KIND_F16 ? 0 : (CF::BN * 8 + NTHR - 1) / NTHR;
   if (rows) {
 #pragma unroll
-    for (int i = 0; i < CF::A_CHUNKS; i++) {
-      const int cid = tid + kThreads * i, row = cid >> 3, cc = cid & 7;
+    for (int i = 0; i < A_CH; i++) {
+      const int cid = tid + NTHR * i, row = cid >> 3, cc = cid & 7;
+      if (cid >= CF::BM * 8) break;
       const int gr = min(m0 + row, p.M - 1);
       const int64_t kb = kbyte0 + cc * 16;
       const v4i v = kb < p.a_row_bytes ? *reinterpret_cast<const v4i*>(p.A + (int64_t)gr * p.a_row_bytes + kb)
@@ -149,8 +205,9 @@ MX_DEV void copy_stage_regs(const Args& p, char* buf, int m0, int n0, int s, int
       *reinterpret_cast<v4i*>(buf + lds_off(row, cc)) = v;
     }
 #pragma unroll
-    for (int i = 0; i < CF::B_CHUNKS; i++) {
-      const int cid = tid + kThreads * i, row = cid >> 3, cc = cid & 7;
+    for (int i = 0; i < B_CH; i++) {
+      const int cid = tid + NTHR * i, row = cid >> 3, cc = cid & 7;
+      if (cid >= CF::BN * 8) break;
       const int gr = min(n0 + row, p.N - 1);
       const int64_t kb = kbyte0 + cc * 16;
       const v4i v = kb < p.a_row_bytes ? *reinterpret_cast<const v4i*>(p.B + (int64_t)gr * p.a_row_bytes + kb)
@@ -162,7 +219,7 @@ MX_DEV void copy_stage_regs(const Args& p, char* buf, int m0, int n0, int s, int
     if (scales) {
       constexpr int per_row = CF::NSB / 4;
       uint32_t* sl = reinterpret_cast<uint32_t*>(buf + CF::TILE_BYTES);
-      for (int did = tid; did < CF::SCALE_DW; did += kThreads) {
+      for (int did = tid; did < CF::SCALE_DW; did += NTHR) {
         const int row = did / per_row, dw = did % per_row;
         const bool isA = row < CF::BM;
         const int gr = isA ? min(m0 + row, p.M - 1) : min(n0 + row - CF::BM, p.N - 1);
@@ -188,7 +245,7 @@ template <class CF>
 MX_DEV void load_btrans(BTrans<CF>& bt, const Args& p, int n0, int s, int tid) {
 #pragma unroll
   for (int u = 0; u < CF::B_MICRO; u++) {
-    const int mb = tid + kThreads * u;
+    const int mb = tid + CF::THREADS * u;
     constexpr int nchunks = CF::BN / 8;
     const int nc = mb % nchunks, kg = mb / nchunks;
     const int n = n0 + nc * 8;
@@ -205,7 +262,7 @@ template <class CF>
 MX_DEV void store_btrans(const BTrans<CF>& bt, char* buf, int tid) {
 #pragma unroll
   for (int u = 0; u < CF::B_MICRO; u++) {
-    const int mb = tid + kThreads * u;
+    const int mb = tid + CF::THREADS * u;
     if (mb >= CF::BN) break;
     constexpr int nchunks = CF::BN / 8;
     const int nc = mb % nchunks, kg = mb / nchunks;
@@ -223,6 +280,16 @@ MX_DEV void store_btrans(const BTrans<CF>& bt, char* buf, int tid) {
     }
   }
 }
+
+// Workgroup barrier without the release/acquire fences of __syncthreads(): those fences make the
+// compiler wait for every outstanding direct global->LDS load (vmcnt(0)) at each barrier, which
+// would serialise the next stage's copy into the current one. The memory clobber keeps the
+// compiler from moving memory operations across it; the waits the protocol needs are explicit:
+// wait_lds() before a barrier that releases an LDS buffer for overwriting, wait_vm() before a
+// barrier that publishes a direct copy.
+MX_DEV void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+MX_DEV void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0) only
+MX_DEV void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0) only
 
 MX_DEV v4i lds_read16(const char* lds, int row, int chunk) {
   return *reinterpret_cast<const v4i*>(lds + lds_off(row, chunk));
@@ -301,10 +368,11 @@ MX_DEV void compute_stage(const char* buf, v4f (&acc)[CF::FN][CF::FM], int wm, i
 }
 
 template <class CF, int KIND>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Args p) {
+__global__ __launch_bounds__(CF::THREADS, 1) void gemm_kernel(Args p) {
   __shared__ __attribute__((aligned(16))) char lds[CF::LDS_BYTES];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
+  const int wm = wave % CF::WAVES_M, wn = wave / CF::WAVES_M;
   const int r16 = lane & 15, q = lane >> 4;
 
   // XCD-aware tile order (see file comment).
@@ -323,11 +391,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Args p) {
 
   // Start the copy of stage s into buffer b. Returns after queueing direct loads (full stages)
   // or after finishing register copies (tail stage, unaligned scales).
+  const TileSrc tsrc = tile_src<CF>(p, m0, n0);
   auto start_stage = [&](int s, char* buf) {
     const bool full = (int64_t)(s + 1) * kRowBytes <= p.a_row_bytes;
-    if (full) issue_direct_rows<CF, KIND>(p, buf, m0, n0, s, wave, lane);
+    if (full) issue_direct_rows<CF, KIND>(p, tsrc, buf, s, wave, lane);
     if constexpr (KIND != KIND_F16) {
-      if (full && aligned_scales) issue_direct_scales<CF>(p, buf, m0, n0, s, wave, lane);
+      if (full && aligned_scales) issue_direct_scales<CF>(p, tsrc, buf, s, wave, lane);
       if (!full || !aligned_scales) copy_stage_regs<CF, KIND>(p, buf, m0, n0, s, tid, !full, true);
     } else {
       if (!full) copy_stage_regs<CF, KIND>(p, buf, m0, n0, s, tid, true, false);
@@ -356,8 +425,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Args p) {
       __builtin_amdgcn_sched_barrier(0);
       if (more) store_btrans<CF>(bt, nxt, tid);
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads have landed in LDS
-    __syncthreads();                // ... and every other wave's
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies (direct and register) have landed in LDS
+    raw_barrier();                  // ... and every other wave's
   }
 
   // Epilogue: fp32 -> fp16 (nearest even), lane holds C[m][n..n+3].
@@ -382,16 +451,234 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(Args p) {
   }
 }
 
+
+// ------------------------------------------------------------------------------------------------
+// Ping-pong variant for the MX formats (8 waves, 4 x 2, two per SIMD).
+//
+// Waves 0-3 (group 0, left half of the tile's N) and waves 4-7 (group 1, right half) run half a
+// stage apart. Each wave alternates a load phase (LDS -> registers: its A/B fragments and scale
+// bytes of one stage; plus its 1/8 share of a direct global->LDS stage copy) and a compute phase
+// (all MFMAs of the stage, from registers only). While one wave of a SIMD computes, its partner
+// loads, so the matrix core always has an instruction stream, and the (blocking) issue of the
+// copy loads never sits inside an MFMA stream. Stage t lives in buffer t&1:
+//   phase 2t   : group 0 queues its share of stage t+1 (buffer (t+1)&1), reads stage t
+//                group 1 computes stage t-1
+//   phase 2t+1 : group 0 computes stage t
+//                group 1 reads stage t, then queues its share of stage t+2 into buffer t&1
+// A copy into a buffer starts only after both groups have read the stage it replaces; each group
+// waits for its own copies at the end of its compute phase, before the stage is first read.
+// Stages 0 and 1 are copied by all waves before the loop. Workgroup barriers separate phases and
+// both groups execute the same number of them.
+// ------------------------------------------------------------------------------------------------
+template <class CF, int KIND>
+struct Frags {
+  // E4M3: one 32-byte fragment per 16 rows; E2M1: two 16-byte halves (K-halves of the stage)
+  v8i a8[KIND == KIND_E4M3 ? CF::FM : 1], b8[KIND == KIND_E4M3 ? CF::FN : 1];
+  v4i a4[KIND == KIND_E2M1 ? CF::FM : 1][2], b4[KIND == KIND_E2M1 ? CF::FN : 1][2];
+  int sa[CF::FM], sb[CF::FN];
+};
+
+template <class CF, int KIND>
+MX_DEV void load_frags(Frags<CF, KIND>& f, const char* buf, int wm, int wn, int r16, int q) {
+  const uint8_t* sc = reinterpret_cast<const uint8_t*>(buf + CF::TILE_BYTES);
+#pragma unroll
+  for (int j = 0; j < CF::FM; j++) {
+    const int row = wm * CF::WM + 16 * j + r16;
+    if constexpr (KIND == KIND_E4M3) {
+      f.a8[j] = cat(lds_read16(buf, row, q), lds_read16(buf, row, 4 + q));
+      f.sa[j] = sc[row * CF::NSB + q];
+    } else {
+      f.a4[j][0] = lds_read16(buf, row, q);
+      f.a4[j][1] = lds_read16(buf, row, 4 + q);
+      f.sa[j] = sc[row * CF::NSB + q] | (sc[row * CF::NSB + 4 + q] << 8);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CF::FN; i++) {
+    const int row = CF::BM + wn * CF::WN + 16 * i + r16;
+    if constexpr (KIND == KIND_E4M3) {
+      f.b8[i] = cat(lds_read16(buf, row, q), lds_read16(buf, row, 4 + q));
+      f.sb[i] = sc[row * CF::NSB + q];
+    } else {
+      f.b4[i][0] = lds_read16(buf, row, q);
+      f.b4[i][1] = lds_read16(buf, row, 4 + q);
+      f.sb[i] = sc[row * CF::NSB + q] | (sc[row * CF::NSB + 4 + q] << 8);
+    }
+  }
+}
+
+// Route every fragment register through an empty volatile asm, ordered after the preceding
+// barrier, so the MFMAs that consume them cannot be scheduled before it.
+template <class CF, int KIND>
+MX_DEV void pin_frags(Frags<CF, KIND>& f) {
+#pragma unroll
+  for (int j = 0; j < CF::FM; j++) {
+    if constexpr (KIND == KIND_E4M3) asm volatile("" : "+v"(f.a8[j]));
+    else asm volatile("" : "+v"(f.a4[j][0]), "+v"(f.a4[j][1]));
+    asm volatile("" : "+v"(f.sa[j]));
+  }
+#pragma unroll
+  for (int i = 0; i < CF::FN; i++) {
+    if constexpr (KIND == KIND_E4M3) asm volatile("" : "+v"(f.b8[i]));
+    else asm volatile("" : "+v"(f.b4[i][0]), "+v"(f.b4[i][1]));
+    asm volatile("" : "+v"(f.sb[i]));
+  }
+}
+
+template <class CF, int KIND>
+MX_DEV void mfma_frags(const Frags<CF, KIND>& f, v4f (&acc)[CF::FN][CF::FM]) {
+  if constexpr (KIND == KIND_E4M3) {
+#pragma unroll
+    for (int i = 0; i < CF::FN; i++)
+#pragma unroll
+      for (int j = 0; j < CF::FM; j++)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(f.b8[i], f.a8[j], acc[i][j], 0, 0, 0, f.sb[i], 0, f.sa[j]);
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+      for (int i = 0; i < CF::FN; i++)
+#pragma unroll
+        for (int j = 0; j < CF::FM; j++) {
+          if (h == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(f.b4[i][0]), widen(f.a4[j][0]), acc[i][j], 4,
+                                                                         4, 0, f.sb[i], 0, f.sa[j]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(widen(f.b4[i][1]), widen(f.a4[j][1]), acc[i][j], 4,
+                                                                         4, 1, f.sb[i], 1, f.sa[j]);
+        }
+  }
+}
+
+template <class CF, int KIND>
+MX_DEV void pin_acc(v4f (&acc)[CF::FN][CF::FM]) {
+#pragma unroll
+  for (int i = 0; i < CF::FN; i++)
+#pragma unroll
+    for (int j = 0; j < CF::FM; j++) asm volatile("" : "+v"(acc[i][j]));
+}
+
+template <class CF, int KIND>
+__global__ __launch_bounds__(CF::THREADS, 1) void gemm_pp_kernel(Args p) {
+  static_assert(CF::WAVES_M == 4 && CF::WAVES_N == 2 && KIND != KIND_F16, "ping-pong layout");
+  __shared__ __attribute__((aligned(16))) char lds[CF::LDS_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) index
+  const int wm = wave % CF::WAVES_M, wn = wave / CF::WAVES_M;  // group = wn
+  const int r16 = lane & 15, q = lane >> 4;
+  const int gw = wave & 3;                                     // wave index inside its group
+
+  int bid = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
+  const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
+  const int m0 = tm * CF::BM, n0 = tn * CF::BN;
+
+  v4f acc[CF::FN][CF::FM];
+#pragma unroll
+  for (int i = 0; i < CF::FN; i++)
+#pragma unroll
+    for (int j = 0; j < CF::FM; j++) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // The host uses this kernel only when every stage is full (K a multiple of the stage) and the
+  // scale rows are dword aligned (K/32 % 4 == 0). Prologue: all 8 waves copy stages 0 and 1.
+  const TileSrc tsrc = tile_src<CF>(p, m0, n0);
+  issue_direct_rows<CF, KIND, 8>(p, tsrc, lds, 0, wave, lane);
+  issue_direct_scales<CF, 8>(p, tsrc, lds, 0, wave, lane);
+  if (p.nstages > 1) {
+    issue_direct_rows<CF, KIND, 8>(p, tsrc, lds + CF::STAGE_BYTES, 1, wave, lane);
+    issue_direct_scales<CF, 8>(p, tsrc, lds + CF::STAGE_BYTES, 1, wave, lane);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  raw_barrier();
+
+  Frags<CF, KIND> f;
+  if (wn == 0) {
+    for (int t = 0; t < p.nstages; t++) {
+      char* cur = lds + (t & 1) * CF::STAGE_BYTES;
+      if (t >= 1 && t + 1 < p.nstages) {  // phase 2t: this wave's share of stage t+1
+        char* nxt = lds + ((t + 1) & 1) * CF::STAGE_BYTES;
+        issue_direct_rows<CF, KIND, 8>(p, tsrc, nxt, t + 1, wave, lane);
+        issue_direct_scales<CF, 8>(p, tsrc, nxt, t + 1, wave, lane);
+      }
+      load_frags<CF, KIND>(f, cur, wm, wn, r16, q);
+      wait_lds();
+      raw_barrier();
+      pin_frags<CF, KIND>(f);
+      mfma_frags<CF, KIND>(f, acc);  // phase 2t+1
+      pin_acc<CF, KIND>(acc);
+      wait_vm();                     // the share of stage t+1 queued in phase 2t has landed
+      raw_barrier();
+    }
+    raw_barrier();
+  } else {
+    raw_barrier();  // phase 0
+    for (int t = 0; t < p.nstages; t++) {
+      char* cur = lds + (t & 1) * CF::STAGE_BYTES;
+      load_frags<CF, KIND>(f, cur, wm, wn, r16, q);  // phase 2t+1
+      wait_lds();
+      if (t + 2 < p.nstages) {  // this wave's share of stage t+2 into the buffer just read
+        issue_direct_rows<CF, KIND, 8>(p, tsrc, cur, t + 2, wave, lane);
+        issue_direct_scales<CF, 8>(p, tsrc, cur, t + 2, wave, lane);
+      }
+      raw_barrier();
+      pin_frags<CF, KIND>(f);
+      mfma_frags<CF, KIND>(f, acc);  // phase 2t+2
+      pin_acc<CF, KIND>(acc);
+      wait_vm();                     // the share of stage t+2 queued in phase 2t+1 has landed
+      raw_barrier();
+    }
+  }
+
+  const bool vec = (p.N & 3) == 0;
+#pragma unroll
+  for (int i = 0; i < CF::FN; i++) {
+    const int n = n0 + wn * CF::WN + 16 * i + 4 * q;
+#pragma unroll
+    for (int j = 0; j < CF::FM; j++) {
+      const int m = m0 + wm * CF::WM + 16 * j + r16;
+      if (m >= p.M) continue;
+      _Float16* crow = p.C + (int64_t)m * p.N;
+      const v4f a = acc[i][j];
+      if (vec && n + 3 < p.N) {
+        *reinterpret_cast<v4h*>(crow + n) = v4h{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3]};
+      } else {
+#pragma unroll
+        for (int v = 0; v < 4; v++)
+          if (n + v < p.N) crow[n + v] = (_Float16)a[v];
+      }
+    }
+  }
+}
+
 template <int KIND, int BM, int BN>
+int launch_pp(const Args& a0, hipStream_t stream) {
+  if constexpr (KIND == KIND_F16) {
+    return MX_ERR_FORMAT;
+  } else {
+    using CF = Cfg<KIND, BM, BN, 4, 2>;
+    if (a0.a_row_bytes % kRowBytes != 0 || (a0.nblk & 3) != 0) return launch<KIND, BM, BN, 4, 2>(a0, stream);
+    Args a = a0;
+    a.tiles_m = (a.M + BM - 1) / BM;
+    a.tiles_n = (a.N + BN - 1) / BN;
+    a.nstages = (int)((a.a_row_bytes + kRowBytes - 1) / kRowBytes);
+    const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
+    if (tiles > 0x7FFFFFFF) return MX_ERR_SHAPE;
+    hipLaunchKernelGGL((gemm_pp_kernel<CF, KIND>), dim3((unsigned)tiles), dim3(CF::THREADS), 0, stream, a);
+    return mx::launch_status();
+  }
+}
+
+template <int KIND, int BM, int BN, int WGM, int WGN>
 int launch(const Args& a0, hipStream_t stream) {
-  using CF = Cfg<KIND, BM, BN>;
+  using CF = Cfg<KIND, BM, BN, WGM, WGN>;
   Args a = a0;
   a.tiles_m = (a.M + BM - 1) / BM;
   a.tiles_n = (a.N + BN - 1) / BN;
   a.nstages = (int)((a.a_row_bytes + kRowBytes - 1) / kRowBytes);
   const int64_t tiles = (int64_t)a.tiles_m * a.tiles_n;
   if (tiles > 0x7FFFFFFF) return MX_ERR_SHAPE;
-  hipLaunchKernelGGL((gemm_kernel<CF, KIND>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((gemm_kernel<CF, KIND>), dim3((unsigned)tiles), dim3(CF::THREADS), 0, stream, a);
   return mx::launch_status();
 }
 
@@ -413,16 +700,24 @@ int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void
   a.K = K;
   a.nblk = K / 32;
   a.a_row_bytes = kind == KIND_E4M3 ? K : (kind == KIND_E2M1 ? K / 2 : 2 * (int64_t)K);
-#define MX_TILE(ID, BM, BN)                                             \
-  case ID:                                                              \
-    if (kind == KIND_E4M3) return launch<KIND_E4M3, BM, BN>(a, stream); \
-    if (kind == KIND_E2M1) return launch<KIND_E2M1, BM, BN>(a, stream); \
-    return launch<KIND_F16, BM, BN>(a, stream);
+#define MX_TILE(ID, BM, BN, WGM, WGN)                                             \
+  case ID:                                                                        \
+    if (kind == KIND_E4M3) return launch<KIND_E4M3, BM, BN, WGM, WGN>(a, stream); \
+    if (kind == KIND_E2M1) return launch<KIND_E2M1, BM, BN, WGM, WGN>(a, stream); \
+    return launch<KIND_F16, BM, BN, WGM, WGN>(a, stream);
   switch (tile_id) {
-    MX_TILE(0, 256, 256)
-    MX_TILE(1, 256, 224)
-    MX_TILE(2, 128, 128)
-    MX_TILE(3, 64, 64)
+    MX_TILE(0, 256, 256, 2, 2)
+    MX_TILE(1, 256, 224, 2, 2)
+    MX_TILE(2, 128, 128, 2, 2)
+    MX_TILE(3, 64, 64, 2, 2)
+    MX_TILE(4, 256, 256, 4, 2)
+    MX_TILE(5, 256, 224, 4, 2)
+    case 6:
+      if (kind == KIND_F16) return launch<KIND_F16, 256, 256, 4, 2>(a, stream);
+      return kind == KIND_E4M3 ? launch_pp<KIND_E4M3, 256, 256>(a, stream) : launch_pp<KIND_E2M1, 256, 256>(a, stream);
+    case 7:
+      if (kind == KIND_F16) return launch<KIND_F16, 256, 224, 4, 2>(a, stream);
+      return kind == KIND_E4M3 ? launch_pp<KIND_E4M3, 256, 224>(a, stream) : launch_pp<KIND_E2M1, 256, 224>(a, stream);
     default: return MX_ERR_FORMAT;
   }
 #undef MX_TILE

@@ -102,8 +102,10 @@ int mxgemm_run(mxgemm_t p, const void* A, const void* SA, const void* B, const v
 /* mxgemm_destroy -- release a plan (NULL is accepted and ignored). */
 int mxgemm_destroy(mxgemm_t p);
 
-/* Kernel tile chosen by a plan (for reports): block rows, block cols, K per pipeline stage. */
-int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k);
+/* Kernel chosen by a plan (for reports): output tile rows and columns, K elements per pipeline
+ * stage, and the kernel variant (0: 4 waves, 1: 8 waves, 2: 8-wave ping-pong schedule). The
+ * environment variable MXGEMM_TILE (a tile id 0..7), read at mxgemm_create, overrides the choice. */
+int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* variant);
 
 /* ------------------------------------------------------------------------------------------ */
 /* Dequant matvec for decode.                                                                   */

@@ -58,13 +58,30 @@ def test_mx_small_config_full(orc, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 4])
-@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7])
 def test_mx_every_tile_ragged(orc, fmt, tile):
     """Each tile configuration on a shape spanning several tiles with ragged M, N and K tails."""
     api = require_gpu()
     M, N, K = 300, 520, 416          # K = 13 blocks: partial last stage for both formats
     say(f"mx ragged fmt={fmt} tile={tile}")
     C, (oA, oSA, oB, oSB) = mx_case(orc, api, fmt, M, N, K, 4242 + tile, tile=tile)
+    ref = orc.mxgemm(fmt, fmt, oA, oSA, oB, oSB, M, N, K)
+    ok, ratio, bad = orc.check(C, ref, K, R_of(orc, fmt, oA, oSA, oB, oSB, M, N, K))
+    assert ok, (ratio, bad)
+
+
+@pytest.mark.parametrize("fmt", [0, 4])
+@pytest.mark.parametrize("tile", [6, 7])
+@pytest.mark.parametrize("K", [128, 256, 512, 1024])
+def test_mx_pingpong_ragged_mn(orc, fmt, tile, K):
+    """The 8-wave ping-pong kernels (whole stages only: K % 128 (E4M3) / 256 (E2M1) == 0) on ragged
+    M and N, from one and two stages up to several."""
+    api = require_gpu()
+    if fmt == 4 and K % 256:
+        pytest.skip("E2M1 stages are 256 wide")
+    M, N = 300, 520
+    say(f"mx ping-pong fmt={fmt} tile={tile} K={K}")
+    C, (oA, oSA, oB, oSB) = mx_case(orc, api, fmt, M, N, K, 999 + K + tile, tile=tile)
     ref = orc.mxgemm(fmt, fmt, oA, oSA, oB, oSB, M, N, K)
     ok, ratio, bad = orc.check(C, ref, K, R_of(orc, fmt, oA, oSA, oB, oSB, M, N, K))
     assert ok, (ratio, bad)
@@ -195,7 +212,7 @@ def fp16_case(orc, api, M, N, K, seed, tile=None):
     return A, B, C
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 3])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7])
 def test_f16_every_tile_ragged(orc, tile):
     api = require_gpu()
     M, N, K = 300, 520, 200

@@ -119,9 +119,9 @@ def test_validation_errors_without_gpu():
     assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 0, 1) == api.MX_ERR_FORMAT     # flags
     assert lib.mxgemm_create(ctypes.byref(h), 16, 12, 32, 16, 16, 0) == api.MX_ERR_SHAPE    # fp16 N % 8
     assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 0, 0) == api.MX_OK
-    tm, tn, tk = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
-    assert lib.mxgemm_plan_info(h, ctypes.byref(tm), ctypes.byref(tn), ctypes.byref(tk)) == 0
-    assert (tm.value, tn.value, tk.value) == (64, 64, 128)
+    tm, tn, tk, tv = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    assert lib.mxgemm_plan_info(h, ctypes.byref(tm), ctypes.byref(tn), ctypes.byref(tk), ctypes.byref(tv)) == 0
+    assert (tm.value, tn.value, tk.value, tv.value) == (64, 64, 128, 0)
     assert lib.mxgemm_run(h, None, 16, 16, 16, 16, None) == api.MX_ERR_NULL
     assert lib.mxgemm_run(h, 16, None, 16, 16, 16, None) == api.MX_ERR_NULL               # scales needed
     assert lib.mxgemm_run(h, 17, 16, 16, 16, 16, None) == api.MX_ERR_ALIGN
