@@ -203,6 +203,7 @@ void orc_matvec(int fw, int64_t M, int64_t N, int64_t K, const uint16_t* x, cons
 /* ------------------------------------------------------------------------------------------ */
 
 void orc_dequant(int fmt, int64_t rows, int64_t cols, const uint8_t* codes, const void* scales, float* out) {
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; r++)
     for (int64_t c = 0; c < cols; c++) {
       double v;
@@ -225,16 +226,27 @@ void orc_dequant(int fmt, int64_t rows, int64_t cols, const uint8_t* codes, cons
 /* The element search is brute force over the format's own decode values (not bit arithmetic). */
 /* ------------------------------------------------------------------------------------------ */
 
-/* Nearest finite code magnitude for |v| (search over codes 0..ncodes-1 of the positive half).
- * Values at or beyond the largest finite element saturate to it; below it every candidate
- * distance that can decide the choice is exact in fp64. */
+/* The positive finite element values of a format, indexed by code (E4M3: 0x00..0x7E, E2M1: 0..7),
+ * filled once from the closed-form decoders above. */
+static double g_tab_e4m3[0x7F], g_tab_e2m1[8];
+static int g_tab_ready = 0;
+static void build_tables(void) {
+  if (g_tab_ready) return;
+  for (unsigned c = 0; c < 0x7Fu; c++) g_tab_e4m3[c] = orc_dec_e4m3(c);
+  for (unsigned c = 0; c < 8u; c++) g_tab_e2m1[c] = orc_dec_e2m1(c);
+  g_tab_ready = 1;
+}
+
+/* Nearest finite code magnitude for |v|: brute-force search over every positive finite code,
+ * ties to the even code. Values at or beyond the largest finite element saturate to it; below it
+ * every candidate distance that can decide the choice is exact in fp64. */
 static unsigned nearest_code(double av, int fmt) {
-  unsigned best = 0, ncodes = (fmt == ORC_E4M3) ? 0x7Fu : 8u; /* E4M3: 0x00..0x7E are finite */
+  const double* tab = (fmt == ORC_E4M3) ? g_tab_e4m3 : g_tab_e2m1;
+  unsigned best = 0, ncodes = (fmt == ORC_E4M3) ? 0x7Fu : 8u;
   double bestd = INFINITY;
-  double vmax = (fmt == ORC_E4M3) ? orc_dec_e4m3(0x7Eu) : orc_dec_e2m1(7u);
-  if (av >= vmax) return ncodes - 1u;
+  if (av >= tab[ncodes - 1u]) return ncodes - 1u;
   for (unsigned c = 0; c < ncodes; c++) {
-    double d = fabs(av - (fmt == ORC_E4M3 ? orc_dec_e4m3(c) : orc_dec_e2m1(c)));
+    double d = fabs(av - tab[c]);
     if (d < bestd || (d == bestd && (c & 1u) == 0u)) { bestd = d; best = c; }
   }
   return best;
@@ -242,6 +254,7 @@ static unsigned nearest_code(double av, int fmt) {
 
 /* Element encoder: the code whose value is nearest to v (sign kept, -0 allowed). */
 unsigned orc_enc_elem(int fmt, double v) {
+  build_tables();
   unsigned mag = nearest_code(fabs(v), fmt);
   unsigned sbit = (fmt == ORC_E4M3) ? 0x80u : 0x8u;
   return signbit(v) ? (mag | sbit) : mag;
@@ -269,7 +282,9 @@ unsigned orc_mx_scale_code(int fmt, double amax) {
  * scale 0xFF and zero codes. */
 void orc_mx_quantize(int fmt, int64_t rows, int64_t cols, const float* src, uint8_t* codes, uint8_t* scales) {
   int64_t rb = mx_row_bytes(fmt, cols);
+  build_tables();
   memset(codes, 0, (size_t)(rows * rb));
+#pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; r++)
     for (int64_t b = 0; b < cols / 32; b++) {
       const float* x = src + r * cols + 32 * b;
@@ -315,6 +330,7 @@ unsigned orc_enc_f16(double x) {
  *   q = 0 where s = 0. qmax = 127 (int8) or 7 (int4). Output q as int8 [K][N] (one per byte),
  *   scales binary16 bits [K/32][N]. Packing of int4 is separate (orc_pack_int4). */
 void orc_int_quantize(int qmax, int64_t K, int64_t N, const float* w, int8_t* q, uint16_t* s16) {
+#pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < K / 32; b++)
     for (int64_t n = 0; n < N; n++) {
       float amax = 0.0f;
