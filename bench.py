@@ -170,12 +170,16 @@ def main():
             for Mv in (1, 8):
                 y = torch.empty((Mv, Nm), dtype=torch.float16, device=dev)
                 xv = xd[:Mv].contiguous()
-                t = timed(lambda i: api.mxmatvec_run(Mv, Nm, Km, xv, wsets[i % copies][0], fw, wsets[i % copies][1],
-                                                     y, stream), args.steps, args.warmup)
+                need = api.mxmatvec_workspace_size(Mv, Nm, Km, fw)
+                ws = torch.zeros(max(16, need), dtype=torch.uint8, device=dev)
                 nbytes = W.numel() + Ws.numel() * 2 + Mv * Km * 2 + Mv * Nm * 2
-                gbs = nbytes / (t * 1e-3) / 1e9
-                detail[f"matvec_{name}_M{Mv}"] = {"us": t * 1e3, "gbs": gbs, "frac_hbm": gbs / PEAK["hbm_gbs"],
-                                                  "bytes": nbytes, "weight_copies": copies}
+                for label, wsp in (("", ws), ("_single_pass", None)):
+                    t = timed(lambda i: api.mxmatvec_run(Mv, Nm, Km, xv, wsets[i % copies][0], fw, wsets[i % copies][1],
+                                                         y, wsp, None, stream), args.steps, args.warmup)
+                    gbs = nbytes / (t * 1e-3) / 1e9
+                    detail[f"matvec_{name}_M{Mv}{label}"] = {"us": t * 1e3, "gbs": gbs, "frac_hbm": gbs / PEAK["hbm_gbs"],
+                                                            "bytes": nbytes, "weight_copies": copies,
+                                                            "workspace_bytes": need if wsp is not None else 0}
             del wsets
         del wd
 

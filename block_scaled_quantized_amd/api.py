@@ -30,7 +30,8 @@ EXPORTS = {
     "mxgemm_run": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "mxgemm_destroy": (_i, [_vp]),
     "mxgemm_plan_info": (_i, [_vp, ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i)]),
-    "mxmatvec_run": (_i, [_i, _i, _i, _vp, _vp, _i, _vp, _vp, _vp]),
+    "mxmatvec_run": (_i, [_i, _i, _i, _vp, _vp, _i, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "mxmatvec_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "mx_pack_run": (_i, [_i, _vp, _i, _i, _vp, _vp, _vp]),
     "mx_unpack_run": (_i, [_i, _vp, _vp, _i, _i, _vp, _vp]),
     "mx_pack_host": (_i, [_i, _vp, _i64, _i64, _vp, _vp]),
@@ -123,8 +124,18 @@ def mxgemm_destroy(plan: Plan) -> None:
     plan.close()
 
 
-def mxmatvec_run(M: int, N: int, K: int, x, W, fw: int, Ws, y, stream=None) -> None:
-    _check(_lib.mxmatvec_run(M, N, K, _ptr(x), _ptr(W), fw, _ptr(Ws), _ptr(y), _stream(stream)), "mxmatvec_run")
+def mxmatvec_run(M: int, N: int, K: int, x, W, fw: int, Ws, y, workspace=None, workspace_bytes=None,
+                 stream=None) -> None:
+    """workspace: a zero-filled device buffer (tensor or address) of workspace_bytes bytes (a
+    tensor's own size when omitted), or None for the single-pass kernel."""
+    if workspace is not None and workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.mxmatvec_run(M, N, K, _ptr(x), _ptr(W), fw, _ptr(Ws), _ptr(y), _ptr(workspace),
+                             int(workspace_bytes or 0), _stream(stream)), "mxmatvec_run")
+
+
+def mxmatvec_workspace_size(M: int, N: int, K: int, fw: int) -> int:
+    return int(_lib.mxmatvec_workspace_size(M, N, K, fw))
 
 
 def mx_pack_run(f: int, src, rows: int, cols: int, codes, scales, stream=None) -> None:

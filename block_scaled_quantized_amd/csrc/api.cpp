@@ -10,8 +10,9 @@
 namespace mx {
 int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
                 int N, int K, hipStream_t stream);
-int matvec_launch(int M, int N, int K, const void* x, const void* W, bool int8, const void* Ws, void* y,
-                  hipStream_t stream);
+int matvec_launch(int M, int N, int K, const void* x, const void* W, bool int8, const void* Ws, void* y, void* ws,
+                  size_t ws_bytes, hipStream_t stream);
+size_t matvec_workspace(int M, int N, int K, bool int8);
 
 namespace {
 constexpr int kMaxDevices = 64;
@@ -144,14 +145,27 @@ int mxgemm_run(mxgemm_t p, const void* A, const void* SA, const void* B, const v
   return gemm_launch(p->kind, p->tile_id, A, SA, B, SB, C, p->M, p->N, p->K, as_stream(stream));
 }
 
-int mxmatvec_run(int M, int N, int K, const void* x, const void* W, int fw, const void* Ws, void* y, void* stream) {
-  if (!x || !W || !Ws || !y) return MX_ERR_NULL;
+static int matvec_shape(int M, int N, int K, int fw) {
   if (fw != MX_INT8 && fw != MX_INT4) return MX_ERR_FORMAT;
   if (M < 1 || M > 8 || N < 1 || N > MX_MAX_DIM || K < 32 || K > MX_MAX_DIM || K % 32) return MX_ERR_SHAPE;
   if (fw == MX_INT8 ? (N % 16) : (N % 32)) return MX_ERR_SHAPE;
+  return MX_OK;
+}
+
+size_t mxmatvec_workspace_size(int M, int N, int K, int fw) {
+  if (matvec_shape(M, N, K, fw)) return 0;
+  return matvec_workspace(M, N, K, fw == MX_INT8);
+}
+
+int mxmatvec_run(int M, int N, int K, const void* x, const void* W, int fw, const void* Ws, void* y, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  if (!x || !W || !Ws || !y) return MX_ERR_NULL;
+  if (int s = matvec_shape(M, N, K, fw)) return s;
   if (!aligned16(x) || !aligned16(W) || !aligned16(Ws) || !aligned16(y)) return MX_ERR_ALIGN;
+  if (workspace && !aligned16(workspace)) return MX_ERR_ALIGN;
   if (int a = check_arch()) return a;
-  return matvec_launch(M, N, K, x, W, fw == MX_INT8, Ws, y, as_stream(stream));
+  return matvec_launch(M, N, K, x, W, fw == MX_INT8, Ws, y, workspace, workspace ? workspace_bytes : 0,
+                       as_stream(stream));
 }
 
 }  // extern "C"

@@ -1,4 +1,4 @@
-// matvec.hip -- int8 / int4 dequant matvec for decode (M <= 8 activation rows), no MFMA.
+// matvec.hip -- int8 / int4 dequant matvec for decode (M <= 8 activation rows).
 //
 //   y[m,n] = sum_b Ws[b,n] * sum_{k in block b} x[m,k] * q[k,n]     (32-row blocks b)
 //
@@ -6,17 +6,22 @@
 // (revised strategy), with the int4 packing of section "VALIDATED ON M4 MAX", fact 5.
 //
 // The weight matrix is the only large operand, so the kernel is organised around streaming it
-// exactly once from HBM:
-//  - A workgroup owns a strip of TW = 64 columns over the whole of K, so every output is finished
-//    by one workgroup (no partial sums leave the chip, no second pass, no scratch memory).
-//  - Lane l of a wave owns 8 adjacent columns (column group l%8) and one "row phase" (l/8); the
-//    8 waves give 64 row phases, and phase p walks the 8-row chunks p, p+64, p+128, ... of K.
-//    One load instruction of a wave fetches 8 rows x 64 contiguous bytes (int8).
-//  - Weights are turned into exact fp16 pairs (q[k,n], q[k+1,n]) with a byte permute and one
-//    packed fp16 subtract (1024+128+q in the fp16 mantissa, minus 1152); the MACs are
-//    v_dot2_f32_f16 with fp32 accumulation; the fp16 block scale multiplies each 8-row partial.
-//  - Row phases of a wave are summed with xor shuffles (lane bits 3..5), then the 8 waves' sums
-//    in LDS; the fp32 result is rounded once to fp16.
+// exactly once from HBM with many bytes in flight per CU:
+//  - A workgroup owns a strip of TW = 16*C columns over the whole of K, so every output is
+//    finished by one workgroup (no partial sums leave the chip, no second pass, no scratch).
+//  - Its W waves split K: wave w takes the 32-row blocks w, w+W, w+2W, ...
+//  - One 32-row block of the strip is one fp16 MFMA 16x16x32 per column offset j < C:
+//      A (16 x 32) = x rows 0..15 of the block (rows >= M repeat row M-1; their results are dropped),
+//      B (32 x 16) = exact fp16 weights of the columns col0 + C*i + j, i = 0..15,
+//    so lane l (i = l%16, q = l/16) loads rows 8q..8q+7 of the block for its C adjacent columns
+//    and needs no cross-lane exchange. The MFMA does the M-fold reuse of every weight, which
+//    keeps the vector ALU work per weight independent of M.
+//  - Weights become exact fp16 pairs (q[k,n], q[k+1,n]) with one byte permute, one xor that
+//    plants the fp16 exponent of 1024 and the offset-binary bit, and one packed fp16 subtract.
+//  - The block's fp32 product is multiplied by the fp16 block scale of its column and added to
+//    an fp32 accumulator; the waves' accumulators meet in LDS, and the sum is rounded once to
+//    fp16.
+//  - Loads run P blocks ahead of the MFMAs through a ring of registers.
 #include "codec_math.h"
 
 using namespace mx;
@@ -24,170 +29,620 @@ using namespace mx;
 namespace {
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
-constexpr int kCG = 8;                 // column groups per wave
-constexpr int kCPL = 8;                // columns per lane
-constexpr int kTW = kCG * kCPL;        // columns per workgroup
-constexpr int kPhases = kWaves * (64 / kCG);
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 MX_DEV v2h as_v2h(uint32_t u) { return __builtin_bit_cast(v2h, u); }
 
-// fp16 pairs (q[2p][c], q[2p+1][c]) for the 4 columns held in one dword of two consecutive rows.
-// ua/ub: offset-binary bytes (q + 128) of rows 2p and 2p+1. Output w[j] for column j of the dword.
-MX_DEV void pairs_from_bytes(uint32_t ua, uint32_t ub, uint32_t bias_bits, v2h (&w)[4]) {
+// One block's loads for one lane: 8 weight rows (C columns each), the lane's x fragment and the
+// C block scales.
+template <bool I8, int C>
+struct Stage {
+  static constexpr int kWordsPerRow = I8 ? C / 4 : C / 8 > 0 ? C / 8 : 1;
+  uint32_t w[8][kWordsPerRow];
+  uint4 xa;
+  uint32_t sc[C / 2];
+};
+
+// Buffer resource over `bytes` bytes at `base` (raw buffer, no swizzle); lane offsets stay 32-bit.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+MX_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Per-lane, loop-invariant byte offsets of the loads (lanes past N or M read in-range data whose
+// products land only in dropped outputs).
+struct LaneOffsets {
+  uint32_t w;   // weight row 8q of a block, the lane's first column
+  uint32_t x;   // activation row, element 8q of a block
+  uint32_t s;   // block scale of the lane's first column
+};
+
+// Loads of block `blk`: W rows 32*blk + 8q + r (r < 8) of the lane's C columns, its C block scales
+// and (XG) its x fragment. The weight and scale resources are rebased per block, so offsets stay small
+// for any matrix size.
+template <bool I8, int C, bool XG>
+MX_DEV void load_stage(Stage<I8, C>& s, const uint8_t* __restrict__ Wt, rsrc_t xr, const _Float16* __restrict__ Ws,
+                       uint32_t N, int blk, const LaneOffsets& lo) {
+  const uint32_t row_bytes = I8 ? N : N / 2;
+  const rsrc_t wr = make_rsrc(Wt + (int64_t)blk * 32 * row_bytes, 32u * row_bytes);
+  constexpr int WPR = Stage<I8, C>::kWordsPerRow;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const uint32_t sel = (uint32_t)j | (0x0Cu << 8) | ((uint32_t)(4 + j) << 16) | (0x0Cu << 24);
-    const uint32_t pr = __builtin_amdgcn_perm(ub, ua, sel) | 0x64006400u;
-    w[j] = as_v2h(pr) - as_v2h(bias_bits);
+  for (int r = 0; r < 8; r++) {
+    const int so = (int)(r * row_bytes);
+    if constexpr (!I8 && C == 4) {
+      s.w[r][0] = __builtin_amdgcn_raw_buffer_load_b16(wr, (int)lo.w, so, 0);
+    } else if constexpr (WPR == 1) {
+      s.w[r][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, (int)lo.w, so, 0);
+    } else if constexpr (WPR == 2) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(wr, (int)lo.w, so, 0);
+      s.w[r][0] = v[0];
+      s.w[r][1] = v[1];
+    } else {
+      static_assert(WPR == 4, "4, 8, 16 int8 or 4, 8, 16, 32 int4 columns per lane");
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)lo.w, so, 0);
+#pragma unroll
+      for (int e = 0; e < 4; e++) s.w[r][e] = v[e];
+    }
+  }
+  if constexpr (XG) {
+    const auto xv = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)lo.x, blk * 64, 0);
+    s.xa = make_uint4(xv[0], xv[1], xv[2], xv[3]);
+  }
+  const rsrc_t sr = make_rsrc(Ws + (int64_t)blk * N, 2u * N);
+  if constexpr (C == 4) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(sr, (int)lo.s, 0, 0);
+    s.sc[0] = v[0];
+    s.sc[1] = v[1];
+  } else {
+#pragma unroll
+    for (int h = 0; h < C / 8; h++) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(sr, (int)lo.s + 16 * h, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; e++) s.sc[4 * h + e] = v[e];
+    }
   }
 }
 
-template <int M, bool I8>
-__global__ __launch_bounds__(kThreads) void matvec_kernel(const _Float16* __restrict__ x, const uint8_t* __restrict__ W,
-                                                          const _Float16* __restrict__ Ws, _Float16* __restrict__ y,
-                                                          int N, int K) {
-  __shared__ float red[kWaves][M][kTW];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cg = lane % kCG, phase = wave * (64 / kCG) + lane / kCG;
+// fp16 pair (lo = byte a of word u0, hi = byte b of word u1) as an exact fp16 pair of the
+// integers, given offset-binary conversion: bytes xor `flip` give 1024 + q + bias, minus `bias2`.
+MX_DEV uint32_t pick_pair(uint32_t u1, uint32_t u0, uint32_t sel) { return __builtin_amdgcn_perm(u1, u0, sel); }
 
-  int bid = blockIdx.x;
-  const int nwg = gridDim.x;
-  if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);  // neighbouring strips share an XCD
-  const int n0 = bid * kTW, nc = n0 + cg * kCPL;                   // first column of this lane
-  const bool active = nc < N;
-
-  float acc[M][kCPL];
+// B fragments of one block for the 4 columns 4g..4g+3 of the lane: frag[e] = the 8 fp16 weights
+// (rows 8q..8q+7) of column 4g+e, as pairs (q[2p][c], q[2p+1][c]).
+template <bool I8, int C>
+MX_DEV void weights_to_frags(const Stage<I8, C>& s, int g, v8h (&frag)[4]) {
+  uint32_t f[4][4];
+  if constexpr (I8) {
+    // fp16 bits 0x64XX = 1024 + XX; XX = q ^ 0x80 = q + 128, so subtract 1152 (0x6480).
+    const v2h bias = as_v2h(0x64806480u);
 #pragma unroll
-  for (int m = 0; m < M; m++)
+    for (int p = 0; p < 4; p++)
 #pragma unroll
-    for (int c = 0; c < kCPL; c++) acc[m][c] = 0.0f;
-
-  // int8: 1024+128 = 1152 (0x6480); int4: 1024+8 = 1032 (0x6408)
-  const uint32_t bias_bits = I8 ? 0x64806480u : 0x64086408u;
-  const int nchunks = K / 8;
-  if (active) {
-    for (int ch = phase; ch < nchunks; ch += kPhases) {
-      const int k0 = ch * 8;
-      // 8 rows x 8 columns of weights as fp16 pairs: wp[c][p] = (q[k0+2p][c], q[k0+2p+1][c])
-      v2h wp[kCPL][4];
-      if constexpr (I8) {
-        uint2 raw[8];
+      for (int b = 0; b < 4; b++) {
+        // byte b of word g of row 2p (low half) and of row 2p+1 (high half), zero elsewhere
+        const uint32_t sel = (uint32_t)b | (0x0Cu << 8) | ((uint32_t)(4 + b) << 16) | (0x0Cu << 24);
+        const uint32_t pr = pick_pair(s.w[2 * p + 1][g], s.w[2 * p][g], sel) ^ 0x64806480u;
+        f[b][p] = __builtin_bit_cast(uint32_t, as_v2h(pr) - bias);
+      }
+  } else {
+    // nibble u (two's complement q) ^ 8 = q + 8; fp16 1024 + q + 8, subtract 1032 (0x6408).
+    const v2h bias = as_v2h(0x64086408u);
 #pragma unroll
-        for (int r = 0; r < 8; r++) raw[r] = *reinterpret_cast<const uint2*>(W + (int64_t)(k0 + r) * N + nc);
-#pragma unroll
-        for (int p = 0; p < 4; p++) {
-          v2h t0[4], t1[4];
-          pairs_from_bytes(raw[2 * p].x ^ 0x80808080u, raw[2 * p + 1].x ^ 0x80808080u, bias_bits, t0);
-          pairs_from_bytes(raw[2 * p].y ^ 0x80808080u, raw[2 * p + 1].y ^ 0x80808080u, bias_bits, t1);
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            wp[j][p] = t0[j];
-            wp[4 + j][p] = t1[j];
-          }
-        }
+    for (int p = 0; p < 4; p++) {
+      if constexpr (C == 4) {
+        // rows 2p, 2p+1: 4 nibbles each (columns 0..3, even column in the low nibble)
+        const uint32_t d = s.w[2 * p][0] | (s.w[2 * p + 1][0] << 16);
+        const uint32_t e = d & 0x0F0F0F0Fu, o = (d >> 4) & 0x0F0F0F0Fu;  // cols 0,2 | 1,3 (row 2p: bytes 0,1)
+        f[0][p] = __builtin_bit_cast(uint32_t, as_v2h(pick_pair(e, e, 0x0C020C00u) ^ 0x64086408u) - bias);
+        f[1][p] = __builtin_bit_cast(uint32_t, as_v2h(pick_pair(o, o, 0x0C020C00u) ^ 0x64086408u) - bias);
+        f[2][p] = __builtin_bit_cast(uint32_t, as_v2h(pick_pair(e, e, 0x0C030C01u) ^ 0x64086408u) - bias);
+        f[3][p] = __builtin_bit_cast(uint32_t, as_v2h(pick_pair(o, o, 0x0C030C01u) ^ 0x64086408u) - bias);
       } else {
-        uint32_t raw[8];
+        // word g/2 of rows 2p, 2p+1 holds 8 nibbles (column 2b in the low nibble of byte b); this
+        // group is its bytes 2*(g%2) and 2*(g%2)+1
+        const uint32_t ua = s.w[2 * p][g / 2], ub = s.w[2 * p + 1][g / 2];
+        const uint32_t ea = ua & 0x0F0F0F0Fu, oa = (ua >> 4) & 0x0F0F0F0Fu;
+        const uint32_t eb = ub & 0x0F0F0F0Fu, ob = (ub >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
-        for (int r = 0; r < 8; r++) raw[r] = *reinterpret_cast<const uint32_t*>(W + ((int64_t)(k0 + r) * N + nc) / 2);
-#pragma unroll
-        for (int p = 0; p < 4; p++) {
-          // even columns (low nibbles) and odd columns (high nibbles) spread into bytes
-          const uint32_t ae = (raw[2 * p] & 0x0F0F0F0Fu) ^ 0x08080808u, ao = ((raw[2 * p] >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
-          const uint32_t be = (raw[2 * p + 1] & 0x0F0F0F0Fu) ^ 0x08080808u,
-                         bo = ((raw[2 * p + 1] >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;
-          v2h te[4], to[4];
-          pairs_from_bytes(ae, be, bias_bits, te);
-          pairs_from_bytes(ao, bo, bias_bits, to);
-#pragma unroll
-          for (int j = 0; j < 4; j++) {
-            wp[2 * j][p] = te[j];
-            wp[2 * j + 1][p] = to[j];
-          }
-        }
-      }
-      // block scales of these 8 columns
-      const uint4 sraw = *reinterpret_cast<const uint4*>(Ws + (int64_t)(k0 / 32) * N + nc);
-      float s[kCPL];
-      {
-        const uint32_t sv[4] = {sraw.x, sraw.y, sraw.z, sraw.w};
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-          const v2h h = as_v2h(sv[j]);
-          s[2 * j] = (float)h[0];
-          s[2 * j + 1] = (float)h[1];
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < M; m++) {
-        const uint4 xr = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + k0);
-        const v2h xp[4] = {as_v2h(xr.x), as_v2h(xr.y), as_v2h(xr.z), as_v2h(xr.w)};
-#pragma unroll
-        for (int c = 0; c < kCPL; c++) {
-          float t = 0.0f;
-#pragma unroll
-          for (int p = 0; p < 4; p++) t = __builtin_amdgcn_fdot2(xp[p], wp[c][p], t, false);
-          acc[m][c] = __builtin_fmaf(s[c], t, acc[m][c]);
+        for (int h = 0; h < 2; h++) {
+          const uint32_t b = 2u * (uint32_t)(g % 2) + (uint32_t)h;
+          const uint32_t sel = b | (0x0Cu << 8) | ((4u + b) << 16) | (0x0Cu << 24);
+          f[2 * h][p] = __builtin_bit_cast(uint32_t, as_v2h(pick_pair(eb, ea, sel) ^ 0x64086408u) - bias);
+          f[2 * h + 1][p] = __builtin_bit_cast(uint32_t, as_v2h(pick_pair(ob, oa, sel) ^ 0x64086408u) - bias);
         }
       }
     }
   }
+#pragma unroll
+  for (int e = 0; e < 4; e++) frag[e] = __builtin_bit_cast(v8h, make_uint4(f[e][0], f[e][1], f[e][2], f[e][3]));
+}
 
-  // Sum the 8 row phases of this wave (lane bits 3..5), then the waves through LDS.
+// One block: per group of 4 columns, the 4 block products (MFMA, fp32) scaled by their columns'
+// fp16 block scales and added to the accumulators.
+template <bool I8, int C>
+MX_DEV void compute_stage(const Stage<I8, C>& s, const v8h xa, v4f (&acc)[C]) {
 #pragma unroll
-  for (int m = 0; m < M; m++)
+  for (int g = 0; g < C / 4; g++) {
+    v8h frag[4];
+    weights_to_frags<I8, C>(s, g, frag);
+    v4f d[4];  // independent products first, so the MFMAs pipeline
 #pragma unroll
-    for (int c = 0; c < kCPL; c++) {
-      float v = acc[m][c];
-      v += __shfl_xor(v, 8);
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      acc[m][c] = v;
+    for (int e = 0; e < 4; e++) d[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, frag[e], v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int j = 4 * g + e;
+      const v2h sp = as_v2h(s.sc[j / 2]);
+      const float sj = (float)sp[j & 1];
+#pragma unroll
+      for (int v = 0; v < 4; v++) acc[j][v] = __builtin_fmaf(sj, d[e][v], acc[j][v]);
     }
-  if (lane < kCG) {
+  }
+}
+
+// Single-pass kernel (no workspace): one workgroup owns a column strip of TW = 16*C columns over
+// all of K. Its W waves take every W-th 32-row block, each wave covering all TW columns, so with 8
+// (int8) or 16 (int4) columns per lane a load instruction reads whole 128-byte lines of 4 rows.
+// The waves' sums meet in LDS and the workgroup writes y.
+constexpr int kXsMax = 16384;  // activation halfs staged in LDS per workgroup (M * K)
+
+template <bool I8, int C, int W, int P, bool XL>
+__global__ __launch_bounds__(W * 64) void matvec_kernel(const _Float16* __restrict__ x, const uint8_t* __restrict__ Wt,
+                                                        const _Float16* __restrict__ Ws, _Float16* __restrict__ y,
+                                                        int M, int N, int K) {
+  constexpr int TW = 16 * C;
+  constexpr int kRedFloats = W * 8 * TW;
+  constexpr int kLdsFloats = kRedFloats > kXsMax / 2 ? kRedFloats : kXsMax / 2;
+  __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];  // x staging, then the wave sums
+  _Float16* xs = reinterpret_cast<_Float16*>(lds);
+  float(*red)[8][TW] = reinterpret_cast<float(*)[8][TW]>(lds);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15, q = lane >> 4;
+  const int strip = blockIdx.x, kb0 = 0, kb1 = K / 32;
+  const int KC = K;
+  const int n0 = strip * TW, col = n0 + C * i;
+
+  if constexpr (XL) {  // activations x[m][0 .. K) -> xs[m*K + ...]
+    for (int e = 8 * threadIdx.x; e < M * KC; e += 8 * W * 64) {
+      const int m = e / KC, kk = e - m * KC;
+      *reinterpret_cast<uint4*>(&xs[e]) = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + 32 * kb0 + kk);
+    }
+  }
+  // N is a multiple of C, so a lane's columns are all in or all out; lanes past N load the last
+  // C columns, lanes past M the last activation row: their results are never stored.
+  const uint32_t cl = (uint32_t)(col < N ? col : N - C);
+  const int xrow = i < M ? i : M - 1;
+  LaneOffsets lo;
+  lo.w = I8 ? 8u * q * (uint32_t)N + cl : (8u * q * (uint32_t)N + cl) / 2u;
+  lo.x = 2u * ((uint32_t)xrow * (uint32_t)K + 8u * q);
+  lo.s = 2u * cl;
+  const rsrc_t xr = make_rsrc(x, XL ? 0u : 2u * (uint32_t)M * (uint32_t)K);
+  const _Float16* xl = xs + xrow * KC + 8 * q;  // XL: + 32*(blk - kb0) is the lane's x fragment
+
+  v4f acc[C];
 #pragma unroll
-    for (int m = 0; m < M; m++)
+  for (int j = 0; j < C; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  if constexpr (XL) __syncthreads();
+
+  // this wave's blocks: kb0 + wave + W*u, u < cnt
+  const int cnt = kb1 - kb0 > wave ? (kb1 - kb0 - wave + W - 1) / W : 0;
+  auto blk = [&](int u) { return kb0 + wave + W * u; };
+  auto xfrag = [&](const Stage<I8, C>& st, int u) {
+    if constexpr (XL) return *reinterpret_cast<const v8h*>(xl + 32 * (wave + W * u));
+    else return __builtin_bit_cast(v8h, st.xa);
+  };
+  Stage<I8, C> ring[P];
+  int t = 0;
+  if (cnt >= 2 * P) {
+    // Steady state: every slot is computed and refilled in order, with no conditions, so the
+    // loads of a slot are always followed by those of the other P-1 slots and each compute waits
+    // only for its own slot's loads.
 #pragma unroll
-      for (int c = 0; c < kCPL; c++) red[wave][m][cg * kCPL + c] = acc[m][c];
+    for (int s = 0; s < P; s++) {
+      load_stage<I8, C, !XL>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(s), lo);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    do {
+#pragma unroll
+      for (int s = 0; s < P; s++) {
+        compute_stage<I8, C>(ring[s], xfrag(ring[s], t + s), acc);
+        load_stage<I8, C, !XL>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(t + s + P), lo);
+        // keep the refill here: left alone, the scheduler sinks every refill below all P computes
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      t += P;
+    } while (t + 2 * P <= cnt);
+  } else {
+#pragma unroll
+    for (int s = 0; s < P; s++)
+      if (s < cnt) load_stage<I8, C, !XL>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(s), lo);
+  }
+  // drain: fewer than 2P blocks left, the first P of them (those < cnt) already in the ring
+#pragma unroll
+  for (int s = 0; s < P; s++) {
+    if (t + s < cnt) {
+      compute_stage<I8, C>(ring[s], xfrag(ring[s], t + s), acc);
+      if (t + s + P < cnt) load_stage<I8, C, !XL>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(t + s + P), lo);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < P; s++)
+    if (t + P + s < cnt) compute_stage<I8, C>(ring[s], xfrag(ring[s], t + P + s), acc);
+
+  // acc[j][v] = this wave's share of y[4q+v][col+j]; rows >= M and columns >= N are dropped.
+  if constexpr (XL) __syncthreads();  // every wave is done with xs before red overwrites it
+  if (q < 2) {
+#pragma unroll
+    for (int j = 0; j < C; j++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) red[wave][4 * q + v][C * i + j] = acc[j][v];
   }
   __syncthreads();
-  for (int o = tid; o < M * kTW; o += kThreads) {
-    const int m = o / kTW, col = o % kTW;
+  for (int o = threadIdx.x; o < M * TW; o += W * 64) {
+    const int m = o / TW, c = o % TW;
+    if (n0 + c >= N) continue;
     float v = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; w++) v += red[w][m][col];
-    if (n0 + col < N) y[(int64_t)m * N + n0 + col] = (_Float16)v;
+    for (int w = 0; w < W; w++) v += red[w][m][c];
+    y[(int64_t)m * N + n0 + c] = (_Float16)v;
   }
+}
+
+constexpr int kMaxSplits = 16;
+
+// ---------------------------------------------------------------------------------------------
+// Split-K kernel with LDS staging. HBM streams best when a load instruction covers long runs of
+// bytes (16 bytes per lane, 256-byte runs of 4 rows); the MFMA operand layout wants 8 rows of a
+// few adjacent columns per lane. Direct global->LDS loads decouple the two:
+//  - A workgroup (8 waves) owns a strip of 256 bytes of every row (256 int8 / 512 int4 columns)
+//    and the 32-row blocks [kb0, kb1) of its K split.
+//  - A stage is one block: 8 chunks of 4 rows x 256 bytes plus the block's scale row, copied
+//    straight into an R-stage LDS ring. Chunks are padded to 1056 bytes, so the fragment reads
+//    below hit 4 disjoint bank groups.
+//  - Waves (cg, par), cg < 4, par < 2: stages go in pairs (a step); the waves of parity par
+//    compute stage 2u+par of step u, wave cg the strip's columns [16*C*cg, 16*C*(cg+1)) (64 bytes
+//    of each row). Lane (i, q) reads the dword of rows 8q..8q+7 holding its C columns, exactly
+//    the register layout of the single-pass kernel, and the same convert / MFMA / scale code runs.
+//  - The activations of the split's K range sit in LDS (staged once).
+// ---------------------------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+constexpr int kLChunk = 4 * 256 + 32;        // LDS bytes of 4 weight rows, padded
+constexpr int kLStage = 8 * kLChunk + 1024;  // a block: 8 chunks + its scale row (<= 1 KB)
+constexpr int kXsLds = 8192;                 // activation halfs staged per workgroup
+
+// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
+MX_DEV void wait_vm_n(int n) {
+  switch (n) {
+#define MX_W(k) \
+  case k: __builtin_amdgcn_s_waitcnt(((k) & 0xF) | 0x0F70 | ((((k) >> 4) & 3) << 14)); break;
+    MX_W(0) MX_W(1) MX_W(2) MX_W(3) MX_W(4) MX_W(5) MX_W(6) MX_W(7) MX_W(8) MX_W(9) MX_W(10) MX_W(11)
+    MX_W(12) MX_W(13) MX_W(14) MX_W(15) MX_W(16) MX_W(17) MX_W(18) MX_W(19) MX_W(20) MX_W(21)
+#undef MX_W
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+}
+// Workgroup barrier without the fences of __syncthreads() (which would wait for every queued
+// direct copy); the waits the ring needs are explicit.
+MX_DEV void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+MX_DEV void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0) only
+
+// The lane's 8 fragment dwords (rows 8q..8q+7 of a stage: chunk offsets 0, 256, 512, 768, then
+// the next chunk) and its C scales, read from the ring with one lgkmcnt wait. Written as inline
+// assembly because the compiler cannot tell these reads from the ring slot that the direct copies
+// queued just before are filling, and would otherwise wait for every queued copy (vmcnt(0)) here.
+// The outputs are early-clobber: a read's destination must not be an address register of a later
+// read in the block (its data may land before that read issues).
+template <bool I8, int C>
+MX_DEV void read_stage(Stage<I8, C>& sg, uint32_t aw, uint32_t as) {
+  static_assert(kLChunk == 1056 && Stage<I8, C>::kWordsPerRow == 1, "offsets below");
+  if constexpr (C == 4) {
+    uint64_t sc;
+    asm volatile(
+        "ds_read_b32 %0, %9 offset:0\n"
+        "ds_read_b32 %1, %9 offset:256\n"
+        "ds_read_b32 %2, %9 offset:512\n"
+        "ds_read_b32 %3, %9 offset:768\n"
+        "ds_read_b32 %4, %9 offset:1056\n"
+        "ds_read_b32 %5, %9 offset:1312\n"
+        "ds_read_b32 %6, %9 offset:1568\n"
+        "ds_read_b32 %7, %9 offset:1824\n"
+        "ds_read_b64 %8, %10\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(sg.w[0][0]), "=&v"(sg.w[1][0]), "=&v"(sg.w[2][0]), "=&v"(sg.w[3][0]), "=&v"(sg.w[4][0]),
+          "=&v"(sg.w[5][0]), "=&v"(sg.w[6][0]), "=&v"(sg.w[7][0]), "=&v"(sc)
+        : "v"(aw), "v"(as));
+    sg.sc[0] = (uint32_t)sc;
+    sg.sc[1] = (uint32_t)(sc >> 32);
+  } else {
+    static_assert(C == 8, "4 or 8 columns per lane");
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    u4 sc;
+    asm volatile(
+        "ds_read_b32 %0, %9 offset:0\n"
+        "ds_read_b32 %1, %9 offset:256\n"
+        "ds_read_b32 %2, %9 offset:512\n"
+        "ds_read_b32 %3, %9 offset:768\n"
+        "ds_read_b32 %4, %9 offset:1056\n"
+        "ds_read_b32 %5, %9 offset:1312\n"
+        "ds_read_b32 %6, %9 offset:1568\n"
+        "ds_read_b32 %7, %9 offset:1824\n"
+        "ds_read_b128 %8, %10\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(sg.w[0][0]), "=&v"(sg.w[1][0]), "=&v"(sg.w[2][0]), "=&v"(sg.w[3][0]), "=&v"(sg.w[4][0]),
+          "=&v"(sg.w[5][0]), "=&v"(sg.w[6][0]), "=&v"(sg.w[7][0]), "=&v"(sc)
+        : "v"(aw), "v"(as));
+    sg.sc[0] = sc[0];
+    sg.sc[1] = sc[1];
+    sg.sc[2] = sc[2];
+    sg.sc[3] = sc[3];
+  }
+}
+
+template <bool I8, int R>
+__global__ __launch_bounds__(512) void matvec_lds_kernel(const _Float16* __restrict__ x, const uint8_t* __restrict__ Wt,
+                                                         const _Float16* __restrict__ Ws, _Float16* __restrict__ y,
+                                                         float* __restrict__ part, unsigned* __restrict__ counters,
+                                                         int M, int N, int K, int S) {
+  constexpr int C = I8 ? 4 : 8, TW = I8 ? 256 : 512;  // columns per lane, per strip
+  constexpr int SB = 2 * TW;                          // scale bytes of a strip row
+  constexpr int SLANES = SB / 4 / 16;                 // lanes per wave copying scales (8 or 16)
+  constexpr int kLoads = 3;                           // direct copies per wave per step
+  constexpr int RS = R / 2;                           // ring slots of 2 stages (a step)
+  static_assert(R % 2 == 0 && RS >= 2 && kLoads * (RS - 2) <= 21, "wait_vm_n range");
+  static_assert(R * kLStage >= 4 * 64 * 4 * C * 4, "the parity-1 sums fit in the ring");
+  __shared__ __attribute__((aligned(16))) char ring[R * kLStage];
+  __shared__ __attribute__((aligned(16))) _Float16 xs[kXsLds];
+  __shared__ int s_last;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int cg = wave & 3, par = wave >> 2;  // column group, stage parity
+  const int i = lane & 15, q = lane >> 4;
+  const int strip = blockIdx.x, sk = blockIdx.y, nblk = K / 32;
+  const int kb0 = (int)((int64_t)sk * nblk / S), kb1 = (int)((int64_t)(sk + 1) * nblk / S);
+  const int nb = kb1 - kb0, KC = 32 * nb, nsteps = (nb + 1) / 2;
+  const int n0 = strip * TW, col = n0 + 16 * C * cg + C * i;
+  const uint32_t row_bytes = I8 ? (uint32_t)N : (uint32_t)N / 2;
+
+  // activations x[m][32*kb0 .. 32*kb1) -> xs[m*KC + ...]
+  for (int e = 8 * threadIdx.x; e < M * KC; e += 8 * 512) {
+    const int m = e / KC, kk = e - m * KC;
+    *reinterpret_cast<uint4*>(&xs[e]) = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + 32 * kb0 + kk);
+  }
+
+  // Copy offsets. Bytes past the end of a row (last strip) are clamped back into the row; the
+  // columns they feed are never stored. Row bytes and 2N are multiples of 16.
+  uint32_t colb = (uint32_t)strip * 256u + 16u * (uint32_t)i;
+  if (colb > row_bytes - 16u) colb = row_bytes - 16u;
+  const uint32_t voff0 = (4u * (2u * cg) + (uint32_t)q) * row_bytes + colb;
+  const uint32_t voff1 = voff0 + 4u * row_bytes;
+  uint32_t scb = 2u * (uint32_t)n0 + (uint32_t)cg * (SB / 4) + 16u * (uint32_t)lane;
+  if (scb > 2u * (uint32_t)N - 16u) scb = 2u * (uint32_t)N - 16u;
+
+  // Step u: wave (cg, par) copies chunks 2cg, 2cg+1 and scale quarter cg of stage 2u+par. A stage
+  // past the split (odd block count) re-reads the split's last block, so every wave queues the
+  // same number of copies per step and the vmcnt accounting stays exact.
+  auto issue = [&](int u) {
+    const int stage = 2 * u + par, blk = kb0 + (stage < nb ? stage : nb - 1);
+    char* st = ring + ((u % RS) * 2 + par) * kLStage;
+    const rsrc_t wr = make_rsrc(Wt + (int64_t)blk * 32 * row_bytes, 32u * row_bytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(st + (2 * cg) * kLChunk), 16, voff0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(st + (2 * cg + 1) * kLChunk), 16, voff1, 0, 0, 0);
+    const rsrc_t sr = make_rsrc(Ws + (int64_t)blk * N, 2u * (uint32_t)N);
+    if (lane < SLANES)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(st + 8 * kLChunk + cg * (SB / 4)), 16, scb, 0, 0, 0);
+  };
+
+  const int xrow = i < M ? i : M - 1;
+  const _Float16* xl = xs + xrow * KC + 8 * q;
+  // LDS byte addresses of the lane's fragment dword (rows 8q.. of this parity's stage in ring
+  // slot 0) and of its scales
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(lds_ptr_t)ring + (uint32_t)(par * kLStage);
+  const uint32_t lds_w = ring0 + (uint32_t)(2 * q * kLChunk + cg * 64 + 4 * i);
+  const uint32_t lds_s = ring0 + (uint32_t)(8 * kLChunk + 2 * (16 * C * cg + C * i));
+  v4f acc[C];
+#pragma unroll
+  for (int j = 0; j < C; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  __syncthreads();  // xs complete (before any direct copy is queued: this barrier waits for vmcnt(0))
+#pragma unroll
+  for (int u = 0; u < RS - 1; u++)
+    if (u < nsteps) issue(u);
+
+  for (int u = 0; u < nsteps; u++) {
+    const int after = nsteps - 1 - u < RS - 2 ? nsteps - 1 - u : RS - 2;  // steps queued after u
+    wait_vm_n(kLoads * after);  // this wave's copies of step u have landed ...
+    wait_lds();                 // ... and its reads of step u-1 are done
+    raw_barrier();              // every wave: step u visible, slot (u-1)%RS free
+    if (u + RS - 1 < nsteps) issue(u + RS - 1);
+    if (2 * u + par < nb) {
+      Stage<I8, C> sg;
+      const uint32_t so = (uint32_t)((u % RS) * 2 * kLStage);
+      read_stage<I8, C>(sg, lds_w + so, lds_s + so);
+      compute_stage<I8, C>(sg, *reinterpret_cast<const v8h*>(xl + 32 * (2 * u + par)), acc);
+    }
+  }
+
+  // the two parities' sums meet in LDS (the ring is free once every wave is past its last read)
+  wait_lds();
+  raw_barrier();
+  float* red = reinterpret_cast<float*>(ring) + (cg * 64 + lane) * (4 * C);
+  if (par == 1) {
+#pragma unroll
+    for (int j = 0; j < C; j++) *reinterpret_cast<v4f*>(red + 4 * j) = acc[j];
+  }
+  __syncthreads();
+  if (par == 0) {
+#pragma unroll
+    for (int j = 0; j < C; j++) acc[j] += *reinterpret_cast<const v4f*>(red + 4 * j);
+  }
+
+  // acc[j][v] (parity-0 waves) = the split's y[4q+v][col+j]; rows >= M and columns >= N are
+  // dropped.
+  if (S == 1) {
+    if (par == 0 && col < N) {
+#pragma unroll
+      for (int v = 0; v < 4; v++) {
+        const int m = 4 * q + v;
+        if (m < M) {
+#pragma unroll
+          for (int g = 0; g < C / 4; g++) {
+            v4h o;
+#pragma unroll
+            for (int e = 0; e < 4; e++) o[e] = (_Float16)acc[4 * g + e][v];
+            *reinterpret_cast<v4h*>(y + (int64_t)m * N + col + 4 * g) = o;
+          }
+        }
+      }
+    }
+    return;
+  }
+  // Cross-split sum. The partial tile is written through to memory (system-scope atomic stores of
+  // column pairs, so no XCD's cache keeps a stale copy) and acknowledged (vmcnt(0)) before the
+  // strip's counter is incremented; the workgroup that takes the counter from S-1 (back to 0) is
+  // the last one and adds the S partials, read with system-scope atomic loads, in split order.
+  if (par == 0 && col < N) {
+#pragma unroll
+    for (int v = 0; v < 4; v++) {
+      const int m = 4 * q + v;
+      if (m < M) {
+#pragma unroll
+        for (int g = 0; g < C / 4; g++) {
+          uint64_t* dst = reinterpret_cast<uint64_t*>(part + ((int64_t)sk * M + m) * N + col + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 2; e++) {
+            // element copies first: a bit cast of an ext-vector element read element 0 here
+            const float lo = acc[4 * g + 2 * e][v], hi = acc[4 * g + 2 * e + 1][v];
+            const uint64_t pr = (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+            __hip_atomic_store(dst + e, pr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          }
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicInc(&counters[strip], (unsigned)(S - 1)) == (unsigned)(S - 1);
+  __syncthreads();
+  if (!s_last) return;
+  // Each thread sums up to two 4-column groups (M * TW / 4 <= 1024 = 2 * 512), with every split's
+  // load of both groups in flight at once (8-byte system-scope loads), in split order.
+  {
+    constexpr int kG = 2;
+    uint64_t v[kG][kMaxSplits][2];
+    int og[kG];
+#pragma unroll
+    for (int g = 0; g < kG; g++) {
+      const int o = 4 * (threadIdx.x + 512 * g), m = o / TW, c = n0 + (o - m * TW);
+      og[g] = (o < M * TW && c < N) ? o : -1;
+      if (og[g] < 0) continue;
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; sp++)
+        if (sp < S) {
+          const uint64_t* src = reinterpret_cast<const uint64_t*>(part + ((int64_t)sp * M + m) * N + c);
+          v[g][sp][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+          v[g][sp][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < kG; g++) {
+      if (og[g] < 0) continue;
+      const int o = og[g], m = o / TW, c = n0 + (o - m * TW);
+      float sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int sp = 0; sp < kMaxSplits; sp++)
+        if (sp < S) {
+#pragma unroll
+          for (int e = 0; e < 2; e++) {
+            sum[2 * e] += __builtin_bit_cast(float, (uint32_t)v[g][sp][e]);
+            sum[2 * e + 1] += __builtin_bit_cast(float, (uint32_t)(v[g][sp][e] >> 32));
+          }
+        }
+      v4h h;
+#pragma unroll
+      for (int e = 0; e < 4; e++) h[e] = (_Float16)sum[e];
+      *reinterpret_cast<v4h*>(y + (int64_t)m * N + c) = h;
+    }
+  }
+}
+
+// Single-pass kernel shape (no workspace): 8 (int8) or 16 (int4) columns per lane, so a strip is
+// 128 bytes of every row; 8 waves per workgroup, 4 (int8) or 3 (int4) blocks of loads in flight
+// per wave.
+constexpr int kC8 = 8, kC4 = 16, kW = 8, kP8 = 4, kP4 = 3;
+// Split kernel: an R-deep LDS ring; K is split until about kTargetWGs workgroups run.
+constexpr int kR = 8, kTargetWGs = 256;
+
+// Workspace layout: a fixed counter region (one counter per column strip, room for the largest
+// strip count any shape can have), then the fp32 partials [S][M][N]. Counters never share bytes
+// with partials of any shape, so a workspace whose counters one call left at zero is valid for
+// every later call.
+constexpr size_t kCounterBytes = 16384;
+static_assert(kCounterBytes / 4 >= MX_MAX_DIM / 256, "a counter per int8 strip of the widest matrix");
+
+struct SplitPlan {
+  int S, NS;     // K splits, column strips of the split kernel (S == 1: single-pass kernel)
+  size_t bytes;  // workspace bytes (0 when S == 1)
+};
+
+SplitPlan split_plan(int M, int N, int K, bool int8) {
+  const int tw = int8 ? 256 : 512, nblk = K / 32;
+  SplitPlan p;
+  p.NS = (N + tw - 1) / tw;
+  int S = kTargetWGs / p.NS;
+  if (S > kMaxSplits) S = kMaxSplits;
+  if (S > nblk / 4) S = nblk / 4;  // at least 4 blocks per split
+  if (S < 2) {                     // not worth splitting: single pass
+    p.S = 1;
+    p.bytes = 0;
+    return p;
+  }
+  while (M * 32 * ((nblk + S - 1) / S) > kXsLds) S++;  // the split's activations fit in LDS
+  if (S > kMaxSplits) {                                 // too many: single pass
+    p.S = 1;
+    p.bytes = 0;
+    return p;
+  }
+  p.S = S;
+  p.bytes = kCounterBytes + (size_t)S * M * N * 4;
+  return p;
 }
 
 template <bool I8>
-int launch_m(int M, int N, int K, const void* x, const void* W, const void* Ws, void* y, hipStream_t st) {
-  const dim3 grid((unsigned)((N + kTW - 1) / kTW)), block(kThreads);
-  auto xx = (const _Float16*)x;
-  auto ww = (const uint8_t*)W;
-  auto ss = (const _Float16*)Ws;
-  auto yy = (_Float16*)y;
-  switch (M) {
-    case 1: hipLaunchKernelGGL((matvec_kernel<1, I8>), grid, block, 0, st, xx, ww, ss, yy, N, K); break;
-    case 2: hipLaunchKernelGGL((matvec_kernel<2, I8>), grid, block, 0, st, xx, ww, ss, yy, N, K); break;
-    case 3: hipLaunchKernelGGL((matvec_kernel<3, I8>), grid, block, 0, st, xx, ww, ss, yy, N, K); break;
-    case 4: hipLaunchKernelGGL((matvec_kernel<4, I8>), grid, block, 0, st, xx, ww, ss, yy, N, K); break;
-    case 5: hipLaunchKernelGGL((matvec_kernel<5, I8>), grid, block, 0, st, xx, ww, ss, yy, N, K); break;
-    case 6: hipLaunchKernelGGL((matvec_kernel<6, I8>), grid, block, 0, st, xx, ww, ss, yy, N, K); break;
-    case 7: hipLaunchKernelGGL((matvec_kernel<7, I8>), grid, block, 0, st, xx, ww, ss, yy, N, K); break;
-    case 8: hipLaunchKernelGGL((matvec_kernel<8, I8>), grid, block, 0, st, xx, ww, ss, yy, N, K); break;
-    default: return MX_ERR_SHAPE;
+int launch(int M, int N, int K, const void* x, const void* W, const void* Ws, void* y, void* ws, size_t ws_bytes,
+           hipStream_t st) {
+  const SplitPlan sp = split_plan(M, N, K, I8);
+  if (sp.S > 1 && ws && ws_bytes >= sp.bytes) {
+    unsigned* counters = (unsigned*)ws;
+    float* part = (float*)((char*)ws + kCounterBytes);
+    hipLaunchKernelGGL((matvec_lds_kernel<I8, kR>), dim3((unsigned)sp.NS, (unsigned)sp.S), dim3(512), 0, st,
+                       (const _Float16*)x, (const uint8_t*)W, (const _Float16*)Ws, (_Float16*)y, part, counters, M, N,
+                       K, sp.S);
+    return launch_status();
   }
+  constexpr int C = I8 ? kC8 : kC4, P = I8 ? kP8 : kP4;
+  const int NS1 = (N + 16 * C - 1) / (16 * C);
+  const bool xl = (int64_t)M * K <= kXsMax;
+  if (xl)
+    hipLaunchKernelGGL((matvec_kernel<I8, C, kW, P, true>), dim3((unsigned)NS1), dim3(kW * 64), 0, st,
+                       (const _Float16*)x, (const uint8_t*)W, (const _Float16*)Ws, (_Float16*)y, M, N, K);
+  else
+    hipLaunchKernelGGL((matvec_kernel<I8, C, kW, P, false>), dim3((unsigned)NS1), dim3(kW * 64), 0, st,
+                       (const _Float16*)x, (const uint8_t*)W, (const _Float16*)Ws, (_Float16*)y, M, N, K);
   return launch_status();
 }
 
 }  // namespace
 
 namespace mx {
-int matvec_launch(int M, int N, int K, const void* x, const void* W, bool int8, const void* Ws, void* y,
-                  hipStream_t stream) {
-  return int8 ? launch_m<true>(M, N, K, x, W, Ws, y, stream) : launch_m<false>(M, N, K, x, W, Ws, y, stream);
+size_t matvec_workspace(int M, int N, int K, bool int8) { return split_plan(M, N, K, int8).bytes; }
+
+int matvec_launch(int M, int N, int K, const void* x, const void* W, bool int8, const void* Ws, void* y, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+  return int8 ? launch<true>(M, N, K, x, W, Ws, y, ws, ws_bytes, stream)
+              : launch<false>(M, N, K, x, W, Ws, y, ws, ws_bytes, stream);
 }
 }  // namespace mx

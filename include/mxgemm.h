@@ -28,6 +28,7 @@
 #ifndef MXGEMM_H
 #define MXGEMM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -121,10 +122,23 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
  *   Ws binary16 [K/32][N]   y binary16 [M][N]
  * Shape rules: 1 <= M <= 8; K % 32 == 0, 32 <= K <= MX_MAX_DIM; 1 <= N <= MX_MAX_DIM;
  * N % 16 == 0 (int8) or N % 32 == 0 (int4). Device pointers, 16-byte aligned.
- * Uses no scratch memory: every output is finished by one workgroup.
+ *
+ * Workspace: at decode shapes K is split across workgroups. Their fp32 partial sums and one
+ * counter per column strip live in a caller-owned device buffer of mxmatvec_workspace_size()
+ * bytes (16-byte aligned). The buffer must be zero-filled once before its first use (hipMemset,
+ * or any zeroed allocation); every call leaves its counters at zero again, so the buffer stays
+ * valid for any later call whose requirement it meets. The last workgroup of each strip adds the
+ * partial sums in a fixed order, so results are deterministic. Calls that may overlap in time
+ * (different streams) need separate workspaces. With workspace == NULL, or workspace_bytes below
+ * the requirement, K is not split across workgroups and the buffer is not touched (same results
+ * up to fp32 summation order; slower when N is small compared with the number of compute units).
  */
 int mxmatvec_run(int M, int N, int K, const void* x, const void* W, int fw, const void* Ws, void* y,
-                 void* stream);
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mxmatvec_run uses for this shape (0: none needed, or an invalid shape). The
+ * requirement never decreases as M grows for fixed N, K and fw. */
+size_t mxmatvec_workspace_size(int M, int N, int K, int fw);
 
 /* ------------------------------------------------------------------------------------------ */
 /* Codecs on the GPU (bit-exact with the host codecs below).                                    */

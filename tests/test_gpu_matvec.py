@@ -3,7 +3,10 @@
 Weights W [K][N] are drawn 0.02*N(0,1) and quantised by the GPU codec (checked bit-exact against
 the oracle's quantiser first); x is fp16 from N(0,1). Every output is compared with the oracle's
 fp64 block formula under |y - y_ref| <= 2^-10 |y_ref| + 1e-3 sqrt(K) R, R the rms of |x_mk w_kn|
-over the dequantised weights.
+over the dequantised weights. Both paths run: K split across workgroups and unsplit (no
+workspace). The split path shares one workspace, zeroed once, across every case in this file, so
+each case also checks that the calls before it left the workspace's counters at zero; it is called
+twice per case to check that it is deterministic.
 """
 import numpy as np
 import pytest
@@ -15,7 +18,20 @@ from gpu_common import dev, empty, gpu_int_pack, host, require_gpu, say
 pytestmark = pytest.mark.gpu
 
 
-def run_case(orc, api, fw, M, K, N, seed_w, seed_x):
+_WS = {}
+
+
+def workspace(api, M, N, K, fw):
+    """The shared workspace, zeroed once (and again only when it must grow)."""
+    need = api.mxmatvec_workspace_size(M, N, K, fw)
+    if need == 0:
+        return None
+    if _WS.get("buf") is None or _WS["buf"].numel() < need:
+        _WS["buf"] = torch.zeros(max(need, 8 << 20), dtype=torch.uint8, device="cuda")
+    return _WS["buf"]
+
+
+def run_case(orc, api, fw, M, K, N, seed_w, seed_x, path="split"):
     w = synth.normal((K, N), 0.02, seed_w)
     x = synth.normal((8, K), 1.0, seed_x).astype(np.float16)[:M]
     W, Ws = gpu_int_pack(api, fw, w)
@@ -23,8 +39,14 @@ def run_case(orc, api, fw, M, K, N, seed_w, seed_x):
     oW = q.view(np.uint8) if fw == api.MX_INT8 else orc.pack_int4(q)
     assert np.array_equal(host(W), oW) and np.array_equal(host(Ws).view(np.uint16), s.view(np.uint16))
     y = empty((M, N), torch.float16)
-    api.mxmatvec_run(M, N, K, dev(x), W, fw, Ws, y)
-    got = host(y).astype(np.float64)
+    ws = workspace(api, M, N, K, fw) if path == "split" else None
+    xd = dev(x)
+    api.mxmatvec_run(M, N, K, xd, W, fw, Ws, y, ws)
+    got16 = host(y).copy()
+    if ws is not None:      # a second call: the same bits
+        api.mxmatvec_run(M, N, K, xd, W, fw, Ws, y, ws)
+        assert np.array_equal(host(y).view(np.uint16), got16.view(np.uint16)), "split path not repeatable"
+    got = got16.astype(np.float64)
     ref = orc.matvec(fw, x, oW, s, K, N)
     wdeq = orc.dequant(fw, oW, s, K, N)
     R = orc.rms_ab(x.astype(np.float64), wdeq)
@@ -32,25 +54,28 @@ def run_case(orc, api, fw, M, K, N, seed_w, seed_x):
     return ok, ratio, bad
 
 
+@pytest.mark.parametrize("path", ["split", "single"])
 @pytest.mark.parametrize("fw", [32, 33])
 @pytest.mark.parametrize("M", [1, 8])
-def test_matvec_decode_shape_full(orc, fw, M):
+def test_matvec_decode_shape_full(orc, fw, M, path):
     """K=4096, N=14336 at M=1 and M=8: every output."""
     api = require_gpu()
-    say(f"matvec fw={fw} M={M} full size")
+    say(f"matvec fw={fw} M={M} full size path={path}")
     ok, ratio, bad = run_case(orc, api, fw, M, 4096, 14336, synth.seed_for(synth.MATVEC, 1),
-                              synth.seed_for(synth.MATVEC, 0))
+                              synth.seed_for(synth.MATVEC, 0), path)
     say(f"worst err/bound {ratio:.3f}")
     assert ok, (ratio, bad)
 
 
+@pytest.mark.parametrize("path", ["split", "single"])
 @pytest.mark.parametrize("fw", [32, 33])
 @pytest.mark.parametrize("M,K,N", [(1, 32, 32), (2, 64, 96), (3, 96, 160), (5, 4096, 64), (7, 1024, 1056),
-                                   (8, 160, 4128), (4, 8192, 512), (6, 544, 14336)])
-def test_matvec_ragged(orc, fw, M, K, N):
+                                   (8, 160, 4128), (4, 8192, 512), (6, 544, 14336), (8, 32768, 96),
+                                   (1, 1024, 32768)])
+def test_matvec_ragged(orc, fw, M, K, N, path):
     api = require_gpu()
-    say(f"matvec fw={fw} M={M} K={K} N={N}")
-    ok, ratio, bad = run_case(orc, api, fw, M, K, N, 7 * K + N, 3 * M + K)
+    say(f"matvec fw={fw} M={M} K={K} N={N} path={path}")
+    ok, ratio, bad = run_case(orc, api, fw, M, K, N, 7 * K + N, 3 * M + K, path)
     assert ok, (ratio, bad)
 
 
@@ -73,3 +98,24 @@ def test_matvec_zero_block_and_repeat(orc):
     ok, ratio, bad = orc.check(first.astype(np.float64), ref, K,
                                orc.rms_ab(x.astype(np.float64), orc.dequant(32, q.view(np.uint8), s, K, N)))
     assert ok, (ratio, bad)
+
+
+def test_matvec_small_workspace_falls_back(orc):
+    """A workspace below the requirement runs the single-pass kernel: still within the bound."""
+    api = require_gpu()
+    M, K, N = 8, 4096, 1024
+    need = api.mxmatvec_workspace_size(M, N, K, api.MX_INT8)
+    say(f"matvec small workspace need={need}")
+    assert need > 0
+    w = synth.normal((K, N), 0.02, 11)
+    x = synth.normal((M, K), 1.0, 12).astype(np.float16)
+    W, Ws = gpu_int_pack(api, api.MX_INT8, w)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    y = empty((M, N), torch.float16)
+    api.mxmatvec_run(M, N, K, dev(x), W, api.MX_INT8, Ws, y, ws, need - 16)
+    q, s = orc.int_quantize(api.MX_INT8, w)
+    ref = orc.matvec(api.MX_INT8, x, q.view(np.uint8), s, K, N)
+    R = orc.rms_ab(x.astype(np.float64), orc.dequant(32, q.view(np.uint8), s, K, N))
+    ok, ratio, bad = orc.check(host(y).astype(np.float64), ref, K, R)
+    assert ok, (ratio, bad)
+    assert int(ws.sum().item()) == 0      # untouched

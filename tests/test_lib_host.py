@@ -127,12 +127,13 @@ def test_validation_errors_without_gpu():
     assert lib.mxgemm_run(h, 17, 16, 16, 16, 16, None) == api.MX_ERR_ALIGN
     assert lib.mxgemm_destroy(h) == 0
     assert lib.mxgemm_destroy(None) == 0
-    assert lib.mxmatvec_run(9, 16, 32, 16, 16, 32, 16, 16, None) == api.MX_ERR_SHAPE       # M > 8
-    assert lib.mxmatvec_run(1, 16, 40, 16, 16, 32, 16, 16, None) == api.MX_ERR_SHAPE       # K % 32
-    assert lib.mxmatvec_run(1, 16, 32, 16, 16, 33, 16, 16, None) == api.MX_ERR_SHAPE       # int4 N % 32
-    assert lib.mxmatvec_run(1, 16, 32, 16, 16, 0, 16, 16, None) == api.MX_ERR_FORMAT
-    assert lib.mxmatvec_run(1, 16, 32, None, 16, 32, 16, 16, None) == api.MX_ERR_NULL
-    assert lib.mxmatvec_run(1, 16, 32, 16, 24, 32, 16, 16, None) == api.MX_ERR_ALIGN
+    assert lib.mxmatvec_run(9, 16, 32, 16, 16, 32, 16, 16, None, 0, None) == api.MX_ERR_SHAPE       # M > 8
+    assert lib.mxmatvec_run(1, 16, 40, 16, 16, 32, 16, 16, None, 0, None) == api.MX_ERR_SHAPE       # K % 32
+    assert lib.mxmatvec_run(1, 16, 32, 16, 16, 33, 16, 16, None, 0, None) == api.MX_ERR_SHAPE       # int4 N % 32
+    assert lib.mxmatvec_run(1, 16, 32, 16, 16, 0, 16, 16, None, 0, None) == api.MX_ERR_FORMAT
+    assert lib.mxmatvec_run(1, 16, 32, None, 16, 32, 16, 16, None, 0, None) == api.MX_ERR_NULL
+    assert lib.mxmatvec_run(1, 16, 32, 16, 24, 32, 16, 16, None, 0, None) == api.MX_ERR_ALIGN
+    assert lib.mxmatvec_run(1, 16, 32, 16, 16, 32, 16, 16, 8, 64, None) == api.MX_ERR_ALIGN          # workspace
     assert lib.mx_pack_run(0, 16, 4, 48, 16, 16, None) == api.MX_ERR_SHAPE
     assert lib.mx_pack_run(32, 16, 40, 16, 16, 16, None) == api.MX_ERR_SHAPE
     assert lib.mx_pack_run(16, 16, 32, 32, 16, 16, None) == api.MX_ERR_FORMAT
@@ -141,3 +142,17 @@ def test_validation_errors_without_gpu():
     buf = np.zeros(64, np.float32)
     assert lib.mx_pack_host(0, buf.ctypes.data, 1, 40, buf.ctypes.data, buf.ctypes.data) == api.MX_ERR_SHAPE
     assert lib.mx_pack_host(16, buf.ctypes.data, 1, 32, buf.ctypes.data, buf.ctypes.data) == api.MX_ERR_FORMAT
+
+
+def test_matvec_workspace_size():
+    """Split-K workspace: fp32 partials [S][M][N] (256-byte rounded) plus a counter per strip;
+    zero for invalid shapes, never decreasing in M."""
+    assert api.mxmatvec_workspace_size(9, 14336, 4096, api.MX_INT8) == 0
+    assert api.mxmatvec_workspace_size(1, 14336, 4096, 0) == 0
+    for fw in (api.MX_INT8, api.MX_INT4):
+        sizes = [api.mxmatvec_workspace_size(m, 14336, 4096, fw) for m in range(1, 9)]
+        assert sizes[0] > 0 and all(b >= a for a, b in zip(sizes, sizes[1:])), sizes
+        for m, b in enumerate(sizes, 1):
+            assert b >= 2 * m * 14336 * 4     # at least two splits at the decode shape
+    # a tiny K is never split
+    assert api.mxmatvec_workspace_size(8, 14336, 32, api.MX_INT8) == 0
