@@ -197,6 +197,18 @@ def main():
         t = timed(lambda i: api.mx_unpack_run(api.MX_E4M3, A8, S8, rows, cols, out, stream), args.steps, args.warmup)
         detail["unpack_e4m3_2048x4096"] = {"us": t * 1e3, "gbs": nbytes / (t * 1e-3) / 1e9}
 
+    # ---------------- plain device copy (HBM reference and traffic-counter calibration) ------------
+    if want("copy"):
+        log("timing device copy")
+        nbytes = 256 << 20
+        csrc = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        cdst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        csrc.fill_(1)
+        t = timed(lambda i: cdst.copy_(csrc), args.steps, args.warmup)
+        detail["device_copy_256MiB"] = {"us": t * 1e3, "gbs": 2 * nbytes / (t * 1e-3) / 1e9,
+                                        "bytes_read": nbytes, "bytes_written": nbytes}
+        del csrc, cdst
+
     # ---------------- CPU baseline: the oracle on a bounded sample ------------------------------
     cpu = None
     if not args.no_cpu_baseline:

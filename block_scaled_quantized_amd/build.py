@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmxgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "host_codec.cpp", "codec.hip", "mxgemm.hip", "matvec.hip"]
+SOURCES = ["api.cpp", "host_codec.cpp", "codec.hip", "mxgemm.hip", "mxgemm_ring.hip", "matvec.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument", f"-I{INCLUDE}", f"-I{CSRC}"]

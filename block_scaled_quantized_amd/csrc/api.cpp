@@ -50,7 +50,8 @@ struct mxgemm_plan {
 namespace {
 
 struct TileInfo {
-  int bm, bn, waves, variant;  // variant: 0 = 4 waves, 1 = 8 waves, 2 = 8-wave ping-pong (MX only)
+  int bm, bn, waves, variant;  // variant: 0 = 4 waves, 1 = 8 waves, 2 = 8-wave ping-pong (MX only),
+                               // 3 = 4-stage LDS ring (MXFP8 only)
   int eff[3];                  // measured relative efficiency per kind (E4M3, E2M1, F16), percent
 };
 // Tile ids understood by gemm_launch. The efficiencies rank the tiles (MI355X measurements at the
@@ -58,11 +59,14 @@ struct TileInfo {
 constexpr TileInfo kTiles[] = {
     {256, 256, 4, 0, {85, 85, 90}}, {256, 224, 4, 0, {80, 75, 55}}, {128, 128, 4, 0, {50, 45, 50}},
     {64, 64, 4, 0, {25, 25, 25}},   {256, 256, 8, 1, {90, 100, 100}}, {256, 224, 8, 1, {88, 95, 60}},
-    {256, 256, 8, 2, {60, 60, 99}}, {256, 224, 8, 2, {100, 95, 60}}};
+    {256, 256, 8, 2, {60, 60, 99}}, {256, 224, 8, 2, {100, 95, 60}}, {256, 256, 4, 3, {200, 1, 1}}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
+constexpr int kRingTile = 8;
 constexpr int kCUs = 256;
 
-int choose_tile(int kind, int M, int N) {
+bool ring_ok(int kind, int N, int K) { return kind == 0 && K % 512 == 0 && N % 4 == 0; }
+
+int choose_tile(int kind, int M, int N, int K) {
   if (const char* env = std::getenv("MXGEMM_TILE")) {
     int t = std::atoi(env);
     if (t >= 0 && t < kNumTiles) return t;
@@ -70,6 +74,7 @@ int choose_tile(int kind, int M, int N) {
   int best = 0;
   double best_cost = 1e300;
   for (int t = 0; t < kNumTiles; t++) {
+    if (t == kRingTile && !ring_ok(kind, N, K)) continue;
     const int64_t tiles = (int64_t)((M + kTiles[t].bm - 1) / kTiles[t].bm) * ((N + kTiles[t].bn - 1) / kTiles[t].bn);
     const int64_t waves = (tiles + kCUs - 1) / kCUs;
     const double cost = (double)waves * kTiles[t].bm * kTiles[t].bn * 100.0 / kTiles[t].eff[kind];
@@ -113,7 +118,7 @@ int mxgemm_create(mxgemm_t* out, int M, int N, int K, int fa, int fb, unsigned f
   if (M < 1 || N < 1 || K < 32 || M > MX_MAX_DIM || N > MX_MAX_DIM || K > MX_MAX_DIM) return MX_ERR_SHAPE;
   if (kind != 2 && K % 32) return MX_ERR_SHAPE;
   if (kind == 2 && (K % 8 || N % 8)) return MX_ERR_SHAPE;
-  mxgemm_plan* p = new (std::nothrow) mxgemm_plan{M, N, K, fa, fb, kind, choose_tile(kind, M, N)};
+  mxgemm_plan* p = new (std::nothrow) mxgemm_plan{M, N, K, fa, fb, kind, choose_tile(kind, M, N, K)};
   if (!p) return MX_ERR_NOMEM;
   *out = p;
   return MX_OK;
@@ -130,6 +135,12 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
   *tile_m = t.bm;
   *tile_n = t.bn;
   *tile_k = p->kind == 0 ? 128 : (p->kind == 1 ? 256 : 64);
+  if (p->tile_id == kRingTile) {  // the ring kernel, or the 8-wave kernel where it does not apply
+    const bool ring = ring_ok(p->kind, p->N, p->K);
+    *tile_k = ring ? 64 : *tile_k;
+    *variant = ring ? 3 : 1;
+    return MX_OK;
+  }
   // the ping-pong kernel needs whole stages and dword-aligned scale rows; otherwise 8 waves run
   const bool pp_ok = p->kind != 2 && (p->kind == 0 ? p->K % 128 == 0 : p->K % 256 == 0) && (p->K / 32) % 4 == 0;
   *variant = (t.variant == 2 && !pp_ok) ? 1 : (t.variant == 2 && p->kind == 2 ? 1 : t.variant);

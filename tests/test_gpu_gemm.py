@@ -58,7 +58,7 @@ def test_mx_small_config_full(orc, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 4])
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7, 8])
 def test_mx_every_tile_ragged(orc, fmt, tile):
     """Each tile configuration on a shape spanning several tiles with ragged M, N and K tails."""
     api = require_gpu()
@@ -84,6 +84,19 @@ def test_mx_pingpong_ragged_mn(orc, fmt, tile, K):
     C, (oA, oSA, oB, oSB) = mx_case(orc, api, fmt, M, N, K, 999 + K + tile, tile=tile)
     ref = orc.mxgemm(fmt, fmt, oA, oSA, oB, oSB, M, N, K)
     ok, ratio, bad = orc.check(C, ref, K, R_of(orc, fmt, oA, oSA, oB, oSB, M, N, K))
+    assert ok, (ratio, bad)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 520, 512), (300, 520, 1024), (257, 260, 4096), (1, 4, 512),
+                                   (512, 512, 1536), (33, 1028, 2560)])
+def test_mx_ring_ragged(orc, M, N, K):
+    """The MXFP8 4-stage ring kernel (K % 512 == 0, N % 4 == 0): one scale group up to several,
+    partial tiles in M and N, a single row and column strip."""
+    api = require_gpu()
+    say(f"mx ring M={M} N={N} K={K}")
+    C, (oA, oSA, oB, oSB) = mx_case(orc, api, 0, M, N, K, 31 + M + N + K, tile=8)
+    ref = orc.mxgemm(0, 0, oA, oSA, oB, oSB, M, N, K)
+    ok, ratio, bad = orc.check(C, ref, K, R_of(orc, 0, oA, oSA, oB, oSB, M, N, K))
     assert ok, (ratio, bad)
 
 
@@ -212,7 +225,7 @@ def fp16_case(orc, api, M, N, K, seed, tile=None):
     return A, B, C
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7, 8])
 def test_f16_every_tile_ragged(orc, tile):
     api = require_gpu()
     M, N, K = 300, 520, 200

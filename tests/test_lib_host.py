@@ -144,6 +144,27 @@ def test_validation_errors_without_gpu():
     assert lib.mx_pack_host(16, buf.ctypes.data, 1, 32, buf.ctypes.data, buf.ctypes.data) == api.MX_ERR_FORMAT
 
 
+def test_ring_tile_plan_info(monkeypatch):
+    """Tile 8 is the MXFP8 4-stage ring (64-byte K stages) where K % 512 == 0 and N % 4 == 0, and
+    the 8-wave 256x256 kernel elsewhere; without the override the ring is never picked for other
+    shapes or formats."""
+    def info(M, N, K, f):
+        p = api.mxgemm_create(M, N, K, f, f)
+        try:
+            return api.mxgemm_plan_info(p)
+        finally:
+            api.mxgemm_destroy(p)
+    monkeypatch.setenv("MXGEMM_TILE", "8")
+    assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 256, 64, 3)
+    assert info(300, 520, 416, api.MX_E4M3) == (256, 256, 128, 1)
+    assert info(300, 522, 512, api.MX_E4M3) == (256, 256, 128, 1)
+    assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 256, 1)
+    assert info(512, 512, 512, api.MX_F16) == (256, 256, 64, 1)
+    monkeypatch.delenv("MXGEMM_TILE")
+    for M, N, K, f in [(300, 520, 416, api.MX_E4M3), (4096, 8192, 8192, api.MX_E2M1), (512, 512, 512, api.MX_F16)]:
+        assert info(M, N, K, f)[3] != 3
+
+
 def test_matvec_workspace_size():
     """Split-K workspace: fp32 partials [S][M][N] (256-byte rounded) plus a counter per strip;
     zero for invalid shapes, never decreasing in M."""
