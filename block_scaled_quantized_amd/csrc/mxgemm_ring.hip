@@ -290,29 +290,58 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
     ring_stage<7>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
   }
 
-  // The last stages queued copies of stage nst-1 into free slots; let them land before the
-  // workgroup (and its LDS) can end.
+  // The last stages queued copies of stage nst-1 into free slots: let them land, and let every
+  // wave finish with the ring, before the slots are reused for the output.
   __builtin_amdgcn_s_waitcnt(0x0F70);
+  raw_barrier();
 
-  // epilogue: lane holds C[m0 + 128wm + 32j + r32][n0 + 128wn + 32i + 8q + 4h + e] in acc[i][j][4q + e]
+  // Epilogue. The lane holds C[m0 + 128wm + 32j + r32][n0 + 128wn + 32i + 8q + 4h + e] in
+  // acc[i][j][4q + e]: 8 bytes per row, so storing straight from registers would write each
+  // 128-byte line of C in eight pieces from eight instructions. Instead each wave converts to fp16
+  // into its own slot, 64 rows at a time (rows padded to 264 bytes: the 8-byte writes of 32 rows
+  // then fall on distinct banks), and writes the rows back 16 bytes per lane, 256 contiguous bytes
+  // per row.
+  char* stage = wave == 0 ? slot0 : (wave == 1 ? slot1 : (wave == 2 ? slot2 : slot3));
+  constexpr int EROW = 264;
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const int m = m0 + 128 * wm + 32 * j + r32;
-    if (m >= p.M) continue;
+  for (int half = 0; half < 2; half++) {
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int jj = 0; jj < 2; jj++)
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const int n = n0 + 128 * wn + 32 * i + 8 * q + 4 * h;
-        if (n >= p.N) continue;
-        v4h o;
+      for (int i = 0; i < 4; i++)
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const float v = acc[i][j][4 * q + e];
-          o[e] = (_Float16)v;
+        for (int q = 0; q < 4; q++) {
+          v4h o;
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const float v = acc[i][2 * half + jj][4 * q + e];
+            o[e] = (_Float16)v;
+          }
+          *reinterpret_cast<v4h*>(stage + (32 * jj + r32) * EROW + (32 * i + 8 * q + 4 * h) * 2) = o;
         }
-        *reinterpret_cast<v4h*>(p.C + (int64_t)m * p.N + n) = o;
+    // 64 rows x 256 bytes: instruction s covers rows 4s..4s+3, lane l row 4s + l/16, bytes 16(l%16)
+    const int cl = lane & 15, n = n0 + 128 * wn + 8 * cl;
+#pragma unroll
+    for (int s4 = 0; s4 < 16; s4++) {
+      const int lr = 4 * s4 + (lane >> 4);
+      const int m = m0 + 128 * wm + 64 * half + lr;
+      typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+      const char* src = stage + lr * EROW + 16 * cl;
+      const v4h lo = *reinterpret_cast<const v4h*>(src), hi = *reinterpret_cast<const v4h*>(src + 8);
+      if (m < p.M) {
+        _Float16* dst = p.C + (int64_t)m * p.N + n;
+        if (n + 8 <= p.N) {
+          if ((p.N & 7) == 0) {  // rows start 16-byte aligned
+            *reinterpret_cast<v8h*>(dst) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          } else {
+            *reinterpret_cast<v4h*>(dst) = lo;
+            *reinterpret_cast<v4h*>(dst + 4) = hi;
+          }
+        } else if (n + 4 <= p.N) {
+          *reinterpret_cast<v4h*>(dst) = lo;
+        }
       }
+    }
   }
 }
 
