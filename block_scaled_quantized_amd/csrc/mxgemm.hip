@@ -367,6 +367,55 @@ MX_DEV void compute_stage(const char* buf, v4f (&acc)[CF::FN][CF::FM], int wm, i
   }
 }
 
+// ------------------------------------------------------------------------------------------------
+// Epilogue shared by the 16x16-MFMA kernels: fp32 -> fp16 (nearest even). acc[i][j] holds, in lane
+// l, C[mb + 16j + l%16][nb + 16i + 4(l/16) + v] for v = 0..3: 8 bytes of a row, so stores straight
+// from registers would write every 128-byte line of C in pieces from several instructions. The
+// wave instead writes 16 rows at a time into its own LDS scratch (row pitch 2*WN + 16 bytes: the
+// 8-byte writes of 16 rows x 2 column groups land on distinct banks) and stores them back as
+// 16-byte pieces, consecutive lanes along a row.
+template <class CF>
+constexpr int C_PITCH = 2 * CF::WN + 16;
+
+template <class CF>
+MX_DEV void store_c(const Args& p, const v4f (&acc)[CF::FN][CF::FM], char* ws, int mb, int nb, int lane) {
+  static_assert(CF::NWAVES * 16 * C_PITCH<CF> <= CF::LDS_BYTES, "epilogue scratch");
+  typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+  constexpr int LPR = CF::WN / 8;  // 16-byte pieces per row
+  constexpr int PIECES = 16 * LPR;
+  const int r16 = lane & 15, q = lane >> 4;
+  const bool rows16 = (p.N & 7) == 0, rows8 = (p.N & 3) == 0;  // row starts 16- / 8-byte aligned
+#pragma unroll
+  for (int j = 0; j < CF::FM; j++) {
+#pragma unroll
+    for (int i = 0; i < CF::FN; i++) {
+      const v4f a = acc[i][j];
+      *reinterpret_cast<v4h*>(ws + r16 * C_PITCH<CF> + (16 * i + 4 * q) * 2) =
+          v4h{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3]};
+    }
+#pragma unroll
+    for (int s0 = 0; s0 < PIECES; s0 += 64) {
+      const int piece = s0 + lane;
+      if (PIECES % 64 != 0 && piece >= PIECES) continue;
+      const int lr = piece / LPR, c = piece % LPR;
+      const v8h v = *reinterpret_cast<const v8h*>(ws + lr * C_PITCH<CF> + 16 * c);
+      const int m = mb + 16 * j + lr, n = nb + 8 * c;
+      if (m >= p.M) continue;
+      _Float16* dst = p.C + (int64_t)m * p.N + n;
+      if (rows16 && n + 8 <= p.N) {
+        *reinterpret_cast<v8h*>(dst) = v;
+      } else if (rows8 && n + 8 <= p.N) {
+        *reinterpret_cast<v4h*>(dst) = __builtin_shufflevector(v, v, 0, 1, 2, 3);
+        *reinterpret_cast<v4h*>(dst + 4) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          if (n + e < p.N) dst[e] = v[e];
+      }
+    }
+  }
+}
+
 template <class CF, int KIND>
 __global__ __launch_bounds__(CF::THREADS, 1) void gemm_kernel(Args p) {
   __shared__ __attribute__((aligned(16))) char lds[CF::LDS_BYTES];
@@ -429,26 +478,8 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_kernel(Args p) {
     raw_barrier();                  // ... and every other wave's
   }
 
-  // Epilogue: fp32 -> fp16 (nearest even), lane holds C[m][n..n+3].
-  const bool vec = (p.N & 3) == 0;
-#pragma unroll
-  for (int i = 0; i < CF::FN; i++) {
-    const int n = n0 + wn * CF::WN + 16 * i + 4 * q;
-#pragma unroll
-    for (int j = 0; j < CF::FM; j++) {
-      const int m = m0 + wm * CF::WM + 16 * j + r16;
-      if (m >= p.M) continue;
-      _Float16* crow = p.C + (int64_t)m * p.N;
-      const v4f a = acc[i][j];
-      if (vec && n + 3 < p.N) {
-        *reinterpret_cast<v4h*>(crow + n) = v4h{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3]};
-      } else {
-#pragma unroll
-        for (int v = 0; v < 4; v++)
-          if (n + v < p.N) crow[n + v] = (_Float16)a[v];
-      }
-    }
-  }
+  // Epilogue: every wave is past the last stage's barrier, so the stage buffers are free.
+  store_c<CF>(p, acc, lds + wave * 16 * C_PITCH<CF>, m0 + wm * CF::WM, n0 + wn * CF::WN, lane);
 }
 
 
@@ -630,25 +661,8 @@ __global__ __launch_bounds__(CF::THREADS, 1) void gemm_pp_kernel(Args p) {
     }
   }
 
-  const bool vec = (p.N & 3) == 0;
-#pragma unroll
-  for (int i = 0; i < CF::FN; i++) {
-    const int n = n0 + wn * CF::WN + 16 * i + 4 * q;
-#pragma unroll
-    for (int j = 0; j < CF::FM; j++) {
-      const int m = m0 + wm * CF::WM + 16 * j + r16;
-      if (m >= p.M) continue;
-      _Float16* crow = p.C + (int64_t)m * p.N;
-      const v4f a = acc[i][j];
-      if (vec && n + 3 < p.N) {
-        *reinterpret_cast<v4h*>(crow + n) = v4h{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3]};
-      } else {
-#pragma unroll
-        for (int v = 0; v < 4; v++)
-          if (n + v < p.N) crow[n + v] = (_Float16)a[v];
-      }
-    }
-  }
+  // Epilogue: every wave is past its last barrier, so the stage buffers are free.
+  store_c<CF>(p, acc, lds + wave * 16 * C_PITCH<CF>, m0 + wm * CF::WM, n0 + wn * CF::WN, lane);
 }
 
 template <int KIND, int BM, int BN>
