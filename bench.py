@@ -8,8 +8,9 @@ reported under "detail": the MXFP4 GEMM (M=4096, N=8192, K=8192), the fp16 GEMM 
 small MXFP8 GEMM (128x256x128, a latency figure), the int8/int4 dequant matvec (M=1 and M=8,
 K=4096, N=14336; GB/s of algorithmic bytes) and the GPU pack/unpack codecs.
 
-Timing: W warm-up steps, then K steps between two HIP events recorded on the stream the kernels
-are launched on, bracketed by device synchronisation. Inputs rotate over several copies so that
+Timing: per workload, --settle seconds (default 0.5) of untimed calls so that the shader clock
+reaches its sustained-load level, W warm-up steps, then K steps between two HIP events recorded
+on the stream the kernels are launched on, bracketed by device synchronisation. Inputs rotate over several copies so that
 repeats are not served by the 256 MB Infinity Cache (3 sets for GEMMs, >= 384 MB of weights for
 the matvec). The CPU baseline is the oracle timed on the host on a bounded row sample.
 """
@@ -33,11 +34,33 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def hbm_traffic(kernel, tile, shape):
+    """HBM bytes per launch of the headline kernel, as measured by the rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes summarised under profiles/ (a line "traffic_record: {json}" naming kernel,
+    tile and shape). None when no record matches the kernel this run uses."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None, None
+    for name in sorted(os.listdir(pdir)):
+        if not name.endswith((".md", ".txt")):
+            continue
+        with open(os.path.join(pdir, name)) as f:
+            for line in f:
+                if not line.startswith("traffic_record: "):
+                    continue
+                rec = json.loads(line[len("traffic_record: "):])
+                if rec.get("kernel") == kernel and rec.get("tile") == tile and tuple(rec.get("shape", ())) == shape:
+                    return rec["bytes_per_launch"], f"profiles/{name}"
+    return None, None
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--settle", type=float, default=0.5,
+                   help="seconds of untimed load before each workload's warm-up steps (clock ramp)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--only", default="", help="comma list of detail workloads to run (default all)")
     return p.parse_args()
@@ -61,8 +84,21 @@ def main():
     def d(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
+    def settle(fn, seconds=0.5):
+        """Run fn until `seconds` of wall time have passed: under sustained MFMA load the shader
+        clock takes a few hundred ms to reach its steady state, and a timed region of a few ms
+        that starts cold measures the ramp, not the kernel."""
+        t_end = time.perf_counter() + seconds
+        i = 0
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
+
     def timed(fn, steps, warmup):
         """Mean ms per call of fn(i) over `steps` calls, HIP events on the launch stream."""
+        settle(fn, args.settle)
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
@@ -238,6 +274,9 @@ def main():
                          f"({rows_done}x{N}x{K} MACs in {t_cpu:.1f} s, fp64, closed-form decode per element)",
                "seconds": t_cpu, "gpu_rows_worst_err_over_bound": worst}
 
+    kname = {3: "gemm_ring_kernel", 2: "gemm_pp_kernel"}.get(tile[3], "gemm_kernel")
+    traffic, traffic_src = hbm_traffic(kname, list(tile), (M, N, K))
+
     out = {
         "metric": "block-scaled GEMM TFLOPS & % MFMA peak (MXFP8/MXFP4); int8 matvec GB/s",
         "value": tflops,
@@ -245,6 +284,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": args.settle,
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
@@ -254,9 +294,9 @@ def main():
         "config": {"workload": "mxfp8_gemm_prefill M=2048 N=14336 K=4096", "M": M, "N": N, "K": K,
                    "tile_m_n_k": list(tile), "input_sets_rotated": 3},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK["mxfp8"], "unit": "TFLOP/s",
-                     "frac": tflops / PEAK["mxfp8"], "traffic": None,
-                     "kernel": f"{'gemm_pp_kernel' if tile[3] == 2 else 'gemm_kernel'}<E4M3, {tile[0]}x{tile[1]}>",
-                     "flops_per_launch": flops},
+                     "frac": tflops / PEAK["mxfp8"], "traffic": traffic,
+                     "kernel": f"{kname}<E4M3, {tile[0]}x{tile[1]}>",
+                     "flops_per_launch": flops, "traffic_source": traffic_src},
         "cpu_baseline": cpu,
         "detail": detail,
     }
