@@ -51,7 +51,7 @@ namespace {
 
 struct TileInfo {
   int bm, bn, waves, variant;  // variant: 0 = 4 waves, 1 = 8 waves, 2 = 8-wave ping-pong (MX only),
-                               // 3 = 4-stage LDS ring (MXFP8 only)
+                               // 3 = 4-stage LDS ring (MX formats)
   int eff[3];                  // measured relative efficiency per kind (E4M3, E2M1, F16), percent
 };
 // Tile ids understood by gemm_launch. The efficiencies rank the tiles (MI355X measurements at the
@@ -59,12 +59,14 @@ struct TileInfo {
 constexpr TileInfo kTiles[] = {
     {256, 256, 4, 0, {85, 85, 90}}, {256, 224, 4, 0, {80, 75, 55}}, {128, 128, 4, 0, {50, 45, 50}},
     {64, 64, 4, 0, {25, 25, 25}},   {256, 256, 8, 1, {90, 100, 100}}, {256, 224, 8, 1, {88, 95, 60}},
-    {256, 256, 8, 2, {60, 60, 99}}, {256, 224, 8, 2, {100, 95, 60}}, {256, 256, 4, 3, {200, 1, 1}}};
+    {256, 256, 8, 2, {60, 60, 99}}, {256, 224, 8, 2, {100, 95, 60}}, {256, 256, 4, 3, {200, 200, 1}}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kRingTile = 8;
 constexpr int kCUs = 256;
 
-bool ring_ok(int kind, int N, int K) { return kind == 0 && K % 512 == 0 && N % 4 == 0; }
+bool ring_ok(int kind, int N, int K) {
+  return N % 4 == 0 && ((kind == 0 && K % 512 == 0) || (kind == 1 && K % 1024 == 0));
+}
 
 int choose_tile(int kind, int M, int N, int K) {
   if (const char* env = std::getenv("MXGEMM_TILE")) {
@@ -137,7 +139,7 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
   *tile_k = p->kind == 0 ? 128 : (p->kind == 1 ? 256 : 64);
   if (p->tile_id == kRingTile) {  // the ring kernel, or the 8-wave kernel where it does not apply
     const bool ring = ring_ok(p->kind, p->N, p->K);
-    *tile_k = ring ? 64 : *tile_k;
+    *tile_k = ring ? (p->kind == 0 ? 64 : 128) : *tile_k;
     *variant = ring ? 3 : 1;
     return MX_OK;
   }

@@ -1,4 +1,5 @@
-// mxgemm_ring.hip -- MXFP8 (E4M3 x E4M3, E8M0 scales per 32 along K) GEMM with a 4-stage LDS ring.
+// mxgemm_ring.hip -- MXFP8 / MXFP4 (E4M3 or E2M1 data, E8M0 scales per 32 along K) GEMM with a
+// 4-stage LDS ring.
 //
 //   C[m,n] = sum_k 2^(SA[m,k/32]-127) A[m,k] * 2^(SB[n,k/32]-127) B[n,k]   (fp32 accumulate, fp16 out)
 //
@@ -43,10 +44,23 @@ constexpr int BM = 256, BN = 256;       // tile
 constexpr int ROWB = 64;                // K bytes per stage
 constexpr int ROWS = BM + BN;           // LDS rows per stage (A then B)
 constexpr int SLOT = ROWS * ROWB;       // 32 KB
-constexpr int SGRP = ROWS * 16;         // 8 KB: scales of 8 stages
 constexpr int GROUP = 8;                // stages per scale group
 constexpr int DMA_PER_STAGE = SLOT / 1024 / 4;  // direct copies per wave per stage (8)
-constexpr int DMA_PER_GROUP = SGRP / 1024 / 4;  // direct copies per wave per scale group (2)
+
+// Per-format constants. A 64-byte stage is one MFMA K-step of E4M3 (64 elements, 2 scale blocks)
+// or two of E2M1 (128 elements, 4 blocks); a group of 8 stages then holds 16 or 32 scale bytes per
+// row, and each lane keeps 8 or 16 of them (its own K-block h of every K-step), 2 or 4 dwords.
+template <int KIND>
+struct RingFmt {
+  static constexpr bool FP4 = KIND == 1;
+  static constexpr int KSTEPS = FP4 ? 2 : 1;        // MFMA K-steps per stage
+  static constexpr int CBSZ = FP4 ? 4 : 0;          // MFMA operand format (FP4 / FP8)
+  static constexpr int SB_ROW = 16 * KSTEPS;        // scale bytes per row per group
+  static constexpr int SGRP = ROWS * SB_ROW;        // 8 / 16 KB
+  static constexpr int SDW = 2 * KSTEPS;            // packed scale dwords per row per lane
+  static constexpr int DMA_PER_GROUP = SGRP / 1024 / 4;  // scale copies per wave per group (2 / 4)
+  static constexpr int ELEMS_PER_BYTE = FP4 ? 2 : 1;
+};
 
 // The size goes through readfirstlane: clamps of uniform values can be selected as vector ops
 // (v_med3), and a resource that is not provably scalar turns each buffer access into a loop.
@@ -78,43 +92,65 @@ struct Args {
   int M, N, K, tiles_m;
 };
 
+// Per lane: byte u%4 of dword u/4 is the lane's scale for MFMA K-step u of the group (u = stage for
+// E4M3, 2*stage + k for K-step k of a stage for E2M1).
+template <int KIND>
 struct Scales {
-  uint32_t a[4][2], b[4][2];  // per lane: byte S8%4 of dword S8/4 = this lane's scale for stage S8 of the group
+  uint32_t a[4][RingFmt<KIND>::SDW], b[4][RingFmt<KIND>::SDW];
 };
 
 MX_DEV int phys_off(int row, int chunk) { return row * ROWB + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
 MX_DEV v4i lds16(const char* base, int off) { return *reinterpret_cast<const v4i*>(base + off); }
 
-// The lane's 16 scale bytes of a row hold (stage s, block b) at byte 2s + b. Half d (bytes 8d..8d+7,
-// stages 4d..4d+3) becomes dword d of the lane's packed scales, keeping its own block h: bytes h,
-// 2+h, 4+h, 6+h. Stages 0-3 of a group use dword 0 and stages 4-7 dword 1, so the next group's
-// half 0 is read during stage 4 and packed at the end of stage 6, and its half 1 is read after
-// the last MFMA of stage 7 and packed at the end of the next group's stage 2: the reads have a
-// stage or more to land before anything waits for them. The packed value of stage 2 is unchanged
-// in group 0, whose halves the prologue packs.
-typedef int v2i __attribute__((ext_vector_type(2)));
+// Scale layout in LDS. E4M3: row r's 16 bytes of the group at r*16, (stage s, block b) at byte
+// 2s + b. E2M1: two planes of 8 KB (stages 0-3, 4-7), row r's 16 bytes of plane d at d*8192 + r*16,
+// (stage s, K-step k, block b) at byte 4(s%4) + 2k + b. Half d of a row covers stages 4d..4d+3
+// and becomes dwords d*KSTEPS.. of the lane's packed scales, keeping its own block h: from each 8
+// source bytes, bytes h, 2+h, 4+h, 6+h. Stages 0-3 of a group use the dwords of half 0 and stages
+// 4-7 those of half 1, so the next group's half 0 is read during stage 4 and packed at the end of
+// stage 6, and its half 1 is read after the last MFMA of stage 7 and packed at the end of the next
+// group's stage 2: the reads have a stage or more to land before anything waits for them. The
+// packed value of stage 2 is unchanged in group 0, whose halves the prologue packs.
+template <int KIND>
 struct RawScales {
-  v2i a[4], b[4];
+  typedef int raw_t __attribute__((ext_vector_type(2 * RingFmt<KIND>::KSTEPS)));
+  raw_t a[4], b[4];
 };
 
-MX_DEV void read_raw_scales(const char* sg, RawScales& r, int d, int wm, int wn, int r32) {
-#pragma unroll
-  for (int j = 0; j < 4; j++) r.a[j] = *reinterpret_cast<const v2i*>(sg + (128 * wm + 32 * j + r32) * 16 + 8 * d);
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-    r.b[i] = *reinterpret_cast<const v2i*>(sg + (BM + 128 * wn + 32 * i + r32) * 16 + 8 * d);
+template <int KIND>
+MX_DEV const typename RawScales<KIND>::raw_t& raw_at(const char* sg, int row, int d) {
+  typedef typename RawScales<KIND>::raw_t raw_t;
+  if constexpr (RingFmt<KIND>::FP4) return *reinterpret_cast<const raw_t*>(sg + d * 8192 + row * 16);
+  else return *reinterpret_cast<const raw_t*>(sg + row * 16 + 8 * d);
 }
 
-MX_DEV void pack_scales(const RawScales& r, Scales& s, int d, int h) {
+template <int KIND>
+MX_DEV void read_raw_scales(const char* sg, RawScales<KIND>& r, int d, int wm, int wn, int r32) {
+#pragma unroll
+  for (int j = 0; j < 4; j++) r.a[j] = raw_at<KIND>(sg, 128 * wm + 32 * j + r32, d);
+#pragma unroll
+  for (int i = 0; i < 4; i++) r.b[i] = raw_at<KIND>(sg, BM + 128 * wn + 32 * i + r32, d);
+}
+
+template <int KIND>
+MX_DEV void pack_scales(const RawScales<KIND>& r, Scales<KIND>& s, int d, int h) {
+  constexpr int KS = RingFmt<KIND>::KSTEPS;
   const uint32_t sel = h ? 0x07050301u : 0x06040200u;
 #pragma unroll
-  for (int j = 0; j < 4; j++) s.a[j][d] = __builtin_amdgcn_perm((uint32_t)r.a[j][1], (uint32_t)r.a[j][0], sel);
+  for (int w = 0; w < KS; w++) {
 #pragma unroll
-  for (int i = 0; i < 4; i++) s.b[i][d] = __builtin_amdgcn_perm((uint32_t)r.b[i][1], (uint32_t)r.b[i][0], sel);
+    for (int j = 0; j < 4; j++)
+      s.a[j][KS * d + w] = __builtin_amdgcn_perm((uint32_t)r.a[j][2 * w + 1], (uint32_t)r.a[j][2 * w], sel);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      s.b[i][KS * d + w] = __builtin_amdgcn_perm((uint32_t)r.b[i][2 * w + 1], (uint32_t)r.b[i][2 * w], sel);
+  }
 }
 
-// B fragment i of one stage (rows 256 + 128*wn + 32i + l%32) and A fragment j (rows 128*wm + 32j).
+// B fragment i of one stage (rows 256 + 128*wn + 32i + l%32) and A fragment j (rows 128*wm + 32j):
+// chunks h and 2+h of the row, i.e. the lane's K bytes of the E4M3 MFMA, or its 16 bytes (K-block
+// h) of E2M1 K-steps 0 and 1 in the low and high halves.
 MX_DEV v8i read_b(const char* slot, int i, int wn, int r32, int h) {
   const int row = BM + 128 * wn + 32 * i + r32;
   return __builtin_shufflevector(lds16(slot, phys_off(row, h)), lds16(slot, phys_off(row, 2 + h)), 0, 1, 2, 3, 4, 5,
@@ -126,19 +162,24 @@ MX_DEV v8i read_a(const char* slot, int j, int wm, int r32, int h) {
                                  6, 7);
 }
 
-// Per-workgroup constants of the main loop.
+// Per-workgroup constants of the main loop (rscale: the first DMA_PER_GROUP of the format are set).
 struct Ctx {
   rsrc_t rdata[DMA_PER_STAGE];
-  rsrc_t rscale[DMA_PER_GROUP];
+  rsrc_t rscale[4];
   uint32_t voff, svoff;
   int wave, wm, wn, r32, h, nst, ngroups;
 };
 
+// Scale copy k of this wave: 64 rows (A rows 64(wave) + l for even k, B rows for odd k), 16 bytes
+// each: bytes 16(k/2).. of the row's group (E2M1: plane k/2).
+template <int KIND>
 MX_DEV void issue_scales(const Ctx& c, char* sg, int g) {
+  constexpr int NK = RingFmt<KIND>::DMA_PER_GROUP;
+  const int goff = g * (RingFmt<KIND>::FP4 ? 32 : 16);  // bytes of the group's first scale
 #pragma unroll
-  for (int k = 0; k < DMA_PER_GROUP; k++)
+  for (int k = 0; k < NK; k++)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rscale[k], (lds_ptr_t)(sg + (c.wave + 4 * k) * 1024), 16, c.svoff,
-                                             16 * g, 0, 0);
+                                             goff + 16 * (k >> 1), 0, 0);
 }
 
 // One stage t = 8g + S8: slot t%4 holds stage t (its fragments already in ca/cb). Before the
@@ -149,28 +190,46 @@ MX_DEV void issue_scales(const Ctx& c, char* sg, int g) {
 // B tile needs all four, then the B fragments in the order their tiles come.
 // The next-stage reads are unconditional (after the last stage they fetch unused bytes): a
 // conditional overwrite would keep the old contents alive through the stage.
-template <int S8>
+template <int KIND, int S8>
 MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[4], const v8i (&cb)[4],
-                       v8i (&na)[4], v8i (&nb)[4], const char* slot_nxt, char* slot_fill, Scales& sc,
-                       RawScales& raw, v16f (&acc)[4][4]) {
-  constexpr int D = S8 / 4, OP = S8 % 4;
+                       v8i (&na)[4], v8i (&nb)[4], const char* slot_nxt, char* slot_fill, Scales<KIND>& sc,
+                       RawScales<KIND>& raw, v16f (&acc)[4][4]) {
+  using F = RingFmt<KIND>;
   const int t = GROUP * g + S8;
   // Copies queued after this wave's copies of stage t+1 (issued at stage t-2): those of stage t+2
   // (at stage t-1) and, at S8 == 3, the scale group issued at S8 == 2 ahead of them. From S8 == 4
   // on, the next group's scales are visible.
-  wait_vm_n(S8 == 3 ? DMA_PER_STAGE + DMA_PER_GROUP : DMA_PER_STAGE);
+  wait_vm_n(S8 == 3 ? DMA_PER_STAGE + F::DMA_PER_GROUP : DMA_PER_STAGE);
   raw_barrier();
   // The scale array still holds half 1 of group g, read at the end of stage 7 of group g-1. Every
   // wave has waited for those reads before stage 1's MFMAs (they precede the fragment reads of
   // stage 0 in the wave's LDS queue), so past stage 2's barrier the array is free.
-  if (S8 == 2) issue_scales(c, sgrp, min(g + 1, c.ngroups - 1));
+  if (S8 == 2) issue_scales<KIND>(c, sgrp, min(g + 1, c.ngroups - 1));
   const uint32_t fill_off = ROWB * min(t + 3, c.nst - 1);
 #pragma unroll
   for (int i = 0; i < 4; i++) {
 #pragma unroll
-    for (int j = 0; j < 4; j++)
-      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[i], ca[j], acc[i][j], 0, 0, OP, sc.b[i][D], OP,
-                                                                   sc.a[j][D]);
+    for (int k = 0; k < F::KSTEPS; k++) {
+      constexpr int U0 = F::KSTEPS * S8;  // first K-step of the stage within the group
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if constexpr (F::FP4) {
+          const v8i bk = k ? __builtin_shufflevector(cb[i], cb[i], 4, 5, 6, 7, -1, -1, -1, -1)
+                           : __builtin_shufflevector(cb[i], cb[i], 0, 1, 2, 3, -1, -1, -1, -1);
+          const v8i ak = k ? __builtin_shufflevector(ca[j], ca[j], 4, 5, 6, 7, -1, -1, -1, -1)
+                           : __builtin_shufflevector(ca[j], ca[j], 0, 1, 2, 3, -1, -1, -1, -1);
+          if (k == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bk, ak, acc[i][j], 4, 4, U0 % 4, sc.b[i][U0 / 4], U0 % 4, sc.a[j][U0 / 4]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bk, ak, acc[i][j], 4, 4, (U0 + 1) % 4, sc.b[i][(U0 + 1) / 4], (U0 + 1) % 4, sc.a[j][(U0 + 1) / 4]);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[i], ca[j], acc[i][j], 0, 0, U0 % 4,
+                                                                       sc.b[i][U0 / 4], U0 % 4, sc.a[j][U0 / 4]);
+        }
+      }
+    }
 #pragma unroll
     for (int k = 2 * i; k < 2 * i + 2; k++)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(slot_fill + (c.wave + 4 * k) * 1024), 16,
@@ -182,20 +241,22 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[4], cons
       nb[2 * i - 4] = read_b(slot_nxt, 2 * i - 4, c.wn, c.r32, c.h);
       nb[2 * i - 3] = read_b(slot_nxt, 2 * i - 3, c.wn, c.r32, c.h);
     }
-    if (S8 == 4 && i == 1) read_raw_scales(sgrp, raw, 0, c.wm, c.wn, c.r32);
+    if (S8 == 4 && i == 1) read_raw_scales<KIND>(sgrp, raw, 0, c.wm, c.wn, c.r32);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (S8 == 2) pack_scales(raw, sc, 1, c.h);
-  if (S8 == 6) pack_scales(raw, sc, 0, c.h);
-  if (S8 == GROUP - 1) read_raw_scales(sgrp, raw, 1, c.wm, c.wn, c.r32);
+  if (S8 == 2) pack_scales<KIND>(raw, sc, 1, c.h);
+  if (S8 == 6) pack_scales<KIND>(raw, sc, 0, c.h);
+  if (S8 == GROUP - 1) read_raw_scales<KIND>(sgrp, raw, 1, c.wm, c.wn, c.r32);
 }
 
+template <int KIND>
 __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
+  using F = RingFmt<KIND>;
   __shared__ __attribute__((aligned(16))) char slot0[SLOT];
   __shared__ __attribute__((aligned(16))) char slot1[SLOT];
   __shared__ __attribute__((aligned(16))) char slot2[SLOT];
   __shared__ __attribute__((aligned(16))) char slot3[SLOT];
-  __shared__ __attribute__((aligned(16))) char sgrp[SGRP];
+  __shared__ __attribute__((aligned(16))) char sgrp[F::SGRP];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -208,8 +269,8 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
   const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
-  const uint32_t K = (uint32_t)p.K, nblk = K / 32;
-  const int nst = p.K / ROWB, ngroups = nst / GROUP;
+  const uint32_t RB = (uint32_t)p.K / F::ELEMS_PER_BYTE, nblk = (uint32_t)p.K / 32;  // row bytes, K-blocks
+  const int nst = (int)RB / ROWB, ngroups = nst / GROUP;
 
   // Direct copies. Copy k (0..7) of this wave in a stage is stage instruction i = wave + 4k: rows
   // 16i + l/4 of the stage (A rows for k < 4, B rows 16(i-16) + l/4 for k >= 4), lane l filling
@@ -225,22 +286,22 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   c.nst = nst;
   c.ngroups = ngroups;
   const uint32_t lrow = (uint32_t)(lane >> 2), lchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-  c.voff = lrow * K + 16u * lchunk;
+  c.voff = lrow * RB + 16u * lchunk;
 #pragma unroll
   for (int k = 0; k < DMA_PER_STAGE; k++) {
     const int i = wave + 4 * k;
     const bool isA = k < 4;
     const int r0 = isA ? 16 * i : 16 * i - BM, rows = isA ? rows_a : rows_b;
     const int nr = max(0, min(16, rows - r0));
-    const uint8_t* base = (isA ? p.A + (int64_t)m0 * K : p.B + (int64_t)n0 * K) + (int64_t)(nr ? r0 : 0) * K;
-    c.rdata[k] = make_rsrc(base, (uint32_t)nr * K);
+    const uint8_t* base = (isA ? p.A + (int64_t)m0 * RB : p.B + (int64_t)n0 * RB) + (int64_t)(nr ? r0 : 0) * RB;
+    c.rdata[k] = make_rsrc(base, (uint32_t)nr * RB);
   }
-  // Scale copy k (0, 1) of this wave: instruction i = wave + 4k, rows 64i + l (A for k == 0).
+  // Scale copy k of this wave: rows 64i + l with i = wave + 4(k%2) (A rows for even k).
   c.svoff = (uint32_t)lane * nblk;
 #pragma unroll
-  for (int k = 0; k < DMA_PER_GROUP; k++) {
-    const int i = wave + 4 * k;
-    const bool isA = k == 0;
+  for (int k = 0; k < F::DMA_PER_GROUP; k++) {
+    const int i = wave + 4 * (k & 1);
+    const bool isA = (k & 1) == 0;
     const int r0 = isA ? 64 * i : 64 * i - BM, rows = isA ? rows_a : rows_b;
     const int nr = max(0, min(64, rows - r0));
     const uint8_t* base = (isA ? p.SA + (int64_t)m0 * nblk : p.SB + (int64_t)n0 * nblk) + (int64_t)(nr ? r0 : 0) * nblk;
@@ -256,7 +317,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
   // prologue: scale group 0 and stages 0, 1, 2
-  issue_scales(c, sgrp, 0);
+  issue_scales<KIND>(c, sgrp, 0);
   for (int t = 0; t < 3 && t < nst; t++) {
     char* slot = t == 0 ? slot0 : (t == 1 ? slot1 : slot2);
 #pragma unroll
@@ -267,12 +328,12 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): prologue copies of this wave
   raw_barrier();
   v8i xa[4], xb[4], ya[4], yb[4];
-  Scales sc;
-  RawScales raw;
-  read_raw_scales(sgrp, raw, 0, wm, wn, r32);
-  pack_scales(raw, sc, 0, h);
-  read_raw_scales(sgrp, raw, 1, wm, wn, r32);
-  pack_scales(raw, sc, 1, h);
+  Scales<KIND> sc;
+  RawScales<KIND> raw;
+  read_raw_scales<KIND>(sgrp, raw, 0, wm, wn, r32);
+  pack_scales<KIND>(raw, sc, 0, h);
+  read_raw_scales<KIND>(sgrp, raw, 1, wm, wn, r32);
+  pack_scales<KIND>(raw, sc, 1, h);
 #pragma unroll
   for (int j = 0; j < 4; j++) xa[j] = read_a(slot0, j, wm, r32, h);
 #pragma unroll
@@ -280,14 +341,14 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
 
   // Stage t uses slot t%4 (t = 8g + s: slot s%4); even stages compute from x*, odd from y*.
   for (int g = 0; g < ngroups; g++) {
-    ring_stage<0>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, acc);
-    ring_stage<1>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, acc);
-    ring_stage<2>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, acc);
-    ring_stage<3>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
-    ring_stage<4>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, acc);
-    ring_stage<5>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, acc);
-    ring_stage<6>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, acc);
-    ring_stage<7>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
+    ring_stage<KIND, 0>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, acc);
+    ring_stage<KIND, 1>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, acc);
+    ring_stage<KIND, 2>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, acc);
+    ring_stage<KIND, 3>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
+    ring_stage<KIND, 4>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, acc);
+    ring_stage<KIND, 5>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, acc);
+    ring_stage<KIND, 6>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, acc);
+    ring_stage<KIND, 7>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
   }
 
   // The last stages queued copies of stage nst-1 into free slots: let them land, and let every
@@ -348,9 +409,10 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
 }  // namespace
 
 namespace mx {
-// MXFP8 ring kernel: requires K % 512 == 0 and N % 4 == 0 (checked by the caller).
-int gemm_ring_launch(const void* A, const void* SA, const void* B, const void* SB, void* C, int M, int N, int K,
-                     hipStream_t stream) {
+// MX ring kernels. fp4 = false: E4M3, requires K % 512 == 0; fp4 = true: E2M1, requires
+// K % 1024 == 0; both require N % 4 == 0 (checked by the caller).
+int gemm_ring_launch(bool fp4, const void* A, const void* SA, const void* B, const void* SB, void* C, int M, int N,
+                     int K, hipStream_t stream) {
   Args a{};
   a.A = (const uint8_t*)A;
   a.SA = (const uint8_t*)SA;
@@ -362,7 +424,10 @@ int gemm_ring_launch(const void* A, const void* SA, const void* B, const void* S
   a.K = K;
   a.tiles_m = (M + BM - 1) / BM;
   const int tiles = a.tiles_m * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL(gemm_ring_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, a);
+  if (fp4)
+    hipLaunchKernelGGL(gemm_ring_kernel<1>, dim3((unsigned)tiles), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(gemm_ring_kernel<0>, dim3((unsigned)tiles), dim3(256), 0, stream, a);
   return launch_status();
 }
 }  // namespace mx

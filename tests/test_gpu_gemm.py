@@ -87,16 +87,19 @@ def test_mx_pingpong_ragged_mn(orc, fmt, tile, K):
     assert ok, (ratio, bad)
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 520, 512), (300, 520, 1024), (257, 260, 4096), (1, 4, 512),
-                                   (512, 512, 1536), (33, 1028, 2560)])
-def test_mx_ring_ragged(orc, M, N, K):
-    """The MXFP8 4-stage ring kernel (K % 512 == 0, N % 4 == 0): one scale group up to several,
-    partial tiles in M and N, a single row and column strip."""
+@pytest.mark.parametrize("fmt,M,N,K", [
+    (0, 300, 520, 512), (0, 300, 520, 1024), (0, 257, 260, 4096), (0, 1, 4, 512), (0, 512, 512, 1536),
+    (0, 33, 1028, 2560),
+    (4, 300, 520, 1024), (4, 257, 260, 4096), (4, 1, 4, 1024), (4, 512, 512, 2048), (4, 33, 1028, 3072),
+])
+def test_mx_ring_ragged(orc, fmt, M, N, K):
+    """The 4-stage ring kernels (N % 4 == 0; K % 512 == 0 for E4M3, K % 1024 == 0 for E2M1): one
+    scale group up to several, partial tiles in M and N, a single row and column strip."""
     api = require_gpu()
-    say(f"mx ring M={M} N={N} K={K}")
-    C, (oA, oSA, oB, oSB) = mx_case(orc, api, 0, M, N, K, 31 + M + N + K, tile=8)
-    ref = orc.mxgemm(0, 0, oA, oSA, oB, oSB, M, N, K)
-    ok, ratio, bad = orc.check(C, ref, K, R_of(orc, 0, oA, oSA, oB, oSB, M, N, K))
+    say(f"mx ring fmt={fmt} M={M} N={N} K={K}")
+    C, (oA, oSA, oB, oSB) = mx_case(orc, api, fmt, M, N, K, 31 + M + N + K, tile=8)
+    ref = orc.mxgemm(fmt, fmt, oA, oSA, oB, oSB, M, N, K)
+    ok, ratio, bad = orc.check(C, ref, K, R_of(orc, fmt, oA, oSA, oB, oSB, M, N, K))
     assert ok, (ratio, bad)
 
 

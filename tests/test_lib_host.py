@@ -145,9 +145,9 @@ def test_validation_errors_without_gpu():
 
 
 def test_ring_tile_plan_info(monkeypatch):
-    """Tile 8 is the MXFP8 4-stage ring (64-byte K stages) where K % 512 == 0 and N % 4 == 0, and
-    the 8-wave 256x256 kernel elsewhere; without the override the ring is never picked for other
-    shapes or formats."""
+    """Tile 8 is the MX 4-stage ring (64-byte K stages: 64 E4M3 or 128 E2M1 elements) where
+    N % 4 == 0 and K % 512 == 0 (E4M3) or K % 1024 == 0 (E2M1), and the 8-wave 256x256 kernel
+    elsewhere; without the override the ring is never picked where it does not apply."""
     def info(M, N, K, f):
         p = api.mxgemm_create(M, N, K, f, f)
         try:
@@ -158,10 +158,11 @@ def test_ring_tile_plan_info(monkeypatch):
     assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 256, 64, 3)
     assert info(300, 520, 416, api.MX_E4M3) == (256, 256, 128, 1)
     assert info(300, 522, 512, api.MX_E4M3) == (256, 256, 128, 1)
-    assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 256, 1)
+    assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 128, 3)
+    assert info(4096, 8192, 1536, api.MX_E2M1) == (256, 256, 256, 1)
     assert info(512, 512, 512, api.MX_F16) == (256, 256, 64, 1)
     monkeypatch.delenv("MXGEMM_TILE")
-    for M, N, K, f in [(300, 520, 416, api.MX_E4M3), (4096, 8192, 8192, api.MX_E2M1), (512, 512, 512, api.MX_F16)]:
+    for M, N, K, f in [(300, 520, 416, api.MX_E4M3), (4096, 8192, 1536, api.MX_E2M1), (512, 512, 512, api.MX_F16)]:
         assert info(M, N, K, f)[3] != 3
 
 
