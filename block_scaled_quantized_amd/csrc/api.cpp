@@ -55,13 +55,16 @@ struct TileInfo {
   int eff[3];                  // measured relative efficiency per kind (E4M3, E2M1, F16), percent
 };
 // Tile ids understood by gemm_launch. The efficiencies rank the tiles (MI355X measurements at the
-// prefill / large GEMM shapes; 256x256 ping-pong spills registers and is ranked low).
+// prefill / large GEMM shapes; 256x256 ping-pong spills registers and is ranked low; the 256x224
+// ring runs the prefill shape in two whole rounds but no faster than the 256x256 ring's 1.75, so it
+// is ranked below it).
 constexpr TileInfo kTiles[] = {
     {256, 256, 4, 0, {85, 85, 90}}, {256, 224, 4, 0, {80, 75, 55}}, {128, 128, 4, 0, {50, 45, 50}},
     {64, 64, 4, 0, {25, 25, 25}},   {256, 256, 8, 1, {90, 100, 100}}, {256, 224, 8, 1, {88, 95, 60}},
-    {256, 256, 8, 2, {60, 60, 99}}, {256, 224, 8, 2, {100, 95, 60}}, {256, 256, 4, 3, {200, 200, 1}}};
+    {256, 256, 8, 2, {60, 60, 99}}, {256, 224, 8, 2, {100, 95, 60}}, {256, 256, 4, 3, {200, 200, 1}},
+    {256, 224, 4, 3, {170, 160, 1}}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
-constexpr int kRingTile = 8;
+constexpr int kRingTile = 8, kRingTile224 = 9;
 constexpr int kCUs = 256;
 
 bool ring_ok(int kind, int N, int K) {
@@ -76,7 +79,7 @@ int choose_tile(int kind, int M, int N, int K) {
   int best = 0;
   double best_cost = 1e300;
   for (int t = 0; t < kNumTiles; t++) {
-    if (t == kRingTile && !ring_ok(kind, N, K)) continue;
+    if ((t == kRingTile || t == kRingTile224) && !ring_ok(kind, N, K)) continue;
     const int64_t tiles = (int64_t)((M + kTiles[t].bm - 1) / kTiles[t].bm) * ((N + kTiles[t].bn - 1) / kTiles[t].bn);
     const int64_t waves = (tiles + kCUs - 1) / kCUs;
     const double cost = (double)waves * kTiles[t].bm * kTiles[t].bn * 100.0 / kTiles[t].eff[kind];
@@ -137,7 +140,7 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
   *tile_m = t.bm;
   *tile_n = t.bn;
   *tile_k = p->kind == 0 ? 128 : (p->kind == 1 ? 256 : 64);
-  if (p->tile_id == kRingTile) {  // the ring kernel, or the 8-wave kernel where it does not apply
+  if (p->tile_id == kRingTile || p->tile_id == kRingTile224) {  // the ring, or the 8-wave kernel where it does not apply
     const bool ring = ring_ok(p->kind, p->N, p->K);
     *tile_k = ring ? (p->kind == 0 ? 64 : 128) : *tile_k;
     *variant = ring ? 3 : 1;

@@ -700,8 +700,8 @@ int launch(const Args& a0, hipStream_t stream) {
 
 namespace mx {
 
-int gemm_ring_launch(bool fp4, const void* A, const void* SA, const void* B, const void* SB, void* C, int M, int N,
-                     int K, hipStream_t stream);
+int gemm_ring_launch(bool fp4, int bn, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
+                     int N, int K, hipStream_t stream);
 
 // Tile configurations, indexed by the plan. Returns MX_ERR_FORMAT for an unknown id.
 int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
@@ -736,11 +736,17 @@ int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void
       if (kind == KIND_F16) return launch<KIND_F16, 256, 224, 4, 2>(a, stream);
       return kind == KIND_E4M3 ? launch_pp<KIND_E4M3, 256, 224>(a, stream) : launch_pp<KIND_E2M1, 256, 224>(a, stream);
     case 8:  // MX 4-stage ring (N % 4 == 0; K % 512 == 0 E4M3, K % 1024 == 0 E2M1); otherwise the 8-wave kernel
-      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(false, A, SA, B, SB, C, M, N, K, stream);
-      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(true, A, SA, B, SB, C, M, N, K, stream);
+      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(false, 256, A, SA, B, SB, C, M, N, K, stream);
+      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(true, 256, A, SA, B, SB, C, M, N, K, stream);
       if (kind == KIND_E4M3) return launch<KIND_E4M3, 256, 256, 4, 2>(a, stream);
       if (kind == KIND_E2M1) return launch<KIND_E2M1, 256, 256, 4, 2>(a, stream);
       return launch<KIND_F16, 256, 256, 4, 2>(a, stream);
+    case 9:  // the same ring with 256x224 tiles; otherwise the 8-wave 256x224 kernel
+      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(false, 224, A, SA, B, SB, C, M, N, K, stream);
+      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(true, 224, A, SA, B, SB, C, M, N, K, stream);
+      if (kind == KIND_E4M3) return launch<KIND_E4M3, 256, 224, 4, 2>(a, stream);
+      if (kind == KIND_E2M1) return launch<KIND_E2M1, 256, 224, 4, 2>(a, stream);
+      return launch<KIND_F16, 256, 224, 4, 2>(a, stream);
     default: return MX_ERR_FORMAT;
   }
 #undef MX_TILE

@@ -8,44 +8,64 @@
 //
 // Why a ring of short stages: a 256x224 tile with 128-byte K stages fills LDS with two stages, so
 // each stage's copy has to land within one stage of MFMAs (about 1800 cycles), less than the L2 /
-// MALL latency under load. Here a stage is 64 bytes of K, one scaled MFMA 32x32x64 deep:
-//  - Tile 256 x 256, 4 waves (one per SIMD), each wave 128 x 128 = 4 x 4 MFMA tiles of 32 x 32.
+// MALL latency under load. Here a stage is 64 bytes of K: one scaled MFMA 32x32x64 deep for E4M3,
+// two for E2M1.
+//  - Tile 256 x 256 with 4 waves (one per SIMD) of 128 x 128 = 4 x 4 MFMA tiles of 32 x 32, or
+//    256 x 224 with 4 waves of 64 x 224 = 2 x 7 MFMA tiles (224 = 7 x 32 does not split in two:
+//    the 256 x 224 tile exists so that N = 14336 gives 64 column tiles, a whole number of rounds
+//    on 256 CUs at M = 2048).
 //  - LDS ring of 4 stages (4 separate arrays, so the compiler can tell a fragment read of one
-//    stage from the direct copies filling another): 256 + 256 rows x 64 bytes per stage. Copies for
-//    stage t+3 are queued while stage t computes, three stages (about 3000 cycles) ahead.
+//    stage from the direct copies filling another): up to 256 + 256 rows x 64 bytes per stage.
+//    Copies for stage t+3 are queued while stage t computes, three stages ahead.
 //  - 64-byte rows hold four 16-byte chunks, stored at chunk ^ ((row >> 2) & 3): a 16-lane quarter of
 //    a fragment read (16 rows, one chunk) then covers all 64 banks once.
 //  - Direct global->LDS copies (16 bytes per lane): instruction i of a stage fills rows
-//    16i..16i+15; lane l fills physical chunk l%4 of row 16i + l/4.
-//  - E8M0 scales for 8 stages (16 bytes per row) are copied once per group into the scale array
-//    (after every wave has read the previous group's); each lane packs its own K-block's bytes so that byte s%4 of dword s/4 is its scale for
-//    stage s of the group (op_sel picks the byte).
+//    16i..16i+15; lane l fills physical chunk l%4 of row 16i + l/4. Each wave issues 8 per stage;
+//    instructions past the tile's rows get an empty buffer resource and fill unused slot bytes
+//    with zeros, so every wave's copy count (and its vmcnt bookkeeping) is the same.
+//  - E8M0 scales for 8 stages (16 / 32 bytes per row) are copied once per group into the scale
+//    array (after every wave has read the previous group's); each lane packs its own K-block's
+//    bytes so that byte u%4 of dword u/4 is its scale for K-step u of the group (op_sel picks the
+//    byte).
 //  - Fragments of stage t+1 are read from LDS while the MFMAs of stage t run; one barrier per
 //    stage, after this wave's copies of stage t+1 have landed (vmcnt), publishes stage t+1 and
 //    frees the slot of stage t-1.
-// Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 (measured): lane l feeds row l%32 and K bytes
-// 16h..16h+15 and 32+16h..32+16h+15 (h = l/32) and supplies the scale of (row l%32, K-block h);
-// output element e of lane l is row 8(e/4) + 4h + e%4 of the first operand and column l%32 of the
-// second. B is the first operand, so each lane ends with 4 consecutive n of one row m.
+// Operand layout of v_mfma_scale_f32_32x32x64_f8f6f4 (measured): lane l feeds row l%32 and, with
+// h = l/32, E4M3 K bytes 16h..16h+15 and 32+16h..32+16h+15, or E2M1 elements 32h..32h+31 (16
+// bytes); it supplies the scale of (row l%32, K-block h); output element e of lane l is row
+// 8(e/4) + 4h + e%4 of the first operand and column l%32 of the second. B is the first operand, so
+// each lane ends with 4 consecutive n of one row m.
 #include <type_traits>
 
 #include "common.h"
 
 namespace {
 
+typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int BM = 256, BN = 256;       // tile
+constexpr int BM = 256;                 // tile rows (both shapes)
 constexpr int ROWB = 64;                // K bytes per stage
-constexpr int ROWS = BM + BN;           // LDS rows per stage (A then B)
-constexpr int SLOT = ROWS * ROWB;       // 32 KB
+constexpr int SLOT = 512 * ROWB;        // 32 KB: room for 256 + 256 rows
 constexpr int GROUP = 8;                // stages per scale group
 constexpr int DMA_PER_STAGE = SLOT / 1024 / 4;  // direct copies per wave per stage (8)
+
+// Tile shapes. WAVES_M waves along M (the rest along N); each wave holds FA x FB MFMA tiles of
+// 32 x 32 (FA along M, FB along N).
+template <int WAVES_M_>
+struct RingTile {
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = 4 / WAVES_M;
+  static constexpr int BN = WAVES_M == 2 ? 256 : 224;
+  static constexpr int FA = BM / 32 / WAVES_M, FB = BN / 32 / WAVES_N;
+  static constexpr int F = FA + FB;  // fragments read per stage per wave
+  static_assert(WAVES_M == 2 || WAVES_M == 4, "tile");
+};
 
 // Per-format constants. A 64-byte stage is one MFMA K-step of E4M3 (64 elements, 2 scale blocks)
 // or two of E2M1 (128 elements, 4 blocks); a group of 8 stages then holds 16 or 32 scale bytes per
@@ -54,9 +74,7 @@ template <int KIND>
 struct RingFmt {
   static constexpr bool FP4 = KIND == 1;
   static constexpr int KSTEPS = FP4 ? 2 : 1;        // MFMA K-steps per stage
-  static constexpr int CBSZ = FP4 ? 4 : 0;          // MFMA operand format (FP4 / FP8)
-  static constexpr int SB_ROW = 16 * KSTEPS;        // scale bytes per row per group
-  static constexpr int SGRP = ROWS * SB_ROW;        // 8 / 16 KB
+  static constexpr int SGRP = 512 * 16 * KSTEPS;    // scale array: 8 / 16 KB
   static constexpr int SDW = 2 * KSTEPS;            // packed scale dwords per row per lane
   static constexpr int DMA_PER_GROUP = SGRP / 1024 / 4;  // scale copies per wave per group (2 / 4)
   static constexpr int ELEMS_PER_BYTE = FP4 ? 2 : 1;
@@ -94,9 +112,9 @@ struct Args {
 
 // Per lane: byte u%4 of dword u/4 is the lane's scale for MFMA K-step u of the group (u = stage for
 // E4M3, 2*stage + k for K-step k of a stage for E2M1).
-template <int KIND>
+template <int KIND, class T>
 struct Scales {
-  uint32_t a[4][RingFmt<KIND>::SDW], b[4][RingFmt<KIND>::SDW];
+  uint32_t a[T::FA][RingFmt<KIND>::SDW], b[T::FB][RingFmt<KIND>::SDW];
 };
 
 MX_DEV int phys_off(int row, int chunk) { return row * ROWB + ((chunk ^ ((row >> 2) & 3)) << 4); }
@@ -113,51 +131,55 @@ MX_DEV v4i lds16(const char* base, int off) { return *reinterpret_cast<const v4i
 // group's stage 2: the reads have a stage or more to land before anything waits for them. The
 // packed value of stage 2 is unchanged in group 0, whose halves the prologue packs.
 template <int KIND>
-struct RawScales {
-  typedef int raw_t __attribute__((ext_vector_type(2 * RingFmt<KIND>::KSTEPS)));
-  raw_t a[4], b[4];
+struct RawT {
+  typedef int type __attribute__((ext_vector_type(2 * RingFmt<KIND>::KSTEPS)));
 };
 
+template <int KIND, class T>
+struct RawScales {
+  typename RawT<KIND>::type a[T::FA], b[T::FB];
+};
+
+// Rows of the wave's fragments: A fragment j is LDS row 32*FA*wm + 32j + l%32, B fragment i is
+// row BM + 32*FB*wn + 32i + l%32.
+template <class T>
+MX_DEV int row_a(int j, int wm, int r32) { return 32 * T::FA * wm + 32 * j + r32; }
+template <class T>
+MX_DEV int row_b(int i, int wn, int r32) { return BM + 32 * T::FB * wn + 32 * i + r32; }
+
 template <int KIND>
-MX_DEV const typename RawScales<KIND>::raw_t& raw_at(const char* sg, int row, int d) {
-  typedef typename RawScales<KIND>::raw_t raw_t;
+MX_DEV typename RawT<KIND>::type raw_at(const char* sg, int row, int d) {
+  typedef typename RawT<KIND>::type raw_t;
   if constexpr (RingFmt<KIND>::FP4) return *reinterpret_cast<const raw_t*>(sg + d * 8192 + row * 16);
   else return *reinterpret_cast<const raw_t*>(sg + row * 16 + 8 * d);
 }
 
-template <int KIND>
-MX_DEV void read_raw_scales(const char* sg, RawScales<KIND>& r, int d, int wm, int wn, int r32) {
+template <int KIND, class T>
+MX_DEV void read_raw_scales(const char* sg, RawScales<KIND, T>& r, int d, int wm, int wn, int r32) {
 #pragma unroll
-  for (int j = 0; j < 4; j++) r.a[j] = raw_at<KIND>(sg, 128 * wm + 32 * j + r32, d);
+  for (int j = 0; j < T::FA; j++) r.a[j] = raw_at<KIND>(sg, row_a<T>(j, wm, r32), d);
 #pragma unroll
-  for (int i = 0; i < 4; i++) r.b[i] = raw_at<KIND>(sg, BM + 128 * wn + 32 * i + r32, d);
+  for (int i = 0; i < T::FB; i++) r.b[i] = raw_at<KIND>(sg, row_b<T>(i, wn, r32), d);
 }
 
-template <int KIND>
-MX_DEV void pack_scales(const RawScales<KIND>& r, Scales<KIND>& s, int d, int h) {
+template <int KIND, class T>
+MX_DEV void pack_scales(const RawScales<KIND, T>& r, Scales<KIND, T>& s, int d, int h) {
   constexpr int KS = RingFmt<KIND>::KSTEPS;
   const uint32_t sel = h ? 0x07050301u : 0x06040200u;
 #pragma unroll
   for (int w = 0; w < KS; w++) {
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < T::FA; j++)
       s.a[j][KS * d + w] = __builtin_amdgcn_perm((uint32_t)r.a[j][2 * w + 1], (uint32_t)r.a[j][2 * w], sel);
 #pragma unroll
-    for (int i = 0; i < 4; i++)
+    for (int i = 0; i < T::FB; i++)
       s.b[i][KS * d + w] = __builtin_amdgcn_perm((uint32_t)r.b[i][2 * w + 1], (uint32_t)r.b[i][2 * w], sel);
   }
 }
 
-// B fragment i of one stage (rows 256 + 128*wn + 32i + l%32) and A fragment j (rows 128*wm + 32j):
-// chunks h and 2+h of the row, i.e. the lane's K bytes of the E4M3 MFMA, or its 16 bytes (K-block
-// h) of E2M1 K-steps 0 and 1 in the low and high halves.
-MX_DEV v8i read_b(const char* slot, int i, int wn, int r32, int h) {
-  const int row = BM + 128 * wn + 32 * i + r32;
-  return __builtin_shufflevector(lds16(slot, phys_off(row, h)), lds16(slot, phys_off(row, 2 + h)), 0, 1, 2, 3, 4, 5,
-                                 6, 7);
-}
-MX_DEV v8i read_a(const char* slot, int j, int wm, int r32, int h) {
-  const int row = 128 * wm + 32 * j + r32;
+// A fragment of one stage: chunks h and 2+h of its row, i.e. the lane's K bytes of the E4M3 MFMA,
+// or its 16 bytes (K-block h) of E2M1 K-steps 0 and 1 in the low and high halves.
+MX_DEV v8i read_frag(const char* slot, int row, int h) {
   return __builtin_shufflevector(lds16(slot, phys_off(row, h)), lds16(slot, phys_off(row, 2 + h)), 0, 1, 2, 3, 4, 5,
                                  6, 7);
 }
@@ -185,15 +207,15 @@ MX_DEV void issue_scales(const Ctx& c, char* sg, int g) {
 // One stage t = 8g + S8: slot t%4 holds stage t (its fragments already in ca/cb). Before the
 // barrier this wave's copies of stage t+1 must have landed; after it, slot (t+3)%4 (stage t-1,
 // read during stage t-2) is free and stage t+1 is readable by every wave. The MFMAs go B tile by B
-// tile; after each tile come two copies of stage t+3 and two of the next stage's fragments, into
-// the other register set (dead during this stage): the A fragments first, as the next stage's first
-// B tile needs all four, then the B fragments in the order their tiles come.
-// The next-stage reads are unconditional (after the last stage they fetch unused bytes): a
+// tile; after each tile come its share of the 8 copies of stage t+3 and of the next stage's
+// fragments, read into the other register set (dead during this stage): the A fragments first, as
+// the next stage's first B tile needs all of them, then the B fragments in the order their tiles
+// come. The next-stage reads are unconditional (after the last stage they fetch unused bytes): a
 // conditional overwrite would keep the old contents alive through the stage.
-template <int KIND, int S8>
-MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[4], const v8i (&cb)[4],
-                       v8i (&na)[4], v8i (&nb)[4], const char* slot_nxt, char* slot_fill, Scales<KIND>& sc,
-                       RawScales<KIND>& raw, v16f (&acc)[4][4]) {
+template <int KIND, class T, int S8>
+MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], const v8i (&cb)[T::FB],
+                       v8i (&na)[T::FA], v8i (&nb)[T::FB], const char* slot_nxt, char* slot_fill,
+                       Scales<KIND, T>& sc, RawScales<KIND, T>& raw, v16f (&acc)[T::FB][T::FA]) {
   using F = RingFmt<KIND>;
   const int t = GROUP * g + S8;
   // Copies queued after this wave's copies of stage t+1 (issued at stage t-2): those of stage t+2
@@ -207,12 +229,12 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[4], cons
   if (S8 == 2) issue_scales<KIND>(c, sgrp, min(g + 1, c.ngroups - 1));
   const uint32_t fill_off = ROWB * min(t + 3, c.nst - 1);
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < T::FB; i++) {
 #pragma unroll
     for (int k = 0; k < F::KSTEPS; k++) {
       constexpr int U0 = F::KSTEPS * S8;  // first K-step of the stage within the group
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
+      for (int j = 0; j < T::FA; j++) {
         if constexpr (F::FP4) {
           const v8i bk = k ? __builtin_shufflevector(cb[i], cb[i], 4, 5, 6, 7, -1, -1, -1, -1)
                            : __builtin_shufflevector(cb[i], cb[i], 0, 1, 2, 3, -1, -1, -1, -1);
@@ -230,28 +252,30 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[4], cons
         }
       }
     }
+    // this tile's share of the stage copies: copies [8i/FB, 8(i+1)/FB)
 #pragma unroll
-    for (int k = 2 * i; k < 2 * i + 2; k++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(slot_fill + (c.wave + 4 * k) * 1024), 16,
+    for (int q = DMA_PER_STAGE * i / T::FB; q < DMA_PER_STAGE * (i + 1) / T::FB; q++)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[q], (lds_ptr_t)(slot_fill + (c.wave + 4 * q) * 1024), 16,
                                                c.voff, fill_off, 0, 0);
-    if (i < 2) {
-      na[2 * i] = read_a(slot_nxt, 2 * i, c.wm, c.r32, c.h);
-      na[2 * i + 1] = read_a(slot_nxt, 2 * i + 1, c.wm, c.r32, c.h);
-    } else {
-      nb[2 * i - 4] = read_b(slot_nxt, 2 * i - 4, c.wn, c.r32, c.h);
-      nb[2 * i - 3] = read_b(slot_nxt, 2 * i - 3, c.wn, c.r32, c.h);
+    // and of the next stage's fragments: list positions [F*i/FB, F*(i+1)/FB) of A0.., B0..
+#pragma unroll
+    for (int f = T::F * i / T::FB; f < T::F * (i + 1) / T::FB; f++) {
+      if (f < T::FA) na[f] = read_frag(slot_nxt, row_a<T>(f, c.wm, c.r32), c.h);
+      else nb[f - T::FA] = read_frag(slot_nxt, row_b<T>(f - T::FA, c.wn, c.r32), c.h);
     }
-    if (S8 == 4 && i == 1) read_raw_scales<KIND>(sgrp, raw, 0, c.wm, c.wn, c.r32);
+    if (S8 == 4 && i == 1) read_raw_scales<KIND, T>(sgrp, raw, 0, c.wm, c.wn, c.r32);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (S8 == 2) pack_scales<KIND>(raw, sc, 1, c.h);
-  if (S8 == 6) pack_scales<KIND>(raw, sc, 0, c.h);
-  if (S8 == GROUP - 1) read_raw_scales<KIND>(sgrp, raw, 1, c.wm, c.wn, c.r32);
+  if (S8 == 2) pack_scales<KIND, T>(raw, sc, 1, c.h);
+  if (S8 == 6) pack_scales<KIND, T>(raw, sc, 0, c.h);
+  if (S8 == GROUP - 1) read_raw_scales<KIND, T>(sgrp, raw, 1, c.wm, c.wn, c.r32);
 }
 
-template <int KIND>
+template <int KIND, int WAVES_M>
 __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   using F = RingFmt<KIND>;
+  using T = RingTile<WAVES_M>;
+  constexpr int BN = T::BN;
   __shared__ __attribute__((aligned(16))) char slot0[SLOT];
   __shared__ __attribute__((aligned(16))) char slot1[SLOT];
   __shared__ __attribute__((aligned(16))) char slot2[SLOT];
@@ -260,7 +284,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % T::WAVES_M, wn = wave / T::WAVES_M;
   const int r32 = lane & 31, h = lane >> 5;
 
   int bid = blockIdx.x;
@@ -273,10 +297,10 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   const int nst = (int)RB / ROWB, ngroups = nst / GROUP;
 
   // Direct copies. Copy k (0..7) of this wave in a stage is stage instruction i = wave + 4k: rows
-  // 16i + l/4 of the stage (A rows for k < 4, B rows 16(i-16) + l/4 for k >= 4), lane l filling
+  // 16i + l/4 of the stage (A rows for i < 16, B rows 16(i-16) + l/4 beyond), lane l filling
   // physical chunk l%4, i.e. logical chunk (l%4) ^ ((l/16) & 3). Each copy gets its own buffer
-  // resource over its 16 rows (clamped to the matrix), so one lane offset serves all eight and rows
-  // past the edge fall outside the resource and read as zero (their outputs are never stored).
+  // resource over its 16 rows (clamped to the matrix, empty past the tile), so one lane offset
+  // serves all eight and rows past the edge read as zero (their outputs are never stored).
   Ctx c;
   c.wave = wave;
   c.wm = wm;
@@ -308,11 +332,11 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
     c.rscale[k] = make_rsrc(base, (uint32_t)nr * nblk);
   }
 
-  v16f acc[4][4];
+  v16f acc[T::FB][T::FA];
 #pragma unroll
-  for (int i = 0; i < 4; i++)
+  for (int i = 0; i < T::FB; i++)
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+    for (int j = 0; j < T::FA; j++)
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
@@ -327,28 +351,28 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): prologue copies of this wave
   raw_barrier();
-  v8i xa[4], xb[4], ya[4], yb[4];
-  Scales<KIND> sc;
-  RawScales<KIND> raw;
-  read_raw_scales<KIND>(sgrp, raw, 0, wm, wn, r32);
-  pack_scales<KIND>(raw, sc, 0, h);
-  read_raw_scales<KIND>(sgrp, raw, 1, wm, wn, r32);
-  pack_scales<KIND>(raw, sc, 1, h);
+  v8i xa[T::FA], xb[T::FB], ya[T::FA], yb[T::FB];
+  Scales<KIND, T> sc;
+  RawScales<KIND, T> raw;
+  read_raw_scales<KIND, T>(sgrp, raw, 0, wm, wn, r32);
+  pack_scales<KIND, T>(raw, sc, 0, h);
+  read_raw_scales<KIND, T>(sgrp, raw, 1, wm, wn, r32);
+  pack_scales<KIND, T>(raw, sc, 1, h);
 #pragma unroll
-  for (int j = 0; j < 4; j++) xa[j] = read_a(slot0, j, wm, r32, h);
+  for (int j = 0; j < T::FA; j++) xa[j] = read_frag(slot0, row_a<T>(j, wm, r32), h);
 #pragma unroll
-  for (int i = 0; i < 4; i++) xb[i] = read_b(slot0, i, wn, r32, h);
+  for (int i = 0; i < T::FB; i++) xb[i] = read_frag(slot0, row_b<T>(i, wn, r32), h);
 
   // Stage t uses slot t%4 (t = 8g + s: slot s%4); even stages compute from x*, odd from y*.
   for (int g = 0; g < ngroups; g++) {
-    ring_stage<KIND, 0>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, acc);
-    ring_stage<KIND, 1>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, acc);
-    ring_stage<KIND, 2>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, acc);
-    ring_stage<KIND, 3>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
-    ring_stage<KIND, 4>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, acc);
-    ring_stage<KIND, 5>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, acc);
-    ring_stage<KIND, 6>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, acc);
-    ring_stage<KIND, 7>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
+    ring_stage<KIND, T, 0>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, acc);
+    ring_stage<KIND, T, 1>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, acc);
+    ring_stage<KIND, T, 2>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, acc);
+    ring_stage<KIND, T, 3>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
+    ring_stage<KIND, T, 4>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, acc);
+    ring_stage<KIND, T, 5>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, acc);
+    ring_stage<KIND, T, 6>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, acc);
+    ring_stage<KIND, T, 7>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
   }
 
   // The last stages queued copies of stage nst-1 into free slots: let them land, and let every
@@ -356,43 +380,43 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);
   raw_barrier();
 
-  // Epilogue. The lane holds C[m0 + 128wm + 32j + r32][n0 + 128wn + 32i + 8q + 4h + e] in
+  // Epilogue. The lane holds C[m0 + 32*FA*wm + 32j + r32][n0 + 32*FB*wn + 32i + 8q + 4h + e] in
   // acc[i][j][4q + e]: 8 bytes per row, so storing straight from registers would write each
-  // 128-byte line of C in eight pieces from eight instructions. Instead each wave converts to fp16
-  // into its own slot, 64 rows at a time (rows padded to 264 bytes: the 8-byte writes of 32 rows
-  // then fall on distinct banks), and writes the rows back 16 bytes per lane, 256 contiguous bytes
-  // per row.
+  // 128-byte line of C in pieces from several instructions. Instead each wave converts to fp16 into
+  // its own slot, 32 rows (one A tile) at a time with rows padded by 8 bytes (the 8-byte writes of
+  // the 32 rows then fall on distinct banks), and writes the rows back as 16-byte pieces,
+  // consecutive lanes along a row.
   char* stage = wave == 0 ? slot0 : (wave == 1 ? slot1 : (wave == 2 ? slot2 : slot3));
-  constexpr int EROW = 264;
+  constexpr int WCOLS = 32 * T::FB;            // columns of the wave's block
+  constexpr int EROW = 2 * WCOLS + 8;          // staged row pitch, bytes
+  constexpr int LPR = WCOLS / 8;               // 16-byte pieces per row
+  constexpr int PIECES = 32 * LPR;             // per A tile: a multiple of 64
+  static_assert(PIECES % 64 == 0 && 32 * EROW <= SLOT, "epilogue staging");
+  const bool rows16 = (p.N & 7) == 0;          // row starts 16-byte aligned
 #pragma unroll
-  for (int half = 0; half < 2; half++) {
+  for (int j = 0; j < T::FA; j++) {
 #pragma unroll
-    for (int jj = 0; jj < 2; jj++)
+    for (int i = 0; i < T::FB; i++)
 #pragma unroll
-      for (int i = 0; i < 4; i++)
+      for (int q = 0; q < 4; q++) {
+        v4h o;
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-          v4h o;
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const float v = acc[i][2 * half + jj][4 * q + e];
-            o[e] = (_Float16)v;
-          }
-          *reinterpret_cast<v4h*>(stage + (32 * jj + r32) * EROW + (32 * i + 8 * q + 4 * h) * 2) = o;
+        for (int e = 0; e < 4; e++) {
+          const float v = acc[i][j][4 * q + e];
+          o[e] = (_Float16)v;
         }
-    // 64 rows x 256 bytes: instruction s covers rows 4s..4s+3, lane l row 4s + l/16, bytes 16(l%16)
-    const int cl = lane & 15, n = n0 + 128 * wn + 8 * cl;
+        *reinterpret_cast<v4h*>(stage + r32 * EROW + (32 * i + 8 * q + 4 * h) * 2) = o;
+      }
 #pragma unroll
-    for (int s4 = 0; s4 < 16; s4++) {
-      const int lr = 4 * s4 + (lane >> 4);
-      const int m = m0 + 128 * wm + 64 * half + lr;
-      typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-      const char* src = stage + lr * EROW + 16 * cl;
+    for (int s0 = 0; s0 < PIECES; s0 += 64) {
+      const int piece = s0 + lane, lr = piece / LPR, cp = piece % LPR;
+      const char* src = stage + lr * EROW + 16 * cp;
       const v4h lo = *reinterpret_cast<const v4h*>(src), hi = *reinterpret_cast<const v4h*>(src + 8);
+      const int m = m0 + 32 * T::FA * wm + 32 * j + lr, n = n0 + WCOLS * wn + 8 * cp;
       if (m < p.M) {
         _Float16* dst = p.C + (int64_t)m * p.N + n;
         if (n + 8 <= p.N) {
-          if ((p.N & 7) == 0) {  // rows start 16-byte aligned
+          if (rows16) {
             *reinterpret_cast<v8h*>(dst) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           } else {
             *reinterpret_cast<v4h*>(dst) = lo;
@@ -410,9 +434,9 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
 
 namespace mx {
 // MX ring kernels. fp4 = false: E4M3, requires K % 512 == 0; fp4 = true: E2M1, requires
-// K % 1024 == 0; both require N % 4 == 0 (checked by the caller).
-int gemm_ring_launch(bool fp4, const void* A, const void* SA, const void* B, const void* SB, void* C, int M, int N,
-                     int K, hipStream_t stream) {
+// K % 1024 == 0; both require N % 4 == 0 (checked by the caller). bn = 256 or 224.
+int gemm_ring_launch(bool fp4, int bn, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
+                     int N, int K, hipStream_t stream) {
   Args a{};
   a.A = (const uint8_t*)A;
   a.SA = (const uint8_t*)SA;
@@ -423,11 +447,15 @@ int gemm_ring_launch(bool fp4, const void* A, const void* SA, const void* B, con
   a.N = N;
   a.K = K;
   a.tiles_m = (M + BM - 1) / BM;
-  const int tiles = a.tiles_m * ((N + BN - 1) / BN);
-  if (fp4)
-    hipLaunchKernelGGL(gemm_ring_kernel<1>, dim3((unsigned)tiles), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(gemm_ring_kernel<0>, dim3((unsigned)tiles), dim3(256), 0, stream, a);
+  const int tiles = a.tiles_m * ((N + bn - 1) / bn);
+  const dim3 grid((unsigned)tiles), block(256);
+  if (bn == 224) {
+    if (fp4) hipLaunchKernelGGL((gemm_ring_kernel<1, 4>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gemm_ring_kernel<0, 4>), grid, block, 0, stream, a);
+  } else {
+    if (fp4) hipLaunchKernelGGL((gemm_ring_kernel<1, 2>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((gemm_ring_kernel<0, 2>), grid, block, 0, stream, a);
+  }
   return launch_status();
 }
 }  // namespace mx

@@ -58,7 +58,7 @@ def test_mx_small_config_full(orc, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 4])
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
 def test_mx_every_tile_ragged(orc, fmt, tile):
     """Each tile configuration on a shape spanning several tiles with ragged M, N and K tails."""
     api = require_gpu()
@@ -92,12 +92,14 @@ def test_mx_pingpong_ragged_mn(orc, fmt, tile, K):
     (0, 33, 1028, 2560),
     (4, 300, 520, 1024), (4, 257, 260, 4096), (4, 1, 4, 1024), (4, 512, 512, 2048), (4, 33, 1028, 3072),
 ])
-def test_mx_ring_ragged(orc, fmt, M, N, K):
-    """The 4-stage ring kernels (N % 4 == 0; K % 512 == 0 for E4M3, K % 1024 == 0 for E2M1): one
-    scale group up to several, partial tiles in M and N, a single row and column strip."""
+@pytest.mark.parametrize("tile", [8, 9])
+def test_mx_ring_ragged(orc, fmt, M, N, K, tile):
+    """The 4-stage ring kernels, 256x256 (tile 8) and 256x224 (tile 9) tiles (N % 4 == 0; K % 512 == 0
+    for E4M3, K % 1024 == 0 for E2M1): one scale group up to several, partial tiles in M and N, a
+    single row and column strip."""
     api = require_gpu()
-    say(f"mx ring fmt={fmt} M={M} N={N} K={K}")
-    C, (oA, oSA, oB, oSB) = mx_case(orc, api, fmt, M, N, K, 31 + M + N + K, tile=8)
+    say(f"mx ring tile={tile} fmt={fmt} M={M} N={N} K={K}")
+    C, (oA, oSA, oB, oSB) = mx_case(orc, api, fmt, M, N, K, 31 + M + N + K, tile=tile)
     ref = orc.mxgemm(fmt, fmt, oA, oSA, oB, oSB, M, N, K)
     ok, ratio, bad = orc.check(C, ref, K, R_of(orc, fmt, oA, oSA, oB, oSB, M, N, K))
     assert ok, (ratio, bad)
@@ -228,7 +230,7 @@ def fp16_case(orc, api, M, N, K, seed, tile=None):
     return A, B, C
 
 
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4, 5, 6, 7, 8, 9])
 def test_f16_every_tile_ragged(orc, tile):
     api = require_gpu()
     M, N, K = 300, 520, 200

@@ -161,7 +161,13 @@ def test_ring_tile_plan_info(monkeypatch):
     assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 128, 3)
     assert info(4096, 8192, 1536, api.MX_E2M1) == (256, 256, 256, 1)
     assert info(512, 512, 512, api.MX_F16) == (256, 256, 64, 1)
+    monkeypatch.setenv("MXGEMM_TILE", "9")
+    assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 224, 64, 3)
+    assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 224, 128, 3)
+    assert info(300, 520, 416, api.MX_E4M3) == (256, 224, 128, 1)
     monkeypatch.delenv("MXGEMM_TILE")
+    assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 256, 64, 3)
+    assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 128, 3)
     for M, N, K, f in [(300, 520, 416, api.MX_E4M3), (4096, 8192, 1536, api.MX_E2M1), (512, 512, 512, api.MX_F16)]:
         assert info(M, N, K, f)[3] != 3
 
