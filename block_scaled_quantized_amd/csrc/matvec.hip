@@ -141,16 +141,25 @@ MX_DEV void weights_to_frags(const Stage<I8, C>& s, int g, v8h (&frag)[4]) {
         f[3][p] = __builtin_bit_cast(uint32_t, as_v2h(pick_pair(o, o, 0x0C030C01u) ^ 0x64086408u) - bias);
       } else {
         // word g/2 of rows 2p, 2p+1 holds 8 nibbles (column 2b in the low nibble of byte b); this
-        // group is its bytes 2*(g%2) and 2*(g%2)+1
-        const uint32_t ua = s.w[2 * p][g / 2], ub = s.w[2 * p + 1][g / 2];
-        const uint32_t ea = ua & 0x0F0F0F0Fu, oa = (ua >> 4) & 0x0F0F0F0Fu;
-        const uint32_t eb = ub & 0x0F0F0F0Fu, ob = (ub >> 4) & 0x0F0F0F0Fu;
+        // group is its bytes 2*(g%2) and 2*(g%2)+1. With every nibble xor 8 (offset binary q + 8),
+        // byte b of both rows goes to bits 0-7 and 16-23; the low nibbles or'ed into fp16 1024
+        // give 1024 + q + 8 (subtract 1032), the high nibbles give 1024 + 16 (q + 8) (times 1/16,
+        // minus 72): one permute, two and-or and one packed fp16 op per pair of weights, all exact.
+        // (the masks and the exponent live in VGPRs, so each and-or is one v_and_or_b32: a VOP3
+        // instruction cannot take two literal constants)
+        uint32_t m_lo, m_hi, e_one;
+        asm("v_mov_b32 %0, 0x000f000f" : "=v"(m_lo));
+        asm("v_mov_b32 %0, 0x00f000f0" : "=v"(m_hi));
+        asm("v_mov_b32 %0, 0x64006400" : "=v"(e_one));
+        const uint32_t ua = s.w[2 * p][g / 2] ^ 0x88888888u, ub = s.w[2 * p + 1][g / 2] ^ 0x88888888u;
 #pragma unroll
         for (int h = 0; h < 2; h++) {
           const uint32_t b = 2u * (uint32_t)(g % 2) + (uint32_t)h;
           const uint32_t sel = b | (0x0Cu << 8) | ((4u + b) << 16) | (0x0Cu << 24);
-          f[2 * h][p] = __builtin_bit_cast(uint32_t, as_v2h(pick_pair(eb, ea, sel) ^ 0x64086408u) - bias);
-          f[2 * h + 1][p] = __builtin_bit_cast(uint32_t, as_v2h(pick_pair(ob, oa, sel) ^ 0x64086408u) - bias);
+          const uint32_t xb = pick_pair(ub, ua, sel);
+          const v2h lo = as_v2h((xb & m_lo) | e_one), hi = as_v2h((xb & m_hi) | e_one);
+          f[2 * h][p] = __builtin_bit_cast(uint32_t, lo - bias);
+          f[2 * h + 1][p] = __builtin_bit_cast(uint32_t, hi * as_v2h(0x2C002C00u) - as_v2h(0x54805480u));
         }
       }
     }
