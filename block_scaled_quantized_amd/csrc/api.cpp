@@ -9,7 +9,7 @@
 
 namespace mx {
 int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
-                int N, int K, hipStream_t stream);
+                int N, int K, bool relu, hipStream_t stream);
 int matvec_launch(int M, int N, int K, const void* x, const void* W, bool int8, const void* Ws, void* y, void* ws,
                   size_t ws_bytes, hipStream_t stream);
 size_t matvec_workspace(int M, int N, int K, bool int8);
@@ -45,6 +45,7 @@ using namespace mx;
 
 struct mxgemm_plan {
   int M, N, K, fa, fb, kind, tile_id;
+  unsigned flags;
 };
 
 namespace {
@@ -114,7 +115,7 @@ int mx_version(void) { return 100; }
 int mxgemm_create(mxgemm_t* out, int M, int N, int K, int fa, int fb, unsigned flags) {
   if (!out) return MX_ERR_NULL;
   *out = nullptr;
-  if (flags != 0u) return MX_ERR_FORMAT;
+  if (flags & ~(unsigned)MXGEMM_RELU) return MX_ERR_FORMAT;
   int kind;
   if (fa == MX_E4M3 && fb == MX_E4M3) kind = 0;
   else if (fa == MX_E2M1 && fb == MX_E2M1) kind = 1;
@@ -123,7 +124,7 @@ int mxgemm_create(mxgemm_t* out, int M, int N, int K, int fa, int fb, unsigned f
   if (M < 1 || N < 1 || K < 32 || M > MX_MAX_DIM || N > MX_MAX_DIM || K > MX_MAX_DIM) return MX_ERR_SHAPE;
   if (kind != 2 && K % 32) return MX_ERR_SHAPE;
   if (kind == 2 && (K % 8 || N % 8)) return MX_ERR_SHAPE;
-  mxgemm_plan* p = new (std::nothrow) mxgemm_plan{M, N, K, fa, fb, kind, choose_tile(kind, M, N, K)};
+  mxgemm_plan* p = new (std::nothrow) mxgemm_plan{M, N, K, fa, fb, kind, choose_tile(kind, M, N, K), flags};
   if (!p) return MX_ERR_NOMEM;
   *out = p;
   return MX_OK;
@@ -158,7 +159,8 @@ int mxgemm_run(mxgemm_t p, const void* A, const void* SA, const void* B, const v
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return MX_ERR_ALIGN;
   if (p->kind != 2 && (!aligned16(SA) || !aligned16(SB))) return MX_ERR_ALIGN;
   if (int a = check_arch()) return a;
-  return gemm_launch(p->kind, p->tile_id, A, SA, B, SB, C, p->M, p->N, p->K, as_stream(stream));
+  return gemm_launch(p->kind, p->tile_id, A, SA, B, SB, C, p->M, p->N, p->K, (p->flags & MXGEMM_RELU) != 0u,
+                     as_stream(stream));
 }
 
 static int matvec_shape(int M, int N, int K, int fw) {

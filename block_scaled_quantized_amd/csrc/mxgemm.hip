@@ -88,6 +88,7 @@ struct Args {
   int64_t a_row_bytes;  // bytes of one row of A (and of B for MX kinds)
   int nblk;             // K / 32
   int nstages;
+  int relu;             // epilogue: C = max(C, 0) (IEEE maxNum: NaN gives 0)
 };
 
 MX_DEV void g2l(const void* g, char* lds_wave_base, int size) {
@@ -389,7 +390,10 @@ MX_DEV void store_c(const Args& p, const v4f (&acc)[CF::FN][CF::FM], char* ws, i
   for (int j = 0; j < CF::FM; j++) {
 #pragma unroll
     for (int i = 0; i < CF::FN; i++) {
-      const v4f a = acc[i][j];
+      v4f a = acc[i][j];
+      if (p.relu)
+#pragma unroll
+        for (int v = 0; v < 4; v++) a[v] = fmaxf(a[v], 0.0f);
       *reinterpret_cast<v4h*>(ws + r16 * C_PITCH<CF> + (16 * i + 4 * q) * 2) =
           v4h{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3]};
     }
@@ -701,11 +705,11 @@ int launch(const Args& a0, hipStream_t stream) {
 namespace mx {
 
 int gemm_ring_launch(bool fp4, int bn, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
-                     int N, int K, hipStream_t stream);
+                     int N, int K, bool relu, hipStream_t stream);
 
 // Tile configurations, indexed by the plan. Returns MX_ERR_FORMAT for an unknown id.
 int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
-                int N, int K, hipStream_t stream) {
+                int N, int K, bool relu, hipStream_t stream) {
   Args a{};
   a.A = (const uint8_t*)A;
   a.SA = (const uint8_t*)SA;
@@ -716,6 +720,7 @@ int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void
   a.N = N;
   a.K = K;
   a.nblk = K / 32;
+  a.relu = relu ? 1 : 0;
   a.a_row_bytes = kind == KIND_E4M3 ? K : (kind == KIND_E2M1 ? K / 2 : 2 * (int64_t)K);
 #define MX_TILE(ID, BM, BN, WGM, WGN)                                             \
   case ID:                                                                        \
@@ -736,14 +741,14 @@ int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void
       if (kind == KIND_F16) return launch<KIND_F16, 256, 224, 4, 2>(a, stream);
       return kind == KIND_E4M3 ? launch_pp<KIND_E4M3, 256, 224>(a, stream) : launch_pp<KIND_E2M1, 256, 224>(a, stream);
     case 8:  // MX 4-stage ring (N % 4 == 0; K % 512 == 0 E4M3, K % 1024 == 0 E2M1); otherwise the 8-wave kernel
-      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(false, 256, A, SA, B, SB, C, M, N, K, stream);
-      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(true, 256, A, SA, B, SB, C, M, N, K, stream);
+      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(false, 256, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(true, 256, A, SA, B, SB, C, M, N, K, relu, stream);
       if (kind == KIND_E4M3) return launch<KIND_E4M3, 256, 256, 4, 2>(a, stream);
       if (kind == KIND_E2M1) return launch<KIND_E2M1, 256, 256, 4, 2>(a, stream);
       return launch<KIND_F16, 256, 256, 4, 2>(a, stream);
     case 9:  // the same ring with 256x224 tiles; otherwise the 8-wave 256x224 kernel
-      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(false, 224, A, SA, B, SB, C, M, N, K, stream);
-      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(true, 224, A, SA, B, SB, C, M, N, K, stream);
+      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(false, 224, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(true, 224, A, SA, B, SB, C, M, N, K, relu, stream);
       if (kind == KIND_E4M3) return launch<KIND_E4M3, 256, 224, 4, 2>(a, stream);
       if (kind == KIND_E2M1) return launch<KIND_E2M1, 256, 224, 4, 2>(a, stream);
       return launch<KIND_F16, 256, 224, 4, 2>(a, stream);

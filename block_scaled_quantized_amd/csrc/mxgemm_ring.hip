@@ -108,6 +108,7 @@ struct Args {
   const uint8_t* SB;
   _Float16* C;
   int M, N, K, tiles_m;
+  int relu;  // epilogue: C = max(C, 0) (IEEE maxNum: NaN gives 0)
 };
 
 // Per lane: byte u%4 of dword u/4 is the lane's scale for MFMA K-step u of the group (u = stage for
@@ -403,7 +404,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
 #pragma unroll
         for (int e = 0; e < 4; e++) {
           const float v = acc[i][j][4 * q + e];
-          o[e] = (_Float16)v;
+          o[e] = (_Float16)(p.relu ? fmaxf(v, 0.0f) : v);
         }
         *reinterpret_cast<v4h*>(stage + r32 * EROW + (32 * i + 8 * q + 4 * h) * 2) = o;
       }
@@ -436,7 +437,7 @@ namespace mx {
 // MX ring kernels. fp4 = false: E4M3, requires K % 512 == 0; fp4 = true: E2M1, requires
 // K % 1024 == 0; both require N % 4 == 0 (checked by the caller). bn = 256 or 224.
 int gemm_ring_launch(bool fp4, int bn, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
-                     int N, int K, hipStream_t stream) {
+                     int N, int K, bool relu, hipStream_t stream) {
   Args a{};
   a.A = (const uint8_t*)A;
   a.SA = (const uint8_t*)SA;
@@ -446,6 +447,7 @@ int gemm_ring_launch(bool fp4, int bn, const void* A, const void* SA, const void
   a.M = M;
   a.N = N;
   a.K = K;
+  a.relu = relu ? 1 : 0;
   a.tiles_m = (M + BM - 1) / BM;
   const int tiles = a.tiles_m * ((N + bn - 1) / bn);
   const dim3 grid((unsigned)tiles), block(256);

@@ -64,6 +64,12 @@ int mx_version(void);
 
 typedef struct mxgemm_plan* mxgemm_t;
 
+/* mxgemm_create flag: epilogue ReLU, C = max(A*B, 0) elementwise before the fp16 store, with
+ * IEEE maxNum semantics (a NaN product gives 0). This is the postfix activation of the "Running
+ * inline ML operations in a shader with Metal 4" sample, section "Combine an element-wise
+ * function" (there applied with max(value, 0) to the product tile in registers). */
+#define MXGEMM_RELU 1u
+
 /*
  * mxgemm_create -- validate a GEMM problem C[M,N] = A[M,K] * B[K,N] and choose its kernel.
  *
@@ -76,9 +82,9 @@ typedef struct mxgemm_plan* mxgemm_t;
  * Supported pairs: (MX_E4M3, MX_E4M3), (MX_E2M1, MX_E2M1), (MX_F16, MX_F16).
  * Shape rules: 1 <= M, N <= MX_MAX_DIM; 32 <= K <= MX_MAX_DIM; MX formats need K % 32 == 0;
  * MX_F16 needs K % 8 == 0 and N % 8 == 0.
- * `flags` must be 0 (reserved). Host only: queues no GPU work. *out receives a plan that holds
- * host metadata only; release it with mxgemm_destroy. A plan may be used from several threads
- * and streams at once.
+ * `flags` is 0 or MXGEMM_RELU (other bits: MX_ERR_FORMAT). Host only: queues no GPU work. *out
+ * receives a plan that holds host metadata only; release it with mxgemm_destroy. A plan may be
+ * used from several threads and streams at once.
  */
 int mxgemm_create(mxgemm_t* out, int M, int N, int K, int fa, int fb, unsigned flags);
 

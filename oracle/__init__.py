@@ -133,6 +133,15 @@ def mxgemm_points(fa, fb, A, SA, B, SB, K, ms, ns) -> np.ndarray:
     return out
 
 
+def relu(C) -> np.ndarray:
+    """Epilogue ReLU of the "Running inline ML operations in a shader with Metal 4" sample, section
+    "Combine an element-wise function": every negative element of the product becomes zero, the
+    sample writing it as max(value, 0). max is taken with IEEE maxNum semantics, so a NaN element
+    becomes 0 (the reading of max for a NaN argument). Applied to the fp64 product; rounding to
+    fp16 afterwards gives the same values, since nearest-even rounding keeps the sign and zero."""
+    return np.fmax(np.asarray(C, dtype=np.float64), 0.0)
+
+
 def gemm_f16(A16, B16, row0=0, nrows=None) -> np.ndarray:
     """fp64 C = A @ B for binary16 A [M][K], B [K][N] (numpy float16 arrays)."""
     A = np.ascontiguousarray(A16, dtype=np.float16).view(np.uint16)

@@ -173,6 +173,59 @@ def test_mx_nonfinite_and_extreme_scales(orc, fmt):
     assert ok, (ratio, bad)
 
 
+@pytest.mark.parametrize("fmt,tile,M,N,K", [
+    (0, 8, 300, 520, 1024), (4, 8, 300, 520, 1024), (0, 7, 300, 520, 512), (4, 4, 300, 520, 416),
+    (0, 3, 17, 40, 96), (0, 9, 257, 260, 512),
+])
+def test_mx_relu_epilogue(orc, fmt, tile, M, N, K):
+    """MXGEMM_RELU: C = max(A*B, 0) for every kernel family (ring, ping-pong, 8-wave, 4-wave)."""
+    api = require_gpu()
+    say(f"mx relu fmt={fmt} tile={tile} M={M} N={N} K={K}")
+    a_src = synth.normal((M, K), 1.0, 600 + tile)
+    b_src = synth.normal((N, K), 1.0, 601 + tile)
+    A, SA = gpu_mx_pack(api, fmt, a_src)
+    B, SB = gpu_mx_pack(api, fmt, b_src)
+    oA, oSA = orc.mx_quantize(fmt, a_src)
+    oB, oSB = orc.mx_quantize(fmt, b_src)
+    old = os.environ.get("MXGEMM_TILE")
+    os.environ["MXGEMM_TILE"] = str(tile)
+    try:
+        C = gpu_gemm(api, fmt, A, SA, B, SB, M, N, K, flags=api.MXGEMM_RELU)
+    finally:
+        if old is None:
+            del os.environ["MXGEMM_TILE"]
+        else:
+            os.environ["MXGEMM_TILE"] = old
+    ref = orc.relu(orc.mxgemm(fmt, fmt, oA, oSA, oB, oSB, M, N, K))
+    assert (C >= 0).all() and (C == 0).mean() > 0.3      # about half the outputs are clipped
+    ok, ratio, bad = orc.check(C, ref, K, R_of(orc, fmt, oA, oSA, oB, oSB, M, N, K))
+    assert ok, (ratio, bad)
+
+
+def test_relu_epilogue_nan_and_f16(orc):
+    """ReLU maps a NaN product (NaN scale) to 0, and applies to the fp16 GEMM too."""
+    api = require_gpu()
+    M, N, K = 64, 96, 256
+    say("relu nan / f16")
+    A = small_codes(0, (M, K), 5)
+    B = small_codes(0, (N, K), 6)
+    SA = synth.random_ints((M, K // 32), 118, 128, 7)
+    SB = synth.random_ints((N, K // 32), 118, 128, 8)
+    SA[3, 2] = 0xFF
+    C = gpu_gemm(api, 0, dev(A), dev(SA), dev(B), dev(SB), M, N, K, flags=api.MXGEMM_RELU)
+    ref = orc.mxgemm(0, 0, A, SA, B, SB, M, N, K)
+    assert np.isnan(ref[3]).all() and (C[3] == 0).all()
+    R = orc.rms_ab(np.nan_to_num(orc.dequant(0, A, SA, M, K)), orc.dequant(0, B, SB, N, K).T)
+    ok, ratio, bad = orc.check(C, orc.relu(ref), K, R)
+    assert ok, (ratio, bad)
+    A16 = synth.uniform_pm1((M, K), 70).astype(np.float16)
+    B16 = synth.uniform_pm1((K, N), 71).astype(np.float16)
+    C16 = gpu_gemm(api, api.MX_F16, dev(A16), None, dev(B16), None, M, N, K, flags=api.MXGEMM_RELU)
+    ok, ratio, bad = orc.check(C16, orc.relu(orc.gemm_f16(A16, B16)), K,
+                               orc.rms_ab(A16.astype(np.float64), B16.astype(np.float64)))
+    assert ok, (ratio, bad)
+
+
 def test_mx_unit_scales_fp8_exact_products(orc):
     """Scale 127 everywhere: the oracle equals a plain fp8 matmul; the GPU must match within the bound."""
     api = require_gpu()

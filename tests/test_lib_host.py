@@ -116,7 +116,9 @@ def test_validation_errors_without_gpu():
     assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 48, 0, 0, 0) == api.MX_ERR_SHAPE     # K % 32
     assert lib.mxgemm_create(ctypes.byref(h), 0, 16, 32, 0, 0, 0) == api.MX_ERR_SHAPE
     assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 4, 0) == api.MX_ERR_FORMAT     # mixed pair
-    assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 0, 1) == api.MX_ERR_FORMAT     # flags
+    assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 0, 2) == api.MX_ERR_FORMAT     # flags
+    assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 0, api.MXGEMM_RELU) == api.MX_OK
+    assert lib.mxgemm_destroy(h) == 0
     assert lib.mxgemm_create(ctypes.byref(h), 16, 12, 32, 16, 16, 0) == api.MX_ERR_SHAPE    # fp16 N % 8
     assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 0, 0) == api.MX_OK
     tm, tn, tk, tv = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_int()

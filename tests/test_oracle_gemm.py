@@ -270,3 +270,16 @@ def test_bound_has_teeth(orc):
     assert not ok
     ok, _, _ = orc.check(C.T.copy(), C, K, R)        # transposed output
     assert not ok
+
+
+def test_relu_special_values(orc):
+    """The epilogue ReLU: negatives (and -Inf) to zero, positives and +Inf kept, NaN to zero (IEEE
+    maxNum, the reading of the sample's max(value, 0) for a NaN), zero kept as a zero."""
+    x = np.array([-1.0, -0.0, 0.0, 2.5, np.nan, -np.inf, np.inf, -1e-300, 65504.0])
+    y = orc.relu(x)
+    assert y.tolist()[:4] == [0.0, 0.0, 0.0, 2.5]
+    assert y[4] == 0.0 and y[5] == 0.0 and y[6] == np.inf and y[7] == 0.0 and y[8] == 65504.0
+    C = orc.mxgemm(0, 0, np.full((2, 32), 0x38, np.uint8), np.array([[127], [127]], np.uint8),
+                   np.array([[0x38] * 32, [0xB8] * 32], np.uint8), np.array([[127], [127]], np.uint8), 2, 2, 32)
+    assert C.tolist() == [[32.0, -32.0], [32.0, -32.0]]          # 32 products of +-1
+    assert orc.relu(C).tolist() == [[32.0, 0.0], [32.0, 0.0]]
