@@ -8,6 +8,7 @@ from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import ctypes
 import subprocess
 import sys
 
@@ -43,6 +44,13 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # A kernel template that the host pass of hipcc fails to instantiate leaves an undefined device
+    # stub behind without any diagnostic; linking a shared library lets that through, so resolve
+    # every symbol now (no GPU is needed to load the library).
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW | os.RTLD_LOCAL)
+    except OSError as e:
+        raise RuntimeError(f"built library does not load: {e}") from e
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

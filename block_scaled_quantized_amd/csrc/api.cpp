@@ -75,8 +75,9 @@ bool ring_ok(int kind, int N, int K) {
 int choose_tile(int kind, int M, int N, int K) {
   if (const char* env = std::getenv("MXGEMM_TILE")) {
     int t = std::atoi(env);
-    if (t >= 0 && t < kNumTiles) return t;
+    if (t >= 0 && t < kNumTiles) return kind >= 3 ? (t == kRingTile224 ? t : kRingTile) : t;
   }
+  if (kind >= 3) return kRingTile;  // mixed pairs: the ring kernel only
   int best = 0;
   double best_cost = 1e300;
   for (int t = 0; t < kNumTiles; t++) {
@@ -120,10 +121,13 @@ int mxgemm_create(mxgemm_t* out, int M, int N, int K, int fa, int fb, unsigned f
   if (fa == MX_E4M3 && fb == MX_E4M3) kind = 0;
   else if (fa == MX_E2M1 && fb == MX_E2M1) kind = 1;
   else if (fa == MX_F16 && fb == MX_F16) kind = 2;
+  else if (fa == MX_E4M3 && fb == MX_E2M1) kind = 3;
+  else if (fa == MX_E2M1 && fb == MX_E4M3) kind = 4;
   else return MX_ERR_FORMAT;
   if (M < 1 || N < 1 || K < 32 || M > MX_MAX_DIM || N > MX_MAX_DIM || K > MX_MAX_DIM) return MX_ERR_SHAPE;
   if (kind != 2 && K % 32) return MX_ERR_SHAPE;
   if (kind == 2 && (K % 8 || N % 8)) return MX_ERR_SHAPE;
+  if (kind >= 3 && (K % 512 || N % 4)) return MX_ERR_SHAPE;  // mixed pairs run on the ring kernel only
   mxgemm_plan* p = new (std::nothrow) mxgemm_plan{M, N, K, fa, fb, kind, choose_tile(kind, M, N, K), flags};
   if (!p) return MX_ERR_NOMEM;
   *out = p;
@@ -140,10 +144,10 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
   const TileInfo& t = kTiles[p->tile_id];
   *tile_m = t.bm;
   *tile_n = t.bn;
-  *tile_k = p->kind == 0 ? 128 : (p->kind == 1 ? 256 : 64);
+  *tile_k = p->kind == 0 ? 128 : (p->kind == 1 ? 256 : 64);  // mixed pairs: 64 (the ring's stage)
   if (p->tile_id == kRingTile || p->tile_id == kRingTile224) {  // the ring, or the 8-wave kernel where it does not apply
-    const bool ring = ring_ok(p->kind, p->N, p->K);
-    *tile_k = ring ? (p->kind == 0 ? 64 : 128) : *tile_k;
+    const bool ring = p->kind >= 3 || ring_ok(p->kind, p->N, p->K);
+    *tile_k = ring ? (p->kind == 1 ? 128 : 64) : *tile_k;
     *variant = ring ? 3 : 1;
     return MX_OK;
   }

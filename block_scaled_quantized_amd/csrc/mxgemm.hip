@@ -704,12 +704,14 @@ int launch(const Args& a0, hipStream_t stream) {
 
 namespace mx {
 
-int gemm_ring_launch(bool fp4, int bn, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
+int gemm_ring_launch(int kind, int bn, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
                      int N, int K, bool relu, hipStream_t stream);
 
 // Tile configurations, indexed by the plan. Returns MX_ERR_FORMAT for an unknown id.
 int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
                 int N, int K, bool relu, hipStream_t stream) {
+  // mixed pairs (3: E4M3 A x E2M1 B, 4: E2M1 A x E4M3 B) run on the ring kernel only
+  if (kind >= 3) return gemm_ring_launch(kind - 1, tile_id == 9 ? 224 : 256, A, SA, B, SB, C, M, N, K, relu, stream);
   Args a{};
   a.A = (const uint8_t*)A;
   a.SA = (const uint8_t*)SA;
@@ -741,14 +743,14 @@ int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void
       if (kind == KIND_F16) return launch<KIND_F16, 256, 224, 4, 2>(a, stream);
       return kind == KIND_E4M3 ? launch_pp<KIND_E4M3, 256, 224>(a, stream) : launch_pp<KIND_E2M1, 256, 224>(a, stream);
     case 8:  // MX 4-stage ring (N % 4 == 0; K % 512 == 0 E4M3, K % 1024 == 0 E2M1); otherwise the 8-wave kernel
-      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(false, 256, A, SA, B, SB, C, M, N, K, relu, stream);
-      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(true, 256, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(0, 256, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(1, 256, A, SA, B, SB, C, M, N, K, relu, stream);
       if (kind == KIND_E4M3) return launch<KIND_E4M3, 256, 256, 4, 2>(a, stream);
       if (kind == KIND_E2M1) return launch<KIND_E2M1, 256, 256, 4, 2>(a, stream);
       return launch<KIND_F16, 256, 256, 4, 2>(a, stream);
     case 9:  // the same ring with 256x224 tiles; otherwise the 8-wave 256x224 kernel
-      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(false, 224, A, SA, B, SB, C, M, N, K, relu, stream);
-      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(true, 224, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(0, 224, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(1, 224, A, SA, B, SB, C, M, N, K, relu, stream);
       if (kind == KIND_E4M3) return launch<KIND_E4M3, 256, 224, 4, 2>(a, stream);
       if (kind == KIND_E2M1) return launch<KIND_E2M1, 256, 224, 4, 2>(a, stream);
       return launch<KIND_F16, 256, 224, 4, 2>(a, stream);

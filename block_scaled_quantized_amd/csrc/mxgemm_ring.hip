@@ -1,5 +1,5 @@
-// mxgemm_ring.hip -- MXFP8 / MXFP4 (E4M3 or E2M1 data, E8M0 scales per 32 along K) GEMM with a
-// 4-stage LDS ring.
+// mxgemm_ring.hip -- MX GEMM (E4M3 and/or E2M1 data, E8M0 scales per 32 along K) with a 4-stage
+// LDS ring: MXFP8, MXFP4 and the mixed pairs E4M3 x E2M1, E2M1 x E4M3.
 //
 //   C[m,n] = sum_k 2^(SA[m,k/32]-127) A[m,k] * 2^(SB[n,k/32]-127) B[n,k]   (fp32 accumulate, fp16 out)
 //
@@ -8,8 +8,8 @@
 //
 // Why a ring of short stages: a 256x224 tile with 128-byte K stages fills LDS with two stages, so
 // each stage's copy has to land within one stage of MFMAs (about 1800 cycles), less than the L2 /
-// MALL latency under load. Here a stage is 64 bytes of K: one scaled MFMA 32x32x64 deep for E4M3,
-// two for E2M1.
+// MALL latency under load. Here a stage is one scaled MFMA 32x32x64 deep (64 bytes of an E4M3 row,
+// 32 of an E2M1 row), two for E2M1 x E2M1 (64 bytes of each row).
 //  - Tile 256 x 256 with 4 waves (one per SIMD) of 128 x 128 = 4 x 4 MFMA tiles of 32 x 32, or
 //    256 x 224 with 4 waves of 64 x 224 = 2 x 7 MFMA tiles (224 = 7 x 32 does not split in two:
 //    the 256 x 224 tile exists so that N = 14336 gives 64 column tiles, a whole number of rounds
@@ -17,10 +17,12 @@
 //  - LDS ring of 4 stages (4 separate arrays, so the compiler can tell a fragment read of one
 //    stage from the direct copies filling another): up to 256 + 256 rows x 64 bytes per stage.
 //    Copies for stage t+3 are queued while stage t computes, three stages ahead.
-//  - 64-byte rows hold four 16-byte chunks, stored at chunk ^ ((row >> 2) & 3): a 16-lane quarter of
-//    a fragment read (16 rows, one chunk) then covers all 64 banks once.
-//  - Direct global->LDS copies (16 bytes per lane): instruction i of a stage fills rows
-//    16i..16i+15; lane l fills physical chunk l%4 of row 16i + l/4. Each wave issues 8 per stage;
+//  - 64-byte rows hold four 16-byte chunks, stored at chunk ^ ((row >> 2) & 3) (32-byte rows: two,
+//    at chunk ^ ((row >> 3) & 1)): a 16-lane quarter of a fragment read (16 rows, one chunk) then
+//    covers all 64 banks once.
+//  - Direct global->LDS copies (16 bytes per lane): instruction i of a stage fills 1 KB, rows
+//    16i..16i+15 of 64 bytes (lane l: physical chunk l%4 of row 16i + l/4) or 32 rows of 32
+//    bytes. Each wave issues 8 per stage (6 for a mixed pair);
 //    instructions past the tile's rows get an empty buffer resource and fill unused slot bytes
 //    with zeros, so every wave's copy count (and its vmcnt bookkeeping) is the same.
 //  - E8M0 scales for 8 stages (16 / 32 bytes per row) are copied once per group into the scale
@@ -51,10 +53,10 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int BM = 256;                 // tile rows (both shapes)
-constexpr int ROWB = 64;                // K bytes per stage
+constexpr int ROWB = 64;                // bytes per operand row per stage, at most
 constexpr int SLOT = 512 * ROWB;        // 32 KB: room for 256 + 256 rows
 constexpr int GROUP = 8;                // stages per scale group
-constexpr int DMA_PER_STAGE = SLOT / 1024 / 4;  // direct copies per wave per stage (8)
+constexpr int MAX_DPS = 8;              // direct copies per wave per stage, at most
 
 // Tile shapes. WAVES_M waves along M (the rest along N); each wave holds FA x FB MFMA tiles of
 // 32 x 32 (FA along M, FB along N).
@@ -67,17 +69,30 @@ struct RingTile {
   static_assert(WAVES_M == 2 || WAVES_M == 4, "tile");
 };
 
-// Per-format constants. A 64-byte stage is one MFMA K-step of E4M3 (64 elements, 2 scale blocks)
-// or two of E2M1 (128 elements, 4 blocks); a group of 8 stages then holds 16 or 32 scale bytes per
-// row, and each lane keeps 8 or 16 of them (its own K-block h of every K-step), 2 or 4 dwords.
+// Per-format constants. KIND 0: E4M3 x E4M3, 1: E2M1 x E2M1, 2: E4M3 A x E2M1 B, 3: E2M1 A x E4M3 B.
+// A stage is one MFMA K-step of 64 elements (2 scale blocks), or for E2M1 x E2M1 two K-steps of
+// 64 (128 elements, 4 blocks) so that its rows are 64 bytes too. An operand's stage row is 64 bytes,
+// or 32 for the E2M1 side of a mixed pair. A group of 8 stages holds 16 or 32 scale bytes per row,
+// and each lane keeps 8 or 16 of them (its own K-block h of every K-step), 2 or 4 dwords.
 template <int KIND>
 struct RingFmt {
-  static constexpr bool FP4 = KIND == 1;
-  static constexpr int KSTEPS = FP4 ? 2 : 1;        // MFMA K-steps per stage
-  static constexpr int SGRP = 512 * 16 * KSTEPS;    // scale array: 8 / 16 KB
-  static constexpr int SDW = 2 * KSTEPS;            // packed scale dwords per row per lane
-  static constexpr int DMA_PER_GROUP = SGRP / 1024 / 4;  // scale copies per wave per group (2 / 4)
-  static constexpr int ELEMS_PER_BYTE = FP4 ? 2 : 1;
+  // (enumerators rather than static data members: the host pass of hipcc sees these in device-only
+  // templates, where it mishandles static constexpr members)
+  enum : int {
+    A4 = KIND == 1 || KIND == 3, B4 = KIND == 1 || KIND == 2,  // E2M1 operands
+    FP4 = KIND == 1,                                   // both E2M1: two K-steps per stage, two scale planes
+    KSTEPS = FP4 ? 2 : 1,                              // MFMA K-steps per stage
+    ELEMS = 64 * KSTEPS,                               // K elements per stage
+    SRB_A = A4 && !FP4 ? 32 : 64, SRB_B = B4 && !FP4 ? 32 : 64,  // stage bytes per row
+    NI_A = BM * SRB_A / 1024,                          // 1 KB copy instructions per stage for A (16 / 8)
+    NI_B = 256 * SRB_B / 1024,                         // ... and for B (room for 256 rows)
+    DPS = (NI_A + NI_B) / 4,                           // copies per wave per stage (8 or 6)
+    CBSZ = B4 ? 4 : 0, BLGP = A4 ? 4 : 0,              // MFMA formats of the B and A operands
+    SGRP = 512 * 16 * KSTEPS,                          // scale array: 8 / 16 KB
+    SDW = 2 * KSTEPS,                                  // packed scale dwords per row per lane
+    DMA_PER_GROUP = SGRP / 1024 / 4                    // scale copies per wave per group (2 / 4)
+  };
+  static_assert(NI_A % 4 == 0 && NI_B % 4 == 0 && DPS <= MAX_DPS, "copies");
 };
 
 // The size goes through readfirstlane: clamps of uniform values can be selected as vector ops
@@ -118,7 +133,14 @@ struct Scales {
   uint32_t a[T::FA][RingFmt<KIND>::SDW], b[T::FB][RingFmt<KIND>::SDW];
 };
 
-MX_DEV int phys_off(int row, int chunk) { return row * ROWB + ((chunk ^ ((row >> 2) & 3)) << 4); }
+// Byte offset of 16-byte chunk `chunk` of row `row` within an operand's region of a slot. 64-byte
+// rows store chunk c at c ^ ((row >> 2) & 3) and 32-byte rows at c ^ ((row >> 3) & 1): the 16 rows
+// of a quarter-wave fragment read then cover all 64 banks once.
+template <int SRB>
+MX_DEV int phys_off(int row, int chunk) {
+  if constexpr (SRB == 64) return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+  else return row * 32 + ((chunk ^ ((row >> 3) & 1)) << 4);
+}
 
 MX_DEV v4i lds16(const char* base, int off) { return *reinterpret_cast<const v4i*>(base + off); }
 
@@ -141,12 +163,13 @@ struct RawScales {
   typename RawT<KIND>::type a[T::FA], b[T::FB];
 };
 
-// Rows of the wave's fragments: A fragment j is LDS row 32*FA*wm + 32j + l%32, B fragment i is
-// row BM + 32*FB*wn + 32i + l%32.
+// Rows of the wave's fragments within their operand: A fragment j is row 32*FA*wm + 32j + l%32,
+// B fragment i is row 32*FB*wn + 32i + l%32. The scale array numbers A rows 0..255 and B rows from
+// 256 (BM) on.
 template <class T>
 MX_DEV int row_a(int j, int wm, int r32) { return 32 * T::FA * wm + 32 * j + r32; }
 template <class T>
-MX_DEV int row_b(int i, int wn, int r32) { return BM + 32 * T::FB * wn + 32 * i + r32; }
+MX_DEV int row_b(int i, int wn, int r32) { return 32 * T::FB * wn + 32 * i + r32; }
 
 template <int KIND>
 MX_DEV typename RawT<KIND>::type raw_at(const char* sg, int row, int d) {
@@ -160,7 +183,7 @@ MX_DEV void read_raw_scales(const char* sg, RawScales<KIND, T>& r, int d, int wm
 #pragma unroll
   for (int j = 0; j < T::FA; j++) r.a[j] = raw_at<KIND>(sg, row_a<T>(j, wm, r32), d);
 #pragma unroll
-  for (int i = 0; i < T::FB; i++) r.b[i] = raw_at<KIND>(sg, row_b<T>(i, wn, r32), d);
+  for (int i = 0; i < T::FB; i++) r.b[i] = raw_at<KIND>(sg, BM + row_b<T>(i, wn, r32), d);
 }
 
 template <int KIND, class T>
@@ -178,18 +201,25 @@ MX_DEV void pack_scales(const RawScales<KIND, T>& r, Scales<KIND, T>& s, int d, 
   }
 }
 
-// A fragment of one stage: chunks h and 2+h of its row, i.e. the lane's K bytes of the E4M3 MFMA,
-// or its 16 bytes (K-block h) of E2M1 K-steps 0 and 1 in the low and high halves.
-MX_DEV v8i read_frag(const char* slot, int row, int h) {
-  return __builtin_shufflevector(lds16(slot, phys_off(row, h)), lds16(slot, phys_off(row, 2 + h)), 0, 1, 2, 3, 4, 5,
-                                 6, 7);
+// A fragment of one stage. 64-byte rows: chunks h and 2+h, i.e. the lane's K bytes of the E4M3
+// MFMA, or its 16 bytes (K-block h) of E2M1 K-steps 0 and 1 in the low and high halves. 32-byte rows
+// (the E2M1 side of a mixed pair): chunk h, the lane's 16 bytes, in the low half.
+template <int SRB>
+MX_DEV v8i read_frag(const char* region, int row, int h) {
+  if constexpr (SRB == 64)
+    return __builtin_shufflevector(lds16(region, phys_off<64>(row, h)), lds16(region, phys_off<64>(row, 2 + h)), 0, 1,
+                                   2, 3, 4, 5, 6, 7);
+  else {
+    const v4i x = lds16(region, phys_off<32>(row, h));
+    return __builtin_shufflevector(x, x, 0, 1, 2, 3, -1, -1, -1, -1);
+  }
 }
 
 // Per-workgroup constants of the main loop (rscale: the first DMA_PER_GROUP of the format are set).
 struct Ctx {
-  rsrc_t rdata[DMA_PER_STAGE];
+  rsrc_t rdata[MAX_DPS];
   rsrc_t rscale[4];
-  uint32_t voff, svoff;
+  uint32_t voff_a, voff_b, svoff;  // lane offsets of the A and B stage copies and of the scale copies
   int wave, wm, wn, r32, h, nst, ngroups;
 };
 
@@ -222,13 +252,13 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
   // Copies queued after this wave's copies of stage t+1 (issued at stage t-2): those of stage t+2
   // (at stage t-1) and, at S8 == 3, the scale group issued at S8 == 2 ahead of them. From S8 == 4
   // on, the next group's scales are visible.
-  wait_vm_n(S8 == 3 ? DMA_PER_STAGE + F::DMA_PER_GROUP : DMA_PER_STAGE);
+  wait_vm_n(S8 == 3 ? F::DPS + F::DMA_PER_GROUP : F::DPS);
   raw_barrier();
   // The scale array still holds half 1 of group g, read at the end of stage 7 of group g-1. Every
   // wave has waited for those reads before stage 1's MFMAs (they precede the fragment reads of
   // stage 0 in the wave's LDS queue), so past stage 2's barrier the array is free.
   if (S8 == 2) issue_scales<KIND>(c, sgrp, min(g + 1, c.ngroups - 1));
-  const uint32_t fill_off = ROWB * min(t + 3, c.nst - 1);
+  const uint32_t fill_stage = (uint32_t)min(t + 3, c.nst - 1);
 #pragma unroll
   for (int i = 0; i < T::FB; i++) {
 #pragma unroll
@@ -248,21 +278,29 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 bk, ak, acc[i][j], 4, 4, (U0 + 1) % 4, sc.b[i][(U0 + 1) / 4], (U0 + 1) % 4, sc.a[j][(U0 + 1) / 4]);
         } else {
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[i], ca[j], acc[i][j], 0, 0, U0 % 4,
+          // E4M3 x E4M3 or a mixed pair: one K-step; the E2M1 side's fragment is its low half
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[i], ca[j], acc[i][j], F::CBSZ, F::BLGP, U0 % 4,
                                                                        sc.b[i][U0 / 4], U0 % 4, sc.a[j][U0 / 4]);
         }
       }
     }
-    // this tile's share of the stage copies: copies [8i/FB, 8(i+1)/FB)
+    // this tile's share of the stage copies: copies [DPS*i/FB, DPS*(i+1)/FB) (copy q is an A copy
+    // when q < NI_A/4)
 #pragma unroll
-    for (int q = DMA_PER_STAGE * i / T::FB; q < DMA_PER_STAGE * (i + 1) / T::FB; q++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[q], (lds_ptr_t)(slot_fill + (c.wave + 4 * q) * 1024), 16,
-                                               c.voff, fill_off, 0, 0);
+    for (int q = F::DPS * i / T::FB; q < F::DPS * (i + 1) / T::FB; q++) {
+      // (offsets computed into locals first: the host pass of hipcc drops the kernel, silently, when
+      // these builtin arguments are written as conditional expressions of the format constants)
+      const bool qa = q < F::NI_A / 4;
+      const uint32_t vo = qa ? c.voff_a : c.voff_b;
+      const uint32_t so = (uint32_t)(qa ? (int)F::SRB_A : (int)F::SRB_B) * fill_stage;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[q], (lds_ptr_t)(slot_fill + (c.wave + 4 * q) * 1024), 16, vo,
+                                               so, 0, 0);
+    }
     // and of the next stage's fragments: list positions [F*i/FB, F*(i+1)/FB) of A0.., B0..
 #pragma unroll
     for (int f = T::F * i / T::FB; f < T::F * (i + 1) / T::FB; f++) {
-      if (f < T::FA) na[f] = read_frag(slot_nxt, row_a<T>(f, c.wm, c.r32), c.h);
-      else nb[f - T::FA] = read_frag(slot_nxt, row_b<T>(f - T::FA, c.wn, c.r32), c.h);
+      if (f < T::FA) na[f] = read_frag<F::SRB_A>(slot_nxt, row_a<T>(f, c.wm, c.r32), c.h);
+      else nb[f - T::FA] = read_frag<F::SRB_B>(slot_nxt + BM * F::SRB_A, row_b<T>(f - T::FA, c.wn, c.r32), c.h);
     }
     if (S8 == 4 && i == 1) read_raw_scales<KIND, T>(sgrp, raw, 0, c.wm, c.wn, c.r32);
     __builtin_amdgcn_sched_barrier(0);
@@ -294,14 +332,17 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
   const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
-  const uint32_t RB = (uint32_t)p.K / F::ELEMS_PER_BYTE, nblk = (uint32_t)p.K / 32;  // row bytes, K-blocks
-  const int nst = (int)RB / ROWB, ngroups = nst / GROUP;
+  const uint32_t RBA = (uint32_t)p.K / (F::A4 ? 2 : 1), RBB = (uint32_t)p.K / (F::B4 ? 2 : 1);  // row bytes
+  const uint32_t nblk = (uint32_t)p.K / 32;                                                   // K-blocks
+  const int nst = p.K / F::ELEMS, ngroups = nst / GROUP;
 
-  // Direct copies. Copy k (0..7) of this wave in a stage is stage instruction i = wave + 4k: rows
-  // 16i + l/4 of the stage (A rows for i < 16, B rows 16(i-16) + l/4 beyond), lane l filling
-  // physical chunk l%4, i.e. logical chunk (l%4) ^ ((l/16) & 3). Each copy gets its own buffer
-  // resource over its 16 rows (clamped to the matrix, empty past the tile), so one lane offset
-  // serves all eight and rows past the edge read as zero (their outputs are never stored).
+  // Direct copies. Copy k of this wave in a stage is stage instruction i = wave + 4k, which fills
+  // 1 KB of the slot at i * 1024: A rows for i < NI_A, then B rows. With 64-byte rows it covers 16
+  // rows, lane l filling physical chunk l%4 of row l/4 (logical chunk (l%4) ^ ((l/16) & 3)); with
+  // 32-byte rows 32 rows, lane l filling physical chunk l%2 of row l/2 (logical (l%2) ^ ((l/16) & 1)).
+  // Each copy gets its own buffer resource over its rows (clamped to the matrix, empty past the
+  // tile), so one lane offset per operand serves all of them and rows past the edge read as zero
+  // (their outputs are never stored).
   Ctx c;
   c.wave = wave;
   c.wm = wm;
@@ -310,16 +351,20 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   c.h = h;
   c.nst = nst;
   c.ngroups = ngroups;
-  const uint32_t lrow = (uint32_t)(lane >> 2), lchunk = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-  c.voff = lrow * RB + 16u * lchunk;
+  const uint32_t l = (uint32_t)lane;
+  const uint32_t off64 = 16u * ((l & 3) ^ ((l >> 4) & 3)), off32 = 16u * ((l & 1) ^ ((l >> 4) & 1));
+  c.voff_a = F::SRB_A == 64 ? (l >> 2) * RBA + off64 : (l >> 1) * RBA + off32;
+  c.voff_b = F::SRB_B == 64 ? (l >> 2) * RBB + off64 : (l >> 1) * RBB + off32;
 #pragma unroll
-  for (int k = 0; k < DMA_PER_STAGE; k++) {
+  for (int k = 0; k < F::DPS; k++) {
     const int i = wave + 4 * k;
-    const bool isA = k < 4;
-    const int r0 = isA ? 16 * i : 16 * i - BM, rows = isA ? rows_a : rows_b;
-    const int nr = max(0, min(16, rows - r0));
-    const uint8_t* base = (isA ? p.A + (int64_t)m0 * RB : p.B + (int64_t)n0 * RB) + (int64_t)(nr ? r0 : 0) * RB;
-    c.rdata[k] = make_rsrc(base, (uint32_t)nr * RB);
+    const bool isA = k < F::NI_A / 4;
+    const int rpi = (isA ? F::SRB_A : F::SRB_B) == 64 ? 16 : 32;  // rows per instruction
+    const int r0 = rpi * (isA ? i : i - F::NI_A), rows = isA ? rows_a : rows_b;
+    const uint32_t rb = isA ? RBA : RBB;
+    const int nr = max(0, min(rpi, rows - r0));
+    const uint8_t* base = (isA ? p.A + (int64_t)m0 * rb : p.B + (int64_t)n0 * rb) + (int64_t)(nr ? r0 : 0) * rb;
+    c.rdata[k] = make_rsrc(base, (uint32_t)nr * rb);
   }
   // Scale copy k of this wave: rows 64i + l with i = wave + 4(k%2) (A rows for even k).
   c.svoff = (uint32_t)lane * nblk;
@@ -346,9 +391,13 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   for (int t = 0; t < 3 && t < nst; t++) {
     char* slot = t == 0 ? slot0 : (t == 1 ? slot1 : slot2);
 #pragma unroll
-    for (int k = 0; k < DMA_PER_STAGE; k++)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(slot + (wave + 4 * k) * 1024), 16, c.voff,
-                                               ROWB * t, 0, 0);
+    for (int k = 0; k < F::DPS; k++) {
+      const bool qa = k < F::NI_A / 4;
+      const uint32_t vo = qa ? c.voff_a : c.voff_b;
+      const uint32_t so = (uint32_t)((qa ? (int)F::SRB_A : (int)F::SRB_B) * t);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(slot + (wave + 4 * k) * 1024), 16, vo, so, 0,
+                                               0);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): prologue copies of this wave
   raw_barrier();
@@ -360,9 +409,9 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   read_raw_scales<KIND, T>(sgrp, raw, 1, wm, wn, r32);
   pack_scales<KIND, T>(raw, sc, 1, h);
 #pragma unroll
-  for (int j = 0; j < T::FA; j++) xa[j] = read_frag(slot0, row_a<T>(j, wm, r32), h);
+  for (int j = 0; j < T::FA; j++) xa[j] = read_frag<F::SRB_A>(slot0, row_a<T>(j, wm, r32), h);
 #pragma unroll
-  for (int i = 0; i < T::FB; i++) xb[i] = read_frag(slot0, row_b<T>(i, wn, r32), h);
+  for (int i = 0; i < T::FB; i++) xb[i] = read_frag<F::SRB_B>(slot0 + BM * F::SRB_A, row_b<T>(i, wn, r32), h);
 
   // Stage t uses slot t%4 (t = 8g + s: slot s%4); even stages compute from x*, odd from y*.
   for (int g = 0; g < ngroups; g++) {
@@ -434,9 +483,10 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
 }  // namespace
 
 namespace mx {
-// MX ring kernels. fp4 = false: E4M3, requires K % 512 == 0; fp4 = true: E2M1, requires
-// K % 1024 == 0; both require N % 4 == 0 (checked by the caller). bn = 256 or 224.
-int gemm_ring_launch(bool fp4, int bn, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
+// MX ring kernels. kind 0: E4M3 x E4M3, 1: E2M1 x E2M1, 2: E4M3 A x E2M1 B, 3: E2M1 A x E4M3 B.
+// Requires N % 4 == 0 and K % 512 == 0 (K % 1024 == 0 for kind 1), checked by the caller.
+// bn = 256 or 224.
+int gemm_ring_launch(int kind, int bn, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
                      int N, int K, bool relu, hipStream_t stream) {
   Args a{};
   a.A = (const uint8_t*)A;
@@ -451,13 +501,23 @@ int gemm_ring_launch(bool fp4, int bn, const void* A, const void* SA, const void
   a.tiles_m = (M + BM - 1) / BM;
   const int tiles = a.tiles_m * ((N + bn - 1) / bn);
   const dim3 grid((unsigned)tiles), block(256);
+#define MX_RING(KD, WM) hipLaunchKernelGGL((gemm_ring_kernel<KD, WM>), grid, block, 0, stream, a)
   if (bn == 224) {
-    if (fp4) hipLaunchKernelGGL((gemm_ring_kernel<1, 4>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gemm_ring_kernel<0, 4>), grid, block, 0, stream, a);
+    switch (kind) {
+      case 0: MX_RING(0, 4); break;
+      case 1: MX_RING(1, 4); break;
+      case 2: MX_RING(2, 4); break;
+      default: MX_RING(3, 4); break;
+    }
   } else {
-    if (fp4) hipLaunchKernelGGL((gemm_ring_kernel<1, 2>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((gemm_ring_kernel<0, 2>), grid, block, 0, stream, a);
+    switch (kind) {
+      case 0: MX_RING(0, 2); break;
+      case 1: MX_RING(1, 2); break;
+      case 2: MX_RING(2, 2); break;
+      default: MX_RING(3, 2); break;
+    }
   }
+#undef MX_RING
   return launch_status();
 }
 }  // namespace mx

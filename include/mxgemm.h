@@ -79,7 +79,10 @@ typedef struct mxgemm_plan* mxgemm_t;
  * accumulated in fp32 and written once as fp16 (rounded to nearest even). C is overwritten
  * (C = A*B, not C += A*B). For fa == fb == MX_F16 there are no scales: C = A*B in fp32, fp16 out.
  *
- * Supported pairs: (MX_E4M3, MX_E4M3), (MX_E2M1, MX_E2M1), (MX_F16, MX_F16).
+ * Supported pairs: (MX_E4M3, MX_E4M3), (MX_E2M1, MX_E2M1), (MX_F16, MX_F16), and the mixed MX pairs
+ * (MX_E4M3, MX_E2M1), (MX_E2M1, MX_E4M3) (A and B each in its own format, scales as above; the
+ * scaled MFMA takes each operand's format separately). Mixed pairs need K % 512 == 0 and
+ * N % 4 == 0, else MX_ERR_SHAPE.
  * Shape rules: 1 <= M, N <= MX_MAX_DIM; 32 <= K <= MX_MAX_DIM; MX formats need K % 32 == 0;
  * MX_F16 needs K % 8 == 0 and N % 8 == 0.
  * `flags` is 0 or MXGEMM_RELU (other bits: MX_ERR_FORMAT). Host only: queues no GPU work. *out

@@ -50,8 +50,8 @@ def gpu_int_pack(api, fw, w: np.ndarray):
     return codes, scales
 
 
-def gpu_gemm(api, fa, A, SA, B, SB, M, N, K, flags=0) -> np.ndarray:
-    plan = api.mxgemm_create(M, N, K, fa, fa, flags)
+def gpu_gemm(api, fa, A, SA, B, SB, M, N, K, flags=0, fb=None) -> np.ndarray:
+    plan = api.mxgemm_create(M, N, K, fa, fa if fb is None else fb, flags)
     C = empty((M, N), torch.float16)
     api.mxgemm_run(plan, A, SA, B, SB, C)
     out = host(C).astype(np.float64)

@@ -226,6 +226,37 @@ def test_relu_epilogue_nan_and_f16(orc):
     assert ok, (ratio, bad)
 
 
+@pytest.mark.parametrize("fa,fb", [(0, 4), (4, 0)])
+@pytest.mark.parametrize("tile,M,N,K", [
+    (8, 300, 520, 1024), (8, 257, 260, 4096), (8, 1, 4, 512), (8, 33, 1028, 2560), (9, 300, 520, 512),
+    (9, 257, 260, 1536),
+])
+def test_mx_mixed_pairs(orc, fa, fb, tile, M, N, K):
+    """Mixed MX pairs (E4M3 A x E2M1 B and E2M1 A x E4M3 B) on the ring kernels, every output."""
+    api = require_gpu()
+    say(f"mx mixed fa={fa} fb={fb} tile={tile} M={M} N={N} K={K}")
+    a_src = synth.normal((M, K), 1.0, 700 + M + K)
+    b_src = synth.normal((N, K), 1.0, 701 + N + K)
+    A, SA = gpu_mx_pack(api, fa, a_src)
+    B, SB = gpu_mx_pack(api, fb, b_src)
+    oA, oSA = orc.mx_quantize(fa, a_src)
+    oB, oSB = orc.mx_quantize(fb, b_src)
+    assert np.array_equal(host(A), oA) and np.array_equal(host(B), oB)
+    old = os.environ.get("MXGEMM_TILE")
+    os.environ["MXGEMM_TILE"] = str(tile)
+    try:
+        C = gpu_gemm(api, fa, A, SA, B, SB, M, N, K, fb=fb)
+    finally:
+        if old is None:
+            del os.environ["MXGEMM_TILE"]
+        else:
+            os.environ["MXGEMM_TILE"] = old
+    ref = orc.mxgemm(fa, fb, oA, oSA, oB, oSB, M, N, K)
+    R = orc.rms_ab(orc.dequant(fa, oA, oSA, M, K), orc.dequant(fb, oB, oSB, N, K).T)
+    ok, ratio, bad = orc.check(C, ref, K, R)
+    assert ok, (ratio, bad)
+
+
 def test_mx_unit_scales_fp8_exact_products(orc):
     """Scale 127 everywhere: the oracle equals a plain fp8 matmul; the GPU must match within the bound."""
     api = require_gpu()

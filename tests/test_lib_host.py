@@ -115,7 +115,8 @@ def test_validation_errors_without_gpu():
     assert lib.mxgemm_create(None, 16, 16, 32, 0, 0, 0) == api.MX_ERR_NULL
     assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 48, 0, 0, 0) == api.MX_ERR_SHAPE     # K % 32
     assert lib.mxgemm_create(ctypes.byref(h), 0, 16, 32, 0, 0, 0) == api.MX_ERR_SHAPE
-    assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 4, 0) == api.MX_ERR_FORMAT     # mixed pair
+    assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 16, 0) == api.MX_ERR_FORMAT    # MX x fp16 pair
+    assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 4, 0) == api.MX_ERR_SHAPE     # mixed pair, K % 512
     assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 0, 2) == api.MX_ERR_FORMAT     # flags
     assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 0, api.MXGEMM_RELU) == api.MX_OK
     assert lib.mxgemm_destroy(h) == 0
@@ -172,6 +173,27 @@ def test_ring_tile_plan_info(monkeypatch):
     assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 128, 3)
     for M, N, K, f in [(300, 520, 416, api.MX_E4M3), (4096, 8192, 1536, api.MX_E2M1), (512, 512, 512, api.MX_F16)]:
         assert info(M, N, K, f)[3] != 3
+
+
+def test_mixed_pairs_plan(monkeypatch):
+    """Mixed MX pairs are accepted where the ring kernel applies (K % 512 == 0, N % 4 == 0) and
+    refused with MX_ERR_SHAPE elsewhere; they always plan the ring."""
+    monkeypatch.delenv("MXGEMM_TILE", raising=False)
+    for fa, fb in ((api.MX_E4M3, api.MX_E2M1), (api.MX_E2M1, api.MX_E4M3)):
+        p = api.mxgemm_create(2048, 14336, 4096, fa, fb)
+        assert api.mxgemm_plan_info(p) == (256, 256, 64, 3)
+        api.mxgemm_destroy(p)
+        for M, N, K in ((64, 64, 416), (64, 66, 512)):
+            with pytest.raises(RuntimeError):
+                api.mxgemm_create(M, N, K, fa, fb)
+    monkeypatch.setenv("MXGEMM_TILE", "9")
+    p = api.mxgemm_create(300, 520, 512, api.MX_E4M3, api.MX_E2M1)
+    assert api.mxgemm_plan_info(p) == (256, 224, 64, 3)
+    api.mxgemm_destroy(p)
+    monkeypatch.setenv("MXGEMM_TILE", "4")
+    p = api.mxgemm_create(300, 520, 512, api.MX_E2M1, api.MX_E4M3)
+    assert api.mxgemm_plan_info(p) == (256, 256, 64, 3)
+    api.mxgemm_destroy(p)
 
 
 def test_matvec_workspace_size():
