@@ -4,7 +4,8 @@ Prints ONE JSON line. The headline step is one MXFP8 GEMM of the prefill shape M
 K=4096, N=14336 (E4M3 data, E8M0 scales per 32 along K, fp32 accumulation, fp16 C): `value` is
 its throughput in TFLOP/s (2*M*N*K per step over the HIP-event time of the timed steps, inputs
 already resident in HBM). The other workloads of the path are measured in the same run and
-reported under "detail": the MXFP4 GEMM (M=4096, N=8192, K=8192), the fp16 GEMM (4096^3), the
+reported under "detail": the MXFP4 GEMM (M=4096, N=8192, K=8192), the mixed E4M3 x E2M1 GEMM at the
+prefill shape (against the E4M3 peak), the fp16 GEMM (4096^3), the
 small MXFP8 GEMM (128x256x128, a latency figure), the int8/int4 dequant matvec (M=1 and M=8,
 K=4096, N=14336; GB/s of algorithmic bytes) and the GPU pack/unpack codecs.
 
@@ -161,6 +162,22 @@ def main():
         detail["mxfp4_gemm_4096x8192x8192"] = {"ms": t, "tflops": tf, "frac_peak": tf / PEAK["mxfp4"],
                                                "tile": api.mxgemm_plan_info(p4)}
         del s4, C4
+
+    # ---------------- mixed MX pair: E4M3 activations x E2M1 weights at the prefill shape -----------
+    if want("mixed_prefill"):
+        log("timing mixed E4M3 x E2M1 GEMM")
+        sa, _, _ = mx_operands(api.MX_E4M3, M, 64, K, synth.MXFP8_PREFILL, 1.0, 1)   # A (E4M3) only
+        sb, _, _ = mx_operands(api.MX_E2M1, 64, N, K, synth.MXFP4_LARGE, 0.02, 1)    # B (E2M1) only
+        A8, SA8 = sa[0][0], sa[0][1]
+        B4, SB4 = sb[0][2], sb[0][3]
+        msets = [(A8, SA8, B4, SB4)] + [(A8.clone(), SA8.clone(), B4.clone(), SB4.clone()) for _ in range(2)]
+        pm = api.mxgemm_create(M, N, K, api.MX_E4M3, api.MX_E2M1)
+        Cm = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(3)]
+        t = timed(lambda i: api.mxgemm_run(pm, *msets[i % 3], Cm[i % 3], stream), args.steps, args.warmup)
+        tf = flops / (t * 1e-3) / 1e12
+        detail["mixed_e4m3_x_e2m1_gemm_2048x14336x4096"] = {"ms": t, "tflops": tf, "frac_peak": tf / PEAK["mxfp8"],
+                                                            "tile": api.mxgemm_plan_info(pm)}
+        del sa, sb, msets, Cm
 
     # ---------------- fp16 GEMM ----------------------------------------------------------------
     if want("f16_square"):
