@@ -379,21 +379,26 @@ template <class CF>
 constexpr int C_PITCH = 2 * CF::WN + 16;
 
 template <class CF>
-MX_DEV void store_c(const Args& p, const v4f (&acc)[CF::FN][CF::FM], char* ws, int mb, int nb, int lane) {
+MX_DEV void store_c(const Args& p, v4f (&acc)[CF::FN][CF::FM], char* ws, int mb, int nb, int lane) {
   static_assert(CF::NWAVES * 16 * C_PITCH<CF> <= CF::LDS_BYTES, "epilogue scratch");
   typedef _Float16 v8h __attribute__((ext_vector_type(8)));
   constexpr int LPR = CF::WN / 8;  // 16-byte pieces per row
   constexpr int PIECES = 16 * LPR;
   const int r16 = lane & 15, q = lane >> 4;
   const bool rows16 = (p.N & 7) == 0, rows8 = (p.N & 3) == 0;  // row starts 16- / 8-byte aligned
+  if (p.relu) {  // (one uniform branch, not a select per element)
+#pragma unroll
+    for (int i = 0; i < CF::FN; i++)
+#pragma unroll
+      for (int j = 0; j < CF::FM; j++)
+#pragma unroll
+        for (int v = 0; v < 4; v++) acc[i][j][v] = fmaxf(acc[i][j][v], 0.0f);
+  }
 #pragma unroll
   for (int j = 0; j < CF::FM; j++) {
 #pragma unroll
     for (int i = 0; i < CF::FN; i++) {
-      v4f a = acc[i][j];
-      if (p.relu)
-#pragma unroll
-        for (int v = 0; v < 4; v++) a[v] = fmaxf(a[v], 0.0f);
+      const v4f a = acc[i][j];
       *reinterpret_cast<v4h*>(ws + r16 * C_PITCH<CF> + (16 * i + 4 * q) * 2) =
           v4h{(_Float16)a[0], (_Float16)a[1], (_Float16)a[2], (_Float16)a[3]};
     }

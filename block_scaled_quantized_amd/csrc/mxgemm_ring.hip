@@ -433,36 +433,47 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   // Epilogue. The lane holds C[m0 + 32*FA*wm + 32j + r32][n0 + 32*FB*wn + 32i + 8q + 4h + e] in
   // acc[i][j][4q + e]: 8 bytes per row, so storing straight from registers would write each
   // 128-byte line of C in pieces from several instructions. Instead each wave converts to fp16 into
-  // its own slot, 32 rows (one A tile) at a time with rows padded by 8 bytes (the 8-byte writes of
-  // the 32 rows then fall on distinct banks), and writes the rows back as 16-byte pieces,
-  // consecutive lanes along a row.
+  // its own slot, 64 rows (two A tiles) at a time with rows padded by 8 bytes (the 8-byte writes of
+  // 32 rows then fall on distinct banks), and writes the rows back as 16-byte pieces, consecutive
+  // lanes along a row.
   char* stage = wave == 0 ? slot0 : (wave == 1 ? slot1 : (wave == 2 ? slot2 : slot3));
   constexpr int WCOLS = 32 * T::FB;            // columns of the wave's block
   constexpr int EROW = 2 * WCOLS + 8;          // staged row pitch, bytes
   constexpr int LPR = WCOLS / 8;               // 16-byte pieces per row
-  constexpr int PIECES = 32 * LPR;             // per A tile: a multiple of 64
-  static_assert(PIECES % 64 == 0 && 32 * EROW <= SLOT, "epilogue staging");
+  constexpr int JP = T::FA < 2 ? T::FA : 2;    // A tiles per pass
+  constexpr int PIECES = 32 * JP * LPR;        // per pass: a multiple of 64
+  static_assert(PIECES % 64 == 0 && 32 * JP * EROW <= SLOT && T::FA % JP == 0, "epilogue staging");
   const bool rows16 = (p.N & 7) == 0;          // row starts 16-byte aligned
-#pragma unroll
-  for (int j = 0; j < T::FA; j++) {
+  if (p.relu) {  // (one uniform branch, not a select per element)
 #pragma unroll
     for (int i = 0; i < T::FB; i++)
 #pragma unroll
-      for (int q = 0; q < 4; q++) {
-        v4h o;
+      for (int j = 0; j < T::FA; j++)
 #pragma unroll
-        for (int e = 0; e < 4; e++) {
-          const float v = acc[i][j][4 * q + e];
-          o[e] = (_Float16)(p.relu ? fmaxf(v, 0.0f) : v);
+        for (int e = 0; e < 16; e++) acc[i][j][e] = fmaxf(acc[i][j][e], 0.0f);
+  }
+#pragma unroll
+  for (int j0 = 0; j0 < T::FA; j0 += JP) {
+#pragma unroll
+    for (int jj = 0; jj < JP; jj++)
+#pragma unroll
+      for (int i = 0; i < T::FB; i++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          v4h o;
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const float v = acc[i][j0 + jj][4 * q + e];
+            o[e] = (_Float16)v;
+          }
+          *reinterpret_cast<v4h*>(stage + (32 * jj + r32) * EROW + (32 * i + 8 * q + 4 * h) * 2) = o;
         }
-        *reinterpret_cast<v4h*>(stage + r32 * EROW + (32 * i + 8 * q + 4 * h) * 2) = o;
-      }
 #pragma unroll
     for (int s0 = 0; s0 < PIECES; s0 += 64) {
       const int piece = s0 + lane, lr = piece / LPR, cp = piece % LPR;
       const char* src = stage + lr * EROW + 16 * cp;
       const v4h lo = *reinterpret_cast<const v4h*>(src), hi = *reinterpret_cast<const v4h*>(src + 8);
-      const int m = m0 + 32 * T::FA * wm + 32 * j + lr, n = n0 + WCOLS * wn + 8 * cp;
+      const int m = m0 + 32 * T::FA * wm + 32 * j0 + lr, n = n0 + WCOLS * wn + 8 * cp;
       if (m < p.M) {
         _Float16* dst = p.C + (int64_t)m * p.N + n;
         if (n + 8 <= p.N) {
