@@ -52,7 +52,7 @@ namespace {
 
 struct TileInfo {
   int bm, bn, waves, variant;  // variant: 0 = 4 waves, 1 = 8 waves, 2 = 8-wave ping-pong (MX only),
-                               // 3 = 4-stage LDS ring (MX formats)
+                               // 3 = 4-stage LDS ring (MX formats; fp16 on 256x256)
   int eff[3];                  // measured relative efficiency per kind (E4M3, E2M1, F16), percent
 };
 // Tile ids understood by gemm_launch. The efficiencies rank the tiles (MI355X measurements at the
@@ -62,13 +62,17 @@ struct TileInfo {
 constexpr TileInfo kTiles[] = {
     {256, 256, 4, 0, {85, 85, 90}}, {256, 224, 4, 0, {80, 75, 55}}, {128, 128, 4, 0, {50, 45, 50}},
     {64, 64, 4, 0, {25, 25, 25}},   {256, 256, 8, 1, {90, 100, 100}}, {256, 224, 8, 1, {88, 95, 60}},
-    {256, 256, 8, 2, {60, 60, 99}}, {256, 224, 8, 2, {100, 95, 60}}, {256, 256, 4, 3, {200, 200, 1}},
+    {256, 256, 8, 2, {60, 60, 99}}, {256, 224, 8, 2, {100, 95, 60}}, {256, 256, 4, 3, {200, 200, 200}},
     {256, 224, 4, 3, {170, 160, 1}}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kRingTile = 8, kRingTile224 = 9;
 constexpr int kCUs = 256;
 
-bool ring_ok(int kind, int N, int K) {
+// Whether ring tile `tile` (8: 256x256, 9: 256x224) runs the ring kernel for this problem; the
+// fp16 ring exists for 256x256 only.
+bool ring_ok(int kind, int N, int K, int tile) {
+  if (kind == 2)
+    return tile == 8 && N % 256 == 0 && K % 256 == 0 && 2 * (int64_t)K * N < ((int64_t)1 << 31);
   return N % 4 == 0 && ((kind == 0 && K % 512 == 0) || (kind == 1 && K % 1024 == 0));
 }
 
@@ -81,7 +85,7 @@ int choose_tile(int kind, int M, int N, int K) {
   int best = 0;
   double best_cost = 1e300;
   for (int t = 0; t < kNumTiles; t++) {
-    if ((t == kRingTile || t == kRingTile224) && !ring_ok(kind, N, K)) continue;
+    if ((t == kRingTile || t == kRingTile224) && !ring_ok(kind, N, K, t)) continue;
     const int64_t tiles = (int64_t)((M + kTiles[t].bm - 1) / kTiles[t].bm) * ((N + kTiles[t].bn - 1) / kTiles[t].bn);
     const int64_t waves = (tiles + kCUs - 1) / kCUs;
     const double cost = (double)waves * kTiles[t].bm * kTiles[t].bn * 100.0 / kTiles[t].eff[kind];
@@ -146,8 +150,8 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
   *tile_n = t.bn;
   *tile_k = p->kind == 0 ? 128 : (p->kind == 1 ? 256 : 64);  // mixed pairs: 64 (the ring's stage)
   if (p->tile_id == kRingTile || p->tile_id == kRingTile224) {  // the ring, or the 8-wave kernel where it does not apply
-    const bool ring = p->kind >= 3 || ring_ok(p->kind, p->N, p->K);
-    *tile_k = ring ? (p->kind == 1 ? 128 : 64) : *tile_k;
+    const bool ring = p->kind >= 3 || ring_ok(p->kind, p->N, p->K, p->tile_id);
+    *tile_k = ring ? (p->kind == 1 ? 128 : (p->kind == 2 ? 32 : 64)) : *tile_k;
     *variant = ring ? 3 : 1;
     return MX_OK;
   }

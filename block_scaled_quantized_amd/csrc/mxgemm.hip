@@ -747,9 +747,12 @@ int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void
     case 7:
       if (kind == KIND_F16) return launch<KIND_F16, 256, 224, 4, 2>(a, stream);
       return kind == KIND_E4M3 ? launch_pp<KIND_E4M3, 256, 224>(a, stream) : launch_pp<KIND_E2M1, 256, 224>(a, stream);
-    case 8:  // MX 4-stage ring (N % 4 == 0; K % 512 == 0 E4M3, K % 1024 == 0 E2M1); otherwise the 8-wave kernel
+    case 8:  // 4-stage ring (N % 4 == 0; K % 512 == 0 E4M3, K % 1024 == 0 E2M1; fp16: N % 256 == 0,
+             // K % 256 == 0, 2KN < 2^31); otherwise the 8-wave kernel
       if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(0, 256, A, SA, B, SB, C, M, N, K, relu, stream);
       if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(1, 256, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_F16 && K % 256 == 0 && N % 256 == 0 && 2 * (int64_t)K * N < ((int64_t)1 << 31))
+        return gemm_ring_launch(4, 256, A, SA, B, SB, C, M, N, K, relu, stream);
       if (kind == KIND_E4M3) return launch<KIND_E4M3, 256, 256, 4, 2>(a, stream);
       if (kind == KIND_E2M1) return launch<KIND_E2M1, 256, 256, 4, 2>(a, stream);
       return launch<KIND_F16, 256, 256, 4, 2>(a, stream);

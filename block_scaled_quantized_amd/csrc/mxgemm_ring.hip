@@ -69,28 +69,33 @@ struct RingTile {
   static_assert(WAVES_M == 2 || WAVES_M == 4, "tile");
 };
 
-// Per-format constants. KIND 0: E4M3 x E4M3, 1: E2M1 x E2M1, 2: E4M3 A x E2M1 B, 3: E2M1 A x E4M3 B.
+// Per-format constants. KIND 0: E4M3 x E4M3, 1: E2M1 x E2M1, 2: E4M3 A x E2M1 B, 3: E2M1 A x E4M3 B,
+// 4: fp16 x fp16 (no scales).
 // A stage is one MFMA K-step of 64 elements (2 scale blocks), or for E2M1 x E2M1 two K-steps of
 // 64 (128 elements, 4 blocks) so that its rows are 64 bytes too. An operand's stage row is 64 bytes,
 // or 32 for the E2M1 side of a mixed pair. A group of 8 stages holds 16 or 32 scale bytes per row,
 // and each lane keeps 8 or 16 of them (its own K-block h of every K-step), 2 or 4 dwords.
+// fp16: a stage is 32 K-elements, two K-steps of the 32x32x16 fp16 MFMA; A rows are 64 bytes as
+// above, and B (K x N, N-contiguous) is staged as 32 K-rows of 512 bytes (256 columns), read with
+// transposing LDS loads.
 template <int KIND>
 struct RingFmt {
   // (enumerators rather than static data members: the host pass of hipcc sees these in device-only
   // templates, where it mishandles static constexpr members)
   enum : int {
+    F16 = KIND == 4,                                   // fp16 x fp16: no scale plane
     A4 = KIND == 1 || KIND == 3, B4 = KIND == 1 || KIND == 2,  // E2M1 operands
     FP4 = KIND == 1,                                   // both E2M1: two K-steps per stage, two scale planes
-    KSTEPS = FP4 ? 2 : 1,                              // MFMA K-steps per stage
-    ELEMS = 64 * KSTEPS,                               // K elements per stage
-    SRB_A = A4 && !FP4 ? 32 : 64, SRB_B = B4 && !FP4 ? 32 : 64,  // stage bytes per row
+    KSTEPS = FP4 || F16 ? 2 : 1,                       // MFMA K-steps per stage
+    ELEMS = F16 ? 32 : 64 * KSTEPS,                    // K elements per stage
+    SRB_A = A4 && !FP4 ? 32 : 64, SRB_B = B4 && !FP4 ? 32 : 64,  // stage bytes per row (fp16 B: per 16 columns)
     NI_A = BM * SRB_A / 1024,                          // 1 KB copy instructions per stage for A (16 / 8)
-    NI_B = 256 * SRB_B / 1024,                         // ... and for B (room for 256 rows)
+    NI_B = 256 * SRB_B / 1024,                         // ... and for B (room for 256 rows / columns)
     DPS = (NI_A + NI_B) / 4,                           // copies per wave per stage (8 or 6)
     CBSZ = B4 ? 4 : 0, BLGP = A4 ? 4 : 0,              // MFMA formats of the B and A operands
-    SGRP = 512 * 16 * KSTEPS,                          // scale array: 8 / 16 KB
+    SGRP = F16 ? 16 : 512 * 16 * KSTEPS,               // scale array: 8 / 16 KB (fp16: unused)
     SDW = 2 * KSTEPS,                                  // packed scale dwords per row per lane
-    DMA_PER_GROUP = SGRP / 1024 / 4                    // scale copies per wave per group (2 / 4)
+    DMA_PER_GROUP = F16 ? 0 : SGRP / 1024 / 4          // scale copies per wave per group (2 / 4)
   };
   static_assert(NI_A % 4 == 0 && NI_B % 4 == 0 && DPS <= MAX_DPS, "copies");
 };
@@ -215,13 +220,47 @@ MX_DEV v8i read_frag(const char* region, int row, int h) {
   }
 }
 
+// fp16 B fragment of one stage from the staged K x 256 block (32 rows of 512 bytes; 16-byte chunk c
+// of row k stored at chunk c ^ 4(k & 3)). ds_read_b64_tr_b16 (measured on gfx950): within each
+// 16-lane group, output lane j element r is element j%4 of the 8 bytes that lane j/4 + 4r
+// addressed. With lane i of a group addressing row i/4 (plus the group's K offset), columns
+// 4(i%4)..+3 of the group's 16, lane j receives column j at 4 consecutive K. Lane l (h = l/32) thus
+// gets column l%32 of the B tile at K = 16s + 8h + 0..7 for K-step s: the same K as its A fragment
+// (chunk 2s + h of its A row). `off` is the lane's byte offset for K-step 0, first half; the other
+// three reads are 4 and 16 rows on. A half-wave reads 4 rows x 64 bytes, whose chunks the swizzle
+// puts on all 64 banks once.
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+MX_DEV v2i lds_tr8(const char* p) {
+  return __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_ptr)(
+                                     (__attribute__((address_space(3))) char*)p)));
+}
+MX_DEV v8i read_frag_bt(const char* region, uint32_t off) {
+  const v2i r0 = lds_tr8(region + off), r1 = lds_tr8(region + off + 4 * 512);
+  const v2i r2 = lds_tr8(region + off + 16 * 512), r3 = lds_tr8(region + off + 20 * 512);
+  const v4i lo = __builtin_shufflevector(r0, r1, 0, 1, 2, 3), hi = __builtin_shufflevector(r2, r3, 0, 1, 2, 3);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // Per-workgroup constants of the main loop (rscale: the first DMA_PER_GROUP of the format are set).
 struct Ctx {
   rsrc_t rdata[MAX_DPS];
   rsrc_t rscale[4];
   uint32_t voff_a, voff_b, svoff;  // lane offsets of the A and B stage copies and of the scale copies
+  uint32_t bstage;                 // fp16: bytes between the B rows of consecutive stages (32 rows)
+  uint32_t bt_off[4];              // fp16: the lane's B fragment offsets (read_frag_bt), per B tile
   int wave, wm, wn, r32, h, nst, ngroups;
 };
+
+// Wave-uniform offset of a stage copy: along the row for A and MX B, 32 rows down for fp16 B.
+template <int KIND>
+MX_DEV uint32_t stage_soff(const Ctx& c, bool qa, uint32_t stage) {
+  using F = RingFmt<KIND>;
+  uint32_t step_b;
+  if constexpr (F::F16) step_b = c.bstage;
+  else step_b = (uint32_t)F::SRB_B;
+  return (qa ? (uint32_t)F::SRB_A : step_b) * stage;
+}
 
 // Scale copy k of this wave: 64 rows (A rows 64(wave) + l for even k, B rows for odd k), 16 bytes
 // each: bytes 16(k/2).. of the row's group (E2M1: plane k/2).
@@ -257,7 +296,8 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
   // The scale array still holds half 1 of group g, read at the end of stage 7 of group g-1. Every
   // wave has waited for those reads before stage 1's MFMAs (they precede the fragment reads of
   // stage 0 in the wave's LDS queue), so past stage 2's barrier the array is free.
-  if (S8 == 2) issue_scales<KIND>(c, sgrp, min(g + 1, c.ngroups - 1));
+  if constexpr (!F::F16)
+    if (S8 == 2) issue_scales<KIND>(c, sgrp, min(g + 1, c.ngroups - 1));
   const uint32_t fill_stage = (uint32_t)min(t + 3, c.nst - 1);
 #pragma unroll
   for (int i = 0; i < T::FB; i++) {
@@ -266,7 +306,13 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
       constexpr int U0 = F::KSTEPS * S8;  // first K-step of the stage within the group
 #pragma unroll
       for (int j = 0; j < T::FA; j++) {
-        if constexpr (F::FP4) {
+        if constexpr (F::F16) {
+          const v8h bk = __builtin_bit_cast(v8h, k ? __builtin_shufflevector(cb[i], cb[i], 4, 5, 6, 7)
+                                                   : __builtin_shufflevector(cb[i], cb[i], 0, 1, 2, 3));
+          const v8h ak = __builtin_bit_cast(v8h, k ? __builtin_shufflevector(ca[j], ca[j], 4, 5, 6, 7)
+                                                   : __builtin_shufflevector(ca[j], ca[j], 0, 1, 2, 3));
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bk, ak, acc[i][j], 0, 0, 0);
+        } else if constexpr (F::FP4) {
           const v8i bk = k ? __builtin_shufflevector(cb[i], cb[i], 4, 5, 6, 7, -1, -1, -1, -1)
                            : __builtin_shufflevector(cb[i], cb[i], 0, 1, 2, 3, -1, -1, -1, -1);
           const v8i ak = k ? __builtin_shufflevector(ca[j], ca[j], 4, 5, 6, 7, -1, -1, -1, -1)
@@ -292,7 +338,7 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
       // these builtin arguments are written as conditional expressions of the format constants)
       const bool qa = q < F::NI_A / 4;
       const uint32_t vo = qa ? c.voff_a : c.voff_b;
-      const uint32_t so = (uint32_t)(qa ? (int)F::SRB_A : (int)F::SRB_B) * fill_stage;
+      const uint32_t so = stage_soff<KIND>(c, qa, fill_stage);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[q], (lds_ptr_t)(slot_fill + (c.wave + 4 * q) * 1024), 16, vo,
                                                so, 0, 0);
     }
@@ -300,14 +346,18 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
 #pragma unroll
     for (int f = T::F * i / T::FB; f < T::F * (i + 1) / T::FB; f++) {
       if (f < T::FA) na[f] = read_frag<F::SRB_A>(slot_nxt, row_a<T>(f, c.wm, c.r32), c.h);
+      else if constexpr (F::F16) nb[f - T::FA] = read_frag_bt(slot_nxt + BM * F::SRB_A, c.bt_off[f - T::FA]);
       else nb[f - T::FA] = read_frag<F::SRB_B>(slot_nxt + BM * F::SRB_A, row_b<T>(f - T::FA, c.wn, c.r32), c.h);
     }
-    if (S8 == 4 && i == 1) read_raw_scales<KIND, T>(sgrp, raw, 0, c.wm, c.wn, c.r32);
+    if constexpr (!F::F16)
+      if (S8 == 4 && i == 1) read_raw_scales<KIND, T>(sgrp, raw, 0, c.wm, c.wn, c.r32);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (S8 == 2) pack_scales<KIND, T>(raw, sc, 1, c.h);
-  if (S8 == 6) pack_scales<KIND, T>(raw, sc, 0, c.h);
-  if (S8 == GROUP - 1) read_raw_scales<KIND, T>(sgrp, raw, 1, c.wm, c.wn, c.r32);
+  if constexpr (!F::F16) {
+    if (S8 == 2) pack_scales<KIND, T>(raw, sc, 1, c.h);
+    if (S8 == 6) pack_scales<KIND, T>(raw, sc, 0, c.h);
+    if (S8 == GROUP - 1) read_raw_scales<KIND, T>(sgrp, raw, 1, c.wm, c.wn, c.r32);
+  }
 }
 
 template <int KIND, int WAVES_M>
@@ -332,7 +382,9 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
   const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
-  const uint32_t RBA = (uint32_t)p.K / (F::A4 ? 2 : 1), RBB = (uint32_t)p.K / (F::B4 ? 2 : 1);  // row bytes
+  // row bytes (fp16 B: a K-row of N columns)
+  const uint32_t RBA = F::F16 ? 2u * (uint32_t)p.K : (uint32_t)p.K / (F::A4 ? 2 : 1);
+  const uint32_t RBB = F::F16 ? 2u * (uint32_t)p.N : (uint32_t)p.K / (F::B4 ? 2 : 1);
   const uint32_t nblk = (uint32_t)p.K / 32;                                                   // K-blocks
   const int nst = p.K / F::ELEMS, ngroups = nst / GROUP;
 
@@ -343,6 +395,11 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   // Each copy gets its own buffer resource over its rows (clamped to the matrix, empty past the
   // tile), so one lane offset per operand serves all of them and rows past the edge read as zero
   // (their outputs are never stored).
+  // fp16 B: B copy b (instruction NI_A + b) fills K-rows 2b and 2b+1 of the stage, 512 bytes each
+  // (columns n0..n0+255; N % 256 == 0), lane l filling physical chunk l%32 of row 2b + l/32 from
+  // logical chunk (l%32) ^ 4(row & 3); row & 3 = 2(wave & 1) + l/32 for every copy of the wave. Its
+  // resource starts at row 2b of the tile's columns and runs to the end of B; the stage offset moves
+  // 32 rows down.
   Ctx c;
   c.wave = wave;
   c.wm = wm;
@@ -355,6 +412,16 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   const uint32_t off64 = 16u * ((l & 3) ^ ((l >> 4) & 3)), off32 = 16u * ((l & 1) ^ ((l >> 4) & 1));
   c.voff_a = F::SRB_A == 64 ? (l >> 2) * RBA + off64 : (l >> 1) * RBA + off32;
   c.voff_b = F::SRB_B == 64 ? (l >> 2) * RBB + off64 : (l >> 1) * RBB + off32;
+  c.bstage = 32u * RBB;
+  if constexpr (F::F16) {
+    c.voff_b = (l >> 5) * RBB + 16u * ((l & 31) ^ (8u * ((uint32_t)wave & 1) + 4u * (l >> 5)));
+    const uint32_t g16 = l >> 4, i16 = l & 15, y = i16 >> 2;
+#pragma unroll
+    for (int i = 0; i < T::FB; i++) {
+      const uint32_t cc = 4u * (uint32_t)(T::FB * wn + i) + 2u * (g16 & 1) + ((i16 & 3) >> 1);
+      c.bt_off[i] = (8u * (g16 >> 1) + y) * 512u + 16u * (cc ^ (4u * y)) + 8u * (i16 & 1);
+    }
+  }
 #pragma unroll
   for (int k = 0; k < F::DPS; k++) {
     const int i = wave + 4 * k;
@@ -365,6 +432,12 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
     const int nr = max(0, min(rpi, rows - r0));
     const uint8_t* base = (isA ? p.A + (int64_t)m0 * rb : p.B + (int64_t)n0 * rb) + (int64_t)(nr ? r0 : 0) * rb;
     c.rdata[k] = make_rsrc(base, (uint32_t)nr * rb);
+    if constexpr (F::F16) {
+      if (!isA) {
+        const int64_t start = (int64_t)2 * (i - F::NI_A) * RBB + 2 * (int64_t)n0;
+        c.rdata[k] = make_rsrc(p.B + start, (uint32_t)((int64_t)p.K * RBB - start));
+      }
+    }
   }
   // Scale copy k of this wave: rows 64i + l with i = wave + 4(k%2) (A rows for even k).
   c.svoff = (uint32_t)lane * nblk;
@@ -387,14 +460,14 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
   // prologue: scale group 0 and stages 0, 1, 2
-  issue_scales<KIND>(c, sgrp, 0);
+  if constexpr (!F::F16) issue_scales<KIND>(c, sgrp, 0);
   for (int t = 0; t < 3 && t < nst; t++) {
     char* slot = t == 0 ? slot0 : (t == 1 ? slot1 : slot2);
 #pragma unroll
     for (int k = 0; k < F::DPS; k++) {
       const bool qa = k < F::NI_A / 4;
       const uint32_t vo = qa ? c.voff_a : c.voff_b;
-      const uint32_t so = (uint32_t)((qa ? (int)F::SRB_A : (int)F::SRB_B) * t);
+      const uint32_t so = stage_soff<KIND>(c, qa, (uint32_t)t);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(slot + (wave + 4 * k) * 1024), 16, vo, so, 0,
                                                0);
     }
@@ -404,14 +477,19 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   v8i xa[T::FA], xb[T::FB], ya[T::FA], yb[T::FB];
   Scales<KIND, T> sc;
   RawScales<KIND, T> raw;
-  read_raw_scales<KIND, T>(sgrp, raw, 0, wm, wn, r32);
-  pack_scales<KIND, T>(raw, sc, 0, h);
-  read_raw_scales<KIND, T>(sgrp, raw, 1, wm, wn, r32);
-  pack_scales<KIND, T>(raw, sc, 1, h);
+  if constexpr (!F::F16) {
+    read_raw_scales<KIND, T>(sgrp, raw, 0, wm, wn, r32);
+    pack_scales<KIND, T>(raw, sc, 0, h);
+    read_raw_scales<KIND, T>(sgrp, raw, 1, wm, wn, r32);
+    pack_scales<KIND, T>(raw, sc, 1, h);
+  }
 #pragma unroll
   for (int j = 0; j < T::FA; j++) xa[j] = read_frag<F::SRB_A>(slot0, row_a<T>(j, wm, r32), h);
 #pragma unroll
-  for (int i = 0; i < T::FB; i++) xb[i] = read_frag<F::SRB_B>(slot0 + BM * F::SRB_A, row_b<T>(i, wn, r32), h);
+  for (int i = 0; i < T::FB; i++) {
+    if constexpr (F::F16) xb[i] = read_frag_bt(slot0 + BM * F::SRB_A, c.bt_off[i]);
+    else xb[i] = read_frag<F::SRB_B>(slot0 + BM * F::SRB_A, row_b<T>(i, wn, r32), h);
+  }
 
   // Stage t uses slot t%4 (t = 8g + s: slot s%4); even stages compute from x*, odd from y*.
   for (int g = 0; g < ngroups; g++) {
@@ -494,8 +572,9 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
 }  // namespace
 
 namespace mx {
-// MX ring kernels. kind 0: E4M3 x E4M3, 1: E2M1 x E2M1, 2: E4M3 A x E2M1 B, 3: E2M1 A x E4M3 B.
-// Requires N % 4 == 0 and K % 512 == 0 (K % 1024 == 0 for kind 1), checked by the caller.
+// Ring kernels. kind 0: E4M3 x E4M3, 1: E2M1 x E2M1, 2: E4M3 A x E2M1 B, 3: E2M1 A x E4M3 B,
+// 4: fp16 x fp16 (B K x N). Requires N % 4 == 0 and K % 512 == 0 (K % 1024 == 0 for kind 1); for
+// kind 4 N % 256 == 0, K % 256 == 0 and 2*K*N < 2^31, bn = 256 only. Checked by the caller.
 // bn = 256 or 224.
 int gemm_ring_launch(int kind, int bn, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
                      int N, int K, bool relu, hipStream_t stream) {
@@ -518,14 +597,16 @@ int gemm_ring_launch(int kind, int bn, const void* A, const void* SA, const void
       case 0: MX_RING(0, 4); break;
       case 1: MX_RING(1, 4); break;
       case 2: MX_RING(2, 4); break;
-      default: MX_RING(3, 4); break;
+      case 3: MX_RING(3, 4); break;
+      default: return MX_ERR_FORMAT;
     }
   } else {
     switch (kind) {
       case 0: MX_RING(0, 2); break;
       case 1: MX_RING(1, 2); break;
       case 2: MX_RING(2, 2); break;
-      default: MX_RING(3, 2); break;
+      case 3: MX_RING(3, 2); break;
+      default: MX_RING(4, 2); break;
     }
   }
 #undef MX_RING

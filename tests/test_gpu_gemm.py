@@ -325,6 +325,41 @@ def test_f16_every_tile_ragged(orc, tile):
     assert ok, (ratio, bad)
 
 
+@pytest.mark.parametrize("M,N,K", [(256, 256, 256), (300, 512, 512), (520, 768, 1280), (40, 256, 768)])
+def test_f16_ring(orc, M, N, K):
+    """The fp16 ring (tile 8 where N % 256 == 0 and K % 256 == 0): B staged as K-rows and read
+    through transposing LDS loads; one group of 8 stages up to several, partial tiles in M."""
+    api = require_gpu()
+    say(f"f16 ring M={M} N={N} K={K}")
+    A, B, C = fp16_case(orc, api, M, N, K, 700 + M + N + K, tile=8)
+    ref = orc.gemm_f16(A, B)
+    ok, ratio, bad = orc.check(C, ref, K, orc.rms_ab(A.astype(np.float64), B.astype(np.float64)))
+    assert ok, (ratio, bad)
+
+
+def test_f16_ring_exact_integers(orc):
+    """Small integer operands make every product and partial sum exact in fp32, so the fp16 ring's
+    output must equal the oracle's sum rounded to fp16 exactly: any A/B element paired with the
+    wrong K shows up."""
+    api = require_gpu()
+    M, N, K = 512, 768, 768
+    say("f16 ring exact integers")
+    A = (synth.random_ints((M, K), 0, 6, 720).astype(np.int64) - 3).astype(np.float16)
+    B = (synth.random_ints((K, N), 0, 6, 721).astype(np.int64) - 3).astype(np.float16)
+    old = os.environ.get("MXGEMM_TILE")
+    os.environ["MXGEMM_TILE"] = "8"
+    try:
+        C = gpu_gemm(api, api.MX_F16, dev(A), None, dev(B), None, M, N, K)
+    finally:
+        if old is None:
+            del os.environ["MXGEMM_TILE"]
+        else:
+            os.environ["MXGEMM_TILE"] = old
+    ref = orc.gemm_f16(A, B)
+    assert np.abs(ref).max() < 2048                 # integers, exact in fp16
+    assert np.array_equal(C.astype(np.float64), ref)
+
+
 def test_f16_square_full_size_sampled(orc):
     """fp16 GEMM M=N=K=4096, U(-1,1) inputs."""
     api = require_gpu()

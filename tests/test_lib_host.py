@@ -148,9 +148,10 @@ def test_validation_errors_without_gpu():
 
 
 def test_ring_tile_plan_info(monkeypatch):
-    """Tile 8 is the MX 4-stage ring (64-byte K stages: 64 E4M3 or 128 E2M1 elements) where
-    N % 4 == 0 and K % 512 == 0 (E4M3) or K % 1024 == 0 (E2M1), and the 8-wave 256x256 kernel
-    elsewhere; without the override the ring is never picked where it does not apply."""
+    """Tile 8 is the 4-stage ring (64-byte K stages: 64 E4M3 or 128 E2M1 elements, 32 fp16) where
+    N % 4 == 0 and K % 512 == 0 (E4M3) or K % 1024 == 0 (E2M1), or for fp16 N % 256 == 0,
+    K % 256 == 0 and 2KN < 2^31, and the 8-wave 256x256 kernel elsewhere (the fp16 ring has no
+    256x224 form); without the override the ring is never picked where it does not apply."""
     def info(M, N, K, f):
         p = api.mxgemm_create(M, N, K, f, f)
         try:
@@ -163,15 +164,21 @@ def test_ring_tile_plan_info(monkeypatch):
     assert info(300, 522, 512, api.MX_E4M3) == (256, 256, 128, 1)
     assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 128, 3)
     assert info(4096, 8192, 1536, api.MX_E2M1) == (256, 256, 256, 1)
-    assert info(512, 512, 512, api.MX_F16) == (256, 256, 64, 1)
+    assert info(512, 512, 512, api.MX_F16) == (256, 256, 32, 3)
+    assert info(300, 768, 1280, api.MX_F16) == (256, 256, 32, 3)
+    assert info(512, 520, 512, api.MX_F16) == (256, 256, 64, 1)       # N % 256
+    assert info(512, 512, 384, api.MX_F16) == (256, 256, 64, 1)       # K % 256
+    assert info(256, 32768, 32768, api.MX_F16) == (256, 256, 64, 1)   # 2KN = 2^31
     monkeypatch.setenv("MXGEMM_TILE", "9")
+    assert info(512, 512, 512, api.MX_F16) == (256, 224, 64, 1)
     assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 224, 64, 3)
     assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 224, 128, 3)
     assert info(300, 520, 416, api.MX_E4M3) == (256, 224, 128, 1)
     monkeypatch.delenv("MXGEMM_TILE")
     assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 256, 64, 3)
     assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 128, 3)
-    for M, N, K, f in [(300, 520, 416, api.MX_E4M3), (4096, 8192, 1536, api.MX_E2M1), (512, 512, 512, api.MX_F16)]:
+    assert info(4096, 4096, 4096, api.MX_F16) == (256, 256, 32, 3)
+    for M, N, K, f in [(300, 520, 416, api.MX_E4M3), (4096, 8192, 1536, api.MX_E2M1), (512, 520, 512, api.MX_F16)]:
         assert info(M, N, K, f)[3] != 3
 
 
