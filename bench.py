@@ -7,7 +7,8 @@ already resident in HBM). The other workloads of the path are measured in the sa
 reported under "detail": the MXFP4 GEMM (M=4096, N=8192, K=8192), the mixed E4M3 x E2M1 GEMM at the
 prefill shape (against the E4M3 peak), the fp16 GEMM (4096^3), the
 small MXFP8 GEMM (128x256x128, a latency figure), the int8/int4 dequant matvec (M=1 and M=8,
-K=4096, N=14336; GB/s of algorithmic bytes) and the GPU pack/unpack codecs.
+K=4096, N=14336; GB/s of algorithmic bytes), the same int8/int4-weight product at M=128 (N=12288)
+and M=64 (N=4096) with K=4096 (TFLOP/s against the fp16 peak) and the GPU pack/unpack codecs.
 
 Timing: per workload, --settle seconds (default 0.5) of untimed calls so that the shader clock
 reaches its sustained-load level, W warm-up steps, then K steps between two HIP events recorded
@@ -235,6 +236,30 @@ def main():
                                                             "workspace_bytes": need if wsp is not None else 0}
             del wsets
         del wd
+
+    # ---------------- int8 / int4-weight GEMM with fp16 block scales at small M ----------------------
+    if want("wq_gemm"):
+        log("timing small-M weight-quantised GEMM")
+        for Mq, Nq, Kq in ((128, 12288, 4096), (64, 4096, 4096)):
+            wq = d(synth.normal((Kq, Nq), 0.02, synth.seed_for(synth.WQ_PREFILL, 1)))
+            xq = d(synth.normal((Mq, Kq), 1.0, synth.seed_for(synth.WQ_PREFILL, 0)).astype(np.float16))
+            yq = torch.empty((Mq, Nq), dtype=torch.float16, device=dev)
+            for fw, name in ((api.MX_INT4, "int4"), (api.MX_INT8, "int8")):
+                cs, ss = api.int_shapes(fw, Kq, Nq)
+                W = torch.empty(cs, dtype=torch.uint8, device=dev)
+                Ws = torch.empty(ss, dtype=torch.float16, device=dev)
+                api.mx_pack_run(fw, wq, Kq, Nq, W, Ws)
+                # enough weight copies (>= 384 MB) that repeats are not served by the Infinity Cache
+                nq = max(3, -(-(384 << 20) // (W.numel() + 2 * Ws.numel())))
+                qsets = [(W, Ws)] + [(W.clone(), Ws.clone()) for _ in range(nq - 1)]
+                t = timed(lambda i: api.mxmatvec_run(Mq, Nq, Kq, xq, qsets[i % nq][0], fw, qsets[i % nq][1], yq,
+                                                     None, None, stream), args.steps, args.warmup)
+                tf = 2.0 * Mq * Nq * Kq / (t * 1e-3) / 1e12
+                nbytes = W.numel() + Ws.numel() * 2 + Mq * Kq * 2 + Mq * Nq * 2
+                detail[f"wq_gemm_{name}_{Mq}x{Nq}x{Kq}"] = {"us": t * 1e3, "tflops": tf, "frac_peak_fp16": tf / PEAK["fp16"],
+                                                            "gbs": nbytes / (t * 1e-3) / 1e9, "weight_copies": nq}
+                del qsets
+            del wq, xq, yq
 
     # ---------------- codecs -------------------------------------------------------------------------
     if want("codec"):

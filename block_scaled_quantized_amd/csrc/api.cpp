@@ -173,7 +173,7 @@ int mxgemm_run(mxgemm_t p, const void* A, const void* SA, const void* B, const v
 
 static int matvec_shape(int M, int N, int K, int fw) {
   if (fw != MX_INT8 && fw != MX_INT4) return MX_ERR_FORMAT;
-  if (M < 1 || M > 8 || N < 1 || N > MX_MAX_DIM || K < 32 || K > MX_MAX_DIM || K % 32) return MX_ERR_SHAPE;
+  if (M < 1 || M > 256 || N < 1 || N > MX_MAX_DIM || K < 32 || K > MX_MAX_DIM || K % 32) return MX_ERR_SHAPE;
   if (fw == MX_INT8 ? (N % 16) : (N % 32)) return MX_ERR_SHAPE;
   return MX_OK;
 }

@@ -1,4 +1,5 @@
-// matvec.hip -- int8 / int4 dequant matvec for decode (M <= 8 activation rows).
+// matvec.hip -- int8 / int4 dequant matvec for decode (M <= 8 activation rows), and the same
+// product at 9 <= M <= 256 rows (gemm_wq_kernel below).
 //
 //   y[m,n] = sum_b Ws[b,n] * sum_{k in block b} x[m,k] * q[k,n]     (32-row blocks b)
 //
@@ -35,13 +36,13 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 MX_DEV v2h as_v2h(uint32_t u) { return __builtin_bit_cast(v2h, u); }
 
-// One block's loads for one lane: 8 weight rows (C columns each), the lane's x fragment and the
-// C block scales.
-template <bool I8, int C>
+// One block's loads for one lane: 8 weight rows (C columns each), the lane's x fragment of each of
+// MT 16-row activation tiles and the C block scales.
+template <bool I8, int C, int MT = 1>
 struct Stage {
   static constexpr int kWordsPerRow = I8 ? C / 4 : C / 8 > 0 ? C / 8 : 1;
   uint32_t w[8][kWordsPerRow];
-  uint4 xa;
+  uint4 xa[MT];
   uint32_t sc[C / 2];
 };
 
@@ -57,48 +58,52 @@ struct LaneOffsets {
   uint32_t w;   // weight row 8q of a block, the lane's first column
   uint32_t x;   // activation row, element 8q of a block
   uint32_t s;   // block scale of the lane's first column
+  uint32_t xt;  // bytes between the activation tiles (16 rows)
 };
 
 // Loads of block `blk`: W rows 32*blk + 8q + r (r < 8) of the lane's C columns, its C block scales
 // and (XG) its x fragment. The weight and scale resources are rebased per block, so offsets stay small
 // for any matrix size.
-template <bool I8, int C, bool XG>
-MX_DEV void load_stage(Stage<I8, C>& s, const uint8_t* __restrict__ Wt, rsrc_t xr, const _Float16* __restrict__ Ws,
+template <bool I8, int C, bool XG, int MT = 1, int WPOL = 0>
+MX_DEV void load_stage(Stage<I8, C, MT>& s, const uint8_t* __restrict__ Wt, rsrc_t xr, const _Float16* __restrict__ Ws,
                        uint32_t N, int blk, const LaneOffsets& lo) {
   const uint32_t row_bytes = I8 ? N : N / 2;
   const rsrc_t wr = make_rsrc(Wt + (int64_t)blk * 32 * row_bytes, 32u * row_bytes);
-  constexpr int WPR = Stage<I8, C>::kWordsPerRow;
+  constexpr int WPR = Stage<I8, C, MT>::kWordsPerRow;
 #pragma unroll
   for (int r = 0; r < 8; r++) {
     const int so = (int)(r * row_bytes);
     if constexpr (!I8 && C == 4) {
-      s.w[r][0] = __builtin_amdgcn_raw_buffer_load_b16(wr, (int)lo.w, so, 0);
+      s.w[r][0] = __builtin_amdgcn_raw_buffer_load_b16(wr, (int)lo.w, so, WPOL);
     } else if constexpr (WPR == 1) {
-      s.w[r][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, (int)lo.w, so, 0);
+      s.w[r][0] = __builtin_amdgcn_raw_buffer_load_b32(wr, (int)lo.w, so, WPOL);
     } else if constexpr (WPR == 2) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(wr, (int)lo.w, so, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(wr, (int)lo.w, so, WPOL);
       s.w[r][0] = v[0];
       s.w[r][1] = v[1];
     } else {
       static_assert(WPR == 4, "4, 8, 16 int8 or 4, 8, 16, 32 int4 columns per lane");
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)lo.w, so, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)lo.w, so, WPOL);
 #pragma unroll
       for (int e = 0; e < 4; e++) s.w[r][e] = v[e];
     }
   }
   if constexpr (XG) {
-    const auto xv = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)lo.x, blk * 64, 0);
-    s.xa = make_uint4(xv[0], xv[1], xv[2], xv[3]);
+#pragma unroll
+    for (int t = 0; t < MT; t++) {
+      const auto xv = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(lo.x + t * lo.xt), blk * 64, 0);
+      s.xa[t] = make_uint4(xv[0], xv[1], xv[2], xv[3]);
+    }
   }
   const rsrc_t sr = make_rsrc(Ws + (int64_t)blk * N, 2u * N);
   if constexpr (C == 4) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(sr, (int)lo.s, 0, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(sr, (int)lo.s, 0, WPOL);
     s.sc[0] = v[0];
     s.sc[1] = v[1];
   } else {
 #pragma unroll
     for (int h = 0; h < C / 8; h++) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(sr, (int)lo.s + 16 * h, 0, 0);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(sr, (int)lo.s + 16 * h, 0, WPOL);
 #pragma unroll
       for (int e = 0; e < 4; e++) s.sc[4 * h + e] = v[e];
     }
@@ -111,8 +116,8 @@ MX_DEV uint32_t pick_pair(uint32_t u1, uint32_t u0, uint32_t sel) { return __bui
 
 // B fragments of one block for the 4 columns 4g..4g+3 of the lane: frag[e] = the 8 fp16 weights
 // (rows 8q..8q+7) of column 4g+e, as pairs (q[2p][c], q[2p+1][c]).
-template <bool I8, int C>
-MX_DEV void weights_to_frags(const Stage<I8, C>& s, int g, v8h (&frag)[4]) {
+template <bool I8, int C, int MT>
+MX_DEV void weights_to_frags(const Stage<I8, C, MT>& s, int g, v8h (&frag)[4]) {
   uint32_t f[4][4];
   if constexpr (I8) {
     // fp16 bits 0x64XX = 1024 + XX; XX = q ^ 0x80 = q + 128, so subtract 1152 (0x6480).
@@ -228,6 +233,7 @@ __global__ __launch_bounds__(W * 64) void matvec_kernel(const _Float16* __restri
   lo.w = I8 ? 8u * q * (uint32_t)N + cl : (8u * q * (uint32_t)N + cl) / 2u;
   lo.x = 2u * ((uint32_t)xrow * (uint32_t)K + 8u * q);
   lo.s = 2u * cl;
+  lo.xt = 0;
   const rsrc_t xr = make_rsrc(x, XL ? 0u : 2u * (uint32_t)M * (uint32_t)K);
   const _Float16* xl = xs + xrow * KC + 8 * q;  // XL: + 32*(blk - kb0) is the lane's x fragment
 
@@ -241,7 +247,7 @@ __global__ __launch_bounds__(W * 64) void matvec_kernel(const _Float16* __restri
   auto blk = [&](int u) { return kb0 + wave + W * u; };
   auto xfrag = [&](const Stage<I8, C>& st, int u) {
     if constexpr (XL) return *reinterpret_cast<const v8h*>(xl + 32 * (wave + W * u));
-    else return __builtin_bit_cast(v8h, st.xa);
+    else return __builtin_bit_cast(v8h, st.xa[0]);
   };
   Stage<I8, C> ring[P];
   int t = 0;
@@ -297,6 +303,170 @@ __global__ __launch_bounds__(W * 64) void matvec_kernel(const _Float16* __restri
 #pragma unroll
     for (int w = 0; w < W; w++) v += red[w][m][c];
     y[(int64_t)m * N + n0 + c] = (_Float16)v;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Small-M GEMM form (9 <= M <= 256 activation rows: the same block-scaled product at prefill-like
+// shapes). A workgroup owns MT tiles of 16 activation rows and a strip of TW = 16*C columns over
+// the whole of K; its W waves split K as in the single-pass kernel. Each dequantised weight
+// fragment of a block feeds MT MFMAs, one per activation tile, so the weight conversion is shared
+// by 16*MT rows; every block product is still scaled by its fp16 block scale in fp32 (one FMA per
+// output per block) and added to an fp32 accumulator. The waves' accumulators meet in LDS.
+// ---------------------------------------------------------------------------------------------
+// One block, software-pipelined across the column offsets e of the lane's 4 columns: the MFMAs of
+// offset e (one per activation tile) alternate with the scale FMAs of offset e-1, whose products
+// were issued a full round of MFMAs earlier, so neither the matrix core nor the vector ALU waits
+// on the other. The products of the last offset stay pending and are scaled during the first MFMA
+// round of the next block; flush_pending() scales what the last block left. The full scheduling
+// barriers keep this issue order (left alone, the scheduler puts each FMA right behind the MFMA
+// that produces its input).
+template <int MT>
+struct Pending {
+  v4f d[MT];   // products of the last column offset (column 3) of the previous block
+  uint32_t s;  // its fp16 scale (low half)
+};
+
+template <int C, int MT>
+MX_DEV void scale_add(v4f (&acc)[MT][C], const v4f& d, int t, int j, uint32_t sh) {
+  const float sj = (float)as_v2h(sh)[0];
+#pragma unroll
+  for (int v = 0; v < 4; v++) acc[t][j][v] = __builtin_fmaf(sj, d[v], acc[t][j][v]);
+}
+
+template <bool I8, int C, int MT>
+MX_DEV void compute_stage_mt(const Stage<I8, C, MT>& s, v4f (&acc)[MT][C], Pending<MT>& pend) {
+  static_assert(C == 4, "one group of 4 columns per lane");
+  v8h frag[4];
+  weights_to_frags<I8, C>(s, 0, frag);
+  uint32_t sh[4];  // fp16 scale of column e in the low half
+#pragma unroll
+  for (int e = 0; e < 4; e++) sh[e] = (e & 1) ? (s.sc[e / 2] >> 16) : s.sc[e / 2];
+  __builtin_amdgcn_sched_barrier(0);
+  v4f d[2][MT];
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+#pragma unroll
+    for (int t = 0; t < MT; t++) {
+      d[e & 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, s.xa[t]), frag[e],
+                                                           v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      if (e == 0) scale_add<C, MT>(acc, pend.d[t], t, 3, pend.s);
+      else scale_add<C, MT>(acc, d[(e - 1) & 1][t], t, e - 1, sh[e - 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MT; t++) pend.d[t] = d[1][t];
+  pend.s = sh[3];
+}
+
+template <int C, int MT>
+MX_DEV void flush_pending(v4f (&acc)[MT][C], const Pending<MT>& pend) {
+#pragma unroll
+  for (int t = 0; t < MT; t++) scale_add<C, MT>(acc, pend.d[t], t, 3, pend.s);
+}
+
+constexpr int kWqWPol = 0;  // cache policy of the weight and scale loads
+
+template <bool I8, int C, int MT, int W, int P>
+__global__ __launch_bounds__(W * 64) void gemm_wq_kernel(const _Float16* __restrict__ x, const uint8_t* __restrict__ Wt,
+                                                         const _Float16* __restrict__ Ws, _Float16* __restrict__ y,
+                                                         int M, int N, int K) {
+  constexpr int TW = 16 * C, RT = 16 * MT;  // columns and activation rows of the workgroup's tile
+  __shared__ __attribute__((aligned(16))) float red[W][RT][TW];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = lane & 15, q = lane >> 4;
+  // Workgroups go to the 8 XCDs (each with its own L2) round-robin by id. A strip is 16*C columns,
+  // less than a 128-byte line of a weight row (32 bytes for int4), so neighbouring strips share
+  // lines: the id is remapped so that each XCD takes a contiguous range of (strip, row tile) pairs,
+  // row tiles fastest, and every line is fetched into one L2 only.
+  const int nwg = (int)gridDim.x, mtiles = (M + RT - 1) / RT;
+  int bid = (int)blockIdx.x;
+  {
+    const int xcd = bid & 7, idx = bid >> 3, qq = nwg >> 3, rr = nwg & 7;
+    bid = (xcd < rr ? xcd * (qq + 1) : rr * (qq + 1) + (xcd - rr) * qq) + idx;
+  }
+  const int n0 = (bid / mtiles) * TW, m0 = (bid % mtiles) * RT, col = n0 + C * i;
+  const int nblk = K / 32;
+
+  // Columns as in the single-pass kernel (lanes past N load the last C columns). Activation rows
+  // come through a resource over rows m0..M-1: rows past M read as zero, their outputs are dropped.
+  const uint32_t cl = (uint32_t)(col < N ? col : N - C);
+  LaneOffsets lo;
+  lo.w = I8 ? 8u * q * (uint32_t)N + cl : (8u * q * (uint32_t)N + cl) / 2u;
+  lo.x = 2u * ((uint32_t)i * (uint32_t)K + 8u * q);
+  lo.s = 2u * cl;
+  lo.xt = 32u * (uint32_t)K;
+  const rsrc_t xr = make_rsrc(x + (int64_t)m0 * K, 2u * (uint32_t)(M - m0) * (uint32_t)K);
+
+  v4f acc[MT][C];
+#pragma unroll
+  for (int t = 0; t < MT; t++)
+#pragma unroll
+    for (int j = 0; j < C; j++) acc[t][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  Pending<MT> pend;  // nothing pending yet: zero products (adding +0 leaves the +0 accumulators)
+#pragma unroll
+  for (int t = 0; t < MT; t++) pend.d[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  pend.s = 0;
+
+  // this wave's blocks: wave + W*u, u < cnt; loads run P blocks ahead through a register ring
+  const int cnt = nblk > wave ? (nblk - wave + W - 1) / W : 0;
+  auto blk = [&](int u) { return wave + W * u; };
+  Stage<I8, C, MT> ring[P];
+  int t = 0;
+  if (cnt >= 2 * P) {
+#pragma unroll
+    for (int s = 0; s < P; s++) {
+      load_stage<I8, C, true, MT, kWqWPol>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(s), lo);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    do {
+#pragma unroll
+      for (int s = 0; s < P; s++) {
+        compute_stage_mt<I8, C, MT>(ring[s], acc, pend);
+        load_stage<I8, C, true, MT, kWqWPol>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(t + s + P), lo);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      t += P;
+    } while (t + 2 * P <= cnt);
+  } else {
+#pragma unroll
+    for (int s = 0; s < P; s++)
+      if (s < cnt) load_stage<I8, C, true, MT, kWqWPol>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(s), lo);
+  }
+#pragma unroll
+  for (int s = 0; s < P; s++) {
+    if (t + s < cnt) {
+      compute_stage_mt<I8, C, MT>(ring[s], acc, pend);
+      if (t + s + P < cnt) load_stage<I8, C, true, MT, kWqWPol>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(t + s + P), lo);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < P; s++)
+    if (t + P + s < cnt) compute_stage_mt<I8, C, MT>(ring[s], acc, pend);
+
+  flush_pending<C, MT>(acc, pend);
+  // acc[t][j][v] = this wave's share of y[m0 + 16t + 4q + v][col + j]
+#pragma unroll
+  for (int tt = 0; tt < MT; tt++)
+#pragma unroll
+    for (int j = 0; j < C; j++)
+#pragma unroll
+      for (int v = 0; v < 4; v++) red[wave][16 * tt + 4 * q + v][C * i + j] = acc[tt][j][v];
+  __syncthreads();
+  const int rows = min(RT, M - m0);
+  for (int o = threadIdx.x; o < rows * (TW / 4); o += W * 64) {
+    const int r = o / (TW / 4), c = 4 * (o % (TW / 4));
+    if (n0 + c >= N) continue;  // N % 4 == 0: a 4-column group is all in or all out
+    v4f v = *reinterpret_cast<const v4f*>(&red[0][r][c]);
+#pragma unroll
+    for (int w = 1; w < W; w++) v += *reinterpret_cast<const v4f*>(&red[w][r][c]);
+    v4h h;
+#pragma unroll
+    for (int e = 0; e < 4; e++) h[e] = (_Float16)v[e];
+    *reinterpret_cast<v4h*>(y + (int64_t)(m0 + r) * N + n0 + c) = h;
   }
 }
 
@@ -644,13 +814,40 @@ int launch(int M, int N, int K, const void* x, const void* W, const void* Ws, vo
   return launch_status();
 }
 
+// Small-M GEMM form (M > 8): 4 columns per lane (64-column strips). The row tile is the smallest of
+// 16, 32, 64 or 128 activation rows that keeps the grid within 3 rounds of the 256 compute units:
+// more workgroups hide more latency, fewer re-convert each weight fewer times. Measured on MI355X
+// (int4 and int8 alike): M=128, N=12288, K=4096: 32 rows with 8 waves 35 us, 128 rows with 4 waves
+// 38 us, 16 rows 48 us; M=64, N=4096: 16 rows 10 us, 32 rows 13 us, 64 rows 20 us.
+constexpr int kWqC = 4, kWqMaxWGs = 3 * 256;
+
+template <bool I8, int MT, int W, int P>
+int launch_wq_mt(int M, int N, int K, const void* x, const void* Wt, const void* Ws, void* y, hipStream_t st) {
+  const dim3 grid((unsigned)(((N + 16 * kWqC - 1) / (16 * kWqC)) * ((M + 16 * MT - 1) / (16 * MT))));
+  hipLaunchKernelGGL((gemm_wq_kernel<I8, kWqC, MT, W, P>), grid, dim3(W * 64), 0, st, (const _Float16*)x,
+                     (const uint8_t*)Wt, (const _Float16*)Ws, (_Float16*)y, M, N, K);
+  return launch_status();
+}
+
+template <bool I8>
+int launch_wq(int M, int N, int K, const void* x, const void* W, const void* Ws, void* y, hipStream_t st) {
+  const int64_t strips = (N + 16 * kWqC - 1) / (16 * kWqC);
+  auto wgs = [&](int rows) { return strips * ((M + rows - 1) / rows); };
+  if (wgs(16) <= kWqMaxWGs) return launch_wq_mt<I8, 1, 8, 4>(M, N, K, x, W, Ws, y, st);
+  if (wgs(32) <= kWqMaxWGs) return launch_wq_mt<I8, 2, 8, 2>(M, N, K, x, W, Ws, y, st);
+  if (wgs(64) <= kWqMaxWGs) return launch_wq_mt<I8, 4, 8, 2>(M, N, K, x, W, Ws, y, st);
+  return launch_wq_mt<I8, 8, 4, 3>(M, N, K, x, W, Ws, y, st);
+}
+
 }  // namespace
 
 namespace mx {
-size_t matvec_workspace(int M, int N, int K, bool int8) { return split_plan(M, N, K, int8).bytes; }
+size_t matvec_workspace(int M, int N, int K, bool int8) { return M > 8 ? 0 : split_plan(M, N, K, int8).bytes; }
 
 int matvec_launch(int M, int N, int K, const void* x, const void* W, bool int8, const void* Ws, void* y, void* ws,
                   size_t ws_bytes, hipStream_t stream) {
+  if (M > 8)
+    return int8 ? launch_wq<true>(M, N, K, x, W, Ws, y, stream) : launch_wq<false>(M, N, K, x, W, Ws, y, stream);
   return int8 ? launch<true>(M, N, K, x, W, Ws, y, ws, ws_bytes, stream)
               : launch<false>(M, N, K, x, W, Ws, y, ws, ws_bytes, stream);
 }

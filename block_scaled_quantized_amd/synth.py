@@ -12,12 +12,13 @@ from __future__ import annotations
 
 import numpy as np
 
-# Workload numbering used for seeds ("Inputs").
+# Workload numbering used for seeds.
 MXFP8_SMALL = 0      # MXFP8 GEMM M=128, N=256, K=128
 F16_SQUARE = 1       # fp16 GEMM M=N=K=4096
 MXFP8_PREFILL = 2    # MXFP8 GEMM M=2048, N=14336, K=4096
 MATVEC = 3           # dequant matvec K=4096, N=14336, M in {1, 8}
 MXFP4_LARGE = 4      # MXFP4 GEMM M=4096, N=8192, K=8192
+WQ_PREFILL = 5       # int8/int4-weight GEMM, fp16 block scales: M=128 N=12288 K=4096; M=64 N=4096 K=4096
 
 
 def seed_for(workload: int, operand: int) -> int:

@@ -132,10 +132,14 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
  *
  *   x  binary16 [M][K]      W int8 [K][N]  (fw = MX_INT8)  or packed int4 [K][N/2] (fw = MX_INT4)
  *   Ws binary16 [K/32][N]   y binary16 [M][N]
- * Shape rules: 1 <= M <= 8; K % 32 == 0, 32 <= K <= MX_MAX_DIM; 1 <= N <= MX_MAX_DIM;
+ * Shape rules: 1 <= M <= 256; K % 32 == 0, 32 <= K <= MX_MAX_DIM; 1 <= N <= MX_MAX_DIM;
  * N % 16 == 0 (int8) or N % 32 == 0 (int4). Device pointers, 16-byte aligned.
+ * M <= 8 is the decode matvec; 9 <= M <= 256 (the W8A16 / W4A16 prefill-like GEMM with the same
+ * arbitrary fp16 block scales, TensorOps notes, section "Kernel-phase findings") runs a small-M
+ * GEMM kernel: each block product is still formed exactly in fp32 and scaled once by its fp16
+ * block scale.
  *
- * Workspace: at decode shapes K is split across workgroups. Their fp32 partial sums and one
+ * Workspace (M <= 8 only; M > 8 never uses one): at decode shapes K is split across workgroups. Their fp32 partial sums and one
  * counter per column strip live in a caller-owned device buffer of mxmatvec_workspace_size()
  * bytes (16-byte aligned). The buffer must be zero-filled once before its first use (hipMemset,
  * or any zeroed allocation); every call leaves its counters at zero again, so the buffer stays
@@ -148,8 +152,8 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
 int mxmatvec_run(int M, int N, int K, const void* x, const void* W, int fw, const void* Ws, void* y,
                  void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes mxmatvec_run uses for this shape (0: none needed, or an invalid shape). The
- * requirement never decreases as M grows for fixed N, K and fw. */
+/* Workspace bytes mxmatvec_run uses for this shape (0: none needed, or an invalid shape). For
+ * 1 <= M <= 8 the requirement never decreases as M grows for fixed N, K and fw; for M > 8 it is 0. */
 size_t mxmatvec_workspace_size(int M, int N, int K, int fw);
 
 /* ------------------------------------------------------------------------------------------ */

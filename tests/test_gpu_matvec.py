@@ -119,3 +119,51 @@ def test_matvec_small_workspace_falls_back(orc):
     ok, ratio, bad = orc.check(host(y).astype(np.float64), ref, K, R)
     assert ok, (ratio, bad)
     assert int(ws.sum().item()) == 0      # untouched
+
+
+# ---- the same product at 9 <= M <= 256 (small-M GEMM kernel) --------------------------------
+
+def wq_case(orc, api, fw, M, K, N, seed_w, seed_x):
+    w = synth.normal((K, N), 0.02, seed_w)
+    x = synth.normal((M, K), 1.0, seed_x).astype(np.float16)
+    W, Ws = gpu_int_pack(api, fw, w)
+    q, s = orc.int_quantize(fw, w)
+    oW = q.view(np.uint8) if fw == api.MX_INT8 else orc.pack_int4(q)
+    assert np.array_equal(host(W), oW) and np.array_equal(host(Ws).view(np.uint16), s.view(np.uint16))
+    assert api.mxmatvec_workspace_size(M, N, K, fw) == 0
+    y = empty((M, N), torch.float16)
+    api.mxmatvec_run(M, N, K, dev(x), W, fw, Ws, y)
+    R = orc.rms_ab(x.astype(np.float64), orc.dequant(fw, oW, s, K, N))
+    return x, oW, s, host(y).astype(np.float64), R
+
+
+@pytest.mark.parametrize("fw", [32, 33])
+@pytest.mark.parametrize("M,K,N", [(9, 32, 32), (16, 1024, 1056), (31, 96, 160), (33, 4096, 64), (64, 544, 4128),
+                                   (100, 256, 12288), (128, 4096, 512), (129, 160, 96), (200, 1024, 1024),
+                                   (256, 2048, 320), (150, 96, 12800), (200, 64, 16384), (129, 64, 19200)])
+def test_wq_gemm_ragged(orc, fw, M, K, N):
+    """Every output: partial row tiles, partial column strips, one block of K up to many. The row
+    tile grows with the grid: 16 rows for most of these, 32 at M=100/N=12288, 64 at M=150/N=12800,
+    128 at M=200/N=16384 and M=129/N=19200 (two row tiles, the second with one row)."""
+    api = require_gpu()
+    say(f"wq gemm fw={fw} M={M} K={K} N={N}")
+    x, oW, s, got, R = wq_case(orc, api, fw, M, K, N, 13 * K + N + M, 5 * K + M)
+    ok, ratio, bad = orc.check(got, orc.matvec(fw, x, oW, s, K, N), K, R)
+    assert ok, (ratio, bad)
+
+
+@pytest.mark.parametrize("fw", [32, 33])
+@pytest.mark.parametrize("M,K,N", [(128, 4096, 12288), (64, 4096, 4096)])
+def test_wq_gemm_full_size_sampled(orc, fw, M, K, N):
+    """The W8A16 / W4A16 prefill shapes: 2048 sampled outputs (corners included) against the
+    oracle's per-element formula, and all of y finite."""
+    api = require_gpu()
+    say(f"wq gemm full fw={fw} M={M} K={K} N={N}")
+    x, oW, s, got, R = wq_case(orc, api, fw, M, K, N, synth.seed_for(synth.WQ_PREFILL, 1),
+                                synth.seed_for(synth.WQ_PREFILL, 0))
+    assert np.isfinite(got).all()
+    ms, ns = synth.sample_points(M, N, 2048, 77)
+    ref = np.array([orc.matvec_elem(fw, x, oW, s, K, N, int(m), int(n)) for m, n in zip(ms, ns)])
+    ok, ratio, bad = orc.check(got[ms, ns], ref, K, R)
+    say(f"worst err/bound {ratio:.3f}")
+    assert ok, (ratio, bad)

@@ -130,7 +130,7 @@ def test_validation_errors_without_gpu():
     assert lib.mxgemm_run(h, 17, 16, 16, 16, 16, None) == api.MX_ERR_ALIGN
     assert lib.mxgemm_destroy(h) == 0
     assert lib.mxgemm_destroy(None) == 0
-    assert lib.mxmatvec_run(9, 16, 32, 16, 16, 32, 16, 16, None, 0, None) == api.MX_ERR_SHAPE       # M > 8
+    assert lib.mxmatvec_run(257, 16, 32, 16, 16, 32, 16, 16, None, 0, None) == api.MX_ERR_SHAPE     # M > 256
     assert lib.mxmatvec_run(1, 16, 40, 16, 16, 32, 16, 16, None, 0, None) == api.MX_ERR_SHAPE       # K % 32
     assert lib.mxmatvec_run(1, 16, 32, 16, 16, 33, 16, 16, None, 0, None) == api.MX_ERR_SHAPE       # int4 N % 32
     assert lib.mxmatvec_run(1, 16, 32, 16, 16, 0, 16, 16, None, 0, None) == api.MX_ERR_FORMAT
@@ -215,3 +215,12 @@ def test_matvec_workspace_size():
             assert b >= 2 * m * 14336 * 4     # at least two splits at the decode shape
     # a tiny K is never split
     assert api.mxmatvec_workspace_size(8, 14336, 32, api.MX_INT8) == 0
+
+
+def test_small_m_gemm_shape_rules():
+    """9 <= M <= 256 is the small-M GEMM form: accepted up to 256 rows and never given a workspace."""
+    for M in (9, 64, 128, 256):
+        assert api.mxmatvec_workspace_size(M, 12288, 4096, api.MX_INT4) == 0
+        assert api.mxmatvec_workspace_size(M, 4096, 4096, api.MX_INT8) == 0
+    assert api.mxmatvec_workspace_size(257, 4096, 4096, api.MX_INT8) == 0     # invalid shape
+    assert api.mxmatvec_workspace_size(8, 4096, 4096, api.MX_INT8) > 0
