@@ -762,6 +762,12 @@ int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void
       if (kind == KIND_E4M3) return launch<KIND_E4M3, 256, 224, 4, 2>(a, stream);
       if (kind == KIND_E2M1) return launch<KIND_E2M1, 256, 224, 4, 2>(a, stream);
       return launch<KIND_F16, 256, 224, 4, 2>(a, stream);
+    case 10:  // the ring with 256x192 tiles (E4M3 / E2M1 on the ring's shapes); otherwise the 8-wave 256x256 kernel
+      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(0, 192, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(1, 192, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_E4M3) return launch<KIND_E4M3, 256, 256, 4, 2>(a, stream);
+      if (kind == KIND_E2M1) return launch<KIND_E2M1, 256, 256, 4, 2>(a, stream);
+      return launch<KIND_F16, 256, 256, 4, 2>(a, stream);
     default: return MX_ERR_FORMAT;
   }
 #undef MX_TILE

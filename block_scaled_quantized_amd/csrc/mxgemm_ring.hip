@@ -59,14 +59,14 @@ constexpr int GROUP = 8;                // stages per scale group
 constexpr int MAX_DPS = 8;              // direct copies per wave per stage, at most
 
 // Tile shapes. WAVES_M waves along M (the rest along N); each wave holds FA x FB MFMA tiles of
-// 32 x 32 (FA along M, FB along N).
-template <int WAVES_M_>
+// 32 x 32 (FA along M, FB along N). 256 x 256 and 256 x 192 with 2 x 2 waves, 256 x 224 with 4 x 1.
+template <int WAVES_M_, int BN_>
 struct RingTile {
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = 4 / WAVES_M;
-  static constexpr int BN = WAVES_M == 2 ? 256 : 224;
+  static constexpr int BN = BN_;
   static constexpr int FA = BM / 32 / WAVES_M, FB = BN / 32 / WAVES_N;
   static constexpr int F = FA + FB;  // fragments read per stage per wave
-  static_assert(WAVES_M == 2 || WAVES_M == 4, "tile");
+  static_assert((WAVES_M == 2 && (BN == 256 || BN == 192)) || (WAVES_M == 4 && BN == 224), "tile");
 };
 
 // Per-format constants. KIND 0: E4M3 x E4M3, 1: E2M1 x E2M1, 2: E4M3 A x E2M1 B, 3: E2M1 A x E4M3 B,
@@ -98,6 +98,20 @@ struct RingFmt {
     DMA_PER_GROUP = F16 ? 0 : SGRP / 1024 / 4          // scale copies per wave per group (2 / 4)
   };
   static_assert(NI_A % 4 == 0 && NI_B % 4 == 0 && DPS <= MAX_DPS, "copies");
+};
+
+// Copies of a stage for a tile width: NI_A for A, then enough 1 KB copies for the tile's B rows,
+// rounded up so that the 4 waves issue the same number (the extra ones fill unused slot bytes with
+// zeros from an empty resource): DPS per wave.
+template <int KIND, class T>
+struct RingCopies {
+  enum : int {
+    NI_A = RingFmt<KIND>::NI_A,
+    NI_B0 = (T::BN * RingFmt<KIND>::SRB_B + 1023) / 1024,
+    NI_B = (NI_A + NI_B0 + 3) / 4 * 4 - NI_A,
+    DPS = (NI_A + NI_B) / 4
+  };
+  static_assert(DPS <= MAX_DPS && (!RingFmt<KIND>::F16 || T::BN == 256), "copies");
 };
 
 // The size goes through readfirstlane: clamps of uniform values can be selected as vector ops
@@ -287,11 +301,12 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
                        v8i (&na)[T::FA], v8i (&nb)[T::FB], const char* slot_nxt, char* slot_fill,
                        Scales<KIND, T>& sc, RawScales<KIND, T>& raw, v16f (&acc)[T::FB][T::FA]) {
   using F = RingFmt<KIND>;
+  using CP = RingCopies<KIND, T>;
   const int t = GROUP * g + S8;
   // Copies queued after this wave's copies of stage t+1 (issued at stage t-2): those of stage t+2
   // (at stage t-1) and, at S8 == 3, the scale group issued at S8 == 2 ahead of them. From S8 == 4
   // on, the next group's scales are visible.
-  wait_vm_n(S8 == 3 ? F::DPS + F::DMA_PER_GROUP : F::DPS);
+  wait_vm_n(S8 == 3 ? CP::DPS + F::DMA_PER_GROUP : CP::DPS);
   raw_barrier();
   // The scale array still holds half 1 of group g, read at the end of stage 7 of group g-1. Every
   // wave has waited for those reads before stage 1's MFMAs (they precede the fragment reads of
@@ -333,7 +348,7 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
     // this tile's share of the stage copies: copies [DPS*i/FB, DPS*(i+1)/FB) (copy q is an A copy
     // when q < NI_A/4)
 #pragma unroll
-    for (int q = F::DPS * i / T::FB; q < F::DPS * (i + 1) / T::FB; q++) {
+    for (int q = CP::DPS * i / T::FB; q < CP::DPS * (i + 1) / T::FB; q++) {
       // (offsets computed into locals first: the host pass of hipcc drops the kernel, silently, when
       // these builtin arguments are written as conditional expressions of the format constants)
       const bool qa = q < F::NI_A / 4;
@@ -360,10 +375,11 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
   }
 }
 
-template <int KIND, int WAVES_M>
+template <int KIND, int WAVES_M, int BN_>
 __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   using F = RingFmt<KIND>;
-  using T = RingTile<WAVES_M>;
+  using T = RingTile<WAVES_M, BN_>;
+  using CP = RingCopies<KIND, T>;
   constexpr int BN = T::BN;
   __shared__ __attribute__((aligned(16))) char slot0[SLOT];
   __shared__ __attribute__((aligned(16))) char slot1[SLOT];
@@ -423,7 +439,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
     }
   }
 #pragma unroll
-  for (int k = 0; k < F::DPS; k++) {
+  for (int k = 0; k < CP::DPS; k++) {
     const int i = wave + 4 * k;
     const bool isA = k < F::NI_A / 4;
     const int rpi = (isA ? F::SRB_A : F::SRB_B) == 64 ? 16 : 32;  // rows per instruction
@@ -464,7 +480,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   for (int t = 0; t < 3 && t < nst; t++) {
     char* slot = t == 0 ? slot0 : (t == 1 ? slot1 : slot2);
 #pragma unroll
-    for (int k = 0; k < F::DPS; k++) {
+    for (int k = 0; k < CP::DPS; k++) {
       const bool qa = k < F::NI_A / 4;
       const uint32_t vo = qa ? c.voff_a : c.voff_b;
       const uint32_t so = stage_soff<KIND>(c, qa, (uint32_t)t);
@@ -575,7 +591,7 @@ namespace mx {
 // Ring kernels. kind 0: E4M3 x E4M3, 1: E2M1 x E2M1, 2: E4M3 A x E2M1 B, 3: E2M1 A x E4M3 B,
 // 4: fp16 x fp16 (B K x N). Requires N % 4 == 0 and K % 512 == 0 (K % 1024 == 0 for kind 1); for
 // kind 4 N % 256 == 0, K % 256 == 0 and 2*K*N < 2^31, bn = 256 only. Checked by the caller.
-// bn = 256 or 224.
+// bn = 256, 224 or 192 (192: kinds 0 and 1).
 int gemm_ring_launch(int kind, int bn, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
                      int N, int K, bool relu, hipStream_t stream) {
   Args a{};
@@ -591,22 +607,28 @@ int gemm_ring_launch(int kind, int bn, const void* A, const void* SA, const void
   a.tiles_m = (M + BM - 1) / BM;
   const int tiles = a.tiles_m * ((N + bn - 1) / bn);
   const dim3 grid((unsigned)tiles), block(256);
-#define MX_RING(KD, WM) hipLaunchKernelGGL((gemm_ring_kernel<KD, WM>), grid, block, 0, stream, a)
+#define MX_RING(KD, WM, BNT) hipLaunchKernelGGL((gemm_ring_kernel<KD, WM, BNT>), grid, block, 0, stream, a)
   if (bn == 224) {
     switch (kind) {
-      case 0: MX_RING(0, 4); break;
-      case 1: MX_RING(1, 4); break;
-      case 2: MX_RING(2, 4); break;
-      case 3: MX_RING(3, 4); break;
+      case 0: MX_RING(0, 4, 224); break;
+      case 1: MX_RING(1, 4, 224); break;
+      case 2: MX_RING(2, 4, 224); break;
+      case 3: MX_RING(3, 4, 224); break;
+      default: return MX_ERR_FORMAT;
+    }
+  } else if (bn == 192) {
+    switch (kind) {
+      case 0: MX_RING(0, 2, 192); break;
+      case 1: MX_RING(1, 2, 192); break;
       default: return MX_ERR_FORMAT;
     }
   } else {
     switch (kind) {
-      case 0: MX_RING(0, 2); break;
-      case 1: MX_RING(1, 2); break;
-      case 2: MX_RING(2, 2); break;
-      case 3: MX_RING(3, 2); break;
-      default: MX_RING(4, 2); break;
+      case 0: MX_RING(0, 2, 256); break;
+      case 1: MX_RING(1, 2, 256); break;
+      case 2: MX_RING(2, 2, 256); break;
+      case 3: MX_RING(3, 2, 256); break;
+      default: MX_RING(4, 2, 256); break;
     }
   }
 #undef MX_RING

@@ -115,9 +115,10 @@ int mxgemm_destroy(mxgemm_t p);
 /* Kernel chosen by a plan (for reports): output tile rows and columns, K elements per pipeline
  * stage, and the kernel variant (0: 4 waves, 1: 8 waves, 2: 8-wave ping-pong schedule, 3: 4-stage
  * LDS ring of 64-byte K stages, for MX formats with N % 4 == 0 and K % 512 == 0 (E4M3) or
- * K % 1024 == 0 (E2M1)). The environment variable MXGEMM_TILE (a tile id 0..9; 8 and 9 are the ring
- * with 256x256 and 256x224 tiles where it applies, else the 8-wave kernel of that tile), read at
- * mxgemm_create, overrides the choice. */
+ * K % 1024 == 0 (E2M1), and for fp16 with N % 256 == 0, K % 256 == 0 on 256x256 tiles). The
+ * environment variable MXGEMM_TILE (a tile id 0..10; 8, 9 and 10 are the ring with 256x256,
+ * 256x224 and 256x192 tiles where it applies, else an 8-wave kernel: 256x256 for 8 and 10,
+ * 256x224 for 9), read at mxgemm_create, overrides the choice. */
 int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* variant);
 
 /* ------------------------------------------------------------------------------------------ */

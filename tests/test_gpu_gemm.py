@@ -92,11 +92,11 @@ def test_mx_pingpong_ragged_mn(orc, fmt, tile, K):
     (0, 33, 1028, 2560),
     (4, 300, 520, 1024), (4, 257, 260, 4096), (4, 1, 4, 1024), (4, 512, 512, 2048), (4, 33, 1028, 3072),
 ])
-@pytest.mark.parametrize("tile", [8, 9])
+@pytest.mark.parametrize("tile", [8, 9, 10])
 def test_mx_ring_ragged(orc, fmt, M, N, K, tile):
-    """The 4-stage ring kernels, 256x256 (tile 8) and 256x224 (tile 9) tiles (N % 4 == 0; K % 512 == 0
-    for E4M3, K % 1024 == 0 for E2M1): one scale group up to several, partial tiles in M and N, a
-    single row and column strip."""
+    """The 4-stage ring kernels, 256x256 (tile 8), 256x224 (tile 9) and 256x192 (tile 10) tiles
+    (N % 4 == 0; K % 512 == 0 for E4M3, K % 1024 == 0 for E2M1): one scale group up to several,
+    partial tiles in M and N, a single row and column strip."""
     api = require_gpu()
     say(f"mx ring tile={tile} fmt={fmt} M={M} N={N} K={K}")
     C, (oA, oSA, oB, oSB) = mx_case(orc, api, fmt, M, N, K, 31 + M + N + K, tile=tile)

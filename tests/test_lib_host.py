@@ -169,6 +169,11 @@ def test_ring_tile_plan_info(monkeypatch):
     assert info(512, 520, 512, api.MX_F16) == (256, 256, 64, 1)       # N % 256
     assert info(512, 512, 384, api.MX_F16) == (256, 256, 64, 1)       # K % 256
     assert info(256, 32768, 32768, api.MX_F16) == (256, 256, 64, 1)   # 2KN = 2^31
+    monkeypatch.setenv("MXGEMM_TILE", "10")
+    assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 192, 64, 3)
+    assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 192, 128, 3)
+    assert info(300, 520, 416, api.MX_E4M3) == (256, 256, 128, 1)       # not a ring shape: 8-wave 256x256
+    assert info(512, 512, 512, api.MX_F16) == (256, 256, 64, 1)
     monkeypatch.setenv("MXGEMM_TILE", "9")
     assert info(512, 512, 512, api.MX_F16) == (256, 224, 64, 1)
     assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 224, 64, 3)
@@ -178,6 +183,8 @@ def test_ring_tile_plan_info(monkeypatch):
     assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 256, 64, 3)
     assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 128, 3)
     assert info(4096, 4096, 4096, api.MX_F16) == (256, 256, 32, 3)
+    assert info(2048, 12288, 4096, api.MX_E4M3) == (256, 192, 64, 3)     # whole rounds of 256x192
+    assert info(2048, 6144, 4096, api.MX_E4M3) == (256, 192, 64, 3)
     for M, N, K, f in [(300, 520, 416, api.MX_E4M3), (4096, 8192, 1536, api.MX_E2M1), (512, 520, 512, api.MX_F16)]:
         assert info(M, N, K, f)[3] != 3
 
