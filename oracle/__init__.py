@@ -25,7 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-E4M3, E2M1, F16, INT8, INT4 = 0, 4, 16, 32, 33
+E4M3, E5M2, E2M1, F16, INT8, INT4 = 0, 1, 4, 16, 32, 33
 
 _lib = None
 
@@ -49,7 +49,7 @@ def lib():
     d, u, i, i64, p = ctypes.c_double, ctypes.c_uint, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
     sig = {
         "orc_num_threads": (i, []),
-        "orc_dec_e4m3": (d, [u]), "orc_dec_e2m1": (d, [u]), "orc_dec_e8m0": (d, [u]),
+        "orc_dec_e4m3": (d, [u]), "orc_dec_e5m2": (d, [u]), "orc_dec_e2m1": (d, [u]), "orc_dec_e8m0": (d, [u]),
         "orc_dec_int4": (d, [u]), "orc_dec_f16": (d, [u]),
         "orc_mx_dot": (d, [i, i, i64, p, p, p, p, i64, i64]),
         "orc_mxgemm_rows": (None, [i, i, i64, i64, i64, p, p, p, p, i64, i64, p]),
@@ -88,6 +88,10 @@ def num_threads() -> int:
 
 def dec_e4m3(codes) -> np.ndarray:
     return np.array([lib().orc_dec_e4m3(int(c)) for c in np.ravel(codes)]).reshape(np.shape(codes))
+
+
+def dec_e5m2(codes) -> np.ndarray:
+    return np.array([lib().orc_dec_e5m2(int(c)) for c in np.ravel(codes)]).reshape(np.shape(codes))
 
 
 def dec_e2m1(codes) -> np.ndarray:

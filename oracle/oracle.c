@@ -20,9 +20,11 @@
  *    matmul (E4M3 data plane, half output).
  *  - "TileLang Metal Backend Internals", section 1.4: fp32 accumulation, fp16 output by a cast
  *    at store.
- * The pages name E4M3, fp4 and E8M0 without giving their bits. The readings used here are the
- * OCP Microscaling (MX) v1.0 element formats: E4M3 "FN" (bias 7, S.1111.111 = NaN, no Inf, max
- * 448), E2M1 (bias 1, values +-{0,.5,1,1.5,2,3,4,6}, no NaN/Inf) and E8M0 (2^(e-127), 0xFF=NaN).
+ * The pages name E4M3, fp8, fp4, "MX scaling formats" and E8M0 without giving their bits (TensorOps
+ * notes, quantized dtype support matrix). The readings used here are the OCP Microscaling (MX) v1.0
+ * element formats: E4M3 "FN" (bias 7, S.1111.111 = NaN, no Inf, max 448), E5M2 (bias 15,
+ * S.11111.00 = Inf, S.11111.xx = NaN, max 57344), E2M1 (bias 1, values +-{0,.5,1,1.5,2,3,4,6},
+ * no NaN/Inf) and E8M0 (2^(e-127), 0xFF=NaN).
  *
  * Every function here has a pin in the CPU test suite (library dtypes, closed forms, exact
  * brute force, invariants); none is "parity unpinned".
@@ -35,7 +37,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_E4M3 = 0, ORC_E2M1 = 4, ORC_F16 = 16, ORC_INT8 = 32, ORC_INT4 = 33 };
+enum { ORC_E4M3 = 0, ORC_E5M2 = 1, ORC_E2M1 = 4, ORC_F16 = 16, ORC_INT8 = 32, ORC_INT4 = 33 };
 
 int orc_num_threads(void) {
 #ifdef _OPENMP
@@ -57,6 +59,17 @@ double orc_dec_e4m3(unsigned b) {
   if ((b & 0x7Fu) == 0x7Fu) return NAN;
   if (e == 0) v = ldexp((double)f, -9);
   else v = ldexp(1.0 + (double)f / 8.0, (int)e - 7);
+  return s ? -v : v;
+}
+
+/* E5M2: sign 1, exponent 5 (bias 15), mantissa 2. Exponent 0 is subnormal f*2^-16. Exponent 31
+ * is infinity (mantissa 0) or NaN (mantissa nonzero). */
+double orc_dec_e5m2(unsigned b) {
+  unsigned s = (b >> 7) & 1u, e = (b >> 2) & 31u, f = b & 3u;
+  double v;
+  if (e == 31) v = f ? NAN : INFINITY;
+  else if (e == 0) v = ldexp((double)f, -16);
+  else v = ldexp(1.0 + (double)f / 4.0, (int)e - 15);
   return s ? -v : v;
 }
 
@@ -100,7 +113,8 @@ static unsigned nibble(const uint8_t* row, int64_t j) {
 
 /* Dequantised value of element k of one MX row (codes along K, scales one per 32 along K). */
 static double mx_elem(int fmt, const uint8_t* codes_row, const uint8_t* scales_row, int64_t k) {
-  double v = (fmt == ORC_E4M3) ? orc_dec_e4m3(codes_row[k]) : orc_dec_e2m1(nibble(codes_row, k));
+  double v = (fmt == ORC_E4M3) ? orc_dec_e4m3(codes_row[k])
+             : (fmt == ORC_E5M2) ? orc_dec_e5m2(codes_row[k]) : orc_dec_e2m1(nibble(codes_row, k));
   return v * orc_dec_e8m0(scales_row[k / 32]);
 }
 
@@ -207,7 +221,7 @@ void orc_dequant(int fmt, int64_t rows, int64_t cols, const uint8_t* codes, cons
   for (int64_t r = 0; r < rows; r++)
     for (int64_t c = 0; c < cols; c++) {
       double v;
-      if (fmt == ORC_E4M3 || fmt == ORC_E2M1) {
+      if (fmt == ORC_E4M3 || fmt == ORC_E5M2 || fmt == ORC_E2M1) {
         v = mx_elem(fmt, codes + r * mx_row_bytes(fmt, cols), (const uint8_t*)scales + r * (cols / 32), c);
       } else {
         double s = orc_dec_f16(((const uint16_t*)scales)[(r / 32) * cols + c]);
@@ -220,19 +234,20 @@ void orc_dequant(int fmt, int64_t rows, int64_t cols, const uint8_t* codes, cons
 /* ------------------------------------------------------------------------------------------ */
 /* Encoders. These are encodings, so they follow the quantisation steps in order:               */
 /*  1. amax of the 32-element block, 2. j = floor(log2 amax) from the exact binary exponent,     */
-/*  3. E = clamp(j - emax + 127, 0, 254) with emax = 8 (E4M3) or 2 (E2M1),                       */
+/*  3. E = clamp(j - emax + 127, 0, 254) with emax = 8 (E4M3), 15 (E5M2) or 2 (E2M1),          */
 /*  4. v = x * 2^(127-E) exactly, 5. the element code nearest to v, ties to the even code,       */
 /*     values beyond the largest finite element saturate to it, the sign is kept.              */
 /* The element search is brute force over the format's own decode values (not bit arithmetic). */
 /* ------------------------------------------------------------------------------------------ */
 
-/* The positive finite element values of a format, indexed by code (E4M3: 0x00..0x7E, E2M1: 0..7),
- * filled once from the closed-form decoders above. */
-static double g_tab_e4m3[0x7F], g_tab_e2m1[8];
+/* The positive finite element values of a format, indexed by code (E4M3: 0x00..0x7E, E5M2:
+ * 0x00..0x7B, E2M1: 0..7), filled once from the closed-form decoders above. */
+static double g_tab_e4m3[0x7F], g_tab_e5m2[0x7C], g_tab_e2m1[8];
 static int g_tab_ready = 0;
 static void build_tables(void) {
   if (g_tab_ready) return;
   for (unsigned c = 0; c < 0x7Fu; c++) g_tab_e4m3[c] = orc_dec_e4m3(c);
+  for (unsigned c = 0; c < 0x7Cu; c++) g_tab_e5m2[c] = orc_dec_e5m2(c);
   for (unsigned c = 0; c < 8u; c++) g_tab_e2m1[c] = orc_dec_e2m1(c);
   g_tab_ready = 1;
 }
@@ -241,8 +256,8 @@ static void build_tables(void) {
  * ties to the even code. Values at or beyond the largest finite element saturate to it; below it
  * every candidate distance that can decide the choice is exact in fp64. */
 static unsigned nearest_code(double av, int fmt) {
-  const double* tab = (fmt == ORC_E4M3) ? g_tab_e4m3 : g_tab_e2m1;
-  unsigned best = 0, ncodes = (fmt == ORC_E4M3) ? 0x7Fu : 8u;
+  const double* tab = (fmt == ORC_E4M3) ? g_tab_e4m3 : (fmt == ORC_E5M2) ? g_tab_e5m2 : g_tab_e2m1;
+  unsigned best = 0, ncodes = (fmt == ORC_E4M3) ? 0x7Fu : (fmt == ORC_E5M2) ? 0x7Cu : 8u;
   double bestd = INFINITY;
   if (av >= tab[ncodes - 1u]) return ncodes - 1u;
   for (unsigned c = 0; c < ncodes; c++) {
@@ -256,7 +271,7 @@ static unsigned nearest_code(double av, int fmt) {
 unsigned orc_enc_elem(int fmt, double v) {
   build_tables();
   unsigned mag = nearest_code(fabs(v), fmt);
-  unsigned sbit = (fmt == ORC_E4M3) ? 0x80u : 0x8u;
+  unsigned sbit = (fmt == ORC_E2M1) ? 0x8u : 0x80u;
   return signbit(v) ? (mag | sbit) : mag;
 }
 
@@ -269,7 +284,7 @@ int orc_floor_log2(double a) {
 
 /* The E8M0 scale code of one block, from its amax (step 2-3). */
 unsigned orc_mx_scale_code(int fmt, double amax) {
-  int emax = (fmt == ORC_E4M3) ? 8 : 2, E;
+  int emax = (fmt == ORC_E4M3) ? 8 : (fmt == ORC_E5M2) ? 15 : 2, E;
   if (!(amax > 0.0)) return 0u; /* amax = 0: log2 is -inf, clamps to 0 */
   E = orc_floor_log2(amax) - emax + 127;
   if (E < 0) E = 0;
@@ -300,7 +315,7 @@ void orc_mx_quantize(int fmt, int64_t rows, int64_t cols, const float* src, uint
       for (int i = 0; i < 32; i++) {
         int64_t c = 32 * b + i;
         unsigned code = orc_enc_elem(fmt, ldexp((double)x[i], 127 - (int)E));
-        if (fmt == ORC_E4M3) codes[r * rb + c] = (uint8_t)code;
+        if (fmt != ORC_E2M1) codes[r * rb + c] = (uint8_t)code;
         else codes[r * rb + c / 2] |= (uint8_t)((c % 2 == 0) ? code : (code << 4));
       }
     }

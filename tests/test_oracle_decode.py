@@ -28,6 +28,12 @@ def test_e4m3_all_codes_match_torch(orc):
     _same(orc.dec_e4m3(codes), ref)
 
 
+def test_e5m2_all_codes_match_torch(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    _same(orc.dec_e5m2(codes), ref)
+
+
 def test_e4m3_golden_specials(orc):
     for code, val in read_golden("e4m3_specials.txt"):
         got = orc.dec_e4m3([int(code, 16)])[0]

@@ -1,7 +1,7 @@
 """Pins of the oracle's GEMM, matvec and dequant against what the mathematics fixes.
 
 - Unit scales reduce the MX GEMM to a plain fp8 matmul: compared bit-for-bit with torch's fp64
-  matmul of torch-decoded E4M3 (all partial sums are exact in fp64 at these sizes).
+  matmul of torch-decoded E4M3 / E5M2 (all partial sums are exact in fp64 at these sizes).
 - Tiny shapes with random scales: the exact rational sum (fractions.Fraction) within the fp64
   recursive-summation bound.
 - Scale shift and block locality invariants, on data chosen so every sum is exact.
@@ -54,6 +54,35 @@ def test_mx_e4m3_unit_scales_is_plain_fp8_matmul(orc, M, N, K):
     C = orc.mxgemm(orc.E4M3, orc.E4M3, A, SA, B, SB, M, N, K)
     ref = (torch_e4m3(A) @ torch_e4m3(B).T).numpy()
     assert np.array_equal(C, ref)
+
+
+E5M2_NONFINITE = tuple(c for c in range(256) if (c & 0x7C) == 0x7C)   # Inf and NaN codes
+
+
+def torch_e5m2(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e5m2).to(torch.float64)
+
+
+@pytest.mark.parametrize("M,N,K", [(7, 5, 32), (16, 16, 128)])
+def test_mx_e5m2_unit_scales_is_plain_fp8_matmul(orc, M, N, K):
+    """E5M2, and E5M2 x E4M3, at unit scales: torch's fp64 matmul of torch-decoded codes. Exponent
+    fields 8..23 (values 2^-7 .. 1.75*2^8, zero included) keep every product a multiple of 2^-16
+    below 2^18, so all partial sums are exact in fp64 whatever the order."""
+    g = np.random.Generator(np.random.PCG64(15 + K))
+
+    def codes(shape):
+        e = g.integers(8, 24, size=shape)
+        e[g.random(shape) < 0.05] = 0                        # some zeros and subnormal-field codes
+        return ((g.integers(0, 2, size=shape) << 7) | (e << 2) | g.integers(0, 4, size=shape)).astype(np.uint8)
+    A = codes((M, K))
+    B = codes((N, K))
+    SA = np.full((M, K // 32), 127, np.uint8)
+    SB = np.full((N, K // 32), 127, np.uint8)
+    C = orc.mxgemm(orc.E5M2, orc.E5M2, A, SA, B, SB, M, N, K)
+    assert np.array_equal(C, (torch_e5m2(A) @ torch_e5m2(B).T).numpy())
+    B8 = synth.random_bytes((N, K), 18 + K, exclude=E4M3_NAN)
+    C = orc.mxgemm(orc.E5M2, orc.E4M3, A, SA, B8, SB, M, N, K)
+    assert np.array_equal(C, (torch_e5m2(A) @ torch_e4m3(B8).T).numpy())
 
 
 def test_mx_e2m1_unit_scales_is_plain_fp4_matmul(orc):
@@ -218,6 +247,12 @@ def test_dequant_mx_vs_torch(orc):
     ref = (a * s).numpy()
     assert np.array_equal(out.view(np.uint32)[~np.isnan(ref)], ref.view(np.uint32)[~np.isnan(ref)])
     assert np.array_equal(np.isnan(out), np.isnan(ref))
+    # E5M2: every code (Inf and NaN included) times scale, fp32 product
+    out5 = orc.dequant(1, A, S, rows, cols)
+    ref5 = (torch.from_numpy(A).view(torch.float8_e5m2).float() * s).numpy()
+    fin5 = ~np.isnan(ref5)
+    assert np.array_equal(out5.view(np.uint32)[fin5], ref5.view(np.uint32)[fin5])
+    assert np.array_equal(np.isnan(out5), np.isnan(ref5))
     # E2M1: table value times scale, fp32 product
     A4 = synth.random_bytes((rows, cols // 2), 73)
     out4 = orc.dequant(4, A4, S, rows, cols)

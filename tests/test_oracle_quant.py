@@ -3,6 +3,8 @@
 - E4M3 element encoding: torch's fp32 -> float8_e4m3fn cast (round to nearest even) on every
   midpoint, midpoint +- 1 ulp and random values up to 464 (torch returns NaN above 464, where the
   oracle saturates to 448 by the reading taken for overflow).
+- E5M2 element encoding: torch's fp32 -> float8_e5m2 cast below 61440 (Inf there in torch; the
+  oracle saturates to 57344).
 - E2M1 element encoding: numpy's half-to-even np.round on the spacing of each binade.
 - floor(log2): the defining inequality 2^j <= a < 2^(j+1), checked exactly.
 - Block scale rule: closed cases (powers of two and their predecessors, zero, clamps).
@@ -55,6 +57,37 @@ def test_enc_e4m3_matches_torch_in_range(orc):
     assert np.array_equal(got, torch_enc_e4m3(allv))
 
 
+def torch_enc_e5m2(v32):
+    return torch.from_numpy(np.ascontiguousarray(v32, dtype=np.float32)).to(torch.float8_e5m2).view(torch.uint8).numpy()
+
+
+def test_enc_e5m2_matches_torch_in_range(orc):
+    """E5M2 (fmt 1): torch's round-to-nearest-even cast on every midpoint, midpoint +- 1 ulp and
+    random values below 61440 (from there torch gives Inf, the oracle saturates to 57344)."""
+    pos = np.arange(0x7C, dtype=np.uint8)
+    vals = torch.from_numpy(pos).view(torch.float8_e5m2).to(torch.float64).numpy()
+    mids = (vals[:-1] + vals[1:]) / 2
+    mids32 = mids.astype(np.float32)
+    assert np.array_equal(mids32.astype(np.float64), mids)
+    up = np.nextafter(mids32, np.float32(np.inf))
+    dn = np.nextafter(mids32, np.float32(-np.inf))
+    g = np.random.Generator(np.random.PCG64(17))
+    rnd = (g.random(20000) * 61439.0).astype(np.float32)
+    tiny = (g.random(5000) * 2.0 ** -14).astype(np.float32)
+    allv = np.concatenate([mids32, up, dn, rnd, tiny, vals.astype(np.float32), [np.float32(61439.99)]])
+    allv = np.concatenate([allv, -allv])
+    got = orc.enc_elem(1, allv.astype(np.float64))
+    assert np.array_equal(got, torch_enc_e5m2(allv))
+
+
+def test_enc_e5m2_saturates_and_keeps_sign(orc):
+    big = np.array([61440.0, 65536.0, 1e6, 3e38, 1e300])
+    assert np.all(orc.enc_elem(1, big) == 0x7B) and np.all(orc.enc_elem(1, -big) == 0xFB)   # +-57344
+    assert orc.enc_elem(1, [-0.0])[0] == 0x80
+    assert orc.enc_elem(1, [2.0 ** -17])[0] == 0x00       # tie between 0 and 2^-16: even code 0
+    assert orc.enc_elem(1, [-2.0 ** -16])[0] == 0x81
+
+
 def test_enc_e4m3_saturates_and_keeps_sign(orc):
     big = np.array([464.0001, 480.0, 511.9, 512.0, 1e6, 3e38])
     assert np.all(orc.enc_elem(0, big) == 0x7E)
@@ -98,7 +131,7 @@ def test_floor_log2_defining_inequality(orc):
         assert math.ldexp(1.0, j) <= a < math.ldexp(1.0, j + 1)
 
 
-@pytest.mark.parametrize("fmt,emax", [(0, 8), (4, 2)])
+@pytest.mark.parametrize("fmt,emax", [(0, 8), (1, 15), (4, 2)])
 def test_scale_rule_closed_cases(orc, fmt, emax):
     for j in range(-60, 60):
         p = math.ldexp(1.0, j)
@@ -129,6 +162,30 @@ def test_mx_quantize_e4m3_vs_torch(orc):
             ref = torch_enc_e4m3(v)
             sat = np.abs(v) > 464
             ref[sat] = np.where(v[sat] < 0, 0xFE, 0x7E)
+            assert np.array_equal(codes[r, 32 * b:32 * b + 32], ref)
+
+
+def test_mx_quantize_e5m2_vs_torch(orc):
+    rows, cols = 64, 512
+    x = synth.normal((rows, cols), 1.0, 1001)
+    x[3, :32] = 0.0
+    x[4, 32:64] *= 1e-30
+    x[5, 64:96] *= 1e20
+    codes, scales = orc.mx_quantize(1, x)
+    for r in range(rows):
+        for b in range(cols // 32):
+            blk = x[r, 32 * b:32 * b + 32].astype(np.float64)
+            amax = np.max(np.abs(blk))
+            E = int(scales[r, b])
+            if amax == 0:
+                assert E == 0
+            else:
+                j = E - 127 + 15
+                assert math.ldexp(1.0, j) <= amax < math.ldexp(1.0, j + 1)
+            v = (blk * math.ldexp(1.0, 127 - E)).astype(np.float32)
+            ref = torch_enc_e5m2(v)
+            sat = np.abs(v) >= 61440
+            ref[sat] = np.where(v[sat] < 0, 0xFB, 0x7B)
             assert np.array_equal(codes[r, 32 * b:32 * b + 32], ref)
 
 
