@@ -4,8 +4,8 @@ Prints ONE JSON line. The headline step is one MXFP8 GEMM of the prefill shape M
 K=4096, N=14336 (E4M3 data, E8M0 scales per 32 along K, fp32 accumulation, fp16 C): `value` is
 its throughput in TFLOP/s (2*M*N*K per step over the HIP-event time of the timed steps, inputs
 already resident in HBM). The other workloads of the path are measured in the same run and
-reported under "detail": the MXFP4 GEMM (M=4096, N=8192, K=8192), the mixed E4M3 x E2M1 GEMM at the
-prefill shape (against the E4M3 peak), the fp16 GEMM (4096^3), the
+reported under "detail": the MXFP4 GEMM (M=4096, N=8192, K=8192), the mixed E4M3 x E2M1 GEMM and
+the E5M2 x E5M2 GEMM at the prefill shape (against the fp8 peak), the fp16 GEMM (4096^3), the
 small MXFP8 GEMM (128x256x128, a latency figure), the int8/int4 dequant matvec (M=1 and M=8,
 K=4096, N=14336; GB/s of algorithmic bytes), the same int8/int4-weight product at M=128 (N=12288)
 and M=64 (N=4096) with K=4096 (TFLOP/s against the fp16 peak) and the GPU pack/unpack codecs.
@@ -179,6 +179,18 @@ def main():
         detail["mixed_e4m3_x_e2m1_gemm_2048x14336x4096"] = {"ms": t, "tflops": tf, "frac_peak": tf / PEAK["mxfp8"],
                                                             "tile": api.mxgemm_plan_info(pm)}
         del sa, sb, msets, Cm
+
+    # ---------------- E5M2 x E5M2 at the prefill shape -------------------------------------------------
+    if want("e5m2_prefill"):
+        log("timing E5M2 GEMM")
+        s5, _, _ = mx_operands(api.MX_E5M2, M, N, K, synth.MXFP8_PREFILL, 0.02, 3)
+        p5 = api.mxgemm_create(M, N, K, api.MX_E5M2, api.MX_E5M2)
+        C5 = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(3)]
+        t = timed(lambda i: api.mxgemm_run(p5, *s5[i % 3], C5[i % 3], stream), args.steps, args.warmup)
+        tf = flops / (t * 1e-3) / 1e12
+        detail["mxfp8_e5m2_gemm_2048x14336x4096"] = {"ms": t, "tflops": tf, "frac_peak": tf / PEAK["mxfp8"],
+                                                     "tile": api.mxgemm_plan_info(p5)}
+        del s5, C5
 
     # ---------------- fp16 GEMM ----------------------------------------------------------------
     if want("f16_square"):

@@ -82,9 +82,10 @@ bool ring_ok(int kind, int N, int K, int tile) {
 int choose_tile(int kind, int M, int N, int K) {
   if (const char* env = std::getenv("MXGEMM_TILE")) {
     int t = std::atoi(env);
-    if (t >= 0 && t < kNumTiles) return kind >= 3 ? (t == kRingTile224 ? t : kRingTile) : t;
+    // pairs other than the three plain ones run on the ring only (256x224 for E4M3 / E2M1 mixes)
+    if (t >= 0 && t < kNumTiles) return kind >= 3 ? (t == kRingTile224 && kind <= 4 ? t : kRingTile) : t;
   }
-  if (kind >= 3) return kRingTile;  // mixed pairs: the ring kernel only
+  if (kind >= 3) return kRingTile;  // mixed and E5M2 pairs: the ring kernel only
   int best = 0;
   double best_cost = 1e300;
   for (int t = 0; t < kNumTiles; t++) {
@@ -130,11 +131,16 @@ int mxgemm_create(mxgemm_t* out, int M, int N, int K, int fa, int fb, unsigned f
   else if (fa == MX_F16 && fb == MX_F16) kind = 2;
   else if (fa == MX_E4M3 && fb == MX_E2M1) kind = 3;
   else if (fa == MX_E2M1 && fb == MX_E4M3) kind = 4;
+  else if (fa == MX_E5M2 && fb == MX_E5M2) kind = 5;
+  else if (fa == MX_E4M3 && fb == MX_E5M2) kind = 6;
+  else if (fa == MX_E5M2 && fb == MX_E4M3) kind = 7;
+  else if (fa == MX_E5M2 && fb == MX_E2M1) kind = 8;
+  else if (fa == MX_E2M1 && fb == MX_E5M2) kind = 9;
   else return MX_ERR_FORMAT;
   if (M < 1 || N < 1 || K < 32 || M > MX_MAX_DIM || N > MX_MAX_DIM || K > MX_MAX_DIM) return MX_ERR_SHAPE;
   if (kind != 2 && K % 32) return MX_ERR_SHAPE;
   if (kind == 2 && (K % 8 || N % 8)) return MX_ERR_SHAPE;
-  if (kind >= 3 && (K % 512 || N % 4)) return MX_ERR_SHAPE;  // mixed pairs run on the ring kernel only
+  if (kind >= 3 && (K % 512 || N % 4)) return MX_ERR_SHAPE;  // mixed and E5M2 pairs: the ring kernel only
   mxgemm_plan* p = new (std::nothrow) mxgemm_plan{M, N, K, fa, fb, kind, choose_tile(kind, M, N, K), flags};
   if (!p) return MX_ERR_NOMEM;
   *out = p;

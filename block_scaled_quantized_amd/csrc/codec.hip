@@ -3,7 +3,7 @@
 //
 // MX pack: 8 lanes own one 32-element block (4 elements each, one 16-byte load per lane); the
 // block amax and the non-finite flag are reduced over those 8 lanes with xor shuffles; every lane
-// then encodes its 4 elements into one 32-bit (E4M3) or 16-bit (E2M1) store. A wave covers eight
+// then encodes its 4 elements into one 32-bit (E4M3, E5M2) or 16-bit (E2M1) store. A wave covers eight
 // consecutive blocks, i.e. 1 KiB of contiguous fp32 input.
 #include "quant_rules.h"
 
@@ -13,7 +13,8 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void pack_mx_kernel(bool fp8, const float* __restrict__ src,
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void pack_mx_kernel(const float* __restrict__ src,
                                                            int64_t nblocks, int64_t blocks_per_row,
                                                            uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ scales) {
@@ -36,23 +37,23 @@ __global__ __launch_bounds__(kThreads) void pack_mx_kernel(bool fp8, const float
       nonfinite |= (uint32_t)__shfl_xor((int)nonfinite, off, 8);
     }
     int t;
-    const uint32_t E = mx_block_scale(amax, nonfinite != 0u, fp8, &t);
+    const uint32_t E = mx_block_scale(amax, nonfinite != 0u, FMT, &t);
     if (sub == 0) {
       const int64_t r = blk / blocks_per_row, b = blk % blocks_per_row;
       scales[r * blocks_per_row + b] = (uint8_t)E;
     }
-    if (fp8) {
+    if constexpr (is_byte_fmt(FMT)) {
       uint32_t w = 0u;
       if (!nonfinite) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) w |= enc_elem_scaled(true, x[i], t) << (8 * i);
+        for (int i = 0; i < 4; i++) w |= enc_elem_fmt(FMT, x[i], t) << (8 * i);
       }
       reinterpret_cast<uint32_t*>(codes)[blk * 8 + sub] = w;
     } else {
       uint32_t w = 0u;
       if (!nonfinite) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) w |= enc_elem_scaled(false, x[i], t) << (4 * i);
+        for (int i = 0; i < 4; i++) w |= enc_elem_fmt(FMT, x[i], t) << (4 * i);
       }
       reinterpret_cast<uint16_t*>(codes)[blk * 8 + sub] = (uint16_t)w;
     }
@@ -94,17 +95,19 @@ __global__ __launch_bounds__(kThreads) void pack_int_kernel(bool i8, const float
 }
 
 // MX unpack: one thread per 4 consecutive elements of a row (cols % 32 == 0).
-__global__ __launch_bounds__(kThreads) void unpack_mx_kernel(bool fp8, const uint8_t* __restrict__ codes,
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void unpack_mx_kernel(const uint8_t* __restrict__ codes,
                                                              const uint8_t* __restrict__ scales, int64_t nquads,
                                                              int64_t cols, float* __restrict__ out) {
   for (int64_t qd = (int64_t)blockIdx.x * kThreads + threadIdx.x; qd < nquads; qd += (int64_t)gridDim.x * kThreads) {
     const int64_t e0 = qd * 4, r = e0 / cols, c = e0 % cols;
     const float s = dec_e8m0(scales[r * (cols / 32) + c / 32]);
-    uint32_t w = fp8 ? reinterpret_cast<const uint32_t*>(codes)[qd] : reinterpret_cast<const uint16_t*>(codes)[qd];
+    uint32_t w = is_byte_fmt(FMT) ? reinterpret_cast<const uint32_t*>(codes)[qd]
+                                  : reinterpret_cast<const uint16_t*>(codes)[qd];
     float4 o;
-    if (fp8) {
-      o = make_float4(dec_e4m3(w & 255u) * s, dec_e4m3((w >> 8) & 255u) * s, dec_e4m3((w >> 16) & 255u) * s,
-                      dec_e4m3(w >> 24) * s);
+    if constexpr (is_byte_fmt(FMT)) {
+      o = make_float4(dec_elem_fmt(FMT, w & 255u) * s, dec_elem_fmt(FMT, (w >> 8) & 255u) * s,
+                      dec_elem_fmt(FMT, (w >> 16) & 255u) * s, dec_elem_fmt(FMT, w >> 24) * s);
     } else {
       o = make_float4(dec_e2m1(w & 15u) * s, dec_e2m1((w >> 4) & 15u) * s, dec_e2m1((w >> 8) & 15u) * s,
                       dec_e2m1((w >> 12) & 15u) * s);
@@ -138,12 +141,18 @@ extern "C" int mx_pack_run(int f, const float* src, int rows, int cols, void* co
   if (rows < 1 || cols < 1 || rows > MX_MAX_DIM || cols > MX_MAX_DIM) return MX_ERR_SHAPE;
   if (!aligned16(src) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGN;
   hipStream_t st = as_stream(stream);
-  if (f == MX_E4M3 || f == MX_E2M1) {
+  if (f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1) {
     if (cols % 32) return MX_ERR_SHAPE;
     if (int a = check_arch()) return a;
     const int64_t nblocks = (int64_t)rows * (cols / 32);
-    hipLaunchKernelGGL(pack_mx_kernel, dim3(grid_for(nblocks, kThreads / 8)), dim3(kThreads), 0, st,
-                       f == MX_E4M3, src, nblocks, (int64_t)(cols / 32), (uint8_t*)codes, (uint8_t*)scales);
+    const dim3 grid(grid_for(nblocks, kThreads / 8)), block(kThreads);
+    const int64_t bpr = cols / 32;
+    if (f == MX_E4M3)
+      hipLaunchKernelGGL(pack_mx_kernel<MX_E4M3>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
+    else if (f == MX_E5M2)
+      hipLaunchKernelGGL(pack_mx_kernel<MX_E5M2>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
+    else
+      hipLaunchKernelGGL(pack_mx_kernel<MX_E2M1>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
     return launch_status();
   }
   if (f == MX_INT8 || f == MX_INT4) {
@@ -163,12 +172,18 @@ extern "C" int mx_unpack_run(int f, const void* codes, const void* scales, int r
   if (rows < 1 || cols < 1 || rows > MX_MAX_DIM || cols > MX_MAX_DIM) return MX_ERR_SHAPE;
   if (!aligned16(codes) || !aligned16(scales) || !aligned16(out)) return MX_ERR_ALIGN;
   hipStream_t st = as_stream(stream);
-  if (f == MX_E4M3 || f == MX_E2M1) {
+  if (f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1) {
     if (cols % 32) return MX_ERR_SHAPE;
     if (int a = check_arch()) return a;
     const int64_t nquads = (int64_t)rows * cols / 4;
-    hipLaunchKernelGGL(unpack_mx_kernel, dim3(grid_for(nquads, kThreads)), dim3(kThreads), 0, st, f == MX_E4M3,
-                       (const uint8_t*)codes, (const uint8_t*)scales, nquads, (int64_t)cols, out);
+    const dim3 grid(grid_for(nquads, kThreads)), block(kThreads);
+    const uint8_t *cd = (const uint8_t*)codes, *sc = (const uint8_t*)scales;
+    if (f == MX_E4M3)
+      hipLaunchKernelGGL(unpack_mx_kernel<MX_E4M3>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
+    else if (f == MX_E5M2)
+      hipLaunchKernelGGL(unpack_mx_kernel<MX_E5M2>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
+    else
+      hipLaunchKernelGGL(unpack_mx_kernel<MX_E2M1>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
     return launch_status();
   }
   if (f == MX_INT8 || f == MX_INT4) {

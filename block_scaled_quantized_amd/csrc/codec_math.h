@@ -3,8 +3,11 @@
 // are bit-identical by construction).
 //
 // Element formats (named by "Optimize custom machine learning operations with Metal tensors",
-// quantized data types and MXFP8 tensor type; bit layouts from the OCP Microscaling v1.0 spec):
+// quantized data types and MXFP8 tensor type, and by the TensorOps notes' dtype matrix: fp8, fp4,
+// MX scaling formats; bit layouts from the OCP Microscaling v1.0 spec):
 //   E4M3 "FN": s.eeee.mmm, bias 7, exponent 0 subnormal (m * 2^-9), s.1111.111 NaN, max 448.
+//   E5M2:      s.eeeee.mm, bias 15, exponent 0 subnormal (m * 2^-16), s.11111.00 Inf,
+//              s.11111.mm (m != 0) NaN, max 57344.
 //   E2M1:      s.ee.m, bias 1, exponent 0 subnormal (m * 0.5), max 6, no NaN.
 //   E8M0:      2^(e-127), 0xFF = NaN.
 // Encoding is round-to-nearest, ties to the even code, with saturation to the largest finite
@@ -52,6 +55,21 @@ MX_HD uint32_t e4m3_mag(uint32_t a, int t) {
   return rne_shift(sig, 14 - ev);                // subnormal E4M3: multiples of 2^-9 (0..8)
 }
 
+// E5M2 magnitude code (0..0x7B) of |x| * 2^t, a = bits of |x| (finite).
+MX_HD uint32_t e5m2_mag(uint32_t a, int t) {
+  if (a == 0u) return 0u;
+  int ev = ilog2_bits(a) + t;
+  uint32_t sig = norm_sig(a);
+  if (ev > 15 || (ev == 15 && sig >= 0xE00000u)) return 0x7Bu;  // >= 57344: saturate
+  if (ev >= -14) {                               // normal E5M2: 2 fraction bits
+    uint32_t r = rne_shift(sig, 21);
+    int e = ev;
+    if (r == 8u) { r = 4u; e++; }
+    return ((uint32_t)(e + 15) << 2) | (r - 4u);
+  }
+  return rne_shift(sig, 7 - ev);                 // subnormal E5M2: multiples of 2^-16 (0..4)
+}
+
 // E2M1 magnitude code (0..7) of |x| * 2^t.
 MX_HD uint32_t e2m1_mag(uint32_t a, int t) {
   if (a == 0u) return 0u;
@@ -67,10 +85,15 @@ MX_HD uint32_t e2m1_mag(uint32_t a, int t) {
   return rne_shift(sig, 22 - ev);                // subnormal E2M1: multiples of 0.5 (0..2)
 }
 
-// Element code of x * 2^t with the sign of x kept (E4M3 when fp8, else E2M1).
-MX_HD uint32_t enc_elem_scaled(bool fp8, float x, int t) {
+// Element formats by their mx_format codes: E4M3 = 0, E5M2 = 1, E2M1 = 4.
+constexpr bool is_byte_fmt(int fmt) { return fmt == MX_E4M3 || fmt == MX_E5M2; }
+
+// Element code of x * 2^t with the sign of x kept, in format fmt.
+MX_HD uint32_t enc_elem_fmt(int fmt, float x, int t) {
   uint32_t u = fbits(x), a = u & 0x7FFFFFFFu, s = u >> 31;
-  return fp8 ? ((s << 7) | e4m3_mag(a, t)) : ((s << 3) | e2m1_mag(a, t));
+  if (fmt == MX_E4M3) return (s << 7) | e4m3_mag(a, t);
+  if (fmt == MX_E5M2) return (s << 7) | e5m2_mag(a, t);
+  return (s << 3) | e2m1_mag(a, t);
 }
 
 // E8M0 scale code of a block from the bit pattern of its amax (finite, >= 0):
@@ -95,10 +118,24 @@ MX_HD float dec_e4m3(uint32_t b) {
   return bitsf(s | fbits((float)m * 0.001953125f));  // m * 2^-9, exact
 }
 
+MX_HD float dec_e5m2(uint32_t b) {
+  uint32_t s = (b & 0x80u) << 24, e = (b >> 2) & 31u, m = b & 3u;
+  if (e == 31u) return bitsf(s | (m ? 0x7FC00000u : 0x7F800000u));
+  if (e) return bitsf(s | ((e + 112u) << 23) | (m << 21));
+  return bitsf(s | fbits((float)m * 1.52587890625e-05f));  // m * 2^-16, exact
+}
+
 MX_HD float dec_e2m1(uint32_t n) {
   uint32_t s = (n & 8u) << 28, e = (n >> 1) & 3u, m = n & 1u;
   if (e) return bitsf(s | ((e + 126u) << 23) | (m << 22));
   return bitsf(s | (m ? 0x3F000000u : 0u));          // 0 or 0.5
+}
+
+// Element decoder by format (byte code for E4M3 / E5M2, nibble for E2M1).
+MX_HD float dec_elem_fmt(int fmt, uint32_t c) {
+  if (fmt == MX_E4M3) return dec_e4m3(c);
+  if (fmt == MX_E5M2) return dec_e5m2(c);
+  return dec_e2m1(c & 15u);
 }
 
 MX_HD float dec_f16(uint16_t h) {

@@ -9,11 +9,12 @@ using namespace mx;
 
 namespace {
 
-bool is_mx(int f) { return f == MX_E4M3 || f == MX_E2M1; }
+bool is_mx(int f) { return f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1; }
 bool is_int(int f) { return f == MX_INT8 || f == MX_INT4; }
 
-int pack_mx(bool fp8, const float* src, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales) {
-  const int64_t rb = fp8 ? cols : cols / 2, nb = cols / 32;
+int pack_mx(int fmt, const float* src, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales) {
+  const bool byte = is_byte_fmt(fmt);
+  const int64_t rb = byte ? cols : cols / 2, nb = cols / 32;
   for (int64_t r = 0; r < rows; r++)
     for (int64_t b = 0; b < nb; b++) {
       const float* x = src + r * cols + 32 * b;
@@ -25,14 +26,14 @@ int pack_mx(bool fp8, const float* src, int64_t rows, int64_t cols, uint8_t* cod
         amax = a > amax ? a : amax;  // magnitude order equals bit order for finite floats
       }
       int t;
-      scales[r * nb + b] = (uint8_t)mx_block_scale(amax, nonfinite, fp8, &t);
-      uint8_t* out = codes + r * rb + (fp8 ? 32 * b : 16 * b);
-      if (nonfinite) { memset(out, 0, fp8 ? 32 : 16); continue; }
-      if (fp8) {
-        for (int i = 0; i < 32; i++) out[i] = (uint8_t)enc_elem_scaled(true, x[i], t);
+      scales[r * nb + b] = (uint8_t)mx_block_scale(amax, nonfinite, fmt, &t);
+      uint8_t* out = codes + r * rb + (byte ? 32 * b : 16 * b);
+      if (nonfinite) { memset(out, 0, byte ? 32 : 16); continue; }
+      if (byte) {
+        for (int i = 0; i < 32; i++) out[i] = (uint8_t)enc_elem_fmt(fmt, x[i], t);
       } else {
         for (int i = 0; i < 16; i++)
-          out[i] = (uint8_t)(enc_elem_scaled(false, x[2 * i], t) | (enc_elem_scaled(false, x[2 * i + 1], t) << 4));
+          out[i] = (uint8_t)(enc_elem_fmt(fmt, x[2 * i], t) | (enc_elem_fmt(fmt, x[2 * i + 1], t) << 4));
       }
     }
   return MX_OK;
@@ -68,7 +69,7 @@ extern "C" int mx_pack_host(int f, const float* src, int64_t rows, int64_t cols,
   if (rows < 1 || cols < 1 || rows > MX_MAX_DIM || cols > MX_MAX_DIM) return MX_ERR_SHAPE;
   if (is_mx(f)) {
     if (cols % 32) return MX_ERR_SHAPE;
-    return pack_mx(f == MX_E4M3, src, rows, cols, (uint8_t*)codes, (uint8_t*)scales);
+    return pack_mx(f, src, rows, cols, (uint8_t*)codes, (uint8_t*)scales);
   }
   if (is_int(f)) {
     if (rows % 32 || (f == MX_INT4 && cols % 2)) return MX_ERR_SHAPE;
@@ -84,12 +85,12 @@ extern "C" int mx_unpack_host(int f, const void* codes_v, const void* scales_v, 
   if (is_mx(f)) {
     if (cols % 32) return MX_ERR_SHAPE;
     const uint8_t* sc = (const uint8_t*)scales_v;
-    const bool fp8 = f == MX_E4M3;
-    const int64_t rb = fp8 ? cols : cols / 2;
+    const bool byte = is_byte_fmt(f);
+    const int64_t rb = byte ? cols : cols / 2;
     for (int64_t r = 0; r < rows; r++)
       for (int64_t c = 0; c < cols; c++) {
-        uint32_t code = fp8 ? codes[r * rb + c] : (codes[r * rb + c / 2] >> (4 * (c % 2))) & 0xFu;
-        float v = fp8 ? dec_e4m3(code) : dec_e2m1(code);
+        uint32_t code = byte ? codes[r * rb + c] : (codes[r * rb + c / 2] >> (4 * (c % 2))) & 0xFu;
+        float v = dec_elem_fmt(f, code);
         out[r * cols + c] = v * dec_e8m0(sc[r * (cols / 32) + c / 32]);
       }
     return MX_OK;
@@ -109,14 +110,14 @@ extern "C" int mx_unpack_host(int f, const void* codes_v, const void* scales_v, 
 }
 
 extern "C" uint8_t mx_encode_host(int f, float v) {
-  if (f == MX_E4M3) return (uint8_t)enc_elem_scaled(true, v, 0);
-  if (f == MX_E2M1) return (uint8_t)enc_elem_scaled(false, v, 0);
+  if (is_mx(f)) return (uint8_t)enc_elem_fmt(f, v, 0);
   return 0;
 }
 
 extern "C" float mx_decode_host(int f, uint8_t code) {
   switch (f) {
     case MX_E4M3: return dec_e4m3(code);
+    case MX_E5M2: return dec_e5m2(code);
     case MX_E2M1: return dec_e2m1(code & 0xFu);
     case MX_INT8: return (float)(int8_t)code;
     case MX_INT4: return (float)((int)((code & 0xFu) ^ 8u) - 8);

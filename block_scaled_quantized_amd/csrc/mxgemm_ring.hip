@@ -100,6 +100,14 @@ struct RingFmt {
   static_assert(NI_A % 4 == 0 && NI_B % 4 == 0 && DPS <= MAX_DPS, "copies");
 };
 
+// MFMA format codes of the two operands (the instruction's cbsz for its first operand, our B, and
+// blgp for the second, our A): 4 for E2M1; for a byte operand 0 (E4M3) or 1 (E5M2) as given by
+// F8A / F8B. E5M2 has E4M3's storage and layout, so only these codes change.
+template <int KIND, int F8A, int F8B>
+struct RingMfma {
+  enum : int { CBSZ = RingFmt<KIND>::B4 ? 4 : F8B, BLGP = RingFmt<KIND>::A4 ? 4 : F8A };
+};
+
 // Copies of a stage for a tile width: NI_A for A, then enough 1 KB copies for the tile's B rows,
 // rounded up so that the 4 waves issue the same number (the extra ones fill unused slot bytes with
 // zeros from an empty resource): DPS per wave.
@@ -296,12 +304,13 @@ MX_DEV void issue_scales(const Ctx& c, char* sg, int g) {
 // the next stage's first B tile needs all of them, then the B fragments in the order their tiles
 // come. The next-stage reads are unconditional (after the last stage they fetch unused bytes): a
 // conditional overwrite would keep the old contents alive through the stage.
-template <int KIND, class T, int S8>
+template <int KIND, class T, int S8, int F8A, int F8B>
 MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], const v8i (&cb)[T::FB],
                        v8i (&na)[T::FA], v8i (&nb)[T::FB], const char* slot_nxt, char* slot_fill,
                        Scales<KIND, T>& sc, RawScales<KIND, T>& raw, v16f (&acc)[T::FB][T::FA]) {
   using F = RingFmt<KIND>;
   using CP = RingCopies<KIND, T>;
+  using MF = RingMfma<KIND, F8A, F8B>;
   const int t = GROUP * g + S8;
   // Copies queued after this wave's copies of stage t+1 (issued at stage t-2): those of stage t+2
   // (at stage t-1) and, at S8 == 3, the scale group issued at S8 == 2 ahead of them. From S8 == 4
@@ -340,7 +349,7 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
                 bk, ak, acc[i][j], 4, 4, (U0 + 1) % 4, sc.b[i][(U0 + 1) / 4], (U0 + 1) % 4, sc.a[j][(U0 + 1) / 4]);
         } else {
           // E4M3 x E4M3 or a mixed pair: one K-step; the E2M1 side's fragment is its low half
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[i], ca[j], acc[i][j], F::CBSZ, F::BLGP, U0 % 4,
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[i], ca[j], acc[i][j], MF::CBSZ, MF::BLGP, U0 % 4,
                                                                        sc.b[i][U0 / 4], U0 % 4, sc.a[j][U0 / 4]);
         }
       }
@@ -375,7 +384,7 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
   }
 }
 
-template <int KIND, int WAVES_M, int BN_>
+template <int KIND, int WAVES_M, int BN_, int F8A, int F8B>
 __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   using F = RingFmt<KIND>;
   using T = RingTile<WAVES_M, BN_>;
@@ -509,14 +518,14 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
 
   // Stage t uses slot t%4 (t = 8g + s: slot s%4); even stages compute from x*, odd from y*.
   for (int g = 0; g < ngroups; g++) {
-    ring_stage<KIND, T, 0>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, acc);
-    ring_stage<KIND, T, 1>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, acc);
-    ring_stage<KIND, T, 2>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, acc);
-    ring_stage<KIND, T, 3>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
-    ring_stage<KIND, T, 4>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, acc);
-    ring_stage<KIND, T, 5>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, acc);
-    ring_stage<KIND, T, 6>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, acc);
-    ring_stage<KIND, T, 7>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
+    ring_stage<KIND, T, 0, F8A, F8B>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, acc);
+    ring_stage<KIND, T, 1, F8A, F8B>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, acc);
+    ring_stage<KIND, T, 2, F8A, F8B>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, acc);
+    ring_stage<KIND, T, 3, F8A, F8B>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
+    ring_stage<KIND, T, 4, F8A, F8B>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, acc);
+    ring_stage<KIND, T, 5, F8A, F8B>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, acc);
+    ring_stage<KIND, T, 6, F8A, F8B>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, acc);
+    ring_stage<KIND, T, 7, F8A, F8B>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
   }
 
   // The last stages queued copies of stage nst-1 into free slots: let them land, and let every
@@ -591,9 +600,10 @@ namespace mx {
 // Ring kernels. kind 0: E4M3 x E4M3, 1: E2M1 x E2M1, 2: E4M3 A x E2M1 B, 3: E2M1 A x E4M3 B,
 // 4: fp16 x fp16 (B K x N). Requires N % 4 == 0 and K % 512 == 0 (K % 1024 == 0 for kind 1); for
 // kind 4 N % 256 == 0, K % 256 == 0 and 2*K*N < 2^31, bn = 256 only. Checked by the caller.
-// bn = 256, 224 or 192 (192: kinds 0 and 1).
-int gemm_ring_launch(int kind, int bn, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
-                     int N, int K, bool relu, hipStream_t stream) {
+// bn = 256, 224 or 192 (192: kinds 0 and 1). e5a / e5b: the byte-format A / B operand is E5M2
+// instead of E4M3 (kinds 0, 2 (A) and 3 (B); 256 x 256 tiles only).
+int gemm_ring_launch(int kind, int bn, bool e5a, bool e5b, const void* A, const void* SA, const void* B,
+                     const void* SB, void* C, int M, int N, int K, bool relu, hipStream_t stream) {
   Args a{};
   a.A = (const uint8_t*)A;
   a.SA = (const uint8_t*)SA;
@@ -607,28 +617,36 @@ int gemm_ring_launch(int kind, int bn, const void* A, const void* SA, const void
   a.tiles_m = (M + BM - 1) / BM;
   const int tiles = a.tiles_m * ((N + bn - 1) / bn);
   const dim3 grid((unsigned)tiles), block(256);
-#define MX_RING(KD, WM, BNT) hipLaunchKernelGGL((gemm_ring_kernel<KD, WM, BNT>), grid, block, 0, stream, a)
+#define MX_RING(KD, WM, BNT, FA8, FB8) \
+  hipLaunchKernelGGL((gemm_ring_kernel<KD, WM, BNT, FA8, FB8>), grid, block, 0, stream, a)
   if (bn == 224) {
     switch (kind) {
-      case 0: MX_RING(0, 4, 224); break;
-      case 1: MX_RING(1, 4, 224); break;
-      case 2: MX_RING(2, 4, 224); break;
-      case 3: MX_RING(3, 4, 224); break;
+      case 0: MX_RING(0, 4, 224, 0, 0); break;
+      case 1: MX_RING(1, 4, 224, 0, 0); break;
+      case 2: MX_RING(2, 4, 224, 0, 0); break;
+      case 3: MX_RING(3, 4, 224, 0, 0); break;
       default: return MX_ERR_FORMAT;
     }
   } else if (bn == 192) {
     switch (kind) {
-      case 0: MX_RING(0, 2, 192); break;
-      case 1: MX_RING(1, 2, 192); break;
+      case 0: MX_RING(0, 2, 192, 0, 0); break;
+      case 1: MX_RING(1, 2, 192, 0, 0); break;
       default: return MX_ERR_FORMAT;
     }
+  } else if (e5a || e5b) {  // E5M2 operands: 256 x 256 tiles
+    if (kind == 0 && e5a && e5b) MX_RING(0, 2, 256, 1, 1);
+    else if (kind == 0 && e5b) MX_RING(0, 2, 256, 0, 1);
+    else if (kind == 0) MX_RING(0, 2, 256, 1, 0);
+    else if (kind == 2 && e5a) MX_RING(2, 2, 256, 1, 0);
+    else if (kind == 3 && e5b) MX_RING(3, 2, 256, 0, 1);
+    else return MX_ERR_FORMAT;
   } else {
     switch (kind) {
-      case 0: MX_RING(0, 2, 256); break;
-      case 1: MX_RING(1, 2, 256); break;
-      case 2: MX_RING(2, 2, 256); break;
-      case 3: MX_RING(3, 2, 256); break;
-      default: MX_RING(4, 2, 256); break;
+      case 0: MX_RING(0, 2, 256, 0, 0); break;
+      case 1: MX_RING(1, 2, 256, 0, 0); break;
+      case 2: MX_RING(2, 2, 256, 0, 0); break;
+      case 3: MX_RING(3, 2, 256, 0, 0); break;
+      default: MX_RING(4, 2, 256, 0, 0); break;
     }
   }
 #undef MX_RING

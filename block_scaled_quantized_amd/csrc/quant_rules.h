@@ -3,7 +3,8 @@
 //
 // MX blocks (32 consecutive elements along K share one E8M0 scale: "TensorOps ... notes",
 // section "Scale planes"; WWDC26 session 330 summary, auxiliary scale plane with blockFactors
-// {32,1}): E = clamp(floor(log2 amax) - emax + 127, 0, 254), emax = 8 for E4M3 and 2 for E2M1,
+// {32,1}): E = clamp(floor(log2 amax) - emax + 127, 0, 254), emax = 8 for E4M3, 15 for E5M2 and 2
+// for E2M1 (the exponent of the format's largest element),
 // elements encoded as x * 2^(127-E). A block holding Inf/NaN gets E = 0xFF and zero codes.
 //
 // Integer weight blocks (32 rows of one column share one fp16 scale: the per-block fp16 scales of
@@ -30,13 +31,13 @@ MX_HD float rint_even(float x) {
 #endif
 }
 
-constexpr int emax_of(bool fp8) { return fp8 ? 8 : 2; }
+constexpr int emax_of(int fmt) { return fmt == MX_E4M3 ? 8 : (fmt == MX_E5M2 ? 15 : 2); }
 
-// Scale code and exponent offset t = 127 - E of one MX block from its amax bit pattern and a
-// non-finite flag. Returns the scale code; *t receives the offset.
-MX_HD uint32_t mx_block_scale(uint32_t amax_bits, bool nonfinite, bool fp8, int* t) {
+// Scale code and exponent offset t = 127 - E of one MX block (element format fmt) from its amax
+// bit pattern and a non-finite flag. Returns the scale code; *t receives the offset.
+MX_HD uint32_t mx_block_scale(uint32_t amax_bits, bool nonfinite, int fmt, int* t) {
   if (nonfinite) { *t = 0; return 0xFFu; }
-  uint32_t E = scale_code(amax_bits, emax_of(fp8));
+  uint32_t E = scale_code(amax_bits, emax_of(fmt));
   *t = 127 - (int)E;
   return E;
 }

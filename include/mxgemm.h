@@ -16,6 +16,8 @@
  *
  * Formats (the pages name the types, the OCP Microscaling v1.0 formats give their bits):
  *  - MX_E4M3: FP8 E4M3 "FN" (bias 7, S.1111.111 = NaN, no Inf, max 448), one byte per element.
+ *  - MX_E5M2: FP8 E5M2 (bias 15, S.11111.00 = Inf, S.11111.xx = NaN, max 57344), one byte per
+ *    element (the pages' fp8 / "MX scaling formats", TensorOps notes, quantized dtype matrix).
  *  - MX_E2M1: FP4 E2M1 (bias 1, +-{0,.5,1,1.5,2,3,4,6}), two elements per byte, the element with
  *    the even index in the low nibble.
  *  - Scales of MX operands: E8M0 bytes, value 2^(e-127), 0xFF = NaN; one scale per 32
@@ -47,7 +49,7 @@ typedef enum {
 } mx_status;
 
 /* MX_E8M0 names the scale format; it is accepted only by mx_decode_host. */
-typedef enum { MX_E4M3 = 0, MX_E2M1 = 4, MX_E8M0 = 8, MX_F16 = 16, MX_INT8 = 32, MX_INT4 = 33 } mx_format;
+typedef enum { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M1 = 4, MX_E8M0 = 8, MX_F16 = 16, MX_INT8 = 32, MX_INT4 = 33 } mx_format;
 
 /* Largest accepted dimension of any matrix (rows or columns). */
 #define MX_MAX_DIM (1 << 20)
@@ -81,7 +83,9 @@ typedef struct mxgemm_plan* mxgemm_t;
  *
  * Supported pairs: (MX_E4M3, MX_E4M3), (MX_E2M1, MX_E2M1), (MX_F16, MX_F16), and the mixed MX pairs
  * (MX_E4M3, MX_E2M1), (MX_E2M1, MX_E4M3) (A and B each in its own format, scales as above; the
- * scaled MFMA takes each operand's format separately). Mixed pairs need K % 512 == 0 and
+ * scaled MFMA takes each operand's format separately), and every pair with an MX_E5M2 operand:
+ * (MX_E5M2, MX_E5M2), (MX_E4M3, MX_E5M2), (MX_E5M2, MX_E4M3), (MX_E5M2, MX_E2M1),
+ * (MX_E2M1, MX_E5M2). All pairs other than the three plain ones need K % 512 == 0 and
  * N % 4 == 0, else MX_ERR_SHAPE.
  * Shape rules: 1 <= M, N <= MX_MAX_DIM; 32 <= K <= MX_MAX_DIM; MX formats need K % 32 == 0;
  * MX_F16 needs K % 8 == 0 and N % 8 == 0.
@@ -95,9 +99,9 @@ int mxgemm_create(mxgemm_t* out, int M, int N, int K, int fa, int fb, unsigned f
  * mxgemm_run -- queue the GEMM of plan p on `stream`.
  *
  * Layouts (all device pointers, 16-byte aligned):
- *   MX:  A  codes [M][K] (E4M3) or [M][K/2] (E2M1), K contiguous;
+ *   MX:  A  codes [M][K] (E4M3, E5M2) or [M][K/2] (E2M1), K contiguous;
  *        SA E8M0 [M][K/32];
- *        B  codes stored K-contiguous, i.e. [N][K] (E4M3) or [N][K/2] (E2M1): the scaled right
+ *        B  codes stored K-contiguous, i.e. [N][K] (E4M3, E5M2) or [N][K/2] (E2M1): the scaled right
  *           operand is the transposed one ("Kernel-phase findings", fact 2);
  *        SB E8M0 [N][K/32];
  *   F16: A binary16 [M][K]; B binary16 [K][N] (row-major K x N); SA = SB = NULL.
@@ -163,12 +167,13 @@ size_t mxmatvec_workspace_size(int M, int N, int K, int fw);
 
 /*
  * mx_pack_run -- quantise fp32 src [rows][cols] on the GPU.
- *  f = MX_E4M3 / MX_E2M1: blocks of 32 along cols. Per block: amax = max|x|; E = clamp(
- *      floor(log2 amax) - emax + 127, 0, 254) with emax = 8 (E4M3) or 2 (E2M1) (amax = 0 gives
- *      E = 0); codes = x * 2^(127-E) rounded to the nearest element value, ties to the even
- *      code, saturated to +-448 / +-6, sign kept (negative values that round to zero give -0).
- *      A block holding Inf or NaN gets E = 0xFF and zero codes. codes: [rows][cols] or
- *      [rows][cols/2]; scales: E8M0 [rows][cols/32]. cols % 32 == 0.
+ *  f = MX_E4M3 / MX_E5M2 / MX_E2M1: blocks of 32 along cols. Per block: amax = max|x|;
+ *      E = clamp(floor(log2 amax) - emax + 127, 0, 254) with emax = 8 (E4M3), 15 (E5M2) or 2
+ *      (E2M1) (amax = 0 gives E = 0); codes = x * 2^(127-E) rounded to the nearest element
+ *      value, ties to the even code, saturated to +-448 / +-57344 / +-6, sign kept (negative
+ *      values that round to zero give -0). A block holding Inf or NaN gets E = 0xFF and zero
+ *      codes. codes: [rows][cols] (E4M3, E5M2) or [rows][cols/2] (E2M1); scales: E8M0
+ *      [rows][cols/32]. cols % 32 == 0.
  *  f = MX_INT8 / MX_INT4: src is a weight W [K=rows][N=cols], blocks of 32 along rows. Per
  *      column and block: s = fp16(amax / qmax) (fp32 division, nearest-even to fp16) with
  *      qmax = 127 or 7; q = clamp(round_half_even(fp32(w / s)), -qmax, qmax), q = 0 where
@@ -192,9 +197,10 @@ int mx_unpack_run(int f, const void* codes, const void* scales, int rows, int co
 int mx_pack_host(int f, const float* src, int64_t rows, int64_t cols, void* codes, void* scales);
 int mx_unpack_host(int f, const void* codes, const void* scales, int64_t rows, int64_t cols, float* out);
 
-/* Single-element encoder/decoder of the host codec. mx_encode_host: f = MX_E4M3 or MX_E2M1,
- * nearest code, ties to even, saturating, sign kept (0 for other f). mx_decode_host: f = MX_E4M3,
- * MX_E2M1 (low nibble), MX_E8M0, MX_INT8 or MX_INT4 (low nibble); NaN for other f. */
+/* Single-element encoder/decoder of the host codec. mx_encode_host: f = MX_E4M3, MX_E5M2 or
+ * MX_E2M1, nearest code, ties to even, saturating, sign kept (0 for other f). mx_decode_host:
+ * f = MX_E4M3, MX_E5M2, MX_E2M1 (low nibble), MX_E8M0, MX_INT8 or MX_INT4 (low nibble); NaN for
+ * other f. */
 uint8_t mx_encode_host(int f, float v);
 float mx_decode_host(int f, uint8_t code);
 

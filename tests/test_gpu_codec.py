@@ -27,13 +27,17 @@ def edge_rows(cols, seed):
     x[10, :32] = np.float32(448.0)
     x[10, 1:32] = mids[np.linspace(0, len(mids) - 1, 31).astype(int)]
     x[12, :32] = -x[10, :32]
+    x[13, :32] = np.float32(57344.0)               # E5M2 block amax 57344 -> scale 2^0: its ties
+    e5 = torch.arange(0x7C, dtype=torch.uint8).view(torch.float8_e5m2).float().numpy()
+    x[13, 1:32] = ((e5[:-1] + e5[1:]) / 2)[np.linspace(0, len(e5) - 2, 31).astype(int)]
+    x[14, :32] = np.float32(60000.0) * np.sign(x[14, :32])   # E5M2 saturation
     x[11, :32] = np.float32(4.0)                   # E2M1 block amax 4 -> scale 2^0
     x[11, 1:16] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25, -1.75, -2.5,
                             -3.5, -5.0, 0.1], np.float32)
     return x.astype(np.float32)
 
 
-@pytest.mark.parametrize("fmt", [0, 4])
+@pytest.mark.parametrize("fmt", [0, 1, 4])
 @pytest.mark.parametrize("case", ["normal1", "normal002", "edges", "prefill_rows"])
 def test_mx_pack_unpack_bitexact(orc, fmt, case):
     api = require_gpu()
@@ -56,15 +60,16 @@ def test_mx_pack_unpack_bitexact(orc, fmt, case):
     assert bitequal_f32(host(out), orc.dequant(fmt, oc, os_, rows, cols))
 
 
-@pytest.mark.parametrize("fmt", [0, 4])
+@pytest.mark.parametrize("fmt", [0, 1, 4])
 def test_mx_unpack_every_code_and_scale(orc, fmt):
     api = require_gpu()
     say(f"mx unpack exhaustive fmt={fmt}")
     # every code byte against every scale byte: 256 rows (one per scale) x 256 or 512 columns
-    cols = 256 if fmt == 0 else 512
+    byte = fmt in (0, 1)
+    cols = 256 if byte else 512
     per_row = np.arange(256, dtype=np.uint8)
-    codes = np.tile(per_row, (256, 1)) if fmt == 0 else np.tile(np.repeat(per_row, 1), (256, 1))
-    codes = np.ascontiguousarray(codes[:, : (cols if fmt == 0 else cols // 2)])
+    codes = np.tile(per_row, (256, 1))
+    codes = np.ascontiguousarray(codes[:, : (cols if byte else cols // 2)])
     scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], cols // 32, axis=1)
     out = empty((256, cols), torch.float32)
     api.mx_unpack_run(fmt, dev(codes), dev(scales), 256, cols, out)

@@ -257,6 +257,48 @@ def test_mx_mixed_pairs(orc, fa, fb, tile, M, N, K):
     assert ok, (ratio, bad)
 
 
+@pytest.mark.parametrize("fa,fb", [(1, 1), (0, 1), (1, 0), (1, 4), (4, 1)])
+@pytest.mark.parametrize("M,N,K", [(300, 520, 512), (257, 260, 1536), (64, 1028, 1024)])
+def test_mx_e5m2_pairs(orc, fa, fb, M, N, K):
+    """Pairs with an E5M2 operand on the ring (the MFMA's bf8 format code), every output: the GPU's
+    E5M2 pack must equal the oracle's, and the product must meet the bound."""
+    api = require_gpu()
+    say(f"mx e5m2 fa={fa} fb={fb} M={M} N={N} K={K}")
+    a_src = synth.normal((M, K), 1.0, 800 + M + K)
+    b_src = synth.normal((N, K), 0.02, 801 + N + K)
+    A, SA = gpu_mx_pack(api, fa, a_src)
+    B, SB = gpu_mx_pack(api, fb, b_src)
+    oA, oSA = orc.mx_quantize(fa, a_src)
+    oB, oSB = orc.mx_quantize(fb, b_src)
+    assert np.array_equal(host(A), oA) and np.array_equal(host(SA), oSA)
+    assert np.array_equal(host(B), oB) and np.array_equal(host(SB), oSB)
+    C = gpu_gemm(api, fa, A, SA, B, SB, M, N, K, fb=fb)
+    ref = orc.mxgemm(fa, fb, oA, oSA, oB, oSB, M, N, K)
+    R = orc.rms_ab(orc.dequant(fa, oA, oSA, M, K), orc.dequant(fb, oB, oSB, N, K).T)
+    ok, ratio, bad = orc.check(C, ref, K, R)
+    assert ok, (ratio, bad)
+
+
+def test_mx_e5m2_unit_scales_exact(orc):
+    """E5M2 x E5M2 at unit scales on codes whose products and sums are exact in fp32: the GPU must
+    equal the oracle (its plain fp8 matmul) after the fp16 rounding, output for output."""
+    api = require_gpu()
+    M, N, K = 256, 512, 1024
+    say("mx e5m2 unit scales exact")
+    g = np.random.Generator(np.random.PCG64(811))
+
+    def codes(shape):   # exponent fields 13..17: values 2^-2 .. 1.75*2^2, signs random
+        return ((g.integers(0, 2, size=shape) << 7) | (g.integers(13, 18, size=shape) << 2)
+                | g.integers(0, 4, size=shape)).astype(np.uint8)
+    A, B = codes((M, K)), codes((N, K))
+    SA = np.full((M, K // 32), 127, np.uint8)
+    SB = np.full((N, K // 32), 127, np.uint8)
+    C = gpu_gemm(api, 1, dev(A), dev(SA), dev(B), dev(SB), M, N, K)
+    ref = orc.mxgemm(1, 1, A, SA, B, SB, M, N, K)
+    assert np.abs(ref).max() < 60000
+    assert np.array_equal(C, ref.astype(np.float16).astype(np.float64))
+
+
 def test_mx_unit_scales_fp8_exact_products(orc):
     """Scale 127 everywhere: the oracle equals a plain fp8 matmul; the GPU must match within the bound."""
     api = require_gpu()

@@ -40,6 +40,8 @@ def test_host_element_codec_all_codes(orc):
     for code in range(256):
         a, b = api.mx_decode_host(api.MX_E4M3, code), orc.dec_e4m3([code])[0]
         assert (np.isnan(a) and np.isnan(b)) or (a == b and np.signbit(a) == np.signbit(b))
+        a, b = api.mx_decode_host(api.MX_E5M2, code), orc.dec_e5m2([code])[0]
+        assert (np.isnan(a) and np.isnan(b)) or (a == b and np.signbit(a) == np.signbit(b))
         e = api.mx_decode_host(api.MX_E8M0, code)
         r = orc.dec_e8m0([code])[0]
         assert (np.isnan(e) and np.isnan(r)) or e == r
@@ -48,10 +50,13 @@ def test_host_element_codec_all_codes(orc):
         assert api.mx_decode_host(api.MX_INT4, code) == orc.dec_int4([code])[0]
     g = np.random.Generator(np.random.PCG64(3))
     vals = np.concatenate([g.standard_normal(3000) * 100, g.standard_normal(3000) * 1e-3,
-                           [0.0, -0.0, 448.0, 464.0, 465.0, 1e30, -1e30, 6.0, 7.0, 5.0, 0.25]]).astype(np.float32)
+                           g.standard_normal(3000) * 3e4, g.standard_normal(3000) * 1e-5,
+                           [0.0, -0.0, 448.0, 464.0, 465.0, 1e30, -1e30, 6.0, 7.0, 5.0, 0.25, 57344.0, 61439.0,
+                            61440.0, 2.0 ** -17, 3.0 * 2.0 ** -17]]).astype(np.float32)
     for v in vals:
         assert api.mx_encode_host(api.MX_E4M3, float(v)) == orc.enc_elem(0, [float(v)])[0], v
         assert api.mx_encode_host(api.MX_E2M1, float(v)) == orc.enc_elem(4, [float(v)])[0], v
+        assert api.mx_encode_host(api.MX_E5M2, float(v)) == orc.enc_elem(1, [float(v)])[0], v
 
 
 def _edge_rows(cols, seed):
@@ -64,10 +69,12 @@ def _edge_rows(cols, seed):
     x[5, 40] = np.nan
     x[6, :32] = np.float32(2.0) ** np.arange(-16, 16, dtype=np.float32)
     x[7] = np.float32(448.0 * 3) * np.sign(x[7])  # saturation after scaling
+    x[8, :32] = np.float32(57344.0 * 1.1) * np.sign(x[8, :32])  # E5M2 block amax above its largest element
+    x[9, :32] = np.float32(2.0) ** np.arange(-40, -8, dtype=np.float32)  # E5M2 subnormals after scaling
     return x.astype(np.float32)
 
 
-@pytest.mark.parametrize("fmt", [0, 4])
+@pytest.mark.parametrize("fmt", [0, 1, 4])
 def test_host_mx_pack_matches_oracle(orc, fmt):
     cols = 256
     for seed, x in [(1, synth.normal((96, cols), 1.0, 1)), (2, synth.normal((64, cols), 0.02, 2)), (3, _edge_rows(cols, 3))]:
@@ -187,6 +194,32 @@ def test_ring_tile_plan_info(monkeypatch):
     assert info(2048, 6144, 4096, api.MX_E4M3) == (256, 192, 64, 3)
     for M, N, K, f in [(300, 520, 416, api.MX_E4M3), (4096, 8192, 1536, api.MX_E2M1), (512, 520, 512, api.MX_F16)]:
         assert info(M, N, K, f)[3] != 3
+
+
+def test_e5m2_pairs_plan(monkeypatch):
+    """Every pair with an E5M2 operand is accepted where the ring applies (K % 512 == 0,
+    N % 4 == 0), runs the 256x256 ring whatever the override, and is refused with MX_ERR_SHAPE
+    elsewhere."""
+    pairs = ((api.MX_E5M2, api.MX_E5M2), (api.MX_E4M3, api.MX_E5M2), (api.MX_E5M2, api.MX_E4M3),
+             (api.MX_E5M2, api.MX_E2M1), (api.MX_E2M1, api.MX_E5M2))
+    for tile in (None, "9", "10", "4"):
+        if tile is None:
+            monkeypatch.delenv("MXGEMM_TILE", raising=False)
+        else:
+            monkeypatch.setenv("MXGEMM_TILE", tile)
+        for fa, fb in pairs:
+            p = api.mxgemm_create(2048, 14336, 4096, fa, fb)
+            assert api.mxgemm_plan_info(p) == (256, 256, 64, 3)
+            api.mxgemm_destroy(p)
+    for fa, fb in pairs:
+        for M, N, K in ((64, 64, 416), (64, 66, 512), (64, 64, 256)):
+            with pytest.raises(RuntimeError):
+                api.mxgemm_create(M, N, K, fa, fb)
+    lib = api._lib
+    h = ctypes.c_void_p()
+    assert lib.mxgemm_create(ctypes.byref(h), 64, 64, 512, api.MX_E5M2, api.MX_F16, 0) == api.MX_ERR_FORMAT
+    assert lib.mxgemm_create(ctypes.byref(h), 64, 64, 512, api.MX_E5M2, api.MX_E5M2, 0) == 0
+    assert lib.mxgemm_destroy(h) == 0
 
 
 def test_mixed_pairs_plan(monkeypatch):
