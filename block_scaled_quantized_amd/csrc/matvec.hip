@@ -314,16 +314,16 @@ __global__ __launch_bounds__(W * 64) void matvec_kernel(const _Float16* __restri
 // by 16*MT rows; every block product is still scaled by its fp16 block scale in fp32 (one FMA per
 // output per block) and added to an fp32 accumulator. The waves' accumulators meet in LDS.
 // ---------------------------------------------------------------------------------------------
-// One block, software-pipelined across the column offsets e of the lane's 4 columns: the MFMAs of
+// One block, software-pipelined across the column offsets e of the lane's C columns: the MFMAs of
 // offset e (one per activation tile) alternate with the scale FMAs of offset e-1, whose products
 // were issued a full round of MFMAs earlier, so neither the matrix core nor the vector ALU waits
-// on the other. The products of the last offset stay pending and are scaled during the first MFMA
-// round of the next block; flush_pending() scales what the last block left. The full scheduling
-// barriers keep this issue order (left alone, the scheduler puts each FMA right behind the MFMA
-// that produces its input).
+// on the other. Each group of 4 columns is converted just before its first MFMA. The products of
+// the last offset stay pending and are scaled during the first MFMA round of the next block;
+// flush_pending() scales what the last block left. The full scheduling barriers keep this issue
+// order (left alone, the scheduler puts each FMA right behind the MFMA that produces its input).
 template <int MT>
 struct Pending {
-  v4f d[MT];   // products of the last column offset (column 3) of the previous block
+  v4f d[MT];   // products of the last column offset (column C-1) of the previous block
   uint32_t s;  // its fp16 scale (low half)
 };
 
@@ -336,34 +336,33 @@ MX_DEV void scale_add(v4f (&acc)[MT][C], const v4f& d, int t, int j, uint32_t sh
 
 template <bool I8, int C, int MT>
 MX_DEV void compute_stage_mt(const Stage<I8, C, MT>& s, v4f (&acc)[MT][C], Pending<MT>& pend) {
-  static_assert(C == 4, "one group of 4 columns per lane");
+  static_assert(C % 4 == 0, "groups of 4 columns per lane");
   v8h frag[4];
-  weights_to_frags<I8, C>(s, 0, frag);
-  uint32_t sh[4];  // fp16 scale of column e in the low half
-#pragma unroll
-  for (int e = 0; e < 4; e++) sh[e] = (e & 1) ? (s.sc[e / 2] >> 16) : s.sc[e / 2];
-  __builtin_amdgcn_sched_barrier(0);
   v4f d[2][MT];
 #pragma unroll
-  for (int e = 0; e < 4; e++) {
+  for (int e = 0; e < C; e++) {
+    if (e % 4 == 0) {
+      weights_to_frags<I8, C>(s, e / 4, frag);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int t = 0; t < MT; t++) {
-      d[e & 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, s.xa[t]), frag[e],
+      d[e & 1][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, s.xa[t]), frag[e % 4],
                                                            v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      if (e == 0) scale_add<C, MT>(acc, pend.d[t], t, 3, pend.s);
-      else scale_add<C, MT>(acc, d[(e - 1) & 1][t], t, e - 1, sh[e - 1]);
+      if (e == 0) scale_add<C, MT>(acc, pend.d[t], t, C - 1, pend.s);
+      else scale_add<C, MT>(acc, d[(e - 1) & 1][t], t, e - 1, (e - 1) & 1 ? s.sc[(e - 1) / 2] >> 16 : s.sc[(e - 1) / 2]);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
-  for (int t = 0; t < MT; t++) pend.d[t] = d[1][t];
-  pend.s = sh[3];
+  for (int t = 0; t < MT; t++) pend.d[t] = d[(C - 1) & 1][t];
+  pend.s = (C - 1) & 1 ? s.sc[(C - 1) / 2] >> 16 : s.sc[(C - 1) / 2];
 }
 
 template <int C, int MT>
 MX_DEV void flush_pending(v4f (&acc)[MT][C], const Pending<MT>& pend) {
 #pragma unroll
-  for (int t = 0; t < MT; t++) scale_add<C, MT>(acc, pend.d[t], t, 3, pend.s);
+  for (int t = 0; t < MT; t++) scale_add<C, MT>(acc, pend.d[t], t, C - 1, pend.s);
 }
 
 constexpr int kWqWPol = 0;  // cache policy of the weight and scale loads
@@ -814,29 +813,31 @@ int launch(int M, int N, int K, const void* x, const void* W, const void* Ws, vo
   return launch_status();
 }
 
-// Small-M GEMM form (M > 8): 4 columns per lane (64-column strips). The row tile is the smallest of
-// 16, 32, 64 or 128 activation rows that keeps the grid within 3 rounds of the 256 compute units:
-// more workgroups hide more latency, fewer re-convert each weight fewer times. Measured on MI355X
-// (int4 and int8 alike): M=128, N=12288, K=4096: 32 rows with 8 waves 35 us, 128 rows with 4 waves
-// 38 us, 16 rows 48 us; M=64, N=4096: 16 rows 10 us, 32 rows 13 us, 64 rows 20 us.
-constexpr int kWqC = 4, kWqMaxWGs = 3 * 256;
+// Small-M GEMM form (M > 8). Measured on MI355X (int4 / int8), K=4096:
+//   M=128, N=12288: 8 columns per lane with 64-row tiles (128-column strips, 192 workgroups of 4
+//     waves) 29-30 us; 4 columns with 32-row tiles and 8 waves 36-37 us; 16 columns 33-35 us.
+//   M=64, N=4096: 4 columns with 16-row tiles and 8 waves 10 us; 8 columns 14-16 us.
+// Wider strips cut the activation re-reads (each strip reads all of its row tile's x) and taller
+// row tiles re-convert each weight fewer times, while too few workgroups leave CUs idle. So the
+// 128-column strips run where they still give 192 or more workgroups and M > 32; otherwise 64-column
+// strips with 16-row tiles, or 32-row tiles where 16 would give more than 3 rounds of workgroups.
+constexpr int kWqMaxWGs = 3 * 256, kWqMinWide = 192;
 
-template <bool I8, int MT, int W, int P>
+template <bool I8, int C, int MT, int W, int P>
 int launch_wq_mt(int M, int N, int K, const void* x, const void* Wt, const void* Ws, void* y, hipStream_t st) {
-  const dim3 grid((unsigned)(((N + 16 * kWqC - 1) / (16 * kWqC)) * ((M + 16 * MT - 1) / (16 * MT))));
-  hipLaunchKernelGGL((gemm_wq_kernel<I8, kWqC, MT, W, P>), grid, dim3(W * 64), 0, st, (const _Float16*)x,
+  const dim3 grid((unsigned)(((N + 16 * C - 1) / (16 * C)) * ((M + 16 * MT - 1) / (16 * MT))));
+  hipLaunchKernelGGL((gemm_wq_kernel<I8, C, MT, W, P>), grid, dim3(W * 64), 0, st, (const _Float16*)x,
                      (const uint8_t*)Wt, (const _Float16*)Ws, (_Float16*)y, M, N, K);
   return launch_status();
 }
 
 template <bool I8>
 int launch_wq(int M, int N, int K, const void* x, const void* W, const void* Ws, void* y, hipStream_t st) {
-  const int64_t strips = (N + 16 * kWqC - 1) / (16 * kWqC);
-  auto wgs = [&](int rows) { return strips * ((M + rows - 1) / rows); };
-  if (wgs(16) <= kWqMaxWGs) return launch_wq_mt<I8, 1, 8, 4>(M, N, K, x, W, Ws, y, st);
-  if (wgs(32) <= kWqMaxWGs) return launch_wq_mt<I8, 2, 8, 2>(M, N, K, x, W, Ws, y, st);
-  if (wgs(64) <= kWqMaxWGs) return launch_wq_mt<I8, 4, 8, 2>(M, N, K, x, W, Ws, y, st);
-  return launch_wq_mt<I8, 8, 4, 3>(M, N, K, x, W, Ws, y, st);
+  const int64_t strips4 = (N + 63) / 64, strips8 = (N + 127) / 128;
+  if (M > 32 && strips8 * ((M + 63) / 64) >= kWqMinWide) return launch_wq_mt<I8, 8, 4, 4, 2>(M, N, K, x, W, Ws, y, st);
+  if (strips4 * ((M + 15) / 16) <= kWqMaxWGs) return launch_wq_mt<I8, 4, 1, 8, 4>(M, N, K, x, W, Ws, y, st);
+  if (strips4 * ((M + 31) / 32) <= kWqMaxWGs) return launch_wq_mt<I8, 4, 2, 8, 2>(M, N, K, x, W, Ws, y, st);
+  return launch_wq_mt<I8, 8, 4, 4, 2>(M, N, K, x, W, Ws, y, st);
 }
 
 }  // namespace

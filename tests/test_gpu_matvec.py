@@ -140,11 +140,13 @@ def wq_case(orc, api, fw, M, K, N, seed_w, seed_x):
 @pytest.mark.parametrize("fw", [32, 33])
 @pytest.mark.parametrize("M,K,N", [(9, 32, 32), (16, 1024, 1056), (31, 96, 160), (33, 4096, 64), (64, 544, 4128),
                                    (100, 256, 12288), (128, 4096, 512), (129, 160, 96), (200, 1024, 1024),
-                                   (256, 2048, 320), (150, 96, 12800), (200, 64, 16384), (129, 64, 19200)])
+                                   (256, 2048, 320), (150, 96, 12800), (200, 64, 16384), (129, 64, 19200),
+                                   (20, 64, 25600), (144, 96, 6144)])
 def test_wq_gemm_ragged(orc, fw, M, K, N):
-    """Every output: partial row tiles, partial column strips, one block of K up to many. The row
-    tile grows with the grid: 16 rows for most of these, 32 at M=100/N=12288, 64 at M=150/N=12800,
-    128 at M=200/N=16384 and M=129/N=19200 (two row tiles, the second with one row)."""
+    """Every output: partial row tiles, partial column strips, one block of K up to many. Launch
+    shapes: 128-column strips with 64-row tiles at M=100/N=12288, M=150/N=12800, M=200/N=16384 and
+    M=129/N=19200 (the last tile with 1 row); 64-column strips with 32-row tiles at M=20/N=25600 and
+    M=144/N=6144; 64-column strips with 16-row tiles for the rest."""
     api = require_gpu()
     say(f"wq gemm fw={fw} M={M} K={K} N={N}")
     x, oW, s, got, R = wq_case(orc, api, fw, M, K, N, 13 * K + N + M, 5 * K + M)
