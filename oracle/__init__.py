@@ -25,7 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-E4M3, E5M2, E2M1, F16, INT8, INT4 = 0, 1, 4, 16, 32, 33
+E4M3, E5M2, E2M3, E3M2, E2M1, F16, INT8, INT4 = 0, 1, 2, 3, 4, 16, 32, 33
 
 _lib = None
 
@@ -50,6 +50,7 @@ def lib():
     sig = {
         "orc_num_threads": (i, []),
         "orc_dec_e4m3": (d, [u]), "orc_dec_e5m2": (d, [u]), "orc_dec_e2m1": (d, [u]), "orc_dec_e8m0": (d, [u]),
+        "orc_dec_e2m3": (d, [u]), "orc_dec_e3m2": (d, [u]),
         "orc_dec_int4": (d, [u]), "orc_dec_f16": (d, [u]),
         "orc_mx_dot": (d, [i, i, i64, p, p, p, p, i64, i64]),
         "orc_mxgemm_rows": (None, [i, i, i64, i64, i64, p, p, p, p, i64, i64, p]),
@@ -94,6 +95,14 @@ def dec_e5m2(codes) -> np.ndarray:
     return np.array([lib().orc_dec_e5m2(int(c)) for c in np.ravel(codes)]).reshape(np.shape(codes))
 
 
+def dec_e2m3(codes) -> np.ndarray:
+    return np.array([lib().orc_dec_e2m3(int(c)) for c in np.ravel(codes)]).reshape(np.shape(codes))
+
+
+def dec_e3m2(codes) -> np.ndarray:
+    return np.array([lib().orc_dec_e3m2(int(c)) for c in np.ravel(codes)]).reshape(np.shape(codes))
+
+
 def dec_e2m1(codes) -> np.ndarray:
     return np.array([lib().orc_dec_e2m1(int(c)) for c in np.ravel(codes)]).reshape(np.shape(codes))
 
@@ -113,7 +122,9 @@ def dec_f16(bits) -> np.ndarray:
 # ---- GEMMs -----------------------------------------------------------------------------------
 
 def _mx_shapes(fmt, rows, K):
-    return (rows, K // 2) if fmt == E2M1 else (rows, K)
+    if fmt == E2M1:
+        return (rows, K // 2)
+    return (rows, K // 4 * 3) if fmt in (E2M3, E3M2) else (rows, K)
 
 
 def mxgemm(fa, fb, A, SA, B, SB, M, N, K, row0=0, nrows=None) -> np.ndarray:

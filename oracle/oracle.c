@@ -23,8 +23,10 @@
  * The pages name E4M3, fp8, fp4, "MX scaling formats" and E8M0 without giving their bits (TensorOps
  * notes, quantized dtype support matrix). The readings used here are the OCP Microscaling (MX) v1.0
  * element formats: E4M3 "FN" (bias 7, S.1111.111 = NaN, no Inf, max 448), E5M2 (bias 15,
- * S.11111.00 = Inf, S.11111.xx = NaN, max 57344), E2M1 (bias 1, values +-{0,.5,1,1.5,2,3,4,6},
- * no NaN/Inf) and E8M0 (2^(e-127), 0xFF=NaN).
+ * S.11111.00 = Inf, S.11111.xx = NaN, max 57344), the FP6 pair E2M3 (bias 1, max 7.5) and E3M2
+ * (bias 3, max 28) without NaN/Inf, E2M1 (bias 1, values +-{0,.5,1,1.5,2,3,4,6}, no NaN/Inf) and
+ * E8M0 (2^(e-127), 0xFF=NaN). FP6 rows are packed as a little-endian bit stream: element j in
+ * bits 6j..6j+5 (4 elements in 3 bytes).
  *
  * Every function here has a pin in the CPU test suite (library dtypes, closed forms, exact
  * brute force, invariants); none is "parity unpinned".
@@ -37,7 +39,7 @@
 #include <omp.h>
 #endif
 
-enum { ORC_E4M3 = 0, ORC_E5M2 = 1, ORC_E2M1 = 4, ORC_F16 = 16, ORC_INT8 = 32, ORC_INT4 = 33 };
+enum { ORC_E4M3 = 0, ORC_E5M2 = 1, ORC_E2M3 = 2, ORC_E3M2 = 3, ORC_E2M1 = 4, ORC_F16 = 16, ORC_INT8 = 32, ORC_INT4 = 33 };
 
 int orc_num_threads(void) {
 #ifdef _OPENMP
@@ -70,6 +72,20 @@ double orc_dec_e5m2(unsigned b) {
   if (e == 31) v = f ? NAN : INFINITY;
   else if (e == 0) v = ldexp((double)f, -16);
   else v = ldexp(1.0 + (double)f / 4.0, (int)e - 15);
+  return s ? -v : v;
+}
+
+/* E2M3 (FP6): sign 1 (bit 5), exponent 2 (bias 1), mantissa 3. Exponent 0 is subnormal f*2^-3. */
+double orc_dec_e2m3(unsigned c) {
+  unsigned s = (c >> 5) & 1u, e = (c >> 3) & 3u, f = c & 7u;
+  double v = e ? ldexp(1.0 + (double)f / 8.0, (int)e - 1) : ldexp((double)f, -3);
+  return s ? -v : v;
+}
+
+/* E3M2 (FP6): sign 1 (bit 5), exponent 3 (bias 3), mantissa 2. Exponent 0 is subnormal f*2^-4. */
+double orc_dec_e3m2(unsigned c) {
+  unsigned s = (c >> 5) & 1u, e = (c >> 2) & 7u, f = c & 3u;
+  double v = e ? ldexp(1.0 + (double)f / 4.0, (int)e - 3) : ldexp((double)f, -4);
   return s ? -v : v;
 }
 
@@ -111,14 +127,27 @@ static unsigned nibble(const uint8_t* row, int64_t j) {
   return (j % 2 == 0) ? (by & 0xFu) : (by >> 4);
 }
 
+/* Element j of a row of 6-bit codes: bits 6j..6j+5 of the row read as a little-endian bit stream. */
+static unsigned sixbit(const uint8_t* row, int64_t j) {
+  int64_t bit = 6 * j;
+  unsigned two = (unsigned)row[bit / 8] | ((bit % 8 > 2) ? (unsigned)row[bit / 8 + 1] << 8 : 0u);
+  return (two >> (bit % 8)) & 63u;
+}
+
+static int is_fp6(int fmt) { return fmt == ORC_E2M3 || fmt == ORC_E3M2; }
+
 /* Dequantised value of element k of one MX row (codes along K, scales one per 32 along K). */
 static double mx_elem(int fmt, const uint8_t* codes_row, const uint8_t* scales_row, int64_t k) {
-  double v = (fmt == ORC_E4M3) ? orc_dec_e4m3(codes_row[k])
-             : (fmt == ORC_E5M2) ? orc_dec_e5m2(codes_row[k]) : orc_dec_e2m1(nibble(codes_row, k));
+  double v;
+  if (fmt == ORC_E4M3) v = orc_dec_e4m3(codes_row[k]);
+  else if (fmt == ORC_E5M2) v = orc_dec_e5m2(codes_row[k]);
+  else if (fmt == ORC_E2M3) v = orc_dec_e2m3(sixbit(codes_row, k));
+  else if (fmt == ORC_E3M2) v = orc_dec_e3m2(sixbit(codes_row, k));
+  else v = orc_dec_e2m1(nibble(codes_row, k));
   return v * orc_dec_e8m0(scales_row[k / 32]);
 }
 
-static int64_t mx_row_bytes(int fmt, int64_t K) { return fmt == ORC_E2M1 ? K / 2 : K; }
+static int64_t mx_row_bytes(int fmt, int64_t K) { return fmt == ORC_E2M1 ? K / 2 : (is_fp6(fmt) ? K / 4 * 3 : K); }
 
 /* ------------------------------------------------------------------------------------------ */
 /* MX GEMM: C[m,n] = sum_k (dec(A[m,k]) * 2^(SA[m,k/32]-127)) * (dec(B[k,n]) * 2^(SB[n,k/32]-127)) */
@@ -221,7 +250,7 @@ void orc_dequant(int fmt, int64_t rows, int64_t cols, const uint8_t* codes, cons
   for (int64_t r = 0; r < rows; r++)
     for (int64_t c = 0; c < cols; c++) {
       double v;
-      if (fmt == ORC_E4M3 || fmt == ORC_E5M2 || fmt == ORC_E2M1) {
+      if (fmt == ORC_E4M3 || fmt == ORC_E5M2 || is_fp6(fmt) || fmt == ORC_E2M1) {
         v = mx_elem(fmt, codes + r * mx_row_bytes(fmt, cols), (const uint8_t*)scales + r * (cols / 32), c);
       } else {
         double s = orc_dec_f16(((const uint16_t*)scales)[(r / 32) * cols + c]);
@@ -234,7 +263,8 @@ void orc_dequant(int fmt, int64_t rows, int64_t cols, const uint8_t* codes, cons
 /* ------------------------------------------------------------------------------------------ */
 /* Encoders. These are encodings, so they follow the quantisation steps in order:               */
 /*  1. amax of the 32-element block, 2. j = floor(log2 amax) from the exact binary exponent,     */
-/*  3. E = clamp(j - emax + 127, 0, 254) with emax = 8 (E4M3), 15 (E5M2) or 2 (E2M1),          */
+/*  3. E = clamp(j - emax + 127, 0, 254) with emax = 8 (E4M3), 15 (E5M2), 2 (E2M3), 4 (E3M2)   */
+/*     or 2 (E2M1),                                                                            */
 /*  4. v = x * 2^(127-E) exactly, 5. the element code nearest to v, ties to the even code,       */
 /*     values beyond the largest finite element saturate to it, the sign is kept.              */
 /* The element search is brute force over the format's own decode values (not bit arithmetic). */
@@ -242,12 +272,14 @@ void orc_dequant(int fmt, int64_t rows, int64_t cols, const uint8_t* codes, cons
 
 /* The positive finite element values of a format, indexed by code (E4M3: 0x00..0x7E, E5M2:
  * 0x00..0x7B, E2M1: 0..7), filled once from the closed-form decoders above. */
-static double g_tab_e4m3[0x7F], g_tab_e5m2[0x7C], g_tab_e2m1[8];
+static double g_tab_e4m3[0x7F], g_tab_e5m2[0x7C], g_tab_e2m3[32], g_tab_e3m2[32], g_tab_e2m1[8];
 static int g_tab_ready = 0;
 static void build_tables(void) {
   if (g_tab_ready) return;
   for (unsigned c = 0; c < 0x7Fu; c++) g_tab_e4m3[c] = orc_dec_e4m3(c);
   for (unsigned c = 0; c < 0x7Cu; c++) g_tab_e5m2[c] = orc_dec_e5m2(c);
+  for (unsigned c = 0; c < 32u; c++) g_tab_e2m3[c] = orc_dec_e2m3(c);
+  for (unsigned c = 0; c < 32u; c++) g_tab_e3m2[c] = orc_dec_e3m2(c);
   for (unsigned c = 0; c < 8u; c++) g_tab_e2m1[c] = orc_dec_e2m1(c);
   g_tab_ready = 1;
 }
@@ -256,8 +288,9 @@ static void build_tables(void) {
  * ties to the even code. Values at or beyond the largest finite element saturate to it; below it
  * every candidate distance that can decide the choice is exact in fp64. */
 static unsigned nearest_code(double av, int fmt) {
-  const double* tab = (fmt == ORC_E4M3) ? g_tab_e4m3 : (fmt == ORC_E5M2) ? g_tab_e5m2 : g_tab_e2m1;
-  unsigned best = 0, ncodes = (fmt == ORC_E4M3) ? 0x7Fu : (fmt == ORC_E5M2) ? 0x7Cu : 8u;
+  const double* tab = (fmt == ORC_E4M3) ? g_tab_e4m3 : (fmt == ORC_E5M2) ? g_tab_e5m2
+                      : (fmt == ORC_E2M3) ? g_tab_e2m3 : (fmt == ORC_E3M2) ? g_tab_e3m2 : g_tab_e2m1;
+  unsigned best = 0, ncodes = (fmt == ORC_E4M3) ? 0x7Fu : (fmt == ORC_E5M2) ? 0x7Cu : is_fp6(fmt) ? 32u : 8u;
   double bestd = INFINITY;
   if (av >= tab[ncodes - 1u]) return ncodes - 1u;
   for (unsigned c = 0; c < ncodes; c++) {
@@ -271,7 +304,7 @@ static unsigned nearest_code(double av, int fmt) {
 unsigned orc_enc_elem(int fmt, double v) {
   build_tables();
   unsigned mag = nearest_code(fabs(v), fmt);
-  unsigned sbit = (fmt == ORC_E2M1) ? 0x8u : 0x80u;
+  unsigned sbit = (fmt == ORC_E2M1) ? 0x8u : is_fp6(fmt) ? 0x20u : 0x80u;
   return signbit(v) ? (mag | sbit) : mag;
 }
 
@@ -284,7 +317,7 @@ int orc_floor_log2(double a) {
 
 /* The E8M0 scale code of one block, from its amax (step 2-3). */
 unsigned orc_mx_scale_code(int fmt, double amax) {
-  int emax = (fmt == ORC_E4M3) ? 8 : (fmt == ORC_E5M2) ? 15 : 2, E;
+  int emax = (fmt == ORC_E4M3) ? 8 : (fmt == ORC_E5M2) ? 15 : (fmt == ORC_E3M2) ? 4 : 2, E;
   if (!(amax > 0.0)) return 0u; /* amax = 0: log2 is -inf, clamps to 0 */
   E = orc_floor_log2(amax) - emax + 127;
   if (E < 0) E = 0;
@@ -315,8 +348,12 @@ void orc_mx_quantize(int fmt, int64_t rows, int64_t cols, const float* src, uint
       for (int i = 0; i < 32; i++) {
         int64_t c = 32 * b + i;
         unsigned code = orc_enc_elem(fmt, ldexp((double)x[i], 127 - (int)E));
-        if (fmt != ORC_E2M1) codes[r * rb + c] = (uint8_t)code;
-        else codes[r * rb + c / 2] |= (uint8_t)((c % 2 == 0) ? code : (code << 4));
+        if (fmt == ORC_E2M1) codes[r * rb + c / 2] |= (uint8_t)((c % 2 == 0) ? code : (code << 4));
+        else if (is_fp6(fmt)) {
+          int64_t bit = 6 * c;
+          codes[r * rb + bit / 8] |= (uint8_t)(code << (bit % 8));
+          if (bit % 8 > 2) codes[r * rb + bit / 8 + 1] |= (uint8_t)(code >> (8 - bit % 8));
+        } else codes[r * rb + c] = (uint8_t)code;
       }
     }
 }

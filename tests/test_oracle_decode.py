@@ -8,6 +8,7 @@ worked by hand. binary16: numpy's float16.
 import math
 
 import numpy as np
+import pytest
 import torch
 
 from conftest import read_golden
@@ -32,6 +33,26 @@ def test_e5m2_all_codes_match_torch(orc):
     codes = np.arange(256, dtype=np.uint8)
     ref = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
     _same(orc.dec_e5m2(codes), ref)
+
+
+@pytest.mark.parametrize("fp6,fp8_dtype,vmax,vmin", [("e2m3", torch.float8_e4m3fn, 7.5, 0.125),
+                                                       ("e3m2", torch.float8_e5m2, 28.0, 0.0625)])
+def test_fp6_embeds_into_torch_fp8(orc, fp6, fp8_dtype, vmax, vmin):
+    """Every FP6 value lies on the fp8 grid with the same mantissa width (E2M3 in E4M3, E3M2 in
+    E5M2, both decoded by torch), positive codes 0..31 increase strictly from 0 to the largest
+    element, the smallest nonzero is the subnormal unit, each binade holds the same number of
+    codes, and bit 5 is the sign."""
+    dec = getattr(orc, "dec_" + fp6)
+    grid = set(torch.arange(256, dtype=torch.uint8).view(fp8_dtype).to(torch.float64).numpy().tolist())
+    pos = dec(np.arange(32))
+    neg = dec(np.arange(32, 64))
+    assert all(v in grid for v in pos)
+    assert np.all(np.diff(pos) > 0) and pos[0] == 0.0 and pos[-1] == vmax and pos[1] == vmin
+    assert np.array_equal(neg, -pos) and np.signbit(neg[0])
+    per = 8 if fp6 == "e2m3" else 4                     # codes per binade: 2^mantissa bits
+    normals = pos[per:]
+    expo = np.floor(np.log2(normals))
+    assert all(np.sum(expo == e) == per for e in np.unique(expo))
 
 
 def test_e4m3_golden_specials(orc):

@@ -85,6 +85,25 @@ def test_mx_e5m2_unit_scales_is_plain_fp8_matmul(orc, M, N, K):
     assert np.array_equal(C, (torch_e5m2(A) @ torch_e4m3(B8).T).numpy())
 
 
+@pytest.mark.parametrize("fa,fb", [(2, 2), (3, 3), (2, 3)])
+def test_mx_fp6_unit_scales_is_plain_matmul(orc, fa, fb):
+    """FP6 at unit scales: numpy's matmul of the decoded elements (multiples of 2^-4 below 28, so
+    every sum is exact), with the 6-bit fields unpacked by numpy's little-endian bit stream."""
+    M, N, K = 9, 11, 128
+    g = np.random.Generator(np.random.PCG64(40 + fa + fb))
+    def pack(codes):
+        bits = ((codes[..., None] >> np.arange(6)) & 1).astype(np.uint8).reshape(codes.shape[0], -1)
+        return np.packbits(bits, axis=1, bitorder="little")
+    ca, cb = g.integers(0, 64, (M, K)), g.integers(0, 64, (N, K))
+    names = {2: "e2m3", 3: "e3m2"}
+    a = getattr(orc, "dec_" + names[fa])(ca)
+    b = getattr(orc, "dec_" + names[fb])(cb)
+    SA = np.full((M, K // 32), 127, np.uint8)
+    SB = np.full((N, K // 32), 127, np.uint8)
+    C = orc.mxgemm(fa, fb, pack(ca), SA, pack(cb), SB, M, N, K)
+    assert np.array_equal(C, a @ b.T)
+
+
 def test_mx_e2m1_unit_scales_is_plain_fp4_matmul(orc):
     M, N, K = 9, 11, 96
     A = synth.random_bytes((M, K // 2), 13)

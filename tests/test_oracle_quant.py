@@ -118,6 +118,62 @@ def test_enc_e2m1_matches_binade_rounding(orc):
     assert list(e2m1_table()[got]) == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]
 
 
+def grid_enc_fp6(v, fmt):
+    """Nearest FP6 code by rounding |v| on its binade's spacing with np.round (half to even),
+    saturating at the largest element; bit 5 carries the sign."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if fmt == 2:   # E2M3: spacing 1/8 below 2, then 1/4, 1/2; max 7.5
+        sp = np.where(a < 2.0, 0.125, np.where(a < 4.0, 0.25, 0.5))
+        top = 7.5
+    else:          # E3M2: spacing 1/16 below 0.5, doubling per binade; max 28
+        sp = np.where(a < 0.5, 0.0625, 2.0 ** np.floor(np.log2(np.maximum(a, 0.5))) / 4)
+        top = 28.0
+    r = np.minimum(np.round(a / sp) * sp, top)
+    return r
+
+
+@pytest.mark.parametrize("fmt,name", [(2, "e2m3"), (3, "e3m2")])
+def test_enc_fp6_matches_binade_rounding(orc, fmt, name):
+    tab = getattr(orc, "dec_" + name)(np.arange(32))
+    mids = (tab[:-1] + tab[1:]) / 2
+    g = np.random.Generator(np.random.PCG64(30 + fmt))
+    vals = np.concatenate([tab, mids, mids + 1e-9, mids - 1e-9, g.random(5000) * tab[-1] * 1.2,
+                           [tab[-1] * 1.5, 1e6, 1e-30]])
+    vals = np.concatenate([vals, -vals])
+    codes = orc.enc_elem(fmt, vals)
+    got = getattr(orc, "dec_" + name)(codes)
+    assert np.array_equal(got, np.copysign(grid_enc_fp6(vals, fmt), vals))
+    assert np.array_equal(codes >> 5, np.signbit(vals).astype(np.uint8))
+
+
+@pytest.mark.parametrize("fmt,name", [(2, "e2m3"), (3, "e3m2")])
+def test_mx_quantize_fp6_vs_binade_rounding_and_packing(orc, fmt, name):
+    """Block quantiser: scale rule with emax 2 (E2M3) / 4 (E3M2), elements by binade rounding, and
+    the 6-bit packing checked against numpy's little-endian bit stream."""
+    emax = 2 if fmt == 2 else 4
+    rows, cols = 32, 256
+    x = synth.normal((rows, cols), 1.0, 1100 + fmt)
+    x[3, :32] = 0.0
+    codes, scales = orc.mx_quantize(fmt, x)
+    assert codes.shape == (rows, cols // 4 * 3)
+    bits = np.unpackbits(codes, axis=1, bitorder="little").reshape(rows, cols, 6)
+    elems = (bits * (1 << np.arange(6))).sum(axis=2)
+    for r in range(rows):
+        for b in range(cols // 32):
+            blk = x[r, 32 * b:32 * b + 32].astype(np.float64)
+            amax = np.max(np.abs(blk))
+            E = int(scales[r, b])
+            if amax == 0:
+                assert E == 0
+            else:
+                j = E - 127 + emax
+                assert math.ldexp(1.0, j) <= amax < math.ldexp(1.0, j + 1)
+            v = blk * math.ldexp(1.0, 127 - E)
+            got = getattr(orc, "dec_" + name)(elems[r, 32 * b:32 * b + 32])
+            assert np.array_equal(got, np.copysign(grid_enc_fp6(v, fmt), v))
+
+
 def test_floor_log2_defining_inequality(orc):
     g = np.random.Generator(np.random.PCG64(9))
     vals = list(g.random(2000) * 10.0 ** g.integers(-40, 38, 2000))
@@ -131,7 +187,7 @@ def test_floor_log2_defining_inequality(orc):
         assert math.ldexp(1.0, j) <= a < math.ldexp(1.0, j + 1)
 
 
-@pytest.mark.parametrize("fmt,emax", [(0, 8), (1, 15), (4, 2)])
+@pytest.mark.parametrize("fmt,emax", [(0, 8), (1, 15), (2, 2), (3, 4), (4, 2)])
 def test_scale_rule_closed_cases(orc, fmt, emax):
     for j in range(-60, 60):
         p = math.ldexp(1.0, j)
