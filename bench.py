@@ -5,7 +5,8 @@ K=4096, N=14336 (E4M3 data, E8M0 scales per 32 along K, fp32 accumulation, fp16 
 its throughput in TFLOP/s (2*M*N*K per step over the HIP-event time of the timed steps, inputs
 already resident in HBM). The other workloads of the path are measured in the same run and
 reported under "detail": the MXFP4 GEMM (M=4096, N=8192, K=8192), the mixed E4M3 x E2M1 GEMM and
-the E5M2 x E5M2 GEMM at the prefill shape (against the fp8 peak), the fp16 GEMM (4096^3), the
+the E5M2 x E5M2 GEMM at the prefill shape (against the fp8 peak), the FP6 E2M3 x E2M3 GEMM at the
+prefill shape (against the fp6 peak, equal to fp4's), the fp16 GEMM (4096^3), the
 small MXFP8 GEMM (128x256x128, a latency figure), the int8/int4 dequant matvec (M=1 and M=8,
 K=4096, N=14336; GB/s of algorithmic bytes), the same int8/int4-weight product at M=128 (N=12288)
 and M=64 (N=4096) with K=4096 (TFLOP/s against the fp16 peak) and the GPU pack/unpack codecs.
@@ -28,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK = {  # MI355X dense peaks (256 CUs x 2.4 GHz x flop/clk/CU) and HBM bandwidth
-    "mxfp8": 5033.2, "mxfp4": 10066.3, "fp16": 2516.6, "hbm_gbs": 8000.0,
+    "mxfp8": 5033.2, "mxfp6": 10066.3, "mxfp4": 10066.3, "fp16": 2516.6, "hbm_gbs": 8000.0,
 }
 
 
@@ -191,6 +192,18 @@ def main():
         detail["mxfp8_e5m2_gemm_2048x14336x4096"] = {"ms": t, "tflops": tf, "frac_peak": tf / PEAK["mxfp8"],
                                                      "tile": api.mxgemm_plan_info(p5)}
         del s5, C5
+
+    # ---------------- FP6 E2M3 x E2M3 at the prefill shape ----------------------------------------------
+    if want("fp6_prefill"):
+        log("timing FP6 GEMM")
+        s6, _, _ = mx_operands(api.MX_E2M3, M, N, K, synth.MXFP8_PREFILL, 0.02, 3)
+        p6 = api.mxgemm_create(M, N, K, api.MX_E2M3, api.MX_E2M3)
+        C6 = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(3)]
+        t = timed(lambda i: api.mxgemm_run(p6, *s6[i % 3], C6[i % 3], stream), args.steps, args.warmup)
+        tf = flops / (t * 1e-3) / 1e12
+        detail["mxfp6_e2m3_gemm_2048x14336x4096"] = {"ms": t, "tflops": tf, "frac_peak": tf / PEAK["mxfp6"],
+                                                     "tile": api.mxgemm_plan_info(p6)}
+        del s6, C6
 
     # ---------------- fp16 GEMM ----------------------------------------------------------------
     if want("f16_square"):

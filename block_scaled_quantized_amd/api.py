@@ -13,7 +13,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmxgemm.so")
 
-MX_E4M3, MX_E5M2, MX_E2M1, MX_E8M0, MX_F16, MX_INT8, MX_INT4 = 0, 1, 4, 8, 16, 32, 33
+MX_E4M3, MX_E5M2, MX_E2M3, MX_E3M2, MX_E2M1, MX_E8M0, MX_F16, MX_INT8, MX_INT4 = 0, 1, 2, 3, 4, 8, 16, 32, 33
 MXGEMM_RELU = 1  # mxgemm_create flag: C = max(A*B, 0) in the epilogue
 MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_FORMAT, MX_ERR_ARCH, MX_ERR_LAUNCH, MX_ERR_NOMEM = \
     0, -1, -2, -3, -4, -5, -6, -7
@@ -167,7 +167,13 @@ def mx_decode_host(f: int, code: int) -> float:
 
 def mx_shapes(fmt: int, rows: int, K: int):
     """(codes shape, scales shape) of an MX operand with `rows` rows of K elements."""
-    return ((rows, K // 2) if fmt == MX_E2M1 else (rows, K)), (rows, K // 32)
+    if fmt == MX_E2M1:
+        codes = (rows, K // 2)
+    elif fmt in (MX_E2M3, MX_E3M2):
+        codes = (rows, K // 4 * 3)
+    else:
+        codes = (rows, K)
+    return codes, (rows, K // 32)
 
 
 def int_shapes(fw: int, K: int, N: int):

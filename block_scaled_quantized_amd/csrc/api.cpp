@@ -136,11 +136,15 @@ int mxgemm_create(mxgemm_t* out, int M, int N, int K, int fa, int fb, unsigned f
   else if (fa == MX_E5M2 && fb == MX_E4M3) kind = 7;
   else if (fa == MX_E5M2 && fb == MX_E2M1) kind = 8;
   else if (fa == MX_E2M1 && fb == MX_E5M2) kind = 9;
+  else if (fa == MX_E2M3 && fb == MX_E2M3) kind = 10;
+  else if (fa == MX_E3M2 && fb == MX_E3M2) kind = 11;
+  else if (fa == MX_E2M3 && fb == MX_E3M2) kind = 12;
+  else if (fa == MX_E3M2 && fb == MX_E2M3) kind = 13;
   else return MX_ERR_FORMAT;
   if (M < 1 || N < 1 || K < 32 || M > MX_MAX_DIM || N > MX_MAX_DIM || K > MX_MAX_DIM) return MX_ERR_SHAPE;
   if (kind != 2 && K % 32) return MX_ERR_SHAPE;
   if (kind == 2 && (K % 8 || N % 8)) return MX_ERR_SHAPE;
-  if (kind >= 3 && (K % 512 || N % 4)) return MX_ERR_SHAPE;  // mixed and E5M2 pairs: the ring kernel only
+  if (kind >= 3 && (K % 512 || N % 4)) return MX_ERR_SHAPE;  // mixed, E5M2 and FP6 pairs: the ring kernel only
   mxgemm_plan* p = new (std::nothrow) mxgemm_plan{M, N, K, fa, fb, kind, choose_tile(kind, M, N, K), flags};
   if (!p) return MX_ERR_NOMEM;
   *out = p;

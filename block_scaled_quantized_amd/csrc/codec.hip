@@ -49,6 +49,16 @@ __global__ __launch_bounds__(kThreads) void pack_mx_kernel(const float* __restri
         for (int i = 0; i < 4; i++) w |= enc_elem_fmt(FMT, x[i], t) << (8 * i);
       }
       reinterpret_cast<uint32_t*>(codes)[blk * 8 + sub] = w;
+    } else if constexpr (is_fp6_fmt(FMT)) {  // 24 bits per lane: bytes 3 sub.. of the block's 24
+      uint32_t w = 0u;
+      if (!nonfinite) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) w |= enc_elem_fmt(FMT, x[i], t) << (6 * i);
+      }
+      uint8_t* o = codes + blk * 24 + 3 * sub;
+      o[0] = (uint8_t)w;
+      o[1] = (uint8_t)(w >> 8);
+      o[2] = (uint8_t)(w >> 16);
     } else {
       uint32_t w = 0u;
       if (!nonfinite) {
@@ -102,10 +112,16 @@ __global__ __launch_bounds__(kThreads) void unpack_mx_kernel(const uint8_t* __re
   for (int64_t qd = (int64_t)blockIdx.x * kThreads + threadIdx.x; qd < nquads; qd += (int64_t)gridDim.x * kThreads) {
     const int64_t e0 = qd * 4, r = e0 / cols, c = e0 % cols;
     const float s = dec_e8m0(scales[r * (cols / 32) + c / 32]);
-    uint32_t w = is_byte_fmt(FMT) ? reinterpret_cast<const uint32_t*>(codes)[qd]
-                                  : reinterpret_cast<const uint16_t*>(codes)[qd];
+    uint32_t w;
+    if constexpr (is_byte_fmt(FMT)) w = reinterpret_cast<const uint32_t*>(codes)[qd];
+    else if constexpr (is_fp6_fmt(FMT))
+      w = (uint32_t)codes[3 * qd] | ((uint32_t)codes[3 * qd + 1] << 8) | ((uint32_t)codes[3 * qd + 2] << 16);
+    else w = reinterpret_cast<const uint16_t*>(codes)[qd];
     float4 o;
-    if constexpr (is_byte_fmt(FMT)) {
+    if constexpr (is_fp6_fmt(FMT)) {
+      o = make_float4(dec_elem_fmt(FMT, w & 63u) * s, dec_elem_fmt(FMT, (w >> 6) & 63u) * s,
+                      dec_elem_fmt(FMT, (w >> 12) & 63u) * s, dec_elem_fmt(FMT, (w >> 18) & 63u) * s);
+    } else if constexpr (is_byte_fmt(FMT)) {
       o = make_float4(dec_elem_fmt(FMT, w & 255u) * s, dec_elem_fmt(FMT, (w >> 8) & 255u) * s,
                       dec_elem_fmt(FMT, (w >> 16) & 255u) * s, dec_elem_fmt(FMT, w >> 24) * s);
     } else {
@@ -141,7 +157,7 @@ extern "C" int mx_pack_run(int f, const float* src, int rows, int cols, void* co
   if (rows < 1 || cols < 1 || rows > MX_MAX_DIM || cols > MX_MAX_DIM) return MX_ERR_SHAPE;
   if (!aligned16(src) || !aligned16(codes) || !aligned16(scales)) return MX_ERR_ALIGN;
   hipStream_t st = as_stream(stream);
-  if (f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1) {
+  if (f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M3 || f == MX_E3M2 || f == MX_E2M1) {
     if (cols % 32) return MX_ERR_SHAPE;
     if (int a = check_arch()) return a;
     const int64_t nblocks = (int64_t)rows * (cols / 32);
@@ -151,6 +167,10 @@ extern "C" int mx_pack_run(int f, const float* src, int rows, int cols, void* co
       hipLaunchKernelGGL(pack_mx_kernel<MX_E4M3>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
     else if (f == MX_E5M2)
       hipLaunchKernelGGL(pack_mx_kernel<MX_E5M2>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
+    else if (f == MX_E2M3)
+      hipLaunchKernelGGL(pack_mx_kernel<MX_E2M3>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
+    else if (f == MX_E3M2)
+      hipLaunchKernelGGL(pack_mx_kernel<MX_E3M2>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
     else
       hipLaunchKernelGGL(pack_mx_kernel<MX_E2M1>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
     return launch_status();
@@ -172,7 +192,7 @@ extern "C" int mx_unpack_run(int f, const void* codes, const void* scales, int r
   if (rows < 1 || cols < 1 || rows > MX_MAX_DIM || cols > MX_MAX_DIM) return MX_ERR_SHAPE;
   if (!aligned16(codes) || !aligned16(scales) || !aligned16(out)) return MX_ERR_ALIGN;
   hipStream_t st = as_stream(stream);
-  if (f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1) {
+  if (f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M3 || f == MX_E3M2 || f == MX_E2M1) {
     if (cols % 32) return MX_ERR_SHAPE;
     if (int a = check_arch()) return a;
     const int64_t nquads = (int64_t)rows * cols / 4;
@@ -182,6 +202,10 @@ extern "C" int mx_unpack_run(int f, const void* codes, const void* scales, int r
       hipLaunchKernelGGL(unpack_mx_kernel<MX_E4M3>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
     else if (f == MX_E5M2)
       hipLaunchKernelGGL(unpack_mx_kernel<MX_E5M2>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
+    else if (f == MX_E2M3)
+      hipLaunchKernelGGL(unpack_mx_kernel<MX_E2M3>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
+    else if (f == MX_E3M2)
+      hipLaunchKernelGGL(unpack_mx_kernel<MX_E3M2>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
     else
       hipLaunchKernelGGL(unpack_mx_kernel<MX_E2M1>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
     return launch_status();

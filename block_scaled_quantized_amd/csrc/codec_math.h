@@ -8,6 +8,9 @@
 //   E4M3 "FN": s.eeee.mmm, bias 7, exponent 0 subnormal (m * 2^-9), s.1111.111 NaN, max 448.
 //   E5M2:      s.eeeee.mm, bias 15, exponent 0 subnormal (m * 2^-16), s.11111.00 Inf,
 //              s.11111.mm (m != 0) NaN, max 57344.
+//   E2M3:      s.ee.mmm (6 bits), bias 1, exponent 0 subnormal (m * 2^-3), max 7.5, no NaN/Inf.
+//   E3M2:      s.eee.mm (6 bits), bias 3, exponent 0 subnormal (m * 2^-4), max 28, no NaN/Inf.
+//              FP6 rows pack element j into bits 6j..6j+5 of a little-endian bit stream.
 //   E2M1:      s.ee.m, bias 1, exponent 0 subnormal (m * 0.5), max 6, no NaN.
 //   E8M0:      2^(e-127), 0xFF = NaN.
 // Encoding is round-to-nearest, ties to the even code, with saturation to the largest finite
@@ -70,6 +73,36 @@ MX_HD uint32_t e5m2_mag(uint32_t a, int t) {
   return rne_shift(sig, 7 - ev);                 // subnormal E5M2: multiples of 2^-16 (0..4)
 }
 
+// E2M3 magnitude code (0..31) of |x| * 2^t.
+MX_HD uint32_t e2m3_mag(uint32_t a, int t) {
+  if (a == 0u) return 0u;
+  int ev = ilog2_bits(a) + t;
+  uint32_t sig = norm_sig(a);
+  if (ev > 2 || (ev == 2 && sig >= 0xF00000u)) return 31u;     // >= 7.5: saturate
+  if (ev >= 0) {                                 // normal E2M3: 3 fraction bits
+    uint32_t r = rne_shift(sig, 20);
+    int e = ev;
+    if (r == 16u) { r = 8u; e++; }
+    return ((uint32_t)(e + 1) << 3) | (r - 8u);
+  }
+  return rne_shift(sig, 20 - ev);                // subnormal E2M3: multiples of 2^-3 (0..8)
+}
+
+// E3M2 magnitude code (0..31) of |x| * 2^t.
+MX_HD uint32_t e3m2_mag(uint32_t a, int t) {
+  if (a == 0u) return 0u;
+  int ev = ilog2_bits(a) + t;
+  uint32_t sig = norm_sig(a);
+  if (ev > 4 || (ev == 4 && sig >= 0xE00000u)) return 31u;     // >= 28: saturate
+  if (ev >= -2) {                                // normal E3M2: 2 fraction bits
+    uint32_t r = rne_shift(sig, 21);
+    int e = ev;
+    if (r == 8u) { r = 4u; e++; }
+    return ((uint32_t)(e + 3) << 2) | (r - 4u);
+  }
+  return rne_shift(sig, 19 - ev);                // subnormal E3M2: multiples of 2^-4 (0..4)
+}
+
 // E2M1 magnitude code (0..7) of |x| * 2^t.
 MX_HD uint32_t e2m1_mag(uint32_t a, int t) {
   if (a == 0u) return 0u;
@@ -85,14 +118,17 @@ MX_HD uint32_t e2m1_mag(uint32_t a, int t) {
   return rne_shift(sig, 22 - ev);                // subnormal E2M1: multiples of 0.5 (0..2)
 }
 
-// Element formats by their mx_format codes: E4M3 = 0, E5M2 = 1, E2M1 = 4.
+// Element formats by their mx_format codes: E4M3 = 0, E5M2 = 1, E2M3 = 2, E3M2 = 3, E2M1 = 4.
 constexpr bool is_byte_fmt(int fmt) { return fmt == MX_E4M3 || fmt == MX_E5M2; }
+constexpr bool is_fp6_fmt(int fmt) { return fmt == MX_E2M3 || fmt == MX_E3M2; }
 
 // Element code of x * 2^t with the sign of x kept, in format fmt.
 MX_HD uint32_t enc_elem_fmt(int fmt, float x, int t) {
   uint32_t u = fbits(x), a = u & 0x7FFFFFFFu, s = u >> 31;
   if (fmt == MX_E4M3) return (s << 7) | e4m3_mag(a, t);
   if (fmt == MX_E5M2) return (s << 7) | e5m2_mag(a, t);
+  if (fmt == MX_E2M3) return (s << 5) | e2m3_mag(a, t);
+  if (fmt == MX_E3M2) return (s << 5) | e3m2_mag(a, t);
   return (s << 3) | e2m1_mag(a, t);
 }
 
@@ -125,16 +161,30 @@ MX_HD float dec_e5m2(uint32_t b) {
   return bitsf(s | fbits((float)m * 1.52587890625e-05f));  // m * 2^-16, exact
 }
 
+MX_HD float dec_e2m3(uint32_t c) {
+  uint32_t s = (c & 0x20u) << 26, e = (c >> 3) & 3u, m = c & 7u;
+  if (e) return bitsf(s | ((e + 126u) << 23) | (m << 20));
+  return bitsf(s | fbits((float)m * 0.125f));
+}
+
+MX_HD float dec_e3m2(uint32_t c) {
+  uint32_t s = (c & 0x20u) << 26, e = (c >> 2) & 7u, m = c & 3u;
+  if (e) return bitsf(s | ((e + 124u) << 23) | (m << 21));
+  return bitsf(s | fbits((float)m * 0.0625f));
+}
+
 MX_HD float dec_e2m1(uint32_t n) {
   uint32_t s = (n & 8u) << 28, e = (n >> 1) & 3u, m = n & 1u;
   if (e) return bitsf(s | ((e + 126u) << 23) | (m << 22));
   return bitsf(s | (m ? 0x3F000000u : 0u));          // 0 or 0.5
 }
 
-// Element decoder by format (byte code for E4M3 / E5M2, nibble for E2M1).
+// Element decoder by format (byte code for E4M3 / E5M2, 6-bit code for E2M3 / E3M2, nibble for E2M1).
 MX_HD float dec_elem_fmt(int fmt, uint32_t c) {
   if (fmt == MX_E4M3) return dec_e4m3(c);
   if (fmt == MX_E5M2) return dec_e5m2(c);
+  if (fmt == MX_E2M3) return dec_e2m3(c & 63u);
+  if (fmt == MX_E3M2) return dec_e3m2(c & 63u);
   return dec_e2m1(c & 15u);
 }
 

@@ -9,12 +9,15 @@ using namespace mx;
 
 namespace {
 
-bool is_mx(int f) { return f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M1; }
+bool is_mx(int f) { return f == MX_E4M3 || f == MX_E5M2 || f == MX_E2M3 || f == MX_E3M2 || f == MX_E2M1; }
+
+// Row bytes of an MX row of n elements.
+int64_t mx_row_bytes(int f, int64_t n) { return is_byte_fmt(f) ? n : (is_fp6_fmt(f) ? n / 4 * 3 : n / 2); }
 bool is_int(int f) { return f == MX_INT8 || f == MX_INT4; }
 
 int pack_mx(int fmt, const float* src, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales) {
-  const bool byte = is_byte_fmt(fmt);
-  const int64_t rb = byte ? cols : cols / 2, nb = cols / 32;
+  const bool byte = is_byte_fmt(fmt), fp6 = is_fp6_fmt(fmt);
+  const int64_t rb = mx_row_bytes(fmt, cols), nb = cols / 32, bb = byte ? 32 : (fp6 ? 24 : 16);
   for (int64_t r = 0; r < rows; r++)
     for (int64_t b = 0; b < nb; b++) {
       const float* x = src + r * cols + 32 * b;
@@ -27,10 +30,18 @@ int pack_mx(int fmt, const float* src, int64_t rows, int64_t cols, uint8_t* code
       }
       int t;
       scales[r * nb + b] = (uint8_t)mx_block_scale(amax, nonfinite, fmt, &t);
-      uint8_t* out = codes + r * rb + (byte ? 32 * b : 16 * b);
-      if (nonfinite) { memset(out, 0, byte ? 32 : 16); continue; }
+      uint8_t* out = codes + r * rb + bb * b;
+      if (nonfinite) { memset(out, 0, (size_t)bb); continue; }
       if (byte) {
         for (int i = 0; i < 32; i++) out[i] = (uint8_t)enc_elem_fmt(fmt, x[i], t);
+      } else if (fp6) {  // 4 elements per 3 bytes, little-endian bit stream
+        for (int q = 0; q < 8; q++) {
+          uint32_t w = 0u;
+          for (int i = 0; i < 4; i++) w |= enc_elem_fmt(fmt, x[4 * q + i], t) << (6 * i);
+          out[3 * q] = (uint8_t)w;
+          out[3 * q + 1] = (uint8_t)(w >> 8);
+          out[3 * q + 2] = (uint8_t)(w >> 16);
+        }
       } else {
         for (int i = 0; i < 16; i++)
           out[i] = (uint8_t)(enc_elem_fmt(fmt, x[2 * i], t) | (enc_elem_fmt(fmt, x[2 * i + 1], t) << 4));
@@ -85,11 +96,16 @@ extern "C" int mx_unpack_host(int f, const void* codes_v, const void* scales_v, 
   if (is_mx(f)) {
     if (cols % 32) return MX_ERR_SHAPE;
     const uint8_t* sc = (const uint8_t*)scales_v;
-    const bool byte = is_byte_fmt(f);
-    const int64_t rb = byte ? cols : cols / 2;
+    const bool byte = is_byte_fmt(f), fp6 = is_fp6_fmt(f);
+    const int64_t rb = mx_row_bytes(f, cols);
     for (int64_t r = 0; r < rows; r++)
       for (int64_t c = 0; c < cols; c++) {
-        uint32_t code = byte ? codes[r * rb + c] : (codes[r * rb + c / 2] >> (4 * (c % 2))) & 0xFu;
+        uint32_t code;
+        if (byte) code = codes[r * rb + c];
+        else if (fp6) {
+          const uint8_t* g = codes + r * rb + 3 * (c / 4);  // the 3 bytes of c's group of 4
+          code = (((uint32_t)g[0] | ((uint32_t)g[1] << 8) | ((uint32_t)g[2] << 16)) >> (6 * (c % 4))) & 63u;
+        } else code = (codes[r * rb + c / 2] >> (4 * (c % 2))) & 0xFu;
         float v = dec_elem_fmt(f, code);
         out[r * cols + c] = v * dec_e8m0(sc[r * (cols / 32) + c / 32]);
       }
@@ -118,6 +134,8 @@ extern "C" float mx_decode_host(int f, uint8_t code) {
   switch (f) {
     case MX_E4M3: return dec_e4m3(code);
     case MX_E5M2: return dec_e5m2(code);
+    case MX_E2M3: return dec_e2m3(code & 63u);
+    case MX_E3M2: return dec_e3m2(code & 63u);
     case MX_E2M1: return dec_e2m1(code & 0xFu);
     case MX_INT8: return (float)(int8_t)code;
     case MX_INT4: return (float)((int)((code & 0xFu) ^ 8u) - 8);

@@ -709,7 +709,7 @@ int launch(const Args& a0, hipStream_t stream) {
 
 namespace mx {
 
-int gemm_ring_launch(int kind, int bn, bool e5a, bool e5b, const void* A, const void* SA, const void* B,
+int gemm_ring_launch(int kind, int bn, int fca, int fcb, const void* A, const void* SA, const void* B,
                      const void* SB, void* C, int M, int N, int K, bool relu, hipStream_t stream);
 
 // Tile configurations, indexed by the plan. Returns MX_ERR_FORMAT for an unknown id.
@@ -717,13 +717,14 @@ int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void
                 int N, int K, bool relu, hipStream_t stream) {
   // The other pairs run on the ring kernel only: 3: E4M3 A x E2M1 B, 4: E2M1 A x E4M3 B (256x256 or
   // 256x224 tiles); with E5M2 (256x256): 5: E5M2 x E5M2, 6: E4M3 x E5M2, 7: E5M2 x E4M3,
-  // 8: E5M2 x E2M1, 9: E2M1 x E5M2.
+  // 8: E5M2 x E2M1, 9: E2M1 x E5M2; FP6 (256x256): 10: E2M3 x E2M3, 11: E3M2 x E3M2, 12: E2M3 x E3M2,
+  // 13: E3M2 x E2M3.
   if (kind == 3 || kind == 4)
-    return gemm_ring_launch(kind - 1, tile_id == 9 ? 224 : 256, false, false, A, SA, B, SB, C, M, N, K, relu, stream);
-  if (kind >= 5 && kind <= 9) {
-    static const int rk[5] = {0, 0, 0, 2, 3};
-    static const bool ea[5] = {true, false, true, true, false}, eb[5] = {true, true, false, false, true};
-    return gemm_ring_launch(rk[kind - 5], 256, ea[kind - 5], eb[kind - 5], A, SA, B, SB, C, M, N, K, relu, stream);
+    return gemm_ring_launch(kind - 1, tile_id == 9 ? 224 : 256, 0, 0, A, SA, B, SB, C, M, N, K, relu, stream);
+  if (kind >= 5 && kind <= 13) {
+    static const int rk[9] = {0, 0, 0, 2, 3, 5, 5, 5, 5};
+    static const int fa[9] = {1, 0, 1, 1, 0, 2, 3, 2, 3}, fb[9] = {1, 1, 0, 0, 1, 2, 3, 3, 2};
+    return gemm_ring_launch(rk[kind - 5], 256, fa[kind - 5], fb[kind - 5], A, SA, B, SB, C, M, N, K, relu, stream);
   }
   Args a{};
   a.A = (const uint8_t*)A;
@@ -757,22 +758,22 @@ int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void
       return kind == KIND_E4M3 ? launch_pp<KIND_E4M3, 256, 224>(a, stream) : launch_pp<KIND_E2M1, 256, 224>(a, stream);
     case 8:  // 4-stage ring (N % 4 == 0; K % 512 == 0 E4M3, K % 1024 == 0 E2M1; fp16: N % 256 == 0,
              // K % 256 == 0, 2KN < 2^31); otherwise the 8-wave kernel
-      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(0, 256, false, false, A, SA, B, SB, C, M, N, K, relu, stream);
-      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(1, 256, false, false, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(0, 256, 0, 0, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(1, 256, 0, 0, A, SA, B, SB, C, M, N, K, relu, stream);
       if (kind == KIND_F16 && K % 256 == 0 && N % 256 == 0 && 2 * (int64_t)K * N < ((int64_t)1 << 31))
-        return gemm_ring_launch(4, 256, false, false, A, SA, B, SB, C, M, N, K, relu, stream);
+        return gemm_ring_launch(4, 256, 0, 0, A, SA, B, SB, C, M, N, K, relu, stream);
       if (kind == KIND_E4M3) return launch<KIND_E4M3, 256, 256, 4, 2>(a, stream);
       if (kind == KIND_E2M1) return launch<KIND_E2M1, 256, 256, 4, 2>(a, stream);
       return launch<KIND_F16, 256, 256, 4, 2>(a, stream);
     case 9:  // the same ring with 256x224 tiles; otherwise the 8-wave 256x224 kernel
-      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(0, 224, false, false, A, SA, B, SB, C, M, N, K, relu, stream);
-      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(1, 224, false, false, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(0, 224, 0, 0, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(1, 224, 0, 0, A, SA, B, SB, C, M, N, K, relu, stream);
       if (kind == KIND_E4M3) return launch<KIND_E4M3, 256, 224, 4, 2>(a, stream);
       if (kind == KIND_E2M1) return launch<KIND_E2M1, 256, 224, 4, 2>(a, stream);
       return launch<KIND_F16, 256, 224, 4, 2>(a, stream);
     case 10:  // the ring with 256x192 tiles (E4M3 / E2M1 on the ring's shapes); otherwise the 8-wave 256x256 kernel
-      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(0, 192, false, false, A, SA, B, SB, C, M, N, K, relu, stream);
-      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(1, 192, false, false, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(0, 192, 0, 0, A, SA, B, SB, C, M, N, K, relu, stream);
+      if (kind == KIND_E2M1 && K % 1024 == 0 && N % 4 == 0) return gemm_ring_launch(1, 192, 0, 0, A, SA, B, SB, C, M, N, K, relu, stream);
       if (kind == KIND_E4M3) return launch<KIND_E4M3, 256, 256, 4, 2>(a, stream);
       if (kind == KIND_E2M1) return launch<KIND_E2M1, 256, 256, 4, 2>(a, stream);
       return launch<KIND_F16, 256, 256, 4, 2>(a, stream);

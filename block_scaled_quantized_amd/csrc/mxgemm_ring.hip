@@ -70,7 +70,9 @@ struct RingTile {
 };
 
 // Per-format constants. KIND 0: E4M3 x E4M3, 1: E2M1 x E2M1, 2: E4M3 A x E2M1 B, 3: E2M1 A x E4M3 B,
-// 4: fp16 x fp16 (no scales).
+// 4: fp16 x fp16 (no scales), 5: FP6 x FP6 (E2M3 / E3M2: a stage row is 48 bytes in memory, copied
+// as four 12-byte pieces, one per 16-byte LDS chunk: a 12-byte direct copy writes lane i at 16 i,
+// measured).
 // A stage is one MFMA K-step of 64 elements (2 scale blocks), or for E2M1 x E2M1 two K-steps of
 // 64 (128 elements, 4 blocks) so that its rows are 64 bytes too. An operand's stage row is 64 bytes,
 // or 32 for the E2M1 side of a mixed pair. A group of 8 stages holds 16 or 32 scale bytes per row,
@@ -84,13 +86,17 @@ struct RingFmt {
   // templates, where it mishandles static constexpr members)
   enum : int {
     F16 = KIND == 4,                                   // fp16 x fp16: no scale plane
+    F6 = KIND == 5,                                    // FP6 x FP6: 48-byte stage rows in memory
+    CPY = F6 ? 12 : 16,                                // bytes per lane of a stage copy
+    CPYB = 1024,                                       // LDS bytes of one copy instruction
     A4 = KIND == 1 || KIND == 3, B4 = KIND == 1 || KIND == 2,  // E2M1 operands
     FP4 = KIND == 1,                                   // both E2M1: two K-steps per stage, two scale planes
     KSTEPS = FP4 || F16 ? 2 : 1,                       // MFMA K-steps per stage
     ELEMS = F16 ? 32 : 64 * KSTEPS,                    // K elements per stage
-    SRB_A = A4 && !FP4 ? 32 : 64, SRB_B = B4 && !FP4 ? 32 : 64,  // stage bytes per row (fp16 B: per 16 columns)
-    NI_A = BM * SRB_A / 1024,                          // 1 KB copy instructions per stage for A (16 / 8)
-    NI_B = 256 * SRB_B / 1024,                         // ... and for B (room for 256 rows / columns)
+    SRB_A = A4 && !FP4 ? 32 : 64, SRB_B = B4 && !FP4 ? 32 : 64,  // LDS bytes per stage row (fp16 B: per 16 columns)
+    GSB_A = F6 ? 48 : SRB_A, GSB_B = F6 ? 48 : SRB_B,  // bytes per stage row in memory
+    NI_A = BM * SRB_A / CPYB,                          // copy instructions per stage for A (16 / 8)
+    NI_B = 256 * SRB_B / CPYB,                         // ... and for B (room for 256 rows / columns)
     DPS = (NI_A + NI_B) / 4,                           // copies per wave per stage (8 or 6)
     CBSZ = B4 ? 4 : 0, BLGP = A4 ? 4 : 0,              // MFMA formats of the B and A operands
     SGRP = F16 ? 16 : 512 * 16 * KSTEPS,               // scale array: 8 / 16 KB (fp16: unused)
@@ -115,7 +121,7 @@ template <int KIND, class T>
 struct RingCopies {
   enum : int {
     NI_A = RingFmt<KIND>::NI_A,
-    NI_B0 = (T::BN * RingFmt<KIND>::SRB_B + 1023) / 1024,
+    NI_B0 = (T::BN * RingFmt<KIND>::SRB_B + RingFmt<KIND>::CPYB - 1) / RingFmt<KIND>::CPYB,
     NI_B = (NI_A + NI_B0 + 3) / 4 * 4 - NI_A,
     DPS = (NI_A + NI_B) / 4
   };
@@ -231,6 +237,16 @@ MX_DEV void pack_scales(const RawScales<KIND, T>& r, Scales<KIND, T>& s, int d, 
 // A fragment of one stage. 64-byte rows: chunks h and 2+h, i.e. the lane's K bytes of the E4M3
 // MFMA, or its 16 bytes (K-block h) of E2M1 K-steps 0 and 1 in the low and high halves. 32-byte rows
 // (the E2M1 side of a mixed pair): chunk h, the lane's 16 bytes, in the low half.
+// FP6 fragment: the lane's 32 elements (K-block h) are the 24 bytes 24h.. of its 48-byte row, i.e.
+// pieces 2h and 2h+1 (12 bytes each) of the row's four 16-byte chunks.
+typedef int v3i __attribute__((ext_vector_type(3)));
+MX_DEV v8i read_frag6(const char* region, int row, int h) {
+  const v3i lo = *reinterpret_cast<const v3i*>(region + phys_off<64>(row, 2 * h));
+  const v3i hi = *reinterpret_cast<const v3i*>(region + phys_off<64>(row, 2 * h + 1));
+  const v4i a = __builtin_shufflevector(lo, lo, 0, 1, 2, -1), b = __builtin_shufflevector(hi, hi, 0, 1, 2, -1);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 4, 5, 6, -1, -1);
+}
+
 template <int SRB>
 MX_DEV v8i read_frag(const char* region, int row, int h) {
   if constexpr (SRB == 64)
@@ -280,8 +296,8 @@ MX_DEV uint32_t stage_soff(const Ctx& c, bool qa, uint32_t stage) {
   using F = RingFmt<KIND>;
   uint32_t step_b;
   if constexpr (F::F16) step_b = c.bstage;
-  else step_b = (uint32_t)F::SRB_B;
-  return (qa ? (uint32_t)F::SRB_A : step_b) * stage;
+  else step_b = (uint32_t)F::GSB_B;
+  return (qa ? (uint32_t)F::GSB_A : step_b) * stage;
 }
 
 // Scale copy k of this wave: 64 rows (A rows 64(wave) + l for even k, B rows for odd k), 16 bytes
@@ -363,13 +379,20 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
       const bool qa = q < F::NI_A / 4;
       const uint32_t vo = qa ? c.voff_a : c.voff_b;
       const uint32_t so = stage_soff<KIND>(c, qa, fill_stage);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[q], (lds_ptr_t)(slot_fill + (c.wave + 4 * q) * 1024), 16, vo,
-                                               so, 0, 0);
+      if constexpr (F::F6)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[q], (lds_ptr_t)(slot_fill + (c.wave + 4 * q) * 1024), 12, vo,
+                                                 so, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[q], (lds_ptr_t)(slot_fill + (c.wave + 4 * q) * 1024), 16, vo,
+                                                 so, 0, 0);
     }
     // and of the next stage's fragments: list positions [F*i/FB, F*(i+1)/FB) of A0.., B0..
 #pragma unroll
     for (int f = T::F * i / T::FB; f < T::F * (i + 1) / T::FB; f++) {
-      if (f < T::FA) na[f] = read_frag<F::SRB_A>(slot_nxt, row_a<T>(f, c.wm, c.r32), c.h);
+      if constexpr (F::F6) {
+        if (f < T::FA) na[f] = read_frag6(slot_nxt, row_a<T>(f, c.wm, c.r32), c.h);
+        else nb[f - T::FA] = read_frag6(slot_nxt + BM * F::SRB_A, row_b<T>(f - T::FA, c.wn, c.r32), c.h);
+      } else if (f < T::FA) na[f] = read_frag<F::SRB_A>(slot_nxt, row_a<T>(f, c.wm, c.r32), c.h);
       else if constexpr (F::F16) nb[f - T::FA] = read_frag_bt(slot_nxt + BM * F::SRB_A, c.bt_off[f - T::FA]);
       else nb[f - T::FA] = read_frag<F::SRB_B>(slot_nxt + BM * F::SRB_A, row_b<T>(f - T::FA, c.wn, c.r32), c.h);
     }
@@ -408,8 +431,8 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
   // row bytes (fp16 B: a K-row of N columns)
-  const uint32_t RBA = F::F16 ? 2u * (uint32_t)p.K : (uint32_t)p.K / (F::A4 ? 2 : 1);
-  const uint32_t RBB = F::F16 ? 2u * (uint32_t)p.N : (uint32_t)p.K / (F::B4 ? 2 : 1);
+  const uint32_t RBA = F::F16 ? 2u * (uint32_t)p.K : F::F6 ? (uint32_t)p.K / 4u * 3u : (uint32_t)p.K / (F::A4 ? 2 : 1);
+  const uint32_t RBB = F::F16 ? 2u * (uint32_t)p.N : F::F6 ? (uint32_t)p.K / 4u * 3u : (uint32_t)p.K / (F::B4 ? 2 : 1);
   const uint32_t nblk = (uint32_t)p.K / 32;                                                   // K-blocks
   const int nst = p.K / F::ELEMS, ngroups = nst / GROUP;
 
@@ -437,6 +460,11 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   const uint32_t off64 = 16u * ((l & 3) ^ ((l >> 4) & 3)), off32 = 16u * ((l & 1) ^ ((l >> 4) & 1));
   c.voff_a = F::SRB_A == 64 ? (l >> 2) * RBA + off64 : (l >> 1) * RBA + off32;
   c.voff_b = F::SRB_B == 64 ? (l >> 2) * RBB + off64 : (l >> 1) * RBB + off32;
+  if constexpr (F::F6) {  // lane l fills chunk l%4 of row l/4 with 12-byte piece (l%4) ^ ((l/16) & 3)
+    const uint32_t pc = 12u * ((l & 3) ^ ((l >> 4) & 3));
+    c.voff_a = (l >> 2) * RBA + pc;
+    c.voff_b = (l >> 2) * RBB + pc;
+  }
   c.bstage = 32u * RBB;
   if constexpr (F::F16) {
     c.voff_b = (l >> 5) * RBB + 16u * ((l & 31) ^ (8u * ((uint32_t)wave & 1) + 4u * (l >> 5)));
@@ -451,7 +479,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   for (int k = 0; k < CP::DPS; k++) {
     const int i = wave + 4 * k;
     const bool isA = k < F::NI_A / 4;
-    const int rpi = (isA ? F::SRB_A : F::SRB_B) == 64 ? 16 : 32;  // rows per instruction
+    const int rpi = F::CPYB / (isA ? F::SRB_A : F::SRB_B);  // rows per instruction (16 or 32)
     const int r0 = rpi * (isA ? i : i - F::NI_A), rows = isA ? rows_a : rows_b;
     const uint32_t rb = isA ? RBA : RBB;
     const int nr = max(0, min(rpi, rows - r0));
@@ -493,8 +521,10 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
       const bool qa = k < F::NI_A / 4;
       const uint32_t vo = qa ? c.voff_a : c.voff_b;
       const uint32_t so = stage_soff<KIND>(c, qa, (uint32_t)t);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(slot + (wave + 4 * k) * 1024), 16, vo, so, 0,
-                                               0);
+      if constexpr (F::F6)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(slot + (wave + 4 * k) * 1024), 12, vo, so, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(slot + (wave + 4 * k) * 1024), 16, vo, so, 0, 0);
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): prologue copies of this wave
@@ -509,10 +539,14 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
     pack_scales<KIND, T>(raw, sc, 1, h);
   }
 #pragma unroll
-  for (int j = 0; j < T::FA; j++) xa[j] = read_frag<F::SRB_A>(slot0, row_a<T>(j, wm, r32), h);
+  for (int j = 0; j < T::FA; j++) {
+    if constexpr (F::F6) xa[j] = read_frag6(slot0, row_a<T>(j, wm, r32), h);
+    else xa[j] = read_frag<F::SRB_A>(slot0, row_a<T>(j, wm, r32), h);
+  }
 #pragma unroll
   for (int i = 0; i < T::FB; i++) {
-    if constexpr (F::F16) xb[i] = read_frag_bt(slot0 + BM * F::SRB_A, c.bt_off[i]);
+    if constexpr (F::F6) xb[i] = read_frag6(slot0 + BM * F::SRB_A, row_b<T>(i, wn, r32), h);
+    else if constexpr (F::F16) xb[i] = read_frag_bt(slot0 + BM * F::SRB_A, c.bt_off[i]);
     else xb[i] = read_frag<F::SRB_B>(slot0 + BM * F::SRB_A, row_b<T>(i, wn, r32), h);
   }
 
@@ -600,9 +634,10 @@ namespace mx {
 // Ring kernels. kind 0: E4M3 x E4M3, 1: E2M1 x E2M1, 2: E4M3 A x E2M1 B, 3: E2M1 A x E4M3 B,
 // 4: fp16 x fp16 (B K x N). Requires N % 4 == 0 and K % 512 == 0 (K % 1024 == 0 for kind 1); for
 // kind 4 N % 256 == 0, K % 256 == 0 and 2*K*N < 2^31, bn = 256 only. Checked by the caller.
-// bn = 256, 224 or 192 (192: kinds 0 and 1). e5a / e5b: the byte-format A / B operand is E5M2
-// instead of E4M3 (kinds 0, 2 (A) and 3 (B); 256 x 256 tiles only).
-int gemm_ring_launch(int kind, int bn, bool e5a, bool e5b, const void* A, const void* SA, const void* B,
+// bn = 256, 224 or 192 (192: kinds 0 and 1). fca / fcb: the MFMA format code of the A / B operand
+// where it is a byte or FP6 operand: 0 E4M3, 1 E5M2 (kinds 0, 2 (A), 3 (B)), 2 E2M3, 3 E3M2
+// (kind 5); other than 0 only with 256 x 256 tiles. Returns MX_ERR_FORMAT for other combinations.
+int gemm_ring_launch(int kind, int bn, int fca, int fcb, const void* A, const void* SA, const void* B,
                      const void* SB, void* C, int M, int N, int K, bool relu, hipStream_t stream) {
   Args a{};
   a.A = (const uint8_t*)A;
@@ -619,7 +654,8 @@ int gemm_ring_launch(int kind, int bn, bool e5a, bool e5b, const void* A, const 
   const dim3 grid((unsigned)tiles), block(256);
 #define MX_RING(KD, WM, BNT, FA8, FB8) \
   hipLaunchKernelGGL((gemm_ring_kernel<KD, WM, BNT, FA8, FB8>), grid, block, 0, stream, a)
-  if (bn == 224) {
+  const bool plain = fca == 0 && fcb == 0;  // E4M3 for every byte operand
+  if (bn == 224 && plain) {
     switch (kind) {
       case 0: MX_RING(0, 4, 224, 0, 0); break;
       case 1: MX_RING(1, 4, 224, 0, 0); break;
@@ -627,18 +663,26 @@ int gemm_ring_launch(int kind, int bn, bool e5a, bool e5b, const void* A, const 
       case 3: MX_RING(3, 4, 224, 0, 0); break;
       default: return MX_ERR_FORMAT;
     }
-  } else if (bn == 192) {
+  } else if (bn == 192 && plain) {
     switch (kind) {
       case 0: MX_RING(0, 2, 192, 0, 0); break;
       case 1: MX_RING(1, 2, 192, 0, 0); break;
       default: return MX_ERR_FORMAT;
     }
-  } else if (e5a || e5b) {  // E5M2 operands: 256 x 256 tiles
-    if (kind == 0 && e5a && e5b) MX_RING(0, 2, 256, 1, 1);
-    else if (kind == 0 && e5b) MX_RING(0, 2, 256, 0, 1);
-    else if (kind == 0) MX_RING(0, 2, 256, 1, 0);
-    else if (kind == 2 && e5a) MX_RING(2, 2, 256, 1, 0);
-    else if (kind == 3 && e5b) MX_RING(3, 2, 256, 0, 1);
+  } else if (bn != 256) {
+    return MX_ERR_FORMAT;
+  } else if (kind == 5) {  // FP6 pairs: codes 2 (E2M3) / 3 (E3M2)
+    if (fca == 2 && fcb == 2) MX_RING(5, 2, 256, 2, 2);
+    else if (fca == 3 && fcb == 3) MX_RING(5, 2, 256, 3, 3);
+    else if (fca == 2 && fcb == 3) MX_RING(5, 2, 256, 2, 3);
+    else if (fca == 3 && fcb == 2) MX_RING(5, 2, 256, 3, 2);
+    else return MX_ERR_FORMAT;
+  } else if (!plain) {  // E5M2 (code 1) byte operands
+    if (kind == 0 && fca == 1 && fcb == 1) MX_RING(0, 2, 256, 1, 1);
+    else if (kind == 0 && fca == 0 && fcb == 1) MX_RING(0, 2, 256, 0, 1);
+    else if (kind == 0 && fca == 1 && fcb == 0) MX_RING(0, 2, 256, 1, 0);
+    else if (kind == 2 && fca == 1) MX_RING(2, 2, 256, 1, 0);
+    else if (kind == 3 && fcb == 1) MX_RING(3, 2, 256, 0, 1);
     else return MX_ERR_FORMAT;
   } else {
     switch (kind) {
@@ -646,7 +690,8 @@ int gemm_ring_launch(int kind, int bn, bool e5a, bool e5b, const void* A, const 
       case 1: MX_RING(1, 2, 256, 0, 0); break;
       case 2: MX_RING(2, 2, 256, 0, 0); break;
       case 3: MX_RING(3, 2, 256, 0, 0); break;
-      default: MX_RING(4, 2, 256, 0, 0); break;
+      case 4: MX_RING(4, 2, 256, 0, 0); break;
+      default: return MX_ERR_FORMAT;
     }
   }
 #undef MX_RING

@@ -3,8 +3,8 @@
 //
 // MX blocks (32 consecutive elements along K share one E8M0 scale: "TensorOps ... notes",
 // section "Scale planes"; WWDC26 session 330 summary, auxiliary scale plane with blockFactors
-// {32,1}): E = clamp(floor(log2 amax) - emax + 127, 0, 254), emax = 8 for E4M3, 15 for E5M2 and 2
-// for E2M1 (the exponent of the format's largest element),
+// {32,1}): E = clamp(floor(log2 amax) - emax + 127, 0, 254), emax = 8 for E4M3, 15 for E5M2, 2 for
+// E2M3, 4 for E3M2 and 2 for E2M1 (the exponent of the format's largest element),
 // elements encoded as x * 2^(127-E). A block holding Inf/NaN gets E = 0xFF and zero codes.
 //
 // Integer weight blocks (32 rows of one column share one fp16 scale: the per-block fp16 scales of
@@ -31,7 +31,7 @@ MX_HD float rint_even(float x) {
 #endif
 }
 
-constexpr int emax_of(int fmt) { return fmt == MX_E4M3 ? 8 : (fmt == MX_E5M2 ? 15 : 2); }
+constexpr int emax_of(int fmt) { return fmt == MX_E4M3 ? 8 : fmt == MX_E5M2 ? 15 : fmt == MX_E3M2 ? 4 : 2; }
 
 // Scale code and exponent offset t = 127 - E of one MX block (element format fmt) from its amax
 // bit pattern and a non-finite flag. Returns the scale code; *t receives the offset.

@@ -18,6 +18,8 @@
  *  - MX_E4M3: FP8 E4M3 "FN" (bias 7, S.1111.111 = NaN, no Inf, max 448), one byte per element.
  *  - MX_E5M2: FP8 E5M2 (bias 15, S.11111.00 = Inf, S.11111.xx = NaN, max 57344), one byte per
  *    element (the pages' fp8 / "MX scaling formats", TensorOps notes, quantized dtype matrix).
+ *  - MX_E2M3 / MX_E3M2: FP6 (bias 1, max 7.5 / bias 3, max 28; no Inf or NaN), four elements per
+ *    three bytes: element j in bits 6j..6j+5 of the row read as a little-endian bit stream.
  *  - MX_E2M1: FP4 E2M1 (bias 1, +-{0,.5,1,1.5,2,3,4,6}), two elements per byte, the element with
  *    the even index in the low nibble.
  *  - Scales of MX operands: E8M0 bytes, value 2^(e-127), 0xFF = NaN; one scale per 32
@@ -49,7 +51,7 @@ typedef enum {
 } mx_status;
 
 /* MX_E8M0 names the scale format; it is accepted only by mx_decode_host. */
-typedef enum { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M1 = 4, MX_E8M0 = 8, MX_F16 = 16, MX_INT8 = 32, MX_INT4 = 33 } mx_format;
+typedef enum { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M3 = 2, MX_E3M2 = 3, MX_E2M1 = 4, MX_E8M0 = 8, MX_F16 = 16, MX_INT8 = 32, MX_INT4 = 33 } mx_format;
 
 /* Largest accepted dimension of any matrix (rows or columns). */
 #define MX_MAX_DIM (1 << 20)

@@ -37,7 +37,7 @@ def edge_rows(cols, seed):
     return x.astype(np.float32)
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 4])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("case", ["normal1", "normal002", "edges", "prefill_rows"])
 def test_mx_pack_unpack_bitexact(orc, fmt, case):
     api = require_gpu()
@@ -60,7 +60,7 @@ def test_mx_pack_unpack_bitexact(orc, fmt, case):
     assert bitequal_f32(host(out), orc.dequant(fmt, oc, os_, rows, cols))
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 4])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 def test_mx_unpack_every_code_and_scale(orc, fmt):
     api = require_gpu()
     say(f"mx unpack exhaustive fmt={fmt}")
@@ -69,7 +69,11 @@ def test_mx_unpack_every_code_and_scale(orc, fmt):
     cols = 256 if byte else 512
     per_row = np.arange(256, dtype=np.uint8)
     codes = np.tile(per_row, (256, 1))
-    codes = np.ascontiguousarray(codes[:, : (cols if byte else cols // 2)])
+    if fmt in (2, 3):   # every 6-bit code, 8 times per row, packed as the little-endian bit stream
+        fields = np.tile(np.arange(64, dtype=np.uint8), cols // 64)
+        bits = ((fields[:, None] >> np.arange(6)) & 1).astype(np.uint8).reshape(-1)
+        codes = np.tile(np.packbits(bits, bitorder="little"), (256, 1))
+    codes = np.ascontiguousarray(codes[:, : (cols if byte else (cols // 4 * 3 if fmt in (2, 3) else cols // 2))])
     scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], cols // 32, axis=1)
     out = empty((256, cols), torch.float32)
     api.mx_unpack_run(fmt, dev(codes), dev(scales), 256, cols, out)

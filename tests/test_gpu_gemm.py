@@ -279,6 +279,50 @@ def test_mx_e5m2_pairs(orc, fa, fb, M, N, K):
     assert ok, (ratio, bad)
 
 
+@pytest.mark.parametrize("fa,fb", [(2, 2), (3, 3), (2, 3), (3, 2)])
+@pytest.mark.parametrize("M,N,K", [(300, 520, 512), (257, 260, 1536), (64, 1028, 1024)])
+def test_mx_fp6_pairs(orc, fa, fb, M, N, K):
+    """FP6 pairs (E2M3 / E3M2, 48-byte stage rows) on the ring, every output: the GPU's FP6 pack must
+    equal the oracle's, and the product must meet the bound."""
+    api = require_gpu()
+    say(f"mx fp6 fa={fa} fb={fb} M={M} N={N} K={K}")
+    a_src = synth.normal((M, K), 1.0, 900 + M + K)
+    b_src = synth.normal((N, K), 0.02, 901 + N + K)
+    A, SA = gpu_mx_pack(api, fa, a_src)
+    B, SB = gpu_mx_pack(api, fb, b_src)
+    oA, oSA = orc.mx_quantize(fa, a_src)
+    oB, oSB = orc.mx_quantize(fb, b_src)
+    assert np.array_equal(host(A), oA) and np.array_equal(host(SA), oSA)
+    assert np.array_equal(host(B), oB) and np.array_equal(host(SB), oSB)
+    C = gpu_gemm(api, fa, A, SA, B, SB, M, N, K, fb=fb)
+    ref = orc.mxgemm(fa, fb, oA, oSA, oB, oSB, M, N, K)
+    R = orc.rms_ab(orc.dequant(fa, oA, oSA, M, K), orc.dequant(fb, oB, oSB, N, K).T)
+    ok, ratio, bad = orc.check(C, ref, K, R)
+    assert ok, (ratio, bad)
+
+
+def test_mx_fp6_unit_scales_exact(orc):
+    """E2M3 x E3M2 at unit scales: every product is a multiple of 2^-7 of magnitude at most 210, so
+    with K=512 every partial sum is below 2^17 and exact in fp32: the GPU must equal the oracle
+    after the fp16 rounding."""
+    api = require_gpu()
+    M, N, K = 256, 512, 512
+    say("mx fp6 unit scales exact")
+    g = np.random.Generator(np.random.PCG64(911))
+
+    def pack(codes):
+        bits = ((codes[..., None] >> np.arange(6)) & 1).astype(np.uint8).reshape(codes.shape[0], -1)
+        return np.ascontiguousarray(np.packbits(bits, axis=1, bitorder="little"))
+    ca, cb = g.integers(0, 64, (M, K)), g.integers(0, 64, (N, K))
+    SA = np.full((M, K // 32), 127, np.uint8)
+    SB = np.full((N, K // 32), 127, np.uint8)
+    A, B = pack(ca), pack(cb)
+    C = gpu_gemm(api, 2, dev(A), dev(SA), dev(B), dev(SB), M, N, K, fb=3)
+    ref = orc.mxgemm(2, 3, A, SA, B, SB, M, N, K)
+    assert np.abs(ref).max() < 60000
+    assert np.array_equal(C, ref.astype(np.float16).astype(np.float64))
+
+
 def test_mx_e5m2_unit_scales_exact(orc):
     """E5M2 x E5M2 at unit scales on codes whose products and sums are exact in fp32: the GPU must
     equal the oracle (its plain fp8 matmul) after the fp16 rounding, output for output."""

@@ -45,6 +45,10 @@ def test_host_element_codec_all_codes(orc):
         e = api.mx_decode_host(api.MX_E8M0, code)
         r = orc.dec_e8m0([code])[0]
         assert (np.isnan(e) and np.isnan(r)) or e == r
+    for code in range(64):
+        for f, dec in ((api.MX_E2M3, orc.dec_e2m3), (api.MX_E3M2, orc.dec_e3m2)):
+            a, b = api.mx_decode_host(f, code), dec([code])[0]
+            assert a == b and np.signbit(a) == np.signbit(b)
     for code in range(16):
         assert api.mx_decode_host(api.MX_E2M1, code) == orc.dec_e2m1([code])[0]
         assert api.mx_decode_host(api.MX_INT4, code) == orc.dec_int4([code])[0]
@@ -57,6 +61,8 @@ def test_host_element_codec_all_codes(orc):
         assert api.mx_encode_host(api.MX_E4M3, float(v)) == orc.enc_elem(0, [float(v)])[0], v
         assert api.mx_encode_host(api.MX_E2M1, float(v)) == orc.enc_elem(4, [float(v)])[0], v
         assert api.mx_encode_host(api.MX_E5M2, float(v)) == orc.enc_elem(1, [float(v)])[0], v
+        assert api.mx_encode_host(api.MX_E2M3, float(v)) == orc.enc_elem(2, [float(v)])[0], v
+        assert api.mx_encode_host(api.MX_E3M2, float(v)) == orc.enc_elem(3, [float(v)])[0], v
 
 
 def _edge_rows(cols, seed):
@@ -74,7 +80,7 @@ def _edge_rows(cols, seed):
     return x.astype(np.float32)
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 4])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 def test_host_mx_pack_matches_oracle(orc, fmt):
     cols = 256
     for seed, x in [(1, synth.normal((96, cols), 1.0, 1)), (2, synth.normal((64, cols), 0.02, 2)), (3, _edge_rows(cols, 3))]:
@@ -197,11 +203,12 @@ def test_ring_tile_plan_info(monkeypatch):
 
 
 def test_e5m2_pairs_plan(monkeypatch):
-    """Every pair with an E5M2 operand is accepted where the ring applies (K % 512 == 0,
+    """Every pair with an E5M2 operand, and the FP6 pairs, is accepted where the ring applies (K % 512 == 0,
     N % 4 == 0), runs the 256x256 ring whatever the override, and is refused with MX_ERR_SHAPE
     elsewhere."""
     pairs = ((api.MX_E5M2, api.MX_E5M2), (api.MX_E4M3, api.MX_E5M2), (api.MX_E5M2, api.MX_E4M3),
-             (api.MX_E5M2, api.MX_E2M1), (api.MX_E2M1, api.MX_E5M2))
+             (api.MX_E5M2, api.MX_E2M1), (api.MX_E2M1, api.MX_E5M2), (api.MX_E2M3, api.MX_E2M3),
+             (api.MX_E3M2, api.MX_E3M2), (api.MX_E2M3, api.MX_E3M2), (api.MX_E3M2, api.MX_E2M3))
     for tile in (None, "9", "10", "4"):
         if tile is None:
             monkeypatch.delenv("MXGEMM_TILE", raising=False)
@@ -218,6 +225,7 @@ def test_e5m2_pairs_plan(monkeypatch):
     lib = api._lib
     h = ctypes.c_void_p()
     assert lib.mxgemm_create(ctypes.byref(h), 64, 64, 512, api.MX_E5M2, api.MX_F16, 0) == api.MX_ERR_FORMAT
+    assert lib.mxgemm_create(ctypes.byref(h), 64, 64, 512, api.MX_E2M3, api.MX_E4M3, 0) == api.MX_ERR_FORMAT
     assert lib.mxgemm_create(ctypes.byref(h), 64, 64, 512, api.MX_E5M2, api.MX_E5M2, 0) == 0
     assert lib.mxgemm_destroy(h) == 0
 
