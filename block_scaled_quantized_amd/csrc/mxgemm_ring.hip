@@ -182,10 +182,12 @@ MX_DEV v4i lds16(const char* base, int off) { return *reinterpret_cast<const v4i
 // (stage s, K-step k, block b) at byte 4(s%4) + 2k + b. Half d of a row covers stages 4d..4d+3
 // and becomes dwords d*KSTEPS.. of the lane's packed scales, keeping its own block h: from each 8
 // source bytes, bytes h, 2+h, 4+h, 6+h. Stages 0-3 of a group use the dwords of half 0 and stages
-// 4-7 those of half 1, so the next group's half 0 is read during stage 4 and packed at the end of
-// stage 6, and its half 1 is read after the last MFMA of stage 7 and packed at the end of the next
-// group's stage 2: the reads have a stage or more to land before anything waits for them. The
-// packed value of stage 2 is unchanged in group 0, whose halves the prologue packs.
+// 4-7 those of half 1, so both halves of the next group are read during stage 4 (into separate
+// registers); half 0 is packed at the end of stage 6 and half 1 at the end of the next group's
+// stage 2: the reads have a stage or more to land before anything waits for them. (An LDS read
+// placed after the last stage of a group lands at the loop head, where the compiler makes it wait
+// for every direct copy in flight.) The packed value of stage 2 is unchanged in group 0, whose
+// halves the prologue packs.
 template <int KIND>
 struct RawT {
   typedef int type __attribute__((ext_vector_type(2 * RingFmt<KIND>::KSTEPS)));
@@ -323,7 +325,8 @@ MX_DEV void issue_scales(const Ctx& c, char* sg, int g) {
 template <int KIND, class T, int S8, int F8A, int F8B>
 MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], const v8i (&cb)[T::FB],
                        v8i (&na)[T::FA], v8i (&nb)[T::FB], const char* slot_nxt, char* slot_fill,
-                       Scales<KIND, T>& sc, RawScales<KIND, T>& raw, v16f (&acc)[T::FB][T::FA]) {
+                       Scales<KIND, T>& sc, RawScales<KIND, T>& raw, RawScales<KIND, T>& raw1,
+                       v16f (&acc)[T::FB][T::FA]) {
   using F = RingFmt<KIND>;
   using CP = RingCopies<KIND, T>;
   using MF = RingMfma<KIND, F8A, F8B>;
@@ -397,13 +400,15 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
       else nb[f - T::FA] = read_frag<F::SRB_B>(slot_nxt + BM * F::SRB_A, row_b<T>(f - T::FA, c.wn, c.r32), c.h);
     }
     if constexpr (!F::F16)
-      if (S8 == 4 && i == 1) read_raw_scales<KIND, T>(sgrp, raw, 0, c.wm, c.wn, c.r32);
+      if (S8 == 4 && i == 1) {
+        read_raw_scales<KIND, T>(sgrp, raw, 0, c.wm, c.wn, c.r32);
+        read_raw_scales<KIND, T>(sgrp, raw1, 1, c.wm, c.wn, c.r32);
+      }
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (!F::F16) {
-    if (S8 == 2) pack_scales<KIND, T>(raw, sc, 1, c.h);
+    if (S8 == 2) pack_scales<KIND, T>(raw1, sc, 1, c.h);
     if (S8 == 6) pack_scales<KIND, T>(raw, sc, 0, c.h);
-    if (S8 == GROUP - 1) read_raw_scales<KIND, T>(sgrp, raw, 1, c.wm, c.wn, c.r32);
   }
 }
 
@@ -531,12 +536,12 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   raw_barrier();
   v8i xa[T::FA], xb[T::FB], ya[T::FA], yb[T::FB];
   Scales<KIND, T> sc;
-  RawScales<KIND, T> raw;
+  RawScales<KIND, T> raw, raw1;
   if constexpr (!F::F16) {
     read_raw_scales<KIND, T>(sgrp, raw, 0, wm, wn, r32);
     pack_scales<KIND, T>(raw, sc, 0, h);
-    read_raw_scales<KIND, T>(sgrp, raw, 1, wm, wn, r32);
-    pack_scales<KIND, T>(raw, sc, 1, h);
+    read_raw_scales<KIND, T>(sgrp, raw1, 1, wm, wn, r32);
+    pack_scales<KIND, T>(raw1, sc, 1, h);
   }
 #pragma unroll
   for (int j = 0; j < T::FA; j++) {
@@ -552,14 +557,14 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
 
   // Stage t uses slot t%4 (t = 8g + s: slot s%4); even stages compute from x*, odd from y*.
   for (int g = 0; g < ngroups; g++) {
-    ring_stage<KIND, T, 0, F8A, F8B>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, acc);
-    ring_stage<KIND, T, 1, F8A, F8B>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, acc);
-    ring_stage<KIND, T, 2, F8A, F8B>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, acc);
-    ring_stage<KIND, T, 3, F8A, F8B>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
-    ring_stage<KIND, T, 4, F8A, F8B>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, acc);
-    ring_stage<KIND, T, 5, F8A, F8B>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, acc);
-    ring_stage<KIND, T, 6, F8A, F8B>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, acc);
-    ring_stage<KIND, T, 7, F8A, F8B>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, acc);
+    ring_stage<KIND, T, 0, F8A, F8B>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, raw1, acc);
+    ring_stage<KIND, T, 1, F8A, F8B>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, raw1, acc);
+    ring_stage<KIND, T, 2, F8A, F8B>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, raw1, acc);
+    ring_stage<KIND, T, 3, F8A, F8B>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, raw1, acc);
+    ring_stage<KIND, T, 4, F8A, F8B>(c, g, sgrp, xa, xb, ya, yb, slot1, slot3, sc, raw, raw1, acc);
+    ring_stage<KIND, T, 5, F8A, F8B>(c, g, sgrp, ya, yb, xa, xb, slot2, slot0, sc, raw, raw1, acc);
+    ring_stage<KIND, T, 6, F8A, F8B>(c, g, sgrp, xa, xb, ya, yb, slot3, slot1, sc, raw, raw1, acc);
+    ring_stage<KIND, T, 7, F8A, F8B>(c, g, sgrp, ya, yb, xa, xb, slot0, slot2, sc, raw, raw1, acc);
   }
 
   // The last stages queued copies of stage nst-1 into free slots: let them land, and let every
