@@ -314,6 +314,35 @@ MX_DEV void issue_scales(const Ctx& c, char* sg, int g) {
                                              goff + 16 * (k >> 1), 0, 0);
 }
 
+// Stage copy q of this wave (copy q is an A copy when q < NI_A/4) into the slot being filled.
+template <int KIND>
+MX_DEV void stage_copy(const Ctx& c, int q, char* slot_fill, uint32_t fill_stage) {
+  using F = RingFmt<KIND>;
+  // (offsets computed into locals first: the host pass of hipcc drops the kernel, silently, when
+  // these builtin arguments are written as conditional expressions of the format constants)
+  const bool qa = q < F::NI_A / 4;
+  const uint32_t vo = qa ? c.voff_a : c.voff_b;
+  const uint32_t so = stage_soff<KIND>(c, qa, fill_stage);
+  if constexpr (F::F6)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[q], (lds_ptr_t)(slot_fill + (c.wave + 4 * q) * 1024), 12, vo, so,
+                                             0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[q], (lds_ptr_t)(slot_fill + (c.wave + 4 * q) * 1024), 16, vo, so,
+                                             0, 0);
+}
+
+// Fragment f of the next stage (A0.., then B0..) from its slot into the other register set.
+template <int KIND, class T>
+MX_DEV void next_frag(const Ctx& c, int f, const char* slot_nxt, v8i (&na)[T::FA], v8i (&nb)[T::FB]) {
+  using F = RingFmt<KIND>;
+  if constexpr (F::F6) {
+    if (f < T::FA) na[f] = read_frag6(slot_nxt, row_a<T>(f, c.wm, c.r32), c.h);
+    else nb[f - T::FA] = read_frag6(slot_nxt + BM * F::SRB_A, row_b<T>(f - T::FA, c.wn, c.r32), c.h);
+  } else if (f < T::FA) na[f] = read_frag<F::SRB_A>(slot_nxt, row_a<T>(f, c.wm, c.r32), c.h);
+  else if constexpr (F::F16) nb[f - T::FA] = read_frag_bt(slot_nxt + BM * F::SRB_A, c.bt_off[f - T::FA]);
+  else nb[f - T::FA] = read_frag<F::SRB_B>(slot_nxt + BM * F::SRB_A, row_b<T>(f - T::FA, c.wn, c.r32), c.h);
+}
+
 // One stage t = 8g + S8: slot t%4 holds stage t (its fragments already in ca/cb). Before the
 // barrier this wave's copies of stage t+1 must have landed; after it, slot (t+3)%4 (stage t-1,
 // read during stage t-2) is free and stage t+1 is readable by every wave. The MFMAs go B tile by B
@@ -371,33 +400,31 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(cb[i], ca[j], acc[i][j], MF::CBSZ, MF::BLGP, U0 % 4,
                                                                        sc.b[i][U0 / 4], U0 % 4, sc.a[j][U0 / 4]);
         }
+        if constexpr (F::F16) {
+          // fp16: the fragment reads spread over the tile's MFMAs, each copy one MFMA after its
+          // share of them (faster than all after the first MFMA, where the compiler puts the MX
+          // formats' reads and copies)
+          if (k == F::KSTEPS - 1) {
+            const int q0 = CP::DPS * i / T::FB, nc = CP::DPS * (i + 1) / T::FB - q0;
+            const int f0 = T::F * i / T::FB, nf = T::F * (i + 1) / T::FB - f0;
+#pragma unroll
+            for (int e = 0; e < nf; e++)
+              if ((e * T::FA) / nf == j) next_frag<KIND, T>(c, f0 + e, slot_nxt, na, nb);
+#pragma unroll
+            for (int e = 0; e < nc; e++)
+              if (min(T::FA - 1, (e * T::FA) / nc + 1) == j) stage_copy<KIND>(c, q0 + e, slot_fill, fill_stage);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       }
     }
-    // this tile's share of the stage copies: copies [DPS*i/FB, DPS*(i+1)/FB) (copy q is an A copy
-    // when q < NI_A/4)
+    // this tile's share of the stage copies, [DPS*i/FB, DPS*(i+1)/FB), and of the next stage's
+    // fragments, list positions [F*i/FB, F*(i+1)/FB) of A0.., B0.. (fp16: placed among the MFMAs)
+    if constexpr (!F::F16) {
 #pragma unroll
-    for (int q = CP::DPS * i / T::FB; q < CP::DPS * (i + 1) / T::FB; q++) {
-      // (offsets computed into locals first: the host pass of hipcc drops the kernel, silently, when
-      // these builtin arguments are written as conditional expressions of the format constants)
-      const bool qa = q < F::NI_A / 4;
-      const uint32_t vo = qa ? c.voff_a : c.voff_b;
-      const uint32_t so = stage_soff<KIND>(c, qa, fill_stage);
-      if constexpr (F::F6)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[q], (lds_ptr_t)(slot_fill + (c.wave + 4 * q) * 1024), 12, vo,
-                                                 so, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[q], (lds_ptr_t)(slot_fill + (c.wave + 4 * q) * 1024), 16, vo,
-                                                 so, 0, 0);
-    }
-    // and of the next stage's fragments: list positions [F*i/FB, F*(i+1)/FB) of A0.., B0..
+      for (int q = CP::DPS * i / T::FB; q < CP::DPS * (i + 1) / T::FB; q++) stage_copy<KIND>(c, q, slot_fill, fill_stage);
 #pragma unroll
-    for (int f = T::F * i / T::FB; f < T::F * (i + 1) / T::FB; f++) {
-      if constexpr (F::F6) {
-        if (f < T::FA) na[f] = read_frag6(slot_nxt, row_a<T>(f, c.wm, c.r32), c.h);
-        else nb[f - T::FA] = read_frag6(slot_nxt + BM * F::SRB_A, row_b<T>(f - T::FA, c.wn, c.r32), c.h);
-      } else if (f < T::FA) na[f] = read_frag<F::SRB_A>(slot_nxt, row_a<T>(f, c.wm, c.r32), c.h);
-      else if constexpr (F::F16) nb[f - T::FA] = read_frag_bt(slot_nxt + BM * F::SRB_A, c.bt_off[f - T::FA]);
-      else nb[f - T::FA] = read_frag<F::SRB_B>(slot_nxt + BM * F::SRB_A, row_b<T>(f - T::FA, c.wn, c.r32), c.h);
+      for (int f = T::F * i / T::FB; f < T::F * (i + 1) / T::FB; f++) next_frag<KIND, T>(c, f, slot_nxt, na, nb);
     }
     if constexpr (!F::F16)
       if (S8 == 4 && i == 1) {
@@ -522,15 +549,7 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   for (int t = 0; t < 3 && t < nst; t++) {
     char* slot = t == 0 ? slot0 : (t == 1 ? slot1 : slot2);
 #pragma unroll
-    for (int k = 0; k < CP::DPS; k++) {
-      const bool qa = k < F::NI_A / 4;
-      const uint32_t vo = qa ? c.voff_a : c.voff_b;
-      const uint32_t so = stage_soff<KIND>(c, qa, (uint32_t)t);
-      if constexpr (F::F6)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(slot + (wave + 4 * k) * 1024), 12, vo, so, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(slot + (wave + 4 * k) * 1024), 16, vo, so, 0, 0);
-    }
+    for (int k = 0; k < CP::DPS; k++) stage_copy<KIND>(c, k, slot, (uint32_t)t);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): prologue copies of this wave
   raw_barrier();
