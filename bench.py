@@ -72,7 +72,7 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs the kernels on one GPU; multi-GPU runs are not implemented (--gpus must be 1)",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import numpy as np

@@ -9,7 +9,7 @@ import torch
 
 def require_gpu():
     if not torch.cuda.is_available():
-        pytest.fail("GPU tests need an MI355X; run them on the GPU box (-m gpu)")
+        pytest.fail("GPU tests need an MI355X (gfx950) device; select them with -m gpu")
     from block_scaled_quantized_amd import api
     return api
 
