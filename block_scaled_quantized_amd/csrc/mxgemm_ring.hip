@@ -365,9 +365,9 @@ MX_DEV void ring_stage(const Ctx& c, int g, char* sgrp, const v8i (&ca)[T::FA], 
   // on, the next group's scales are visible.
   wait_vm_n(S8 == 3 ? CP::DPS + F::DMA_PER_GROUP : CP::DPS);
   raw_barrier();
-  // The scale array still holds half 1 of group g, read at the end of stage 7 of group g-1. Every
-  // wave has waited for those reads before stage 1's MFMAs (they precede the fragment reads of
-  // stage 0 in the wave's LDS queue), so past stage 2's barrier the array is free.
+  // The scale array holds group g, both halves read during stage 4 of group g-1. Every wave has
+  // waited for those reads before stage 5's MFMAs (they precede the fragment reads of stage 5 in
+  // the wave's LDS queue), so past stage 2's barrier the array is free.
   if constexpr (!F::F16)
     if (S8 == 2) issue_scales<KIND>(c, sgrp, min(g + 1, c.ngroups - 1));
   const uint32_t fill_stage = (uint32_t)min(t + 3, c.nst - 1);
