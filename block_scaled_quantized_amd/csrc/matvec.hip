@@ -490,6 +490,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int kLChunk = 4 * 256 + 32;        // LDS bytes of 4 weight rows, padded
 constexpr int kLStage = 8 * kLChunk + 1024;  // a block: 8 chunks + its scale row (<= 1 KB)
 constexpr int kXsLds = 8192;                 // activation halfs staged per workgroup
+static_assert(kXsLds % 512 == 0, "the activation copies fill whole 1 KB pieces of xs");
 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
 MX_DEV void wait_vm_n(int n) {
@@ -585,10 +586,19 @@ __global__ __launch_bounds__(512) void matvec_lds_kernel(const _Float16* __restr
   const int n0 = strip * TW, col = n0 + 16 * C * cg + C * i;
   const uint32_t row_bytes = I8 ? (uint32_t)N : (uint32_t)N / 2;
 
-  // activations x[m][32*kb0 .. 32*kb1) -> xs[m*KC + ...]
-  for (int e = 8 * threadIdx.x; e < M * KC; e += 8 * 512) {
-    const int m = e / KC, kk = e - m * KC;
-    *reinterpret_cast<uint4*>(&xs[e]) = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + 32 * kb0 + kk);
+  // Activations x[m][32*kb0 .. 32*kb1) -> xs[m*KC + ...] as direct copies queued ahead of the
+  // ring's, so the first step's wait covers them: copy j (from wave j % 8) fills xs halfs
+  // 512j .. 512j+511, lane l the 8 from 512j + 8l. Lanes past M*KC re-read x's first 16 bytes into
+  // unused xs (M*KC <= kXsLds, a multiple of 512, so every copy stays inside xs).
+  {
+    const rsrc_t xr = make_rsrc(x, 2u * (uint32_t)M * (uint32_t)K);
+    const int nj = (M * KC + 511) / 512;
+    for (int j = wave; j < nj; j += 8) {
+      const int e = 512 * j + 8 * lane;
+      const int m = e / KC, kk = e - m * KC;
+      const uint32_t vo = e < M * KC ? 2u * (uint32_t)(m * K + 32 * kb0 + kk) : 0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(xs + 512 * j), 16, vo, 0, 0, 0);
+    }
   }
 
   // Copy offsets. Bytes past the end of a row (last strip) are clamped back into the row; the
@@ -625,7 +635,6 @@ __global__ __launch_bounds__(512) void matvec_lds_kernel(const _Float16* __restr
 #pragma unroll
   for (int j = 0; j < C; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  __syncthreads();  // xs complete (before any direct copy is queued: this barrier waits for vmcnt(0))
 #pragma unroll
   for (int u = 0; u < RS - 1; u++)
     if (u < nsteps) issue(u);
