@@ -825,12 +825,16 @@ int launch(int M, int N, int K, const void* x, const void* W, const void* Ws, vo
 // Small-M GEMM form (M > 8). Measured on MI355X (int4 / int8), K=4096:
 //   M=128, N=12288: 8 columns per lane with 64-row tiles (128-column strips, 192 workgroups of 4
 //     waves) 29-30 us; 4 columns with 32-row tiles and 8 waves 36-37 us; 16 columns 33-35 us.
-//   M=64, N=4096: 4 columns with 16-row tiles and 8 waves 10 us; 8 columns 14-16 us.
+//   M=64, N=4096: 4 columns with 16-row tiles and 16 waves 9.6-9.7 us, 8 waves 10.2-10.7 us; 8
+//     columns 14-16 us.
 // Wider strips cut the activation re-reads (each strip reads all of its row tile's x) and taller
 // row tiles re-convert each weight fewer times, while too few workgroups leave CUs idle. So the
 // 128-column strips run where they still give 192 or more workgroups and M > 32; otherwise 64-column
 // strips with 16-row tiles, or 32-row tiles where 16 would give more than 3 rounds of workgroups.
-constexpr int kWqMaxWGs = 3 * 256, kWqMinWide = 192;
+// 16-row tiles take 16 waves (twice the blocks in flight per CU) where the grid is one round of at
+// most 256 workgroups, and 8 waves (two workgroups per CU) beyond: at 512 workgroups 16 waves
+// measured 2-3% slower, at 128-256 they measured 1-9% faster.
+constexpr int kWqMaxWGs = 3 * 256, kWqMinWide = 192, kWqOneRound = 256;
 
 template <bool I8, int C, int MT, int W, int P>
 int launch_wq_mt(int M, int N, int K, const void* x, const void* Wt, const void* Ws, void* y, hipStream_t st) {
@@ -844,6 +848,7 @@ template <bool I8>
 int launch_wq(int M, int N, int K, const void* x, const void* W, const void* Ws, void* y, hipStream_t st) {
   const int64_t strips4 = (N + 63) / 64, strips8 = (N + 127) / 128;
   if (M > 32 && strips8 * ((M + 63) / 64) >= kWqMinWide) return launch_wq_mt<I8, 8, 4, 4, 2>(M, N, K, x, W, Ws, y, st);
+  if (strips4 * ((M + 15) / 16) <= kWqOneRound) return launch_wq_mt<I8, 4, 1, 16, 2>(M, N, K, x, W, Ws, y, st);
   if (strips4 * ((M + 15) / 16) <= kWqMaxWGs) return launch_wq_mt<I8, 4, 1, 8, 4>(M, N, K, x, W, Ws, y, st);
   if (strips4 * ((M + 31) / 32) <= kWqMaxWGs) return launch_wq_mt<I8, 4, 2, 8, 2>(M, N, K, x, W, Ws, y, st);
   return launch_wq_mt<I8, 8, 4, 4, 2>(M, N, K, x, W, Ws, y, st);
