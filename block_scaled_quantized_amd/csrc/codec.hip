@@ -82,11 +82,18 @@ __global__ __launch_bounds__(kThreads) void pack_int_kernel(bool i8, const float
     const int b = (int)(id / pairs), n0 = 2 * (int)(id % pairs);
     const bool two = n0 + 1 < N;
     float amax0 = 0.0f, amax1 = 0.0f;
+    bool nf0 = false, nf1 = false;
     for (int k = 32 * b; k < 32 * b + 32; k++) {
-      amax0 = fmaxf(amax0, fabsf(w[(int64_t)k * N + n0]));
-      if (two) amax1 = fmaxf(amax1, fabsf(w[(int64_t)k * N + n0 + 1]));
+      const float w0 = w[(int64_t)k * N + n0];
+      amax0 = fmaxf(amax0, fabsf(w0));
+      nf0 |= !__builtin_isfinite(w0);
+      if (two) {
+        const float w1 = w[(int64_t)k * N + n0 + 1];
+        amax1 = fmaxf(amax1, fabsf(w1));
+        nf1 |= !__builtin_isfinite(w1);
+      }
     }
-    const uint16_t sb0 = int_block_scale(amax0, qmax), sb1 = int_block_scale(amax1, qmax);
+    const uint16_t sb0 = int_block_scale(amax0, nf0, qmax), sb1 = int_block_scale(amax1, nf1, qmax);
     scales[(int64_t)b * N + n0] = sb0;
     if (two) scales[(int64_t)b * N + n0 + 1] = sb1;
     const float s0 = dec_f16(sb0), s1 = dec_f16(sb1);

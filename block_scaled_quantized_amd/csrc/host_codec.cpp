@@ -56,8 +56,12 @@ int pack_int(bool i8, const float* w, int64_t K, int64_t N, uint8_t* codes, uint
   for (int64_t b = 0; b < K / 32; b++)
     for (int64_t n = 0; n < N; n++) {
       float amax = 0.0f;
-      for (int64_t k = 32 * b; k < 32 * b + 32; k++) amax = std::fmax(amax, std::fabs(w[k * N + n]));
-      uint16_t sb = int_block_scale(amax, qmax);
+      bool nonfinite = false;
+      for (int64_t k = 32 * b; k < 32 * b + 32; k++) {
+        amax = std::fmax(amax, std::fabs(w[k * N + n]));
+        nonfinite |= !std::isfinite(w[k * N + n]);
+      }
+      uint16_t sb = int_block_scale(amax, nonfinite, qmax);
       scales[b * N + n] = sb;
       float s = dec_f16(sb);
       for (int64_t k = 32 * b; k < 32 * b + 32; k++) {

@@ -9,7 +9,7 @@
 //
 // Integer weight blocks (32 rows of one column share one fp16 scale: the per-block fp16 scales of
 // the "Kernel-phase findings" revised strategy): s = fp16(amax / qmax), q = rint(w / s) clamped to
-// [-qmax, qmax], q = 0 when s = 0.
+// [-qmax, qmax], q = 0 when s = 0; a block holding Inf or NaN gets s = NaN and q = 0.
 #pragma once
 #include "codec_math.h"
 
@@ -42,16 +42,21 @@ MX_HD uint32_t mx_block_scale(uint32_t amax_bits, bool nonfinite, int fmt, int* 
   return E;
 }
 
-// Integer symmetric quantisation of one weight given the block's fp16 scale (as fp32).
+// Integer symmetric quantisation of one weight given the block's fp16 scale (as fp32). A zero
+// scale (all-zero block) and a NaN scale (block holding Inf or NaN) give 0, so the cast below only
+// ever sees a finite value.
 MX_HD int int_quant(float w, float s, int qmax) {
-  if (s == 0.0f) return 0;
+  if (!(s > 0.0f)) return 0;
   float r = rint_even(div_rn(w, s));
   r = r > (float)qmax ? (float)qmax : r;
   r = r < (float)-qmax ? (float)-qmax : r;
   return (int)r;
 }
 
-// fp16 block scale (bits) of an integer weight block from its amax.
-MX_HD uint16_t int_block_scale(float amax, int qmax) { return f32_to_f16(div_rn(amax, (float)qmax)); }
+// fp16 block scale (bits) of an integer weight block from its amax; a block holding Inf or NaN
+// gets the NaN scale 0x7E00 (its codes are all 0, so it dequantises to NaN, as an MX block does).
+MX_HD uint16_t int_block_scale(float amax, bool nonfinite, int qmax) {
+  return nonfinite ? (uint16_t)0x7E00u : f32_to_f16(div_rn(amax, (float)qmax));
+}
 
 }  // namespace mx

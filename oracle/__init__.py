@@ -281,17 +281,23 @@ def check(c_gpu, c_ref, K, R):
 
     The output is binary16 rounded to nearest even, so an infinite GPU output is correct exactly
     when the reference, moved by at most its bound toward larger magnitude, reaches the fp16
-    overflow threshold with the same sign; such outputs count as err/bound = 0."""
+    overflow threshold with the same sign; such outputs count as err/bound = 0. An infinite
+    reference (an infinite operand, E5M2's Inf codes) is met only by the same infinity: its bound
+    is infinite too, so it is compared for equality instead."""
     c_gpu = np.asarray(c_gpu, dtype=np.float64)
     c_ref = np.asarray(c_ref, dtype=np.float64)
     nan_ok = np.array_equal(np.isnan(c_gpu), np.isnan(c_ref))
     fin = ~np.isnan(c_ref) & ~np.isnan(c_gpu)
     g, r = c_gpu[fin], c_ref[fin]
-    bnd = bound(r, K, R)
-    inf = np.isinf(g)
-    inf_ok = inf & (np.sign(g) == np.sign(r)) & (np.abs(r) + bnd >= F16_OVERFLOW)
-    err = np.where(inf, 0.0, np.abs(g - r))
-    ok_each = np.where(inf, inf_ok, err <= bnd)
-    ratio = float(np.max(np.where(inf, np.where(inf_ok, 0.0, np.inf), err / bnd))) if g.size else 0.0
+    with np.errstate(invalid="ignore"):
+        bnd = bound(r, K, R)
+        rinf = np.isinf(r)
+        inf = np.isinf(g) & ~rinf
+        inf_ok = inf & (np.sign(g) == np.sign(r)) & (np.abs(r) + bnd >= F16_OVERFLOW)
+        err = np.where(inf | rinf, 0.0, np.abs(g - r))
+        ok_each = np.where(rinf, g == r, np.where(inf, inf_ok, err <= bnd))
+        ratio_each = np.where(rinf, np.where(g == r, 0.0, np.inf),
+                              np.where(inf, np.where(inf_ok, 0.0, np.inf), err / bnd))
+    ratio = float(np.max(ratio_each)) if g.size else 0.0
     bad = int(np.sum(~ok_each))
     return (nan_ok and bad == 0), ratio, bad

@@ -379,22 +379,28 @@ unsigned orc_enc_f16(double x) {
 
 /* Symmetric integer quantisation of W [K][N] (fp32), one fp16 scale per column per 32 rows:
  *   s = fp16(amax / qmax) with the division in fp32; q = clamp(rint(fp32(w / s)), -qmax, qmax),
- *   q = 0 where s = 0. qmax = 127 (int8) or 7 (int4). Output q as int8 [K][N] (one per byte),
+ *   q = 0 where s = 0; a block holding Inf or NaN gets s = NaN and q = 0 (a reading: the pages
+ *   never quantise non-finite weights). qmax = 127 (int8) or 7 (int4). Output q as int8 [K][N] (one per byte),
  *   scales binary16 bits [K/32][N]. Packing of int4 is separate (orc_pack_int4). */
 void orc_int_quantize(int qmax, int64_t K, int64_t N, const float* w, int8_t* q, uint16_t* s16) {
 #pragma omp parallel for schedule(static)
   for (int64_t b = 0; b < K / 32; b++)
     for (int64_t n = 0; n < N; n++) {
       float amax = 0.0f;
-      for (int64_t k = 32 * b; k < 32 * b + 32; k++)
-        if (fabsf(w[k * N + n]) > amax) amax = fabsf(w[k * N + n]);
+      int finite = 1;
+      for (int64_t k = 32 * b; k < 32 * b + 32; k++) {
+        if (!isfinite(w[k * N + n])) finite = 0;
+        else if (fabsf(w[k * N + n]) > amax) amax = fabsf(w[k * N + n]);
+      }
+      /* a block holding Inf or NaN: scale NaN (binary16 0x7E00), every q zero, so the whole block
+       * dequantises to NaN (the same reading as the MX rule for non-finite blocks) */
       float ratio = amax / (float)qmax;
-      unsigned sb = orc_enc_f16((double)ratio);
+      unsigned sb = finite ? orc_enc_f16((double)ratio) : 0x7E00u;
       float s = (float)orc_dec_f16(sb);
       s16[b * N + n] = (uint16_t)sb;
       for (int64_t k = 32 * b; k < 32 * b + 32; k++) {
         int v = 0;
-        if (s != 0.0f) {
+        if (finite && s != 0.0f) {
           float t = w[k * N + n] / s;
           double r = rint((double)t);
           if (r > qmax) r = qmax;

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 from block_scaled_quantized_amd import synth
-from gpu_common import bitequal_f32, dev, empty, gpu_int_pack, gpu_mx_pack, host, require_gpu, say
+from gpu_common import bitequal_f32, dev, empty, sentinel_f32, gpu_int_pack, gpu_mx_pack, host, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,7 @@ def test_mx_pack_unpack_bitexact(orc, fmt, case):
     oc, os_ = orc.mx_quantize(fmt, x)
     assert np.array_equal(host(scales), os_)
     assert np.array_equal(host(codes), oc)
-    out = empty((rows, cols), torch.float32)
+    out = sentinel_f32((rows, cols))
     api.mx_unpack_run(fmt, codes, scales, rows, cols, out)
     assert bitequal_f32(host(out), orc.dequant(fmt, oc, os_, rows, cols))
 
@@ -75,7 +75,7 @@ def test_mx_unpack_every_code_and_scale(orc, fmt):
         codes = np.tile(np.packbits(bits, bitorder="little"), (256, 1))
     codes = np.ascontiguousarray(codes[:, : (cols if byte else (cols // 4 * 3 if fmt in (2, 3) else cols // 2))])
     scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], cols // 32, axis=1)
-    out = empty((256, cols), torch.float32)
+    out = sentinel_f32((256, cols))
     api.mx_unpack_run(fmt, dev(codes), dev(scales), 256, cols, out)
     assert bitequal_f32(host(out), orc.dequant(fmt, codes, scales, 256, cols))
 
@@ -92,11 +92,14 @@ def test_int_pack_unpack_bitexact(orc, fw, shape):
     if K <= 96:
         w[32:64, 3] = 0.0
         w[0:32, 5] *= np.float32(1e-30)
+        w[40, 6] = np.inf                    # non-finite blocks: NaN scale, zero codes
+        w[70, 7] = np.nan
+        w[2, 8] = -np.inf
     codes, scales = gpu_int_pack(api, fw, w)
     q, s = orc.int_quantize(fw, w)
     ref_codes = q.view(np.uint8) if fw == 32 else orc.pack_int4(q)
     assert np.array_equal(host(scales).view(np.uint16), s.view(np.uint16))
     assert np.array_equal(host(codes), ref_codes)
-    out = empty((K, N), torch.float32)
+    out = sentinel_f32((K, N))
     api.mx_unpack_run(fw, codes, scales, K, N, out)
     assert bitequal_f32(host(out), orc.dequant(fw, ref_codes, s, K, N))

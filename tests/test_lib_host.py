@@ -106,6 +106,9 @@ def test_host_int_pack_matches_oracle(orc, fw):
     w = synth.normal((K, N), 0.02, 1031)
     w[32:64, 3] = 0.0
     w[64:96, 4] *= np.float32(1e-6)
+    w[100, 7] = np.inf                   # non-finite blocks: NaN scale, zero codes
+    w[5, 9] = np.nan
+    w[33, 10] = -np.inf
     cs, ss = api.int_shapes(fw, K, N)
     codes = np.zeros(cs, np.uint8)
     scales = np.zeros(ss, np.float16)
@@ -114,9 +117,13 @@ def test_host_int_pack_matches_oracle(orc, fw):
     assert np.array_equal(scales.view(np.uint16), s.view(np.uint16))
     ref_codes = q.view(np.uint8) if fw == 32 else orc.pack_int4(q)
     assert np.array_equal(codes, ref_codes)
+    assert scales.view(np.uint16)[3, 7] == 0x7E00 and scales.view(np.uint16)[0, 9] == 0x7E00
     out = np.zeros((K, N), np.float32)
     api.mx_unpack_host(fw, codes, scales, K, N, out)
-    assert np.array_equal(out.view(np.uint32), orc.dequant(fw, ref_codes, s, K, N).view(np.uint32))
+    ref = orc.dequant(fw, ref_codes, s, K, N)
+    assert np.array_equal(np.isnan(out), np.isnan(ref)) and np.isnan(ref).sum() == 3 * 32
+    fin = ~np.isnan(ref)
+    assert np.array_equal(out.view(np.uint32)[fin], ref.view(np.uint32)[fin])
 
 
 def test_validation_errors_without_gpu():

@@ -337,3 +337,34 @@ def test_relu_special_values(orc):
                    np.array([[0x38] * 32, [0xB8] * 32], np.uint8), np.array([[127], [127]], np.uint8), 2, 2, 32)
     assert C.tolist() == [[32.0, -32.0], [32.0, -32.0]]          # 32 products of +-1
     assert orc.relu(C).tolist() == [[32.0, 0.0], [32.0, 0.0]]
+
+
+@pytest.mark.parametrize("M,K,N,seed", [(3, 5, 4, 1), (7, 2, 11, 2), (1, 9, 1, 3), (6, 13, 2, 4)])
+def test_rms_ab_is_the_triplewise_rms(orc, M, K, N, seed):
+    """R of the acceptance bound is the root mean square of |a_mk b_kn| over every (m, k, n)
+    triple: summed here one triple at a time with math.fsum (an exactly rounded sum), on
+    non-square shapes with M, K and N all different, so a transposed operand, a sum over the wrong
+    axis or a wrong normaliser (M*N, K, ...) fails."""
+    import math
+    g = np.random.Generator(np.random.PCG64(seed))
+    a = g.standard_normal((M, K)) * g.integers(1, 5, size=(M, K))
+    b = g.standard_normal((K, N)) * 3.0
+    terms = [(a[m, k] * b[k, n]) ** 2 for m in range(M) for k in range(K) for n in range(N)]
+    want = math.sqrt(math.fsum(terms) / (M * K * N))
+    assert abs(orc.rms_ab(a, b) - want) <= 1e-13 * want
+    # a scaled operand scales R by the same factor; a single nonzero triple gives |a b| / sqrt(MKN)
+    assert abs(orc.rms_ab(2.0 * a, b) - 2.0 * want) <= 1e-13 * want
+    a1 = np.zeros((M, K))
+    b1 = np.zeros((K, N))
+    a1[M - 1, K - 1], b1[K - 1, N - 1] = 3.0, -5.0
+    assert orc.rms_ab(a1, b1) == pytest.approx(15.0 / math.sqrt(M * K * N), rel=1e-15)
+
+
+def test_check_infinite_reference_needs_the_same_infinity(orc):
+    """An infinite reference (E5M2 Inf codes) is met only by the same infinity: a finite or
+    opposite output fails even though the bound is infinite there."""
+    ref = np.array([np.inf, -np.inf, 1.0])
+    assert orc.check(np.array([np.inf, -np.inf, 1.0]), ref, 32, 1.0)[0]
+    assert not orc.check(np.array([60000.0, -np.inf, 1.0]), ref, 32, 1.0)[0]
+    assert not orc.check(np.array([np.inf, np.inf, 1.0]), ref, 32, 1.0)[0]
+    assert not orc.check(np.array([np.nan, -np.inf, 1.0]), ref, 32, 1.0)[0]

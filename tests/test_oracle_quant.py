@@ -290,3 +290,28 @@ def test_int_quantize_vs_torch(orc, fw, qmax):
     # every non-zero block reaches the end of the range
     qa = np.abs(q.astype(np.int32)).reshape(K // 32, 32, N).max(axis=1)
     assert np.all((qa == qmax) | (amax.numpy() == 0))
+
+
+@pytest.mark.parametrize("fw,qmax", [(32, 127), (33, 7)])
+def test_int_quantize_nonfinite_block(orc, fw, qmax):
+    """A 32-row block holding Inf or NaN gets the NaN scale (binary16 0x7E00) and all-zero codes, so
+    it dequantises to NaN; the other blocks of the same columns and rows are untouched."""
+    K, N = 96, 8
+    w = synth.normal((K, N), 0.02, 77)
+    clean_q, clean_s = orc.int_quantize(fw, w)
+    w[40, 2] = np.inf
+    w[70, 5] = np.nan
+    w[3, 6] = -np.inf
+    q, s = orc.int_quantize(fw, w)
+    s16 = s.view(np.uint16)
+    bad = {(1, 2), (2, 5), (0, 6)}
+    for b in range(K // 32):
+        for n in range(N):
+            if (b, n) in bad:
+                assert s16[b, n] == 0x7E00 and not q[32 * b:32 * b + 32, n].any()
+            else:
+                assert s16[b, n] == clean_s.view(np.uint16)[b, n]
+                assert np.array_equal(q[32 * b:32 * b + 32, n], clean_q[32 * b:32 * b + 32, n])
+    deq = orc.dequant(fw, q.view(np.uint8) if fw == 32 else orc.pack_int4(q), s, K, N)
+    assert np.isnan(deq[32:64, 2]).all() and np.isnan(deq[64:96, 5]).all() and np.isnan(deq[0:32, 6]).all()
+    assert np.isnan(deq).sum() == 3 * 32
