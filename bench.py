@@ -15,7 +15,8 @@ Timing: per workload, --settle seconds (default 0.5) of untimed calls so that th
 reaches its sustained-load level, W warm-up steps, then K steps between two HIP events recorded
 on the stream the kernels are launched on, bracketed by device synchronisation. Inputs rotate over several copies so that
 repeats are not served by the 256 MB Infinity Cache (3 sets for GEMMs, >= 384 MB of weights for
-the matvec). The CPU baseline is the oracle timed on the host on a bounded row sample.
+the matvec). The CPU baseline is the oracle timed on the host cores on every workload measured: the
+whole output where small, else whole rows for about --cpu-seconds each, extrapolated.
 """
 from __future__ import annotations
 
@@ -57,6 +58,105 @@ def hbm_traffic(kernel, tile, shape):
     return None, None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(np, synth, C_prefill, keep, budget_s):
+    """The oracle (oracle/, plain C, fp64) timed on the host on every workload whose GPU output this
+    run kept: the whole output where it is small (the 128x256x128 GEMM, the matvecs), else whole
+    rows of C computed in chunks of one row per thread until `budget_s` seconds have passed, with
+    the full-output time extrapolated (rows are independent and cost the same). The oracle
+    quantises the fp32 sources itself. Each checked GPU row is compared with the acceptance bound."""
+    import oracle as orc
+    affinity = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(affinity, int(env)) if env.isdigit() and int(env) > 0 else affinity
+    orc.set_threads(threads)
+    threads = orc.num_threads()
+    configs = {}
+
+    def rows_leg(name, M, N, K, flops_row, run_rows, R, gpu, unit_flops=True):
+        done, t, worst = 0, 0.0, 0.0
+        while done < M and (t < budget_s or done == 0):
+            n = min(threads, M - done)
+            t0 = time.perf_counter()
+            ref = run_rows(done, n)
+            t += time.perf_counter() - t0
+            _, ratio, _ = orc.check(gpu[done:done + n].cpu().numpy().astype(np.float64), ref, K, R)
+            worst = max(worst, ratio)
+            done += n
+        configs[name] = {"rows": done, "of_rows": M, "seconds": t, "extrapolated": done < M,
+                         "full_output_seconds": t * M / done,
+                         "tflops": flops_row * done / t / 1e12, "gpu_worst_err_over_bound": worst}
+
+    def mx_leg(name, fmt, M, N, K, wl, sigma_b, gpu):
+        a_src = synth.normal((M, K), 1.0, synth.seed_for(wl, 0))
+        b_src = synth.normal((N, K), sigma_b, synth.seed_for(wl, 1))
+        oA, oSA = orc.mx_quantize(fmt, a_src)
+        oB, oSB = orc.mx_quantize(fmt, b_src)
+        del a_src, b_src
+        R = orc.rms_ab(orc.dequant(fmt, oA, oSA, M, K), orc.dequant(fmt, oB, oSB, N, K).T)
+        rows_leg(name, M, N, K, 2.0 * N * K,
+                 lambda r0, n: orc.mxgemm(fmt, fmt, oA, oSA, oB, oSB, M, N, K, row0=r0, nrows=n), R, gpu)
+
+    log_ = lambda m: print(f"[bench] cpu: {m}", file=sys.stderr, flush=True)
+    if "mxfp8_small" in keep:
+        log_("mxfp8 128x256x128")
+        mx_leg("mxfp8_gemm_128x256x128", orc.E4M3, 128, 256, 128, synth.MXFP8_SMALL, 1.0, keep["mxfp8_small"])
+    if "fp16" in keep:
+        log_("fp16 4096^3")
+        A16 = synth.uniform_pm1((4096, 4096), synth.seed_for(synth.F16_SQUARE, 0)).astype(np.float16)
+        B16 = synth.uniform_pm1((4096, 4096), synth.seed_for(synth.F16_SQUARE, 1)).astype(np.float16)
+        R = orc.rms_ab(A16.astype(np.float64), B16.astype(np.float64))
+        rows_leg("fp16_gemm_4096x4096x4096", 4096, 4096, 4096, 2.0 * 4096 * 4096,
+                 lambda r0, n: orc.gemm_f16(A16, B16, row0=r0, nrows=n), R, keep["fp16"])
+        del A16, B16
+    log_("mxfp8 prefill 2048x14336x4096")
+    mx_leg("mxfp8_gemm_2048x14336x4096", orc.E4M3, 2048, 14336, 4096, synth.MXFP8_PREFILL, 0.02, C_prefill)
+    if any(k.startswith("matvec_") for k in keep):
+        Km, Nm = 4096, 14336
+        w = synth.normal((Km, Nm), 0.02, synth.seed_for(synth.MATVEC, 1))
+        x8 = synth.normal((8, Km), 1.0, synth.seed_for(synth.MATVEC, 0)).astype(np.float16)
+        for fw, name in ((orc.INT8, "int8"), (orc.INT4, "int4")):
+            q, s = orc.int_quantize(fw, w)
+            oW = q.view(np.uint8) if fw == orc.INT8 else orc.pack_int4(q)
+            wdeq = orc.dequant(fw, oW, s, Km, Nm)
+            for Mv in (1, 8):
+                key = f"matvec_{name}_M{Mv}"
+                if key not in keep:
+                    continue
+                log_(key)
+                x = x8[:Mv]
+                t0 = time.perf_counter()
+                ref = orc.matvec(fw, x, oW, s, Km, Nm)
+                t = time.perf_counter() - t0
+                _, ratio, _ = orc.check(keep[key].cpu().numpy().astype(np.float64), ref, Km,
+                                        orc.rms_ab(x.astype(np.float64), wdeq))
+                nbytes = oW.size + 2 * s.size + 2 * Mv * Km + 2 * Mv * Nm
+                configs[key] = {"rows": Mv, "of_rows": Mv, "seconds": t, "extrapolated": False,
+                                "full_output_seconds": t, "gbs": nbytes / t / 1e9,
+                                "gpu_worst_err_over_bound": ratio}
+        del w
+    if "mxfp4" in keep:
+        log_("mxfp4 4096x8192x8192")
+        mx_leg("mxfp4_gemm_4096x8192x8192", orc.E2M1, 4096, 8192, 8192, synth.MXFP4_LARGE, 1.0, keep["mxfp4"])
+    head = configs["mxfp8_gemm_2048x14336x4096"]
+    return {"value": head["tflops"], "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"rows 0..{head['rows'] - 1} of C for the MXFP8 GEMM M=2048,N=14336,K=4096 "
+                      f"({head['rows']}x14336x4096 MACs in {head['seconds']:.1f} s, fp64, closed-form decode per "
+                      f"element); the other workloads under 'configs'",
+            "cpu_model": cpu_model(), "affinity_cpus": affinity, "omp_threads": threads,
+            "budget_s_per_config": budget_s, "configs": configs}
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -65,6 +165,8 @@ def parse():
     p.add_argument("--settle", type=float, default=0.5,
                    help="seconds of untimed load before each workload's warm-up steps (clock ramp)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=4.0,
+                   help="oracle seconds per large workload in the CPU baseline (whole rows, extrapolated)")
     p.add_argument("--only", default="", help="comma list of detail workloads to run (default all)")
     return p.parse_args()
 
@@ -147,6 +249,7 @@ def main():
     C0 = Cs[0]
 
     detail = {}
+    keep = {}  # GPU outputs the CPU baseline checks, by workload
     only = set(filter(None, args.only.split(",")))  # "none" skips every detail workload
 
     def want(name):
@@ -160,6 +263,7 @@ def main():
         p4 = api.mxgemm_create(M4, N4, K4, api.MX_E2M1, api.MX_E2M1)
         C4 = [torch.empty((M4, N4), dtype=torch.float16, device=dev) for _ in range(3)]
         t = timed(lambda i: api.mxgemm_run(p4, *s4[i % 3], C4[i % 3], stream), args.steps, args.warmup)
+        keep["mxfp4"] = C4[0]
         tf = 2.0 * M4 * N4 * K4 / (t * 1e-3) / 1e12
         detail["mxfp4_gemm_4096x8192x8192"] = {"ms": t, "tflops": tf, "frac_peak": tf / PEAK["mxfp4"],
                                                "tile": api.mxgemm_plan_info(p4)}
@@ -216,6 +320,7 @@ def main():
         Cf = [torch.empty((Mf, Nf), dtype=torch.float16, device=dev) for _ in range(3)]
         t = timed(lambda i: api.mxgemm_run(pf, fsets[i % 3][0], None, fsets[i % 3][1], None, Cf[i % 3], stream),
                   args.steps, args.warmup)
+        keep["fp16"] = Cf[0]
         tf = 2.0 * Mf * Nf * Kf / (t * 1e-3) / 1e12
         detail["fp16_gemm_4096x4096x4096"] = {"ms": t, "tflops": tf, "frac_peak": tf / PEAK["fp16"],
                                               "tile": api.mxgemm_plan_info(pf)}
@@ -229,6 +334,7 @@ def main():
         ps = api.mxgemm_create(Ms, Ns, Ks, api.MX_E4M3, api.MX_E4M3)
         Csm = torch.empty((Ms, Ns), dtype=torch.float16, device=dev)
         t = timed(lambda i: api.mxgemm_run(ps, *ss_[0], Csm, stream), args.steps, args.warmup)
+        keep["mxfp8_small"] = Csm
         detail["mxfp8_gemm_128x256x128"] = {"us": t * 1e3, "tflops": 2.0 * Ms * Ns * Ks / (t * 1e-3) / 1e12,
                                             "tile": api.mxgemm_plan_info(ps)}
 
@@ -256,6 +362,7 @@ def main():
                     t = timed(lambda i: api.mxmatvec_run(Mv, Nm, Km, xv, wsets[i % copies][0], fw, wsets[i % copies][1],
                                                          y, wsp, None, stream), args.steps, args.warmup)
                     gbs = nbytes / (t * 1e-3) / 1e9
+                    keep[f"matvec_{name}_M{Mv}"] = y.clone()
                     detail[f"matvec_{name}_M{Mv}{label}"] = {"us": t * 1e3, "gbs": gbs, "frac_hbm": gbs / PEAK["hbm_gbs"],
                                                             "bytes": nbytes, "weight_copies": copies,
                                                             "workspace_bytes": need if wsp is not None else 0}
@@ -312,34 +419,12 @@ def main():
                                         "bytes_read": nbytes, "bytes_written": nbytes}
         del csrc, cdst
 
-    # ---------------- CPU baseline: the oracle on a bounded sample ------------------------------
+    # ---------------- CPU baseline: the oracle on each workload ------------------------------------
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        import oracle as orc
         torch.cuda.synchronize()
-        oB, oSB = orc.mx_quantize(orc.E4M3, b_src)
-        oA, oSA = orc.mx_quantize(orc.E4M3, a_src[:64])
-        threads = orc.num_threads()
-        rows_done, t_cpu, R = 0, 0.0, None
-        chunk = max(1, threads)
-        gpu_rows = C0[:64].cpu().numpy().astype(np.float64)
-        worst = 0.0
-        while rows_done < 64 and t_cpu < 12.0:
-            n = min(chunk, 64 - rows_done)
-            t0 = time.perf_counter()
-            ref = orc.mxgemm(orc.E4M3, orc.E4M3, oA, oSA, oB, oSB, 64, N, K, row0=rows_done, nrows=n)
-            t_cpu += time.perf_counter() - t0
-            if R is None:
-                R = orc.rms_ab(orc.dequant(orc.E4M3, oA, oSA, 64, K), orc.dequant(orc.E4M3, oB, oSB, N, K).T)
-            ok, ratio, _ = orc.check(gpu_rows[rows_done:rows_done + n], ref, K, R)
-            worst = max(worst, ratio)
-            rows_done += n
-        cpu_tflops = 2.0 * rows_done * N * K / t_cpu / 1e12
-        cpu = {"value": cpu_tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-               "sample": f"rows 0..{rows_done - 1} of C for the MXFP8 GEMM M=2048,N=14336,K=4096 "
-                         f"({rows_done}x{N}x{K} MACs in {t_cpu:.1f} s, fp64, closed-form decode per element)",
-               "seconds": t_cpu, "gpu_rows_worst_err_over_bound": worst}
+        cpu = cpu_baseline(np, synth, C0, keep, args.cpu_seconds)
 
     kname = {3: "gemm_ring_kernel", 2: "gemm_pp_kernel"}.get(tile[3], "gemm_kernel")
     traffic, traffic_src = hbm_traffic(kname, list(tile), (M, N, K))

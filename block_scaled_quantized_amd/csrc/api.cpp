@@ -105,7 +105,7 @@ int choose_tile(int kind, int M, int N, int K) {
 
 extern "C" {
 
-const char* mx_strerror(int s) {
+const char* mx_strerror(mx_status s) {
   switch (s) {
     case MX_OK: return "ok";
     case MX_ERR_NULL: return "a required pointer is NULL";

@@ -56,8 +56,9 @@ typedef enum { MX_E4M3 = 0, MX_E5M2 = 1, MX_E2M3 = 2, MX_E3M2 = 3, MX_E2M1 = 4, 
 /* Largest accepted dimension of any matrix (rows or columns). */
 #define MX_MAX_DIM (1 << 20)
 
-/* Human-readable name of a status code (static storage, never NULL). */
-const char* mx_strerror(int status);
+/* Human-readable name of a status code (static storage, never NULL; unknown codes are named as
+ * such). */
+const char* mx_strerror(mx_status status);
 
 /* Library version as 10000*major + 100*minor + patch. */
 int mx_version(void);
@@ -87,8 +88,10 @@ typedef struct mxgemm_plan* mxgemm_t;
  * (MX_E4M3, MX_E2M1), (MX_E2M1, MX_E4M3) (A and B each in its own format, scales as above; the
  * scaled MFMA takes each operand's format separately), and every pair with an MX_E5M2 operand:
  * (MX_E5M2, MX_E5M2), (MX_E4M3, MX_E5M2), (MX_E5M2, MX_E4M3), (MX_E5M2, MX_E2M1),
- * (MX_E2M1, MX_E5M2). All pairs other than the three plain ones need K % 512 == 0 and
- * N % 4 == 0, else MX_ERR_SHAPE.
+ * (MX_E2M1, MX_E5M2), and the four FP6 pairs (MX_E2M3, MX_E2M3), (MX_E3M2, MX_E3M2),
+ * (MX_E2M3, MX_E3M2), (MX_E3M2, MX_E2M3) (the pages' "MX scaling formats", TensorOps notes,
+ * quantized dtype matrix). All pairs other than the three plain ones need K % 512 == 0 and
+ * N % 4 == 0, else MX_ERR_SHAPE; FP6 with any other format is MX_ERR_FORMAT.
  * Shape rules: 1 <= M, N <= MX_MAX_DIM; 32 <= K <= MX_MAX_DIM; MX formats need K % 32 == 0;
  * MX_F16 needs K % 8 == 0 and N % 8 == 0.
  * `flags` is 0 or MXGEMM_RELU (other bits: MX_ERR_FORMAT). Host only: queues no GPU work. *out
@@ -101,16 +104,19 @@ int mxgemm_create(mxgemm_t* out, int M, int N, int K, int fa, int fb, unsigned f
  * mxgemm_run -- queue the GEMM of plan p on `stream`.
  *
  * Layouts (all device pointers, 16-byte aligned):
- *   MX:  A  codes [M][K] (E4M3, E5M2) or [M][K/2] (E2M1), K contiguous;
+ *   MX:  A  codes [M][K] (E4M3, E5M2), [M][3K/4] (E2M3, E3M2: 6-bit fields, little-endian bit
+ *           stream) or [M][K/2] (E2M1), K contiguous;
  *        SA E8M0 [M][K/32];
- *        B  codes stored K-contiguous, i.e. [N][K] (E4M3, E5M2) or [N][K/2] (E2M1): the scaled right
- *           operand is the transposed one ("Kernel-phase findings", fact 2);
+ *        B  codes stored K-contiguous, i.e. [N][K], [N][3K/4] or [N][K/2] by format: the scaled
+ *           right operand is the transposed one ("Kernel-phase findings", fact 2);
  *        SB E8M0 [N][K/32];
  *   F16: A binary16 [M][K]; B binary16 [K][N] (row-major K x N); SA = SB = NULL.
  *   C:   binary16 [M][N].
  * Errors: MX_ERR_NULL (p, A, B, C, or a scale pointer of an MX plan), MX_ERR_ALIGN, MX_ERR_ARCH,
  * MX_ERR_LAUNCH. Non-finite inputs propagate: a NaN code or a 0xFF scale makes every output it
- * contributes to NaN.
+ * contributes to NaN. E5M2 Inf codes (S.11111.00) are infinities and follow IEEE arithmetic: an
+ * output with one infinite term is that infinity, +Inf and -Inf terms together give NaN, and an
+ * infinity times a zero element gives NaN (the products are formed exactly and summed in fp32).
  */
 int mxgemm_run(mxgemm_t p, const void* A, const void* SA, const void* B, const void* SB, void* C,
                void* stream);
@@ -146,15 +152,24 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
  * GEMM kernel: each block product is still formed exactly in fp32 and scaled once by its fp16
  * block scale.
  *
- * Workspace (M <= 8 only; M > 8 never uses one): at decode shapes K is split across workgroups. Their fp32 partial sums and one
- * counter per column strip live in a caller-owned device buffer of mxmatvec_workspace_size()
- * bytes (16-byte aligned). The buffer must be zero-filled once before its first use (hipMemset,
- * or any zeroed allocation); every call leaves its counters at zero again, so the buffer stays
- * valid for any later call whose requirement it meets. The last workgroup of each strip adds the
- * partial sums in a fixed order, so results are deterministic. Calls that may overlap in time
- * (different streams) need separate workspaces. With workspace == NULL, or workspace_bytes below
- * the requirement, K is not split across workgroups and the buffer is not touched (same results
- * up to fp32 summation order; slower when N is small compared with the number of compute units).
+ * Workspace (an addition to the call the pages' operation needs: workspace = NULL gives exactly
+ * that call). For M <= 8 the fastest kernel splits K across workgroups: their fp32 partial sums and
+ * one counter per column strip live in a caller-owned device buffer of mxmatvec_workspace_size()
+ * bytes (16-byte aligned). M > 8 never uses one.
+ *  - The buffer must be zero-filled once before its first use (hipMemset, or any zeroed
+ *    allocation). Every call leaves its counters at zero again, so the buffer stays valid for any
+ *    later call whose requirement it meets.
+ *  - The library cannot check the contents. A buffer whose counter region is not zero, or one that
+ *    two calls use at the same time (calls on different streams, or a graph replay that overlaps an
+ *    eager call), makes the wrong workgroup of a column strip (or none) add the partial sums: that
+ *    strip of y is then wrong or left unwritten, and later calls on the same buffer inherit the
+ *    stale counter. Zero the counter region again to recover. Calls that may overlap in time need
+ *    separate workspaces.
+ *  - The last workgroup of each strip adds the partial sums in a fixed order, so results are
+ *    deterministic.
+ *  - With workspace == NULL, or workspace_bytes below the requirement, K is not split across
+ *    workgroups and the buffer is not touched (same results up to fp32 summation order; slower
+ *    when N is small compared with the number of compute units).
  */
 int mxmatvec_run(int M, int N, int K, const void* x, const void* W, int fw, const void* Ws, void* y,
                  void* workspace, size_t workspace_bytes, void* stream);
@@ -168,26 +183,38 @@ size_t mxmatvec_workspace_size(int M, int N, int K, int fw);
 /* ------------------------------------------------------------------------------------------ */
 
 /*
- * mx_pack_run -- quantise fp32 src [rows][cols] on the GPU.
- *  f = MX_E4M3 / MX_E5M2 / MX_E2M1: blocks of 32 along cols. Per block: amax = max|x|;
- *      E = clamp(floor(log2 amax) - emax + 127, 0, 254) with emax = 8 (E4M3), 15 (E5M2) or 2
- *      (E2M1) (amax = 0 gives E = 0); codes = x * 2^(127-E) rounded to the nearest element
- *      value, ties to the even code, saturated to +-448 / +-57344 / +-6, sign kept (negative
+ * mx_pack_run -- quantise fp32 src [rows][cols] on the GPU. The pages start from tensors already
+ * held in a quantized data type with an E8M0 scale plane (WWDC26 session 330 summary, the
+ * multi-plane tensor of data and scale factors, blockFactors {32,1}); the scale rules below are the
+ * synthetic workloads' ("floor(log2(absmax)) - emax + 127" per 32-element block along K; symmetric
+ * int8 with scale = absmax/127 per 32-row group, and an int4 variant of it).
+ *  f = MX_E4M3 / MX_E5M2 / MX_E2M3 / MX_E3M2 / MX_E2M1: blocks of 32 along cols. Per block:
+ *      amax = max|x|; E = clamp(floor(log2 amax) - emax + 127, 0, 254) with emax = 8 (E4M3),
+ *      15 (E5M2), 2 (E2M3), 4 (E3M2) or 2 (E2M1), the exponent of the format's largest element
+ *      (amax = 0 gives E = 0); codes = x * 2^(127-E) rounded to the nearest element value, ties to
+ *      the even code, saturated to +-448 / +-57344 / +-7.5 / +-28 / +-6, sign kept (negative
  *      values that round to zero give -0). A block holding Inf or NaN gets E = 0xFF and zero
- *      codes. codes: [rows][cols] (E4M3, E5M2) or [rows][cols/2] (E2M1); scales: E8M0
+ *      codes. codes: [rows][cols] (E4M3, E5M2), [rows][3*cols/4] (E2M3, E3M2: element j in bits
+ *      6j..6j+5 of the row as a little-endian bit stream) or [rows][cols/2] (E2M1); scales: E8M0
  *      [rows][cols/32]. cols % 32 == 0.
  *  f = MX_INT8 / MX_INT4: src is a weight W [K=rows][N=cols], blocks of 32 along rows. Per
  *      column and block: s = fp16(amax / qmax) (fp32 division, nearest-even to fp16) with
  *      qmax = 127 or 7; q = clamp(round_half_even(fp32(w / s)), -qmax, qmax), q = 0 where
- *      s = 0. codes: int8 [rows][cols] or packed int4 [rows][cols/2]; scales: binary16
- *      [rows/32][cols]. rows % 32 == 0; cols % 2 == 0 for MX_INT4.
+ *      s = 0. A block holding Inf or NaN gets s = NaN (0x7E00) and q = 0. codes: int8
+ *      [rows][cols] or packed int4 [rows][cols/2] (TensorOps notes, "VALIDATED ON M4 MAX",
+ *      fact 5); scales: binary16 [rows/32][cols]. rows % 32 == 0; cols % 2 == 0 for MX_INT4.
+ * Errors: MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_FORMAT (f not listed), MX_ERR_ALIGN, MX_ERR_ARCH,
+ * MX_ERR_LAUNCH; nothing is queued on an error.
  */
 int mx_pack_run(int f, const float* src, int rows, int cols, void* codes, void* scales, void* stream);
 
 /*
  * mx_unpack_run -- dequantise to fp32 on the GPU: out = fp32(value * scale), the exact product
- * rounded once to fp32 (nearest even; subnormals kept; overflow gives +-Inf; NaN propagates).
- * Layouts as in mx_pack_run (MX: scales along cols; INT8/INT4: scales along rows).
+ * rounded once to fp32 (nearest even; subnormals kept; overflow gives +-Inf; NaN propagates). This
+ * is the dequantisation the pages' matmul applies to each element in the kernel (TensorOps notes,
+ * "Scale planes": value times its block's power-of-two scale; "Kernel-phase findings": int weights
+ * times their fp16 block scale), written out as its own result. Layouts as in mx_pack_run (MX:
+ * scales along cols; INT8/INT4: scales along rows). Errors as for mx_pack_run.
  */
 int mx_unpack_run(int f, const void* codes, const void* scales, int rows, int cols, float* out,
                   void* stream);
@@ -199,10 +226,10 @@ int mx_unpack_run(int f, const void* codes, const void* scales, int rows, int co
 int mx_pack_host(int f, const float* src, int64_t rows, int64_t cols, void* codes, void* scales);
 int mx_unpack_host(int f, const void* codes, const void* scales, int64_t rows, int64_t cols, float* out);
 
-/* Single-element encoder/decoder of the host codec. mx_encode_host: f = MX_E4M3, MX_E5M2 or
- * MX_E2M1, nearest code, ties to even, saturating, sign kept (0 for other f). mx_decode_host:
- * f = MX_E4M3, MX_E5M2, MX_E2M1 (low nibble), MX_E8M0, MX_INT8 or MX_INT4 (low nibble); NaN for
- * other f. */
+/* Single-element encoder/decoder of the host codec. mx_encode_host: f = MX_E4M3, MX_E5M2,
+ * MX_E2M3, MX_E3M2 or MX_E2M1, nearest code, ties to even, saturating, sign kept (0 for other f).
+ * mx_decode_host: f = MX_E4M3, MX_E5M2, MX_E2M3 / MX_E3M2 (low 6 bits), MX_E2M1 (low nibble),
+ * MX_E8M0, MX_INT8 or MX_INT4 (low nibble); NaN for other f. */
 uint8_t mx_encode_host(int f, float v);
 float mx_decode_host(int f, uint8_t code);
 

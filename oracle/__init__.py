@@ -48,7 +48,7 @@ def lib():
     L = ctypes.CDLL(_LIB)
     d, u, i, i64, p = ctypes.c_double, ctypes.c_uint, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
     sig = {
-        "orc_num_threads": (i, []),
+        "orc_num_threads": (i, []), "orc_set_threads": (None, [i]),
         "orc_dec_e4m3": (d, [u]), "orc_dec_e5m2": (d, [u]), "orc_dec_e2m1": (d, [u]), "orc_dec_e8m0": (d, [u]),
         "orc_dec_e2m3": (d, [u]), "orc_dec_e3m2": (d, [u]),
         "orc_dec_int4": (d, [u]), "orc_dec_f16": (d, [u]),
@@ -83,6 +83,10 @@ def _ptr(a: np.ndarray):
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_threads(n: int) -> None:
+    lib().orc_set_threads(int(n))
 
 
 # ---- decoders (vectorised over a code array) -------------------------------------------------

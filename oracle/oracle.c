@@ -41,6 +41,15 @@
 
 enum { ORC_E4M3 = 0, ORC_E5M2 = 1, ORC_E2M3 = 2, ORC_E3M2 = 3, ORC_E2M1 = 4, ORC_F16 = 16, ORC_INT8 = 32, ORC_INT4 = 33 };
 
+/* Threads the parallel loops below use from now on (test / benchmark plumbing, no arithmetic). */
+void orc_set_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int orc_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

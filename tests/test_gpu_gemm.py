@@ -4,7 +4,8 @@ Inputs are seeded fp32 sources; the GPU quantises them with mx_pack_run, the ora
 quantiser, and the two code/scale planes must agree bit for bit before the products are compared.
 Products must meet |C_gpu - C_ref| <= 2^-10 |C_ref| + 1e-3 sqrt(K) R (R = rms of |a_mk b_kn|), with
 NaN positions equal. Small and ragged shapes are compared on every output; the full-size
-workloads on sampled outputs (all four corners included) plus a finiteness check of all of C.
+workloads on sampled outputs (all four corners included) plus a finiteness check of all of C, which
+starts NaN-filled, so that check also proves every output was written.
 """
 import os
 
@@ -457,4 +458,159 @@ def test_f16_square_full_size_sampled(orc):
     ref = orc.gemm_f16_points(A, B, ms, ns)
     ok, ratio, bad = orc.check(C[ms, ns], ref, K, orc.rms_ab(A.astype(np.float64), B.astype(np.float64)))
     say(f"f16 square: worst err/bound {ratio:.3f}")
+    assert ok, (ratio, bad)
+
+
+def with_tile(tile, fn):
+    old = os.environ.get("MXGEMM_TILE")
+    if tile is not None:
+        os.environ["MXGEMM_TILE"] = str(tile)
+    try:
+        return fn()
+    finally:
+        if tile is not None:
+            if old is None:
+                del os.environ["MXGEMM_TILE"]
+            else:
+                os.environ["MXGEMM_TILE"] = old
+
+
+def pair_case(orc, api, fa, fb, M, N, K, seed, tile=None, sigma_b=1.0):
+    """GPU-packed MX operands of formats fa / fb, checked bit-exact against the oracle's packing;
+    returns (C, oracle C, R)."""
+    a_src = synth.normal((M, K), 1.0, seed)
+    b_src = synth.normal((N, K), sigma_b, seed + 1)
+    A, SA = gpu_mx_pack(api, fa, a_src)
+    B, SB = gpu_mx_pack(api, fb, b_src)
+    oA, oSA = orc.mx_quantize(fa, a_src)
+    oB, oSB = orc.mx_quantize(fb, b_src)
+    assert np.array_equal(host(A), oA) and np.array_equal(host(SA), oSA)
+    assert np.array_equal(host(B), oB) and np.array_equal(host(SB), oSB)
+    C = with_tile(tile, lambda: gpu_gemm(api, fa, A, SA, B, SB, M, N, K, fb=fb))
+    ref = orc.mxgemm(fa, fb, oA, oSA, oB, oSB, M, N, K)
+    R = orc.rms_ab(orc.dequant(fa, oA, oSA, M, K), orc.dequant(fb, oB, oSB, N, K).T)
+    return C, ref, R
+
+
+@pytest.mark.parametrize("fa,fb,tile,M,N,K", [
+    (0, 0, 8, 512, 1024, 1024), (4, 4, 8, 512, 1024, 2048), (0, 4, 8, 512, 1024, 1024),
+    (4, 0, 8, 512, 1024, 1024), (1, 1, 8, 512, 1024, 1024), (2, 3, 8, 512, 1024, 1024),
+    (0, 0, 8, 1024, 1024, 512), (0, 0, 9, 512, 896, 1024), (4, 4, 9, 512, 896, 2048),
+    (0, 4, 9, 512, 896, 1024), (0, 0, 10, 512, 768, 1024), (4, 4, 10, 512, 768, 2048),
+])
+def test_mx_ring_xcd_remap_every_output(orc, fa, fb, tile, M, N, K):
+    """Ring grids of 8 or 16 tiles, where workgroup ids are remapped so that each XCD takes a
+    contiguous range of tiles: every output against the oracle (the remap is a permutation of the
+    tiles; a wrong one leaves tiles unwritten, and the NaN-filled C shows them)."""
+    api = require_gpu()
+    say(f"ring remap fa={fa} fb={fb} tile={tile} M={M} N={N} K={K}")
+    C, ref, R = pair_case(orc, api, fa, fb, M, N, K, 1300 + M + N + K + tile, tile=tile)
+    assert not np.isnan(C).any()
+    ok, ratio, bad = orc.check(C, ref, K, R)
+    assert ok, (ratio, bad)
+
+
+def test_f16_ring_xcd_remap_every_output(orc):
+    """The fp16 ring on a grid of 8 tiles (remapped), every output."""
+    api = require_gpu()
+    M, N, K = 512, 1024, 512
+    say("f16 ring remap")
+    A, B, C = fp16_case(orc, api, M, N, K, 1400, tile=8)
+    assert not np.isnan(C).any()
+    ok, ratio, bad = orc.check(C, orc.gemm_f16(A, B), K, orc.rms_ab(A.astype(np.float64), B.astype(np.float64)))
+    assert ok, (ratio, bad)
+
+
+def nonfinite_operands(fa, fb, M, N, K, seed):
+    """Random codes of small magnitude with NaN scales, NaN codes (where the format has them) and
+    the extreme scales 0x00 / 0xFE planted in rows of A and columns of B."""
+    def codes(fmt, rows, s):
+        if fmt == 4:
+            return synth.random_bytes((rows, K // 2), s)
+        if fmt in (2, 3):
+            return synth.random_bytes((rows, K // 4 * 3), s)
+        b = synth.random_bytes((rows, K), s)
+        e = synth.random_ints((rows, K), 0, 8, s + 1000) if fmt == 0 else synth.random_ints((rows, K), 8, 16, s + 1000)
+        return ((b & 0x87) | (e << 3)).astype(np.uint8) if fmt == 0 else ((b & 0x83) | (e << 2)).astype(np.uint8)
+    A, B = codes(fa, M, seed), codes(fb, N, seed + 1)
+    SA = synth.random_ints((M, K // 32), 118, 128, seed + 2)
+    SB = synth.random_ints((N, K // 32), 118, 128, seed + 3)
+    SA[3, 2] = 0xFF                      # NaN scale: row 3
+    SB[10, K // 32 - 1] = 0xFF           # NaN scale in the last K-block: column 10
+    SA[5, 1:] = 0                        # 2^-127: tiny but finite products in row 5
+    SA[:, 0] = 1                         # block 0: 2^-126 on every row of A ...
+    SB[20, 0] = 254                      # ... so the largest scale 2^127 on column 20 stays in range
+    SB[N - 1, 3] = 0xFF                  # NaN scale on the last column (a partial tile's edge)
+    if fa in (0, 1):
+        A[7, K // 2 + 1] = 0x7F          # NaN code (E4M3 S.1111.111, E5M2 S.11111.11): row 7
+    if fb in (0, 1):
+        B[30, 200] = 0xFF                # NaN code: column 30
+    return A, SA, B, SB
+
+
+@pytest.mark.parametrize("fa,fb,tile,M,N,K", [
+    (0, 0, 8, 300, 520, 512), (0, 0, 9, 257, 452, 1024), (0, 0, 10, 300, 388, 512),
+    (4, 4, 8, 300, 520, 1024), (4, 4, 9, 257, 452, 1024), (4, 4, 10, 300, 388, 2048),
+    (0, 4, 8, 300, 520, 512), (4, 0, 9, 300, 520, 1024), (1, 1, 8, 300, 520, 512), (1, 4, 8, 64, 260, 1024),
+    (2, 3, 8, 300, 520, 512),
+])
+def test_mx_ring_nonfinite_and_extreme_scales(orc, fa, fb, tile, M, N, K):
+    """The ring kernels with NaN scales, NaN codes and the extreme scales: NaN positions equal the
+    oracle's and every finite output meets the bound (each operand's scales reach the MFMA through
+    their own op_sel byte packing, so a scale fed to the wrong K-step or row shows up)."""
+    api = require_gpu()
+    say(f"ring nonfinite fa={fa} fb={fb} tile={tile} M={M} N={N} K={K}")
+    A, SA, B, SB = nonfinite_operands(fa, fb, M, N, K, 2000 + tile + fa + fb)
+    C = with_tile(tile, lambda: gpu_gemm(api, fa, dev(A), dev(SA), dev(B), dev(SB), M, N, K, fb=fb))
+    ref = orc.mxgemm(fa, fb, A, SA, B, SB, M, N, K)
+    assert np.isnan(ref[3]).all() and np.isnan(ref[:, 10]).all() and np.isnan(ref[:, N - 1]).all()
+    R = orc.rms_ab(np.nan_to_num(orc.dequant(fa, A, SA, M, K)), np.nan_to_num(orc.dequant(fb, B, SB, N, K)).T)
+    ok, ratio, bad = orc.check(C, ref, K, R)
+    assert ok, (ratio, bad)
+
+
+@pytest.mark.parametrize("tile", [8, 9, 10])
+def test_mx_ring_relu_nan(orc, tile):
+    """ReLU on the ring maps NaN products (NaN scale, NaN code) to 0 and clips the negatives."""
+    api = require_gpu()
+    M, N, K = 300, 520, 1024
+    say(f"ring relu nan tile={tile}")
+    A, SA, B, SB = nonfinite_operands(0, 0, M, N, K, 2100 + tile)
+    C = with_tile(tile, lambda: gpu_gemm(api, 0, dev(A), dev(SA), dev(B), dev(SB), M, N, K, flags=api.MXGEMM_RELU))
+    ref = orc.mxgemm(0, 0, A, SA, B, SB, M, N, K)
+    assert np.isnan(ref[3]).all() and (C[3] == 0).all() and (C[:, 30] == 0).all()
+    R = orc.rms_ab(np.nan_to_num(orc.dequant(0, A, SA, M, K)), np.nan_to_num(orc.dequant(0, B, SB, N, K)).T)
+    ok, ratio, bad = orc.check(C, orc.relu(ref), K, R)
+    assert ok, (ratio, bad)
+
+
+def test_mx_e5m2_infinity_codes(orc):
+    """E5M2 Inf codes (S.11111.00) are infinities: an output with one infinite term is that
+    infinity, +Inf + -Inf gives NaN, and Inf times a zero element gives NaN, as in the oracle's
+    IEEE fp64 sum. Compared exactly at those outputs and under the bound elsewhere."""
+    api = require_gpu()
+    M, N, K = 256, 512, 1024
+    say("e5m2 infinity codes")
+    g = np.random.Generator(np.random.PCG64(1500))
+
+    def codes(shape):   # finite nonzero magnitudes 2^-2 .. 1.75*2^2
+        return ((g.integers(0, 2, size=shape) << 7) | (g.integers(13, 18, size=shape) << 2)
+                | g.integers(0, 4, size=shape)).astype(np.uint8)
+    A, B = codes((M, K)), codes((N, K))
+    SA = np.full((M, K // 32), 127, np.uint8)
+    SB = np.full((N, K // 32), 127, np.uint8)
+    A[1, 100] = 0x7C                     # +Inf in row 1
+    A[2, 700] = 0xFC                     # -Inf in row 2
+    B[5, 40] = 0x7C                      # +Inf in column 5
+    A[2, 40] = 0x40                      # row 2 at K=40: +2, so (2, 5) holds -Inf and +Inf: NaN
+    B[9, 100] = 0x00                     # column 9 at K=100: zero, so (1, 9) holds Inf * 0: NaN
+    B[5, 700] = 0x3C                     # +1: (2, 5) also holds -Inf * 1
+    B[0, 100] = B[0, 700] = 0x3C         # +1: (1, 0) = +Inf, (2, 0) = -Inf
+    C = gpu_gemm(api, 1, dev(A), dev(SA), dev(B), dev(SB), M, N, K)
+    ref = orc.mxgemm(1, 1, A, SA, B, SB, M, N, K)
+    assert np.isnan(ref[2, 5]) and np.isnan(ref[1, 9]) and ref[1, 0] == np.inf and ref[2, 0] == -np.inf
+    assert ref[0, 5] in (np.inf, -np.inf)
+    R = orc.rms_ab(np.nan_to_num(orc.dequant(1, A, SA, M, K), posinf=0, neginf=0),
+                   np.nan_to_num(orc.dequant(1, B, SB, N, K), posinf=0, neginf=0).T)
+    ok, ratio, bad = orc.check(C, ref, K, R)
     assert ok, (ratio, bad)
