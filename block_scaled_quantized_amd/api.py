@@ -17,6 +17,8 @@ MX_E4M3, MX_E5M2, MX_E2M3, MX_E3M2, MX_E2M1, MX_E8M0, MX_F16, MX_INT8, MX_INT4 =
 MXGEMM_RELU = 1  # mxgemm_create flag: C = max(A*B, 0) in the epilogue
 MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_FORMAT, MX_ERR_ARCH, MX_ERR_LAUNCH, MX_ERR_NOMEM = \
     0, -1, -2, -3, -4, -5, -6, -7
+MX_ERR_SCRATCH = -8
+MXMATVEC_SCRATCH_BYTES = 8 << 20   # static scratch of mxmatvec_run_noalloc, per GPU
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_scaled_quantized_amd.build`")
@@ -33,6 +35,7 @@ EXPORTS = {
     "mxgemm_plan_info": (_i, [_vp, ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "mxmatvec_run": (_i, [_i, _i, _i, _vp, _vp, _i, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "mxmatvec_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
+    "mxmatvec_run_noalloc": (_i, [_i, _i, _i, _vp, _vp, _i, _vp, _vp, _vp]),
     "mx_pack_run": (_i, [_i, _vp, _i, _i, _vp, _vp, _vp]),
     "mx_unpack_run": (_i, [_i, _vp, _vp, _i, _i, _vp, _vp]),
     "mx_pack_host": (_i, [_i, _vp, _i64, _i64, _vp, _vp]),
@@ -133,6 +136,12 @@ def mxmatvec_run(M: int, N: int, K: int, x, W, fw: int, Ws, y, workspace=None, w
         workspace_bytes = workspace.numel() * workspace.element_size()
     _check(_lib.mxmatvec_run(M, N, K, _ptr(x), _ptr(W), fw, _ptr(Ws), _ptr(y), _ptr(workspace),
                              int(workspace_bytes or 0), _stream(stream)), "mxmatvec_run")
+
+
+def mxmatvec_run_noalloc(M: int, N: int, K: int, x, W, fw: int, Ws, y, stream=None) -> None:
+    """mxmatvec_run with the library's static scratch array in place of a workspace."""
+    _check(_lib.mxmatvec_run_noalloc(M, N, K, _ptr(x), _ptr(W), fw, _ptr(Ws), _ptr(y), _stream(stream)),
+           "mxmatvec_run_noalloc")
 
 
 def mxmatvec_workspace_size(M: int, N: int, K: int, fw: int) -> int:

@@ -13,6 +13,8 @@ int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void
 int matvec_launch(int M, int N, int K, const void* x, const void* W, bool int8, const void* Ws, void* y, void* ws,
                   size_t ws_bytes, hipStream_t stream);
 size_t matvec_workspace(int M, int N, int K, bool int8);
+int matvec_launch_noalloc(int M, int N, int K, const void* x, const void* W, bool int8, const void* Ws, void* y,
+                          hipStream_t stream);
 
 namespace {
 constexpr int kMaxDevices = 64;
@@ -115,6 +117,7 @@ const char* mx_strerror(mx_status s) {
     case MX_ERR_ARCH: return "current device is not gfx950 (or no device)";
     case MX_ERR_LAUNCH: return "kernel launch failed";
     case MX_ERR_NOMEM: return "host allocation failed";
+    case MX_ERR_SCRATCH: return "the shape needs more workspace than the library's static scratch array holds";
     default: return "unknown status";
   }
 }
@@ -207,6 +210,16 @@ int mxmatvec_run(int M, int N, int K, const void* x, const void* W, int fw, cons
   if (int a = check_arch()) return a;
   return matvec_launch(M, N, K, x, W, fw == MX_INT8, Ws, y, workspace, workspace ? workspace_bytes : 0,
                        as_stream(stream));
+}
+
+int mxmatvec_run_noalloc(int M, int N, int K, const void* x, const void* W, int fw, const void* Ws, void* y,
+                         void* stream) {
+  if (!x || !W || !Ws || !y) return MX_ERR_NULL;
+  if (int s = matvec_shape(M, N, K, fw)) return s;
+  if (!aligned16(x) || !aligned16(W) || !aligned16(Ws) || !aligned16(y)) return MX_ERR_ALIGN;
+  if (M <= 8 && matvec_workspace(M, N, K, fw == MX_INT8) > MXMATVEC_SCRATCH_BYTES) return MX_ERR_SCRATCH;
+  if (int a = check_arch()) return a;
+  return matvec_launch_noalloc(M, N, K, x, W, fw == MX_INT8, Ws, y, as_stream(stream));
 }
 
 }  // extern "C"

@@ -23,6 +23,8 @@
 //    an fp32 accumulator; the waves' accumulators meet in LDS, and the sum is rounded once to
 //    fp16.
 //  - Loads run P blocks ahead of the MFMAs through a ring of registers.
+#include <mutex>
+
 #include "codec_math.h"
 
 using namespace mx;
@@ -854,10 +856,70 @@ int launch_wq(int M, int N, int K, const void* x, const void* W, const void* Ws,
   return launch_wq_mt<I8, 8, 4, 4, 2>(M, N, K, x, W, Ws, y, st);
 }
 
+// ---- the variant that allocates nothing ---------------------------------------------------------
+// The split kernel's workspace (counters, then partial sums) lives in this array instead of a
+// caller buffer. Every GPU the library runs on holds its own copy until the process ends; the host
+// name `scratch` is only a stand-in for it, so host code uses the address hipGetSymbolAddress gives
+// for the current device and nothing else. Counters start at zero (the array is zero-initialised
+// static storage, and the first call on a device also queues a clearing kernel ahead of the first
+// matvec); every call leaves them at zero again.
+constexpr size_t kScratchBytes = MXMATVEC_SCRATCH_BYTES;
+static_assert(kScratchBytes > kCounterBytes && kScratchBytes % 256 == 0, "scratch layout");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+__global__ __launch_bounds__(256) void clear_counters_kernel(unsigned* __restrict__ c, int n) {
+  const int i = (int)(blockIdx.x * 256 + threadIdx.x);
+  if (i < n) c[i] = 0u;
+}
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of this device's scratch array, set up on the first call on the device (the
+// clearing kernel goes on `st`, ahead of whatever the caller queues next).
+int scratch_address(hipStream_t st, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) {
+    (void)hipGetLastError();
+    return MX_ERR_ARCH;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return MX_ERR_LAUNCH;
+    }
+    constexpr int n = (int)(kCounterBytes / 4);
+    hipLaunchKernelGGL(clear_counters_kernel, dim3((n + 255) / 256), dim3(256), 0, st, (unsigned*)p, n);
+    if (hipGetLastError() != hipSuccess) return MX_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MX_OK;
+}
+
 }  // namespace
 
 namespace mx {
 size_t matvec_workspace(int M, int N, int K, bool int8) { return M > 8 ? 0 : split_plan(M, N, K, int8).bytes; }
+
+// mxmatvec_run with the split kernel's workspace in the static scratch array: the same kernels and
+// launch shapes as a call with a large enough caller workspace, so the same results bit for bit.
+int matvec_launch_noalloc(int M, int N, int K, const void* x, const void* W, bool int8, const void* Ws, void* y,
+                          hipStream_t stream) {
+  if (M > 8)
+    return int8 ? launch_wq<true>(M, N, K, x, W, Ws, y, stream) : launch_wq<false>(M, N, K, x, W, Ws, y, stream);
+  const size_t need = split_plan(M, N, K, int8).bytes;
+  if (need > kScratchBytes) return MX_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    if (int s = scratch_address(stream, &ws)) return s;
+  }
+  return int8 ? launch<true>(M, N, K, x, W, Ws, y, ws, need, stream)
+              : launch<false>(M, N, K, x, W, Ws, y, ws, need, stream);
+}
 
 int matvec_launch(int M, int N, int K, const void* x, const void* W, bool int8, const void* Ws, void* y, void* ws,
                   size_t ws_bytes, hipStream_t stream) {

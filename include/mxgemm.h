@@ -47,7 +47,8 @@ typedef enum {
   MX_ERR_FORMAT = -4,  /* unsupported format or format pair */
   MX_ERR_ARCH = -5,    /* the current device is not gfx950, or no device is present */
   MX_ERR_LAUNCH = -6,  /* the HIP runtime reported an error when queueing a kernel */
-  MX_ERR_NOMEM = -7    /* host allocation of a plan failed */
+  MX_ERR_NOMEM = -7,   /* host allocation of a plan failed */
+  MX_ERR_SCRATCH = -8  /* mxmatvec_run_noalloc: the shape needs more than MXMATVEC_SCRATCH_BYTES */
 } mx_status;
 
 /* MX_E8M0 names the scale format; it is accepted only by mx_decode_host. */
@@ -177,6 +178,29 @@ int mxmatvec_run(int M, int N, int K, const void* x, const void* W, int fw, cons
 /* Workspace bytes mxmatvec_run uses for this shape (0: none needed, or an invalid shape). For
  * 1 <= M <= 8 the requirement never decreases as M grows for fixed N, K and fw; for M > 8 it is 0. */
 size_t mxmatvec_workspace_size(int M, int N, int K, int fw);
+
+/* Size of the library's static scratch array (8 MiB), the most workspace mxmatvec_run_noalloc can
+ * use. It covers the decode shapes up to N = 14336 at K = 4096 for int8 and int4 at any M <= 8. */
+#define MXMATVEC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/*
+ * mxmatvec_run_noalloc -- mxmatvec_run for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same operation, arguments,
+ * shape rules and kernels as mxmatvec_run with a large enough workspace, and the same results bit
+ * for bit, but the split kernel's workspace is a static device array inside the library
+ * (MXMATVEC_SCRATCH_BYTES per GPU, held until the process ends). Nothing is allocated, by the
+ * library or any library it calls.
+ *  - Shapes whose workspace requirement (mxmatvec_workspace_size) exceeds MXMATVEC_SCRATCH_BYTES
+ *    return MX_ERR_SCRATCH before anything is queued; use mxmatvec_run with a workspace for them.
+ *  - All calls on one GPU share that GPU's array, which keeps the last call's contents (its
+ *    counters are back at zero after every call). Calls that overlap in time on one GPU (different
+ *    streams, or a captured graph replaying beside another call) race on it and give wrong results:
+ *    serialise them, or use mxmatvec_run with separate workspaces.
+ *  - The first call on a GPU looks up the array's device address and queues a small kernel that
+ *    zeroes the counters on `stream` ahead of its own work.
+ */
+int mxmatvec_run_noalloc(int M, int N, int K, const void* x, const void* W, int fw, const void* Ws, void* y,
+                         void* stream);
 
 /* ------------------------------------------------------------------------------------------ */
 /* Codecs on the GPU (bit-exact with the host codecs below).                                    */

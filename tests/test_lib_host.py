@@ -279,3 +279,21 @@ def test_small_m_gemm_shape_rules():
         assert api.mxmatvec_workspace_size(M, 4096, 4096, api.MX_INT8) == 0
     assert api.mxmatvec_workspace_size(257, 4096, 4096, api.MX_INT8) == 0     # invalid shape
     assert api.mxmatvec_workspace_size(8, 4096, 4096, api.MX_INT8) > 0
+
+
+def test_noalloc_rejects_shapes_beyond_the_scratch():
+    """mxmatvec_run_noalloc refuses, before touching any device, a shape whose split workspace is
+    larger than the static scratch array; shape and pointer errors come first as for mxmatvec_run."""
+    M, N, K = 8, 32768, 16384
+    need = api.mxmatvec_workspace_size(M, N, K, api.MX_INT8)
+    assert need > api.MXMATVEC_SCRATCH_BYTES
+    fake = 1 << 20                                    # aligned addresses; nothing is dereferenced
+    assert api._lib.mxmatvec_run_noalloc(M, N, K, fake, fake, api.MX_INT8, fake, fake, None) == api.MX_ERR_SCRATCH
+    assert api._lib.mxmatvec_run_noalloc(M, N, K, None, fake, api.MX_INT8, fake, fake, None) == api.MX_ERR_NULL
+    assert api._lib.mxmatvec_run_noalloc(M, N, 48, fake, fake, api.MX_INT8, fake, fake, None) == api.MX_ERR_SHAPE
+    assert api._lib.mxmatvec_run_noalloc(M, N, K, fake + 8, fake, api.MX_INT8, fake, fake, None) == api.MX_ERR_ALIGN
+    assert "scratch" in api.mx_strerror(api.MX_ERR_SCRATCH)
+    # the decode workloads fit
+    for fw in (api.MX_INT8, api.MX_INT4):
+        for m in (1, 8):
+            assert 0 < api.mxmatvec_workspace_size(m, 14336, 4096, fw) <= api.MXMATVEC_SCRATCH_BYTES
