@@ -93,7 +93,7 @@ def test_int_pack_unpack_bitexact(orc, fw, shape):
         w[32:64, 3] = 0.0
         w[0:32, 5] *= np.float32(1e-30)
         w[40, 6] = np.inf                    # non-finite blocks: NaN scale, zero codes
-        w[70, 7] = np.nan
+        w[45, 7] = np.nan
         w[2, 8] = -np.inf
     codes, scales = gpu_int_pack(api, fw, w)
     q, s = orc.int_quantize(fw, w)
