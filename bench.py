@@ -426,7 +426,7 @@ def main():
         torch.cuda.synchronize()
         cpu = cpu_baseline(np, synth, C0, keep, args.cpu_seconds)
 
-    kname = {3: "gemm_ring_kernel", 2: "gemm_pp_kernel"}.get(tile[3], "gemm_kernel")
+    kname = {4: "gemm_pp_ring_kernel", 3: "gemm_ring_kernel", 2: "gemm_pp_kernel"}.get(tile[3], "gemm_kernel")
     traffic, traffic_src = hbm_traffic(kname, list(tile), (M, N, K))
 
     out = {

@@ -54,7 +54,8 @@ namespace {
 
 struct TileInfo {
   int bm, bn, waves, variant;  // variant: 0 = 4 waves, 1 = 8 waves, 2 = 8-wave ping-pong (MX only),
-                               // 3 = 4-stage LDS ring (MX formats; fp16 on 256x256)
+                               // 3 = 4-stage LDS ring (MX formats; fp16 on 256x256),
+                               // 4 = 8-wave ping-pong ring (E4M3, E2M1)
   int eff[3];                  // measured relative efficiency per kind (E4M3, E2M1, F16), percent
 };
 // Tile ids understood by gemm_launch. The efficiencies rank the tiles (MI355X measurements at the
@@ -62,14 +63,16 @@ struct TileInfo {
 // ring runs the prefill shape in two whole rounds but no faster than the 256x256 ring's 1.75, so it
 // is ranked below it; a partial last round runs faster per tile than a full one, the chip being
 // shared-resource bound). The 256x192 ring wins where it makes whole rounds and 256x256 does not
-// (M=2048, N=12288: 95 against 101 us).
+// (M=2048, N=12288: 95 against 101 us). The 8-wave ping-pong GEMM with 128-byte stage rows (tile
+// 11, E4M3 / E2M1 with K % 1024 == 0) runs the MXFP8 prefill shape in 108-112 us against the ring's
+// 119 us, and the MXFP4 4096 x 8192 x 8192 shape in 133 us against 146-151 us.
 constexpr TileInfo kTiles[] = {
     {256, 256, 4, 0, {85, 85, 90}}, {256, 224, 4, 0, {80, 75, 55}}, {128, 128, 4, 0, {50, 45, 50}},
     {64, 64, 4, 0, {25, 25, 25}},   {256, 256, 8, 1, {90, 100, 100}}, {256, 224, 8, 1, {88, 95, 60}},
     {256, 256, 8, 2, {60, 60, 99}}, {256, 224, 8, 2, {100, 95, 60}}, {256, 256, 4, 3, {200, 200, 200}},
-    {256, 224, 4, 3, {170, 160, 1}}, {256, 192, 4, 3, {170, 160, 1}}};
+    {256, 224, 4, 3, {170, 160, 1}}, {256, 192, 4, 3, {170, 160, 1}}, {256, 256, 8, 4, {215, 220, 1}}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
-constexpr int kRingTile = 8, kRingTile224 = 9, kRingTile192 = 10;
+constexpr int kRingTile = 8, kRingTile224 = 9, kRingTile192 = 10, kPPRingTile = 11;
 constexpr int kCUs = 256;
 
 // Whether ring tile `tile` (8: 256x256, 9: 256x224) runs the ring kernel for this problem; the
@@ -92,6 +95,7 @@ int choose_tile(int kind, int M, int N, int K) {
   double best_cost = 1e300;
   for (int t = 0; t < kNumTiles; t++) {
     if ((t == kRingTile || t == kRingTile224 || t == kRingTile192) && !ring_ok(kind, N, K, t)) continue;
+    if (t == kPPRingTile && !(kind <= 1 && K % 1024 == 0 && N % 4 == 0)) continue;
     const int64_t tiles = (int64_t)((M + kTiles[t].bm - 1) / kTiles[t].bm) * ((N + kTiles[t].bn - 1) / kTiles[t].bn);
     const int64_t waves = (tiles + kCUs - 1) / kCUs;
     const double cost = (double)waves * kTiles[t].bm * kTiles[t].bn * 100.0 / kTiles[t].eff[kind];
@@ -165,9 +169,16 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
   *tile_m = t.bm;
   *tile_n = t.bn;
   *tile_k = p->kind == 0 ? 128 : (p->kind == 1 ? 256 : 64);  // mixed pairs: 64 (the ring's stage)
-  if (p->tile_id == kRingTile || p->tile_id == kRingTile224 || p->tile_id == kRingTile192) {
-    // the ring, or the 8-wave kernel where it does not apply (256 x 256 in place of 256 x 192)
-    const bool ring = p->kind >= 3 || ring_ok(p->kind, p->N, p->K, p->tile_id);
+  if (p->tile_id == kPPRingTile && p->kind <= 1 && p->K % 1024 == 0 && p->N % 4 == 0) {
+    *tile_k = p->kind == 1 ? 128 : 64;  // the 8-wave ping-pong ring
+    *variant = 4;
+    return MX_OK;
+  }
+  if (p->tile_id == kRingTile || p->tile_id == kRingTile224 || p->tile_id == kRingTile192 || p->tile_id == kPPRingTile) {
+    // the ring, or the 8-wave kernel where it does not apply (256 x 256 in place of 256 x 192); tile 11
+    // where the ping-pong ring does not apply falls back as tile 8 does
+    const int rt = p->tile_id == kPPRingTile ? kRingTile : p->tile_id;
+    const bool ring = p->kind >= 3 || ring_ok(p->kind, p->N, p->K, rt);
     if (!ring && p->tile_id == kRingTile192) *tile_n = 256;
     *tile_k = ring ? (p->kind == 1 ? 128 : (p->kind == 2 ? 32 : 64)) : *tile_k;
     *variant = ring ? 3 : 1;

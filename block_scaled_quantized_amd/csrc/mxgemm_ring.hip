@@ -652,6 +652,389 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
   }
 }
 
+
+// ---- 8-wave ping-pong GEMM with 128-byte stage rows ---------------------------------------------
+// Measured on gfx950: direct global->LDS copies move about 30 bytes per clock per CU when each row
+// contributes a 64-byte run to a copy instruction, and about 58 when it contributes 128 bytes (a
+// whole cache line), whatever the number of waves issuing. The ring above stages 64 bytes of every
+// row, and its copies, not its MFMAs or fragment reads, set its speed. This kernel stages 128 bytes
+// of every row per slot (two slots of 256 + 256 rows, 64 KB each) and hides the shorter look-ahead
+// with two waves per SIMD that take turns:
+//  - Each SIMD runs waves w and w+4 of the workgroup (measured: the dispatcher places them so).
+//    While one issues the MFMAs of a step from registers (its C phase), the other queues copies
+//    and reads its fragments of the next step (its L phase); waves 4..7 run one phase behind waves
+//    0..3, and a barrier separates consecutive phases, so each barrier pairs a C phase of one group
+//    with an L phase of the other and each SIMD's matrix core always has a wave with MFMAs to issue.
+//  - Tile 256 x 256; wave w owns rows 128(w%2).. and columns 64(w/2).., 4 x 2 MFMA tiles of
+//    32 x 32: 128 accumulator registers, so two waves fit a SIMD's register file.
+//  - A step is 64 bytes of every row (one 32x32x64 K-step of E4M3, two of E2M1); slot m holds steps
+//    2m and 2m+1. Rows in a slot are 128 bytes, 16-byte chunk c of row r stored at c ^ ((r >> 1) & 7)
+//    (the 16 rows of a quarter-wave fragment read then cover all 64 banks once). A copy instruction
+//    fills 1 KB: 8 rows x 128 bytes, lane l filling physical chunk l%8 of row l/8; wave w issues
+//    instructions w + 8k (k < 4: A rows, k >= 4: B rows) of a slot.
+//  - Two steps of a wave (pp_step2): the first L phase reads the wave's fragments of both steps of
+//    the slot (96 registers), so the slot is free one step earlier and the next-but-one slot's copies
+//    (queued in the second L phase) get three steps to land.
+//  - Scales: groups of 16 bytes per row (8 K-steps: 8 E4M3 steps or 4 E2M1 steps), double buffered;
+//    group q+2 is copied (one 1 KB copy per wave) in the group's second step into the buffer of
+//    group q, whose scales were packed into registers in the step before group q began; group q+1
+//    is read and packed in group q's last step.
+//  - Both groups pass the same number of barriers: 1 after the prologue, 2 per step, and one extra
+//    (at the start for waves 4-7, at the end for waves 0-3), then the epilogue's.
+template <int KIND>
+struct PPFmt {
+  enum : int {
+    G = 8 / RingFmt<KIND>::KSTEPS,  // steps per scale group
+    SLOT2 = 512 * 128,              // bytes of one slot: 256 A + 256 B rows of 128 bytes
+    SBUF = 512 * 16                 // bytes of one scale buffer
+  };
+  static_assert(KIND == 0 || KIND == 1, "ping-pong GEMM: E4M3 x E4M3 and E2M1 x E2M1");
+};
+
+struct PPCtx {
+  rsrc_t rdata[8];
+  rsrc_t rscale;
+  uint32_t voff, svoff;
+  // LDS byte offsets within a slot of the lane's chunk h of its first A and B fragment rows (A: row
+  // 128 wm + r32; B: row 64 wn + r32 of the B region; swizzled). Chunk h + k (k = 0, 2, 4, 6) of the
+  // same row is at that offset XOR 16k: the swizzle only permutes the chunks of a row. Also the
+  // offsets of its scale rows within a scale buffer.
+  uint32_t fa0, fb0, sc_a, sc_b;
+  int wave, wm, wn, r32, h, nst, ngroups, nslots;
+};
+
+MX_DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
+
+// 16-byte LDS reads as inline assembly: the compiler then neither waits for the direct copies in
+// flight (it cannot tell which slot they fill) nor keeps one address register per slot and
+// fragment; the waits are explicit (lgkmcnt(0) at the end of each L phase). Early-clobber outputs:
+// a destination must not share a register with a later read's address. Tiles j and j+1 are 32
+// rows = 4096 bytes apart.
+template <int OFF>
+MX_DEV void pp_read4(v4i& d0, v4i& d1, v4i& d2, v4i& d3, uint32_t a0, uint32_t a1) {
+  asm volatile(
+      "ds_read_b128 %0, %4 offset:%6\n"
+      "ds_read_b128 %1, %5 offset:%6\n"
+      "ds_read_b128 %2, %4 offset:%7\n"
+      "ds_read_b128 %3, %5 offset:%7"
+      : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
+      : "v"(a0), "v"(a1), "i"(OFF), "i"(OFF + 4096));
+}
+MX_DEV void pp_read1(v4i& d, uint32_t a) { asm volatile("ds_read_b128 %0, %1" : "=&v"(d) : "v"(a)); }
+MX_DEV v8i cat8(v4i lo, v4i hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7); }
+
+// The 8 copies of slot m (its steps 2m, 2m+1: bytes 128m.. of every row) into `dst`.
+MX_DEV void pp_slot_copies(const PPCtx& c, char* dst, uint32_t m) {
+#pragma unroll
+  for (int k = 0; k < 8; k++)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff,
+                                             128u * m, 0, 0);
+}
+
+MX_DEV void pp_scale_copy(const PPCtx& c, char* sbuf, int q) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rscale, (lds_ptr_t)(sbuf + c.wave * 1024), 16, c.svoff, 16 * q, 0, 0);
+}
+
+// The lane's packed scales of a group from the 16 bytes r of its row: byte u%4 of dword u/4 is its
+// scale (K-block h) for K-step u of the group.
+MX_DEV void pp_pack(const v4i r, int h, uint32_t (&out)[2]) {
+  const uint32_t sel = h ? 0x07050301u : 0x06040200u;
+  out[0] = __builtin_amdgcn_perm((uint32_t)r[1], (uint32_t)r[0], sel);
+  out[1] = __builtin_amdgcn_perm((uint32_t)r[3], (uint32_t)r[2], sel);
+}
+
+// MFMAs of one step from the fragments f (A tiles 0..3, B tiles 4, 5) with the group's packed
+// scales; U0 = first K-step of the step within its scale group.
+template <int KIND, int U0>
+MX_DEV void pp_mfmas(const v8i (&f)[6], const uint32_t (&sa)[4][2], const uint32_t (&sb)[2][2], v16f (&acc)[2][4]) {
+  using F = RingFmt<KIND>;
+#pragma unroll
+  for (int k = 0; k < F::KSTEPS; k++)
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        if constexpr (F::FP4) {
+          const v8i bk = k ? __builtin_shufflevector(f[4 + i], f[4 + i], 4, 5, 6, 7, -1, -1, -1, -1)
+                           : __builtin_shufflevector(f[4 + i], f[4 + i], 0, 1, 2, 3, -1, -1, -1, -1);
+          const v8i ak = k ? __builtin_shufflevector(f[j], f[j], 4, 5, 6, 7, -1, -1, -1, -1)
+                           : __builtin_shufflevector(f[j], f[j], 0, 1, 2, 3, -1, -1, -1, -1);
+          if (k == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bk, ak, acc[i][j], 4, 4, U0 % 4, sb[i][U0 / 4],
+                                                                         U0 % 4, sa[j][U0 / 4]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                bk, ak, acc[i][j], 4, 4, (U0 + 1) % 4, sb[i][(U0 + 1) / 4], (U0 + 1) % 4, sa[j][(U0 + 1) / 4]);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f[4 + i], f[j], acc[i][j], 0, 0, U0 % 4,
+                                                                       sb[i][U0 / 4], U0 % 4, sa[j][U0 / 4]);
+        }
+      }
+}
+
+MX_DEV void pp_phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  raw_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The lane's fragments of both steps of a slot: x = step 2m (chunks h, 2+h of each row), y = step
+// 2m+1 (chunks 4+h, 6+h).
+MX_DEV void pp_read_slot(const PPCtx& c, const char* slot, v8i (&x)[6], v8i (&y)[6]) {
+  // (an opaque copy of the slot address: otherwise the compiler keeps the 8 sums base + offset of
+  // both slots in registers across the loop, which do not fit beside the accumulators and fragments)
+  uint32_t base = lds_addr(slot);
+  asm volatile("" : "+s"(base));
+  const uint32_t a = base + c.fa0, b = base + c.fb0;
+  v4i r[24];
+#pragma unroll
+  for (int hs = 0; hs < 2; hs++) {
+    // step hs of the slot: chunks 4 hs + h (lo) and 4 hs + 2 + h (hi)
+    const uint32_t alo = a ^ (64u * hs), ahi = a ^ (64u * hs + 32u), blo = b ^ (64u * hs), bhi = b ^ (64u * hs + 32u);
+    pp_read4<0>(r[12 * hs + 0], r[12 * hs + 1], r[12 * hs + 2], r[12 * hs + 3], alo, ahi);
+    pp_read4<8192>(r[12 * hs + 4], r[12 * hs + 5], r[12 * hs + 6], r[12 * hs + 7], alo, ahi);
+    pp_read4<0>(r[12 * hs + 8], r[12 * hs + 9], r[12 * hs + 10], r[12 * hs + 11], blo, bhi);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < 6; t++) {
+    x[t] = cat8(r[2 * t], r[2 * t + 1]);
+    y[t] = cat8(r[12 + 2 * t], r[12 + 2 * t + 1]);
+  }
+}
+
+// Raw scale rows of a group from a scale buffer, packed: sa (A tiles 0..3), sb (B tiles 0, 1).
+MX_DEV void pp_read_scales(const PPCtx& c, const char* sbuf, uint32_t (&sa)[4][2], uint32_t (&sb)[2][2]) {
+  uint32_t sbase = lds_addr(sbuf);
+  asm volatile("" : "+s"(sbase));
+  v4i rs[6];
+#pragma unroll
+  for (int j = 0; j < 4; j++) pp_read1(rs[j], sbase + c.sc_a + 512u * j);
+#pragma unroll
+  for (int i = 0; i < 2; i++) pp_read1(rs[4 + i], sbase + c.sc_b + 512u * i);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 4; j++) pp_pack(rs[j], c.h, sa[j]);
+#pragma unroll
+  for (int i = 0; i < 2; i++) pp_pack(rs[4 + i], c.h, sb[i]);
+}
+
+// Steps u = G*q + S8 and u+1 (S8 even) of a wave of group GR: L_u, C_u, L_{u+1}, C_{u+1}, each
+// phase followed by a barrier.
+//  - L_u reads the fragments of both steps of slot u/2 (`slot_cur`).
+//  - L_{u+1} queues the copies of slot u/2 + 2 (past the last slot, copies of the last one) into the
+//    slot of steps u, u+1, whose reads both groups finished in L_u; at the group's second step
+//    it also queues the scale copy of group q+2 into this group's scale buffer (packed in L_{u-1}
+//    at the latest), and at the group's last step it reads and packs the scales of group q+1.
+//  - Slot u/2 + 2 is first read in L_{u+4}: its copies must have landed before the barrier ahead
+//    of that phase, which ends C_{u+3} for waves 0-3 and L_{u+3} for waves 4-7. Each wave then has
+//    queued the 8 copies of L_{u+3} after them, and the scale copy of the group's second step when
+//    it falls in L_{u+1} or L_{u+3}: vmcnt(8) or vmcnt(9) at the end of every odd step.
+template <int KIND, int GR, int S8>
+MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* sb_cur, char* sb_nxt,
+                     uint32_t (&sa)[4][2], uint32_t (&sb)[2][2], uint32_t (&na)[4][2], uint32_t (&nb)[2][2],
+                     v16f (&acc)[2][4]) {
+  using F = RingFmt<KIND>;
+  constexpr int G = PPFmt<KIND>::G;
+  const int u = G * q + S8;
+  // the wait at the end of odd step S8+1: 8 stage copies of this L phase after the slot's, plus the
+  // scale copy when it was queued in this phase or two steps before (the group's step 1)
+  constexpr int WAIT = 8 + ((S8 + 1) % G == 1 ? 1 : 0) + ((S8 + 1) % G == 3 ? 1 : 0);
+  v8i x[6], y[6];
+  // ---- L_u
+  pp_read_slot(c, slot_cur, x, y);
+  pp_phase_barrier();
+  // ---- C_u
+  pp_mfmas<KIND, F::KSTEPS * S8>(x, sa, sb, acc);
+  pp_phase_barrier();
+  // ---- L_{u+1}
+  pp_slot_copies(c, slot_cur, (uint32_t)min(u / 2 + 2, c.nslots - 1));
+  if (S8 + 1 == 1) pp_scale_copy(c, sb_cur, min(q + 2, c.ngroups - 1));
+  if (S8 + 1 == G - 1) pp_read_scales(c, sb_nxt, na, nb);
+  if (GR == 1) wait_vm_n(WAIT);
+  pp_phase_barrier();
+  // ---- C_{u+1}
+  pp_mfmas<KIND, F::KSTEPS * (S8 + 1)>(y, sa, sb, acc);
+  if (GR == 0) wait_vm_n(WAIT);
+  pp_phase_barrier();
+  if (S8 + 1 == G - 1) {  // the next group's scales take over
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      sa[j][0] = na[j][0];
+      sa[j][1] = na[j][1];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      sb[i][0] = nb[i][0];
+      sb[i][1] = nb[i][1];
+    }
+  }
+}
+
+template <int KIND, int GR>
+MX_DEV void pp_main_loop(const PPCtx& c, char* s0, char* s1, char* sb0, char* sb1, v16f (&acc)[2][4]) {
+  constexpr int G = PPFmt<KIND>::G;
+  uint32_t sa[4][2], sb[2][2], na[4][2], nb[2][2];
+  pp_read_scales(c, sb0, sa, sb);  // group 0
+  if (GR == 1) raw_barrier();      // waves 4-7 start one phase late
+  // Two scale groups per iteration (the group count is even), so the slot and scale buffer of every
+  // step are static and the loop body has no branch: the scheduling barriers then keep every MFMA
+  // in its C phase. Slot of steps u, u+1: (u/2) % 2 (2G steps cover whole pairs of slots).
+  for (int q = 0; q < c.ngroups; q += 2) {
+#define MX_PP(S, QQ, SC, SN) \
+  pp_step2<KIND, GR, S>(c, q + QQ, ((G * QQ + S) / 2) % 2 ? s1 : s0, SC, SN, sa, sb, na, nb, acc)
+    MX_PP(0, 0, sb0, sb1); MX_PP(2, 0, sb0, sb1);
+    if constexpr (G == 8) { MX_PP(4, 0, sb0, sb1); MX_PP(6, 0, sb0, sb1); }
+    MX_PP(0, 1, sb1, sb0); MX_PP(2, 1, sb1, sb0);
+    if constexpr (G == 8) { MX_PP(4, 1, sb1, sb0); MX_PP(6, 1, sb1, sb0); }
+#undef MX_PP
+  }
+  if (GR == 0) raw_barrier();  // matches the late start of waves 4-7
+}
+
+template <int KIND>
+__global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
+  using F = RingFmt<KIND>;
+  using PF = PPFmt<KIND>;
+  constexpr int BN = 256;
+  __shared__ __attribute__((aligned(16))) char slot0[PF::SLOT2];
+  __shared__ __attribute__((aligned(16))) char slot1[PF::SLOT2];
+  __shared__ __attribute__((aligned(16))) char sbuf0[PF::SBUF];
+  __shared__ __attribute__((aligned(16))) char sbuf1[PF::SBUF];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int bid = blockIdx.x;
+  const int nwg = gridDim.x;
+  if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);  // each XCD takes a contiguous tile range
+  const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
+  const uint32_t RB = (uint32_t)p.K / (F::FP4 ? 2 : 1);  // bytes per A / B row
+  const uint32_t nblk = (uint32_t)p.K / 32;
+
+  PPCtx c;
+  c.wave = wave;
+  c.wm = wave & 1;
+  c.wn = wave >> 1;
+  c.r32 = lane & 31;
+  c.h = lane >> 5;
+  c.nst = (int)(RB / 64u);  // steps of 64 row bytes
+  c.nslots = c.nst / 2;
+  c.ngroups = c.nst / PF::G;
+  {
+    // copy instruction i = wave + 8k covers rows 8i..8i+7 of its operand; lane l fills physical chunk
+    // l%8 of row 8i + l/8, logical chunk (l%8) ^ ((row >> 1) & 7) = (l%8) ^ ((4 (i&1) + l/16) & 7),
+    // and i & 1 = wave & 1 for every copy of the wave
+    const uint32_t l = (uint32_t)lane, j = l >> 3, pc = l & 7;
+    const uint32_t lc = pc ^ ((4u * ((uint32_t)wave & 1u) + (j >> 1)) & 7u);
+    c.voff = j * RB + 16u * lc;
+  }
+  {
+    // fragment chunks: row r = 128 wm + 32 j + r32 (A) or 64 wn + 32 i + r32 (B); (r >> 1) & 7 =
+    // (r32 >> 1) & 7; tile j adds 4096 bytes (read offsets)
+    const uint32_t r32 = (uint32_t)c.r32, h = (uint32_t)c.h, sw = (r32 >> 1) & 7u;
+    const uint32_t lo = r32 * 128u + 16u * (h ^ sw);
+    c.fa0 = 16384u * (uint32_t)c.wm + lo;
+    c.fb0 = (uint32_t)BM * 128u + 8192u * (uint32_t)c.wn + lo;
+    c.sc_a = 16u * (128u * (uint32_t)c.wm + r32);
+    c.sc_b = 16u * ((uint32_t)BM + 64u * (uint32_t)c.wn + r32);
+  }
+  // per-copy buffer resources over the copy's 8 rows, clamped to the matrix (empty past the tile)
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    const int i = wave + 8 * k;
+    const bool isA = i < 32;
+    const int r0 = 8 * (isA ? i : i - 32), rows = isA ? rows_a : rows_b;
+    const int nr = max(0, min(8, rows - r0));
+    const uint8_t* base = (isA ? p.A + (int64_t)m0 * RB : p.B + (int64_t)n0 * RB) + (int64_t)(nr ? r0 : 0) * RB;
+    c.rdata[k] = make_rsrc(base, (uint32_t)nr * RB);
+  }
+  {  // scale copy of this wave: 64 rows, A rows 64w.. for w < 4, B rows 64(w-4).. after
+    const bool isA = wave < 4;
+    const int r0 = 64 * (isA ? wave : wave - 4), rows = isA ? rows_a : rows_b;
+    const int nr = max(0, min(64, rows - r0));
+    const uint8_t* base = (isA ? p.SA + (int64_t)m0 * nblk : p.SB + (int64_t)n0 * nblk) + (int64_t)(nr ? r0 : 0) * nblk;
+    c.rscale = make_rsrc(base, (uint32_t)nr * nblk);
+    c.svoff = (uint32_t)lane * nblk;
+  }
+
+  v16f acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; i++)
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+      for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
+
+  // prologue: scale groups 0 and 1, slots 0 and 1 (steps 0..3); wait for group 0 and slot 0 (the
+  // 9 copies of group 1 and slot 1 may still be in flight: the first odd step waits for them)
+  pp_scale_copy(c, sbuf0, 0);
+  pp_slot_copies(c, slot0, 0);
+  pp_scale_copy(c, sbuf1, min(1, c.ngroups - 1));
+  pp_slot_copies(c, slot1, (uint32_t)min(1, c.nslots - 1));
+  wait_vm_n(9);
+  raw_barrier();
+  if (wave < 4) pp_main_loop<KIND, 0>(c, slot0, slot1, sbuf0, sbuf1, acc);
+  else pp_main_loop<KIND, 1>(c, slot0, slot1, sbuf0, sbuf1, acc);
+  // the last steps queued copies into the free slot: let them land, and every wave finish with the
+  // slots, before they are reused for the output
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  raw_barrier();
+
+  // Epilogue: as the ring's, each wave staging 64 rows x 64 columns at a time in its own 16 KB
+  // quarter of a slot (rows padded by 8 bytes), then writing 16-byte row pieces.
+  char* stage = ((wave & 1) ? slot1 : slot0) + (wave >> 1) * 16384;
+  constexpr int WCOLS = 64, EROW = 2 * WCOLS + 8, LPR = WCOLS / 8, PIECES = 64 * LPR;
+  static_assert(64 * EROW <= 16384 && PIECES % 64 == 0, "epilogue staging");
+  const int r32 = c.r32, h = c.h;
+  const bool rows16 = (p.N & 7) == 0;
+  if (p.relu) {
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) acc[i][j][e] = fmaxf(acc[i][j][e], 0.0f);
+  }
+#pragma unroll
+  for (int j0 = 0; j0 < 4; j0 += 2) {
+#pragma unroll
+    for (int jj = 0; jj < 2; jj++)
+#pragma unroll
+      for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int qq = 0; qq < 4; qq++) {
+          v4h o;
+#pragma unroll
+          for (int e = 0; e < 4; e++) o[e] = (_Float16)acc[i][j0 + jj][4 * qq + e];
+          *reinterpret_cast<v4h*>(stage + (32 * jj + r32) * EROW + (32 * i + 8 * qq + 4 * h) * 2) = o;
+        }
+#pragma unroll
+    for (int s0 = 0; s0 < PIECES; s0 += 64) {
+      const int piece = s0 + lane, lr = piece / LPR, cp = piece % LPR;
+      const char* src = stage + lr * EROW + 16 * cp;
+      const v4h lo = *reinterpret_cast<const v4h*>(src), hi = *reinterpret_cast<const v4h*>(src + 8);
+      const int m = m0 + 128 * c.wm + 32 * j0 + lr, n = n0 + WCOLS * c.wn + 8 * cp;
+      if (m < p.M) {
+        _Float16* dst = p.C + (int64_t)m * p.N + n;
+        if (n + 8 <= p.N) {
+          if (rows16) {
+            *reinterpret_cast<v8h*>(dst) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          } else {
+            *reinterpret_cast<v4h*>(dst) = lo;
+            *reinterpret_cast<v4h*>(dst + 4) = hi;
+          }
+        } else if (n + 4 <= p.N) {
+          *reinterpret_cast<v4h*>(dst) = lo;
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 namespace mx {
@@ -719,6 +1102,28 @@ int gemm_ring_launch(int kind, int bn, int fca, int fcb, const void* A, const vo
     }
   }
 #undef MX_RING
+  return launch_status();
+}
+
+// 8-wave ping-pong ring, 256 x 256 tiles: kind 0 (E4M3 x E4M3) or 1 (E2M1 x E2M1), K % 1024 == 0
+// (an even number of scale groups), N % 4 == 0; checked by the caller.
+int gemm_pp_ring_launch(int kind, const void* A, const void* SA, const void* B, const void* SB, void* C, int M, int N,
+                        int K, bool relu, hipStream_t stream) {
+  Args a{};
+  a.A = (const uint8_t*)A;
+  a.SA = (const uint8_t*)SA;
+  a.B = (const uint8_t*)B;
+  a.SB = (const uint8_t*)SB;
+  a.C = (_Float16*)C;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.relu = relu ? 1 : 0;
+  a.tiles_m = (M + BM - 1) / BM;
+  const dim3 grid((unsigned)(a.tiles_m * ((N + 255) / 256))), block(512);
+  if (kind == 0) hipLaunchKernelGGL(gemm_pp_ring_kernel<0>, grid, block, 0, stream, a);
+  else if (kind == 1) hipLaunchKernelGGL(gemm_pp_ring_kernel<1>, grid, block, 0, stream, a);
+  else return MX_ERR_FORMAT;
   return launch_status();
 }
 }  // namespace mx

@@ -614,3 +614,36 @@ def test_mx_e5m2_infinity_codes(orc):
                    np.nan_to_num(orc.dequant(1, B, SB, N, K), posinf=0, neginf=0).T)
     ok, ratio, bad = orc.check(C, ref, K, R)
     assert ok, (ratio, bad)
+
+
+@pytest.mark.parametrize("fmt,M,N,K", [
+    (0, 300, 520, 1024), (0, 257, 260, 4096), (0, 1, 4, 1024), (0, 512, 1024, 2048), (0, 33, 1028, 3072),
+    (0, 1024, 1024, 1024),
+    (4, 300, 520, 1024), (4, 257, 260, 4096), (4, 1, 4, 2048), (4, 512, 1024, 2048), (4, 33, 1028, 3072),
+])
+def test_mx_pp_ring_every_output(orc, fmt, M, N, K):
+    """The 8-wave ping-pong ring (tile 11; K % 1024 == 0): partial tiles in M and N, a single row and
+    column strip, one pair of scale groups up to several, and grids of 8 and 16 tiles (XCD remap)."""
+    api = require_gpu()
+    say(f"pp ring fmt={fmt} M={M} N={N} K={K}")
+    C, ref, R = pair_case(orc, api, fmt, fmt, M, N, K, 1600 + M + N + K, tile=11)
+    assert not np.isnan(C).any()
+    ok, ratio, bad = orc.check(C, ref, K, R)
+    assert ok, (ratio, bad)
+
+
+@pytest.mark.parametrize("fmt", [0, 4])
+def test_mx_pp_ring_nonfinite_and_relu(orc, fmt):
+    """The ping-pong ring with NaN scales and codes, extreme scales, and the ReLU epilogue."""
+    api = require_gpu()
+    M, N, K = 300, 520, 1024
+    say(f"pp ring nonfinite fmt={fmt}")
+    A, SA, B, SB = nonfinite_operands(fmt, fmt, M, N, K, 2200 + fmt)
+    C = with_tile(11, lambda: gpu_gemm(api, fmt, dev(A), dev(SA), dev(B), dev(SB), M, N, K))
+    ref = orc.mxgemm(fmt, fmt, A, SA, B, SB, M, N, K)
+    R = orc.rms_ab(np.nan_to_num(orc.dequant(fmt, A, SA, M, K)), np.nan_to_num(orc.dequant(fmt, B, SB, N, K)).T)
+    ok, ratio, bad = orc.check(C, ref, K, R)
+    assert ok, (ratio, bad)
+    Cr = with_tile(11, lambda: gpu_gemm(api, fmt, dev(A), dev(SA), dev(B), dev(SB), M, N, K, flags=api.MXGEMM_RELU))
+    ok, ratio, bad = orc.check(Cr, orc.relu(ref), K, R)
+    assert ok, (ratio, bad)

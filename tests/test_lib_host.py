@@ -199,9 +199,16 @@ def test_ring_tile_plan_info(monkeypatch):
     assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 224, 64, 3)
     assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 224, 128, 3)
     assert info(300, 520, 416, api.MX_E4M3) == (256, 224, 128, 1)
+    monkeypatch.setenv("MXGEMM_TILE", "11")   # the 8-wave ping-pong GEMM: E4M3 / E2M1, K % 1024 == 0
+    assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 256, 64, 4)
+    assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 128, 4)
+    assert info(300, 520, 512, api.MX_E4M3) == (256, 256, 64, 3)        # K % 1024: the ring
+    assert info(300, 520, 1536, api.MX_E2M1) == (256, 256, 256, 1)      # nor the ring: 8 waves
+    assert info(512, 512, 512, api.MX_F16) == (256, 256, 32, 3)
     monkeypatch.delenv("MXGEMM_TILE")
-    assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 256, 64, 3)
-    assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 128, 3)
+    assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 256, 64, 4)
+    assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 128, 4)
+    assert info(2048, 14336, 3584, api.MX_E4M3) == (256, 256, 64, 3)   # K % 1024 != 0: the ring
     assert info(4096, 4096, 4096, api.MX_F16) == (256, 256, 32, 3)
     assert info(2048, 12288, 4096, api.MX_E4M3) == (256, 192, 64, 3)     # whole rounds of 256x192
     assert info(2048, 6144, 4096, api.MX_E4M3) == (256, 192, 64, 3)
