@@ -672,9 +672,9 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
 //    (the 16 rows of a quarter-wave fragment read then cover all 64 banks once). A copy instruction
 //    fills 1 KB: 8 rows x 128 bytes, lane l filling physical chunk l%8 of row l/8; wave w issues
 //    instructions w + 8k (k < 4: A rows, k >= 4: B rows) of a slot.
-//  - Two steps of a wave (pp_step2): the first L phase reads the wave's fragments of both steps of
-//    the slot (96 registers), so the slot is free one step earlier and the next-but-one slot's copies
-//    (queued in the second L phase) get three steps to land.
+//  - Two steps of a wave (pp_step2): the B rows of a slot are read in the first L phase, so they can
+//    be refilled one step earlier and get three steps to land (the A rows two); reads and copies are
+//    split evenly between the two L phases.
 //  - Scales: groups of 16 bytes per row (8 K-steps: 8 E4M3 steps or 4 E2M1 steps), double buffered;
 //    group q+2 is copied (one 1 KB copy per wave) in the group's second step into the buffer of
 //    group q, whose scales were packed into registers in the step before group q began; group q+1
@@ -723,10 +723,12 @@ MX_DEV void pp_read4(v4i& d0, v4i& d1, v4i& d2, v4i& d3, uint32_t a0, uint32_t a
 MX_DEV void pp_read1(v4i& d, uint32_t a) { asm volatile("ds_read_b128 %0, %1" : "=&v"(d) : "v"(a)); }
 MX_DEV v8i cat8(v4i lo, v4i hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7); }
 
-// The 8 copies of slot m (its steps 2m, 2m+1: bytes 128m.. of every row) into `dst`.
+// The copies of slot m (its steps 2m, 2m+1: bytes 128m.. of every row) into `dst`: the 4 of its A
+// rows (HALF 0) or of its B rows (HALF 1).
+template <int HALF>
 MX_DEV void pp_slot_copies(const PPCtx& c, char* dst, uint32_t m) {
 #pragma unroll
-  for (int k = 0; k < 8; k++)
+  for (int k = 4 * HALF; k < 4 * HALF + 4; k++)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff,
                                              128u * m, 0, 0);
 }
@@ -778,30 +780,42 @@ MX_DEV void pp_phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// The lane's fragments of both steps of a slot: x = step 2m (chunks h, 2+h of each row), y = step
-// 2m+1 (chunks 4+h, 6+h).
-MX_DEV void pp_read_slot(const PPCtx& c, const char* slot, v8i (&x)[6], v8i (&y)[6]) {
-  // (an opaque copy of the slot address: otherwise the compiler keeps the 8 sums base + offset of
-  // both slots in registers across the loop, which do not fit beside the accumulators and fragments)
+// Fragment reads of a slot. Step hs (0, 1) of the slot is chunks 4 hs + h (lo) and 4 hs + 2 + h (hi)
+// of each row. pp_read_ab: A tiles 0..3 and B tiles 0, 1 of step HS into f, plus B tiles 0, 1 of
+// step 1 into yb when YB; pp_read_a: A tiles 0..3 of step 1 into f. Each ends with lgkmcnt(0).
+MX_DEV uint32_t pp_base(const char* slot) {
+  // (an opaque copy of the slot address: otherwise the compiler keeps the sums base + offset of both
+  // slots in registers across the loop, which do not fit beside the accumulators and fragments)
   uint32_t base = lds_addr(slot);
   asm volatile("" : "+s"(base));
-  const uint32_t a = base + c.fa0, b = base + c.fb0;
-  v4i r[24];
-#pragma unroll
-  for (int hs = 0; hs < 2; hs++) {
-    // step hs of the slot: chunks 4 hs + h (lo) and 4 hs + 2 + h (hi)
-    const uint32_t alo = a ^ (64u * hs), ahi = a ^ (64u * hs + 32u), blo = b ^ (64u * hs), bhi = b ^ (64u * hs + 32u);
-    pp_read4<0>(r[12 * hs + 0], r[12 * hs + 1], r[12 * hs + 2], r[12 * hs + 3], alo, ahi);
-    pp_read4<8192>(r[12 * hs + 4], r[12 * hs + 5], r[12 * hs + 6], r[12 * hs + 7], alo, ahi);
-    pp_read4<0>(r[12 * hs + 8], r[12 * hs + 9], r[12 * hs + 10], r[12 * hs + 11], blo, bhi);
-  }
+  return base;
+}
+template <int HS, bool YB>
+MX_DEV void pp_read_ab(const PPCtx& c, const char* slot, v8i (&f)[6], v8i (&yb)[2]) {
+  const uint32_t base = pp_base(slot), a = base + c.fa0, b = base + c.fb0;
+  v4i r[16];
+  pp_read4<0>(r[0], r[1], r[2], r[3], a ^ (64u * HS), a ^ (64u * HS + 32u));
+  pp_read4<8192>(r[4], r[5], r[6], r[7], a ^ (64u * HS), a ^ (64u * HS + 32u));
+  pp_read4<0>(r[8], r[9], r[10], r[11], b ^ (64u * HS), b ^ (64u * HS + 32u));
+  if (YB) pp_read4<0>(r[12], r[13], r[14], r[15], b ^ 64u, b ^ 96u);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int t = 0; t < 6; t++) {
-    x[t] = cat8(r[2 * t], r[2 * t + 1]);
-    y[t] = cat8(r[12 + 2 * t], r[12 + 2 * t + 1]);
+  for (int t = 0; t < 6; t++) f[t] = cat8(r[2 * t], r[2 * t + 1]);
+  if (YB) {
+    yb[0] = cat8(r[12], r[13]);
+    yb[1] = cat8(r[14], r[15]);
   }
+}
+MX_DEV void pp_read_a(const PPCtx& c, const char* slot, v8i (&f)[6]) {
+  const uint32_t a = pp_base(slot) + c.fa0;
+  v4i r[8];
+  pp_read4<0>(r[0], r[1], r[2], r[3], a ^ 64u, a ^ 96u);
+  pp_read4<8192>(r[4], r[5], r[6], r[7], a ^ 64u, a ^ 96u);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < 4; t++) f[t] = cat8(r[2 * t], r[2 * t + 1]);
 }
 
 // Raw scale rows of a group from a scale buffer, packed: sa (A tiles 0..3), sb (B tiles 0, 1).
@@ -822,35 +836,40 @@ MX_DEV void pp_read_scales(const PPCtx& c, const char* sbuf, uint32_t (&sa)[4][2
 }
 
 // Steps u = G*q + S8 and u+1 (S8 even) of a wave of group GR: L_u, C_u, L_{u+1}, C_{u+1}, each
-// phase followed by a barrier.
-//  - L_u reads the fragments of both steps of slot u/2 (`slot_cur`).
-//  - L_{u+1} queues the copies of slot u/2 + 2 (past the last slot, copies of the last one) into the
-//    slot of steps u, u+1, whose reads both groups finished in L_u; at the group's second step
-//    it also queues the scale copy of group q+2 into this group's scale buffer (packed in L_{u-1}
-//    at the latest), and at the group's last step it reads and packs the scales of group q+1.
-//  - Slot u/2 + 2 is first read in L_{u+4}: its copies must have landed before the barrier ahead
-//    of that phase, which ends C_{u+3} for waves 0-3 and L_{u+3} for waves 4-7. Each wave then has
-//    queued the 8 copies of L_{u+3} after them, and the scale copy of the group's second step when
-//    it falls in L_{u+1} or L_{u+3}: vmcnt(8) or vmcnt(9) at the end of every odd step.
+// phase followed by a barrier. Slot u/2 (`slot_cur`) holds both steps; `slot_oth` is the other slot.
+//  - L_u reads the wave's fragments of step u and its B fragments of step u+1 (so the B rows of the
+//    slot are free after it), and queues the A-row copies of slot u/2 + 1 into the other slot, whose
+//    A rows both groups finished reading in L_{u-1}.
+//  - L_{u+1} reads the A fragments of step u+1 and queues the B-row copies of slot u/2 + 2 into this
+//    slot; at the group's second step it also queues the scale copy of group q+2 into this group's
+//    scale buffer (packed in the step before group q began), and at the group's last step it reads
+//    and packs the scales of group q+1.
+//  - (Past the last slot the copies repeat the last slot, into free rows.)
+//  - Slot u/2 + 1 is first read in L_{u+2}: its copies (B rows queued in L_{u-1}, A rows in L_u) must
+//    have landed before the barrier ahead of that phase, which ends C_{u+1} for waves 0-3 and L_{u+1}
+//    for waves 4-7. Each wave then has queued after them the 4 B-row copies of L_{u+1}, and the scale
+//    copy when L_{u+1} is the group's second step: vmcnt(4) or vmcnt(5).
+//  - Reads are split 16 + 8 and copies 4 + 4 between the two L phases, and the B rows get three steps
+//    to land, the A rows two.
 template <int KIND, int GR, int S8>
-MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* sb_cur, char* sb_nxt,
+MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char* sb_cur, char* sb_nxt,
                      uint32_t (&sa)[4][2], uint32_t (&sb)[2][2], uint32_t (&na)[4][2], uint32_t (&nb)[2][2],
                      v16f (&acc)[2][4]) {
   using F = RingFmt<KIND>;
   constexpr int G = PPFmt<KIND>::G;
+  constexpr int WAIT = 4 + ((S8 + 1) % G == 1 ? 1 : 0);
   const int u = G * q + S8;
-  // the wait at the end of odd step S8+1: 8 stage copies of this L phase after the slot's, plus the
-  // scale copy when it was queued in this phase or two steps before (the group's step 1)
-  constexpr int WAIT = 8 + ((S8 + 1) % G == 1 ? 1 : 0) + ((S8 + 1) % G == 3 ? 1 : 0);
   v8i x[6], y[6];
   // ---- L_u
-  pp_read_slot(c, slot_cur, x, y);
+  pp_read_ab<0, true>(c, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
+  pp_slot_copies<0>(c, slot_oth, (uint32_t)min(u / 2 + 1, c.nslots - 1));
   pp_phase_barrier();
   // ---- C_u
   pp_mfmas<KIND, F::KSTEPS * S8>(x, sa, sb, acc);
   pp_phase_barrier();
   // ---- L_{u+1}
-  pp_slot_copies(c, slot_cur, (uint32_t)min(u / 2 + 2, c.nslots - 1));
+  pp_read_a(c, slot_cur, *reinterpret_cast<v8i(*)[6]>(&y[0]));
+  pp_slot_copies<1>(c, slot_cur, (uint32_t)min(u / 2 + 2, c.nslots - 1));
   if (S8 + 1 == 1) pp_scale_copy(c, sb_cur, min(q + 2, c.ngroups - 1));
   if (S8 + 1 == G - 1) pp_read_scales(c, sb_nxt, na, nb);
   if (GR == 1) wait_vm_n(WAIT);
@@ -884,7 +903,7 @@ MX_DEV void pp_main_loop(const PPCtx& c, char* s0, char* s1, char* sb0, char* sb
   // in its C phase. Slot of steps u, u+1: (u/2) % 2 (2G steps cover whole pairs of slots).
   for (int q = 0; q < c.ngroups; q += 2) {
 #define MX_PP(S, QQ, SC, SN) \
-  pp_step2<KIND, GR, S>(c, q + QQ, ((G * QQ + S) / 2) % 2 ? s1 : s0, SC, SN, sa, sb, na, nb, acc)
+  pp_step2<KIND, GR, S>(c, q + QQ, ((G * QQ + S) / 2) % 2 ? s1 : s0, ((G * QQ + S) / 2) % 2 ? s0 : s1, SC, SN, sa, sb, na, nb, acc)
     MX_PP(0, 0, sb0, sb1); MX_PP(2, 0, sb0, sb1);
     if constexpr (G == 8) { MX_PP(4, 0, sb0, sb1); MX_PP(6, 0, sb0, sb1); }
     MX_PP(0, 1, sb1, sb0); MX_PP(2, 1, sb1, sb0);
@@ -969,13 +988,15 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
-  // prologue: scale groups 0 and 1, slots 0 and 1 (steps 0..3); wait for group 0 and slot 0 (the
-  // 9 copies of group 1 and slot 1 may still be in flight: the first odd step waits for them)
+  // prologue: scale groups 0 and 1, slot 0 (steps 0, 1) and the B rows of slot 1 (its A rows are
+  // queued in L_0); wait for group 0 and slot 0 (the 5 copies of group 1 and slot 1's B rows may
+  // still be in flight: the first odd step waits for them)
   pp_scale_copy(c, sbuf0, 0);
-  pp_slot_copies(c, slot0, 0);
+  pp_slot_copies<0>(c, slot0, 0);
+  pp_slot_copies<1>(c, slot0, 0);
   pp_scale_copy(c, sbuf1, min(1, c.ngroups - 1));
-  pp_slot_copies(c, slot1, (uint32_t)min(1, c.nslots - 1));
-  wait_vm_n(9);
+  pp_slot_copies<1>(c, slot1, (uint32_t)min(1, c.nslots - 1));
+  wait_vm_n(5);
   raw_barrier();
   if (wave < 4) pp_main_loop<KIND, 0>(c, slot0, slot1, sbuf0, sbuf1, acc);
   else pp_main_loop<KIND, 1>(c, slot0, slot1, sbuf0, sbuf1, acc);
