@@ -155,7 +155,7 @@ struct Args {
   const uint8_t* B;
   const uint8_t* SB;
   _Float16* C;
-  int M, N, K, tiles_m;
+  int M, N, K, tiles_m, tiles_n;
   int relu;  // epilogue: C = max(C, 0) (IEEE maxNum: NaN gives 0)
 };
 
@@ -725,12 +725,14 @@ MX_DEV v8i cat8(v4i lo, v4i hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2
 
 // The copies of slot m (its steps 2m, 2m+1: bytes 128m.. of every row) into `dst`: the 4 of its A
 // rows (HALF 0) or of its B rows (HALF 1).
+// The loads bypass the CU's L1 (sc0): no byte is read twice by one CU (measured about 3% faster at
+// the MXFP8 prefill shape).
 template <int HALF>
 MX_DEV void pp_slot_copies(const PPCtx& c, char* dst, uint32_t m) {
 #pragma unroll
   for (int k = 4 * HALF; k < 4 * HALF + 4; k++)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff,
-                                             128u * m, 0, 0);
+                                             128u * m, 0, 1);
 }
 
 MX_DEV void pp_scale_copy(const PPCtx& c, char* sbuf, int q) {
@@ -928,7 +930,17 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
   int bid = blockIdx.x;
   const int nwg = gridDim.x;
   if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);  // each XCD takes a contiguous tile range
-  const int tm = bid % p.tiles_m, tn = bid / p.tiles_m;
+  // Tile order: bands of up to 8 tile rows, m fastest within a band, then n. An XCD's 32 concurrent
+  // tiles then share at most 8 A panels and 4 B panels (tall grids in plain m-fastest order put 16 or
+  // more A panels in one XCD's L2 at once).
+  int tm, tn;
+  {
+    const int band = 8 * p.tiles_n, full = p.tiles_m / 8;
+    const int sr = bid / band, r = bid - sr * band;
+    const int rows = sr < full ? 8 : p.tiles_m - 8 * full;
+    tm = 8 * sr + r % rows;
+    tn = r / rows;
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
   const uint32_t RB = (uint32_t)p.K / (F::FP4 ? 2 : 1);  // bytes per A / B row
@@ -1141,7 +1153,8 @@ int gemm_pp_ring_launch(int kind, const void* A, const void* SA, const void* B, 
   a.K = K;
   a.relu = relu ? 1 : 0;
   a.tiles_m = (M + BM - 1) / BM;
-  const dim3 grid((unsigned)(a.tiles_m * ((N + 255) / 256))), block(512);
+  a.tiles_n = (N + 255) / 256;
+  const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(512);
   if (kind == 0) hipLaunchKernelGGL(gemm_pp_ring_kernel<0>, grid, block, 0, stream, a);
   else if (kind == 1) hipLaunchKernelGGL(gemm_pp_ring_kernel<1>, grid, block, 0, stream, a);
   else return MX_ERR_FORMAT;
