@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(HERE, "libmxgemm.so")
 
 MX_E4M3, MX_E5M2, MX_E2M3, MX_E3M2, MX_E2M1, MX_E8M0, MX_F16, MX_INT8, MX_INT4 = 0, 1, 2, 3, 4, 8, 16, 32, 33
 MXGEMM_RELU = 1  # mxgemm_create flag: C = max(A*B, 0) in the epilogue
+MXGEMM_QUANT_A = 2  # mxgemm_create flag: A is binary16, quantised to E4M3 inside the GEMM
 MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_FORMAT, MX_ERR_ARCH, MX_ERR_LAUNCH, MX_ERR_NOMEM = \
     0, -1, -2, -3, -4, -5, -6, -7
 MX_ERR_SCRATCH = -8

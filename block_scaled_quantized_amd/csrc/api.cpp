@@ -9,7 +9,7 @@
 
 namespace mx {
 int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
-                int N, int K, bool relu, hipStream_t stream);
+                int N, int K, bool relu, bool qa, hipStream_t stream);
 int matvec_launch(int M, int N, int K, const void* x, const void* W, bool int8, const void* Ws, void* y, void* ws,
                   size_t ws_bytes, hipStream_t stream);
 size_t matvec_workspace(int M, int N, int K, bool int8);
@@ -131,7 +131,9 @@ int mx_version(void) { return 100; }
 int mxgemm_create(mxgemm_t* out, int M, int N, int K, int fa, int fb, unsigned flags) {
   if (!out) return MX_ERR_NULL;
   *out = nullptr;
-  if (flags & ~(unsigned)MXGEMM_RELU) return MX_ERR_FORMAT;
+  if (flags & ~(unsigned)(MXGEMM_RELU | MXGEMM_QUANT_A)) return MX_ERR_FORMAT;
+  const bool qa = (flags & MXGEMM_QUANT_A) != 0u;
+  if (qa && !(fa == MX_E4M3 && fb == MX_E4M3)) return MX_ERR_FORMAT;
   int kind;
   if (fa == MX_E4M3 && fb == MX_E4M3) kind = 0;
   else if (fa == MX_E2M1 && fb == MX_E2M1) kind = 1;
@@ -152,7 +154,9 @@ int mxgemm_create(mxgemm_t* out, int M, int N, int K, int fa, int fb, unsigned f
   if (kind != 2 && K % 32) return MX_ERR_SHAPE;
   if (kind == 2 && (K % 8 || N % 8)) return MX_ERR_SHAPE;
   if (kind >= 3 && (K % 512 || N % 4)) return MX_ERR_SHAPE;  // mixed, E5M2 and FP6 pairs: the ring kernel only
-  mxgemm_plan* p = new (std::nothrow) mxgemm_plan{M, N, K, fa, fb, kind, choose_tile(kind, M, N, K), flags};
+  if (qa && (K % 1024 || N % 4)) return MX_ERR_SHAPE;         // quantise-on-load: the ping-pong kernel only
+  mxgemm_plan* p = new (std::nothrow) mxgemm_plan{M, N, K, fa, fb, kind, qa ? kPPRingTile : choose_tile(kind, M, N, K),
+                                                  flags};
   if (!p) return MX_ERR_NOMEM;
   *out = p;
   return MX_OK;
@@ -192,11 +196,12 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
 
 int mxgemm_run(mxgemm_t p, const void* A, const void* SA, const void* B, const void* SB, void* C, void* stream) {
   if (!p || !A || !B || !C) return MX_ERR_NULL;
-  if (p->kind != 2 && (!SA || !SB)) return MX_ERR_NULL;
+  const bool qa = (p->flags & MXGEMM_QUANT_A) != 0u;  // A is binary16, SA is not used
+  if (p->kind != 2 && ((!SA && !qa) || !SB)) return MX_ERR_NULL;
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return MX_ERR_ALIGN;
-  if (p->kind != 2 && (!aligned16(SA) || !aligned16(SB))) return MX_ERR_ALIGN;
+  if (p->kind != 2 && ((!qa && !aligned16(SA)) || !aligned16(SB))) return MX_ERR_ALIGN;
   if (int a = check_arch()) return a;
-  return gemm_launch(p->kind, p->tile_id, A, SA, B, SB, C, p->M, p->N, p->K, (p->flags & MXGEMM_RELU) != 0u,
+  return gemm_launch(p->kind, p->tile_id, A, SA, B, SB, C, p->M, p->N, p->K, (p->flags & MXGEMM_RELU) != 0u, qa,
                      as_stream(stream));
 }
 

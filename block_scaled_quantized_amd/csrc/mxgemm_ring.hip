@@ -701,6 +701,12 @@ struct PPCtx {
   // offsets of its scale rows within a scale buffer.
   uint32_t fa0, fb0, sc_a, sc_b;
   int wave, wm, wn, r32, h, nst, ngroups, nslots;
+  // A given as fp16 and quantised on load: resource over the tile's fp16 A rows; this thread's row
+  // rq = tid / 2 and block bq = tid % 2 of each step (64 K-elements = 2 blocks of 32) it quantises:
+  // its source offset, its slot row offset and chunk swizzle; the lane's A-scale read offsets
+  rsrc_t ra16;
+  uint32_t qa_voff, qa_row, qa_sw, qa_asc_w, qa_asc_r;
+  int qa_bq;
 };
 
 MX_DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_ptr_t)p; }
@@ -749,8 +755,11 @@ MX_DEV void pp_pack(const v4i r, int h, uint32_t (&out)[2]) {
 
 // MFMAs of one step from the fragments f (A tiles 0..3, B tiles 4, 5) with the group's packed
 // scales; U0 = first K-step of the step within its scale group.
-template <int KIND, int U0>
-MX_DEV void pp_mfmas(const v8i (&f)[6], const uint32_t (&sa)[4][2], const uint32_t (&sb)[2][2], v16f (&acc)[2][4]) {
+// With the A operand quantised on load (QA) the A scale of each tile is one byte per step, in the
+// low byte of sq[j] (op_sel 0).
+template <int KIND, int U0, bool QA = false>
+MX_DEV void pp_mfmas(const v8i (&f)[6], const uint32_t (&sa)[4][2], const uint32_t (&sb)[2][2], v16f (&acc)[2][4],
+                     const uint32_t* sq = nullptr) {
   using F = RingFmt<KIND>;
 #pragma unroll
   for (int k = 0; k < F::KSTEPS; k++)
@@ -769,6 +778,9 @@ MX_DEV void pp_mfmas(const v8i (&f)[6], const uint32_t (&sa)[4][2], const uint32
           else
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                 bk, ak, acc[i][j], 4, 4, (U0 + 1) % 4, sb[i][(U0 + 1) / 4], (U0 + 1) % 4, sa[j][(U0 + 1) / 4]);
+        } else if constexpr (QA) {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f[4 + i], f[j], acc[i][j], 0, 0, U0 % 4,
+                                                                       sb[i][U0 / 4], 0, sq[j]);
         } else {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f[4 + i], f[j], acc[i][j], 0, 0, U0 % 4,
                                                                        sb[i][U0 / 4], U0 % 4, sa[j][U0 / 4]);
@@ -837,6 +849,113 @@ MX_DEV void pp_read_scales(const PPCtx& c, const char* sbuf, uint32_t (&sa)[4][2
   for (int i = 0; i < 2; i++) pp_pack(rs[4 + i], c.h, sb[i]);
 }
 
+// ---- A quantised on load (E4M3 from fp16) ----
+// A block of 32 fp16 values becomes 32 E4M3 codes and one E8M0 scale by the rule of mx_pack_run:
+// E = clamp(floor(log2 amax) - 8 + 127, 0, 254) from the exact binary exponent of amax (E = 0 for
+// amax = 0; 0xFF with zero codes for a block holding Inf or NaN), codes = x * 2^(127-E) rounded to
+// the nearest E4M3 value, ties to even, saturating to +-448, sign kept. gfx950's scaled conversion
+// v_cvt_scalef32_pk_fp8_f16 (two values per instruction, divided by the scale) gives exactly these
+// codes for every fp16 input and every scale such an fp16 block produces (measured against the
+// library codec on all 65536 fp16 values and scales 2^-40..2^40), except that it writes NaN
+// (S.1111.111) where the scaled value exceeds 464 instead of saturating: those bytes are turned into
+// S.1111.110 (+-448) below. Inputs are upcast exactly, so the codes equal mx_pack_run's on the fp32
+// copy of the fp16 activations.
+typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
+typedef short v2s16 __attribute__((ext_vector_type(2)));
+typedef _Float16 v2f16 __attribute__((ext_vector_type(2)));
+
+MX_DEV void qa_block(const v4i (&w)[4], v4i& lo, v4i& hi, uint32_t& ebyte) {
+  v2u16 m = {0, 0};
+#pragma unroll
+  for (int d = 0; d < 16; d++) {
+    const uint32_t e = (uint32_t)w[d / 4][d % 4] & 0x7FFF7FFFu;
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(v2u16, e));
+  }
+  const uint32_t m0 = m[0], m1 = m[1];
+  const uint32_t a = m0 > m1 ? m0 : m1;  // amax as fp16 magnitude bits
+  const bool nonfinite = a >= 0x7C00u;
+  // floor(log2 amax): the exponent of its exact fp32 copy (fp16 subnormals are normal in fp32);
+  // branch-free, so the loop body stays one basic block
+  const float af = (float)__builtin_bit_cast(_Float16, (unsigned short)a);
+  const int fl = (int)((__builtin_bit_cast(uint32_t, af) >> 23) & 0xFFu) - 127;
+  int E = fl - 8 + 127;
+  E = E < 0 ? 0 : (E > 254 ? 254 : E);
+  E = a == 0u ? 0 : E;
+  // (any scale gives +-0 for an all-zero block; 2^(E-127) is a normal fp32 for every fp16 block)
+  const float scale = a == 0u ? 1.0f : __builtin_bit_cast(float, (uint32_t)E << 23);
+  uint32_t c[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) {
+    // (elements copied to scalars first: a bit cast applied to an ext-vector element reads element 0)
+    const uint32_t e0 = (uint32_t)w[k / 2][2 * (k % 2)], e1 = (uint32_t)w[k / 2][2 * (k % 2) + 1];
+    const v2f16 p0 = __builtin_bit_cast(v2f16, e0), p1 = __builtin_bit_cast(v2f16, e1);
+    v2s16 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16((v2s16){0, 0}, p0, scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(r, p1, scale, true);
+    uint32_t x = __builtin_bit_cast(uint32_t, r);
+    const uint32_t t = x & 0x7F7F7F7Fu, nan = (t + 0x01010101u) & 0x80808080u;  // bytes S.1111.111
+    x ^= nan >> 7;                                                                // -> S.1111.110
+    c[k] = nonfinite ? 0u : x;
+  }
+  lo = (v4i){(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+  hi = (v4i){(int)c[4], (int)c[5], (int)c[6], (int)c[7]};
+  ebyte = nonfinite ? 0xFFu : (uint32_t)E;
+}
+
+// This thread's fp16 source block of step s (64 bytes at byte 128 s of its row): 4 loads.
+MX_DEV void qa_load(const PPCtx& c, int s, v4i (&w)[4]) {
+#pragma unroll
+  for (int k = 0; k < 4; k++)
+    w[k] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(c.ra16, c.qa_voff + 16u * k, 128u * s, 0));
+}
+
+// Quantise the block loaded for step s and write its 32 codes into `slot` (half s % 2 of the row:
+// chunks 4(s%2) + 2 bq and the next, swizzled) and its scale byte into the step's A-scale entry.
+// Inline-assembly stores: the compiler would otherwise wait for every direct copy in flight into
+// the slot arrays before them; the L phase's lgkmcnt(0) completes them before its barrier.
+MX_DEV void qa_store(const PPCtx& c, int s, const v4i (&w)[4], char* slot, char* asc) {
+  v4i lo, hi;
+  uint32_t e;
+  qa_block(w, lo, hi, e);
+  uint32_t base = lds_addr(slot), abase = lds_addr(asc);
+  asm volatile("" : "+s"(base), "+s"(abase));
+  const uint32_t c0 = 4u * (uint32_t)(s & 1) + 2u * (uint32_t)c.qa_bq;
+  const uint32_t a0 = base + c.qa_row + 16u * (c0 ^ c.qa_sw), a1 = base + c.qa_row + 16u * ((c0 + 1u) ^ c.qa_sw);
+  const uint32_t ae = abase + 512u * (uint32_t)(s & 3) + c.qa_asc_w;
+  asm volatile(
+      "ds_write_b128 %0, %3\n"
+      "ds_write_b128 %1, %4\n"
+      "ds_write_b8 %2, %5"
+      :
+      : "v"(a0), "v"(a1), "v"(ae), "v"(lo), "v"(hi), "v"(e)
+      : "memory");
+}
+
+// The lane's A scales of step s (tiles 0..3: rows 128 wm + 32 j + r32, block h), one byte each.
+MX_DEV void qa_read_scales(const PPCtx& c, int s, const char* asc, uint32_t (&sq)[4]) {
+  uint32_t abase = lds_addr(asc);
+  asm volatile("" : "+s"(abase));
+  const uint32_t a = abase + 512u * (uint32_t)(s & 3) + c.qa_asc_r;
+  asm volatile(
+      "ds_read_u8 %0, %4\n"
+      "ds_read_u8 %1, %4 offset:64\n"
+      "ds_read_u8 %2, %4 offset:128\n"
+      "ds_read_u8 %3, %4 offset:192"
+      : "=&v"(sq[0]), "=&v"(sq[1]), "=&v"(sq[2]), "=&v"(sq[3])
+      : "v"(a));
+}
+
+MX_DEV void pp_read_scales_b(const PPCtx& c, const char* sbuf, uint32_t (&sb)[2][2]) {
+  uint32_t sbase = lds_addr(sbuf);
+  asm volatile("" : "+s"(sbase));
+  v4i rs[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) pp_read1(rs[i], sbase + c.sc_b + 512u * i);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 2; i++) pp_pack(rs[i], c.h, sb[i]);
+}
+
 // Steps u = G*q + S8 and u+1 (S8 even) of a wave of group GR: L_u, C_u, L_{u+1}, C_{u+1}, each
 // phase followed by a barrier. Slot u/2 (`slot_cur`) holds both steps; `slot_oth` is the other slot.
 //  - L_u reads the wave's fragments of step u and its B fragments of step u+1 (so the B rows of the
@@ -853,38 +972,60 @@ MX_DEV void pp_read_scales(const PPCtx& c, const char* sbuf, uint32_t (&sa)[4][2
 //    copy when L_{u+1} is the group's second step: vmcnt(4) or vmcnt(5).
 //  - Reads are split 16 + 8 and copies 4 + 4 between the two L phases, and the B rows get three steps
 //    to land, the A rows two.
-template <int KIND, int GR, int S8>
+//  - With A quantised on load (QA): instead of A-row copies, every L phase v quantises this thread's
+//    block of step v+2 (loaded in the wave's previous L phase) into the slot of step v+2, whose A
+//    rows are free since L_{v-1}, and its scale byte into the step's A-scale entry, then loads its
+//    block of step v+3. Issue order per L phase: the 4 A loads, then (odd phases) the B-row copies
+//    and the scale copy; the wait at the end of the odd step then allows the 12 later A loads and
+//    B copies plus the scale copies queued after the slot's B copies.
+template <int KIND, int GR, int S8, bool QA>
 MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char* sb_cur, char* sb_nxt,
                      uint32_t (&sa)[4][2], uint32_t (&sb)[2][2], uint32_t (&na)[4][2], uint32_t (&nb)[2][2],
-                     v16f (&acc)[2][4]) {
+                     v16f (&acc)[2][4], char* asc, v4i (&ld)[4]) {
   using F = RingFmt<KIND>;
   constexpr int G = PPFmt<KIND>::G;
-  constexpr int WAIT = 4 + ((S8 + 1) % G == 1 ? 1 : 0);
+  constexpr int WAIT = QA ? 12 + (S8 == 2 ? 1 : 0) + (S8 == 0 ? 1 : 0) : 4 + ((S8 + 1) % G == 1 ? 1 : 0);
   const int u = G * q + S8;
   v8i x[6], y[6];
+  uint32_t sq[4];
   // ---- L_u
+  if constexpr (QA) {
+    qa_store(c, u + 2, ld, slot_oth, asc);       // step u+2: half 0 of the other slot
+    qa_load(c, min(u + 3, c.nst - 1), ld);
+    qa_read_scales(c, u, asc, sq);
+  }
   pp_read_ab<0, true>(c, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
-  pp_slot_copies<0>(c, slot_oth, (uint32_t)min(u / 2 + 1, c.nslots - 1));
+  if constexpr (!QA) pp_slot_copies<0>(c, slot_oth, (uint32_t)min(u / 2 + 1, c.nslots - 1));
   pp_phase_barrier();
   // ---- C_u
-  pp_mfmas<KIND, F::KSTEPS * S8>(x, sa, sb, acc);
+  pp_mfmas<KIND, F::KSTEPS * S8, QA>(x, sa, sb, acc, sq);
   pp_phase_barrier();
   // ---- L_{u+1}
+  if constexpr (QA) {
+    qa_store(c, u + 3, ld, slot_oth, asc);       // step u+3: half 1 of the other slot
+    qa_load(c, min(u + 4, c.nst - 1), ld);
+    qa_read_scales(c, u + 1, asc, sq);
+  }
   pp_read_a(c, slot_cur, *reinterpret_cast<v8i(*)[6]>(&y[0]));
   pp_slot_copies<1>(c, slot_cur, (uint32_t)min(u / 2 + 2, c.nslots - 1));
   if (S8 + 1 == 1) pp_scale_copy(c, sb_cur, min(q + 2, c.ngroups - 1));
-  if (S8 + 1 == G - 1) pp_read_scales(c, sb_nxt, na, nb);
+  if (S8 + 1 == G - 1) {
+    if constexpr (QA) pp_read_scales_b(c, sb_nxt, nb);
+    else pp_read_scales(c, sb_nxt, na, nb);
+  }
   if (GR == 1) wait_vm_n(WAIT);
   pp_phase_barrier();
   // ---- C_{u+1}
-  pp_mfmas<KIND, F::KSTEPS * (S8 + 1)>(y, sa, sb, acc);
+  pp_mfmas<KIND, F::KSTEPS * (S8 + 1), QA>(y, sa, sb, acc, sq);
   if (GR == 0) wait_vm_n(WAIT);
   pp_phase_barrier();
   if (S8 + 1 == G - 1) {  // the next group's scales take over
+    if constexpr (!QA) {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      sa[j][0] = na[j][0];
-      sa[j][1] = na[j][1];
+      for (int j = 0; j < 4; j++) {
+        sa[j][0] = na[j][0];
+        sa[j][1] = na[j][1];
+      }
     }
 #pragma unroll
     for (int i = 0; i < 2; i++) {
@@ -894,18 +1035,21 @@ MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char
   }
 }
 
-template <int KIND, int GR>
-MX_DEV void pp_main_loop(const PPCtx& c, char* s0, char* s1, char* sb0, char* sb1, v16f (&acc)[2][4]) {
+template <int KIND, int GR, bool QA>
+MX_DEV void pp_main_loop(const PPCtx& c, char* s0, char* s1, char* sb0, char* sb1, v16f (&acc)[2][4], char* asc,
+                         v4i (&ld)[4]) {
   constexpr int G = PPFmt<KIND>::G;
   uint32_t sa[4][2], sb[2][2], na[4][2], nb[2][2];
-  pp_read_scales(c, sb0, sa, sb);  // group 0
-  if (GR == 1) raw_barrier();      // waves 4-7 start one phase late
+  if constexpr (QA) pp_read_scales_b(c, sb0, sb);  // group 0
+  else pp_read_scales(c, sb0, sa, sb);
+  if (GR == 1) raw_barrier();  // waves 4-7 start one phase late
   // Two scale groups per iteration (the group count is even), so the slot and scale buffer of every
   // step are static and the loop body has no branch: the scheduling barriers then keep every MFMA
   // in its C phase. Slot of steps u, u+1: (u/2) % 2 (2G steps cover whole pairs of slots).
   for (int q = 0; q < c.ngroups; q += 2) {
-#define MX_PP(S, QQ, SC, SN) \
-  pp_step2<KIND, GR, S>(c, q + QQ, ((G * QQ + S) / 2) % 2 ? s1 : s0, ((G * QQ + S) / 2) % 2 ? s0 : s1, SC, SN, sa, sb, na, nb, acc)
+#define MX_PP(S, QQ, SC, SN)                                                                                \
+  pp_step2<KIND, GR, S, QA>(c, q + QQ, ((G * QQ + S) / 2) % 2 ? s1 : s0, ((G * QQ + S) / 2) % 2 ? s0 : s1, SC, SN, \
+                            sa, sb, na, nb, acc, asc, ld)
     MX_PP(0, 0, sb0, sb1); MX_PP(2, 0, sb0, sb1);
     if constexpr (G == 8) { MX_PP(4, 0, sb0, sb1); MX_PP(6, 0, sb0, sb1); }
     MX_PP(0, 1, sb1, sb0); MX_PP(2, 1, sb1, sb0);
@@ -915,15 +1059,18 @@ MX_DEV void pp_main_loop(const PPCtx& c, char* s0, char* s1, char* sb0, char* sb
   if (GR == 0) raw_barrier();  // matches the late start of waves 4-7
 }
 
-template <int KIND>
+// QA: A is binary16 [M][K] and is quantised to E4M3 on load (KIND 0 only).
+template <int KIND, bool QA>
 __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
   using F = RingFmt<KIND>;
   using PF = PPFmt<KIND>;
+  static_assert(!QA || KIND == 0, "quantise-on-load: E4M3");
   constexpr int BN = 256;
   __shared__ __attribute__((aligned(16))) char slot0[PF::SLOT2];
   __shared__ __attribute__((aligned(16))) char slot1[PF::SLOT2];
   __shared__ __attribute__((aligned(16))) char sbuf0[PF::SBUF];
   __shared__ __attribute__((aligned(16))) char sbuf1[PF::SBUF];
+  __shared__ __attribute__((aligned(16))) char asc[QA ? 4 * 512 : 16];  // A scales of 4 steps (QA)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -983,9 +1130,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
     const uint8_t* base = (isA ? p.A + (int64_t)m0 * RB : p.B + (int64_t)n0 * RB) + (int64_t)(nr ? r0 : 0) * RB;
     c.rdata[k] = make_rsrc(base, (uint32_t)nr * RB);
   }
-  {  // scale copy of this wave: 64 rows, A rows 64w.. for w < 4, B rows 64(w-4).. after
+  {  // scale copy of this wave: 64 rows, A rows 64w.. for w < 4, B rows 64(w-4).. after (QA: no A
+     // scale plane; the A-row copies read from an empty resource and write unused zeros)
     const bool isA = wave < 4;
-    const int r0 = 64 * (isA ? wave : wave - 4), rows = isA ? rows_a : rows_b;
+    const int r0 = 64 * (isA ? wave : wave - 4), rows = isA ? (QA ? 0 : rows_a) : rows_b;
     const int nr = max(0, min(64, rows - r0));
     const uint8_t* base = (isA ? p.SA + (int64_t)m0 * nblk : p.SB + (int64_t)n0 * nblk) + (int64_t)(nr ? r0 : 0) * nblk;
     c.rscale = make_rsrc(base, (uint32_t)nr * nblk);
@@ -1000,18 +1148,43 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
 #pragma unroll
       for (int e = 0; e < 16; e++) acc[i][j][e] = 0.0f;
 
+  v4i ld[4];
+  if constexpr (QA) {
+    // this thread quantises row rq = tid / 2, block bq = tid % 2 of every step
+    const uint32_t rq = (uint32_t)tid >> 1, bq = (uint32_t)tid & 1u, K2 = 2u * (uint32_t)p.K;
+    c.ra16 = make_rsrc(p.A + (int64_t)m0 * K2, (uint32_t)rows_a * K2);
+    c.qa_voff = rq * K2 + 64u * bq;
+    c.qa_row = rq * 128u;
+    c.qa_sw = (rq >> 1) & 7u;
+    c.qa_bq = (int)bq;
+    c.qa_asc_w = 2u * rq + bq;
+    c.qa_asc_r = 2u * (128u * (uint32_t)c.wm + (uint32_t)c.r32) + (uint32_t)c.h;
+  }
+
   // prologue: scale groups 0 and 1, slot 0 (steps 0, 1) and the B rows of slot 1 (its A rows are
   // queued in L_0); wait for group 0 and slot 0 (the 5 copies of group 1 and slot 1's B rows may
-  // still be in flight: the first odd step waits for them)
+  // still be in flight: the first odd step waits for them). QA: steps 0 and 1 of A are quantised
+  // here, and the block of step 2 loaded.
   pp_scale_copy(c, sbuf0, 0);
-  pp_slot_copies<0>(c, slot0, 0);
+  if constexpr (!QA) pp_slot_copies<0>(c, slot0, 0);
   pp_slot_copies<1>(c, slot0, 0);
   pp_scale_copy(c, sbuf1, min(1, c.ngroups - 1));
   pp_slot_copies<1>(c, slot1, (uint32_t)min(1, c.nslots - 1));
-  wait_vm_n(5);
+  if constexpr (QA) {
+    v4i w0[4], w1[4];
+    qa_load(c, 0, w0);
+    qa_load(c, 1, w1);
+    qa_store(c, 0, w0, slot0, asc);
+    qa_store(c, 1, w1, slot0, asc);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    qa_load(c, min(2, c.nst - 1), ld);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the quantised steps are in LDS
+  } else {
+    wait_vm_n(5);
+  }
   raw_barrier();
-  if (wave < 4) pp_main_loop<KIND, 0>(c, slot0, slot1, sbuf0, sbuf1, acc);
-  else pp_main_loop<KIND, 1>(c, slot0, slot1, sbuf0, sbuf1, acc);
+  if (wave < 4) pp_main_loop<KIND, 0, QA>(c, slot0, slot1, sbuf0, sbuf1, acc, asc, ld);
+  else pp_main_loop<KIND, 1, QA>(c, slot0, slot1, sbuf0, sbuf1, acc, asc, ld);
   // the last steps queued copies into the free slot: let them land, and every wave finish with the
   // slots, before they are reused for the output
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -1140,8 +1313,9 @@ int gemm_ring_launch(int kind, int bn, int fca, int fcb, const void* A, const vo
 
 // 8-wave ping-pong ring, 256 x 256 tiles: kind 0 (E4M3 x E4M3) or 1 (E2M1 x E2M1), K % 1024 == 0
 // (an even number of scale groups), N % 4 == 0; checked by the caller.
+// qa: A is binary16 [M][K], quantised to E4M3 on load (kind 0 only; SA unused).
 int gemm_pp_ring_launch(int kind, const void* A, const void* SA, const void* B, const void* SB, void* C, int M, int N,
-                        int K, bool relu, hipStream_t stream) {
+                        int K, bool relu, bool qa, hipStream_t stream) {
   Args a{};
   a.A = (const uint8_t*)A;
   a.SA = (const uint8_t*)SA;
@@ -1155,9 +1329,16 @@ int gemm_pp_ring_launch(int kind, const void* A, const void* SA, const void* B, 
   a.tiles_m = (M + BM - 1) / BM;
   a.tiles_n = (N + 255) / 256;
   const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(512);
-  if (kind == 0) hipLaunchKernelGGL(gemm_pp_ring_kernel<0>, grid, block, 0, stream, a);
-  else if (kind == 1) hipLaunchKernelGGL(gemm_pp_ring_kernel<1>, grid, block, 0, stream, a);
-  else return MX_ERR_FORMAT;
+  if (qa) {
+    if (kind != 0) return MX_ERR_FORMAT;
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<0, true>), grid, block, 0, stream, a);
+  } else if (kind == 0) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<0, false>), grid, block, 0, stream, a);
+  } else if (kind == 1) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<1, false>), grid, block, 0, stream, a);
+  } else {
+    return MX_ERR_FORMAT;
+  }
   return launch_status();
 }
 }  // namespace mx

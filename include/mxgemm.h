@@ -76,6 +76,16 @@ typedef struct mxgemm_plan* mxgemm_t;
  * function" (there applied with max(value, 0) to the product tile in registers). */
 #define MXGEMM_RELU 1u
 
+/* mxgemm_create flag: the A operand is given unquantised, as binary16 [M][K] (row-major), and is
+ * quantised to E4M3 with E8M0 scales per 32 along K inside the GEMM, as the kernel loads its tiles,
+ * with exactly the codes and scales mx_pack_run(MX_E4M3) gives for the same values (held in fp32):
+ * C equals the product of mx_pack_run's A with B. This is the quantise-on-load of prefill
+ * activations, which the pages' quantized matmul takes already quantized ("TensorOps ... notes",
+ * section "Why this matters here": prefill is the compute-bound stage; scale rule of mx_pack_run).
+ * Needs fa == fb == MX_E4M3 (else MX_ERR_FORMAT), K % 1024 == 0 and N % 4 == 0 (else MX_ERR_SHAPE);
+ * mxgemm_run then takes SA = NULL (ignored). */
+#define MXGEMM_QUANT_A 2u
+
 /*
  * mxgemm_create -- validate a GEMM problem C[M,N] = A[M,K] * B[K,N] and choose its kernel.
  *
@@ -95,7 +105,8 @@ typedef struct mxgemm_plan* mxgemm_t;
  * N % 4 == 0, else MX_ERR_SHAPE; FP6 with any other format is MX_ERR_FORMAT.
  * Shape rules: 1 <= M, N <= MX_MAX_DIM; 32 <= K <= MX_MAX_DIM; MX formats need K % 32 == 0;
  * MX_F16 needs K % 8 == 0 and N % 8 == 0.
- * `flags` is 0 or MXGEMM_RELU (other bits: MX_ERR_FORMAT). Host only: queues no GPU work. *out
+ * `flags` is 0 or a combination of MXGEMM_RELU and MXGEMM_QUANT_A (other bits: MX_ERR_FORMAT).
+ * Host only: queues no GPU work. *out
  * receives a plan that holds host metadata only; release it with mxgemm_destroy. A plan may be
  * used from several threads and streams at once.
  */

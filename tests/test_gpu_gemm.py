@@ -14,7 +14,7 @@ import pytest
 import torch
 
 from block_scaled_quantized_amd import synth
-from gpu_common import dev, empty, gpu_gemm, gpu_mx_pack, host, require_gpu, say
+from gpu_common import dev, empty, gpu_gemm, gpu_mx_pack, host, nan_f16, require_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -646,4 +646,128 @@ def test_mx_pp_ring_nonfinite_and_relu(orc, fmt):
     assert ok, (ratio, bad)
     Cr = with_tile(11, lambda: gpu_gemm(api, fmt, dev(A), dev(SA), dev(B), dev(SB), M, N, K, flags=api.MXGEMM_RELU))
     ok, ratio, bad = orc.check(Cr, orc.relu(ref), K, R)
+    assert ok, (ratio, bad)
+
+
+# ---- A quantised on load (MXGEMM_QUANT_A): fp16 activations, E4M3 inside the GEMM -------------
+
+def fused_case(orc, api, A16, b_src, M, N, K):
+    """C of the fused path (A binary16, quantised on load) and of mx_pack_run(A as fp32) followed by
+    the same kernel (tile 11); plus the oracle's C from its own quantisation of the fp32 copy of A."""
+    B, SB = gpu_mx_pack(api, 0, b_src)
+    plan = api.mxgemm_create(M, N, K, 0, 0, api.MXGEMM_QUANT_A)
+    assert api.mxgemm_plan_info(plan)[3] == 4
+    Cf = nan_f16((M, N))
+    api.mxgemm_run(plan, dev(A16), None, B, SB, Cf)
+    plan.close()
+    A32 = A16.astype(np.float32)
+    A, SA = gpu_mx_pack(api, 0, A32)
+    Cu = with_tile(11, lambda: gpu_gemm(api, 0, A, SA, B, SB, M, N, K))
+    oA, oSA = orc.mx_quantize(0, A32)
+    oB, oSB = orc.mx_quantize(0, b_src)
+    assert np.array_equal(host(A), oA) and np.array_equal(host(SA), oSA)
+    return host(Cf).astype(np.float64), Cu, (oA, oSA, oB, oSB)
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 520, 1024), (257, 260, 4096), (1, 4, 1024), (512, 1024, 2048),
+                                   (33, 1028, 3072), (1024, 1024, 1024)])
+def test_mx_quant_a_fused_equals_pack_then_gemm(orc, M, N, K):
+    """Every output of the fused path equals pack + GEMM on the same kernel schedule bit for bit,
+    and meets the bound against the oracle."""
+    api = require_gpu()
+    say(f"quant-A fused M={M} N={N} K={K}")
+    A16 = synth.normal((M, K), 1.0, 1700 + M + K).astype(np.float16)
+    b_src = synth.normal((N, K), 0.02, 1701 + N + K)
+    Cf, Cu, (oA, oSA, oB, oSB) = fused_case(orc, api, A16, b_src, M, N, K)
+    assert not np.isnan(Cf).any()
+    assert np.array_equal(Cf.astype(np.float16).view(np.uint16), Cu.astype(np.float16).view(np.uint16))
+    ref = orc.mxgemm(0, 0, oA, oSA, oB, oSB, M, N, K)
+    R = orc.rms_ab(orc.dequant(0, oA, oSA, M, K), orc.dequant(0, oB, oSB, N, K).T)
+    ok, ratio, bad = orc.check(Cf, ref, K, R)
+    assert ok, (ratio, bad)
+
+
+def test_mx_quant_a_fused_edge_values(orc):
+    """fp16 blocks at the edges of the quantiser: all-zero and -0 blocks, subnormal fp16 blocks, the
+    largest fp16 values, exact ties of the E4M3 grid, values that saturate (scaled above 464), and
+    blocks holding Inf or NaN (their rows of C are NaN). Fused equals pack + GEMM bit for bit
+    (NaN positions included) and meets the bound on the finite outputs."""
+    api = require_gpu()
+    M, N, K = 96, 260, 1024
+    say("quant-A fused edge values")
+    A = synth.normal((M, K), 1.0, 1800).astype(np.float32)
+    A[0] = 0.0
+    A[1, :64] = -0.0
+    A[2] *= np.float32(2.0 ** -20)                    # fp16 subnormals and tiny normals
+    A[3, 32:64] = np.float32(2.0 ** -24) * np.arange(1, 33, dtype=np.float32)
+    A[4] = np.sign(A[4]) * np.float32(65504.0)        # the largest fp16
+    grid = torch.arange(0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    mids = (grid[:-1] + grid[1:]) / 2
+    A[5, :32] = np.float32(448.0)                     # amax 448: scale 2^0, ties of the grid
+    A[5, 1:32] = mids[np.linspace(0, len(mids) - 1, 31).astype(int)]
+    A[6, :32] = np.float32(500.0)                     # amax 500: scale 2^0, 500 -> 448 (saturates)
+    A[6, 1:32] = np.float32(470.0)
+    A[7, 100] = np.inf
+    A[8, 500] = np.nan
+    A[9, 33] = -np.inf
+    A16 = A.astype(np.float16)
+    b_src = synth.normal((N, K), 0.02, 1801)
+    Cf, Cu, (oA, oSA, oB, oSB) = fused_case(orc, api, A16, b_src, M, N, K)
+    assert np.isnan(Cf[7]).all() and np.isnan(Cf[8]).all() and np.isnan(Cf[9]).all()
+    assert not np.isnan(np.delete(Cf, [7, 8, 9], axis=0)).any()
+    assert np.array_equal(Cf.astype(np.float16).view(np.uint16), Cu.astype(np.float16).view(np.uint16))
+    ref = orc.mxgemm(0, 0, oA, oSA, oB, oSB, M, N, K)
+    R = orc.rms_ab(np.nan_to_num(orc.dequant(0, oA, oSA, M, K)), orc.dequant(0, oB, oSB, N, K).T)
+    ok, ratio, bad = orc.check(Cf, ref, K, R)
+    assert ok, (ratio, bad)
+
+
+def test_mx_quant_a_fused_prefill_every_output(orc):
+    """The prefill shape (M=2048, N=14336, K=4096, fp16 activations N(0,1), weights 0.02 N(0,1)):
+    the fused path equals pack + GEMM on every output, bit for bit, and sampled outputs meet the
+    bound against the oracle."""
+    api = require_gpu()
+    M, N, K = 2048, 14336, 4096
+    say("quant-A fused prefill")
+    A16 = synth.normal((M, K), 1.0, synth.seed_for(synth.MXFP8_PREFILL, 0)).astype(np.float16)
+    b_src = synth.normal((N, K), 0.02, synth.seed_for(synth.MXFP8_PREFILL, 1))
+    B, SB = gpu_mx_pack(api, 0, b_src)
+    plan = api.mxgemm_create(M, N, K, 0, 0, api.MXGEMM_QUANT_A)
+    Cf = nan_f16((M, N))
+    api.mxgemm_run(plan, dev(A16), None, B, SB, Cf)
+    plan.close()
+    A, SA = gpu_mx_pack(api, 0, A16.astype(np.float32))
+    pu = api.mxgemm_create(M, N, K, 0, 0)
+    Cu = nan_f16((M, N))
+    api.mxgemm_run(pu, A, SA, B, SB, Cu)
+    pu.close()
+    cf, cu = host(Cf), host(Cu)
+    assert np.isfinite(cf).all()
+    assert np.array_equal(cf.view(np.uint16), cu.view(np.uint16))
+    oA, oSA = orc.mx_quantize(0, A16.astype(np.float32))
+    oB, oSB = orc.mx_quantize(0, b_src)
+    ms, ns = synth.sample_points(M, N, 2048, 97)
+    ref = orc.mxgemm_points(0, 0, oA, oSA, oB, oSB, K, ms, ns)
+    ok, ratio, bad = orc.check(cf[ms, ns].astype(np.float64), ref, K, R_of(orc, 0, oA, oSA, oB, oSB, M, N, K))
+    say(f"quant-A prefill: worst err/bound {ratio:.3f}")
+    assert ok, (ratio, bad)
+
+
+def test_mx_quant_a_fused_relu(orc):
+    api = require_gpu()
+    M, N, K = 300, 520, 1024
+    say("quant-A fused relu")
+    A16 = synth.normal((M, K), 1.0, 1900).astype(np.float16)
+    b_src = synth.normal((N, K), 1.0, 1901)
+    B, SB = gpu_mx_pack(api, 0, b_src)
+    plan = api.mxgemm_create(M, N, K, 0, 0, api.MXGEMM_QUANT_A | api.MXGEMM_RELU)
+    C = nan_f16((M, N))
+    api.mxgemm_run(plan, dev(A16), None, B, SB, C)
+    plan.close()
+    oA, oSA = orc.mx_quantize(0, A16.astype(np.float32))
+    oB, oSB = orc.mx_quantize(0, b_src)
+    ref = orc.relu(orc.mxgemm(0, 0, oA, oSA, oB, oSB, M, N, K))
+    got = host(C).astype(np.float64)
+    assert (got >= 0).all()
+    ok, ratio, bad = orc.check(got, ref, K, R_of(orc, 0, oA, oSA, oB, oSB, M, N, K))
     assert ok, (ratio, bad)

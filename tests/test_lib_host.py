@@ -137,7 +137,8 @@ def test_validation_errors_without_gpu():
     assert lib.mxgemm_create(ctypes.byref(h), 0, 16, 32, 0, 0, 0) == api.MX_ERR_SHAPE
     assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 16, 0) == api.MX_ERR_FORMAT    # MX x fp16 pair
     assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 4, 0) == api.MX_ERR_SHAPE     # mixed pair, K % 512
-    assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 0, 2) == api.MX_ERR_FORMAT     # flags
+    assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 0, 4) == api.MX_ERR_FORMAT     # flags
+    assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 0, 2) == api.MX_ERR_SHAPE      # quantise-on-load: K % 1024
     assert lib.mxgemm_create(ctypes.byref(h), 16, 16, 32, 0, 0, api.MXGEMM_RELU) == api.MX_OK
     assert lib.mxgemm_destroy(h) == 0
     assert lib.mxgemm_create(ctypes.byref(h), 16, 12, 32, 16, 16, 0) == api.MX_ERR_SHAPE    # fp16 N % 8
@@ -304,3 +305,20 @@ def test_noalloc_rejects_shapes_beyond_the_scratch():
     for fw in (api.MX_INT8, api.MX_INT4):
         for m in (1, 8):
             assert 0 < api.mxmatvec_workspace_size(m, 14336, 4096, fw) <= api.MXMATVEC_SCRATCH_BYTES
+
+
+def test_quant_a_plan_rules():
+    """MXGEMM_QUANT_A: E4M3 x E4M3 only (MX_ERR_FORMAT otherwise), K % 1024 == 0 and N % 4 == 0
+    (MX_ERR_SHAPE otherwise); the plan runs the ping-pong kernel (variant 4)."""
+    lib = ctypes.CDLL(api.LIB_PATH)
+    lib.mxgemm_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)] + [ctypes.c_int] * 5 + [ctypes.c_uint]
+    h = ctypes.c_void_p()
+    Q = api.MXGEMM_QUANT_A
+    assert lib.mxgemm_create(ctypes.byref(h), 256, 256, 1024, api.MX_E2M1, api.MX_E2M1, Q) == api.MX_ERR_FORMAT
+    assert lib.mxgemm_create(ctypes.byref(h), 256, 256, 1024, api.MX_E4M3, api.MX_E2M1, Q) == api.MX_ERR_FORMAT
+    assert lib.mxgemm_create(ctypes.byref(h), 256, 256, 512, api.MX_E4M3, api.MX_E4M3, Q) == api.MX_ERR_SHAPE
+    assert lib.mxgemm_create(ctypes.byref(h), 256, 258, 1024, api.MX_E4M3, api.MX_E4M3, Q) == api.MX_ERR_SHAPE
+    assert lib.mxgemm_create(ctypes.byref(h), 256, 256, 1024, api.MX_E4M3, api.MX_E4M3, 4) == api.MX_ERR_FORMAT
+    p = api.mxgemm_create(300, 520, 2048, api.MX_E4M3, api.MX_E4M3, Q | api.MXGEMM_RELU)
+    assert api.mxgemm_plan_info(p) == (256, 256, 64, 4)
+    p.close()
