@@ -5,7 +5,8 @@ K=4096, N=14336 (E4M3 data, E8M0 scales per 32 along K, fp32 accumulation, fp16 
 its throughput in TFLOP/s (2*M*N*K per step over the HIP-event time of the timed steps, inputs
 already resident in HBM). The other workloads of the path are measured in the same run and
 reported under "detail": the MXFP4 GEMM (M=4096, N=8192, K=8192), the mixed E4M3 x E2M1 GEMM and
-the E5M2 x E5M2 GEMM at the prefill shape (against the fp8 peak), the FP6 E2M3 x E2M3 GEMM at the
+the E5M2 x E5M2 GEMM at the prefill shape (against the fp8 peak), the prefill GEMM with binary16
+activations quantised inside the GEMM against mx_pack_run + GEMM, the FP6 E2M3 x E2M3 GEMM at the
 prefill shape (against the fp6 peak, equal to fp4's), the fp16 GEMM (4096^3), the
 small MXFP8 GEMM (128x256x128, a latency figure), the int8/int4 dequant matvec (M=1 and M=8,
 K=4096, N=14336; GB/s of algorithmic bytes), the same int8/int4-weight product at M=128 (N=12288)
@@ -308,6 +309,29 @@ def main():
         detail["mxfp6_e2m3_gemm_2048x14336x4096"] = {"ms": t, "tflops": tf, "frac_peak": tf / PEAK["mxfp6"],
                                                      "tile": api.mxgemm_plan_info(p6)}
         del s6, C6
+
+    # ---------------- fp16 activations quantised inside the GEMM, against pack + GEMM ---------------
+    if want("quant_a"):
+        log("timing quantise-on-load GEMM")
+        a16 = [d(a_src.astype(np.float16)) for _ in range(3)]
+        a32 = [d(a_src) for _ in range(3)]
+        pq = api.mxgemm_create(M, N, K, api.MX_E4M3, api.MX_E4M3, api.MXGEMM_QUANT_A)
+        Cq = [torch.empty((M, N), dtype=torch.float16, device=dev) for _ in range(3)]
+        t_f = timed(lambda i: api.mxgemm_run(pq, a16[i % 3], None, sets[i % 3][2], sets[i % 3][3], Cq[i % 3], stream),
+                    args.steps, args.warmup)
+
+        def pack_gemm(i):
+            A_, SA_, B_, SB_ = sets[i % 3]
+            api.mx_pack_run(api.MX_E4M3, a32[i % 3], M, K, A_, SA_, stream)
+            api.mxgemm_run(plan, A_, SA_, B_, SB_, Cq[i % 3], stream)
+        t_pg = timed(pack_gemm, args.steps, args.warmup)
+        detail["mxfp8_quant_a_2048x14336x4096"] = {
+            "fused_us": t_f * 1e3, "fused_tflops": flops / (t_f * 1e-3) / 1e12,
+            "pack_fp32_plus_gemm_us": t_pg * 1e3, "pack_plus_gemm_tflops": flops / (t_pg * 1e-3) / 1e12,
+            "default": "pack + GEMM" if t_pg <= t_f else "fused",
+            "note": "fused: binary16 A quantised to E4M3 inside the GEMM (MXGEMM_QUANT_A); pack + GEMM: "
+                    "mx_pack_run from fp32 A, then the GEMM on the codes"}
+        del a16, a32, Cq
 
     # ---------------- fp16 GEMM ----------------------------------------------------------------
     if want("f16_square"):
