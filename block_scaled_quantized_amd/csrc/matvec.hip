@@ -689,25 +689,33 @@ __global__ __launch_bounds__(512) void matvec_lds_kernel(const _Float16* __restr
     }
     return;
   }
-  // Cross-split sum. The partial tile is written through to memory (system-scope atomic stores of
-  // column pairs, so no XCD's cache keeps a stale copy) and acknowledged (vmcnt(0)) before the
-  // strip's counter is incremented; the workgroup that takes the counter from S-1 (back to 0) is
-  // the last one and adds the S partials, read with system-scope atomic loads, in split order.
+  // Cross-split sum. Partial tiles live in the workspace as rows of Npad = NS * TW floats per split
+  // and activation row, permuted within each strip so that every store instruction of a wave writes
+  // 16 lanes x 16 contiguous bytes: column 16 C cg + C i + 4 g of the strip (lane i of column group
+  // cg, its 4-column group g) sits at float ((cg (C/4) + g) 16 + i) 4 of the strip's row. The
+  // stores and the loads below carry the system-coherence bits (sc0 sc1): stores are written
+  // through to memory and loads bypass every cache that is not coherent across XCDs, as relaxed
+  // system-scope atomic accesses are on gfx950. Ordering: every wave waits for its stores to be
+  // acknowledged (vmcnt(0)) before the workgroup's barrier and the strip counter's increment (a
+  // device-scope atomic); the workgroup that takes the counter from S-1 (back to 0) is the last,
+  // every other one has incremented after its stores completed, so its loads see them all; it adds
+  // the S partials in split order.
+  const int Npad = (int)gridDim.x * TW;
   if (par == 0 && col < N) {
+    const rsrc_t pr = make_rsrc(part, (uint32_t)S * (uint32_t)M * (uint32_t)Npad * 4u);
 #pragma unroll
     for (int v = 0; v < 4; v++) {
       const int m = 4 * q + v;
       if (m < M) {
 #pragma unroll
         for (int g = 0; g < C / 4; g++) {
-          uint64_t* dst = reinterpret_cast<uint64_t*>(part + ((int64_t)sk * M + m) * N + col + 4 * g);
-#pragma unroll
-          for (int e = 0; e < 2; e++) {
-            // element copies first: a bit cast of an ext-vector element read element 0 here
-            const float lo = acc[4 * g + 2 * e][v], hi = acc[4 * g + 2 * e + 1][v];
-            const uint64_t pr = (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
-            __hip_atomic_store(dst + e, pr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-          }
+          const uint32_t off = 4u * (uint32_t)(((sk * M + m) * Npad) + n0 + ((cg * (C / 4) + g) * 16 + i) * 4);
+          // element copies first: a bit cast of an ext-vector element read element 0 here
+          const float e0 = acc[4 * g][v], e1 = acc[4 * g + 1][v], e2 = acc[4 * g + 2][v], e3 = acc[4 * g + 3][v];
+          typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+          const u4 val = {__builtin_bit_cast(uint32_t, e0), __builtin_bit_cast(uint32_t, e1),
+                          __builtin_bit_cast(uint32_t, e2), __builtin_bit_cast(uint32_t, e3)};
+          __builtin_amdgcn_raw_buffer_store_b128(val, pr, off, 0, 17);  // sc0 sc1
         }
       }
     }
@@ -718,23 +726,26 @@ __global__ __launch_bounds__(512) void matvec_lds_kernel(const _Float16* __restr
   __syncthreads();
   if (!s_last) return;
   // Each thread sums up to two 4-column groups (M * TW / 4 <= 1024 = 2 * 512), with every split's
-  // load of both groups in flight at once (8-byte system-scope loads), in split order.
+  // 16-byte load of both groups in flight at once, in split order.
   {
     constexpr int kG = 2;
-    uint64_t v[kG][kMaxSplits][2];
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+    const rsrc_t pr = make_rsrc(part, (uint32_t)S * (uint32_t)M * (uint32_t)Npad * 4u);
+    u4 v[kG][kMaxSplits];
     int og[kG];
 #pragma unroll
     for (int g = 0; g < kG; g++) {
-      const int o = 4 * (threadIdx.x + 512 * g), m = o / TW, c = n0 + (o - m * TW);
+      const int o = 4 * (threadIdx.x + 512 * g), m = o / TW, cl = o - m * TW, c = n0 + cl;
       og[g] = (o < M * TW && c < N) ? o : -1;
       if (og[g] < 0) continue;
+      // storage position of column cl of the strip: cl = 16 C cg + C i + 4 gg
+      const int cg2 = cl / (16 * C), rem = cl - cg2 * 16 * C, i2 = rem / C, g2 = (rem - i2 * C) / 4;
+      const int pos = ((cg2 * (C / 4) + g2) * 16 + i2) * 4;
 #pragma unroll
       for (int sp = 0; sp < kMaxSplits; sp++)
-        if (sp < S) {
-          const uint64_t* src = reinterpret_cast<const uint64_t*>(part + ((int64_t)sp * M + m) * N + c);
-          v[g][sp][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-          v[g][sp][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-        }
+        if (sp < S)
+          v[g][sp] = __builtin_bit_cast(
+              u4, __builtin_amdgcn_raw_buffer_load_b128(pr, 4u * (uint32_t)((sp * M + m) * Npad + n0 + pos), 0, 17));
     }
 #pragma unroll
     for (int g = 0; g < kG; g++) {
@@ -744,11 +755,12 @@ __global__ __launch_bounds__(512) void matvec_lds_kernel(const _Float16* __restr
 #pragma unroll
       for (int sp = 0; sp < kMaxSplits; sp++)
         if (sp < S) {
-#pragma unroll
-          for (int e = 0; e < 2; e++) {
-            sum[2 * e] += __builtin_bit_cast(float, (uint32_t)v[g][sp][e]);
-            sum[2 * e + 1] += __builtin_bit_cast(float, (uint32_t)(v[g][sp][e] >> 32));
-          }
+          const u4 w = v[g][sp];
+          const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+          sum[0] += __builtin_bit_cast(float, w0);
+          sum[1] += __builtin_bit_cast(float, w1);
+          sum[2] += __builtin_bit_cast(float, w2);
+          sum[3] += __builtin_bit_cast(float, w3);
         }
       v4h h;
 #pragma unroll
@@ -766,7 +778,8 @@ constexpr int kC8 = 8, kC4 = 16, kW = 8, kP8 = 4, kP4 = 3;
 constexpr int kR = 8, kTargetWGs = 256;
 
 // Workspace layout: a fixed counter region (one counter per column strip, room for the largest
-// strip count any shape can have), then the fp32 partials [S][M][N]. Counters never share bytes
+// strip count any shape can have), then the fp32 partials [S][M][NS * TW] (strips permuted, see the
+// split kernel). Counters never share bytes
 // with partials of any shape, so a workspace whose counters one call left at zero is valid for
 // every later call.
 constexpr size_t kCounterBytes = 16384;
@@ -796,7 +809,7 @@ SplitPlan split_plan(int M, int N, int K, bool int8) {
     return p;
   }
   p.S = S;
-  p.bytes = kCounterBytes + (size_t)S * M * N * 4;
+  p.bytes = kCounterBytes + (size_t)S * M * ((size_t)p.NS * tw) * 4;  // partial rows padded to whole strips
   return p;
 }
 
