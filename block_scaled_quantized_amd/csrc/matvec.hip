@@ -17,8 +17,10 @@
 //    so lane l (i = l%16, q = l/16) loads rows 8q..8q+7 of the block for its C adjacent columns
 //    and needs no cross-lane exchange. The MFMA does the M-fold reuse of every weight, which
 //    keeps the vector ALU work per weight independent of M.
-//  - Weights become exact fp16 pairs (q[k,n], q[k+1,n]) with one byte permute, one xor that
-//    plants the fp16 exponent of 1024 and the offset-binary bit, and one packed fp16 subtract.
+//  - Weights become exact fp16 pairs (q[k,n], q[k+1,n]) by the usual magic-number conversion
+//    (a small integer placed in the significand of fp16 1024 reads as 1024 + integer, so one
+//    subtraction of the bias recovers it exactly): one byte permute, one xor that plants the fp16
+//    exponent of 1024 and the offset-binary bit, and one packed fp16 subtract.
 //  - The block's fp32 product is multiplied by the fp16 block scale of its column and added to
 //    an fp32 accumulator; the waves' accumulators meet in LDS, and the sum is rounded once to
 //    fp16.
