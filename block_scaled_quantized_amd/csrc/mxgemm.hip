@@ -711,18 +711,22 @@ namespace mx {
 
 int gemm_ring_launch(int kind, int bn, int fca, int fcb, const void* A, const void* SA, const void* B,
                      const void* SB, void* C, int M, int N, int K, bool relu, hipStream_t stream);
-int gemm_pp_ring_launch(int kind, const void* A, const void* SA, const void* B, const void* SB, void* C, int M, int N,
-                        int K, bool relu, bool qa, hipStream_t stream);
+int gemm_pp_ring_launch(int kind, int fca, int fcb, const void* A, const void* SA, const void* B, const void* SB,
+                        void* C, int M, int N, int K, bool relu, bool qa, hipStream_t stream);
 
 // Tile configurations, indexed by the plan. Returns MX_ERR_FORMAT for an unknown id.
 // qa: A is binary16 and quantised to E4M3 on load (kind E4M3 on tile 11 only; checked by the caller).
 int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void* B, const void* SB, void* C, int M,
                 int N, int K, bool relu, bool qa, hipStream_t stream) {
-  if (qa) return gemm_pp_ring_launch(0, A, SA, B, SB, C, M, N, K, relu, true, stream);
-  // The other pairs run on the ring kernel only: 3: E4M3 A x E2M1 B, 4: E2M1 A x E4M3 B (256x256 or
-  // 256x224 tiles); with E5M2 (256x256): 5: E5M2 x E5M2, 6: E4M3 x E5M2, 7: E5M2 x E4M3,
-  // 8: E5M2 x E2M1, 9: E2M1 x E5M2; FP6 (256x256): 10: E2M3 x E2M3, 11: E3M2 x E3M2, 12: E2M3 x E3M2,
-  // 13: E3M2 x E2M3.
+  if (qa) return gemm_pp_ring_launch(0, 0, 0, A, SA, B, SB, C, M, N, K, relu, true, stream);
+  // The other pairs: 3: E4M3 A x E2M1 B, 4: E2M1 A x E4M3 B (the ring, 256x256 or 256x224 tiles);
+  // with E5M2: 5: E5M2 x E5M2, 6: E4M3 x E5M2, 7: E5M2 x E4M3 (the ping-pong ring on tile 11 where
+  // K % 1024 == 0 and N % 4 == 0, else the 256x256 ring), 8: E5M2 x E2M1, 9: E2M1 x E5M2 (the ring);
+  // FP6 (the ring, 256x256): 10: E2M3 x E2M3, 11: E3M2 x E3M2, 12: E2M3 x E3M2, 13: E3M2 x E2M3.
+  if (kind >= 5 && kind <= 7 && tile_id == 11 && K % 1024 == 0 && N % 4 == 0) {
+    static const int pfa[3] = {1, 0, 1}, pfb[3] = {1, 1, 0};
+    return gemm_pp_ring_launch(0, pfa[kind - 5], pfb[kind - 5], A, SA, B, SB, C, M, N, K, relu, false, stream);
+  }
   if (kind == 3 || kind == 4)
     return gemm_ring_launch(kind - 1, tile_id == 9 ? 224 : 256, 0, 0, A, SA, B, SB, C, M, N, K, relu, stream);
   if (kind >= 5 && kind <= 13) {
@@ -784,7 +788,7 @@ int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void
     case 11:  // 8-wave ping-pong ring, 256x256 (E4M3 / E2M1, K % 1024 == 0, N % 4 == 0); otherwise the 4-stage
               // ring where it applies, else the 8-wave 256x256 kernel
       if ((kind == KIND_E4M3 || kind == KIND_E2M1) && K % 1024 == 0 && N % 4 == 0)
-        return gemm_pp_ring_launch(kind == KIND_E4M3 ? 0 : 1, A, SA, B, SB, C, M, N, K, relu, false, stream);
+        return gemm_pp_ring_launch(kind == KIND_E4M3 ? 0 : 1, 0, 0, A, SA, B, SB, C, M, N, K, relu, false, stream);
       if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(0, 256, 0, 0, A, SA, B, SB, C, M, N, K, relu, stream);
       if (kind == KIND_F16 && K % 256 == 0 && N % 256 == 0 && 2 * (int64_t)K * N < ((int64_t)1 << 31))
         return gemm_ring_launch(4, 256, 0, 0, A, SA, B, SB, C, M, N, K, relu, stream);

@@ -756,8 +756,9 @@ MX_DEV void pp_pack(const v4i r, int h, uint32_t (&out)[2]) {
 // MFMAs of one step from the fragments f (A tiles 0..3, B tiles 4, 5) with the group's packed
 // scales; U0 = first K-step of the step within its scale group.
 // With the A operand quantised on load (QA) the A scale of each tile is one byte per step, in the
-// low byte of sq[j] (op_sel 0).
-template <int KIND, int U0, bool QA = false>
+// low byte of sq[j] (op_sel 0). FC: the MFMA format codes of byte operands (KIND 0), A's in bits
+// 0-3 and B's in bits 4-7 (0 = E4M3, 1 = E5M2, which share the byte layout).
+template <int KIND, int U0, bool QA = false, int FC = 0>
 MX_DEV void pp_mfmas(const v8i (&f)[6], const uint32_t (&sa)[4][2], const uint32_t (&sb)[2][2], v16f (&acc)[2][4],
                      const uint32_t* sq = nullptr) {
   using F = RingFmt<KIND>;
@@ -782,8 +783,8 @@ MX_DEV void pp_mfmas(const v8i (&f)[6], const uint32_t (&sa)[4][2], const uint32
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f[4 + i], f[j], acc[i][j], 0, 0, U0 % 4,
                                                                        sb[i][U0 / 4], 0, sq[j]);
         } else {
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f[4 + i], f[j], acc[i][j], 0, 0, U0 % 4,
-                                                                       sb[i][U0 / 4], U0 % 4, sa[j][U0 / 4]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f[4 + i], f[j], acc[i][j], FC >> 4, FC & 15,
+                                                                       U0 % 4, sb[i][U0 / 4], U0 % 4, sa[j][U0 / 4]);
         }
       }
 }
@@ -978,7 +979,7 @@ MX_DEV void pp_read_scales_b(const PPCtx& c, const char* sbuf, uint32_t (&sb)[2]
 //    block of step v+3. Issue order per L phase: the 4 A loads, then (odd phases) the B-row copies
 //    and the scale copy; the wait at the end of the odd step then allows the 12 later A loads and
 //    B copies plus the scale copies queued after the slot's B copies.
-template <int KIND, int GR, int S8, bool QA>
+template <int KIND, int GR, int S8, bool QA, int FC>
 MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char* sb_cur, char* sb_nxt,
                      uint32_t (&sa)[4][2], uint32_t (&sb)[2][2], uint32_t (&na)[4][2], uint32_t (&nb)[2][2],
                      v16f (&acc)[2][4], char* asc, v4i (&ld)[4]) {
@@ -998,7 +999,7 @@ MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char
   if constexpr (!QA) pp_slot_copies<0>(c, slot_oth, (uint32_t)min(u / 2 + 1, c.nslots - 1));
   pp_phase_barrier();
   // ---- C_u
-  pp_mfmas<KIND, F::KSTEPS * S8, QA>(x, sa, sb, acc, sq);
+  pp_mfmas<KIND, F::KSTEPS * S8, QA, FC>(x, sa, sb, acc, sq);
   pp_phase_barrier();
   // ---- L_{u+1}
   if constexpr (QA) {
@@ -1016,7 +1017,7 @@ MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char
   if (GR == 1) wait_vm_n(WAIT);
   pp_phase_barrier();
   // ---- C_{u+1}
-  pp_mfmas<KIND, F::KSTEPS * (S8 + 1), QA>(y, sa, sb, acc, sq);
+  pp_mfmas<KIND, F::KSTEPS * (S8 + 1), QA, FC>(y, sa, sb, acc, sq);
   if (GR == 0) wait_vm_n(WAIT);
   pp_phase_barrier();
   if (S8 + 1 == G - 1) {  // the next group's scales take over
@@ -1035,7 +1036,7 @@ MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char
   }
 }
 
-template <int KIND, int GR, bool QA>
+template <int KIND, int GR, bool QA, int FC>
 MX_DEV void pp_main_loop(const PPCtx& c, char* s0, char* s1, char* sb0, char* sb1, v16f (&acc)[2][4], char* asc,
                          v4i (&ld)[4]) {
   constexpr int G = PPFmt<KIND>::G;
@@ -1048,7 +1049,7 @@ MX_DEV void pp_main_loop(const PPCtx& c, char* s0, char* s1, char* sb0, char* sb
   // in its C phase. Slot of steps u, u+1: (u/2) % 2 (2G steps cover whole pairs of slots).
   for (int q = 0; q < c.ngroups; q += 2) {
 #define MX_PP(S, QQ, SC, SN)                                                                                \
-  pp_step2<KIND, GR, S, QA>(c, q + QQ, ((G * QQ + S) / 2) % 2 ? s1 : s0, ((G * QQ + S) / 2) % 2 ? s0 : s1, SC, SN, \
+  pp_step2<KIND, GR, S, QA, FC>(c, q + QQ, ((G * QQ + S) / 2) % 2 ? s1 : s0, ((G * QQ + S) / 2) % 2 ? s0 : s1, SC, SN, \
                             sa, sb, na, nb, acc, asc, ld)
     MX_PP(0, 0, sb0, sb1); MX_PP(2, 0, sb0, sb1);
     if constexpr (G == 8) { MX_PP(4, 0, sb0, sb1); MX_PP(6, 0, sb0, sb1); }
@@ -1059,8 +1060,9 @@ MX_DEV void pp_main_loop(const PPCtx& c, char* s0, char* s1, char* sb0, char* sb
   if (GR == 0) raw_barrier();  // matches the late start of waves 4-7
 }
 
-// QA: A is binary16 [M][K] and is quantised to E4M3 on load (KIND 0 only).
-template <int KIND, bool QA>
+// QA: A is binary16 [M][K] and is quantised to E4M3 on load (KIND 0 only). FC: MFMA format codes of
+// the byte operands (KIND 0; pp_mfmas).
+template <int KIND, bool QA, int FC = 0>
 __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
   using F = RingFmt<KIND>;
   using PF = PPFmt<KIND>;
@@ -1183,8 +1185,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
     wait_vm_n(5);
   }
   raw_barrier();
-  if (wave < 4) pp_main_loop<KIND, 0, QA>(c, slot0, slot1, sbuf0, sbuf1, acc, asc, ld);
-  else pp_main_loop<KIND, 1, QA>(c, slot0, slot1, sbuf0, sbuf1, acc, asc, ld);
+  if (wave < 4) pp_main_loop<KIND, 0, QA, FC>(c, slot0, slot1, sbuf0, sbuf1, acc, asc, ld);
+  else pp_main_loop<KIND, 1, QA, FC>(c, slot0, slot1, sbuf0, sbuf1, acc, asc, ld);
   // the last steps queued copies into the free slot: let them land, and every wave finish with the
   // slots, before they are reused for the output
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -1314,8 +1316,9 @@ int gemm_ring_launch(int kind, int bn, int fca, int fcb, const void* A, const vo
 // 8-wave ping-pong ring, 256 x 256 tiles: kind 0 (E4M3 x E4M3) or 1 (E2M1 x E2M1), K % 1024 == 0
 // (an even number of scale groups), N % 4 == 0; checked by the caller.
 // qa: A is binary16 [M][K], quantised to E4M3 on load (kind 0 only; SA unused).
-int gemm_pp_ring_launch(int kind, const void* A, const void* SA, const void* B, const void* SB, void* C, int M, int N,
-                        int K, bool relu, bool qa, hipStream_t stream) {
+// kind 0 (byte operands, fca / fcb the MFMA format codes of A / B: 0 = E4M3, 1 = E5M2) or 1 (E2M1).
+int gemm_pp_ring_launch(int kind, int fca, int fcb, const void* A, const void* SA, const void* B, const void* SB,
+                        void* C, int M, int N, int K, bool relu, bool qa, hipStream_t stream) {
   Args a{};
   a.A = (const uint8_t*)A;
   a.SA = (const uint8_t*)SA;
@@ -1329,11 +1332,19 @@ int gemm_pp_ring_launch(int kind, const void* A, const void* SA, const void* B, 
   a.tiles_m = (M + BM - 1) / BM;
   a.tiles_n = (N + 255) / 256;
   const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(512);
+  if (kind == 0 && (fca < 0 || fca > 1 || fcb < 0 || fcb > 1)) return MX_ERR_FORMAT;
+  const int fc = kind == 0 ? fca | (fcb << 4) : 0;
   if (qa) {
-    if (kind != 0) return MX_ERR_FORMAT;
+    if (kind != 0 || fc != 0) return MX_ERR_FORMAT;
     hipLaunchKernelGGL((gemm_pp_ring_kernel<0, true>), grid, block, 0, stream, a);
-  } else if (kind == 0) {
-    hipLaunchKernelGGL((gemm_pp_ring_kernel<0, false>), grid, block, 0, stream, a);
+  } else if (kind == 0 && fc == 0x00) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<0, false, 0x00>), grid, block, 0, stream, a);
+  } else if (kind == 0 && fc == 0x11) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<0, false, 0x11>), grid, block, 0, stream, a);
+  } else if (kind == 0 && fc == 0x10) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<0, false, 0x10>), grid, block, 0, stream, a);
+  } else if (kind == 0 && fc == 0x01) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<0, false, 0x01>), grid, block, 0, stream, a);
   } else if (kind == 1) {
     hipLaunchKernelGGL((gemm_pp_ring_kernel<1, false>), grid, block, 0, stream, a);
   } else {

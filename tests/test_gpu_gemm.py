@@ -632,6 +632,40 @@ def test_mx_pp_ring_every_output(orc, fmt, M, N, K):
     assert ok, (ratio, bad)
 
 
+@pytest.mark.parametrize("fa,fb", [(1, 1), (0, 1), (1, 0)])
+@pytest.mark.parametrize("M,N,K", [(300, 520, 1024), (512, 1024, 2048), (33, 1028, 3072), (1, 4, 1024)])
+def test_mx_pp_ring_e5m2_pairs(orc, fa, fb, M, N, K):
+    """E5M2 with E5M2 or E4M3 on the ping-pong ring (its default where K % 1024 == 0): the MFMA's
+    format codes per operand on the E4M3 data path; every output, partial tiles, a grid of 8 tiles,
+    a single row."""
+    api = require_gpu()
+    say(f"pp ring e5m2 fa={fa} fb={fb} M={M} N={N} K={K}")
+    p = api.mxgemm_create(M, N, K, fa, fb)
+    assert api.mxgemm_plan_info(p)[3] == 4
+    api.mxgemm_destroy(p)
+    C, ref, R = pair_case(orc, api, fa, fb, M, N, K, 2600 + 7 * fa + 3 * fb + M + N + K, sigma_b=0.02)
+    assert not np.isnan(C).any()
+    ok, ratio, bad = orc.check(C, ref, K, R)
+    assert ok, (ratio, bad)
+
+
+def test_mx_pp_ring_e5m2_nonfinite_and_relu(orc):
+    """E5M2 x E4M3 on the ping-pong ring with NaN scales and codes, extreme scales, and ReLU."""
+    api = require_gpu()
+    M, N, K = 300, 520, 1024
+    say("pp ring e5m2 x e4m3 nonfinite")
+    A, SA, B, SB = nonfinite_operands(1, 0, M, N, K, 2700)
+    C = gpu_gemm(api, 1, dev(A), dev(SA), dev(B), dev(SB), M, N, K, fb=0)
+    ref = orc.mxgemm(1, 0, A, SA, B, SB, M, N, K)
+    R = orc.rms_ab(np.nan_to_num(orc.dequant(1, A, SA, M, K), posinf=0, neginf=0),
+                   np.nan_to_num(orc.dequant(0, B, SB, N, K)).T)
+    ok, ratio, bad = orc.check(C, ref, K, R)
+    assert ok, (ratio, bad)
+    Cr = gpu_gemm(api, 1, dev(A), dev(SA), dev(B), dev(SB), M, N, K, fb=0, flags=api.MXGEMM_RELU)
+    ok, ratio, bad = orc.check(Cr, orc.relu(ref), K, R)
+    assert ok, (ratio, bad)
+
+
 @pytest.mark.parametrize("fmt", [0, 4])
 def test_mx_pp_ring_nonfinite_and_relu(orc, fmt):
     """The ping-pong ring with NaN scales and codes, extreme scales, and the ReLU epilogue."""

@@ -219,18 +219,23 @@ def test_ring_tile_plan_info(monkeypatch):
 
 def test_e5m2_pairs_plan(monkeypatch):
     """Every pair with an E5M2 operand, and the FP6 pairs, is accepted where the ring applies (K % 512 == 0,
-    N % 4 == 0), runs the 256x256 ring whatever the override, and is refused with MX_ERR_SHAPE
-    elsewhere."""
+    N % 4 == 0), runs the 256x256 ring (E5M2 with E5M2 or E4M3: the ping-pong ring where K % 1024 == 0,
+    unless another tile is forced), and is refused with MX_ERR_SHAPE elsewhere."""
     pairs = ((api.MX_E5M2, api.MX_E5M2), (api.MX_E4M3, api.MX_E5M2), (api.MX_E5M2, api.MX_E4M3),
              (api.MX_E5M2, api.MX_E2M1), (api.MX_E2M1, api.MX_E5M2), (api.MX_E2M3, api.MX_E2M3),
              (api.MX_E3M2, api.MX_E3M2), (api.MX_E2M3, api.MX_E3M2), (api.MX_E3M2, api.MX_E2M3))
-    for tile in (None, "9", "10", "4"):
+    pp_pairs = pairs[:3]   # E5M2 with E5M2 or E4M3: the ping-pong ring by default where K % 1024 == 0
+    for tile in (None, "9", "10", "4", "11"):
         if tile is None:
             monkeypatch.delenv("MXGEMM_TILE", raising=False)
         else:
             monkeypatch.setenv("MXGEMM_TILE", tile)
         for fa, fb in pairs:
+            pp = (fa, fb) in pp_pairs and tile in (None, "11")
             p = api.mxgemm_create(2048, 14336, 4096, fa, fb)
+            assert api.mxgemm_plan_info(p) == (256, 256, 64, 4 if pp else 3)
+            api.mxgemm_destroy(p)
+            p = api.mxgemm_create(300, 520, 1536, fa, fb)   # K % 1024 != 0: the ring
             assert api.mxgemm_plan_info(p) == (256, 256, 64, 3)
             api.mxgemm_destroy(p)
     for fa, fb in pairs:
