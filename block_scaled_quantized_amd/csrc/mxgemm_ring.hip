@@ -688,7 +688,7 @@ struct PPFmt {
     SLOT2 = 512 * 128,              // bytes of one slot: 256 A + 256 B rows of 128 bytes
     SBUF = 512 * 16                 // bytes of one scale buffer
   };
-  static_assert(KIND == 0 || KIND == 1, "ping-pong GEMM: E4M3 x E4M3 and E2M1 x E2M1");
+  static_assert(KIND == 0 || KIND == 1 || KIND == 5, "ping-pong GEMM: byte pairs, E2M1 x E2M1, FP6 pairs");
 };
 
 struct PPCtx {
@@ -700,6 +700,9 @@ struct PPCtx {
   // same row is at that offset XOR 16k: the swizzle only permutes the chunks of a row. Also the
   // offsets of its scale rows within a scale buffer.
   uint32_t fa0, fb0, sc_a, sc_b;
+  // FP6: the lane's 8-byte pieces t = 0..2 of step hs of a row (bytes 48 hs + 24 h + 8 t of the row's
+  // 96 data bytes), as offsets from the row's first byte (fa0 / fb0 are then row starts)
+  uint32_t f6o[2][3];
   int wave, wm, wn, r32, h, nst, ngroups, nslots;
   // A given as fp16 and quantised on load: resource over the tile's fp16 A rows; this thread's row
   // rq = tid / 2 and block bq = tid % 2 of each step (64 K-elements = 2 blocks of 32) it quantises:
@@ -727,18 +730,40 @@ MX_DEV void pp_read4(v4i& d0, v4i& d1, v4i& d2, v4i& d3, uint32_t a0, uint32_t a
       : "v"(a0), "v"(a1), "i"(OFF), "i"(OFF + 4096));
 }
 MX_DEV void pp_read1(v4i& d, uint32_t a) { asm volatile("ds_read_b128 %0, %1" : "=&v"(d) : "v"(a)); }
+// FP6: the same four reads of 12 bytes (a piece of a row's step is 12 bytes in its 16-byte chunk).
+typedef int v3i __attribute__((ext_vector_type(3)));
+template <int OFF>
+MX_DEV void pp_read4_96(v3i& d0, v3i& d1, v3i& d2, v3i& d3, uint32_t a0, uint32_t a1) {
+  asm volatile(
+      "ds_read_b96 %0, %4 offset:%6\n"
+      "ds_read_b96 %1, %5 offset:%6\n"
+      "ds_read_b96 %2, %4 offset:%7\n"
+      "ds_read_b96 %3, %5 offset:%7"
+      : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
+      : "v"(a0), "v"(a1), "i"(OFF), "i"(OFF + 4096));
+}
+MX_DEV v8i cat6(v3i lo, v3i hi) {
+  const v4i a = __builtin_shufflevector(lo, lo, 0, 1, 2, -1), b = __builtin_shufflevector(hi, hi, 0, 1, 2, -1);
+  return __builtin_shufflevector(a, b, 0, 1, 2, 4, 5, 6, -1, -1);
+}
 MX_DEV v8i cat8(v4i lo, v4i hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7); }
 
-// The copies of slot m (its steps 2m, 2m+1: bytes 128m.. of every row) into `dst`: the 4 of its A
+// The copies of slot m (its steps 2m, 2m+1: bytes 128m.. of every row; FP6: the 96 bytes 96m.. in
+// logical chunks 0..5 of the 128-byte LDS row, chunks 6 and 7 unused) into `dst`: the 4 of its A
 // rows (HALF 0) or of its B rows (HALF 1).
 // The loads bypass the CU's L1 (sc0): no byte is read twice by one CU (measured about 3% faster at
 // the MXFP8 prefill shape).
-template <int HALF>
+template <int KIND, int HALF>
 MX_DEV void pp_slot_copies(const PPCtx& c, char* dst, uint32_t m) {
 #pragma unroll
-  for (int k = 4 * HALF; k < 4 * HALF + 4; k++)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff,
-                                             128u * m, 0, 1);
+  for (int k = 4 * HALF; k < 4 * HALF + 4; k++) {
+    if constexpr (KIND == 5)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff,
+                                               96u * m, 0, 1);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff,
+                                               128u * m, 0, 1);
+  }
 }
 
 MX_DEV void pp_scale_copy(const PPCtx& c, char* sbuf, int q) {
@@ -756,8 +781,8 @@ MX_DEV void pp_pack(const v4i r, int h, uint32_t (&out)[2]) {
 // MFMAs of one step from the fragments f (A tiles 0..3, B tiles 4, 5) with the group's packed
 // scales; U0 = first K-step of the step within its scale group.
 // With the A operand quantised on load (QA) the A scale of each tile is one byte per step, in the
-// low byte of sq[j] (op_sel 0). FC: the MFMA format codes of byte operands (KIND 0), A's in bits
-// 0-3 and B's in bits 4-7 (0 = E4M3, 1 = E5M2, which share the byte layout).
+// low byte of sq[j] (op_sel 0). FC: the MFMA format codes of the operands, A's in bits 0-3 and B's in
+// bits 4-7 (KIND 0: 0 = E4M3, 1 = E5M2, which share the byte layout; KIND 5: 2 = E2M3, 3 = E3M2).
 template <int KIND, int U0, bool QA = false, int FC = 0>
 MX_DEV void pp_mfmas(const v8i (&f)[6], const uint32_t (&sa)[4][2], const uint32_t (&sb)[2][2], v16f (&acc)[2][4],
                      const uint32_t* sq = nullptr) {
@@ -804,6 +829,50 @@ MX_DEV uint32_t pp_base(const char* slot) {
   uint32_t base = lds_addr(slot);
   asm volatile("" : "+s"(base));
   return base;
+}
+// FP6 (KIND 5): the lane's fragment of step hs is bytes 48 hs + 24 h .. + 23 of its row's 96 data
+// bytes: three 8-byte reads at the lane's offsets f6o[hs][0..2] (they straddle the swizzled 16-byte
+// chunks), tiles 4096 bytes apart. The reads land in dwords 0-5 of the MFMA operand.
+typedef int v2i __attribute__((ext_vector_type(2)));
+template <int OFF>
+MX_DEV void pp_read3_64(v2i& d0, v2i& d1, v2i& d2, uint32_t a0, uint32_t a1, uint32_t a2) {
+  asm volatile(
+      "ds_read_b64 %0, %3 offset:%6\n"
+      "ds_read_b64 %1, %4 offset:%6\n"
+      "ds_read_b64 %2, %5 offset:%6"
+      : "=&v"(d0), "=&v"(d1), "=&v"(d2)
+      : "v"(a0), "v"(a1), "v"(a2), "i"(OFF));
+}
+MX_DEV v8i cat3x2(v2i x, v2i y, v2i z) {
+  const v4i xy = __builtin_shufflevector(x, y, 0, 1, 2, 3), zz = __builtin_shufflevector(z, z, 0, 1, -1, -1);
+  return __builtin_shufflevector(xy, zz, 0, 1, 2, 3, 4, 5, -1, -1);
+}
+template <int HS, int NT>
+MX_DEV void pp_frags6(const PPCtx& c, uint32_t row, v8i* f) {
+  const uint32_t a0 = row + c.f6o[HS][0], a1 = row + c.f6o[HS][1], a2 = row + c.f6o[HS][2];
+  v2i r[NT][3];
+  pp_read3_64<0>(r[0][0], r[0][1], r[0][2], a0, a1, a2);
+  pp_read3_64<4096>(r[1][0], r[1][1], r[1][2], a0, a1, a2);
+  if constexpr (NT == 4) {
+    pp_read3_64<8192>(r[2][0], r[2][1], r[2][2], a0, a1, a2);
+    pp_read3_64<12288>(r[3][0], r[3][1], r[3][2], a0, a1, a2);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; t++) f[t] = cat3x2(r[t][0], r[t][1], r[t][2]);
+}
+template <int HS, bool YB>
+MX_DEV void pp_read_ab6(const PPCtx& c, const char* slot, v8i (&f)[6], v8i (&yb)[2]) {
+  const uint32_t base = pp_base(slot);
+  pp_frags6<HS, 4>(c, base + c.fa0, &f[0]);
+  pp_frags6<HS, 2>(c, base + c.fb0, &f[4]);
+  if (YB) pp_frags6<1, 2>(c, base + c.fb0, &yb[0]);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+}
+MX_DEV void pp_read_a6(const PPCtx& c, const char* slot, v8i (&f)[6]) {
+  pp_frags6<1, 4>(c, pp_base(slot) + c.fa0, &f[0]);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
 }
 template <int HS, bool YB>
 MX_DEV void pp_read_ab(const PPCtx& c, const char* slot, v8i (&f)[6], v8i (&yb)[2]) {
@@ -995,8 +1064,9 @@ MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char
     qa_load(c, min(u + 3, c.nst - 1), ld);
     qa_read_scales(c, u, asc, sq);
   }
-  pp_read_ab<0, true>(c, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
-  if constexpr (!QA) pp_slot_copies<0>(c, slot_oth, (uint32_t)min(u / 2 + 1, c.nslots - 1));
+  if constexpr (KIND == 5) pp_read_ab6<0, true>(c, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
+  else pp_read_ab<0, true>(c, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
+  if constexpr (!QA) pp_slot_copies<KIND, 0>(c, slot_oth, (uint32_t)min(u / 2 + 1, c.nslots - 1));
   pp_phase_barrier();
   // ---- C_u
   pp_mfmas<KIND, F::KSTEPS * S8, QA, FC>(x, sa, sb, acc, sq);
@@ -1007,8 +1077,9 @@ MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char
     qa_load(c, min(u + 4, c.nst - 1), ld);
     qa_read_scales(c, u + 1, asc, sq);
   }
-  pp_read_a(c, slot_cur, *reinterpret_cast<v8i(*)[6]>(&y[0]));
-  pp_slot_copies<1>(c, slot_cur, (uint32_t)min(u / 2 + 2, c.nslots - 1));
+  if constexpr (KIND == 5) pp_read_a6(c, slot_cur, *reinterpret_cast<v8i(*)[6]>(&y[0]));
+  else pp_read_a(c, slot_cur, *reinterpret_cast<v8i(*)[6]>(&y[0]));
+  pp_slot_copies<KIND, 1>(c, slot_cur, (uint32_t)min(u / 2 + 2, c.nslots - 1));
   if (S8 + 1 == 1) pp_scale_copy(c, sb_cur, min(q + 2, c.ngroups - 1));
   if (S8 + 1 == G - 1) {
     if constexpr (QA) pp_read_scales_b(c, sb_nxt, nb);
@@ -1092,7 +1163,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
   }
   const int m0 = tm * BM, n0 = tn * BN;
   const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
-  const uint32_t RB = (uint32_t)p.K / (F::FP4 ? 2 : 1);  // bytes per A / B row
+  const uint32_t RB = F::F6 ? (uint32_t)p.K / 4u * 3u : (uint32_t)p.K / (F::FP4 ? 2 : 1);  // bytes per A / B row
   const uint32_t nblk = (uint32_t)p.K / 32;
 
   PPCtx c;
@@ -1101,7 +1172,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
   c.wn = wave >> 1;
   c.r32 = lane & 31;
   c.h = lane >> 5;
-  c.nst = (int)(RB / 64u);  // steps of 64 row bytes
+  c.nst = p.K / (64 * F::KSTEPS);  // steps of 64 row bytes (FP6: 48)
   c.nslots = c.nst / 2;
   c.ngroups = c.nst / PF::G;
   {
@@ -1110,13 +1181,24 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
     // and i & 1 = wave & 1 for every copy of the wave
     const uint32_t l = (uint32_t)lane, j = l >> 3, pc = l & 7;
     const uint32_t lc = pc ^ ((4u * ((uint32_t)wave & 1u) + (j >> 1)) & 7u);
-    c.voff = j * RB + 16u * lc;
+    // FP6: 96 data bytes per row, logical chunks 0..5; lanes of chunks 6, 7 re-read chunk 4, 5 of the
+    // same row into unused LDS bytes (the same cache lines, so no extra HBM traffic)
+    c.voff = j * RB + 16u * (F::F6 && lc >= 6u ? lc - 2u : lc);
   }
   {
     // fragment chunks: row r = 128 wm + 32 j + r32 (A) or 64 wn + 32 i + r32 (B); (r >> 1) & 7 =
     // (r32 >> 1) & 7; tile j adds 4096 bytes (read offsets)
     const uint32_t r32 = (uint32_t)c.r32, h = (uint32_t)c.h, sw = (r32 >> 1) & 7u;
-    const uint32_t lo = r32 * 128u + 16u * (h ^ sw);
+    const uint32_t lo = r32 * 128u + (F::F6 ? 0u : 16u * (h ^ sw));
+    if constexpr (F::F6) {
+#pragma unroll
+      for (int hs = 0; hs < 2; hs++)
+#pragma unroll
+        for (int t = 0; t < 3; t++) {
+          const uint32_t o = 48u * (uint32_t)hs + 24u * h + 8u * (uint32_t)t;
+          c.f6o[hs][t] = 16u * ((o >> 4) ^ sw) + (o & 15u);
+        }
+    }
     c.fa0 = 16384u * (uint32_t)c.wm + lo;
     c.fb0 = (uint32_t)BM * 128u + 8192u * (uint32_t)c.wn + lo;
     c.sc_a = 16u * (128u * (uint32_t)c.wm + r32);
@@ -1168,10 +1250,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
   // still be in flight: the first odd step waits for them). QA: steps 0 and 1 of A are quantised
   // here, and the block of step 2 loaded.
   pp_scale_copy(c, sbuf0, 0);
-  if constexpr (!QA) pp_slot_copies<0>(c, slot0, 0);
-  pp_slot_copies<1>(c, slot0, 0);
+  if constexpr (!QA) pp_slot_copies<KIND, 0>(c, slot0, 0);
+  pp_slot_copies<KIND, 1>(c, slot0, 0);
   pp_scale_copy(c, sbuf1, min(1, c.ngroups - 1));
-  pp_slot_copies<1>(c, slot1, (uint32_t)min(1, c.nslots - 1));
+  pp_slot_copies<KIND, 1>(c, slot1, (uint32_t)min(1, c.nslots - 1));
   if constexpr (QA) {
     v4i w0[4], w1[4];
     qa_load(c, 0, w0);
@@ -1316,7 +1398,8 @@ int gemm_ring_launch(int kind, int bn, int fca, int fcb, const void* A, const vo
 // 8-wave ping-pong ring, 256 x 256 tiles: kind 0 (E4M3 x E4M3) or 1 (E2M1 x E2M1), K % 1024 == 0
 // (an even number of scale groups), N % 4 == 0; checked by the caller.
 // qa: A is binary16 [M][K], quantised to E4M3 on load (kind 0 only; SA unused).
-// kind 0 (byte operands, fca / fcb the MFMA format codes of A / B: 0 = E4M3, 1 = E5M2) or 1 (E2M1).
+// kind 0 (byte operands, fca / fcb the MFMA format codes of A / B: 0 = E4M3, 1 = E5M2), 1 (E2M1) or
+// 5 (FP6, codes 2 = E2M3, 3 = E3M2).
 int gemm_pp_ring_launch(int kind, int fca, int fcb, const void* A, const void* SA, const void* B, const void* SB,
                         void* C, int M, int N, int K, bool relu, bool qa, hipStream_t stream) {
   Args a{};
@@ -1333,7 +1416,8 @@ int gemm_pp_ring_launch(int kind, int fca, int fcb, const void* A, const void* S
   a.tiles_n = (N + 255) / 256;
   const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(512);
   if (kind == 0 && (fca < 0 || fca > 1 || fcb < 0 || fcb > 1)) return MX_ERR_FORMAT;
-  const int fc = kind == 0 ? fca | (fcb << 4) : 0;
+  if (kind == 5 && (fca < 2 || fca > 3 || fcb < 2 || fcb > 3)) return MX_ERR_FORMAT;
+  const int fc = kind == 0 || kind == 5 ? fca | (fcb << 4) : 0;
   if (qa) {
     if (kind != 0 || fc != 0) return MX_ERR_FORMAT;
     hipLaunchKernelGGL((gemm_pp_ring_kernel<0, true>), grid, block, 0, stream, a);
@@ -1347,6 +1431,14 @@ int gemm_pp_ring_launch(int kind, int fca, int fcb, const void* A, const void* S
     hipLaunchKernelGGL((gemm_pp_ring_kernel<0, false, 0x01>), grid, block, 0, stream, a);
   } else if (kind == 1) {
     hipLaunchKernelGGL((gemm_pp_ring_kernel<1, false>), grid, block, 0, stream, a);
+  } else if (kind == 5 && fc == 0x22) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<5, false, 0x22>), grid, block, 0, stream, a);
+  } else if (kind == 5 && fc == 0x33) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<5, false, 0x33>), grid, block, 0, stream, a);
+  } else if (kind == 5 && fc == 0x32) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<5, false, 0x32>), grid, block, 0, stream, a);
+  } else if (kind == 5 && fc == 0x23) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<5, false, 0x23>), grid, block, 0, stream, a);
   } else {
     return MX_ERR_FORMAT;
   }

@@ -649,6 +649,63 @@ def test_mx_pp_ring_e5m2_pairs(orc, fa, fb, M, N, K):
     assert ok, (ratio, bad)
 
 
+@pytest.mark.parametrize("fa,fb", [(2, 2), (3, 3), (2, 3), (3, 2)])
+@pytest.mark.parametrize("M,N,K", [(300, 520, 1024), (512, 1024, 2048), (33, 1028, 3072), (1, 4, 1024)])
+def test_mx_pp_ring_fp6_pairs(orc, fa, fb, M, N, K):
+    """FP6 pairs on the ping-pong ring (its default where K % 1024 == 0): 96-byte stage rows copied
+    as 12-byte pieces into 16-byte chunks, 24-byte fragments; every output, partial tiles, a grid of
+    8 tiles, a single row."""
+    api = require_gpu()
+    say(f"pp ring fp6 fa={fa} fb={fb} M={M} N={N} K={K}")
+    p = api.mxgemm_create(M, N, K, fa, fb)
+    assert api.mxgemm_plan_info(p)[3] == 4
+    api.mxgemm_destroy(p)
+    C, ref, R = pair_case(orc, api, fa, fb, M, N, K, 2800 + 5 * fa + 11 * fb + M + N + K, sigma_b=0.02)
+    assert not np.isnan(C).any()
+    ok, ratio, bad = orc.check(C, ref, K, R)
+    assert ok, (ratio, bad)
+
+
+def test_mx_pp_ring_fp6_unit_scales_exact(orc):
+    """E2M3 x E3M2 on the ping-pong ring at unit scales: E2M3 codes of every value, E3M2 codes with
+    exponent fields 0..5 (|b| <= 7), so every product is a multiple of 2^-7 below 53 in magnitude
+    and every partial sum over K=1024 is below 2^16, exact in fp32: the GPU must equal the oracle
+    after the fp16 rounding."""
+    api = require_gpu()
+    M, N, K = 300, 520, 1024
+    say("pp ring fp6 unit scales exact")
+    g = np.random.Generator(np.random.PCG64(2900))
+
+    def pack(codes):
+        bits = ((codes[..., None] >> np.arange(6)) & 1).astype(np.uint8).reshape(codes.shape[0], -1)
+        return np.ascontiguousarray(np.packbits(bits, axis=1, bitorder="little"))
+    ca = g.integers(0, 64, (M, K))
+    cb = (g.integers(0, 2, (N, K)) << 5) | (g.integers(0, 6, (N, K)) << 2) | g.integers(0, 4, (N, K))
+    SA = np.full((M, K // 32), 127, np.uint8)
+    SB = np.full((N, K // 32), 127, np.uint8)
+    A, B = pack(ca), pack(cb)
+    C = gpu_gemm(api, 2, dev(A), dev(SA), dev(B), dev(SB), M, N, K, fb=3)
+    ref = orc.mxgemm(2, 3, A, SA, B, SB, M, N, K)
+    assert np.abs(ref).max() < 60000
+    assert np.array_equal(C, ref.astype(np.float16).astype(np.float64))
+
+
+def test_mx_pp_ring_fp6_nonfinite_and_relu(orc):
+    """E3M2 x E2M3 on the ping-pong ring with NaN scales, extreme scales, and the ReLU epilogue."""
+    api = require_gpu()
+    M, N, K = 300, 520, 1024
+    say("pp ring fp6 nonfinite")
+    A, SA, B, SB = nonfinite_operands(3, 2, M, N, K, 2950)
+    C = gpu_gemm(api, 3, dev(A), dev(SA), dev(B), dev(SB), M, N, K, fb=2)
+    ref = orc.mxgemm(3, 2, A, SA, B, SB, M, N, K)
+    R = orc.rms_ab(np.nan_to_num(orc.dequant(3, A, SA, M, K)), np.nan_to_num(orc.dequant(2, B, SB, N, K)).T)
+    ok, ratio, bad = orc.check(C, ref, K, R)
+    assert ok, (ratio, bad)
+    Cr = gpu_gemm(api, 3, dev(A), dev(SA), dev(B), dev(SB), M, N, K, fb=2, flags=api.MXGEMM_RELU)
+    ok, ratio, bad = orc.check(Cr, orc.relu(ref), K, R)
+    assert ok, (ratio, bad)
+
+
 def test_mx_pp_ring_e5m2_nonfinite_and_relu(orc):
     """E5M2 x E4M3 on the ping-pong ring with NaN scales and codes, extreme scales, and ReLU."""
     api = require_gpu()

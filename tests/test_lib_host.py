@@ -219,12 +219,12 @@ def test_ring_tile_plan_info(monkeypatch):
 
 def test_e5m2_pairs_plan(monkeypatch):
     """Every pair with an E5M2 operand, and the FP6 pairs, is accepted where the ring applies (K % 512 == 0,
-    N % 4 == 0), runs the 256x256 ring (E5M2 with E5M2 or E4M3: the ping-pong ring where K % 1024 == 0,
-    unless another tile is forced), and is refused with MX_ERR_SHAPE elsewhere."""
+    N % 4 == 0), runs the 256x256 ring (E5M2 with E5M2 or E4M3 and the FP6 pairs: the ping-pong ring
+    where K % 1024 == 0, unless another tile is forced), and is refused with MX_ERR_SHAPE elsewhere."""
     pairs = ((api.MX_E5M2, api.MX_E5M2), (api.MX_E4M3, api.MX_E5M2), (api.MX_E5M2, api.MX_E4M3),
              (api.MX_E5M2, api.MX_E2M1), (api.MX_E2M1, api.MX_E5M2), (api.MX_E2M3, api.MX_E2M3),
              (api.MX_E3M2, api.MX_E3M2), (api.MX_E2M3, api.MX_E3M2), (api.MX_E3M2, api.MX_E2M3))
-    pp_pairs = pairs[:3]   # E5M2 with E5M2 or E4M3: the ping-pong ring by default where K % 1024 == 0
+    pp_pairs = pairs[:3] + pairs[5:]   # E5M2 with E5M2 / E4M3, FP6: the ping-pong ring where K % 1024 == 0
     for tile in (None, "9", "10", "4", "11"):
         if tile is None:
             monkeypatch.delenv("MXGEMM_TILE", raising=False)
