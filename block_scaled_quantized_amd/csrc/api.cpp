@@ -209,8 +209,9 @@ int mxgemm_run(mxgemm_t p, const void* A, const void* SA, const void* B, const v
   if (!aligned16(A) || !aligned16(B) || !aligned16(C)) return MX_ERR_ALIGN;
   if (p->kind != 2 && ((!qa && !aligned16(SA)) || !aligned16(SB))) return MX_ERR_ALIGN;
   if (int a = check_arch()) return a;
-  return gemm_launch(p->kind, p->tile_id, A, SA, B, SB, C, p->M, p->N, p->K, (p->flags & MXGEMM_RELU) != 0u, qa,
-                     as_stream(stream));
+  return sync_check(gemm_launch(p->kind, p->tile_id, A, SA, B, SB, C, p->M, p->N, p->K,
+                                (p->flags & MXGEMM_RELU) != 0u, qa, as_stream(stream)),
+                    as_stream(stream));
 }
 
 static int matvec_shape(int M, int N, int K, int fw) {
@@ -232,8 +233,9 @@ int mxmatvec_run(int M, int N, int K, const void* x, const void* W, int fw, cons
   if (!aligned16(x) || !aligned16(W) || !aligned16(Ws) || !aligned16(y)) return MX_ERR_ALIGN;
   if (workspace && !aligned16(workspace)) return MX_ERR_ALIGN;
   if (int a = check_arch()) return a;
-  return matvec_launch(M, N, K, x, W, fw == MX_INT8, Ws, y, workspace, workspace ? workspace_bytes : 0,
-                       as_stream(stream));
+  return sync_check(matvec_launch(M, N, K, x, W, fw == MX_INT8, Ws, y, workspace, workspace ? workspace_bytes : 0,
+                                  as_stream(stream)),
+                    as_stream(stream));
 }
 
 int mxmatvec_run_noalloc(int M, int N, int K, const void* x, const void* W, int fw, const void* Ws, void* y,
@@ -243,7 +245,7 @@ int mxmatvec_run_noalloc(int M, int N, int K, const void* x, const void* W, int 
   if (!aligned16(x) || !aligned16(W) || !aligned16(Ws) || !aligned16(y)) return MX_ERR_ALIGN;
   if (M <= 8 && matvec_workspace(M, N, K, fw == MX_INT8) > MXMATVEC_SCRATCH_BYTES) return MX_ERR_SCRATCH;
   if (int a = check_arch()) return a;
-  return matvec_launch_noalloc(M, N, K, x, W, fw == MX_INT8, Ws, y, as_stream(stream));
+  return sync_check(matvec_launch_noalloc(M, N, K, x, W, fw == MX_INT8, Ws, y, as_stream(stream)), as_stream(stream));
 }
 
 }  // extern "C"

@@ -180,7 +180,7 @@ extern "C" int mx_pack_run(int f, const float* src, int rows, int cols, void* co
       hipLaunchKernelGGL(pack_mx_kernel<MX_E3M2>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
     else
       hipLaunchKernelGGL(pack_mx_kernel<MX_E2M1>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
-    return launch_status();
+    return sync_check(launch_status(), st);
   }
   if (f == MX_INT8 || f == MX_INT4) {
     if (rows % 32 || (f == MX_INT4 && cols % 2)) return MX_ERR_SHAPE;
@@ -188,7 +188,7 @@ extern "C" int mx_pack_run(int f, const float* src, int rows, int cols, void* co
     const int64_t items = (int64_t)(rows / 32) * ((cols + 1) / 2);
     hipLaunchKernelGGL(pack_int_kernel, dim3(grid_for(items, kThreads)), dim3(kThreads), 0, st, f == MX_INT8, src,
                        rows, cols, (uint8_t*)codes, (uint16_t*)scales);
-    return launch_status();
+    return sync_check(launch_status(), st);
   }
   return MX_ERR_FORMAT;
 }
@@ -215,7 +215,7 @@ extern "C" int mx_unpack_run(int f, const void* codes, const void* scales, int r
       hipLaunchKernelGGL(unpack_mx_kernel<MX_E3M2>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
     else
       hipLaunchKernelGGL(unpack_mx_kernel<MX_E2M1>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
-    return launch_status();
+    return sync_check(launch_status(), st);
   }
   if (f == MX_INT8 || f == MX_INT4) {
     if (rows % 32 || (f == MX_INT4 && cols % 2)) return MX_ERR_SHAPE;
@@ -223,7 +223,7 @@ extern "C" int mx_unpack_run(int f, const void* codes, const void* scales, int r
     const int64_t total = (int64_t)rows * cols;
     hipLaunchKernelGGL(unpack_int_kernel, dim3(grid_for(total, kThreads)), dim3(kThreads), 0, st, f == MX_INT8,
                        (const uint8_t*)codes, (const uint16_t*)scales, total, (int64_t)cols, out);
-    return launch_status();
+    return sync_check(launch_status(), st);
   }
   return MX_ERR_FORMAT;
 }

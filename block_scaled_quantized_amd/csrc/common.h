@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "mxgemm.h"
 
@@ -12,6 +13,21 @@ namespace mx {
 
 // Status of the most recent launch on this thread: hipGetLastError after a kernel launch.
 inline int launch_status() { return hipGetLastError() == hipSuccess ? MX_OK : MX_ERR_LAUNCH; }
+
+// The MX_SYNC_CHECK debug switch (environment variable, read at every call; set and not "0"): a GPU
+// entry point whose work was queued waits for its stream and returns MX_ERR_LAUNCH when the stream
+// reports an error, so an asynchronous fault surfaces at the call that caused it. Off by default:
+// entry points then never synchronise.
+inline int sync_check(int status, hipStream_t st) {
+  if (status != MX_OK) return status;
+  const char* e = std::getenv("MX_SYNC_CHECK");
+  if (!e || e[0] == '\0' || (e[0] == '0' && e[1] == '\0')) return status;
+  if (hipStreamSynchronize(st) != hipSuccess) {
+    (void)hipGetLastError();
+    return MX_ERR_LAUNCH;
+  }
+  return status;
+}
 
 // 0 when the current device is gfx950, MX_ERR_ARCH otherwise (cached per device id).
 int check_arch();

@@ -10,6 +10,10 @@
  *  - `stream` is a hipStream_t passed as an opaque pointer (NULL = the default stream). GPU entry
  *    points only enqueue work on that stream and return; they never synchronise. Calls on
  *    different streams may run concurrently.
+ *  - Debugging: with the environment variable MX_SYNC_CHECK set (to anything but "0"; read at
+ *    every call), a GPU entry point that queued work waits for its stream before returning and
+ *    returns MX_ERR_LAUNCH when the stream reports an error, so an asynchronous fault is reported
+ *    by the call that caused it.
  *  - Device pointers must be 16-byte aligned. Matrices are dense and row-major with the leading
  *    dimension equal to the row length given below.
  *  - A GPU entry point called on a device that is not gfx950 returns MX_ERR_ARCH.
@@ -46,7 +50,8 @@ typedef enum {
   MX_ERR_ALIGN = -3,   /* a device pointer is not 16-byte aligned */
   MX_ERR_FORMAT = -4,  /* unsupported format or format pair */
   MX_ERR_ARCH = -5,    /* the current device is not gfx950, or no device is present */
-  MX_ERR_LAUNCH = -6,  /* the HIP runtime reported an error when queueing a kernel */
+  MX_ERR_LAUNCH = -6,  /* the HIP runtime reported an error when queueing a kernel (or, with
+                          MX_SYNC_CHECK, when the stream ran it) */
   MX_ERR_NOMEM = -7,   /* host allocation of a plan failed */
   MX_ERR_SCRATCH = -8  /* mxmatvec_run_noalloc: the shape needs more than MXMATVEC_SCRATCH_BYTES */
 } mx_status;
