@@ -30,6 +30,17 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+# The pages' own throughput figures, on other hardware: context for the fp16 GEMM detail line, not a
+# target (they print none for a block-scaled GEMM or a dequant matvec). "TileLang Metal Backend
+# Internals", section 5.6 (current performance snapshot): fp16 in and out, fp32 accumulation, full
+# tiles, mean of 100 timed runs, Apple M5 with a 10-core GPU.
+PAGES_CONTEXT = {
+    "note": "the pages' figures on Apple M5 (10-core GPU), other hardware: context, not a target",
+    "source": "TileLang Metal Backend Internals, section 5.6",
+    "fp16_gemm_4096x4096x4096_tflops": {"pytorch_mps": 13.6, "mlx": 12.7, "tilelang": 12.9},
+    "compare_with_detail": "fp16_gemm_4096x4096x4096",
+}
+
 PEAK = {  # MI355X dense peaks (256 CUs x 2.4 GHz x flop/clk/CU) and HBM bandwidth
     "mxfp8": 5033.2, "mxfp6": 10066.3, "mxfp4": 10066.3, "fp16": 2516.6, "hbm_gbs": 8000.0,
 }
@@ -475,6 +486,7 @@ def main():
                      "flops_per_launch": flops, "traffic_source": traffic_src},
         "cpu_baseline": cpu,
         "detail": detail,
+        "context": PAGES_CONTEXT,
     }
     print(json.dumps(out))
 
