@@ -411,11 +411,12 @@ MX_DEV void store_c(const Args& p, v4f (&acc)[CF::FN][CF::FM], char* ws, int mb,
       const int m = mb + 16 * j + lr, n = nb + 8 * c;
       if (m >= p.M) continue;
       _Float16* dst = p.C + (int64_t)m * p.N + n;
+      // non-temporal stores: C streams out without displacing operand panels from the caches
       if (rows16 && n + 8 <= p.N) {
-        *reinterpret_cast<v8h*>(dst) = v;
+        __builtin_nontemporal_store(v, reinterpret_cast<v8h*>(dst));
       } else if (rows8 && n + 8 <= p.N) {
-        *reinterpret_cast<v4h*>(dst) = __builtin_shufflevector(v, v, 0, 1, 2, 3);
-        *reinterpret_cast<v4h*>(dst + 4) = __builtin_shufflevector(v, v, 4, 5, 6, 7);
+        __builtin_nontemporal_store(__builtin_shufflevector(v, v, 0, 1, 2, 3), reinterpret_cast<v4h*>(dst));
+        __builtin_nontemporal_store(__builtin_shufflevector(v, v, 4, 5, 6, 7), reinterpret_cast<v4h*>(dst + 4));
       } else {
 #pragma unroll
         for (int e = 0; e < 8; e++)

@@ -636,16 +636,19 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
       const v4h lo = *reinterpret_cast<const v4h*>(src), hi = *reinterpret_cast<const v4h*>(src + 8);
       const int m = m0 + 32 * T::FA * wm + 32 * j0 + lr, n = n0 + WCOLS * wn + 8 * cp;
       if (m < p.M) {
+        // non-temporal stores: C streams out without displacing the A and B panels that other tiles
+        // still read from the L2 and the Infinity Cache
         _Float16* dst = p.C + (int64_t)m * p.N + n;
         if (n + 8 <= p.N) {
           if (rows16) {
-            *reinterpret_cast<v8h*>(dst) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            __builtin_nontemporal_store(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                        reinterpret_cast<v8h*>(dst));
           } else {
-            *reinterpret_cast<v4h*>(dst) = lo;
-            *reinterpret_cast<v4h*>(dst + 4) = hi;
+            __builtin_nontemporal_store(lo, reinterpret_cast<v4h*>(dst));
+            __builtin_nontemporal_store(hi, reinterpret_cast<v4h*>(dst + 4));
           }
         } else if (n + 4 <= p.N) {
-          *reinterpret_cast<v4h*>(dst) = lo;
+          __builtin_nontemporal_store(lo, reinterpret_cast<v4h*>(dst));
         }
       }
     }
@@ -1309,16 +1312,19 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
       const v4h lo = *reinterpret_cast<const v4h*>(src), hi = *reinterpret_cast<const v4h*>(src + 8);
       const int m = m0 + 128 * c.wm + 32 * j0 + lr, n = n0 + WCOLS * c.wn + 8 * cp;
       if (m < p.M) {
+        // non-temporal stores: C streams out without displacing the A and B panels that other tiles
+        // still read from the L2 and the Infinity Cache
         _Float16* dst = p.C + (int64_t)m * p.N + n;
         if (n + 8 <= p.N) {
           if (rows16) {
-            *reinterpret_cast<v8h*>(dst) = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            __builtin_nontemporal_store(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                        reinterpret_cast<v8h*>(dst));
           } else {
-            *reinterpret_cast<v4h*>(dst) = lo;
-            *reinterpret_cast<v4h*>(dst + 4) = hi;
+            __builtin_nontemporal_store(lo, reinterpret_cast<v4h*>(dst));
+            __builtin_nontemporal_store(hi, reinterpret_cast<v4h*>(dst + 4));
           }
         } else if (n + 4 <= p.N) {
-          *reinterpret_cast<v4h*>(dst) = lo;
+          __builtin_nontemporal_store(lo, reinterpret_cast<v4h*>(dst));
         }
       }
     }
