@@ -620,12 +620,14 @@ __global__ __launch_bounds__(512) void matvec_lds_kernel(const _Float16* __restr
   auto issue = [&](int u) {
     const int stage = 2 * u + par, blk = kb0 + (stage < nb ? stage : nb - 1);
     char* st = ring + ((u % RS) * 2 + par) * kLStage;
+    // weights and scales are read exactly once: past the CU's L1 (sc0) and non-temporal (nt) in the
+    // L2 (measured 1-3% faster than the default policy at the decode shapes)
     const rsrc_t wr = make_rsrc(Wt + (int64_t)blk * 32 * row_bytes, 32u * row_bytes);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(st + (2 * cg) * kLChunk), 16, voff0, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(st + (2 * cg + 1) * kLChunk), 16, voff1, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(st + (2 * cg) * kLChunk), 16, voff0, 0, 0, 3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(st + (2 * cg + 1) * kLChunk), 16, voff1, 0, 0, 3);
     const rsrc_t sr = make_rsrc(Ws + (int64_t)blk * N, 2u * (uint32_t)N);
     if (lane < SLANES)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(st + 8 * kLChunk + cg * (SB / 4)), 16, scb, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(st + 8 * kLChunk + cg * (SB / 4)), 16, scb, 0, 0, 3);
   };
 
   const int xrow = i < M ? i : M - 1;
