@@ -64,13 +64,16 @@ struct TileInfo {
 // is ranked below it; a partial last round runs faster per tile than a full one, the chip being
 // shared-resource bound). The 256x192 ring wins where it makes whole rounds and 256x256 does not
 // (M=2048, N=12288: 95 against 101 us). The 8-wave ping-pong GEMM with 128-byte stage rows (tile
-// 11, E4M3 / E2M1 with K % 1024 == 0) runs the MXFP8 prefill shape in 108-112 us against the ring's
-// 119 us, and the MXFP4 4096 x 8192 x 8192 shape in 133 us against 146-151 us.
+// 11, where K % 1024 == 0) is the fastest tile at every shape measured, also where 256x192 ring
+// tiles make whole rounds and its 256x256 tiles do not (E4M3, K=4096: M=2048 N=12288 92.3 against
+// 97.9 us, M=2048 N=4096 37.9 against 38.7 us, M=512 N=8192 K=8192 67.0 against 67.0 us; MXFP8
+// prefill 97.1 against 109.7-126.8 us for the ring tiles; MXFP4 4096 x 8192 x 8192 128.8 against
+// 138.7-167.5 us).
 constexpr TileInfo kTiles[] = {
     {256, 256, 4, 0, {85, 85, 90}}, {256, 224, 4, 0, {80, 75, 55}}, {128, 128, 4, 0, {50, 45, 50}},
     {64, 64, 4, 0, {25, 25, 25}},   {256, 256, 8, 1, {90, 100, 100}}, {256, 224, 8, 1, {88, 95, 60}},
     {256, 256, 8, 2, {60, 60, 99}}, {256, 224, 8, 2, {100, 95, 60}}, {256, 256, 4, 3, {200, 200, 200}},
-    {256, 224, 4, 3, {170, 160, 1}}, {256, 192, 4, 3, {170, 160, 1}}, {256, 256, 8, 4, {215, 220, 1}}};
+    {256, 224, 4, 3, {170, 160, 1}}, {256, 192, 4, 3, {170, 160, 1}}, {256, 256, 8, 4, {240, 240, 1}}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kRingTile = 8, kRingTile224 = 9, kRingTile192 = 10, kPPRingTile = 11;
 constexpr int kCUs = 256;

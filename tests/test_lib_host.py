@@ -211,8 +211,12 @@ def test_ring_tile_plan_info(monkeypatch):
     assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 128, 4)
     assert info(2048, 14336, 3584, api.MX_E4M3) == (256, 256, 64, 3)   # K % 1024 != 0: the ring
     assert info(4096, 4096, 4096, api.MX_F16) == (256, 256, 32, 3)
-    assert info(2048, 12288, 4096, api.MX_E4M3) == (256, 192, 64, 3)     # whole rounds of 256x192
-    assert info(2048, 6144, 4096, api.MX_E4M3) == (256, 192, 64, 3)
+    # the ping-pong kernel also beats whole rounds of 256x192 ring tiles where it applies ...
+    assert info(2048, 12288, 4096, api.MX_E4M3) == (256, 256, 64, 4)
+    assert info(2048, 6144, 4096, api.MX_E4M3) == (256, 256, 64, 4)
+    # ... and 256x192 ring tiles still win where it does not (K % 1024 != 0)
+    assert info(2048, 12288, 3584, api.MX_E4M3) == (256, 192, 64, 3)
+    assert info(2048, 6144, 3584, api.MX_E4M3) == (256, 192, 64, 3)
     for M, N, K, f in [(300, 520, 416, api.MX_E4M3), (4096, 8192, 1536, api.MX_E2M1), (512, 520, 512, api.MX_F16)]:
         assert info(M, N, K, f)[3] != 3
 
