@@ -1,5 +1,6 @@
-// mxgemm_ring.hip -- MX GEMM (E4M3 and/or E2M1 data, E8M0 scales per 32 along K) with a 4-stage
-// LDS ring: MXFP8, MXFP4 and the mixed pairs E4M3 x E2M1, E2M1 x E4M3.
+// mxgemm_ring.hip -- MX GEMMs (E8M0 scales per 32 along K) on two kernels: a 4-stage LDS ring of
+// 64-byte stage rows (every MX pair, and fp16) and, further below, an 8-wave ping-pong kernel of
+// 128-byte stage rows (the byte formats E4M3 / E5M2, E2M1 x E2M1 and the FP6 pairs, K % 1024 == 0).
 //
 //   C[m,n] = sum_k 2^(SA[m,k/32]-127) A[m,k] * 2^(SB[n,k/32]-127) B[n,k]   (fp32 accumulate, fp16 out)
 //
