@@ -81,6 +81,42 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def device_info(torch):
+    """The GPU the run used: name, architecture and compute-unit count (the peaks above assume
+    256 CUs at 2.4 GHz, AMD's MI355X figures)."""
+    pr = torch.cuda.get_device_properties(0)
+    return {"name": pr.name, "gcn_arch": getattr(pr, "gcnArchName", ""), "cus": pr.multi_processor_count,
+            "memory_gib": round(pr.total_memory / 2**30, 1)}
+
+
+def host_pack_times(np, synth):
+    """The library's host codec (mx_pack_host, one thread) packing the fp32 sources of each GEMM
+    workload and the matvec weights: context beside the oracle timings."""
+    import ctypes
+    from block_scaled_quantized_amd import api
+    out = {}
+    for name, fmt, shapes in (("mxfp8_gemm_128x256x128", api.MX_E4M3, ((128, 128), (256, 128))),
+                              ("mxfp8_gemm_2048x14336x4096", api.MX_E4M3, ((2048, 4096), (14336, 4096))),
+                              ("mxfp4_gemm_4096x8192x8192", api.MX_E2M1, ((4096, 8192), (8192, 8192))),
+                              ("matvec_int8_4096x14336", api.MX_INT8, ((4096, 14336),)),
+                              ("matvec_int4_4096x14336", api.MX_INT4, ((4096, 14336),))):
+        secs, nbytes = 0.0, 0
+        for rows, cols in shapes:
+            src = np.ascontiguousarray(synth.normal((rows, cols), 1.0, 7), dtype=np.float32)
+            if fmt in (api.MX_INT8, api.MX_INT4):
+                cs, ss = api.int_shapes(fmt, rows, cols)
+                codes, scales = np.empty(cs, np.uint8), np.empty(ss, np.float16)
+            else:
+                cs, ss = api.mx_shapes(fmt, rows, cols)
+                codes, scales = np.empty(cs, np.uint8), np.empty(ss, np.uint8)
+            t0 = time.perf_counter()
+            api.mx_pack_host(fmt, src, rows, cols, codes, scales)
+            secs += time.perf_counter() - t0
+            nbytes += src.nbytes
+        out[name] = {"seconds": secs, "source_gbs": nbytes / secs / 1e9, "threads": 1}
+    return out
+
+
 def cpu_baseline(np, synth, C_prefill, keep, budget_s):
     """The oracle (oracle/, plain C, fp64) timed on the host on every workload whose GPU output this
     run kept: the whole output where it is small (the 128x256x128 GEMM, the matvecs), else whole
@@ -259,6 +295,15 @@ def main():
     flops = 2.0 * M * N * K
     tflops = flops / (ms * 1e-3) / 1e12
     C0 = Cs[0]
+    # a separate pass with an event pair around every call: the median per call beside the mean
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    median_ms = per_call[len(per_call) // 2]
 
     detail = {}
     keep = {}  # GPU outputs the CPU baseline checks, by workload
@@ -460,6 +505,7 @@ def main():
         log("cpu baseline (oracle)")
         torch.cuda.synchronize()
         cpu = cpu_baseline(np, synth, C0, keep, args.cpu_seconds)
+        cpu["host_pack"] = host_pack_times(np, synth)
 
     kname = {4: "gemm_pp_ring_kernel", 3: "gemm_ring_kernel", 2: "gemm_pp_kernel"}.get(tile[3], "gemm_kernel")
     traffic, traffic_src = hbm_traffic(kname, list(tile), (M, N, K))
@@ -478,8 +524,10 @@ def main():
         "vs_baseline": None,
         "dtype": "mxfp8 (e4m3 x e8m0/32, fp32 accumulate, fp16 out)",
         "data": "synthetic: seeded PCG64, activations N(0,1), weights 0.02*N(0,1), quantised on the GPU",
+        "median_ms_per_call": median_ms,
         "config": {"workload": "mxfp8_gemm_prefill M=2048 N=14336 K=4096", "M": M, "N": N, "K": K,
                    "tile_m_n_k": list(tile), "input_sets_rotated": 3},
+        "device": device_info(torch),
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK["mxfp8"], "unit": "TFLOP/s",
                      "frac": tflops / PEAK["mxfp8"], "traffic": traffic,
                      "kernel": f"{kname}<E4M3, {tile[0]}x{tile[1]}>",
