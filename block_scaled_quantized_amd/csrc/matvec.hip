@@ -201,8 +201,8 @@ MX_DEV void compute_stage(const Stage<I8, C>& s, const v8h xa, v4f (&acc)[C]) {
 
 // Single-pass kernel (no workspace): one workgroup owns a column strip of TW = 16*C columns over
 // all of K. Its W waves take every W-th 32-row block, each wave covering all TW columns, so with 8
-// (int8) or 16 (int4) columns per lane a load instruction reads whole 128-byte lines of 4 rows.
-// The waves' sums meet in LDS and the workgroup writes y.
+// int8 columns per lane a load instruction reads whole 128-byte lines of 4 rows (int4: 64-byte
+// halves, for twice the workgroups). The waves' sums meet in LDS and the workgroup writes y.
 constexpr int kXsMax = 16384;  // activation halfs staged in LDS per workgroup (M * K)
 
 template <bool I8, int C, int W, int P, bool XL>
@@ -774,10 +774,12 @@ __global__ __launch_bounds__(512) void matvec_lds_kernel(const _Float16* __restr
   }
 }
 
-// Single-pass kernel shape (no workspace): 8 (int8) or 16 (int4) columns per lane, so a strip is
-// 128 bytes of every row; 8 waves per workgroup, 4 (int8) or 3 (int4) blocks of loads in flight
-// per wave.
-constexpr int kC8 = 8, kC4 = 16, kW = 8, kP8 = 4, kP4 = 3;
+// Single-pass kernel shape (no workspace): 8 columns per lane (a strip is 128 bytes of every int8
+// row, 64 of every int4 row); 8 waves per workgroup, 4 (int8) or 2 (int4) blocks of loads in flight
+// per wave. Measured at K=4096, N=14336: int4 with 16 columns per lane (128-byte rows, but only 56
+// workgroups) 25.3 us at M=1, with 8 columns and 2 blocks ahead 19.6 us (3 or 4 ahead: 20.1-20.2,
+// 4 columns: 22.8); int8 with 4 columns (224 workgroups of 64-byte rows) 24.3 against 24.1 us.
+constexpr int kC8 = 8, kC4 = 8, kW = 8, kP8 = 4, kP4 = 2;
 // Split kernel: an R-deep LDS ring; K is split until about kTargetWGs workgroups run.
 constexpr int kR = 8, kTargetWGs = 256;
 
