@@ -464,12 +464,21 @@ def main():
                 # enough weight copies (>= 384 MB) that repeats are not served by the Infinity Cache
                 nq = max(3, -(-(384 << 20) // (W.numel() + 2 * Ws.numel())))
                 qsets = [(W, Ws)] + [(W.clone(), Ws.clone()) for _ in range(nq - 1)]
-                t = timed(lambda i: api.mxmatvec_run(Mq, Nq, Kq, xq, qsets[i % nq][0], fw, qsets[i % nq][1], yq,
-                                                     None, None, stream), args.steps, args.warmup)
-                tf = 2.0 * Mq * Nq * Kq / (t * 1e-3) / 1e12
+                # with a workspace K is split across workgroups where the unsplit grid is small (the
+                # default a caller with a workspace gets); without one, the unsplit kernel
+                need = api.mxmatvec_workspace_size(Mq, Nq, Kq, fw)
+                wsq = torch.zeros(max(16, need), dtype=torch.uint8, device=dev) if need else None
                 nbytes = W.numel() + Ws.numel() * 2 + Mq * Kq * 2 + Mq * Nq * 2
-                detail[f"wq_gemm_{name}_{Mq}x{Nq}x{Kq}"] = {"us": t * 1e3, "tflops": tf, "frac_peak_fp16": tf / PEAK["fp16"],
-                                                            "gbs": nbytes / (t * 1e-3) / 1e9, "weight_copies": nq}
+                for label, wsp in (("", wsq), ("_no_workspace", None)):
+                    if label and need == 0:
+                        continue
+                    t = timed(lambda i: api.mxmatvec_run(Mq, Nq, Kq, xq, qsets[i % nq][0], fw, qsets[i % nq][1], yq,
+                                                         wsp, None, stream), args.steps, args.warmup)
+                    tf = 2.0 * Mq * Nq * Kq / (t * 1e-3) / 1e12
+                    detail[f"wq_gemm_{name}_{Mq}x{Nq}x{Kq}{label}"] = {
+                        "us": t * 1e3, "tflops": tf, "frac_peak_fp16": tf / PEAK["fp16"],
+                        "gbs": nbytes / (t * 1e-3) / 1e9, "weight_copies": nq,
+                        "workspace_bytes": need if wsp is not None else 0}
                 del qsets
             del wq, xq, yq
 

@@ -246,7 +246,7 @@ int mxmatvec_run_noalloc(int M, int N, int K, const void* x, const void* W, int 
   if (!x || !W || !Ws || !y) return MX_ERR_NULL;
   if (int s = matvec_shape(M, N, K, fw)) return s;
   if (!aligned16(x) || !aligned16(W) || !aligned16(Ws) || !aligned16(y)) return MX_ERR_ALIGN;
-  if (M <= 8 && matvec_workspace(M, N, K, fw == MX_INT8) > MXMATVEC_SCRATCH_BYTES) return MX_ERR_SCRATCH;
+  if (matvec_workspace(M, N, K, fw == MX_INT8) > MXMATVEC_SCRATCH_BYTES) return MX_ERR_SCRATCH;
   if (int a = check_arch()) return a;
   return sync_check(matvec_launch_noalloc(M, N, K, x, W, fw == MX_INT8, Ws, y, as_stream(stream)), as_stream(stream));
 }

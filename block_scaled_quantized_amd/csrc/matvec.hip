@@ -375,11 +375,25 @@ MX_DEV void flush_pending(v4f (&acc)[MT][C], const Pending<MT>& pend) {
 }
 
 constexpr int kWqWPol = 0;  // cache policy of the weight and scale loads
+constexpr int kWqMaxSplits = 8;  // K splits of the small-M GEMM
+
+// With S > 1 (grid.y = S) K is split too: workgroup (tile, sk) takes the 32-row blocks
+// [sk nblk / S, (sk + 1) nblk / S), writes its fp32 partial tile to part[sk][M][N], and the last
+// workgroup of the tile to arrive adds the S partials in split order (the same protocol as the split
+// matvec below: system-coherent 16-byte stores acknowledged before a device-scope counter increment
+// on counters[tile], which the last workgroup takes from S-1 back to 0).
+// Waves per SIMD the compiler must allow: two workgroups per CU for the 8-wave shapes of 4 columns
+// per lane with at most 32-row tiles (the split epilogue otherwise makes it settle for one workgroup
+// and twice the registers).
+template <int C, int MT, int W>
+constexpr int wq_waves_per_eu() { return C == 4 && W == 8 && MT <= 2 ? 4 : W / 4; }
 
 template <bool I8, int C, int MT, int W, int P>
-__global__ __launch_bounds__(W * 64) void gemm_wq_kernel(const _Float16* __restrict__ x, const uint8_t* __restrict__ Wt,
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(wq_waves_per_eu<C, MT, W>())))
+void gemm_wq_kernel(const _Float16* __restrict__ x, const uint8_t* __restrict__ Wt,
                                                          const _Float16* __restrict__ Ws, _Float16* __restrict__ y,
-                                                         int M, int N, int K) {
+                                                         int M, int N, int K, float* __restrict__ part,
+                                                         unsigned* __restrict__ counters, int S) {
   constexpr int TW = 16 * C, RT = 16 * MT;  // columns and activation rows of the workgroup's tile
   __shared__ __attribute__((aligned(16))) float red[W][RT][TW];
 
@@ -397,7 +411,8 @@ __global__ __launch_bounds__(W * 64) void gemm_wq_kernel(const _Float16* __restr
     bid = (xcd < rr ? xcd * (qq + 1) : rr * (qq + 1) + (xcd - rr) * qq) + idx;
   }
   const int n0 = (bid / mtiles) * TW, m0 = (bid % mtiles) * RT, col = n0 + C * i;
-  const int nblk = K / 32;
+  const int sk = (int)blockIdx.y, nall = K / 32;
+  const int kb0 = (int)((int64_t)sk * nall / S), nblk = (int)((int64_t)(sk + 1) * nall / S) - kb0;
 
   // Columns as in the single-pass kernel (lanes past N load the last C columns). Activation rows
   // come through a resource over rows m0..M-1: rows past M read as zero, their outputs are dropped.
@@ -421,7 +436,7 @@ __global__ __launch_bounds__(W * 64) void gemm_wq_kernel(const _Float16* __restr
 
   // this wave's blocks: wave + W*u, u < cnt; loads run P blocks ahead through a register ring
   const int cnt = nblk > wave ? (nblk - wave + W - 1) / W : 0;
-  auto blk = [&](int u) { return wave + W * u; };
+  auto blk = [&](int u) { return kb0 + wave + W * u; };
   Stage<I8, C, MT> ring[P];
   int t = 0;
   if (cnt >= 2 * P) {
@@ -465,15 +480,66 @@ __global__ __launch_bounds__(W * 64) void gemm_wq_kernel(const _Float16* __restr
       for (int v = 0; v < 4; v++) red[wave][16 * tt + 4 * q + v][C * i + j] = acc[tt][j][v];
   __syncthreads();
   const int rows = min(RT, M - m0);
+  if (S == 1) {
+    for (int o = threadIdx.x; o < rows * (TW / 4); o += W * 64) {
+      const int r = o / (TW / 4), c = 4 * (o % (TW / 4));
+      if (n0 + c >= N) continue;  // N % 4 == 0: a 4-column group is all in or all out
+      v4f v = *reinterpret_cast<const v4f*>(&red[0][r][c]);
+#pragma unroll
+      for (int w = 1; w < W; w++) v += *reinterpret_cast<const v4f*>(&red[w][r][c]);
+      v4h h;
+#pragma unroll
+      for (int e = 0; e < 4; e++) h[e] = (_Float16)v[e];
+      *reinterpret_cast<v4h*>(y + (int64_t)(m0 + r) * N + n0 + c) = h;
+    }
+    return;
+  }
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const rsrc_t pr = make_rsrc(part, (uint32_t)S * (uint32_t)M * (uint32_t)N * 4u);
+#pragma unroll 1
   for (int o = threadIdx.x; o < rows * (TW / 4); o += W * 64) {
     const int r = o / (TW / 4), c = 4 * (o % (TW / 4));
-    if (n0 + c >= N) continue;  // N % 4 == 0: a 4-column group is all in or all out
+    if (n0 + c >= N) continue;
     v4f v = *reinterpret_cast<const v4f*>(&red[0][r][c]);
 #pragma unroll
     for (int w = 1; w < W; w++) v += *reinterpret_cast<const v4f*>(&red[w][r][c]);
+    // element copies first: a bit cast of an ext-vector element read element 0
+    const float e0 = v[0], e1 = v[1], e2 = v[2], e3 = v[3];
+    const u4 val = {__builtin_bit_cast(uint32_t, e0), __builtin_bit_cast(uint32_t, e1), __builtin_bit_cast(uint32_t, e2),
+                    __builtin_bit_cast(uint32_t, e3)};
+    __builtin_amdgcn_raw_buffer_store_b128(val, pr, 4u * (uint32_t)(((sk * M) + m0 + r) * N + n0 + c), 0, 17);  // sc0 sc1
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are acknowledged
+  __syncthreads();
+  // the flag lives in red, free once every thread is past its reads above (an extra LDS variable
+  // would cost this kernel its occupancy: the compiler rounds the allocation up)
+  int* last = reinterpret_cast<int*>(&red[0][0][0]);
+  if (threadIdx.x == 0) *last = atomicInc(&counters[blockIdx.x], (unsigned)(S - 1)) == (unsigned)(S - 1);
+  __syncthreads();
+  if (!*last) return;
+#pragma unroll 1
+  for (int o = threadIdx.x; o < rows * (TW / 4); o += W * 64) {
+    const int r = o / (TW / 4), c = 4 * (o % (TW / 4));
+    if (n0 + c >= N) continue;
+    const uint32_t off = 4u * (uint32_t)((m0 + r) * N + n0 + c), sstride = 4u * (uint32_t)M * (uint32_t)N;
+    u4 v[kWqMaxSplits];
+#pragma unroll
+    for (int sp = 0; sp < kWqMaxSplits; sp++)
+      if (sp < S) v[sp] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(pr, off + sp * sstride, 0, 17));
+    float sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sp = 0; sp < kWqMaxSplits; sp++)
+      if (sp < S) {
+        const u4 w = v[sp];
+        const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+        sum[0] += __builtin_bit_cast(float, w0);
+        sum[1] += __builtin_bit_cast(float, w1);
+        sum[2] += __builtin_bit_cast(float, w2);
+        sum[3] += __builtin_bit_cast(float, w3);
+      }
     v4h h;
 #pragma unroll
-    for (int e = 0; e < 4; e++) h[e] = (_Float16)v[e];
+    for (int e = 0; e < 4; e++) h[e] = (_Float16)sum[e];
     *reinterpret_cast<v4h*>(y + (int64_t)(m0 + r) * N + n0 + c) = h;
   }
 }
@@ -863,15 +929,51 @@ int launch(int M, int N, int K, const void* x, const void* W, const void* Ws, vo
 constexpr int kWqMaxWGs = 3 * 256, kWqMinWide = 192, kWqOneRound = 256;
 
 template <bool I8, int C, int MT, int W, int P>
-int launch_wq_mt(int M, int N, int K, const void* x, const void* Wt, const void* Ws, void* y, hipStream_t st) {
-  const dim3 grid((unsigned)(((N + 16 * C - 1) / (16 * C)) * ((M + 16 * MT - 1) / (16 * MT))));
+int launch_wq_mt(int M, int N, int K, const void* x, const void* Wt, const void* Ws, void* y, hipStream_t st,
+                 float* part = nullptr, unsigned* counters = nullptr, int S = 1) {
+  const dim3 grid((unsigned)(((N + 16 * C - 1) / (16 * C)) * ((M + 16 * MT - 1) / (16 * MT))), (unsigned)S);
   hipLaunchKernelGGL((gemm_wq_kernel<I8, C, MT, W, P>), grid, dim3(W * 64), 0, st, (const _Float16*)x,
-                     (const uint8_t*)Wt, (const _Float16*)Ws, (_Float16*)y, M, N, K);
+                     (const uint8_t*)Wt, (const _Float16*)Ws, (_Float16*)y, M, N, K, part, counters, S);
   return launch_status();
 }
 
+// K split of the small-M GEMM (used when a workspace is given and the unsplit grid would be small):
+// 128-column strips (8 columns per lane, whole 128-byte lines of int8 rows), 32-row tiles, 8 waves,
+// and S splits so that about kTargetWGs workgroups run, each split at least 8 blocks. Measured at
+// K=4096 against the unsplit kernel (int8 / int4): M=64, N=4096 17.1 -> 13.1 / 15.0 -> 12.1 us;
+// M=128, N=4096 24.9 -> 17.4 / 22.4 -> 15.5 us; M=24, N=14336 35.3 -> 20.4 / 27.9 -> 17.2 us; M=16,
+// N=4096 19.4 -> 9.7 / 17.3 -> 8.8 us. 64-column strips with 16-, 32- or 64-row tiles measured up to
+// 12% faster at M <= 32, N=4096, but 25-40% slower at N=14336; 64-row tiles of 128 columns were slower
+// everywhere the split applies. Workspace: the counter region, then the fp32 partials [S][M][N].
+constexpr int kWqSplitC = 8, kWqSplitMT = 2, kWqSplitW = 8;
+struct WqSplit {
+  int S;
+  size_t bytes;
+};
+
+WqSplit wq_split_plan(int M, int N, int K) {
+  WqSplit w{1, 0};
+  if (M <= 8) return w;
+  const int64_t tiles = (int64_t)((N + 16 * kWqSplitC - 1) / (16 * kWqSplitC)) *
+                        ((M + 16 * kWqSplitMT - 1) / (16 * kWqSplitMT));
+  int64_t S = kTargetWGs / tiles;
+  if (S > kWqMaxSplits) S = kWqMaxSplits;
+  if (S > K / 32 / 8) S = K / 32 / 8;
+  if (S < 2) return w;
+  w.S = (int)S;
+  w.bytes = kCounterBytes + ((size_t)S * M * N * 4 + 255) / 256 * 256;
+  return w;
+}
+
 template <bool I8>
-int launch_wq(int M, int N, int K, const void* x, const void* W, const void* Ws, void* y, hipStream_t st) {
+int launch_wq(int M, int N, int K, const void* x, const void* W, const void* Ws, void* y, void* ws, size_t ws_bytes,
+              hipStream_t st) {
+  const WqSplit sp = wq_split_plan(M, N, K);
+  if (sp.S > 1 && ws && ws_bytes >= sp.bytes) {
+    unsigned* counters = (unsigned*)ws;
+    float* part = (float*)((char*)ws + kCounterBytes);
+    return launch_wq_mt<I8, kWqSplitC, kWqSplitMT, kWqSplitW, 2>(M, N, K, x, W, Ws, y, st, part, counters, sp.S);
+  }
   const int64_t strips4 = (N + 63) / 64, strips8 = (N + 127) / 128;
   if (M > 32 && strips8 * ((M + 63) / 64) >= kWqMinWide) return launch_wq_mt<I8, 8, 4, 4, 2>(M, N, K, x, W, Ws, y, st);
   if (strips4 * ((M + 15) / 16) <= kWqOneRound) return launch_wq_mt<I8, 4, 1, 16, 2>(M, N, K, x, W, Ws, y, st);
@@ -927,20 +1029,23 @@ int scratch_address(hipStream_t st, void** out) {
 }  // namespace
 
 namespace mx {
-size_t matvec_workspace(int M, int N, int K, bool int8) { return M > 8 ? 0 : split_plan(M, N, K, int8).bytes; }
+size_t matvec_workspace(int M, int N, int K, bool int8) {
+  return M > 8 ? wq_split_plan(M, N, K).bytes : split_plan(M, N, K, int8).bytes;
+}
 
 // mxmatvec_run with the split kernel's workspace in the static scratch array: the same kernels and
 // launch shapes as a call with a large enough caller workspace, so the same results bit for bit.
 int matvec_launch_noalloc(int M, int N, int K, const void* x, const void* W, bool int8, const void* Ws, void* y,
                           hipStream_t stream) {
-  if (M > 8)
-    return int8 ? launch_wq<true>(M, N, K, x, W, Ws, y, stream) : launch_wq<false>(M, N, K, x, W, Ws, y, stream);
-  const size_t need = split_plan(M, N, K, int8).bytes;
+  const size_t need = matvec_workspace(M, N, K, int8);
   if (need > kScratchBytes) return MX_ERR_SCRATCH;
   void* ws = nullptr;
   if (need > 0) {
     if (int s = scratch_address(stream, &ws)) return s;
   }
+  if (M > 8)
+    return int8 ? launch_wq<true>(M, N, K, x, W, Ws, y, ws, need, stream)
+                : launch_wq<false>(M, N, K, x, W, Ws, y, ws, need, stream);
   return int8 ? launch<true>(M, N, K, x, W, Ws, y, ws, need, stream)
               : launch<false>(M, N, K, x, W, Ws, y, ws, need, stream);
 }
@@ -948,7 +1053,8 @@ int matvec_launch_noalloc(int M, int N, int K, const void* x, const void* W, boo
 int matvec_launch(int M, int N, int K, const void* x, const void* W, bool int8, const void* Ws, void* y, void* ws,
                   size_t ws_bytes, hipStream_t stream) {
   if (M > 8)
-    return int8 ? launch_wq<true>(M, N, K, x, W, Ws, y, stream) : launch_wq<false>(M, N, K, x, W, Ws, y, stream);
+    return int8 ? launch_wq<true>(M, N, K, x, W, Ws, y, ws, ws_bytes, stream)
+                : launch_wq<false>(M, N, K, x, W, Ws, y, ws, ws_bytes, stream);
   return int8 ? launch<true>(M, N, K, x, W, Ws, y, ws, ws_bytes, stream)
               : launch<false>(M, N, K, x, W, Ws, y, ws, ws_bytes, stream);
 }

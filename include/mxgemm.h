@@ -174,9 +174,12 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
  * block scale.
  *
  * Workspace (an addition to the call the pages' operation needs: workspace = NULL gives exactly
- * that call). For M <= 8 the fastest kernel splits K across workgroups: their fp32 partial sums and
- * one counter per column strip live in a caller-owned device buffer of mxmatvec_workspace_size()
- * bytes (16-byte aligned). M > 8 never uses one.
+ * that call). The fastest kernels split K across workgroups: their fp32 partial sums and one counter
+ * per column strip (M <= 8) or per tile (M > 8) live in a caller-owned device buffer of
+ * mxmatvec_workspace_size() bytes (16-byte aligned). For M <= 8 that is every shape with at least
+ * 8 blocks of K; for M > 8 only shapes whose unsplit grid is small (fewer than 128 tiles of 32 rows
+ * by 128 columns and K >= 512; mxmatvec_workspace_size returns 0 for the others, which never touch
+ * the buffer).
  *  - The buffer must be zero-filled once before its first use (hipMemset, or any zeroed
  *    allocation). Every call leaves its counters at zero again, so the buffer stays valid for any
  *    later call whose requirement it meets.
@@ -186,8 +189,8 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
  *    strip of y is then wrong or left unwritten, and later calls on the same buffer inherit the
  *    stale counter. Zero the counter region again to recover. Calls that may overlap in time need
  *    separate workspaces.
- *  - The last workgroup of each strip adds the partial sums in a fixed order, so results are
- *    deterministic.
+ *  - The last workgroup of each strip (or tile) adds the partial sums in a fixed order, so results
+ *    are deterministic.
  *  - With workspace == NULL, or workspace_bytes below the requirement, K is not split across
  *    workgroups and the buffer is not touched (same results up to fp32 summation order; slower
  *    when N is small compared with the number of compute units).
@@ -196,11 +199,13 @@ int mxmatvec_run(int M, int N, int K, const void* x, const void* W, int fw, cons
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes mxmatvec_run uses for this shape (0: none needed, or an invalid shape). For
- * 1 <= M <= 8 the requirement never decreases as M grows for fixed N, K and fw; for M > 8 it is 0. */
+ * 1 <= M <= 8 the requirement never decreases as M grows for fixed N, K and fw; for M > 8 it can
+ * (a larger M has more tiles and so fewer K splits). */
 size_t mxmatvec_workspace_size(int M, int N, int K, int fw);
 
 /* Size of the library's static scratch array (8 MiB), the most workspace mxmatvec_run_noalloc can
- * use. It covers the decode shapes up to N = 14336 at K = 4096 for int8 and int4 at any M <= 8. */
+ * use. It covers the decode shapes up to N = 14336 at K = 4096 for int8 and int4 at any M <= 8,
+ * and every M > 8 shape (at most 256 splits x tiles of 32 x 128 fp32 partials: 4 MiB + 16 KiB). */
 #define MXMATVEC_SCRATCH_BYTES ((size_t)8 << 20)
 
 /*

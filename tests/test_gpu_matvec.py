@@ -131,46 +131,79 @@ def test_matvec_small_workspace_falls_back(orc):
 
 # ---- the same product at 9 <= M <= 256 (small-M GEMM kernel) --------------------------------
 
-def wq_case(orc, api, fw, M, K, N, seed_w, seed_x):
+def wq_case(orc, api, fw, M, K, N, seed_w, seed_x, path):
+    """path "split": with the shared workspace (K split across workgroups where the plan asks for a
+    workspace), called on x, on x2 (checked too, so stale partials or counters show up) and on x
+    again (the same bits); "single": no workspace. Returns x, the codes and scales, y from x, R."""
     w = synth.normal((K, N), 0.02, seed_w)
     x = synth.normal((M, K), 1.0, seed_x).astype(np.float16)
+    x2 = synth.normal((M, K), 1.0, seed_x + 7000).astype(np.float16)
     W, Ws = gpu_int_pack(api, fw, w)
     q, s = orc.int_quantize(fw, w)
     oW = q.view(np.uint8) if fw == api.MX_INT8 else orc.pack_int4(q)
     assert np.array_equal(host(W), oW) and np.array_equal(host(Ws).view(np.uint16), s.view(np.uint16))
-    assert api.mxmatvec_workspace_size(M, N, K, fw) == 0
-    y = nan_f16((M, N))
-    api.mxmatvec_run(M, N, K, dev(x), W, fw, Ws, y)
     R = orc.rms_ab(x.astype(np.float64), orc.dequant(fw, oW, s, K, N))
-    return x, oW, s, host(y).astype(np.float64), R
+    if path == "single":
+        y = nan_f16((M, N))
+        api.mxmatvec_run(M, N, K, dev(x), W, fw, Ws, y)
+        return x, oW, s, host(y).astype(np.float64), R
+    ws = workspace(api, M, N, K, fw)
+    outs = []
+    for xi in (x, x2, x):
+        y = nan_f16((M, N))
+        api.mxmatvec_run(M, N, K, dev(xi), W, fw, Ws, y, ws)
+        outs.append(host(y).copy())
+    assert np.array_equal(outs[0].view(np.uint16), outs[2].view(np.uint16)), "small-M GEMM not repeatable"
+    R2 = orc.rms_ab(x2.astype(np.float64), orc.dequant(fw, oW, s, K, N))
+    ok, ratio, bad = orc.check(outs[1].astype(np.float64), orc.matvec(fw, x2, oW, s, K, N), K, R2)
+    assert ok, ("second activations", ratio, bad)
+    return x, oW, s, outs[0].astype(np.float64), R
 
 
+def wq_splits(M, K, N):
+    """The K split the plan takes with a workspace: 128-column strips, 32-row tiles, about 256
+    workgroups, at most 8 splits and at least 8 blocks each (1: not split)."""
+    tiles = -(-N // 128) * -(-M // 32)
+    S = min(256 // tiles, 8, K // 256)
+    return S if S >= 2 else 1
+
+
+@pytest.mark.parametrize("path", ["split", "single"])
 @pytest.mark.parametrize("fw", [32, 33])
 @pytest.mark.parametrize("M,K,N", [(9, 32, 32), (16, 1024, 1056), (31, 96, 160), (33, 4096, 64), (64, 544, 4128),
                                    (100, 256, 12288), (128, 4096, 512), (129, 160, 96), (200, 1024, 1024),
                                    (256, 2048, 320), (150, 96, 12800), (200, 64, 16384), (129, 64, 19200),
-                                   (20, 64, 25600), (144, 96, 6144)])
-def test_wq_gemm_ragged(orc, fw, M, K, N):
-    """Every output: partial row tiles, partial column strips, one block of K up to many. Launch
-    shapes: 128-column strips with 64-row tiles at M=100/N=12288, M=150/N=12800, M=200/N=16384 and
-    M=129/N=19200 (the last tile with 1 row); 64-column strips with 32-row tiles at M=20/N=25600 and
-    M=144/N=6144; 64-column strips with 16-row tiles for the rest."""
+                                   (20, 64, 25600), (144, 96, 6144), (24, 2048, 1056), (17, 512, 14336)])
+def test_wq_gemm_ragged(orc, fw, M, K, N, path):
+    """Every output: partial row tiles, partial column strips, one block of K up to many. Unsplit
+    launch shapes: 128-column strips with 64-row tiles at M=100/N=12288, M=150/N=12800,
+    M=200/N=16384 and M=129/N=19200 (the last tile with 1 row); 64-column strips with 32-row tiles at
+    M=20/N=25600 and M=144/N=6144; 64-column strips with 16-row tiles for the rest. With a workspace,
+    K is split 4 ways at M=16/N=1056 and M=200/N=1024, 8 ways at M=33/N=64, M=128/N=512,
+    M=256/N=320 and M=24/N=1056, and 2 ways at M=64/K=544 (17 blocks: 8 + 9) and M=17/N=14336."""
     api = require_gpu()
-    say(f"wq gemm fw={fw} M={M} K={K} N={N}")
-    x, oW, s, got, R = wq_case(orc, api, fw, M, K, N, 13 * K + N + M, 5 * K + M)
+    S = wq_splits(M, K, N)
+    need = api.mxmatvec_workspace_size(M, N, K, fw)
+    assert (need > 0) == (S > 1)
+    if S > 1:
+        assert need == 16384 + -(-(S * M * N * 4) // 256) * 256
+    say(f"wq gemm fw={fw} M={M} K={K} N={N} path={path} splits={S if path == 'split' else 1}")
+    x, oW, s, got, R = wq_case(orc, api, fw, M, K, N, 13 * K + N + M, 5 * K + M, path)
     ok, ratio, bad = orc.check(got, orc.matvec(fw, x, oW, s, K, N), K, R)
     assert ok, (ratio, bad)
 
 
+@pytest.mark.parametrize("path", ["split", "single"])
 @pytest.mark.parametrize("fw", [32, 33])
 @pytest.mark.parametrize("M,K,N", [(128, 4096, 12288), (64, 4096, 4096)])
-def test_wq_gemm_full_size_sampled(orc, fw, M, K, N):
+def test_wq_gemm_full_size_sampled(orc, fw, M, K, N, path):
     """The W8A16 / W4A16 prefill shapes: 2048 sampled outputs (corners included) against the
-    oracle's per-element formula, and all of y finite."""
+    oracle's per-element formula, and every output written (y starts as NaN). M=64/N=4096 splits K
+    4 ways with a workspace; M=128/N=12288 is never split."""
     api = require_gpu()
-    say(f"wq gemm full fw={fw} M={M} K={K} N={N}")
+    say(f"wq gemm full fw={fw} M={M} K={K} N={N} path={path}")
     x, oW, s, got, R = wq_case(orc, api, fw, M, K, N, synth.seed_for(synth.WQ_PREFILL, 1),
-                                synth.seed_for(synth.WQ_PREFILL, 0))
+                                synth.seed_for(synth.WQ_PREFILL, 0), path)
     assert np.isfinite(got).all()
     ms, ns = synth.sample_points(M, N, 2048, 77)
     ref = np.array([orc.matvec_elem(fw, x, oW, s, K, N, int(m), int(n)) for m, n in zip(ms, ns)])

@@ -278,7 +278,6 @@ def test_mixed_pairs_plan(monkeypatch):
 def test_matvec_workspace_size():
     """Split-K workspace: fp32 partials [S][M][N] (256-byte rounded) plus a counter per strip;
     zero for invalid shapes, never decreasing in M."""
-    assert api.mxmatvec_workspace_size(9, 14336, 4096, api.MX_INT8) == 0
     assert api.mxmatvec_workspace_size(1, 14336, 4096, 0) == 0
     for fw in (api.MX_INT8, api.MX_INT4):
         sizes = [api.mxmatvec_workspace_size(m, 14336, 4096, fw) for m in range(1, 9)]
@@ -290,10 +289,22 @@ def test_matvec_workspace_size():
 
 
 def test_small_m_gemm_shape_rules():
-    """9 <= M <= 256 is the small-M GEMM form: accepted up to 256 rows and never given a workspace."""
-    for M in (9, 64, 128, 256):
-        assert api.mxmatvec_workspace_size(M, 12288, 4096, api.MX_INT4) == 0
-        assert api.mxmatvec_workspace_size(M, 4096, 4096, api.MX_INT8) == 0
+    """9 <= M <= 256 is the small-M GEMM form, accepted up to 256 rows. With a workspace it splits K
+    where 128-column strips of 32-row tiles make fewer than 128 workgroups: S = min(256 // tiles, 8,
+    K // 256) splits when that is at least 2, each writing fp32 partials [S][M][N] after the
+    16384-byte counter region."""
+    def split_bytes(M, N, K):
+        tiles = -(-N // 128) * -(-M // 32)
+        S = min(256 // tiles, 8, K // 256)
+        return 0 if S < 2 else 16384 + -(-(S * M * N * 4) // 256) * 256
+    for fw in (api.MX_INT8, api.MX_INT4):
+        for M, N, K in ((9, 12288, 4096), (64, 12288, 4096), (128, 12288, 4096), (256, 12288, 4096),
+                        (9, 4096, 4096), (64, 4096, 4096), (128, 4096, 4096), (256, 4096, 4096),
+                        (24, 14336, 4096), (64, 4096, 224), (200, 1024, 1024), (33, 64, 4096)):
+            assert api.mxmatvec_workspace_size(M, N, K, fw) == split_bytes(M, N, K), (M, N, K)
+    assert api.mxmatvec_workspace_size(64, 4096, 4096, api.MX_INT8) == 16384 + 4 * 64 * 4096 * 4
+    assert api.mxmatvec_workspace_size(128, 12288, 4096, api.MX_INT4) == 0   # 384 tiles: not split
+    assert api.mxmatvec_workspace_size(64, 4096, 224, api.MX_INT8) == 0      # 7 blocks: not split
     assert api.mxmatvec_workspace_size(257, 4096, 4096, api.MX_INT8) == 0     # invalid shape
     assert api.mxmatvec_workspace_size(8, 4096, 4096, api.MX_INT8) > 0
 

@@ -41,11 +41,20 @@ def test_noalloc_matches_workspace_call_twice(orc):
     one(orc, api, api.MX_INT8, 3, 1024, 4128, 4200)      # smaller, on the scratch the first left
 
 
-def test_noalloc_small_m_gemm_and_single_pass(orc):
-    """M > 8 (no workspace at all) and a shape the split kernel does not take: same bits as
-    mxmatvec_run."""
+def test_noalloc_small_m_gemm_split_twice(orc):
+    """The small-M GEMM with K split across workgroups (partials and counters in the scratch
+    array): the same bits as the workspace call, then a smaller problem on what the first left."""
     api = require_gpu()
-    for fw, M, K, N in ((api.MX_INT8, 64, 1024, 4096), (api.MX_INT4, 2, 64, 96)):
+    say("noalloc: small-M GEMM split, then a smaller one")
+    one(orc, api, api.MX_INT8, 64, 1024, 4096, 4400)     # 64 tiles, K split 4 ways
+    one(orc, api, api.MX_INT4, 24, 2048, 1056, 4500)     # 9 tiles, K split 8 ways
+
+
+def test_noalloc_small_m_gemm_and_single_pass(orc):
+    """Shapes that need no workspace (a small-M GEMM whose K is too short to split, and a decode
+    shape the split kernel does not take): same bits as mxmatvec_run."""
+    api = require_gpu()
+    for fw, M, K, N in ((api.MX_INT8, 64, 224, 4096), (api.MX_INT4, 2, 64, 96)):
         say(f"noalloc passthrough fw={fw} M={M} K={K} N={N}")
         assert api.mxmatvec_workspace_size(M, N, K, fw) == 0
         w = synth.normal((K, N), 0.02, 4300 + M)
