@@ -321,7 +321,8 @@ __global__ __launch_bounds__(W * 64) void matvec_kernel(const _Float16* __restri
 // the whole of K; its W waves split K as in the single-pass kernel. Each dequantised weight
 // fragment of a block feeds MT MFMAs, one per activation tile, so the weight conversion is shared
 // by 16*MT rows; every block product is still scaled by its fp16 block scale in fp32 (one FMA per
-// output per block) and added to an fp32 accumulator. The waves' accumulators meet in LDS.
+// output per block) and added to an fp32 accumulator. The waves' accumulators meet in LDS. Given a
+// workspace, grids of few tiles also split K across workgroups (wq_split_plan below).
 // ---------------------------------------------------------------------------------------------
 // One block, software-pipelined across the column offsets e of the lane's C columns: the MFMAs of
 // offset e (one per activation tile) alternate with the scale FMAs of offset e-1, whose products
