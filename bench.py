@@ -122,7 +122,8 @@ def cpu_baseline(np, synth, C_prefill, keep, budget_s):
     run kept: the whole output where it is small (the 128x256x128 GEMM, the matvecs), else whole
     rows of C computed in chunks of one row per thread until `budget_s` seconds have passed, with
     the full-output time extrapolated (rows are independent and cost the same). The oracle
-    quantises the fp32 sources itself. Each checked GPU row is compared with the acceptance bound."""
+    quantises the fp32 sources itself. Each checked GPU row is compared with the acceptance bound;
+    the E4M3 pack's rows (the oracle's quantiser on the same fp32 source) are compared bit for bit."""
     import oracle as orc
     affinity = len(os.sched_getaffinity(0))
     env = os.environ.get("OMP_NUM_THREADS", "")
@@ -196,6 +197,37 @@ def cpu_baseline(np, synth, C_prefill, keep, budget_s):
     if "mxfp4" in keep:
         log_("mxfp4 4096x8192x8192")
         mx_leg("mxfp4_gemm_4096x8192x8192", orc.E2M1, 4096, 8192, 8192, synth.MXFP4_LARGE, 1.0, keep["mxfp4"])
+    for Mq, Nq, Kq in ((128, 12288, 4096), (64, 4096, 4096)):   # the small-M weight GEMM, row by row
+        if not any(k.startswith(f"wq_gemm_") and k.endswith(f"_{Mq}x{Nq}x{Kq}") for k in keep):
+            continue
+        w = synth.normal((Kq, Nq), 0.02, synth.seed_for(synth.WQ_PREFILL, 1))
+        xq = synth.normal((Mq, Kq), 1.0, synth.seed_for(synth.WQ_PREFILL, 0)).astype(np.float16)
+        for fw, name in ((orc.INT4, "int4"), (orc.INT8, "int8")):
+            key = f"wq_gemm_{name}_{Mq}x{Nq}x{Kq}"
+            if key not in keep:
+                continue
+            log_(key)
+            q, s = orc.int_quantize(fw, w)
+            oW = q.view(np.uint8) if fw == orc.INT8 else orc.pack_int4(q)
+            R = orc.rms_ab(xq.astype(np.float64), orc.dequant(fw, oW, s, Kq, Nq))
+            rows_leg(key, Mq, Nq, Kq, 2.0 * Nq * Kq,
+                     lambda r0, n: orc.matvec(fw, xq[r0:r0 + n], oW, s, Kq, Nq), R, keep[key])
+        del w
+    if "pack_e4m3" in keep:   # the quantiser (brute-force nearest code per element), row by row
+        log_("pack e4m3 2048x4096")
+        src = synth.normal((2048, 4096), 1.0, synth.seed_for(synth.MXFP8_PREFILL, 0))
+        g_codes, g_scales = (t.cpu().numpy() for t in keep["pack_e4m3"])
+        done, t, exact = 0, 0.0, True
+        while done < 2048 and (t < budget_s or done == 0):
+            n = min(threads, 2048 - done)
+            t0 = time.perf_counter()
+            oc, osc = orc.mx_quantize(orc.E4M3, src[done:done + n])
+            t += time.perf_counter() - t0
+            exact = exact and np.array_equal(oc, g_codes[done:done + n]) and np.array_equal(osc, g_scales[done:done + n])
+            done += n
+        configs["pack_e4m3_2048x4096"] = {"rows": done, "of_rows": 2048, "seconds": t, "extrapolated": done < 2048,
+                                          "full_output_seconds": t * 2048 / done,
+                                          "source_gbs": done * 4096 * 4 / t / 1e9, "gpu_bit_exact": bool(exact)}
     head = configs["mxfp8_gemm_2048x14336x4096"]
     return {"value": head["tflops"], "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"rows 0..{head['rows'] - 1} of C for the MXFP8 GEMM M=2048,N=14336,K=4096 "
@@ -474,6 +506,8 @@ def main():
                         continue
                     t = timed(lambda i: api.mxmatvec_run(Mq, Nq, Kq, xq, qsets[i % nq][0], fw, qsets[i % nq][1], yq,
                                                          wsp, None, stream), args.steps, args.warmup)
+                    if not label:
+                        keep[f"wq_gemm_{name}_{Mq}x{Nq}x{Kq}"] = yq.clone()
                     tf = 2.0 * Mq * Nq * Kq / (t * 1e-3) / 1e12
                     detail[f"wq_gemm_{name}_{Mq}x{Nq}x{Kq}{label}"] = {
                         "us": t * 1e3, "tflops": tf, "frac_peak_fp16": tf / PEAK["fp16"],
@@ -492,6 +526,7 @@ def main():
         t = timed(lambda i: api.mx_pack_run(api.MX_E4M3, src, rows, cols, A8, S8, stream), args.steps, args.warmup)
         nbytes = rows * cols * 4 + rows * cols + rows * cols // 32
         detail["pack_e4m3_2048x4096"] = {"us": t * 1e3, "gbs": nbytes / (t * 1e-3) / 1e9}
+        keep["pack_e4m3"] = (A8.clone(), S8.clone())
         out = torch.empty((rows, cols), dtype=torch.float32, device=dev)
         t = timed(lambda i: api.mx_unpack_run(api.MX_E4M3, A8, S8, rows, cols, out, stream), args.steps, args.warmup)
         detail["unpack_e4m3_2048x4096"] = {"us": t * 1e3, "gbs": nbytes / (t * 1e-3) / 1e9}
