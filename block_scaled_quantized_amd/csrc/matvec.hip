@@ -224,7 +224,17 @@ __global__ __launch_bounds__(W * 64) void matvec_kernel(const _Float16* __restri
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i = lane & 15, q = lane >> 4;
-  const int strip = blockIdx.x, kb0 = 0, kb1 = K / 32;
+  // Workgroups go to the 8 XCDs round-robin by id. A strip narrower than a 128-byte line of a
+  // weight row (int4 here: 64 bytes) shares its lines with a neighbour, so the id is then remapped
+  // to give each XCD a contiguous range of strips and both halves of a line are fetched into the
+  // same L2 (in id order every int4 weight line went to two L2s; the remap measured 2% faster there
+  // and 2% slower on int8's whole-line strips, which keep the id order).
+  int strip = (int)blockIdx.x;
+  if constexpr ((I8 ? C : C / 2) < 128 / 16) {
+    const int nwg = (int)gridDim.x, xcd = strip & 7, idx = strip >> 3, qq = nwg >> 3, rr = nwg & 7;
+    strip = (xcd < rr ? xcd * (qq + 1) : rr * (qq + 1) + (xcd - rr) * qq) + idx;
+  }
+  const int kb0 = 0, kb1 = K / 32;
   const int KC = K;
   const int n0 = strip * TW, col = n0 + C * i;
 
@@ -563,9 +573,29 @@ constexpr int kMaxSplits = 16;
 //  - The activations of the split's K range sit in LDS (staged once).
 // ---------------------------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-constexpr int kLChunk = 4 * 256 + 32;        // LDS bytes of 4 weight rows, padded
-constexpr int kLStage = 8 * kLChunk + 1024;  // a block: 8 chunks + its scale row (<= 1 KB)
 constexpr int kXsLds = 8192;                 // activation halfs staged per workgroup
+
+// Geometry of the split kernel with CG column groups of 64 bytes per row: a strip is 64*CG bytes of
+// every row (TW columns), a copy instruction fills a 1 KB chunk of CR rows, a 32-row block is NCH
+// chunks (padded to LCH bytes, so the fragment reads of the 4 row groups q hit disjoint bank
+// groups) plus its scale row, and the 8 waves are CG column groups x PAR stage parities.
+template <bool I8, int CG>
+struct LdsGeo {
+  static constexpr int C = I8 ? 4 : 8;        // columns per lane
+  static constexpr int TW = 16 * C * CG;      // columns per strip
+  static constexpr int SBYTES = 64 * CG;      // bytes of a row in the strip
+  static constexpr int PAR = 8 / CG;          // stages (32-row blocks) per step
+  static constexpr int CR = 1024 / SBYTES;    // rows per chunk
+  static constexpr int NCH = 32 / CR;         // chunks per block (= 2 CG: wave (cg, par) copies 2cg, 2cg+1)
+  static constexpr int LCH = 1024 + 256 / NCH;  // padded chunk stride
+  static constexpr int SB = 2 * TW;           // scale bytes of a strip row
+  static constexpr int STAGE = NCH * LCH + 1024;  // the scale row (SB <= 1 KB) in a whole 1 KB
+  static constexpr int SLANES = SB / CG / 16;  // lanes per wave copying scales
+  // LDS offset of row j (0..7) of the lane's 8 fragment rows from its first row's dword
+  static constexpr int roff(int j) { return (j / CR) * LCH + (j % CR) * SBYTES; }
+  static_assert(CG == 2 || CG == 4, "strips of 128 or 256 bytes per row");
+  static_assert(NCH == 2 * CG && (LCH / 4) * (8 / CR) % 64 == 16 && SB <= 1024, "copy split and bank layout");
+};
 static_assert(kXsLds % 512 == 0, "the activation copies fill whole 1 KB pieces of xs");
 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
@@ -584,51 +614,54 @@ MX_DEV void wait_vm_n(int n) {
 MX_DEV void raw_barrier() { asm volatile("s_barrier" ::: "memory"); }
 MX_DEV void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }  // lgkmcnt(0) only
 
-// The lane's 8 fragment dwords (rows 8q..8q+7 of a stage: chunk offsets 0, 256, 512, 768, then
-// the next chunk) and its C scales, read from the ring with one lgkmcnt wait. Written as inline
+// The lane's 8 fragment dwords (rows 8q..8q+7 of a stage, at the geometry's row offsets) and its C
+// scales, read from the ring with one lgkmcnt wait. Written as inline
 // assembly because the compiler cannot tell these reads from the ring slot that the direct copies
 // queued just before are filling, and would otherwise wait for every queued copy (vmcnt(0)) here.
 // The outputs are early-clobber: a read's destination must not be an address register of a later
 // read in the block (its data may land before that read issues).
-template <bool I8, int C>
-MX_DEV void read_stage(Stage<I8, C>& sg, uint32_t aw, uint32_t as) {
-  static_assert(kLChunk == 1056 && Stage<I8, C>::kWordsPerRow == 1, "offsets below");
-  if constexpr (C == 4) {
+template <bool I8, int CG>
+MX_DEV void read_stage(Stage<I8, LdsGeo<I8, CG>::C>& sg, uint32_t aw, uint32_t as) {
+  using G = LdsGeo<I8, CG>;
+  static_assert(Stage<I8, G::C>::kWordsPerRow == 1, "one dword per row and lane");
+  if constexpr (G::C == 4) {
     uint64_t sc;
     asm volatile(
-        "ds_read_b32 %0, %9 offset:0\n"
-        "ds_read_b32 %1, %9 offset:256\n"
-        "ds_read_b32 %2, %9 offset:512\n"
-        "ds_read_b32 %3, %9 offset:768\n"
-        "ds_read_b32 %4, %9 offset:1056\n"
-        "ds_read_b32 %5, %9 offset:1312\n"
-        "ds_read_b32 %6, %9 offset:1568\n"
-        "ds_read_b32 %7, %9 offset:1824\n"
+        "ds_read_b32 %0, %9 offset:%11\n"
+        "ds_read_b32 %1, %9 offset:%12\n"
+        "ds_read_b32 %2, %9 offset:%13\n"
+        "ds_read_b32 %3, %9 offset:%14\n"
+        "ds_read_b32 %4, %9 offset:%15\n"
+        "ds_read_b32 %5, %9 offset:%16\n"
+        "ds_read_b32 %6, %9 offset:%17\n"
+        "ds_read_b32 %7, %9 offset:%18\n"
         "ds_read_b64 %8, %10\n"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(sg.w[0][0]), "=&v"(sg.w[1][0]), "=&v"(sg.w[2][0]), "=&v"(sg.w[3][0]), "=&v"(sg.w[4][0]),
           "=&v"(sg.w[5][0]), "=&v"(sg.w[6][0]), "=&v"(sg.w[7][0]), "=&v"(sc)
-        : "v"(aw), "v"(as));
+        : "v"(aw), "v"(as), "i"(G::roff(0)), "i"(G::roff(1)), "i"(G::roff(2)), "i"(G::roff(3)), "i"(G::roff(4)),
+          "i"(G::roff(5)), "i"(G::roff(6)), "i"(G::roff(7)));
     sg.sc[0] = (uint32_t)sc;
     sg.sc[1] = (uint32_t)(sc >> 32);
   } else {
-    static_assert(C == 8, "4 or 8 columns per lane");
+    static_assert(G::C == 8, "4 or 8 columns per lane");
     typedef uint32_t u4 __attribute__((ext_vector_type(4)));
     u4 sc;
     asm volatile(
-        "ds_read_b32 %0, %9 offset:0\n"
-        "ds_read_b32 %1, %9 offset:256\n"
-        "ds_read_b32 %2, %9 offset:512\n"
-        "ds_read_b32 %3, %9 offset:768\n"
-        "ds_read_b32 %4, %9 offset:1056\n"
-        "ds_read_b32 %5, %9 offset:1312\n"
-        "ds_read_b32 %6, %9 offset:1568\n"
-        "ds_read_b32 %7, %9 offset:1824\n"
+        "ds_read_b32 %0, %9 offset:%11\n"
+        "ds_read_b32 %1, %9 offset:%12\n"
+        "ds_read_b32 %2, %9 offset:%13\n"
+        "ds_read_b32 %3, %9 offset:%14\n"
+        "ds_read_b32 %4, %9 offset:%15\n"
+        "ds_read_b32 %5, %9 offset:%16\n"
+        "ds_read_b32 %6, %9 offset:%17\n"
+        "ds_read_b32 %7, %9 offset:%18\n"
         "ds_read_b128 %8, %10\n"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(sg.w[0][0]), "=&v"(sg.w[1][0]), "=&v"(sg.w[2][0]), "=&v"(sg.w[3][0]), "=&v"(sg.w[4][0]),
           "=&v"(sg.w[5][0]), "=&v"(sg.w[6][0]), "=&v"(sg.w[7][0]), "=&v"(sc)
-        : "v"(aw), "v"(as));
+        : "v"(aw), "v"(as), "i"(G::roff(0)), "i"(G::roff(1)), "i"(G::roff(2)), "i"(G::roff(3)), "i"(G::roff(4)),
+          "i"(G::roff(5)), "i"(G::roff(6)), "i"(G::roff(7)));
     sg.sc[0] = sc[0];
     sg.sc[1] = sc[1];
     sg.sc[2] = sc[2];
@@ -636,29 +669,28 @@ MX_DEV void read_stage(Stage<I8, C>& sg, uint32_t aw, uint32_t as) {
   }
 }
 
-template <bool I8, int R>
+template <bool I8, int R, int CG>
 __global__ __launch_bounds__(512) void matvec_lds_kernel(const _Float16* __restrict__ x, const uint8_t* __restrict__ Wt,
                                                          const _Float16* __restrict__ Ws, _Float16* __restrict__ y,
                                                          float* __restrict__ part, unsigned* __restrict__ counters,
                                                          int M, int N, int K, int S) {
-  constexpr int C = I8 ? 4 : 8, TW = I8 ? 256 : 512;  // columns per lane, per strip
-  constexpr int SB = 2 * TW;                          // scale bytes of a strip row
-  constexpr int SLANES = SB / 4 / 16;                 // lanes per wave copying scales (8 or 16)
+  using G = LdsGeo<I8, CG>;
+  constexpr int C = G::C, TW = G::TW, SB = G::SB, PAR = G::PAR, STAGE = G::STAGE;
   constexpr int kLoads = 3;                           // direct copies per wave per step
-  constexpr int RS = R / 2;                           // ring slots of 2 stages (a step)
-  static_assert(R % 2 == 0 && RS >= 2 && kLoads * (RS - 2) <= 21, "wait_vm_n range");
-  static_assert(R * kLStage >= 4 * 64 * 4 * C * 4, "the parity-1 sums fit in the ring");
-  __shared__ __attribute__((aligned(16))) char ring[R * kLStage];
+  constexpr int RS = R / PAR;                         // ring slots of PAR stages (a step)
+  static_assert(R % PAR == 0 && RS >= 2 && kLoads * (RS - 2) <= 21, "wait_vm_n range");
+  static_assert(R * STAGE >= (PAR - 1) * CG * 64 * 4 * C * 4, "the other parities' sums fit in the ring");
+  __shared__ __attribute__((aligned(16))) char ring[R * STAGE];
   __shared__ __attribute__((aligned(16))) _Float16 xs[kXsLds];
   __shared__ int s_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int cg = wave & 3, par = wave >> 2;  // column group, stage parity
+  const int cg = wave % CG, par = wave / CG;  // column group, stage parity
   const int i = lane & 15, q = lane >> 4;
   const int strip = blockIdx.x, sk = blockIdx.y, nblk = K / 32;
   const int kb0 = (int)((int64_t)sk * nblk / S), kb1 = (int)((int64_t)(sk + 1) * nblk / S);
-  const int nb = kb1 - kb0, KC = 32 * nb, nsteps = (nb + 1) / 2;
+  const int nb = kb1 - kb0, KC = 32 * nb, nsteps = (nb + PAR - 1) / PAR;
   const int n0 = strip * TW, col = n0 + 16 * C * cg + C * i;
   const uint32_t row_bytes = I8 ? (uint32_t)N : (uint32_t)N / 2;
 
@@ -677,38 +709,42 @@ __global__ __launch_bounds__(512) void matvec_lds_kernel(const _Float16* __restr
     }
   }
 
-  // Copy offsets. Bytes past the end of a row (last strip) are clamped back into the row; the
-  // columns they feed are never stored. Row bytes and 2N are multiples of 16.
-  uint32_t colb = (uint32_t)strip * 256u + 16u * (uint32_t)i;
+  // Copy offsets: lane l of a chunk copy fills row l / LPR of the chunk, bytes 16 (l % LPR) of the
+  // strip row (LPR = lanes per row). Bytes past the end of a row (last strip) are clamped back into
+  // the row; the columns they feed are never stored. Row bytes and 2N are multiples of 16.
+  constexpr uint32_t LPR = G::SBYTES / 16;
+  uint32_t colb = (uint32_t)strip * G::SBYTES + 16u * ((uint32_t)lane % LPR);
   if (colb > row_bytes - 16u) colb = row_bytes - 16u;
-  const uint32_t voff0 = (4u * (2u * cg) + (uint32_t)q) * row_bytes + colb;
-  const uint32_t voff1 = voff0 + 4u * row_bytes;
-  uint32_t scb = 2u * (uint32_t)n0 + (uint32_t)cg * (SB / 4) + 16u * (uint32_t)lane;
+  const uint32_t voff0 = ((uint32_t)G::CR * (2u * cg) + (uint32_t)lane / LPR) * row_bytes + colb;
+  const uint32_t voff1 = voff0 + (uint32_t)G::CR * row_bytes;
+  uint32_t scb = 2u * (uint32_t)n0 + (uint32_t)cg * (SB / CG) + 16u * (uint32_t)lane;
   if (scb > 2u * (uint32_t)N - 16u) scb = 2u * (uint32_t)N - 16u;
 
-  // Step u: wave (cg, par) copies chunks 2cg, 2cg+1 and scale quarter cg of stage 2u+par. A stage
-  // past the split (odd block count) re-reads the split's last block, so every wave queues the
-  // same number of copies per step and the vmcnt accounting stays exact.
+  // Step u: wave (cg, par) copies chunks 2cg, 2cg+1 and scale part cg of stage PAR u + par. A
+  // stage past the split (a block count that is not a multiple of PAR) re-reads the split's last
+  // block, so every wave queues the same number of copies per step and the vmcnt accounting stays
+  // exact.
   auto issue = [&](int u) {
-    const int stage = 2 * u + par, blk = kb0 + (stage < nb ? stage : nb - 1);
-    char* st = ring + ((u % RS) * 2 + par) * kLStage;
+    const int stage = PAR * u + par, blk = kb0 + (stage < nb ? stage : nb - 1);
+    char* st = ring + ((u % RS) * PAR + par) * STAGE;
     // weights and scales are read exactly once: past the CU's L1 (sc0) and non-temporal (nt) in the
     // L2 (measured 1-3% faster than the default policy at the decode shapes)
     const rsrc_t wr = make_rsrc(Wt + (int64_t)blk * 32 * row_bytes, 32u * row_bytes);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(st + (2 * cg) * kLChunk), 16, voff0, 0, 0, 3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(st + (2 * cg + 1) * kLChunk), 16, voff1, 0, 0, 3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(st + (2 * cg) * G::LCH), 16, voff0, 0, 0, 3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(st + (2 * cg + 1) * G::LCH), 16, voff1, 0, 0, 3);
     const rsrc_t sr = make_rsrc(Ws + (int64_t)blk * N, 2u * (uint32_t)N);
-    if (lane < SLANES)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(st + 8 * kLChunk + cg * (SB / 4)), 16, scb, 0, 0, 3);
+    if (lane < G::SLANES)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_ptr_t)(st + G::NCH * G::LCH + cg * (SB / CG)), 16, scb, 0, 0,
+                                               3);
   };
 
   const int xrow = i < M ? i : M - 1;
   const _Float16* xl = xs + xrow * KC + 8 * q;
   // LDS byte addresses of the lane's fragment dword (rows 8q.. of this parity's stage in ring
   // slot 0) and of its scales
-  const uint32_t ring0 = (uint32_t)(uintptr_t)(lds_ptr_t)ring + (uint32_t)(par * kLStage);
-  const uint32_t lds_w = ring0 + (uint32_t)(2 * q * kLChunk + cg * 64 + 4 * i);
-  const uint32_t lds_s = ring0 + (uint32_t)(8 * kLChunk + 2 * (16 * C * cg + C * i));
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(lds_ptr_t)ring + (uint32_t)(par * STAGE);
+  const uint32_t lds_w = ring0 + (uint32_t)((8 * q / G::CR) * G::LCH + cg * 64 + 4 * i);
+  const uint32_t lds_s = ring0 + (uint32_t)(G::NCH * G::LCH + 2 * (16 * C * cg + C * i));
   v4f acc[C];
 #pragma unroll
   for (int j = 0; j < C; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -723,26 +759,30 @@ __global__ __launch_bounds__(512) void matvec_lds_kernel(const _Float16* __restr
     wait_lds();                 // ... and its reads of step u-1 are done
     raw_barrier();              // every wave: step u visible, slot (u-1)%RS free
     if (u + RS - 1 < nsteps) issue(u + RS - 1);
-    if (2 * u + par < nb) {
+    if (PAR * u + par < nb) {
       Stage<I8, C> sg;
-      const uint32_t so = (uint32_t)((u % RS) * 2 * kLStage);
-      read_stage<I8, C>(sg, lds_w + so, lds_s + so);
-      compute_stage<I8, C>(sg, *reinterpret_cast<const v8h*>(xl + 32 * (2 * u + par)), acc);
+      const uint32_t so = (uint32_t)((u % RS) * PAR * STAGE);
+      read_stage<I8, CG>(sg, lds_w + so, lds_s + so);
+      compute_stage<I8, C>(sg, *reinterpret_cast<const v8h*>(xl + 32 * (PAR * u + par)), acc);
     }
   }
 
-  // the two parities' sums meet in LDS (the ring is free once every wave is past its last read)
+  // the parities' sums meet in LDS (the ring is free once every wave is past its last read): parity
+  // p > 0 writes region p-1, parity 0 adds them in parity order
   wait_lds();
   raw_barrier();
   float* red = reinterpret_cast<float*>(ring) + (cg * 64 + lane) * (4 * C);
-  if (par == 1) {
+  constexpr int RSTRIDE = CG * 64 * 4 * C;  // floats per parity region
+  if (par > 0) {
 #pragma unroll
-    for (int j = 0; j < C; j++) *reinterpret_cast<v4f*>(red + 4 * j) = acc[j];
+    for (int j = 0; j < C; j++) *reinterpret_cast<v4f*>(red + (par - 1) * RSTRIDE + 4 * j) = acc[j];
   }
   __syncthreads();
   if (par == 0) {
 #pragma unroll
-    for (int j = 0; j < C; j++) acc[j] += *reinterpret_cast<const v4f*>(red + 4 * j);
+    for (int p = 1; p < PAR; p++)
+#pragma unroll
+      for (int j = 0; j < C; j++) acc[j] += *reinterpret_cast<const v4f*>(red + (p - 1) * RSTRIDE + 4 * j);
   }
 
   // acc[j][v] (parity-0 waves) = the split's y[4q+v][col+j]; rows >= M and columns >= N are
@@ -852,8 +892,13 @@ __global__ __launch_bounds__(512) void matvec_lds_kernel(const _Float16* __restr
 // workgroups) 25.3 us at M=1, with 8 columns and 2 blocks ahead 19.6 us (3 or 4 ahead: 20.1-20.2,
 // 4 columns: 22.8); int8 with 4 columns (224 workgroups of 64-byte rows) 24.3 against 24.1 us.
 constexpr int kC8 = 8, kC4 = 8, kW = 8, kP8 = 4, kP4 = 2;
-// Split kernel: an R-deep LDS ring; K is split until about kTargetWGs workgroups run.
-constexpr int kR = 8, kTargetWGs = 256;
+// Split kernel: strips of 256 bytes of every row (4 column groups) for int8 and 128 bytes (2 column
+// groups, 4 stage parities) for int4, with rings of 8 and 12 stages (4 and 3 steps); K is split
+// until about kTargetWGs workgroups run. int4 had 512-column strips (256 bytes) with 9 splits at
+// N=14336, whose last workgroup read 9 partial tiles of M x 512 floats alone: 16.5 us at M=8
+// against 14.4 us now (13.3 us at M=1 both ways). int4 rings of 16 / 20 / 24 stages measured 1-6%
+// slower than 12.
+constexpr int kCG8 = 4, kCG4 = 2, kR8 = 8, kR4 = 12, kTargetWGs = 256;
 
 // Workspace layout: a fixed counter region (one counter per column strip, room for the largest
 // strip count any shape can have), then the fp32 partials [S][M][NS * TW] (strips permuted, see the
@@ -869,7 +914,7 @@ struct SplitPlan {
 };
 
 SplitPlan split_plan(int M, int N, int K, bool int8) {
-  const int tw = int8 ? 256 : 512, nblk = K / 32;
+  const int tw = int8 ? LdsGeo<true, kCG8>::TW : LdsGeo<false, kCG4>::TW, nblk = K / 32;
   SplitPlan p;
   p.NS = (N + tw - 1) / tw;
   int S = kTargetWGs / p.NS;
@@ -898,7 +943,8 @@ int launch(int M, int N, int K, const void* x, const void* W, const void* Ws, vo
   if (sp.S > 1 && ws && ws_bytes >= sp.bytes) {
     unsigned* counters = (unsigned*)ws;
     float* part = (float*)((char*)ws + kCounterBytes);
-    hipLaunchKernelGGL((matvec_lds_kernel<I8, kR>), dim3((unsigned)sp.NS, (unsigned)sp.S), dim3(512), 0, st,
+    hipLaunchKernelGGL((matvec_lds_kernel<I8, I8 ? kR8 : kR4, I8 ? kCG8 : kCG4>), dim3((unsigned)sp.NS, (unsigned)sp.S),
+                       dim3(512), 0, st,
                        (const _Float16*)x, (const uint8_t*)W, (const _Float16*)Ws, (_Float16*)y, part, counters, M, N,
                        K, sp.S);
     return launch_status();
