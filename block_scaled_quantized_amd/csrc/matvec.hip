@@ -559,17 +559,18 @@ constexpr int kMaxSplits = 16;
 
 // ---------------------------------------------------------------------------------------------
 // Split-K kernel with LDS staging. HBM streams best when a load instruction covers long runs of
-// bytes (16 bytes per lane, 256-byte runs of 4 rows); the MFMA operand layout wants 8 rows of a
-// few adjacent columns per lane. Direct global->LDS loads decouple the two:
-//  - A workgroup (8 waves) owns a strip of 256 bytes of every row (256 int8 / 512 int4 columns)
-//    and the 32-row blocks [kb0, kb1) of its K split.
-//  - A stage is one block: 8 chunks of 4 rows x 256 bytes plus the block's scale row, copied
-//    straight into an R-stage LDS ring. Chunks are padded to 1056 bytes, so the fragment reads
-//    below hit 4 disjoint bank groups.
-//  - Waves (cg, par), cg < 4, par < 2: stages go in pairs (a step); the waves of parity par
-//    compute stage 2u+par of step u, wave cg the strip's columns [16*C*cg, 16*C*(cg+1)) (64 bytes
-//    of each row). Lane (i, q) reads the dword of rows 8q..8q+7 holding its C columns, exactly
-//    the register layout of the single-pass kernel, and the same convert / MFMA / scale code runs.
+// bytes (16 bytes per lane, whole 128-byte lines); the MFMA operand layout wants 8 rows of a few
+// adjacent columns per lane. Direct global->LDS loads decouple the two:
+//  - A workgroup (8 waves) owns a strip of 64*CG bytes of every row (int8: CG = 4, 256 columns;
+//    int4: CG = 2, 256 columns) and the 32-row blocks [kb0, kb1) of its K split.
+//  - A stage is one block: 1 KB chunks of CR rows (4 rows x 256 bytes or 8 rows x 128 bytes) plus
+//    the block's scale row, copied straight into an R-stage LDS ring. Chunks are padded (1056 or
+//    1088 bytes), so the fragment reads below hit 4 disjoint bank groups.
+//  - Waves (cg, par), cg < CG, par < PAR = 8 / CG: a step is PAR stages; the waves of parity par
+//    compute stage PAR u + par of step u, wave cg the strip's columns [16*C*cg, 16*C*(cg+1)) (64
+//    bytes of each row). Lane (i, q) reads the dword of rows 8q..8q+7 holding its C columns,
+//    exactly the register layout of the single-pass kernel, and the same convert / MFMA / scale
+//    code runs.
 //  - The activations of the split's K range sit in LDS (staged once).
 // ---------------------------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
