@@ -68,15 +68,21 @@ struct TileInfo {
 // tiles make whole rounds and its 256x256 tiles do not (E4M3, K=4096: M=2048 N=12288 92.3 against
 // 97.9 us, M=2048 N=4096 37.9 against 38.7 us, M=512 N=8192 K=8192 67.0 against 67.0 us; MXFP8
 // prefill 97.1 against 109.7-126.8 us for the ring tiles; MXFP4 4096 x 8192 x 8192 128.8 against
-// 138.7-167.5 us).
+// 138.7-167.5 us). fp16 on tile 11 (K % 512 == 0): 4096^3 109.9 against 114.3 us on the ring,
+// 2048 x 14336 x 4096 201.1 against 208.6 us, 8192^3 803 against 1199 us.
 constexpr TileInfo kTiles[] = {
     {256, 256, 4, 0, {85, 85, 90}}, {256, 224, 4, 0, {80, 75, 55}}, {128, 128, 4, 0, {50, 45, 50}},
     {64, 64, 4, 0, {25, 25, 25}},   {256, 256, 8, 1, {90, 100, 100}}, {256, 224, 8, 1, {88, 95, 60}},
     {256, 256, 8, 2, {60, 60, 99}}, {256, 224, 8, 2, {100, 95, 60}}, {256, 256, 4, 3, {200, 200, 200}},
-    {256, 224, 4, 3, {170, 160, 1}}, {256, 192, 4, 3, {170, 160, 1}}, {256, 256, 8, 4, {240, 240, 1}}};
+    {256, 224, 4, 3, {170, 160, 1}}, {256, 192, 4, 3, {170, 160, 1}}, {256, 256, 8, 4, {240, 240, 240}}};
 constexpr int kNumTiles = sizeof(kTiles) / sizeof(kTiles[0]);
 constexpr int kRingTile = 8, kRingTile224 = 9, kRingTile192 = 10, kPPRingTile = 11;
 constexpr int kCUs = 256;
+
+// Whether the ping-pong ring (tile 11) runs fp16 x fp16: K a multiple of 512 (whole pairs of 4-step
+// scale-less groups of 32 K, and at least the 16 steps of the smallest MX case), B rows (2N bytes)
+// in whole 16-byte chunks, byte offsets into B within 31 bits.
+bool pp16_ok(int N, int K) { return K % 512 == 0 && N % 8 == 0 && 2 * (int64_t)K * N < ((int64_t)1 << 31); }
 
 // Whether ring tile `tile` (8: 256x256, 9: 256x224) runs the ring kernel for this problem; the
 // fp16 ring exists for 256x256 only.
@@ -105,7 +111,7 @@ int choose_tile(int kind, int M, int N, int K) {
   double best_cost = 1e300;
   for (int t = 0; t < kNumTiles; t++) {
     if ((t == kRingTile || t == kRingTile224 || t == kRingTile192) && !ring_ok(kind, N, K, t)) continue;
-    if (t == kPPRingTile && !(kind <= 1 && K % 1024 == 0 && N % 4 == 0)) continue;
+    if (t == kPPRingTile && !((kind <= 1 && K % 1024 == 0 && N % 4 == 0) || (kind == 2 && pp16_ok(N, K)))) continue;
     const int64_t tiles = (int64_t)((M + kTiles[t].bm - 1) / kTiles[t].bm) * ((N + kTiles[t].bn - 1) / kTiles[t].bn);
     const int64_t waves = (tiles + kCUs - 1) / kCUs;
     const double cost = (double)waves * kTiles[t].bm * kTiles[t].bn * 100.0 / kTiles[t].eff[kind];
@@ -186,6 +192,11 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
   if (p->tile_id == kPPRingTile && (p->kind <= 1 || (p->kind >= 5 && p->kind <= 7) || p->kind >= 10) &&
       p->K % 1024 == 0 && p->N % 4 == 0) {
     *tile_k = p->kind == 1 ? 128 : 64;  // the 8-wave ping-pong ring
+    *variant = 4;
+    return MX_OK;
+  }
+  if (p->tile_id == kPPRingTile && p->kind == 2 && pp16_ok(p->N, p->K)) {
+    *tile_k = 32;  // fp16 on the ping-pong ring: 64-byte steps of 32 K
     *variant = 4;
     return MX_OK;
   }

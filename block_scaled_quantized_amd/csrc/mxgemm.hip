@@ -791,10 +791,12 @@ int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void
       if (kind == KIND_E4M3) return launch<KIND_E4M3, 256, 256, 4, 2>(a, stream);
       if (kind == KIND_E2M1) return launch<KIND_E2M1, 256, 256, 4, 2>(a, stream);
       return launch<KIND_F16, 256, 256, 4, 2>(a, stream);
-    case 11:  // 8-wave ping-pong ring, 256x256 (E4M3 or E2M1 here, K % 1024 == 0, N % 4 == 0); otherwise the 4-stage
-              // ring where it applies, else the 8-wave 256x256 kernel
+    case 11:  // 8-wave ping-pong ring, 256x256 (E4M3 or E2M1 here, K % 1024 == 0, N % 4 == 0; fp16: K % 512 == 0,
+              // N % 8 == 0, 2KN < 2^31); otherwise the 4-stage ring where it applies, else the 8-wave 256x256 kernel
       if ((kind == KIND_E4M3 || kind == KIND_E2M1) && K % 1024 == 0 && N % 4 == 0)
         return gemm_pp_ring_launch(kind == KIND_E4M3 ? 0 : 1, 0, 0, A, SA, B, SB, C, M, N, K, relu, false, stream);
+      if (kind == KIND_F16 && K % 512 == 0 && N % 8 == 0 && 2 * (int64_t)K * N < ((int64_t)1 << 31))
+        return gemm_pp_ring_launch(4, 0, 0, A, SA, B, SB, C, M, N, K, relu, false, stream);
       if (kind == KIND_E4M3 && K % 512 == 0 && N % 4 == 0) return gemm_ring_launch(0, 256, 0, 0, A, SA, B, SB, C, M, N, K, relu, stream);
       if (kind == KIND_F16 && K % 256 == 0 && N % 256 == 0 && 2 * (int64_t)K * N < ((int64_t)1 << 31))
         return gemm_ring_launch(4, 256, 0, 0, A, SA, B, SB, C, M, N, K, relu, stream);

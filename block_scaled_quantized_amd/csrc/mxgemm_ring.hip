@@ -1,6 +1,7 @@
 // mxgemm_ring.hip -- MX GEMMs (E8M0 scales per 32 along K) on two kernels: a 4-stage LDS ring of
 // 64-byte stage rows (every MX pair, and fp16) and, further below, an 8-wave ping-pong kernel of
-// 128-byte stage rows (the byte formats E4M3 / E5M2, E2M1 x E2M1 and the FP6 pairs, K % 1024 == 0).
+// 128-byte stage rows (the byte formats E4M3 / E5M2, E2M1 x E2M1 and the FP6 pairs, K % 1024 == 0;
+// fp16 x fp16, K % 512 == 0).
 //
 //   C[m,n] = sum_k 2^(SA[m,k/32]-127) A[m,k] * 2^(SB[n,k/32]-127) B[n,k]   (fp32 accumulate, fp16 out)
 //
@@ -676,6 +677,9 @@ __global__ __launch_bounds__(256, 1) void gemm_ring_kernel(Args p) {
 //    (the 16 rows of a quarter-wave fragment read then cover all 64 banks once). A copy instruction
 //    fills 1 KB: 8 rows x 128 bytes, lane l filling physical chunk l%8 of row l/8; wave w issues
 //    instructions w + 8k (k < 4: A rows, k >= 4: B rows) of a slot.
+//  - fp16 (KIND 4): a step is 32 K (64 bytes of an A row, two 32x32x16 fp16 K-steps) with no scale
+//    plane; B is K x N, staged per slot as 64 K-rows of the tile's 256 columns and read into MFMA
+//    fragments by transposing LDS reads (pp_read_ab16).
 //  - Two steps of a wave (pp_step2): the B rows of a slot are read in the first L phase, so they can
 //    be refilled one step earlier and get three steps to land (the A rows two); reads and copies are
 //    split evenly between the two L phases.
@@ -692,7 +696,8 @@ struct PPFmt {
     SLOT2 = 512 * 128,              // bytes of one slot: 256 A + 256 B rows of 128 bytes
     SBUF = 512 * 16                 // bytes of one scale buffer
   };
-  static_assert(KIND == 0 || KIND == 1 || KIND == 5, "ping-pong GEMM: byte pairs, E2M1 x E2M1, FP6 pairs");
+  static_assert(KIND == 0 || KIND == 1 || KIND == 4 || KIND == 5,
+                "ping-pong GEMM: byte pairs, E2M1 x E2M1, fp16 x fp16, FP6 pairs");
 };
 
 struct PPCtx {
@@ -707,6 +712,11 @@ struct PPCtx {
   // FP6: the lane's 8-byte pieces t = 0..2 of step hs of a row (bytes 48 hs + 24 h + 8 t of the row's
   // 96 data bytes), as offsets from the row's first byte (fa0 / fb0 are then row starts)
   uint32_t f6o[2][3];
+  // fp16 (KIND 4): B is K x N, N-contiguous, staged per slot as 64 K-rows of 512 bytes (the tile's
+  // 256 columns; 16-byte chunk c of K-row k at chunk c ^ 4 (k & 3)): the lane offset of its B-row
+  // copies, the bytes between the B rows of consecutive slots, and the lane's transposing-read
+  // offsets of its two B tiles in a step's 32 K-rows
+  uint32_t voff_b, bslot, bt_off[2];
   int wave, wm, wn, r32, h, nst, ngroups, nslots;
   // A given as fp16 and quantised on load: resource over the tile's fp16 A rows; this thread's row
   // rq = tid / 2 and block bq = tid % 2 of each step (64 K-elements = 2 blocks of 32) it quantises:
@@ -764,6 +774,9 @@ MX_DEV void pp_slot_copies(const PPCtx& c, char* dst, uint32_t m) {
     if constexpr (KIND == 5)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff,
                                                96u * m, 0, 1);
+    else if constexpr (KIND == 4 && HALF == 1)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff_b,
+                                               m * c.bslot, 0, 1);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff,
                                                128u * m, 0, 1);
@@ -797,7 +810,13 @@ MX_DEV void pp_mfmas(const v8i (&f)[6], const uint32_t (&sa)[4][2], const uint32
     for (int i = 0; i < 2; i++)
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        if constexpr (F::FP4) {
+        if constexpr (F::F16) {
+          const v8h bk = __builtin_bit_cast(v8h, k ? __builtin_shufflevector(f[4 + i], f[4 + i], 4, 5, 6, 7)
+                                                   : __builtin_shufflevector(f[4 + i], f[4 + i], 0, 1, 2, 3));
+          const v8h ak = __builtin_bit_cast(v8h, k ? __builtin_shufflevector(f[j], f[j], 4, 5, 6, 7)
+                                                   : __builtin_shufflevector(f[j], f[j], 0, 1, 2, 3));
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bk, ak, acc[i][j], 0, 0, 0);
+        } else if constexpr (F::FP4) {
           const v8i bk = k ? __builtin_shufflevector(f[4 + i], f[4 + i], 4, 5, 6, 7, -1, -1, -1, -1)
                            : __builtin_shufflevector(f[4 + i], f[4 + i], 0, 1, 2, 3, -1, -1, -1, -1);
           const v8i ak = k ? __builtin_shufflevector(f[j], f[j], 4, 5, 6, 7, -1, -1, -1, -1)
@@ -893,6 +912,48 @@ MX_DEV void pp_read_ab(const PPCtx& c, const char* slot, v8i (&f)[6], v8i (&yb)[
   if (YB) {
     yb[0] = cat8(r[12], r[13]);
     yb[1] = cat8(r[14], r[15]);
+  }
+}
+// fp16: A fragments are E4M3's (chunks h and h + 2 of the step: K-steps 0 and 1 of the 32x32x16
+// fp16 MFMA); a B fragment is four transposing 8-byte reads of its tile (K-rows 8h + y, + 4, + 16,
+// + 20 of the step: two K-steps of 8 rows each), the second step's rows 16384 bytes on.
+template <int OFF>
+MX_DEV void pp_read_tr4(v2i& d0, v2i& d1, v2i& d2, v2i& d3, uint32_t a) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%5\n"
+      "ds_read_b64_tr_b16 %1, %4 offset:%6\n"
+      "ds_read_b64_tr_b16 %2, %4 offset:%7\n"
+      "ds_read_b64_tr_b16 %3, %4 offset:%8"
+      : "=&v"(d0), "=&v"(d1), "=&v"(d2), "=&v"(d3)
+      : "v"(a), "i"(OFF), "i"(OFF + 2048), "i"(OFF + 8192), "i"(OFF + 10240));
+}
+MX_DEV v8i cat4x2(v2i a, v2i b, v2i c, v2i d) {
+  const v4i ab = __builtin_shufflevector(a, b, 0, 1, 2, 3), cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+  return cat8(ab, cd);
+}
+template <int HS, bool YB>
+MX_DEV void pp_read_ab16(const PPCtx& c, const char* slot, v8i (&f)[6], v8i (&yb)[2]) {
+  const uint32_t base = pp_base(slot), a = base + c.fa0, b = base + (uint32_t)BM * 128u;
+  const uint32_t b0 = b + c.bt_off[0], b1 = b + c.bt_off[1];
+  v4i r[8];
+  v2i t[4][4];
+  pp_read4<0>(r[0], r[1], r[2], r[3], a ^ (64u * HS), a ^ (64u * HS + 32u));
+  pp_read4<8192>(r[4], r[5], r[6], r[7], a ^ (64u * HS), a ^ (64u * HS + 32u));
+  pp_read_tr4<16384 * HS>(t[0][0], t[0][1], t[0][2], t[0][3], b0);
+  pp_read_tr4<16384 * HS>(t[1][0], t[1][1], t[1][2], t[1][3], b1);
+  if (YB) {
+    pp_read_tr4<16384>(t[2][0], t[2][1], t[2][2], t[2][3], b0);
+    pp_read_tr4<16384>(t[3][0], t[3][1], t[3][2], t[3][3], b1);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 4; j++) f[j] = cat8(r[2 * j], r[2 * j + 1]);
+  f[4] = cat4x2(t[0][0], t[0][1], t[0][2], t[0][3]);
+  f[5] = cat4x2(t[1][0], t[1][1], t[1][2], t[1][3]);
+  if (YB) {
+    yb[0] = cat4x2(t[2][0], t[2][1], t[2][2], t[2][3]);
+    yb[1] = cat4x2(t[3][0], t[3][1], t[3][2], t[3][3]);
   }
 }
 MX_DEV void pp_read_a(const PPCtx& c, const char* slot, v8i (&f)[6]) {
@@ -1058,7 +1119,8 @@ MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char
                      v16f (&acc)[2][4], char* asc, v4i (&ld)[4]) {
   using F = RingFmt<KIND>;
   constexpr int G = PPFmt<KIND>::G;
-  constexpr int WAIT = QA ? 12 + (S8 == 2 ? 1 : 0) + (S8 == 0 ? 1 : 0) : 4 + ((S8 + 1) % G == 1 ? 1 : 0);
+  constexpr bool SC = KIND != 4;  // a scale plane (fp16 has none)
+  constexpr int WAIT = QA ? 12 + (S8 == 2 ? 1 : 0) + (S8 == 0 ? 1 : 0) : 4 + (SC && (S8 + 1) % G == 1 ? 1 : 0);
   const int u = G * q + S8;
   v8i x[6], y[6];
   uint32_t sq[4];
@@ -1069,6 +1131,7 @@ MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char
     qa_read_scales(c, u, asc, sq);
   }
   if constexpr (KIND == 5) pp_read_ab6<0, true>(c, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
+  else if constexpr (KIND == 4) pp_read_ab16<0, true>(c, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
   else pp_read_ab<0, true>(c, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
   if constexpr (!QA) pp_slot_copies<KIND, 0>(c, slot_oth, (uint32_t)min(u / 2 + 1, c.nslots - 1));
   pp_phase_barrier();
@@ -1084,10 +1147,12 @@ MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char
   if constexpr (KIND == 5) pp_read_a6(c, slot_cur, *reinterpret_cast<v8i(*)[6]>(&y[0]));
   else pp_read_a(c, slot_cur, *reinterpret_cast<v8i(*)[6]>(&y[0]));
   pp_slot_copies<KIND, 1>(c, slot_cur, (uint32_t)min(u / 2 + 2, c.nslots - 1));
-  if (S8 + 1 == 1) pp_scale_copy(c, sb_cur, min(q + 2, c.ngroups - 1));
-  if (S8 + 1 == G - 1) {
-    if constexpr (QA) pp_read_scales_b(c, sb_nxt, nb);
-    else pp_read_scales(c, sb_nxt, na, nb);
+  if constexpr (SC) {
+    if (S8 + 1 == 1) pp_scale_copy(c, sb_cur, min(q + 2, c.ngroups - 1));
+    if (S8 + 1 == G - 1) {
+      if constexpr (QA) pp_read_scales_b(c, sb_nxt, nb);
+      else pp_read_scales(c, sb_nxt, na, nb);
+    }
   }
   if (GR == 1) wait_vm_n(WAIT);
   pp_phase_barrier();
@@ -1095,7 +1160,7 @@ MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char
   pp_mfmas<KIND, F::KSTEPS * (S8 + 1), QA, FC>(y, sa, sb, acc, sq);
   if (GR == 0) wait_vm_n(WAIT);
   pp_phase_barrier();
-  if (S8 + 1 == G - 1) {  // the next group's scales take over
+  if (SC && S8 + 1 == G - 1) {  // the next group's scales take over
     if constexpr (!QA) {
 #pragma unroll
       for (int j = 0; j < 4; j++) {
@@ -1117,7 +1182,7 @@ MX_DEV void pp_main_loop(const PPCtx& c, char* s0, char* s1, char* sb0, char* sb
   constexpr int G = PPFmt<KIND>::G;
   uint32_t sa[4][2], sb[2][2], na[4][2], nb[2][2];
   if constexpr (QA) pp_read_scales_b(c, sb0, sb);  // group 0
-  else pp_read_scales(c, sb0, sa, sb);
+  else if constexpr (KIND != 4) pp_read_scales(c, sb0, sa, sb);
   if (GR == 1) raw_barrier();  // waves 4-7 start one phase late
   // Two scale groups per iteration (the group count is even), so the slot and scale buffer of every
   // step are static and the loop body has no branch: the scheduling barriers then keep every MFMA
@@ -1167,7 +1232,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
   }
   const int m0 = tm * BM, n0 = tn * BN;
   const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
-  const uint32_t RB = F::F6 ? (uint32_t)p.K / 4u * 3u : (uint32_t)p.K / (F::FP4 ? 2 : 1);  // bytes per A / B row
+  // bytes per A / B row (fp16: per A row; B rows are K-rows of 2N bytes)
+  const uint32_t RB = F::F16 ? 2u * (uint32_t)p.K : F::F6 ? (uint32_t)p.K / 4u * 3u : (uint32_t)p.K / (F::FP4 ? 2 : 1);
   const uint32_t nblk = (uint32_t)p.K / 32;
 
   PPCtx c;
@@ -1176,7 +1242,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
   c.wn = wave >> 1;
   c.r32 = lane & 31;
   c.h = lane >> 5;
-  c.nst = p.K / (64 * F::KSTEPS);  // steps of 64 row bytes (FP6: 48)
+  c.nst = F::F16 ? p.K / 32 : p.K / (64 * F::KSTEPS);  // steps of 64 row bytes (FP6: 48)
   c.nslots = c.nst / 2;
   c.ngroups = c.nst / PF::G;
   {
@@ -1217,6 +1283,31 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
     const int nr = max(0, min(8, rows - r0));
     const uint8_t* base = (isA ? p.A + (int64_t)m0 * RB : p.B + (int64_t)n0 * RB) + (int64_t)(nr ? r0 : 0) * RB;
     c.rdata[k] = make_rsrc(base, (uint32_t)nr * RB);
+    if constexpr (F::F16) {
+      // B copy i - 32 of a slot: K-rows 2 (i - 32) and 2 (i - 32) + 1, 512 bytes from column n0; the
+      // resource runs to the end of B (columns past N read the next row or zeros: never stored)
+      if (!isA) {
+        const uint32_t RBB = 2u * (uint32_t)p.N;
+        const int64_t start = (int64_t)2 * (i - 32) * RBB + 2 * (int64_t)n0;
+        c.rdata[k] = make_rsrc(p.B + start, (uint32_t)((int64_t)p.K * RBB - start));
+      }
+    }
+  }
+  if constexpr (F::F16) {
+    // lane l of a B copy fills physical chunk l % 32 of K-row l / 32 of its pair, whose K-row & 3
+    // is 2 (wave & 1) + l / 32 (copy index and wave have the same parity): logical chunk
+    // (l % 32) ^ 4 (K-row & 3). Transposing reads: within each 16-lane group g, lane i addresses
+    // K-row 8 (g / 2) + i / 4 and columns 4 (i % 4).. of the group's 16 (tile columns 16 (g % 2)..),
+    // so lane l receives column l % 32 of the tile at K = 8 h + 0..3.
+    const uint32_t l = (uint32_t)lane, RBB = 2u * (uint32_t)p.N;
+    c.voff_b = (l >> 5) * RBB + 16u * ((l & 31u) ^ (8u * ((uint32_t)wave & 1u) + 4u * (l >> 5)));
+    c.bslot = 64u * RBB;
+    const uint32_t g16 = l >> 4, i16 = l & 15u, y = i16 >> 2;
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+      const uint32_t cc = 4u * (2u * (uint32_t)c.wn + (uint32_t)i) + 2u * (g16 & 1u) + ((i16 & 3u) >> 1);
+      c.bt_off[i] = (8u * (g16 >> 1) + y) * 512u + 16u * (cc ^ (4u * y)) + 8u * (i16 & 1u);
+    }
   }
   {  // scale copy of this wave: 64 rows, A rows 64w.. for w < 4, B rows 64(w-4).. after (QA: no A
      // scale plane; the A-row copies read from an empty resource and write unused zeros)
@@ -1253,10 +1344,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
   // queued in L_0); wait for group 0 and slot 0 (the 5 copies of group 1 and slot 1's B rows may
   // still be in flight: the first odd step waits for them). QA: steps 0 and 1 of A are quantised
   // here, and the block of step 2 loaded.
-  pp_scale_copy(c, sbuf0, 0);
+  if constexpr (!F::F16) pp_scale_copy(c, sbuf0, 0);
   if constexpr (!QA) pp_slot_copies<KIND, 0>(c, slot0, 0);
   pp_slot_copies<KIND, 1>(c, slot0, 0);
-  pp_scale_copy(c, sbuf1, min(1, c.ngroups - 1));
+  if constexpr (!F::F16) pp_scale_copy(c, sbuf1, min(1, c.ngroups - 1));
   pp_slot_copies<KIND, 1>(c, slot1, (uint32_t)min(1, c.nslots - 1));
   if constexpr (QA) {
     v4i w0[4], w1[4];
@@ -1268,7 +1359,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
     qa_load(c, min(2, c.nst - 1), ld);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the quantised steps are in LDS
   } else {
-    wait_vm_n(5);
+    wait_vm_n(F::F16 ? 4 : 5);  // slot 1's B rows (and group 1's scales) may still be in flight
   }
   raw_barrier();
   if (wave < 4) pp_main_loop<KIND, 0, QA, FC>(c, slot0, slot1, sbuf0, sbuf1, acc, asc, ld);
@@ -1438,6 +1529,8 @@ int gemm_pp_ring_launch(int kind, int fca, int fcb, const void* A, const void* S
     hipLaunchKernelGGL((gemm_pp_ring_kernel<0, false, 0x01>), grid, block, 0, stream, a);
   } else if (kind == 1) {
     hipLaunchKernelGGL((gemm_pp_ring_kernel<1, false>), grid, block, 0, stream, a);
+  } else if (kind == 4) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<4, false>), grid, block, 0, stream, a);
   } else if (kind == 5 && fc == 0x22) {
     hipLaunchKernelGGL((gemm_pp_ring_kernel<5, false, 0x22>), grid, block, 0, stream, a);
   } else if (kind == 5 && fc == 0x33) {

@@ -447,9 +447,47 @@ def test_f16_ring_exact_integers(orc):
     assert np.array_equal(C.astype(np.float64), ref)
 
 
-def test_f16_square_full_size_sampled(orc):
-    """fp16 GEMM M=N=K=4096, U(-1,1) inputs."""
+@pytest.mark.parametrize("M,N,K", [(256, 256, 512), (300, 520, 1024), (512, 1024, 512), (40, 2056, 1536),
+                                   (1024, 2048, 2048)])
+def test_f16_pp_ring(orc, M, N, K):
+    """fp16 on the ping-pong ring (tile 11 where K % 512 == 0 and N % 8 == 0): A in E4M3's byte
+    layout, B staged per slot as 64 K-rows of 512 bytes and read through transposing LDS loads. One
+    tile up to 32 (8 and more: the XCD remap), ragged M, ragged N (N % 256 != 0: the last tile's
+    extra columns are never stored), 4 to 16 groups of K; every output against the oracle."""
     api = require_gpu()
+    plan = with_tile(11, lambda: api.mxgemm_create(M, N, K, api.MX_F16, api.MX_F16))
+    assert list(api.mxgemm_plan_info(plan)) == [256, 256, 32, 4]
+    plan.close()
+    say(f"f16 pp ring M={M} N={N} K={K}")
+    A, B, C = fp16_case(orc, api, M, N, K, 900 + M + N + K, tile=11)
+    ref = orc.gemm_f16(A, B)
+    ok, ratio, bad = orc.check(C, ref, K, orc.rms_ab(A.astype(np.float64), B.astype(np.float64)))
+    assert ok, (ratio, bad)
+
+
+def test_f16_pp_ring_exact_integers_and_relu(orc):
+    """Small integer operands make every product and partial sum exact in fp32, so the fp16
+    ping-pong ring's output must equal the oracle's sum rounded to fp16 exactly (any A or B element
+    paired with the wrong K shows up); then the same with the ReLU epilogue."""
+    api = require_gpu()
+    M, N, K = 512, 776, 1024
+    say("f16 pp ring exact integers, relu")
+    A = (synth.random_ints((M, K), 0, 6, 920).astype(np.int64) - 3).astype(np.float16)
+    B = (synth.random_ints((K, N), 0, 6, 921).astype(np.int64) - 3).astype(np.float16)
+    ref = orc.gemm_f16(A, B)
+    assert np.abs(ref).max() < 2048                 # integers, exact in fp16
+    C = with_tile(11, lambda: gpu_gemm(api, api.MX_F16, dev(A), None, dev(B), None, M, N, K))
+    assert np.array_equal(C, ref)
+    Cr = with_tile(11, lambda: gpu_gemm(api, api.MX_F16, dev(A), None, dev(B), None, M, N, K, flags=api.MXGEMM_RELU))
+    assert np.array_equal(Cr, np.maximum(ref, 0.0))
+
+
+def test_f16_square_full_size_sampled(orc):
+    """fp16 GEMM M=N=K=4096, U(-1,1) inputs, on the plan's own choice (the ping-pong ring)."""
+    api = require_gpu()
+    plan = api.mxgemm_create(4096, 4096, 4096, api.MX_F16, api.MX_F16)
+    assert list(api.mxgemm_plan_info(plan)) == [256, 256, 32, 4]
+    plan.close()
     M = N = K = 4096
     say("f16 square 4096")
     A, B, C = fp16_case(orc, api, M, N, K, synth.seed_for(synth.F16_SQUARE, 0))

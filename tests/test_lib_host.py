@@ -200,17 +200,21 @@ def test_ring_tile_plan_info(monkeypatch):
     assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 224, 64, 3)
     assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 224, 128, 3)
     assert info(300, 520, 416, api.MX_E4M3) == (256, 224, 128, 1)
-    monkeypatch.setenv("MXGEMM_TILE", "11")   # the 8-wave ping-pong GEMM: E4M3 / E2M1, K % 1024 == 0
+    # the 8-wave ping-pong GEMM: E4M3 / E2M1 where K % 1024 == 0, fp16 where K % 512 == 0 and N % 8 == 0
+    monkeypatch.setenv("MXGEMM_TILE", "11")
     assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 256, 64, 4)
     assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 128, 4)
     assert info(300, 520, 512, api.MX_E4M3) == (256, 256, 64, 3)        # K % 1024: the ring
     assert info(300, 520, 1536, api.MX_E2M1) == (256, 256, 256, 1)      # nor the ring: 8 waves
-    assert info(512, 512, 512, api.MX_F16) == (256, 256, 32, 3)
+    assert info(512, 512, 512, api.MX_F16) == (256, 256, 32, 4)
+    assert info(300, 520, 1024, api.MX_F16) == (256, 256, 32, 4)        # N % 256 != 0 is fine here
+    assert info(512, 512, 256, api.MX_F16) == (256, 256, 32, 3)         # K % 512: the fp16 ring
+    assert info(512, 520, 256, api.MX_F16) == (256, 256, 64, 1)         # nor the ring: 8 waves
     monkeypatch.delenv("MXGEMM_TILE")
     assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 256, 64, 4)
     assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 128, 4)
     assert info(2048, 14336, 3584, api.MX_E4M3) == (256, 256, 64, 3)   # K % 1024 != 0: the ring
-    assert info(4096, 4096, 4096, api.MX_F16) == (256, 256, 32, 3)
+    assert info(4096, 4096, 4096, api.MX_F16) == (256, 256, 32, 4)
     # the ping-pong kernel also beats whole rounds of 256x192 ring tiles where it applies ...
     assert info(2048, 12288, 4096, api.MX_E4M3) == (256, 256, 64, 4)
     assert info(2048, 6144, 4096, api.MX_E4M3) == (256, 256, 64, 4)
