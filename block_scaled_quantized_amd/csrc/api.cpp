@@ -55,7 +55,7 @@ namespace {
 struct TileInfo {
   int bm, bn, waves, variant;  // variant: 0 = 4 waves, 1 = 8 waves, 2 = 8-wave ping-pong (MX only),
                                // 3 = 4-stage LDS ring (MX formats; fp16 on 256x256),
-                               // 4 = 8-wave ping-pong ring (E4M3, E2M1)
+                               // 4 = 8-wave ping-pong ring (E4M3, E2M1, fp16)
   int eff[3];                  // measured relative efficiency per kind (E4M3, E2M1, F16), percent
 };
 // Tile ids understood by gemm_launch. The efficiencies rank the tiles (MI355X measurements at the
