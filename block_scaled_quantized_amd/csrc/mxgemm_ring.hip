@@ -774,9 +774,9 @@ MX_DEV void pp_slot_copies(const PPCtx& c, char* dst, uint32_t m) {
     if constexpr (KIND == 5)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff,
                                                96u * m, 0, 1);
-    else if constexpr (KIND == 4 && HALF == 1)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff_b,
-                                               m * c.bslot, 0, 1);
+    else if constexpr (KIND == 4 && HALF == 1)  // (the slot's K rows in the lane offset: see the set-up)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16,
+                                               c.voff_b + m * c.bslot, 0, 0, 1);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff,
                                                128u * m, 0, 1);
@@ -1285,7 +1285,10 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
     c.rdata[k] = make_rsrc(base, (uint32_t)nr * RB);
     if constexpr (F::F16) {
       // B copy i - 32 of a slot: K-rows 2 (i - 32) and 2 (i - 32) + 1, 512 bytes from column n0; the
-      // resource runs to the end of B (columns past N read the next row or zeros: never stored)
+      // resource runs to the end of B. Columns past N (never stored) read the next row, or zeros
+      // past the end of B: the buffer range check covers the lane offset but not the scalar offset,
+      // so the slot's K-row offset goes in the lane offset (N % 8 == 0 keeps each 16-byte piece
+      // inside one row, wholly in range or wholly out)
       if (!isA) {
         const uint32_t RBB = 2u * (uint32_t)p.N;
         const int64_t start = (int64_t)2 * (i - 32) * RBB + 2 * (int64_t)n0;
