@@ -168,6 +168,32 @@ def test_validation_errors_without_gpu():
     assert lib.mx_pack_host(16, buf.ctypes.data, 1, 32, buf.ctypes.data, buf.ctypes.data) == api.MX_ERR_FORMAT
 
 
+
+def test_empty_and_oversized_shapes_rejected():
+    """Every dimension is checked before any work: 0 (an empty problem) and MX_MAX_DIM + 1 return
+    MX_ERR_SHAPE from every entry point, with no GPU needed; MX_MAX_DIM itself is accepted."""
+    lib = ctypes.CDLL(api.LIB_PATH)
+    for f in api.EXPORTS:
+        getattr(lib, f).restype = api.EXPORTS[f][0]
+        getattr(lib, f).argtypes = api.EXPORTS[f][1]
+    big = (1 << 20) + 1
+    h = ctypes.c_void_p()
+    for M, N, K in ((0, 16, 32), (16, 0, 32), (16, 16, 0), (big, 16, 32), (16, big, 32), (16, 16, big + 31)):
+        for fa in (api.MX_E4M3, api.MX_F16):
+            assert lib.mxgemm_create(ctypes.byref(h), M, N, K, fa, fa, 0) == api.MX_ERR_SHAPE, (M, N, K, fa)
+    for M, N, K in ((1 << 20, 4, 4096), (4, 1 << 20, 4096), (5, 12, 1 << 20)):
+        assert lib.mxgemm_create(ctypes.byref(h), M, N, K, api.MX_E4M3, api.MX_E4M3, 0) == api.MX_OK
+        assert lib.mxgemm_destroy(h) == 0
+    for M, N, K in ((0, 16, 32), (1, 0, 32), (1, 16, 0), (1, big - 1 + 16, 32), (1, 16, (1 << 20) + 32)):
+        assert lib.mxmatvec_run(M, N, K, 16, 16, api.MX_INT8, 16, 16, None, 0, None) == api.MX_ERR_SHAPE, (M, N, K)
+        assert api.mxmatvec_workspace_size(M, N, K, api.MX_INT8) == 0
+    buf = np.zeros(64, np.float32)
+    for rows, cols in ((0, 32), (1, 0), (big, 32), (1, big + 31)):
+        assert lib.mx_pack_run(api.MX_E4M3, 16, rows, cols, 16, 16, None) == api.MX_ERR_SHAPE, (rows, cols)
+        assert lib.mx_unpack_run(api.MX_E4M3, 16, 16, rows, cols, 16, None) == api.MX_ERR_SHAPE, (rows, cols)
+        assert lib.mx_pack_host(api.MX_E4M3, buf.ctypes.data, rows, cols, buf.ctypes.data,
+                                buf.ctypes.data) == api.MX_ERR_SHAPE, (rows, cols)
+
 def test_ring_tile_plan_info(monkeypatch):
     """Tile 8 is the 4-stage ring (64-byte K stages: 64 E4M3 or 128 E2M1 elements, 32 fp16) where
     N % 4 == 0 and K % 512 == 0 (E4M3) or K % 1024 == 0 (E2M1), or for fp16 N % 256 == 0,
@@ -210,6 +236,7 @@ def test_ring_tile_plan_info(monkeypatch):
     assert info(300, 520, 1024, api.MX_F16) == (256, 256, 32, 4)        # N % 256 != 0 is fine here
     assert info(512, 512, 256, api.MX_F16) == (256, 256, 32, 3)         # K % 512: the fp16 ring
     assert info(512, 520, 256, api.MX_F16) == (256, 256, 64, 1)         # nor the ring: 8 waves
+    assert info(256, 32768, 32768, api.MX_F16) == (256, 256, 64, 1)     # 2KN = 2^31: 8 waves
     monkeypatch.delenv("MXGEMM_TILE")
     assert info(2048, 14336, 4096, api.MX_E4M3) == (256, 256, 64, 4)
     assert info(4096, 8192, 8192, api.MX_E2M1) == (256, 256, 128, 4)
