@@ -448,12 +448,14 @@ def test_f16_ring_exact_integers(orc):
 
 
 @pytest.mark.parametrize("M,N,K", [(256, 256, 512), (300, 520, 1024), (512, 1024, 512), (40, 2056, 1536),
-                                   (1024, 2048, 2048)])
+                                   (1024, 2048, 2048), (1, 8, 512), (257, 264, 512), (64, 1000, 1024),
+                                   (33, 8, 2560)])
 def test_f16_pp_ring(orc, M, N, K):
     """fp16 on the ping-pong ring (tile 11 where K % 512 == 0 and N % 8 == 0): A in E4M3's byte
     layout, B staged per slot as 64 K-rows of 512 bytes and read through transposing LDS loads. One
-    tile up to 32 (8 and more: the XCD remap), ragged M, ragged N (N % 256 != 0: the last tile's
-    extra columns are never stored), 4 to 16 groups of K; every output against the oracle."""
+    tile up to 32 (8 and more: the XCD remap), ragged M down to a single row, ragged N down to 8
+    columns (N % 256 != 0: the last tile's extra columns read later K rows, or zeros past the end
+    of B, and are never stored), 4 to 20 groups of K; every output against the oracle."""
     api = require_gpu()
     plan = with_tile(11, lambda: api.mxgemm_create(M, N, K, api.MX_F16, api.MX_F16))
     assert list(api.mxgemm_plan_info(plan)) == [256, 256, 32, 4]
