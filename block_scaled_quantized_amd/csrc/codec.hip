@@ -4,7 +4,9 @@
 // MX pack: 8 lanes own one 32-element block (4 elements each, one 16-byte load per lane); the
 // block amax and the non-finite flag are reduced over those 8 lanes with xor shuffles; every lane
 // then encodes its 4 elements into one 32-bit (E4M3, E5M2) or 16-bit (E2M1) store. A wave covers eight
-// consecutive blocks, i.e. 1 KiB of contiguous fp32 input.
+// consecutive blocks, i.e. 1 KiB of contiguous fp32 input. E4M3 and E2M1 encode with gfx950's
+// scaled conversions, which give the rule's codes exactly (see pack_mx_kernel); E5M2 and the FP6
+// formats with the rule's integer arithmetic.
 #include "quant_rules.h"
 
 using namespace mx;
@@ -12,6 +14,7 @@ using namespace mx;
 namespace {
 
 constexpr int kThreads = 256;
+typedef short v2s16 __attribute__((ext_vector_type(2)));
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void pack_mx_kernel(const float* __restrict__ src,
@@ -42,7 +45,21 @@ __global__ __launch_bounds__(kThreads) void pack_mx_kernel(const float* __restri
       const int64_t r = blk / blocks_per_row, b = blk % blocks_per_row;
       scales[r * blocks_per_row + b] = (uint8_t)E;
     }
-    if constexpr (is_byte_fmt(FMT)) {
+    if constexpr (FMT == MX_E4M3) {
+      // gfx950's scaled conversion divides by 2^(E-127) (the scale passed as the bit pattern E << 23,
+      // which it reads as an exponent, E = 0 included) and rounds to nearest even, as the rule
+      // does; it writes NaN (S.1111.111) where the scaled value exceeds 464 instead of saturating,
+      // and those bytes become S.1111.110 (+-448). Checked on the box against the encoder below
+      // for every mantissa of every fp32 exponent that scales to 2^-40..2^8, both signs, at scale
+      // codes from 0 to 254 (fp32 subnormal inputs included): no difference.
+      const float scale = __builtin_bit_cast(float, E << 23);
+      v2s16 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((v2s16){0, 0}, x[0], x[1], scale, false);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, x[2], x[3], scale, true);
+      uint32_t w = __builtin_bit_cast(uint32_t, r);
+      const uint32_t m = w & 0x7F7F7F7Fu, nan = (m + 0x01010101u) & 0x80808080u;  // bytes S.1111.111
+      w ^= nan >> 7;                                                              // -> S.1111.110
+      reinterpret_cast<uint32_t*>(codes)[blk * 8 + sub] = nonfinite ? 0u : w;
+    } else if constexpr (is_byte_fmt(FMT)) {
       uint32_t w = 0u;
       if (!nonfinite) {
 #pragma unroll
@@ -60,12 +77,13 @@ __global__ __launch_bounds__(kThreads) void pack_mx_kernel(const float* __restri
       o[1] = (uint8_t)(w >> 8);
       o[2] = (uint8_t)(w >> 16);
     } else {
-      uint32_t w = 0u;
-      if (!nonfinite) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) w |= enc_elem_fmt(FMT, x[i], t) << (4 * i);
-      }
-      reinterpret_cast<uint16_t*>(codes)[blk * 8 + sub] = (uint16_t)w;
+      // E2M1 by the scaled conversion as for E4M3 (it saturates to +-6 itself; the same check,
+      // over scaled exponents -40..2, found no difference), two elements per byte, the first in
+      // the low nibble
+      const float scale = __builtin_bit_cast(float, E << 23);
+      uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[0], x[1], scale, 0);
+      w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], scale, 1);
+      reinterpret_cast<uint16_t*>(codes)[blk * 8 + sub] = nonfinite ? (uint16_t)0u : (uint16_t)w;
     }
   }
 }
