@@ -37,6 +37,42 @@ def edge_rows(cols, seed):
     return x.astype(np.float32)
 
 
+
+def every_scale_blocks(fmt, nblocks, seed):
+    """Blocks of 32 fp32 values: block b's first element sets the block's scale code to b % 255, or
+    to the largest code a finite fp32 amax reaches (127 - emax + 127: 246 for E4M3, emax 8; 252
+    for E2M1, emax 2). The other 31 are random bit patterns (sign, 23-bit mantissa) with
+    exponents from the amax's down 50 binades (fp32 subnormals where that reaches below 2^-126),
+    so their scaled values sweep every element grid point and the round-off between them."""
+    emax = 8 if fmt == 0 else 2
+    g = synth.rng(seed)
+    E = np.arange(nblocks) % 255
+    ex_amax = np.clip(E + emax, 0, 254)                          # biased fp32 exponent of the amax
+    ex = ex_amax[:, None] - g.integers(0, 51, size=(nblocks, 32))
+    ex[:, 0] = ex_amax
+    ex = np.clip(ex, 0, 254).astype(np.uint32)
+    man = g.integers(0, 1 << 23, size=(nblocks, 32), dtype=np.uint32)
+    man[:, 0] |= np.uint32(1 << 22) * (g.integers(0, 2, size=nblocks, dtype=np.uint32))
+    sign = g.integers(0, 2, size=(nblocks, 32), dtype=np.uint32) << np.uint32(31)
+    bits = sign | (ex << np.uint32(23)) | man
+    return bits.view(np.float32).reshape(nblocks // 64, 64 * 32)
+
+
+@pytest.mark.parametrize("fmt", [0, 4])
+def test_mx_pack_every_scale_code(orc, fmt):
+    """The E4M3 and E2M1 packs (gfx950's scaled conversions) against the oracle's quantiser on
+    blocks that set every scale code a finite fp32 block can have, bit for bit."""
+    api = require_gpu()
+    x = every_scale_blocks(fmt, 1 << 16, 3300 + fmt)
+    rows, cols = x.shape
+    say(f"mx pack every scale code fmt={fmt} {rows}x{cols}")
+    codes, scales = gpu_mx_pack(api, fmt, x)
+    oc, os_ = orc.mx_quantize(fmt, x)
+    top = 127 - (8 if fmt == 0 else 2) + 127
+    assert np.array_equal(np.unique(os_), np.arange(top + 1, dtype=np.uint8))
+    assert np.array_equal(host(scales), os_)
+    assert np.array_equal(host(codes), oc)
+
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("case", ["normal1", "normal002", "edges", "prefill_rows"])
 def test_mx_pack_unpack_bitexact(orc, fmt, case):
