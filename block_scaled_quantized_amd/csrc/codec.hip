@@ -18,7 +18,7 @@ typedef short v2s16 __attribute__((ext_vector_type(2)));
 
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void pack_mx_kernel(const float* __restrict__ src,
-                                                           int64_t nblocks, int64_t blocks_per_row,
+                                                           int64_t nblocks,
                                                            uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ scales) {
   const int sub = threadIdx.x & 7;
@@ -41,10 +41,7 @@ __global__ __launch_bounds__(kThreads) void pack_mx_kernel(const float* __restri
     }
     int t;
     const uint32_t E = mx_block_scale(amax, nonfinite != 0u, FMT, &t);
-    if (sub == 0) {
-      const int64_t r = blk / blocks_per_row, b = blk % blocks_per_row;
-      scales[r * blocks_per_row + b] = (uint8_t)E;
-    }
+    if (sub == 0) scales[blk] = (uint8_t)E;  // scales [rows][cols/32]: block blk's byte is byte blk
     if constexpr (FMT == MX_E4M3) {
       // gfx950's scaled conversion divides by 2^(E-127) (the scale passed as the bit pattern E << 23,
       // which it reads as an exponent, E = 0 included) and rounds to nearest even, as the rule
@@ -133,10 +130,11 @@ __global__ __launch_bounds__(kThreads) void pack_int_kernel(bool i8, const float
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void unpack_mx_kernel(const uint8_t* __restrict__ codes,
                                                              const uint8_t* __restrict__ scales, int64_t nquads,
-                                                             int64_t cols, float* __restrict__ out) {
+                                                             float* __restrict__ out) {
   for (int64_t qd = (int64_t)blockIdx.x * kThreads + threadIdx.x; qd < nquads; qd += (int64_t)gridDim.x * kThreads) {
-    const int64_t e0 = qd * 4, r = e0 / cols, c = e0 % cols;
-    const float s = dec_e8m0(scales[r * (cols / 32) + c / 32]);
+    // scales [rows][cols/32] with cols % 32 == 0: element e's scale is byte e / 32, so quad qd's is
+    // byte qd / 8 (no division by the row length)
+    const float s = dec_e8m0(scales[qd >> 3]);
     uint32_t w;
     if constexpr (is_byte_fmt(FMT)) w = reinterpret_cast<const uint32_t*>(codes)[qd];
     else if constexpr (is_fp6_fmt(FMT))
@@ -187,17 +185,16 @@ extern "C" int mx_pack_run(int f, const float* src, int rows, int cols, void* co
     if (int a = check_arch()) return a;
     const int64_t nblocks = (int64_t)rows * (cols / 32);
     const dim3 grid(grid_for(nblocks, kThreads / 8)), block(kThreads);
-    const int64_t bpr = cols / 32;
     if (f == MX_E4M3)
-      hipLaunchKernelGGL(pack_mx_kernel<MX_E4M3>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
+      hipLaunchKernelGGL(pack_mx_kernel<MX_E4M3>, grid, block, 0, st, src, nblocks, (uint8_t*)codes, (uint8_t*)scales);
     else if (f == MX_E5M2)
-      hipLaunchKernelGGL(pack_mx_kernel<MX_E5M2>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
+      hipLaunchKernelGGL(pack_mx_kernel<MX_E5M2>, grid, block, 0, st, src, nblocks, (uint8_t*)codes, (uint8_t*)scales);
     else if (f == MX_E2M3)
-      hipLaunchKernelGGL(pack_mx_kernel<MX_E2M3>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
+      hipLaunchKernelGGL(pack_mx_kernel<MX_E2M3>, grid, block, 0, st, src, nblocks, (uint8_t*)codes, (uint8_t*)scales);
     else if (f == MX_E3M2)
-      hipLaunchKernelGGL(pack_mx_kernel<MX_E3M2>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
+      hipLaunchKernelGGL(pack_mx_kernel<MX_E3M2>, grid, block, 0, st, src, nblocks, (uint8_t*)codes, (uint8_t*)scales);
     else
-      hipLaunchKernelGGL(pack_mx_kernel<MX_E2M1>, grid, block, 0, st, src, nblocks, bpr, (uint8_t*)codes, (uint8_t*)scales);
+      hipLaunchKernelGGL(pack_mx_kernel<MX_E2M1>, grid, block, 0, st, src, nblocks, (uint8_t*)codes, (uint8_t*)scales);
     return sync_check(launch_status(), st);
   }
   if (f == MX_INT8 || f == MX_INT4) {
@@ -224,15 +221,15 @@ extern "C" int mx_unpack_run(int f, const void* codes, const void* scales, int r
     const dim3 grid(grid_for(nquads, kThreads)), block(kThreads);
     const uint8_t *cd = (const uint8_t*)codes, *sc = (const uint8_t*)scales;
     if (f == MX_E4M3)
-      hipLaunchKernelGGL(unpack_mx_kernel<MX_E4M3>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
+      hipLaunchKernelGGL(unpack_mx_kernel<MX_E4M3>, grid, block, 0, st, cd, sc, nquads, out);
     else if (f == MX_E5M2)
-      hipLaunchKernelGGL(unpack_mx_kernel<MX_E5M2>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
+      hipLaunchKernelGGL(unpack_mx_kernel<MX_E5M2>, grid, block, 0, st, cd, sc, nquads, out);
     else if (f == MX_E2M3)
-      hipLaunchKernelGGL(unpack_mx_kernel<MX_E2M3>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
+      hipLaunchKernelGGL(unpack_mx_kernel<MX_E2M3>, grid, block, 0, st, cd, sc, nquads, out);
     else if (f == MX_E3M2)
-      hipLaunchKernelGGL(unpack_mx_kernel<MX_E3M2>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
+      hipLaunchKernelGGL(unpack_mx_kernel<MX_E3M2>, grid, block, 0, st, cd, sc, nquads, out);
     else
-      hipLaunchKernelGGL(unpack_mx_kernel<MX_E2M1>, grid, block, 0, st, cd, sc, nquads, (int64_t)cols, out);
+      hipLaunchKernelGGL(unpack_mx_kernel<MX_E2M1>, grid, block, 0, st, cd, sc, nquads, out);
     return sync_check(launch_status(), st);
   }
   if (f == MX_INT8 || f == MX_INT4) {
