@@ -19,7 +19,7 @@ MXGEMM_QUANT_A = 2  # mxgemm_create flag: A is binary16, quantised to E4M3 insid
 MX_OK, MX_ERR_NULL, MX_ERR_SHAPE, MX_ERR_ALIGN, MX_ERR_FORMAT, MX_ERR_ARCH, MX_ERR_LAUNCH, MX_ERR_NOMEM = \
     0, -1, -2, -3, -4, -5, -6, -7
 MX_ERR_SCRATCH = -8
-MXMATVEC_SCRATCH_BYTES = 8 << 20   # static scratch of mxmatvec_run_noalloc, per GPU
+MXMATVEC_SCRATCH_BYTES = 17 << 20  # static scratch of mxmatvec_run_noalloc, per GPU
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with `python -m block_scaled_quantized_amd.build`")

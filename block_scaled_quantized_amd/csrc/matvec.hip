@@ -387,27 +387,38 @@ MX_DEV void flush_pending(v4f (&acc)[MT][C], const Pending<MT>& pend) {
 }
 
 constexpr int kWqWPol = 0;  // cache policy of the weight and scale loads
-constexpr int kWqMaxSplits = 8;  // K splits of the small-M GEMM
+constexpr int kWqMaxSplits = 8;  // K splits of the small-M GEMM, and workgroups sharing a tile
 
-// With S > 1 (grid.y = S) K is split too: workgroup (tile, sk) takes the 32-row blocks
-// [sk nblk / S, (sk + 1) nblk / S), writes its fp32 partial tile to part[sk][M][N], and the last
-// workgroup of the tile to arrive adds the S partials in split order (the same protocol as the split
-// matvec below: system-coherent 16-byte stores acknowledged before a device-scope counter increment
-// on counters[tile], which the last workgroup takes from S-1 back to 0).
+// Each workgroup takes one run of 32-row blocks out of the sequence of all tiles' blocks (tile
+// after tile, K order within a tile) and walks it tile by tile:
+// - S > 1 (grid.y = S, QB = 0): K is split, workgroup (tile, sk) takes the blocks
+//   [sk nblk / S, (sk + 1) nblk / S) of its tile and writes its fp32 partial tile to
+//   part[sk][M][N].
+// - RUNS (grid.y = 1, one workgroup per CU): the sequence is dealt out in equal runs of QB
+//   blocks, workgroup w taking [w QB, (w + 1) QB), so every workgroup has the same work however the
+//   tile count falls against the CU count. A run may end inside a tile and the next run go on in
+//   it; a tile wholly inside one run is stored directly. A run ends in at most two shared tiles
+//   (its first and its last), whose fp32 partial tiles go to slots 2w and 2w + 1 of
+//   part[slot][16 MT][16 C].
+// The workgroups that share a tile (its contributors, in run order) store their partials, and the
+// last to arrive adds them in run order (the same protocol as the split matvec below:
+// system-coherent 16-byte stores acknowledged before a device-scope counter increment on
+// counters[tile], which the last workgroup takes from (contributors - 1) back to 0).
 // Waves per SIMD the compiler must allow: two workgroups per CU for the 8-wave shapes of 4 columns
 // per lane with at most 32-row tiles (the split epilogue otherwise makes it settle for one workgroup
 // and twice the registers).
 template <int C, int MT, int W>
 constexpr int wq_waves_per_eu() { return C == 4 && W == 8 && MT <= 2 ? 4 : W / 4; }
 
-template <bool I8, int C, int MT, int W, int P>
+template <bool I8, int C, int MT, int W, int P, bool RUNS>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(wq_waves_per_eu<C, MT, W>())))
 void gemm_wq_kernel(const _Float16* __restrict__ x, const uint8_t* __restrict__ Wt,
                                                          const _Float16* __restrict__ Ws, _Float16* __restrict__ y,
                                                          int M, int N, int K, float* __restrict__ part,
-                                                         unsigned* __restrict__ counters, int S) {
+                                                         unsigned* __restrict__ counters, int S, int QB) {
   constexpr int TW = 16 * C, RT = 16 * MT;  // columns and activation rows of the workgroup's tile
   __shared__ __attribute__((aligned(16))) float red[W][RT][TW];
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -422,137 +433,170 @@ void gemm_wq_kernel(const _Float16* __restrict__ x, const uint8_t* __restrict__ 
     const int xcd = bid & 7, idx = bid >> 3, qq = nwg >> 3, rr = nwg & 7;
     bid = (xcd < rr ? xcd * (qq + 1) : rr * (qq + 1) + (xcd - rr) * qq) + idx;
   }
-  const int n0 = (bid / mtiles) * TW, m0 = (bid % mtiles) * RT, col = n0 + C * i;
   const int sk = (int)blockIdx.y, nall = K / 32;
-  const int kb0 = (int)((int64_t)sk * nall / S), nblk = (int)((int64_t)(sk + 1) * nall / S) - kb0;
+  const int64_t nseq = (int64_t)mtiles * ((N + TW - 1) / TW) * nall;
+  int64_t g, gend;  // this workgroup's run [g, gend) of the block sequence
+  if (RUNS) {
+    g = (int64_t)bid * QB;
+    gend = g + QB < nseq ? g + QB : nseq;
+  } else {
+    g = (int64_t)bid * nall + (int64_t)sk * nall / S;
+    gend = (int64_t)bid * nall + (int64_t)(sk + 1) * nall / S;
+  }
 
-  // Columns as in the single-pass kernel (lanes past N load the last C columns). Activation rows
-  // come through a resource over rows m0..M-1: rows past M read as zero, their outputs are dropped.
-  const uint32_t cl = (uint32_t)(col < N ? col : N - C);
-  LaneOffsets lo;
-  lo.w = I8 ? 8u * q * (uint32_t)N + cl : (8u * q * (uint32_t)N + cl) / 2u;
-  lo.x = 2u * ((uint32_t)i * (uint32_t)K + 8u * q);
-  lo.s = 2u * cl;
-  lo.xt = 32u * (uint32_t)K;
-  const rsrc_t xr = make_rsrc(x + (int64_t)m0 * K, 2u * (uint32_t)(M - m0) * (uint32_t)K);
-
-  v4f acc[MT][C];
-#pragma unroll
-  for (int t = 0; t < MT; t++)
-#pragma unroll
-    for (int j = 0; j < C; j++) acc[t][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  Pending<MT> pend;  // nothing pending yet: zero products (adding +0 leaves the +0 accumulators)
-#pragma unroll
-  for (int t = 0; t < MT; t++) pend.d[t] = v4f{0.f, 0.f, 0.f, 0.f};
-  pend.s = 0;
-
-  // this wave's blocks: wave + W*u, u < cnt; loads run P blocks ahead through a register ring
-  const int cnt = nblk > wave ? (nblk - wave + W - 1) / W : 0;
-  auto blk = [&](int u) { return kb0 + wave + W * u; };
-  Stage<I8, C, MT> ring[P];
-  int t = 0;
-  if (cnt >= 2 * P) {
-#pragma unroll
-    for (int s = 0; s < P; s++) {
-      load_stage<I8, C, true, MT, kWqWPol>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(s), lo);
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
+  for (;;) {
+    const int tile = (int)(g / nall), kb0 = (int)(g - (int64_t)tile * nall);
+    const int64_t tbeg = (int64_t)tile * nall, tend = tbeg + nall;
+    const int nblk = (int)((gend < tend ? gend : tend) - g);
+    int first = 0, nc = S;  // the tile's first contributor and their number
+    if (RUNS) {
+      first = (int)(tbeg / QB);
+      nc = (int)((tend - 1) / QB) - first + 1;
     }
-    do {
+    const int n0 = (tile / mtiles) * TW, m0 = (tile % mtiles) * RT, col = n0 + C * i;
+
+    // Columns as in the single-pass kernel (lanes past N load the last C columns). Activation rows
+    // come through a resource over rows m0..M-1: rows past M read as zero, their outputs are dropped.
+    const uint32_t cl = (uint32_t)(col < N ? col : N - C);
+    LaneOffsets lo;
+    lo.w = I8 ? 8u * q * (uint32_t)N + cl : (8u * q * (uint32_t)N + cl) / 2u;
+    lo.x = 2u * ((uint32_t)i * (uint32_t)K + 8u * q);
+    lo.s = 2u * cl;
+    lo.xt = 32u * (uint32_t)K;
+    const rsrc_t xr = make_rsrc(x + (int64_t)m0 * K, 2u * (uint32_t)(M - m0) * (uint32_t)K);
+
+    v4f acc[MT][C];
+#pragma unroll
+    for (int t = 0; t < MT; t++)
+#pragma unroll
+      for (int j = 0; j < C; j++) acc[t][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    Pending<MT> pend;  // nothing pending yet: zero products (adding +0 leaves the +0 accumulators)
+#pragma unroll
+    for (int t = 0; t < MT; t++) pend.d[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    pend.s = 0;
+
+    // this wave's blocks: wave + W*u, u < cnt; loads run P blocks ahead through a register ring
+    const int cnt = nblk > wave ? (nblk - wave + W - 1) / W : 0;
+    auto blk = [&](int u) { return kb0 + wave + W * u; };
+    Stage<I8, C, MT> ring[P];
+    int t = 0;
+    if (cnt >= 2 * P) {
 #pragma unroll
       for (int s = 0; s < P; s++) {
-        compute_stage_mt<I8, C, MT>(ring[s], acc, pend);
-        load_stage<I8, C, true, MT, kWqWPol>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(t + s + P), lo);
+        load_stage<I8, C, true, MT, kWqWPol>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(s), lo);
         __builtin_amdgcn_sched_barrier(0);
       }
-      t += P;
-    } while (t + 2 * P <= cnt);
-  } else {
+      do {
+#pragma unroll
+        for (int s = 0; s < P; s++) {
+          compute_stage_mt<I8, C, MT>(ring[s], acc, pend);
+          load_stage<I8, C, true, MT, kWqWPol>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(t + s + P), lo);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        t += P;
+      } while (t + 2 * P <= cnt);
+    } else {
+#pragma unroll
+      for (int s = 0; s < P; s++)
+        if (s < cnt) load_stage<I8, C, true, MT, kWqWPol>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(s), lo);
+    }
+#pragma unroll
+    for (int s = 0; s < P; s++) {
+      if (t + s < cnt) {
+        compute_stage_mt<I8, C, MT>(ring[s], acc, pend);
+        if (t + s + P < cnt) load_stage<I8, C, true, MT, kWqWPol>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(t + s + P), lo);
+      }
+    }
 #pragma unroll
     for (int s = 0; s < P; s++)
-      if (s < cnt) load_stage<I8, C, true, MT, kWqWPol>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(s), lo);
-  }
-#pragma unroll
-  for (int s = 0; s < P; s++) {
-    if (t + s < cnt) {
-      compute_stage_mt<I8, C, MT>(ring[s], acc, pend);
-      if (t + s + P < cnt) load_stage<I8, C, true, MT, kWqWPol>(ring[s], Wt, xr, Ws, (uint32_t)N, blk(t + s + P), lo);
-    }
-  }
-#pragma unroll
-  for (int s = 0; s < P; s++)
-    if (t + P + s < cnt) compute_stage_mt<I8, C, MT>(ring[s], acc, pend);
+      if (t + P + s < cnt) compute_stage_mt<I8, C, MT>(ring[s], acc, pend);
 
-  flush_pending<C, MT>(acc, pend);
-  // acc[t][j][v] = this wave's share of y[m0 + 16t + 4q + v][col + j]
+    flush_pending<C, MT>(acc, pend);
+    // acc[t][j][v] = this wave's share of y[m0 + 16t + 4q + v][col + j]
 #pragma unroll
-  for (int tt = 0; tt < MT; tt++)
+    for (int tt = 0; tt < MT; tt++)
 #pragma unroll
-    for (int j = 0; j < C; j++)
+      for (int j = 0; j < C; j++)
 #pragma unroll
-      for (int v = 0; v < 4; v++) red[wave][16 * tt + 4 * q + v][C * i + j] = acc[tt][j][v];
-  __syncthreads();
-  const int rows = min(RT, M - m0);
-  if (S == 1) {
-    for (int o = threadIdx.x; o < rows * (TW / 4); o += W * 64) {
-      const int r = o / (TW / 4), c = 4 * (o % (TW / 4));
-      if (n0 + c >= N) continue;  // N % 4 == 0: a 4-column group is all in or all out
-      v4f v = *reinterpret_cast<const v4f*>(&red[0][r][c]);
+        for (int v = 0; v < 4; v++) red[wave][16 * tt + 4 * q + v][C * i + j] = acc[tt][j][v];
+    __syncthreads();
+    const int rows = min(RT, M - m0);
+    if (nc == 1) {
+      for (int o = threadIdx.x; o < rows * (TW / 4); o += W * 64) {
+        const int r = o / (TW / 4), c = 4 * (o % (TW / 4));
+        if (n0 + c >= N) continue;  // N % 4 == 0: a 4-column group is all in or all out
+        v4f v = *reinterpret_cast<const v4f*>(&red[0][r][c]);
 #pragma unroll
-      for (int w = 1; w < W; w++) v += *reinterpret_cast<const v4f*>(&red[w][r][c]);
-      v4h h;
+        for (int w = 1; w < W; w++) v += *reinterpret_cast<const v4f*>(&red[w][r][c]);
+        v4h h;
 #pragma unroll
-      for (int e = 0; e < 4; e++) h[e] = (_Float16)v[e];
-      *reinterpret_cast<v4h*>(y + (int64_t)(m0 + r) * N + n0 + c) = h;
-    }
-    return;
-  }
-  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
-  const rsrc_t pr = make_rsrc(part, (uint32_t)S * (uint32_t)M * (uint32_t)N * 4u);
-#pragma unroll 1
-  for (int o = threadIdx.x; o < rows * (TW / 4); o += W * 64) {
-    const int r = o / (TW / 4), c = 4 * (o % (TW / 4));
-    if (n0 + c >= N) continue;
-    v4f v = *reinterpret_cast<const v4f*>(&red[0][r][c]);
-#pragma unroll
-    for (int w = 1; w < W; w++) v += *reinterpret_cast<const v4f*>(&red[w][r][c]);
-    // element copies first: a bit cast of an ext-vector element read element 0
-    const float e0 = v[0], e1 = v[1], e2 = v[2], e3 = v[3];
-    const u4 val = {__builtin_bit_cast(uint32_t, e0), __builtin_bit_cast(uint32_t, e1), __builtin_bit_cast(uint32_t, e2),
-                    __builtin_bit_cast(uint32_t, e3)};
-    __builtin_amdgcn_raw_buffer_store_b128(val, pr, 4u * (uint32_t)(((sk * M) + m0 + r) * N + n0 + c), 0, 17);  // sc0 sc1
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are acknowledged
-  __syncthreads();
-  // the flag lives in red, free once every thread is past its reads above (an extra LDS variable
-  // would cost this kernel its occupancy: the compiler rounds the allocation up)
-  int* last = reinterpret_cast<int*>(&red[0][0][0]);
-  if (threadIdx.x == 0) *last = atomicInc(&counters[blockIdx.x], (unsigned)(S - 1)) == (unsigned)(S - 1);
-  __syncthreads();
-  if (!*last) return;
-#pragma unroll 1
-  for (int o = threadIdx.x; o < rows * (TW / 4); o += W * 64) {
-    const int r = o / (TW / 4), c = 4 * (o % (TW / 4));
-    if (n0 + c >= N) continue;
-    const uint32_t off = 4u * (uint32_t)((m0 + r) * N + n0 + c), sstride = 4u * (uint32_t)M * (uint32_t)N;
-    u4 v[kWqMaxSplits];
-#pragma unroll
-    for (int sp = 0; sp < kWqMaxSplits; sp++)
-      if (sp < S) v[sp] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(pr, off + sp * sstride, 0, 17));
-    float sum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int sp = 0; sp < kWqMaxSplits; sp++)
-      if (sp < S) {
-        const u4 w = v[sp];
-        const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
-        sum[0] += __builtin_bit_cast(float, w0);
-        sum[1] += __builtin_bit_cast(float, w1);
-        sum[2] += __builtin_bit_cast(float, w2);
-        sum[3] += __builtin_bit_cast(float, w3);
+        for (int e = 0; e < 4; e++) h[e] = (_Float16)v[e];
+        *reinterpret_cast<v4h*>(y + (int64_t)(m0 + r) * N + n0 + c) = h;
       }
-    v4h h;
+    } else {
+      // byte offset of element (r, c) of contributor j's partial tile
+      auto poff = [&](int j, int r, int c) -> uint32_t {
+        if (RUNS) {
+          const int w = first + j;
+          const int slot = 2 * w + ((int64_t)w * QB >= tbeg ? 0 : 1);  // the run's first or last tile
+          return 4u * (uint32_t)((slot * RT + r) * TW + c);
+        }
+        return 4u * (uint32_t)(((j * M) + m0 + r) * N + n0 + c);
+      };
+      const uint32_t pbytes = RUNS ? 8u * (uint32_t)nwg * RT * TW : 4u * (uint32_t)S * (uint32_t)M * (uint32_t)N;
+      const rsrc_t pr = make_rsrc(part, pbytes);
+      const int jc = RUNS ? bid - first : sk;
+#pragma unroll 1
+      for (int o = threadIdx.x; o < rows * (TW / 4); o += W * 64) {
+        const int r = o / (TW / 4), c = 4 * (o % (TW / 4));
+        if (n0 + c >= N) continue;
+        v4f v = *reinterpret_cast<const v4f*>(&red[0][r][c]);
 #pragma unroll
-    for (int e = 0; e < 4; e++) h[e] = (_Float16)sum[e];
-    *reinterpret_cast<v4h*>(y + (int64_t)(m0 + r) * N + n0 + c) = h;
+        for (int w = 1; w < W; w++) v += *reinterpret_cast<const v4f*>(&red[w][r][c]);
+        // element copies first: a bit cast of an ext-vector element read element 0
+        const float e0 = v[0], e1 = v[1], e2 = v[2], e3 = v[3];
+        const u4 val = {__builtin_bit_cast(uint32_t, e0), __builtin_bit_cast(uint32_t, e1),
+                        __builtin_bit_cast(uint32_t, e2), __builtin_bit_cast(uint32_t, e3)};
+        __builtin_amdgcn_raw_buffer_store_b128(val, pr, poff(jc, r, c), 0, 17);  // sc0 sc1
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are acknowledged
+      __syncthreads();
+      // the flag lives in red, free once every thread is past its reads above (an extra LDS variable
+      // would cost this kernel its occupancy: the compiler rounds the allocation up)
+      int* last = reinterpret_cast<int*>(&red[0][0][0]);
+      if (threadIdx.x == 0) *last = atomicInc(&counters[tile], (unsigned)(nc - 1)) == (unsigned)(nc - 1);
+      __syncthreads();
+      if (*last) {
+#pragma unroll 1
+        for (int o = threadIdx.x; o < rows * (TW / 4); o += W * 64) {
+          const int r = o / (TW / 4), c = 4 * (o % (TW / 4));
+          if (n0 + c >= N) continue;
+          u4 v[kWqMaxSplits];
+#pragma unroll
+          for (int sp = 0; sp < kWqMaxSplits; sp++)
+            if (sp < nc) v[sp] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(pr, poff(sp, r, c), 0, 17));
+          float sum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int sp = 0; sp < kWqMaxSplits; sp++)
+            if (sp < nc) {
+              const u4 w = v[sp];
+              const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+              sum[0] += __builtin_bit_cast(float, w0);
+              sum[1] += __builtin_bit_cast(float, w1);
+              sum[2] += __builtin_bit_cast(float, w2);
+              sum[3] += __builtin_bit_cast(float, w3);
+            }
+          v4h h;
+#pragma unroll
+          for (int e = 0; e < 4; e++) h[e] = (_Float16)sum[e];
+          *reinterpret_cast<v4h*>(y + (int64_t)(m0 + r) * N + n0 + c) = h;
+        }
+      }
+    }
+    g += nblk;
+    if (!RUNS || g >= gend) break;
+    __syncthreads();  // red, and the flag in it, are written again for the next tile
   }
 }
 
@@ -982,12 +1026,13 @@ int launch(int M, int N, int K, const void* x, const void* W, const void* Ws, vo
 // measured 2-3% slower, at 128-256 they measured 1-9% faster.
 constexpr int kWqMaxWGs = 3 * 256, kWqMinWide = 192, kWqOneRound = 256;
 
-template <bool I8, int C, int MT, int W, int P>
+template <bool I8, int C, int MT, int W, int P, bool RUNS = false>
 int launch_wq_mt(int M, int N, int K, const void* x, const void* Wt, const void* Ws, void* y, hipStream_t st,
-                 float* part = nullptr, unsigned* counters = nullptr, int S = 1) {
-  const dim3 grid((unsigned)(((N + 16 * C - 1) / (16 * C)) * ((M + 16 * MT - 1) / (16 * MT))), (unsigned)S);
-  hipLaunchKernelGGL((gemm_wq_kernel<I8, C, MT, W, P>), grid, dim3(W * 64), 0, st, (const _Float16*)x,
-                     (const uint8_t*)Wt, (const _Float16*)Ws, (_Float16*)y, M, N, K, part, counters, S);
+                 float* part = nullptr, unsigned* counters = nullptr, int S = 1, int QB = 0, int G = 0) {
+  const dim3 grid(QB > 0 ? (unsigned)G : (unsigned)(((N + 16 * C - 1) / (16 * C)) * ((M + 16 * MT - 1) / (16 * MT))),
+                  (unsigned)S);
+  hipLaunchKernelGGL((gemm_wq_kernel<I8, C, MT, W, P, RUNS>), grid, dim3(W * 64), 0, st, (const _Float16*)x,
+                     (const uint8_t*)Wt, (const _Float16*)Ws, (_Float16*)y, M, N, K, part, counters, S, QB);
   return launch_status();
 }
 
@@ -999,23 +1044,54 @@ int launch_wq_mt(int M, int N, int K, const void* x, const void* Wt, const void*
 // N=4096 19.4 -> 9.7 / 17.3 -> 8.8 us. 64-column strips with 16-, 32- or 64-row tiles measured up to
 // 12% faster at M <= 32, N=4096, but 25-40% slower at N=14336; 64-row tiles of 128 columns were slower
 // everywhere the split applies. Workspace: the counter region, then the fp32 partials [S][M][N].
+//
+// Block runs (used when a workspace is given and the launch below would run more than 256 of the
+// 64 x 128 tiles, filling less than 90% of their rounds of 256 workgroups, as the 384 tiles of
+// M=256, N=12288 do): one workgroup per CU, each taking an equal run of QB = ceil(tiles * K/32 /
+// 256) blocks of the tiles' block sequence (gemm_wq_kernel). Workspace: the counter region, then
+// two fp32 partial tiles per workgroup. Measured at K=4096 (int4 / int8, whole tiles -> runs):
+// M=256, N=12288 59.8 -> 55.4 / 67.8 -> 59.1 us. A single round that leaves CUs idle measured
+// slower with runs (M=128, N=12288, 192 tiles: 34.4 -> 37.9 / 37.5 -> 40.6 us), so it keeps whole
+// tiles.
 constexpr int kWqSplitC = 8, kWqSplitMT = 2, kWqSplitW = 8;
+constexpr int kWqRunC = 8, kWqRunMT = 4, kWqRunW = 4, kWqRunWGs = 256;
 struct WqSplit {
-  int S;
-  size_t bytes;
+  int S;         // K splits of the 32-row tiles (1: not split)
+  int QB, G;     // block runs: blocks per run and workgroups (QB = 0: no runs)
+  size_t bytes;  // workspace
 };
 
+// Whether the unsplit launch of launch_wq runs the 64 x 128 tiles (8 columns per lane, 4 row tiles).
+bool wq_wide_tiles(int M, int N) {
+  const int64_t strips4 = (N + 63) / 64, strips8 = (N + 127) / 128;
+  if (M > 32 && strips8 * ((M + 63) / 64) >= kWqMinWide) return true;
+  return strips4 * ((M + 15) / 16) > kWqMaxWGs && strips4 * ((M + 31) / 32) > kWqMaxWGs;
+}
+
 WqSplit wq_split_plan(int M, int N, int K) {
-  WqSplit w{1, 0};
+  WqSplit w{1, 0, 0, 0};
   if (M <= 8) return w;
   const int64_t tiles = (int64_t)((N + 16 * kWqSplitC - 1) / (16 * kWqSplitC)) *
                         ((M + 16 * kWqSplitMT - 1) / (16 * kWqSplitMT));
   int64_t S = kTargetWGs / tiles;
   if (S > kWqMaxSplits) S = kWqMaxSplits;
   if (S > K / 32 / 8) S = K / 32 / 8;
-  if (S < 2) return w;
-  w.S = (int)S;
-  w.bytes = kCounterBytes + ((size_t)S * M * N * 4 + 255) / 256 * 256;
+  if (S >= 2) {
+    w.S = (int)S;
+    w.bytes = kCounterBytes + ((size_t)S * M * N * 4 + 255) / 256 * 256;
+    return w;
+  }
+  if (!wq_wide_tiles(M, N)) return w;
+  const int64_t T = (int64_t)((N + 16 * kWqRunC - 1) / (16 * kWqRunC)) * ((M + 16 * kWqRunMT - 1) / (16 * kWqRunMT));
+  const int64_t rounds = (T + kWqRunWGs - 1) / kWqRunWGs, nall = K / 32;
+  if (rounds < 2 || T * 10 >= rounds * kWqRunWGs * 9 || T > (int64_t)(kCounterBytes / 4)) return w;
+  const int64_t nseq = T * nall, QB = (nseq + kWqRunWGs - 1) / kWqRunWGs;
+  if (QB < 8) return w;
+  for (int64_t t = 0; t < T; t++)  // workgroups sharing a tile: at most kWqMaxSplits
+    if (((t + 1) * nall - 1) / QB - t * nall / QB + 1 > kWqMaxSplits) return w;
+  w.QB = (int)QB;
+  w.G = (int)((nseq + QB - 1) / QB);
+  w.bytes = kCounterBytes + (size_t)w.G * 2 * (16 * kWqRunMT) * (16 * kWqRunC) * 4;
   return w;
 }
 
@@ -1023,17 +1099,18 @@ template <bool I8>
 int launch_wq(int M, int N, int K, const void* x, const void* W, const void* Ws, void* y, void* ws, size_t ws_bytes,
               hipStream_t st) {
   const WqSplit sp = wq_split_plan(M, N, K);
-  if (sp.S > 1 && ws && ws_bytes >= sp.bytes) {
+  if ((sp.S > 1 || sp.QB > 0) && ws && ws_bytes >= sp.bytes) {
     unsigned* counters = (unsigned*)ws;
     float* part = (float*)((char*)ws + kCounterBytes);
+    if (sp.QB > 0)
+      return launch_wq_mt<I8, kWqRunC, kWqRunMT, kWqRunW, 2, true>(M, N, K, x, W, Ws, y, st, part, counters, 1, sp.QB, sp.G);
     return launch_wq_mt<I8, kWqSplitC, kWqSplitMT, kWqSplitW, 2>(M, N, K, x, W, Ws, y, st, part, counters, sp.S);
   }
-  const int64_t strips4 = (N + 63) / 64, strips8 = (N + 127) / 128;
-  if (M > 32 && strips8 * ((M + 63) / 64) >= kWqMinWide) return launch_wq_mt<I8, 8, 4, 4, 2>(M, N, K, x, W, Ws, y, st);
+  const int64_t strips4 = (N + 63) / 64;
+  if (wq_wide_tiles(M, N)) return launch_wq_mt<I8, 8, 4, 4, 2>(M, N, K, x, W, Ws, y, st);
   if (strips4 * ((M + 15) / 16) <= kWqOneRound) return launch_wq_mt<I8, 4, 1, 16, 2>(M, N, K, x, W, Ws, y, st);
   if (strips4 * ((M + 15) / 16) <= kWqMaxWGs) return launch_wq_mt<I8, 4, 1, 8, 4>(M, N, K, x, W, Ws, y, st);
-  if (strips4 * ((M + 31) / 32) <= kWqMaxWGs) return launch_wq_mt<I8, 4, 2, 8, 2>(M, N, K, x, W, Ws, y, st);
-  return launch_wq_mt<I8, 8, 4, 4, 2>(M, N, K, x, W, Ws, y, st);
+  return launch_wq_mt<I8, 4, 2, 8, 2>(M, N, K, x, W, Ws, y, st);
 }
 
 // ---- the variant that allocates nothing ---------------------------------------------------------

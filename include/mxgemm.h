@@ -177,9 +177,12 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
  * that call). The fastest kernels split K across workgroups: their fp32 partial sums and one counter
  * per column strip (M <= 8) or per tile (M > 8) live in a caller-owned device buffer of
  * mxmatvec_workspace_size() bytes (16-byte aligned). For M <= 8 that is every shape with at least
- * 8 blocks of K; for M > 8 only shapes whose unsplit grid is small (fewer than 128 tiles of 32 rows
- * by 128 columns and K >= 512; mxmatvec_workspace_size returns 0 for the others, which never touch
- * the buffer).
+ * 8 blocks of K. For M > 8 it is the shapes whose unsplit grid is small (fewer than 128 tiles of 32
+ * rows by 128 columns and K >= 512: K is split), and the shapes that run more than 256 tiles of 64
+ * rows by 128 columns but fill less than 90% of their rounds of 256 workgroups (such as M=256,
+ * N=12288: the tiles' 32-row blocks are dealt out in equal runs to 256 workgroups, and the runs
+ * that share a tile add their partials). mxmatvec_workspace_size returns 0 for the other shapes,
+ * which never touch the buffer.
  *  - The buffer must be zero-filled once before its first use (hipMemset, or any zeroed
  *    allocation). Every call leaves its counters at zero again, so the buffer stays valid for any
  *    later call whose requirement it meets.
@@ -203,10 +206,11 @@ int mxmatvec_run(int M, int N, int K, const void* x, const void* W, int fw, cons
  * (a larger M has more tiles and so fewer K splits). */
 size_t mxmatvec_workspace_size(int M, int N, int K, int fw);
 
-/* Size of the library's static scratch array (8 MiB), the most workspace mxmatvec_run_noalloc can
- * use. It covers the decode shapes up to N = 14336 at K = 4096 for int8 and int4 at any M <= 8,
- * and every M > 8 shape (at most 256 splits x tiles of 32 x 128 fp32 partials: 4 MiB + 16 KiB). */
-#define MXMATVEC_SCRATCH_BYTES ((size_t)8 << 20)
+/* Size of the library's static scratch array (17 MiB), the most workspace mxmatvec_run_noalloc can
+ * use. Every valid shape fits: the requirement is 16 KiB of counters, then fp32 partials of at most
+ * 16 MiB (M <= 8: at most 16 splits x 8 rows x 128 strips of 256 columns; M > 8: at most 256 splits
+ * x tiles of 32 x 128, 4 MiB, or two 64 x 128 tiles for each of at most 256 workgroups, 16 MiB). */
+#define MXMATVEC_SCRATCH_BYTES ((size_t)17 << 20)
 
 /*
  * mxmatvec_run_noalloc -- mxmatvec_run for callers that cannot allocate (code under HIP graph
@@ -215,8 +219,8 @@ size_t mxmatvec_workspace_size(int M, int N, int K, int fw);
  * for bit, but the split kernel's workspace is a static device array inside the library
  * (MXMATVEC_SCRATCH_BYTES per GPU, held until the process ends). Nothing is allocated, by the
  * library or any library it calls.
- *  - Shapes whose workspace requirement (mxmatvec_workspace_size) exceeds MXMATVEC_SCRATCH_BYTES
- *    return MX_ERR_SCRATCH before anything is queued; use mxmatvec_run with a workspace for them.
+ *  - A shape whose workspace requirement (mxmatvec_workspace_size) exceeded MXMATVEC_SCRATCH_BYTES
+ *    would return MX_ERR_SCRATCH before anything is queued; no valid shape does (see above).
  *  - All calls on one GPU share that GPU's array, which keeps the last call's contents (its
  *    counters are back at zero after every call). Calls that overlap in time on one GPU (different
  *    streams, or a captured graph replaying beside another call) race on it and give wrong results:

@@ -168,26 +168,49 @@ def wq_splits(M, K, N):
     return S if S >= 2 else 1
 
 
+def wq_runs(M, K, N):
+    """Blocks per run where the plan deals out the blocks of the 64 x 128 tiles in equal runs to 256
+    workgroups (more than 256 tiles filling less than 90% of their rounds, runs of 8 blocks or
+    more; 0: whole tiles)."""
+    if wq_splits(M, K, N) > 1 or M <= 32:
+        return 0
+    T = -(-N // 128) * -(-M // 64)
+    rounds = -(-T // 256)
+    if T < 192 or rounds < 2 or T * 10 >= rounds * 256 * 9:
+        return 0
+    QB = -(-T * (K // 32) // 256)
+    return QB if QB >= 8 else 0
+
+
 @pytest.mark.parametrize("path", ["split", "single"])
 @pytest.mark.parametrize("fw", [32, 33])
 @pytest.mark.parametrize("M,K,N", [(9, 32, 32), (16, 1024, 1056), (31, 96, 160), (33, 4096, 64), (64, 544, 4128),
                                    (100, 256, 12288), (128, 4096, 512), (129, 160, 96), (200, 1024, 1024),
                                    (256, 2048, 320), (150, 96, 12800), (200, 64, 16384), (129, 64, 19200),
-                                   (20, 64, 25600), (144, 96, 6144), (24, 2048, 1056), (17, 512, 14336)])
+                                   (20, 64, 25600), (144, 96, 6144), (24, 2048, 1056), (17, 512, 14336),
+                                   (160, 1024, 12288), (150, 3104, 12192), (256, 1024, 16512), (40, 512, 102400)])
 def test_wq_gemm_ragged(orc, fw, M, K, N, path):
     """Every output: partial row tiles, partial column strips, one block of K up to many. Unsplit
     launch shapes: 128-column strips with 64-row tiles at M=100/N=12288, M=150/N=12800,
     M=200/N=16384 and M=129/N=19200 (the last tile with 1 row); 64-column strips with 32-row tiles at
     M=20/N=25600 and M=144/N=6144; 64-column strips with 16-row tiles for the rest. With a workspace,
     K is split 4 ways at M=16/N=1056 and M=200/N=1024, 8 ways at M=33/N=64, M=128/N=512,
-    M=256/N=320 and M=24/N=1056, and 2 ways at M=64/K=544 (17 blocks: 8 + 9) and M=17/N=14336."""
+    M=256/N=320 and M=24/N=1056, and 2 ways at M=64/K=544 (17 blocks: 8 + 9) and M=17/N=14336.
+    With a workspace, block runs over 64 x 128 tiles at M=160/N=12288 (288 tiles), M=150/N=12192/
+    K=3104 (a 22-row last row tile, a 32-column last strip, 97 blocks per tile, runs of 110),
+    M=256/N=16512 (516 tiles) and M=40/N=102400 (800 tiles of 40 rows): runs that end inside a tile,
+    tiles shared by two runs and tiles wholly inside one."""
     api = require_gpu()
-    S = wq_splits(M, K, N)
+    S, QB = wq_splits(M, K, N), wq_runs(M, K, N)
     need = api.mxmatvec_workspace_size(M, N, K, fw)
-    assert (need > 0) == (S > 1)
+    assert (need > 0) == (S > 1 or QB > 0)
     if S > 1:
         assert need == 16384 + -(-(S * M * N * 4) // 256) * 256
-    say(f"wq gemm fw={fw} M={M} K={K} N={N} path={path} splits={S if path == 'split' else 1}")
+    if QB > 0:
+        T = -(-N // 128) * -(-M // 64)
+        assert need == 16384 + -(-T * (K // 32) // QB) * 2 * 64 * 128 * 4
+    say(f"wq gemm fw={fw} M={M} K={K} N={N} path={path} splits={S if path == 'split' else 1} "
+        f"runs={QB if path == 'split' else 0}")
     x, oW, s, got, R = wq_case(orc, api, fw, M, K, N, 13 * K + N + M, 5 * K + M, path)
     ok, ratio, bad = orc.check(got, orc.matvec(fw, x, oW, s, K, N), K, R)
     assert ok, (ratio, bad)
@@ -195,11 +218,12 @@ def test_wq_gemm_ragged(orc, fw, M, K, N, path):
 
 @pytest.mark.parametrize("path", ["split", "single"])
 @pytest.mark.parametrize("fw", [32, 33])
-@pytest.mark.parametrize("M,K,N", [(128, 4096, 12288), (64, 4096, 4096)])
+@pytest.mark.parametrize("M,K,N", [(128, 4096, 12288), (64, 4096, 4096), (256, 4096, 12288)])
 def test_wq_gemm_full_size_sampled(orc, fw, M, K, N, path):
     """The W8A16 / W4A16 prefill shapes: 2048 sampled outputs (corners included) against the
     oracle's per-element formula, and every output written (y starts as NaN). M=64/N=4096 splits K
-    4 ways with a workspace; M=128/N=12288 is never split."""
+    4 ways with a workspace; M=128/N=12288 is never split; M=256/N=12288 (384 tiles) takes block
+    runs of 192 blocks with a workspace."""
     api = require_gpu()
     say(f"wq gemm full fw={fw} M={M} K={K} N={N} path={path}")
     x, oW, s, got, R = wq_case(orc, api, fw, M, K, N, synth.seed_for(synth.WQ_PREFILL, 1),

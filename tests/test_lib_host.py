@@ -323,39 +323,66 @@ def test_small_m_gemm_shape_rules():
     """9 <= M <= 256 is the small-M GEMM form, accepted up to 256 rows. With a workspace it splits K
     where 128-column strips of 32-row tiles make fewer than 128 workgroups: S = min(256 // tiles, 8,
     K // 256) splits when that is at least 2, each writing fp32 partials [S][M][N] after the
-    16384-byte counter region."""
+    16384-byte counter region. Otherwise, where the unsplit launch runs more than 256 tiles of 64 x
+    128 that fill less than 90% of their rounds of 256 workgroups, the tiles' 32-row blocks are
+    dealt out in equal runs of QB = ceil(tiles * K/32 / 256) blocks, two fp32 64 x 128 partial
+    tiles per run after the counters."""
     def split_bytes(M, N, K):
         tiles = -(-N // 128) * -(-M // 32)
         S = min(256 // tiles, 8, K // 256)
         return 0 if S < 2 else 16384 + -(-(S * M * N * 4) // 256) * 256
+
+    def run_bytes(M, N, K):
+        strips4, strips8 = -(-N // 64), -(-N // 128)
+        wide = (M > 32 and strips8 * -(-M // 64) >= 192) or strips4 * -(-M // 32) > 768
+        T, nall = strips8 * -(-M // 64), K // 32
+        rounds = -(-T // 256)
+        if not wide or rounds < 2 or T * 10 >= rounds * 256 * 9:
+            return 0
+        QB = -(-T * nall // 256)
+        if QB < 8:
+            return 0
+        return 16384 + -(-T * nall // QB) * 2 * 64 * 128 * 4
+
     for fw in (api.MX_INT8, api.MX_INT4):
         for M, N, K in ((9, 12288, 4096), (64, 12288, 4096), (128, 12288, 4096), (256, 12288, 4096),
                         (9, 4096, 4096), (64, 4096, 4096), (128, 4096, 4096), (256, 4096, 4096),
-                        (24, 14336, 4096), (64, 4096, 224), (200, 1024, 1024), (33, 64, 4096)):
-            assert api.mxmatvec_workspace_size(M, N, K, fw) == split_bytes(M, N, K), (M, N, K)
+                        (24, 14336, 4096), (64, 4096, 224), (200, 1024, 1024), (33, 64, 4096),
+                        (160, 12288, 1024), (150, 12192, 3104), (256, 16512, 1024), (256, 8192, 4096),
+                        (200, 20000 // 32 * 32, 4128), (256, 12288, 224), (40, 98304, 4096)):
+            want = split_bytes(M, N, K) or run_bytes(M, N, K)
+            assert api.mxmatvec_workspace_size(M, N, K, fw) == want, (M, N, K)
     assert api.mxmatvec_workspace_size(64, 4096, 4096, api.MX_INT8) == 16384 + 4 * 64 * 4096 * 4
-    assert api.mxmatvec_workspace_size(128, 12288, 4096, api.MX_INT4) == 0   # 384 tiles: not split
+    assert api.mxmatvec_workspace_size(128, 12288, 4096, api.MX_INT4) == 0   # 192 tiles, one round
+    assert api.mxmatvec_workspace_size(256, 8192, 4096, api.MX_INT4) == 0    # 256 tiles, one full round
+    assert api.mxmatvec_workspace_size(256, 12288, 4096, api.MX_INT4) == 16384 + 256 * 2 * 32768  # 384
     assert api.mxmatvec_workspace_size(64, 4096, 224, api.MX_INT8) == 0      # 7 blocks: not split
     assert api.mxmatvec_workspace_size(257, 4096, 4096, api.MX_INT8) == 0     # invalid shape
     assert api.mxmatvec_workspace_size(8, 4096, 4096, api.MX_INT8) > 0
 
 
-def test_noalloc_rejects_shapes_beyond_the_scratch():
-    """mxmatvec_run_noalloc refuses, before touching any device, a shape whose split workspace is
-    larger than the static scratch array; shape and pointer errors come first as for mxmatvec_run."""
-    M, N, K = 8, 32768, 16384
-    need = api.mxmatvec_workspace_size(M, N, K, api.MX_INT8)
-    assert need > api.MXMATVEC_SCRATCH_BYTES
+def test_noalloc_scratch_covers_every_shape():
+    """mxmatvec_run_noalloc keeps the workspace in a static array of MXMATVEC_SCRATCH_BYTES, which
+    every valid shape's requirement fits (the largest, 16 MiB + 16 KiB, comes from 16 splits of an
+    8-row decode over 128 strips and from 256 block runs of 64 x 128 tiles); pointer and shape
+    errors come first as for mxmatvec_run."""
+    top = 16384 + (16 << 20)
+    worst = 0
+    for fw in (api.MX_INT8, api.MX_INT4):
+        for M in (1, 2, 5, 8, 9, 17, 33, 64, 65, 128, 129, 160, 200, 255, 256):
+            for N in (32, 4096, 12288, 14336, 16512, 32736, 32768, 65536, 98304, 1 << 20):
+                for K in (512, 4096, 16384, 1 << 20):
+                    need = api.mxmatvec_workspace_size(M, N, K, fw)
+                    assert need <= top <= api.MXMATVEC_SCRATCH_BYTES, (M, N, K, fw, need)
+                    worst = max(worst, need)
+    assert worst == top
+    M, N, K = 8, 32736, 16384
+    assert api.mxmatvec_workspace_size(M, N, K, api.MX_INT4) == top
     fake = 1 << 20                                    # aligned addresses; nothing is dereferenced
-    assert api._lib.mxmatvec_run_noalloc(M, N, K, fake, fake, api.MX_INT8, fake, fake, None) == api.MX_ERR_SCRATCH
     assert api._lib.mxmatvec_run_noalloc(M, N, K, None, fake, api.MX_INT8, fake, fake, None) == api.MX_ERR_NULL
     assert api._lib.mxmatvec_run_noalloc(M, N, 48, fake, fake, api.MX_INT8, fake, fake, None) == api.MX_ERR_SHAPE
     assert api._lib.mxmatvec_run_noalloc(M, N, K, fake + 8, fake, api.MX_INT8, fake, fake, None) == api.MX_ERR_ALIGN
     assert "scratch" in api.mx_strerror(api.MX_ERR_SCRATCH)
-    # the decode workloads fit
-    for fw in (api.MX_INT8, api.MX_INT4):
-        for m in (1, 8):
-            assert 0 < api.mxmatvec_workspace_size(m, 14336, 4096, fw) <= api.MXMATVEC_SCRATCH_BYTES
 
 
 def test_quant_a_plan_rules():

@@ -50,6 +50,15 @@ def test_noalloc_small_m_gemm_split_twice(orc):
     one(orc, api, api.MX_INT4, 24, 2048, 1056, 4500)     # 9 tiles, K split 8 ways
 
 
+def test_noalloc_small_m_gemm_block_runs_twice(orc):
+    """The small-M GEMM with block runs over 64 x 128 tiles (partial tiles and counters in the
+    scratch array), then a K split on what it left: the same bits as the workspace call."""
+    api = require_gpu()
+    say("noalloc: small-M GEMM block runs, then a K split")
+    one(orc, api, api.MX_INT4, 160, 1024, 12288, 4600)   # 288 tiles, runs of 36 blocks
+    one(orc, api, api.MX_INT8, 64, 1024, 4096, 4700)     # 64 tiles, K split 4 ways
+
+
 def test_noalloc_small_m_gemm_and_single_pass(orc):
     """Shapes that need no workspace (a small-M GEMM whose K is too short to split, and a decode
     shape the split kernel does not take): same bits as mxmatvec_run."""
