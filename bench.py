@@ -484,7 +484,9 @@ def main():
     # ---------------- int8 / int4-weight GEMM with fp16 block scales at small M ----------------------
     if want("wq_gemm"):
         log("timing small-M weight-quantised GEMM")
-        for Mq, Nq, Kq in ((128, 12288, 4096), (64, 4096, 4096)):
+        # M=160 leaves a second round of 64 x 128 tiles part-filled: with a workspace its blocks are
+        # dealt out in equal runs
+        for Mq, Nq, Kq in ((128, 12288, 4096), (64, 4096, 4096), (160, 12288, 4096)):
             wq = d(synth.normal((Kq, Nq), 0.02, synth.seed_for(synth.WQ_PREFILL, 1)))
             xq = d(synth.normal((Mq, Kq), 1.0, synth.seed_for(synth.WQ_PREFILL, 0)).astype(np.float16))
             yq = torch.empty((Mq, Nq), dtype=torch.float16, device=dev)
