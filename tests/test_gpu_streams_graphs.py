@@ -76,13 +76,15 @@ def test_one_plan_two_streams(monkeypatch):
 
 
 def test_graph_capture_replays_match_eager(monkeypatch):
-    """An MXFP8 GEMM, an fp16 GEMM, the split matvec with a workspace and mxmatvec_run_noalloc,
-    captured in one graph and replayed three times, with eager calls on the same workspace and
-    scratch array between the replays: every replay equals the eager result bit for bit."""
+    """An MXFP8 GEMM, an fp16 GEMM, the split matvec with a workspace, the small-M GEMM's block runs
+    with a workspace and mxmatvec_run_noalloc, captured in one graph and replayed three times, with
+    eager calls on the same workspaces and scratch array between the replays: every replay equals
+    the eager result bit for bit."""
     monkeypatch.delenv("MX_SYNC_CHECK", raising=False)
     api = require_gpu()
     M, N, K = 512, 1024, 2048
-    say(f"graph: MXFP8 and fp16 {M}x{N}x{K}, int8 matvec 1x14336x4096, noalloc int4 8x4096x4096")
+    say(f"graph: MXFP8 and fp16 {M}x{N}x{K}, int8 matvec 1x14336x4096, int4 block runs 160x12288x1024, "
+        f"noalloc int4 8x4096x4096")
     p8 = api.mxgemm_create(M, N, K, api.MX_E4M3, api.MX_E4M3)
     ops8 = mx_operands(api, api.MX_E4M3, M, N, K, 5300)
     p16 = api.mxgemm_create(M, N, K, api.MX_F16, api.MX_F16)
@@ -91,20 +93,24 @@ def test_graph_capture_replays_match_eager(monkeypatch):
     x1, W1, Ws1 = int_operands(api, api.MX_INT8, 1, 4096, 14336, 5320)
     ws = torch.zeros(api.mxmatvec_workspace_size(1, 14336, 4096, api.MX_INT8), dtype=torch.uint8, device="cuda")
     x8, W8, Ws8 = int_operands(api, api.MX_INT4, 8, 4096, 4096, 5330)
+    xr, Wr, Wsr = int_operands(api, api.MX_INT4, 160, 1024, 12288, 5340)
+    wsr = torch.zeros(api.mxmatvec_workspace_size(160, 12288, 1024, api.MX_INT4), dtype=torch.uint8, device="cuda")
+    assert wsr.numel() > 0                                     # 288 tiles of 64 x 128: block runs
 
-    def run_all(c8, c16, y1, y8):
+    def run_all(c8, c16, y1, y8, yr):
         api.mxgemm_run(p8, *ops8, c8)
         api.mxgemm_run(p16, A16, None, B16, None, c16)
         api.mxmatvec_run(1, 14336, 4096, x1, W1, api.MX_INT8, Ws1, y1, ws)
         api.mxmatvec_run_noalloc(8, 4096, 4096, x8, W8, api.MX_INT4, Ws8, y8)
+        api.mxmatvec_run(160, 12288, 1024, xr, Wr, api.MX_INT4, Wsr, yr, wsr)
 
-    eager = [nan_f16((M, N)), nan_f16((M, N)), nan_f16((1, 14336)), nan_f16((8, 4096))]
+    eager = [nan_f16((M, N)), nan_f16((M, N)), nan_f16((1, 14336)), nan_f16((8, 4096)), nan_f16((160, 12288))]
     run_all(*eager)                                            # also the first no-alloc call (set-up)
     want = [bits(t) for t in eager]
     for t in want:
         assert not np.isnan(t.view(np.float16)).any()
 
-    outs = [nan_f16((M, N)), nan_f16((M, N)), nan_f16((1, 14336)), nan_f16((8, 4096))]
+    outs = [nan_f16((M, N)), nan_f16((M, N)), nan_f16((1, 14336)), nan_f16((8, 4096)), nan_f16((160, 12288))]
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
