@@ -696,8 +696,8 @@ struct PPFmt {
     SLOT2 = 512 * 128,              // bytes of one slot: 256 A + 256 B rows of 128 bytes
     SBUF = 512 * 16                 // bytes of one scale buffer
   };
-  static_assert(KIND == 0 || KIND == 1 || KIND == 4 || KIND == 5,
-                "ping-pong GEMM: byte pairs, E2M1 x E2M1, fp16 x fp16, FP6 pairs");
+  static_assert(KIND == 0 || KIND == 1 || KIND == 2 || KIND == 4 || KIND == 5,
+                "ping-pong GEMM: byte pairs, E2M1 x E2M1, byte A x E2M1 B, fp16 x fp16, FP6 pairs");
 };
 
 struct PPCtx {
@@ -764,7 +764,8 @@ MX_DEV v8i cat8(v4i lo, v4i hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2
 
 // The copies of slot m (its steps 2m, 2m+1: bytes 128m.. of every row; FP6: the 96 bytes 96m.. in
 // logical chunks 0..5 of the 128-byte LDS row, chunks 6 and 7 unused) into `dst`: the 4 of its A
-// rows (HALF 0) or of its B rows (HALF 1).
+// rows (HALF 0) or of its B rows (HALF 1). Byte A x E2M1 B (KIND 2): a step is 32 bytes of a B row,
+// so B rows are copied 128 bytes (steps 4m..4m+3) at a time, m then counting those 4-step pairs.
 // The loads bypass the CU's L1 (sc0): no byte is read twice by one CU (measured about 3% faster at
 // the MXFP8 prefill shape).
 template <int KIND, int HALF>
@@ -777,6 +778,9 @@ MX_DEV void pp_slot_copies(const PPCtx& c, char* dst, uint32_t m) {
     else if constexpr (KIND == 4 && HALF == 1)  // (the slot's K rows in the lane offset: see the set-up)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16,
                                                c.voff_b + m * c.bslot, 0, 0, 1);
+    else if constexpr (KIND == 2 && HALF == 1)  // E2M1 B rows (K/2 bytes): m counts 4-step pairs
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff_b,
+                                               128u * m, 0, 1);
     else
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff,
                                                128u * m, 0, 1);
@@ -913,6 +917,26 @@ MX_DEV void pp_read_ab(const PPCtx& c, const char* slot, v8i (&f)[6], v8i (&yb)[
     yb[0] = cat8(r[12], r[13]);
     yb[1] = cat8(r[14], r[15]);
   }
+}
+// Byte A x E2M1 B (KIND 2): A fragments of step 0 of the slot as pp_read_ab's; B rows hold 4 steps
+// of 32 bytes (128 bytes: a 4-step pair), and the E2M1 operand of step s is the lane's 16 bytes (its
+// K-block h: 32 nibbles) in chunk 2s + h. B tiles 0, 1 of steps S0 and S0 + 1 of the pair into f[4],
+// f[5] and yb; the upper four dwords of an E2M1 operand are not read by the MFMA.
+template <int S0>
+MX_DEV void pp_read_ab_m4(const PPCtx& c, const char* slot, const char* bbuf, v8i (&f)[6], v8i (&yb)[2]) {
+  const uint32_t a = pp_base(slot) + c.fa0, b = pp_base(bbuf) + c.fb0;
+  v4i r[8], t[4];
+  pp_read4<0>(r[0], r[1], r[2], r[3], a, a ^ 32u);
+  pp_read4<8192>(r[4], r[5], r[6], r[7], a, a ^ 32u);
+  pp_read4<0>(t[0], t[1], t[2], t[3], b ^ (32u * S0), b ^ (32u * (S0 + 1)));
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 4; j++) f[j] = cat8(r[2 * j], r[2 * j + 1]);
+  f[4] = __builtin_shufflevector(t[0], t[0], 0, 1, 2, 3, -1, -1, -1, -1);
+  f[5] = __builtin_shufflevector(t[2], t[2], 0, 1, 2, 3, -1, -1, -1, -1);
+  yb[0] = __builtin_shufflevector(t[1], t[1], 0, 1, 2, 3, -1, -1, -1, -1);
+  yb[1] = __builtin_shufflevector(t[3], t[3], 0, 1, 2, 3, -1, -1, -1, -1);
 }
 // fp16: A fragments are E4M3's (chunks h and h + 2 of the step: K-steps 0 and 1 of the 32x32x16
 // fp16 MFMA); a B fragment is four transposing 8-byte reads of its tile (K-rows 8h + y, + 4, + 16,
@@ -1116,11 +1140,16 @@ MX_DEV void pp_read_scales_b(const PPCtx& c, const char* sbuf, uint32_t (&sb)[2]
 template <int KIND, int GR, int S8, bool QA, int FC>
 MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char* sb_cur, char* sb_nxt,
                      uint32_t (&sa)[4][2], uint32_t (&sb)[2][2], uint32_t (&na)[4][2], uint32_t (&nb)[2][2],
-                     v16f (&acc)[2][4], char* asc, v4i (&ld)[4]) {
+                     v16f (&acc)[2][4], char* asc, v4i (&ld)[4], char* bb) {
   using F = RingFmt<KIND>;
   constexpr int G = PPFmt<KIND>::G;
   constexpr bool SC = KIND != 4;  // a scale plane (fp16 has none)
-  constexpr int WAIT = QA ? 12 + (S8 == 2 ? 1 : 0) + (S8 == 0 ? 1 : 0) : 4 + (SC && (S8 + 1) % G == 1 ? 1 : 0);
+  // KIND 2: the B rows of steps u..u+3 (u % 4 == 0) sit in the B half of slot (u / 4) % 2 (`bb`); they
+  // are read in L_u and L_{u+2}, and the pair two ahead is copied over them in L_{u+3}, so only steps
+  // with S8 % 4 == 2 queue B copies
+  constexpr bool M4 = KIND == 2;
+  constexpr int BCP = M4 ? (S8 % 4 == 2 ? 4 : 0) : 4;  // B copies this wave queues in L_{u+1}
+  constexpr int WAIT = QA ? 12 + (S8 == 2 ? 1 : 0) + (S8 == 0 ? 1 : 0) : BCP + (SC && (S8 + 1) % G == 1 ? 1 : 0);
   const int u = G * q + S8;
   v8i x[6], y[6];
   uint32_t sq[4];
@@ -1132,6 +1161,7 @@ MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char
   }
   if constexpr (KIND == 5) pp_read_ab6<0, true>(c, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
   else if constexpr (KIND == 4) pp_read_ab16<0, true>(c, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
+  else if constexpr (M4) pp_read_ab_m4<S8 % 4>(c, slot_cur, bb, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
   else pp_read_ab<0, true>(c, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
   if constexpr (!QA) pp_slot_copies<KIND, 0>(c, slot_oth, (uint32_t)min(u / 2 + 1, c.nslots - 1));
   pp_phase_barrier();
@@ -1146,7 +1176,11 @@ MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char
   }
   if constexpr (KIND == 5) pp_read_a6(c, slot_cur, *reinterpret_cast<v8i(*)[6]>(&y[0]));
   else pp_read_a(c, slot_cur, *reinterpret_cast<v8i(*)[6]>(&y[0]));
-  pp_slot_copies<KIND, 1>(c, slot_cur, (uint32_t)min(u / 2 + 2, c.nslots - 1));
+  if constexpr (M4) {
+    if constexpr (S8 % 4 == 2) pp_slot_copies<KIND, 1>(c, bb, (uint32_t)min(u / 4 + 2, c.nslots / 2 - 1));
+  } else {
+    pp_slot_copies<KIND, 1>(c, slot_cur, (uint32_t)min(u / 2 + 2, c.nslots - 1));
+  }
   if constexpr (SC) {
     if (S8 + 1 == 1) pp_scale_copy(c, sb_cur, min(q + 2, c.ngroups - 1));
     if (S8 + 1 == G - 1) {
@@ -1190,7 +1224,7 @@ MX_DEV void pp_main_loop(const PPCtx& c, char* s0, char* s1, char* sb0, char* sb
   for (int q = 0; q < c.ngroups; q += 2) {
 #define MX_PP(S, QQ, SC, SN)                                                                                \
   pp_step2<KIND, GR, S, QA, FC>(c, q + QQ, ((G * QQ + S) / 2) % 2 ? s1 : s0, ((G * QQ + S) / 2) % 2 ? s0 : s1, SC, SN, \
-                            sa, sb, na, nb, acc, asc, ld)
+                            sa, sb, na, nb, acc, asc, ld, ((G * QQ + S) / 4) % 2 ? s1 : s0)
     MX_PP(0, 0, sb0, sb1); MX_PP(2, 0, sb0, sb1);
     if constexpr (G == 8) { MX_PP(4, 0, sb0, sb1); MX_PP(6, 0, sb0, sb1); }
     MX_PP(0, 1, sb1, sb0); MX_PP(2, 1, sb1, sb0);
@@ -1235,6 +1269,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
   // bytes per A / B row (fp16: per A row; B rows are K-rows of 2N bytes)
   const uint32_t RB = F::F16 ? 2u * (uint32_t)p.K : F::F6 ? (uint32_t)p.K / 4u * 3u : (uint32_t)p.K / (F::FP4 ? 2 : 1);
   const uint32_t nblk = (uint32_t)p.K / 32;
+  const uint32_t RBW = KIND == 2 ? (uint32_t)p.K / 2u : RB;  // bytes per B row
 
   PPCtx c;
   c.wave = wave;
@@ -1254,6 +1289,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
     // FP6: 96 data bytes per row, logical chunks 0..5; lanes of chunks 6, 7 re-read chunk 4, 5 of the
     // same row into unused LDS bytes (the same cache lines, so no extra HBM traffic)
     c.voff = j * RB + 16u * (F::F6 && lc >= 6u ? lc - 2u : lc);
+    if constexpr (KIND == 2) c.voff_b = j * RBW + 16u * lc;
   }
   {
     // fragment chunks: row r = 128 wm + 32 j + r32 (A) or 64 wn + 32 i + r32 (B); (r >> 1) & 7 =
@@ -1281,8 +1317,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
     const bool isA = i < 32;
     const int r0 = 8 * (isA ? i : i - 32), rows = isA ? rows_a : rows_b;
     const int nr = max(0, min(8, rows - r0));
-    const uint8_t* base = (isA ? p.A + (int64_t)m0 * RB : p.B + (int64_t)n0 * RB) + (int64_t)(nr ? r0 : 0) * RB;
-    c.rdata[k] = make_rsrc(base, (uint32_t)nr * RB);
+    const uint32_t rb = isA ? RB : RBW;
+    const uint8_t* base = (isA ? p.A + (int64_t)m0 * rb : p.B + (int64_t)n0 * rb) + (int64_t)(nr ? r0 : 0) * rb;
+    c.rdata[k] = make_rsrc(base, (uint32_t)nr * rb);
     if constexpr (F::F16) {
       // B copy i - 32 of a slot: K-rows 2 (i - 32) and 2 (i - 32) + 1, 512 bytes from column n0; the
       // resource runs to the end of B. Columns past N (never stored) read the next row, or zeros
@@ -1499,8 +1536,8 @@ int gemm_ring_launch(int kind, int bn, int fca, int fcb, const void* A, const vo
 // 8-wave ping-pong ring, 256 x 256 tiles: kind 0 (E4M3 x E4M3) or 1 (E2M1 x E2M1), K % 1024 == 0
 // (an even number of scale groups), N % 4 == 0; checked by the caller.
 // qa: A is binary16 [M][K], quantised to E4M3 on load (kind 0 only; SA unused).
-// kind 0 (byte operands, fca / fcb the MFMA format codes of A / B: 0 = E4M3, 1 = E5M2), 1 (E2M1) or
-// 5 (FP6, codes 2 = E2M3, 3 = E3M2).
+// kind 0 (byte operands, fca / fcb the MFMA format codes of A / B: 0 = E4M3, 1 = E5M2), 1 (E2M1),
+// 2 (byte A, code fca, x E2M1 B, fcb = 4) or 5 (FP6, codes 2 = E2M3, 3 = E3M2).
 int gemm_pp_ring_launch(int kind, int fca, int fcb, const void* A, const void* SA, const void* B, const void* SB,
                         void* C, int M, int N, int K, bool relu, bool qa, hipStream_t stream) {
   Args a{};
@@ -1518,7 +1555,8 @@ int gemm_pp_ring_launch(int kind, int fca, int fcb, const void* A, const void* S
   const dim3 grid((unsigned)(a.tiles_m * a.tiles_n)), block(512);
   if (kind == 0 && (fca < 0 || fca > 1 || fcb < 0 || fcb > 1)) return MX_ERR_FORMAT;
   if (kind == 5 && (fca < 2 || fca > 3 || fcb < 2 || fcb > 3)) return MX_ERR_FORMAT;
-  const int fc = kind == 0 || kind == 5 ? fca | (fcb << 4) : 0;
+  if (kind == 2 && (fca < 0 || fca > 1 || fcb != 4)) return MX_ERR_FORMAT;
+  const int fc = kind == 0 || kind == 2 || kind == 5 ? fca | (fcb << 4) : 0;
   if (qa) {
     if (kind != 0 || fc != 0) return MX_ERR_FORMAT;
     hipLaunchKernelGGL((gemm_pp_ring_kernel<0, true>), grid, block, 0, stream, a);
@@ -1532,6 +1570,10 @@ int gemm_pp_ring_launch(int kind, int fca, int fcb, const void* A, const void* S
     hipLaunchKernelGGL((gemm_pp_ring_kernel<0, false, 0x01>), grid, block, 0, stream, a);
   } else if (kind == 1) {
     hipLaunchKernelGGL((gemm_pp_ring_kernel<1, false>), grid, block, 0, stream, a);
+  } else if (kind == 2 && fc == 0x40) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<2, false, 0x40>), grid, block, 0, stream, a);
+  } else if (kind == 2 && fc == 0x41) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<2, false, 0x41>), grid, block, 0, stream, a);
   } else if (kind == 4) {
     hipLaunchKernelGGL((gemm_pp_ring_kernel<4, false>), grid, block, 0, stream, a);
   } else if (kind == 5 && fc == 0x22) {
