@@ -372,6 +372,20 @@ def main():
         tf = flops / (t * 1e-3) / 1e12
         detail["mixed_e4m3_x_e2m1_gemm_2048x14336x4096"] = {"ms": t, "tflops": tf, "frac_peak": tf / PEAK["mxfp8"],
                                                             "tile": api.mxgemm_plan_info(pm)}
+        del sa, sb, msets
+        # the other order: E2M1 activations (A) with E4M3 weights (B)
+        log("timing mixed E2M1 x E4M3 GEMM")
+        sa, _, _ = mx_operands(api.MX_E2M1, M, 64, K, synth.MXFP8_PREFILL, 1.0, 1)   # A (E2M1) only
+        sb, _, _ = mx_operands(api.MX_E4M3, 64, N, K, synth.MXFP4_LARGE, 0.02, 1)    # B (E4M3) only
+        A4, SA4 = sa[0][0], sa[0][1]
+        B8, SB8 = sb[0][2], sb[0][3]
+        msets = [(A4, SA4, B8, SB8)] + [(A4.clone(), SA4.clone(), B8.clone(), SB8.clone()) for _ in range(2)]
+        pm2 = api.mxgemm_create(M, N, K, api.MX_E2M1, api.MX_E4M3)
+        t = timed(lambda i: api.mxgemm_run(pm2, *msets[i % 3], Cm[i % 3], stream), args.steps, args.warmup)
+        tf = flops / (t * 1e-3) / 1e12
+        detail["mixed_e2m1_x_e4m3_gemm_2048x14336x4096"] = {"ms": t, "tflops": tf, "frac_peak": tf / PEAK["mxfp8"],
+                                                            "tile": api.mxgemm_plan_info(pm2)}
+        api.mxgemm_destroy(pm2)
         del sa, sb, msets, Cm
 
     # ---------------- E5M2 x E5M2 at the prefill shape -------------------------------------------------

@@ -99,15 +99,12 @@ int choose_tile(int kind, int M, int N, int K) {
     // pairs other than the three plain ones run on the ring (256x224 for E4M3 / E2M1 mixes), or on
     // the ping-pong ring (tile 11) for E5M2 with E5M2 / E4M3 and the FP6 pairs
     if (t >= 0 && t < kNumTiles) {
-      if ((kind == 3 || (kind >= 5 && kind <= 8) || kind >= 10) && t == kPPRingTile) return t;
+      if (kind >= 3 && t == kPPRingTile) return t;
       return kind >= 3 ? (t == kRingTile224 && kind <= 4 ? t : kRingTile) : t;
     }
   }
-  // E5M2 with itself or E4M3, a byte A (E4M3 / E5M2) with an E2M1 B, and the FP6 pairs: the ping-pong
-  // ring where it applies; the pairs with an E2M1 A: the 4-stage ring only
-  if (kind == 3 || (kind >= 5 && kind <= 8) || kind >= 10)
-    return K % 1024 == 0 && N % 4 == 0 ? kPPRingTile : kRingTile;
-  if (kind >= 3) return kRingTile;
+  // the mixed, E5M2 and FP6 pairs: the ping-pong ring where it applies, else the 4-stage ring
+  if (kind >= 3) return K % 1024 == 0 && N % 4 == 0 ? kPPRingTile : kRingTile;
   int best = 0;
   double best_cost = 1e300;
   for (int t = 0; t < kNumTiles; t++) {
@@ -190,7 +187,7 @@ int mxgemm_plan_info(mxgemm_t p, int* tile_m, int* tile_n, int* tile_k, int* var
   *tile_m = t.bm;
   *tile_n = t.bn;
   *tile_k = p->kind == 0 ? 128 : (p->kind == 1 ? 256 : 64);  // mixed pairs: 64 (the ring's stage)
-  if (p->tile_id == kPPRingTile && (p->kind <= 1 || p->kind == 3 || (p->kind >= 5 && p->kind <= 8) || p->kind >= 10) &&
+  if (p->tile_id == kPPRingTile && p->kind != 2 &&
       p->K % 1024 == 0 && p->N % 4 == 0) {
     *tile_k = p->kind == 1 ? 128 : 64;  // the 8-wave ping-pong ring
     *variant = 4;

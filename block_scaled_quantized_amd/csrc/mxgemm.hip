@@ -722,9 +722,8 @@ int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void
   if (qa) return gemm_pp_ring_launch(0, 0, 0, A, SA, B, SB, C, M, N, K, relu, true, stream);
   // The other pairs: 3: E4M3 A x E2M1 B, 4: E2M1 A x E4M3 B (the ring, 256x256 or 256x224 tiles);
   // with E5M2: 5: E5M2 x E5M2, 6: E4M3 x E5M2, 7: E5M2 x E4M3, 8: E5M2 x E2M1, 9: E2M1 x E5M2;
-  // FP6: 10: E2M3 x E2M3, 11: E3M2 x E3M2, 12: E2M3 x E3M2, 13: E3M2 x E2M3. Kinds 3, 5-8 and 10-13
-  // run on the ping-pong ring on tile 11 where K % 1024 == 0 and N % 4 == 0; otherwise all of them on
-  // the 256x256 ring.
+  // FP6: 10: E2M3 x E2M3, 11: E3M2 x E3M2, 12: E2M3 x E3M2, 13: E3M2 x E2M3. All of them run on the
+  // ping-pong ring on tile 11 where K % 1024 == 0 and N % 4 == 0; otherwise on the 256x256 ring.
   if (kind >= 5 && kind <= 7 && tile_id == 11 && K % 1024 == 0 && N % 4 == 0) {
     static const int pfa[3] = {1, 0, 1}, pfb[3] = {1, 1, 0};
     return gemm_pp_ring_launch(0, pfa[kind - 5], pfb[kind - 5], A, SA, B, SB, C, M, N, K, relu, false, stream);
@@ -735,6 +734,8 @@ int gemm_launch(int kind, int tile_id, const void* A, const void* SA, const void
   }
   if ((kind == 3 || kind == 8) && tile_id == 11 && K % 1024 == 0 && N % 4 == 0)  // byte A x E2M1 B
     return gemm_pp_ring_launch(2, kind == 3 ? 0 : 1, 4, A, SA, B, SB, C, M, N, K, relu, false, stream);
+  if ((kind == 4 || kind == 9) && tile_id == 11 && K % 1024 == 0 && N % 4 == 0)  // E2M1 A x byte B
+    return gemm_pp_ring_launch(3, 4, kind == 4 ? 0 : 1, A, SA, B, SB, C, M, N, K, relu, false, stream);
   if (kind == 3 || kind == 4)
     return gemm_ring_launch(kind - 1, tile_id == 9 ? 224 : 256, 0, 0, A, SA, B, SB, C, M, N, K, relu, stream);
   if (kind >= 5 && kind <= 13) {

@@ -696,8 +696,8 @@ struct PPFmt {
     SLOT2 = 512 * 128,              // bytes of one slot: 256 A + 256 B rows of 128 bytes
     SBUF = 512 * 16                 // bytes of one scale buffer
   };
-  static_assert(KIND == 0 || KIND == 1 || KIND == 2 || KIND == 4 || KIND == 5,
-                "ping-pong GEMM: byte pairs, E2M1 x E2M1, byte A x E2M1 B, fp16 x fp16, FP6 pairs");
+  static_assert(KIND >= 0 && KIND <= 5,
+                "ping-pong GEMM: byte pairs, E2M1 x E2M1, byte x E2M1 mixes, fp16 x fp16, FP6 pairs");
 };
 
 struct PPCtx {
@@ -765,7 +765,8 @@ MX_DEV v8i cat8(v4i lo, v4i hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2
 // The copies of slot m (its steps 2m, 2m+1: bytes 128m.. of every row; FP6: the 96 bytes 96m.. in
 // logical chunks 0..5 of the 128-byte LDS row, chunks 6 and 7 unused) into `dst`: the 4 of its A
 // rows (HALF 0) or of its B rows (HALF 1). Byte A x E2M1 B (KIND 2): a step is 32 bytes of a B row,
-// so B rows are copied 128 bytes (steps 4m..4m+3) at a time, m then counting those 4-step pairs.
+// so B rows are copied 128 bytes (steps 4m..4m+3) at a time, m then counting those 4-step pairs; the
+// same for the A rows of E2M1 A x byte B (KIND 3).
 // The loads bypass the CU's L1 (sc0): no byte is read twice by one CU (measured about 3% faster at
 // the MXFP8 prefill shape).
 template <int KIND, int HALF>
@@ -778,7 +779,7 @@ MX_DEV void pp_slot_copies(const PPCtx& c, char* dst, uint32_t m) {
     else if constexpr (KIND == 4 && HALF == 1)  // (the slot's K rows in the lane offset: see the set-up)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16,
                                                c.voff_b + m * c.bslot, 0, 0, 1);
-    else if constexpr (KIND == 2 && HALF == 1)  // E2M1 B rows (K/2 bytes): m counts 4-step pairs
+    else if constexpr ((KIND == 2 || KIND == 3) && HALF == 1)  // B rows of a mix (KIND 2: E2M1, m counts pairs)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rdata[k], (lds_ptr_t)(dst + (c.wave + 8 * k) * 1024), 16, c.voff_b,
                                                128u * m, 0, 1);
     else
@@ -937,6 +938,43 @@ MX_DEV void pp_read_ab_m4(const PPCtx& c, const char* slot, const char* bbuf, v8
   f[5] = __builtin_shufflevector(t[2], t[2], 0, 1, 2, 3, -1, -1, -1, -1);
   yb[0] = __builtin_shufflevector(t[1], t[1], 0, 1, 2, 3, -1, -1, -1, -1);
   yb[1] = __builtin_shufflevector(t[3], t[3], 0, 1, 2, 3, -1, -1, -1, -1);
+}
+// E2M1 A x byte B (KIND 3): A rows hold 4 steps of 32 bytes; A tiles 0..3 of step S of the pair are
+// chunk 2S + h of their rows (tiles 0, 2 at a, a + 8192; tiles 1, 3 4096 bytes on).
+MX_DEV v8i widen4(v4i t) { return __builtin_shufflevector(t, t, 0, 1, 2, 3, -1, -1, -1, -1); }
+template <int S>
+MX_DEV void pp_frags_a4(const PPCtx& c, const char* abuf, v4i (&t)[4]) {
+  const uint32_t a = (pp_base(abuf) + c.fa0) ^ (32u * S);
+  pp_read4<0>(t[0], t[1], t[2], t[3], a, a + 8192u);
+}
+template <int S0>
+MX_DEV void pp_read_ab_a4(const PPCtx& c, const char* abuf, const char* slot, v8i (&f)[6], v8i (&yb)[2]) {
+  const uint32_t b = pp_base(slot) + c.fb0;
+  v4i t[4], r[8];
+  pp_frags_a4<S0>(c, abuf, t);
+  pp_read4<0>(r[0], r[1], r[2], r[3], b, b ^ 32u);
+  pp_read4<0>(r[4], r[5], r[6], r[7], b ^ 64u, b ^ 96u);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+  f[0] = widen4(t[0]);
+  f[1] = widen4(t[2]);
+  f[2] = widen4(t[1]);
+  f[3] = widen4(t[3]);
+  f[4] = cat8(r[0], r[1]);
+  f[5] = cat8(r[2], r[3]);
+  yb[0] = cat8(r[4], r[5]);
+  yb[1] = cat8(r[6], r[7]);
+}
+template <int S>
+MX_DEV void pp_read_a_a4(const PPCtx& c, const char* abuf, v8i (&f)[6]) {
+  v4i t[4];
+  pp_frags_a4<S>(c, abuf, t);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+  f[0] = widen4(t[0]);
+  f[1] = widen4(t[2]);
+  f[2] = widen4(t[1]);
+  f[3] = widen4(t[3]);
 }
 // fp16: A fragments are E4M3's (chunks h and h + 2 of the step: K-steps 0 and 1 of the 32x32x16
 // fp16 MFMA); a B fragment is four transposing 8-byte reads of its tile (K-rows 8h + y, + 4, + 16,
@@ -1140,16 +1178,22 @@ MX_DEV void pp_read_scales_b(const PPCtx& c, const char* sbuf, uint32_t (&sb)[2]
 template <int KIND, int GR, int S8, bool QA, int FC>
 MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char* sb_cur, char* sb_nxt,
                      uint32_t (&sa)[4][2], uint32_t (&sb)[2][2], uint32_t (&na)[4][2], uint32_t (&nb)[2][2],
-                     v16f (&acc)[2][4], char* asc, v4i (&ld)[4], char* bb) {
+                     v16f (&acc)[2][4], char* asc, v4i (&ld)[4], char* bb, char* bbo) {
   using F = RingFmt<KIND>;
   constexpr int G = PPFmt<KIND>::G;
   constexpr bool SC = KIND != 4;  // a scale plane (fp16 has none)
   // KIND 2: the B rows of steps u..u+3 (u % 4 == 0) sit in the B half of slot (u / 4) % 2 (`bb`); they
   // are read in L_u and L_{u+2}, and the pair two ahead is copied over them in L_{u+3}, so only steps
-  // with S8 % 4 == 2 queue B copies
-  constexpr bool M4 = KIND == 2;
+  // with S8 % 4 == 2 queue B copies.
+  // KIND 3: the A rows of steps u..u+3 sit in the A half of slot (u / 4) % 2 (`bb`), read in L_u ..
+  // L_{u+3}; the next pair is copied into the other A half (`bbo`, free since L_{u-1}) in L_u when
+  // S8 % 4 == 0. The end of a step pair then waits only for copies queued before it (the next
+  // pair's A rows have four steps to land).
+  constexpr bool M4 = KIND == 2, A4M = KIND == 3;
   constexpr int BCP = M4 ? (S8 % 4 == 2 ? 4 : 0) : 4;  // B copies this wave queues in L_{u+1}
-  constexpr int WAIT = QA ? 12 + (S8 == 2 ? 1 : 0) + (S8 == 0 ? 1 : 0) : BCP + (SC && (S8 + 1) % G == 1 ? 1 : 0);
+  constexpr int ACP = A4M ? (S8 % 4 == 0 ? 4 : 0) : 0;  // A copies that need not land in this step pair
+  constexpr int WAIT = QA ? 12 + (S8 == 2 ? 1 : 0) + (S8 == 0 ? 1 : 0)
+                          : ACP + BCP + (SC && (S8 + 1) % G == 1 ? 1 : 0);
   const int u = G * q + S8;
   v8i x[6], y[6];
   uint32_t sq[4];
@@ -1162,8 +1206,13 @@ MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char
   if constexpr (KIND == 5) pp_read_ab6<0, true>(c, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
   else if constexpr (KIND == 4) pp_read_ab16<0, true>(c, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
   else if constexpr (M4) pp_read_ab_m4<S8 % 4>(c, slot_cur, bb, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
+  else if constexpr (A4M) pp_read_ab_a4<S8 % 4>(c, bb, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
   else pp_read_ab<0, true>(c, slot_cur, x, *reinterpret_cast<v8i(*)[2]>(&y[4]));
-  if constexpr (!QA) pp_slot_copies<KIND, 0>(c, slot_oth, (uint32_t)min(u / 2 + 1, c.nslots - 1));
+  if constexpr (A4M) {
+    if constexpr (S8 % 4 == 0) pp_slot_copies<KIND, 0>(c, bbo, (uint32_t)min(u / 4 + 1, c.nslots / 2 - 1));
+  } else if constexpr (!QA) {
+    pp_slot_copies<KIND, 0>(c, slot_oth, (uint32_t)min(u / 2 + 1, c.nslots - 1));
+  }
   pp_phase_barrier();
   // ---- C_u
   pp_mfmas<KIND, F::KSTEPS * S8, QA, FC>(x, sa, sb, acc, sq);
@@ -1175,6 +1224,7 @@ MX_DEV void pp_step2(const PPCtx& c, int q, char* slot_cur, char* slot_oth, char
     qa_read_scales(c, u + 1, asc, sq);
   }
   if constexpr (KIND == 5) pp_read_a6(c, slot_cur, *reinterpret_cast<v8i(*)[6]>(&y[0]));
+  else if constexpr (A4M) pp_read_a_a4<S8 % 4 + 1>(c, bb, *reinterpret_cast<v8i(*)[6]>(&y[0]));
   else pp_read_a(c, slot_cur, *reinterpret_cast<v8i(*)[6]>(&y[0]));
   if constexpr (M4) {
     if constexpr (S8 % 4 == 2) pp_slot_copies<KIND, 1>(c, bb, (uint32_t)min(u / 4 + 2, c.nslots / 2 - 1));
@@ -1224,7 +1274,8 @@ MX_DEV void pp_main_loop(const PPCtx& c, char* s0, char* s1, char* sb0, char* sb
   for (int q = 0; q < c.ngroups; q += 2) {
 #define MX_PP(S, QQ, SC, SN)                                                                                \
   pp_step2<KIND, GR, S, QA, FC>(c, q + QQ, ((G * QQ + S) / 2) % 2 ? s1 : s0, ((G * QQ + S) / 2) % 2 ? s0 : s1, SC, SN, \
-                            sa, sb, na, nb, acc, asc, ld, ((G * QQ + S) / 4) % 2 ? s1 : s0)
+                            sa, sb, na, nb, acc, asc, ld, ((G * QQ + S) / 4) % 2 ? s1 : s0, \
+                            ((G * QQ + S) / 4) % 2 ? s0 : s1)
     MX_PP(0, 0, sb0, sb1); MX_PP(2, 0, sb0, sb1);
     if constexpr (G == 8) { MX_PP(4, 0, sb0, sb1); MX_PP(6, 0, sb0, sb1); }
     MX_PP(0, 1, sb1, sb0); MX_PP(2, 1, sb1, sb0);
@@ -1267,9 +1318,11 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const int rows_a = min(BM, p.M - m0), rows_b = min(BN, p.N - n0);
   // bytes per A / B row (fp16: per A row; B rows are K-rows of 2N bytes)
-  const uint32_t RB = F::F16 ? 2u * (uint32_t)p.K : F::F6 ? (uint32_t)p.K / 4u * 3u : (uint32_t)p.K / (F::FP4 ? 2 : 1);
+  const uint32_t RB = F::F16 ? 2u * (uint32_t)p.K
+                     : F::F6   ? (uint32_t)p.K / 4u * 3u
+                               : (uint32_t)p.K / (F::FP4 || KIND == 3 ? 2 : 1);
   const uint32_t nblk = (uint32_t)p.K / 32;
-  const uint32_t RBW = KIND == 2 ? (uint32_t)p.K / 2u : RB;  // bytes per B row
+  const uint32_t RBW = KIND == 2 ? (uint32_t)p.K / 2u : KIND == 3 ? (uint32_t)p.K : RB;  // bytes per B row
 
   PPCtx c;
   c.wave = wave;
@@ -1289,7 +1342,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_ring_kernel(Args p) {
     // FP6: 96 data bytes per row, logical chunks 0..5; lanes of chunks 6, 7 re-read chunk 4, 5 of the
     // same row into unused LDS bytes (the same cache lines, so no extra HBM traffic)
     c.voff = j * RB + 16u * (F::F6 && lc >= 6u ? lc - 2u : lc);
-    if constexpr (KIND == 2) c.voff_b = j * RBW + 16u * lc;
+    if constexpr (KIND == 2 || KIND == 3) c.voff_b = j * RBW + 16u * lc;
   }
   {
     // fragment chunks: row r = 128 wm + 32 j + r32 (A) or 64 wn + 32 i + r32 (B); (r >> 1) & 7 =
@@ -1537,7 +1590,8 @@ int gemm_ring_launch(int kind, int bn, int fca, int fcb, const void* A, const vo
 // (an even number of scale groups), N % 4 == 0; checked by the caller.
 // qa: A is binary16 [M][K], quantised to E4M3 on load (kind 0 only; SA unused).
 // kind 0 (byte operands, fca / fcb the MFMA format codes of A / B: 0 = E4M3, 1 = E5M2), 1 (E2M1),
-// 2 (byte A, code fca, x E2M1 B, fcb = 4) or 5 (FP6, codes 2 = E2M3, 3 = E3M2).
+// 2 (byte A, code fca, x E2M1 B, fcb = 4), 3 (E2M1 A, fca = 4, x byte B, code fcb) or 5 (FP6, codes
+// 2 = E2M3, 3 = E3M2).
 int gemm_pp_ring_launch(int kind, int fca, int fcb, const void* A, const void* SA, const void* B, const void* SB,
                         void* C, int M, int N, int K, bool relu, bool qa, hipStream_t stream) {
   Args a{};
@@ -1556,7 +1610,8 @@ int gemm_pp_ring_launch(int kind, int fca, int fcb, const void* A, const void* S
   if (kind == 0 && (fca < 0 || fca > 1 || fcb < 0 || fcb > 1)) return MX_ERR_FORMAT;
   if (kind == 5 && (fca < 2 || fca > 3 || fcb < 2 || fcb > 3)) return MX_ERR_FORMAT;
   if (kind == 2 && (fca < 0 || fca > 1 || fcb != 4)) return MX_ERR_FORMAT;
-  const int fc = kind == 0 || kind == 2 || kind == 5 ? fca | (fcb << 4) : 0;
+  if (kind == 3 && (fca != 4 || fcb < 0 || fcb > 1)) return MX_ERR_FORMAT;
+  const int fc = kind == 0 || kind == 2 || kind == 3 || kind == 5 ? fca | (fcb << 4) : 0;
   if (qa) {
     if (kind != 0 || fc != 0) return MX_ERR_FORMAT;
     hipLaunchKernelGGL((gemm_pp_ring_kernel<0, true>), grid, block, 0, stream, a);
@@ -1574,6 +1629,10 @@ int gemm_pp_ring_launch(int kind, int fca, int fcb, const void* A, const void* S
     hipLaunchKernelGGL((gemm_pp_ring_kernel<2, false, 0x40>), grid, block, 0, stream, a);
   } else if (kind == 2 && fc == 0x41) {
     hipLaunchKernelGGL((gemm_pp_ring_kernel<2, false, 0x41>), grid, block, 0, stream, a);
+  } else if (kind == 3 && fc == 0x04) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<3, false, 0x04>), grid, block, 0, stream, a);
+  } else if (kind == 3 && fc == 0x14) {
+    hipLaunchKernelGGL((gemm_pp_ring_kernel<3, false, 0x14>), grid, block, 0, stream, a);
   } else if (kind == 4) {
     hipLaunchKernelGGL((gemm_pp_ring_kernel<4, false>), grid, block, 0, stream, a);
   } else if (kind == 5 && fc == 0x22) {

@@ -145,9 +145,9 @@ int mxgemm_destroy(mxgemm_t p);
  * stage, and the kernel variant (0: 4 waves, 1: 8 waves, 2: 8-wave ping-pong schedule, 3: 4-stage
  * LDS ring of 64-byte K stages, for MX formats with N % 4 == 0 and K % 512 == 0 (E4M3) or
  * K % 1024 == 0 (E2M1), and for fp16 with N % 256 == 0, K % 256 == 0 on 256x256 tiles; 4: 8-wave
- * ping-pong ring of 128-byte stage rows (FP6: 96) on 256x256 tiles, for E4M3 x E4M3, E2M1 x E2M1,
- * E5M2 with E5M2 or E4M3 and the FP6 pairs where K % 1024 == 0 and N % 4 == 0, and for
- * MXGEMM_QUANT_A). The environment
+ * ping-pong ring of 128-byte stage rows (FP6: 96) on 256x256 tiles, for every MX pair where
+ * K % 1024 == 0 and N % 4 == 0 (the E2M1 operand of a mix with a byte format staged four K-steps
+ * at a time), for fp16 where K % 512 == 0 and N % 8 == 0, and for MXGEMM_QUANT_A). The environment
  * variable MXGEMM_TILE (a tile id 0..11; 8, 9 and 10 are the 4-stage ring with 256x256, 256x224
  * and 256x192 tiles where it applies, else an 8-wave kernel: 256x256 for 8 and 10, 256x224 for 9;
  * 11 is the ping-pong ring where it applies, else as 8), read at mxgemm_create, overrides the

@@ -763,38 +763,39 @@ def test_mx_pp_ring_e5m2_nonfinite_and_relu(orc):
     assert ok, (ratio, bad)
 
 
-@pytest.mark.parametrize("fa", [0, 1])
+@pytest.mark.parametrize("fa,fb", [(0, 4), (1, 4), (4, 0), (4, 1)])
 @pytest.mark.parametrize("M,N,K", [(300, 520, 1024), (257, 260, 4096), (512, 1024, 2048), (33, 1028, 3072),
                                    (1, 4, 1024), (256, 8, 5120)])
-def test_mx_pp_ring_byte_a_e2m1_b(orc, fa, M, N, K):
-    """E4M3 or E5M2 A with E2M1 B on the ping-pong ring (its default where K % 1024 == 0): B rows
-    staged 128 bytes (four steps) at a time every other slot, 16-byte E2M1 fragments; every output,
-    partial tiles, a grid of 8 tiles, a single row, ten scale groups."""
+def test_mx_pp_ring_byte_e2m1_mixes(orc, fa, fb, M, N, K):
+    """E4M3 or E5M2 with E2M1, in both orders, on the ping-pong ring (its default where K % 1024 ==
+    0): the E2M1 operand's rows staged 128 bytes (four steps) at a time every other slot, 16-byte
+    E2M1 fragments; every output, partial tiles, a grid of 8 tiles, a single row, ten scale groups."""
     api = require_gpu()
-    say(f"pp ring byte x e2m1 fa={fa} M={M} N={N} K={K}")
-    p = api.mxgemm_create(M, N, K, fa, 4)
+    say(f"pp ring byte x e2m1 fa={fa} fb={fb} M={M} N={N} K={K}")
+    p = api.mxgemm_create(M, N, K, fa, fb)
     assert api.mxgemm_plan_info(p)[3] == 4
     api.mxgemm_destroy(p)
-    C, ref, R = pair_case(orc, api, fa, 4, M, N, K, 2900 + 5 * fa + M + N + K)
+    C, ref, R = pair_case(orc, api, fa, fb, M, N, K, 2900 + 5 * fa + 3 * fb + M + N + K)
     assert not np.isnan(C).any()
     ok, ratio, bad = orc.check(C, ref, K, R)
     assert ok, (ratio, bad)
 
 
-def test_mx_pp_ring_byte_a_e2m1_b_nonfinite_and_relu(orc):
-    """E4M3 A x E2M1 B on the ping-pong ring with NaN scales and codes, extreme scales, and ReLU;
-    the same operands on the 4-stage ring agree with the oracle too."""
+@pytest.mark.parametrize("fa,fb", [(0, 4), (4, 0)])
+def test_mx_pp_ring_byte_e2m1_nonfinite_and_relu(orc, fa, fb):
+    """E4M3 x E2M1 in both orders on the ping-pong ring with NaN scales and codes, extreme scales,
+    and ReLU; the same operands on the 4-stage ring agree with the oracle too."""
     api = require_gpu()
     M, N, K = 300, 520, 1024
-    say("pp ring e4m3 x e2m1 nonfinite")
-    A, SA, B, SB = nonfinite_operands(0, 4, M, N, K, 2950)
-    ref = orc.mxgemm(0, 4, A, SA, B, SB, M, N, K)
-    R = orc.rms_ab(np.nan_to_num(orc.dequant(0, A, SA, M, K)), np.nan_to_num(orc.dequant(4, B, SB, N, K)).T)
+    say(f"pp ring byte x e2m1 nonfinite fa={fa} fb={fb}")
+    A, SA, B, SB = nonfinite_operands(fa, fb, M, N, K, 2950 + fa)
+    ref = orc.mxgemm(fa, fb, A, SA, B, SB, M, N, K)
+    R = orc.rms_ab(np.nan_to_num(orc.dequant(fa, A, SA, M, K)), np.nan_to_num(orc.dequant(fb, B, SB, N, K)).T)
     for tile in (11, 8):
-        C = with_tile(tile, lambda: gpu_gemm(api, 0, dev(A), dev(SA), dev(B), dev(SB), M, N, K, fb=4))
+        C = with_tile(tile, lambda: gpu_gemm(api, fa, dev(A), dev(SA), dev(B), dev(SB), M, N, K, fb=fb))
         ok, ratio, bad = orc.check(C, ref, K, R)
         assert ok, (tile, ratio, bad)
-    Cr = gpu_gemm(api, 0, dev(A), dev(SA), dev(B), dev(SB), M, N, K, fb=4, flags=api.MXGEMM_RELU)
+    Cr = gpu_gemm(api, fa, dev(A), dev(SA), dev(B), dev(SB), M, N, K, fb=fb, flags=api.MXGEMM_RELU)
     ok, ratio, bad = orc.check(Cr, orc.relu(ref), K, R)
     assert ok, (ratio, bad)
 

@@ -254,13 +254,12 @@ def test_ring_tile_plan_info(monkeypatch):
 
 def test_e5m2_pairs_plan(monkeypatch):
     """Every pair with an E5M2 operand, and the FP6 pairs, is accepted where the ring applies (K % 512 == 0,
-    N % 4 == 0), runs the 256x256 ring (E5M2 with E5M2, E4M3 or an E2M1 B, and the FP6 pairs: the
-    ping-pong ring where K % 1024 == 0, unless another tile is forced), and is refused with
-    MX_ERR_SHAPE elsewhere."""
+    N % 4 == 0), runs the ping-pong ring where K % 1024 == 0 (unless another tile is forced) and the
+    256x256 ring elsewhere, and is refused with MX_ERR_SHAPE where neither applies."""
     pairs = ((api.MX_E5M2, api.MX_E5M2), (api.MX_E4M3, api.MX_E5M2), (api.MX_E5M2, api.MX_E4M3),
              (api.MX_E5M2, api.MX_E2M1), (api.MX_E2M1, api.MX_E5M2), (api.MX_E2M3, api.MX_E2M3),
              (api.MX_E3M2, api.MX_E3M2), (api.MX_E2M3, api.MX_E3M2), (api.MX_E3M2, api.MX_E2M3))
-    pp_pairs = pairs[:4] + pairs[5:]   # E5M2 with E5M2 / E4M3 / E2M1 B, FP6: the ping-pong ring where K % 1024 == 0
+    pp_pairs = pairs   # every one: the ping-pong ring where K % 1024 == 0
     for tile in (None, "9", "10", "4", "11"):
         if tile is None:
             monkeypatch.delenv("MXGEMM_TILE", raising=False)
@@ -288,12 +287,12 @@ def test_e5m2_pairs_plan(monkeypatch):
 
 def test_mixed_pairs_plan(monkeypatch):
     """Mixed MX pairs are accepted where the ring kernel applies (K % 512 == 0, N % 4 == 0) and
-    refused with MX_ERR_SHAPE elsewhere; E4M3 A x E2M1 B plans the ping-pong ring where K % 1024 == 0
-    (unless another tile is forced), E2M1 A x E4M3 B always the ring."""
+    refused with MX_ERR_SHAPE elsewhere; they plan the ping-pong ring where K % 1024 == 0 (unless
+    another tile is forced) and the ring elsewhere."""
     monkeypatch.delenv("MXGEMM_TILE", raising=False)
     for fa, fb in ((api.MX_E4M3, api.MX_E2M1), (api.MX_E2M1, api.MX_E4M3)):
         p = api.mxgemm_create(2048, 14336, 4096, fa, fb)
-        assert api.mxgemm_plan_info(p) == (256, 256, 64, 4 if fa == api.MX_E4M3 else 3)
+        assert api.mxgemm_plan_info(p) == (256, 256, 64, 4)
         api.mxgemm_destroy(p)
         p = api.mxgemm_create(300, 520, 1536, fa, fb)   # K % 1024 != 0: the ring
         assert api.mxgemm_plan_info(p) == (256, 256, 64, 3)
